@@ -1,0 +1,213 @@
+"""PyTorch-facing calls of the chunkwise CP linear-attention library.
+
+PyTorch provides device memory and the current HIP stream; every step of the
+computation runs in libcpla's kernels. The split mirrors the Megatron-Core page
+``core.ssm.context_parallel.chunkwise``: ``forward`` = cp_forward_prepare +
+cp_forward_apply over all simulated shards (``chunkwise_cp_forward`` on one
+GPU), ``backward`` = cp_backward_prepare + cp_backward_apply
+(``chunkwise_cp_backward``); ``Context`` plays the part of ``CPSavedContext``
+(tensors only, plus a plain problem description).
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import _lib
+from ._lib import CplaError, Packed, Problem, check
+
+_DTYPE = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _i32p(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+# ---- packed-sequence metadata (host, in the library) --------------------------------
+
+def seq_idx_from_cu_seqlens(cu_seqlens, T: int) -> np.ndarray:
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
+    out = np.empty(T, dtype=np.int32)
+    check(_lib.lib().cpla_seq_idx_from_cu_seqlens(_i32p(cu), len(cu) - 1, T, _i32p(out)))
+    return out
+
+
+def packed_rank_slices(global_seq_idx: np.ndarray, cp_size: int):
+    s = np.ascontiguousarray(global_seq_idx, dtype=np.int32)
+    prs = np.empty(cp_size, dtype=np.int32)
+    frs = np.empty(cp_size, dtype=np.int32)
+    check(_lib.lib().cpla_packed_rank_slices(_i32p(s), len(s), cp_size, _i32p(prs), _i32p(frs)))
+    return prs, frs
+
+
+def build_packed_sequence_cp_metadata(global_seq_idx, cp_rank: int, cp_size: int) -> dict:
+    s = np.ascontiguousarray(np.asarray(global_seq_idx), dtype=np.int32)
+    L = len(s) // cp_size if cp_size > 0 else 0
+    local = np.empty(max(L, 1), dtype=np.int32)
+    cu = np.empty(max(L, 1) + 1, dtype=np.int32)
+    n = ctypes.c_int32()
+    prs = ctypes.c_int32()
+    frs = ctypes.c_int32()
+    pi = ctypes.POINTER(ctypes.c_int32)
+    check(_lib.lib().build_packed_sequence_cp_metadata(
+        _i32p(s), len(s), cp_rank, cp_size, _i32p(local), _i32p(cu), ctypes.cast(ctypes.byref(n), pi),
+        ctypes.cast(ctypes.byref(prs), pi), ctypes.cast(ctypes.byref(frs), pi)))
+    return {"local_seq_idx": local[:L].copy(), "local_cu_seqlens": cu[:n.value + 1].copy(),
+            "preceding_rank_start": prs.value, "following_rank_stop": frs.value}
+
+
+@dataclasses.dataclass
+class PackedMeta:
+    seq_idx: torch.Tensor                 # device int32 [T]
+    preceding_rank_start: torch.Tensor    # device int32 [P]
+    following_rank_stop: torch.Tensor     # device int32 [P]
+
+    def c(self) -> Packed:
+        return Packed(self.seq_idx.data_ptr(), self.preceding_rank_start.data_ptr(),
+                      self.following_rank_stop.data_ptr())
+
+
+def packed_meta(cu_seqlens, T: int, num_shards: int, device) -> PackedMeta:
+    s = seq_idx_from_cu_seqlens(cu_seqlens, T)
+    prs, frs = packed_rank_slices(s, num_shards)
+    dev = torch.device(device)
+    return PackedMeta(torch.from_numpy(s).to(dev), torch.from_numpy(prs).to(dev), torch.from_numpy(frs).to(dev))
+
+
+# ---- forward / backward ----------------------------------------------------------------
+
+@dataclasses.dataclass
+class Context:
+    problem: Problem
+    decay: int
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: Optional[torch.Tensor]
+    packed: Optional[PackedMeta]
+    fwd_summary: torch.Tensor
+    shard_in_state: torch.Tensor
+    final_state: torch.Tensor
+    chunk_states: Optional[torch.Tensor]
+    has_initial_state: bool
+
+
+def _decay_of(g: Optional[torch.Tensor], q: torch.Tensor) -> int:
+    if g is None:
+        return _lib.DECAY_NONE
+    if g.dim() == 3:
+        return _lib.DECAY_SCALAR
+    if g.dim() == 4 and g.shape[-1] == q.shape[-1]:
+        return _lib.DECAY_DIAG
+    raise ValueError(f"g must be [B,T,H] or [B,T,H,dk], got {tuple(g.shape)}")
+
+
+def make_problem(q, v, num_shards: int, decay: int, chunk: int = 64, rank_range=None) -> Problem:
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if q.dtype not in _DTYPE:
+        raise CplaError(3, f"dtype {q.dtype} unsupported")
+    rb, re = (0, num_shards) if rank_range is None else rank_range
+    return Problem(B, T, H, dk, dv, num_shards, chunk, rb, re, _DTYPE[q.dtype], decay)
+
+
+def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor] = None, *,
+            num_shards: int, initial_state: Optional[torch.Tensor] = None, cu_seqlens=None,
+            packed: Optional[PackedMeta] = None, save_for_backward: bool = True, chunk: int = 64,
+            out: Optional[torch.Tensor] = None):
+    """o [B,T,H,dv] (dtype of q) and a Context for ``backward``."""
+    for t in (q, k, v, g, initial_state):
+        if t is not None and not t.is_contiguous():
+            raise CplaError(1, "inputs must be contiguous")
+    decay = _decay_of(g, q)
+    p = make_problem(q, v, num_shards, decay, chunk)
+    if cu_seqlens is not None and packed is None:
+        packed = packed_meta(cu_seqlens, q.shape[1], num_shards, q.device)
+    L = _lib.lib()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    W = L.cpla_summary_width(ctypes.byref(p))
+    dev = q.device
+    fsum = torch.empty((num_shards, B, H, W), device=dev, dtype=torch.float32)
+    s_in = torch.empty((num_shards, B, H, dk, dv), device=dev, dtype=torch.float32)
+    fin = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+    cs = None
+    if save_for_backward:
+        cs = torch.empty((B, H, T // chunk, dk, dv), device=dev, dtype=torch.float32)
+    o = torch.empty(v.shape, device=dev, dtype=q.dtype) if out is None else out
+    pk = ctypes.byref(packed.c()) if packed is not None else None
+    st = _stream()
+    check(L.cp_forward_prepare(ctypes.byref(p), pk, _ptr(k), _ptr(v), _ptr(g), _ptr(fsum), st))
+    check(L.cp_forward_apply(ctypes.byref(p), pk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(fsum),
+                             _ptr(initial_state), _ptr(o), _ptr(s_in), _ptr(fin), _ptr(cs), st))
+    ctx = Context(p, decay, q, k, v, g, packed, fsum, s_in, fin, cs, initial_state is not None)
+    return o, ctx
+
+
+def backward(dO: torch.Tensor, ctx: Context, d_final_state: Optional[torch.Tensor] = None,
+             want_intermediates: bool = False):
+    """(dq, dk, dv, dg, d_initial_state); dg is None without decay, d_initial_state
+    None with packed sequences."""
+    if ctx.chunk_states is None:
+        raise CplaError(1, "forward was run with save_for_backward=False")
+    if not dO.is_contiguous():
+        raise CplaError(1, "dO must be contiguous")
+    L = _lib.lib()
+    p = ctx.problem
+    B, T, H, dk = ctx.q.shape
+    dv = ctx.v.shape[-1]
+    P = p.num_shards
+    dev = dO.device
+    W = L.cpla_summary_width(ctypes.byref(p))
+    bsum = torch.empty((P, B, H, W), device=dev, dtype=torch.float32)
+    s_out = torch.empty((P, B, H, dk, dv), device=dev, dtype=torch.float32)
+    dq = torch.empty_like(ctx.q)
+    dk_ = torch.empty_like(ctx.k)
+    dv_ = torch.empty_like(ctx.v)
+    dg = None if ctx.g is None else torch.empty_like(ctx.g)
+    dS0 = None
+    if ctx.packed is None:
+        dS0 = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+    pk = ctypes.byref(ctx.packed.c()) if ctx.packed is not None else None
+    st = _stream()
+    check(L.cp_backward_prepare(ctypes.byref(p), pk, _ptr(ctx.q), _ptr(ctx.g), _ptr(dO), _ptr(bsum), st))
+    check(L.cp_backward_apply(ctypes.byref(p), pk, _ptr(ctx.q), _ptr(ctx.k), _ptr(ctx.v), _ptr(ctx.g),
+                              _ptr(dO), _ptr(ctx.chunk_states), _ptr(bsum), _ptr(d_final_state), _ptr(dq),
+                              _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(s_out), _ptr(dS0), st))
+    res = (dq, dk_, dv_, dg, dS0)
+    if want_intermediates:
+        return res, {"bwd_summary": bsum, "shard_out_grad": s_out}
+    return res
+
+
+class ChunkwiseLinearAttention(torch.autograd.Function):
+    """Autograd adapter: o = f(q, k, v, g, S_init) with shards simulated on one GPU."""
+
+    @staticmethod
+    def forward(fctx, q, k, v, g, initial_state, num_shards, cu_seqlens):
+        o, c = forward(q, k, v, g, num_shards=num_shards, initial_state=initial_state, cu_seqlens=cu_seqlens)
+        fctx.cpla = c
+        return o
+
+    @staticmethod
+    def backward(fctx, dO):
+        dq, dk, dv, dg, dS0 = backward(dO.contiguous(), fctx.cpla)
+        if not fctx.cpla.has_initial_state:
+            dS0 = None
+        return dq, dk, dv, dg, dS0, None, None
+
+
+def chunkwise_linear_attention(q, k, v, g=None, initial_state=None, *, num_shards: int = 1, cu_seqlens=None):
+    return ChunkwiseLinearAttention.apply(q, k, v, g, initial_state, num_shards, cu_seqlens)

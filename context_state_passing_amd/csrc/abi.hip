@@ -1,0 +1,299 @@
+// C-ABI entry points: host-side validation, then launches on the caller's stream.
+//
+// The four calls are the local-backend protocol of the Megatron-Core page
+// core.ssm.context_parallel.chunkwise (LinearAttentionCPBackend.cp_forward_prepare,
+// cp_forward_apply, cp_backward_prepare, cp_backward_apply). The composition
+// step that the page's orchestrators (chunkwise_cp_forward / chunkwise_cp_backward)
+// perform after gathering summaries runs here as the affine_scan kernel, since on
+// one GPU every shard's summary already sits in one buffer. Validation mirrors
+// _validate_summary_tensor and fails fast on uneven division.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "cpla.h"
+#include "errors.hpp"
+#include "kernels.hpp"
+
+namespace cpla {
+
+static thread_local char g_err[512];
+const char* last_error_buf() { return g_err; }
+void set_error_v(const char* fmt, va_list ap) { vsnprintf(g_err, sizeof(g_err), fmt, ap); }
+void clear_error() { g_err[0] = 0; }
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int64_t m_slot_of(const cpla_problem* p) { return p->decay == CPLA_DECAY_DIAG ? p->dk : 4; }
+
+cpla_status check_problem(const cpla_problem* p) {
+  if (!p) return fail(CPLA_E_INVALID, "problem is NULL");
+  if (p->B <= 0 || p->T <= 0 || p->H <= 0 || p->dk <= 0 || p->dv <= 0)
+    return fail(CPLA_E_SHAPE, "B, T, H, dk, dv must be positive");
+  if (p->dtype != CPLA_F32 && p->dtype != CPLA_BF16) return fail(CPLA_E_DTYPE, "unknown dtype %d", p->dtype);
+  if (p->decay < CPLA_DECAY_NONE || p->decay > CPLA_DECAY_DIAG) return fail(CPLA_E_INVALID, "unknown decay %d", p->decay);
+  if (p->chunk != 64) return fail(CPLA_E_UNSUPPORTED, "chunk %d unsupported (64 only)", p->chunk);
+  if (p->num_shards <= 0) return fail(CPLA_E_SHAPE, "num_shards must be positive");
+  if (p->T % p->num_shards != 0)
+    return fail(CPLA_E_SHAPE, "T=%lld is not divisible by num_shards=%d", (long long)p->T, p->num_shards);
+  if ((p->T / p->num_shards) % p->chunk != 0)
+    return fail(CPLA_E_SHAPE, "shard length %lld is not a multiple of chunk %d", (long long)(p->T / p->num_shards),
+                p->chunk);
+  if (p->num_shards > 64) return fail(CPLA_E_UNSUPPORTED, "num_shards=%d > 64 unsupported", p->num_shards);
+  if (p->rank_begin < 0 || p->rank_end > p->num_shards || p->rank_begin >= p->rank_end)
+    return fail(CPLA_E_INVALID, "rank range [%d, %d) outside [0, %d)", p->rank_begin, p->rank_end, p->num_shards);
+  if (p->dk != p->dv) return fail(CPLA_E_UNSUPPORTED, "dk != dv unsupported");
+  const bool bf = p->dtype == CPLA_BF16;
+  if (!(p->dk == 16 || p->dk == 64 || (bf && p->dk == 128)))
+    return fail(CPLA_E_UNSUPPORTED, "head dim %lld unsupported for dtype %s (bf16: 16, 64, 128; fp32: 16, 64)",
+                (long long)p->dk, bf ? "bf16" : "fp32");
+  if (p->B * p->H > 65535) return fail(CPLA_E_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)(p->B * p->H));
+  return CPLA_OK;
+}
+
+cpla_status check_ptr(const void* ptr, const char* name, bool required) {
+  if (!ptr) return required ? fail(CPLA_E_INVALID, "%s is NULL", name) : CPLA_OK;
+  if (!aligned16(ptr)) return fail(CPLA_E_ALIGN, "%s is not 16-byte aligned", name);
+  return CPLA_OK;
+}
+
+cpla_status check_packed(const cpla_problem* p, const cpla_packed* pk, bool need_prs, bool need_frs) {
+  if (!pk) return CPLA_OK;
+  if (p->B != 1) return fail(CPLA_E_SHAPE, "packed sequences need B == 1 (got %lld)", (long long)p->B);
+  cpla_status st;
+  if ((st = check_ptr(pk->seq_idx, "packed->seq_idx", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(pk->preceding_rank_start, "packed->preceding_rank_start", need_prs)) != CPLA_OK) return st;
+  if ((st = check_ptr(pk->following_rank_stop, "packed->following_rank_stop", need_frs)) != CPLA_OK) return st;
+  return CPLA_OK;
+}
+
+cpla_status check_decay_ptr(const cpla_problem* p, const float* g, const char* name) {
+  if (p->decay == CPLA_DECAY_NONE) {
+    if (g) return fail(CPLA_E_INVALID, "%s must be NULL without decay", name);
+    return CPLA_OK;
+  }
+  return check_ptr(g, name, true);
+}
+
+cpla_status launched(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(CPLA_E_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return CPLA_OK;
+}
+
+// ---- kernel tables --------------------------------------------------------------
+typedef void (*fwd_fn)(FwdArgs);
+typedef void (*bwd_fn)(BwdArgs);
+
+template <bool APPLY>
+fwd_fn pick_fwd(int dtype, int D, int decay) {
+#define CPLA_FWD_CASE(E, DD)                                              \
+  if (D == DD) {                                                          \
+    if (decay == 0) return fwd_walk<E, DD, DD, 0, APPLY>;                 \
+    if (decay == 1) return fwd_walk<E, DD, DD, 1, APPLY>;                 \
+    return fwd_walk<E, DD, DD, 2, APPLY>;                                 \
+  }
+  if (dtype == CPLA_BF16) {
+    CPLA_FWD_CASE(bf16_t, 16)
+    CPLA_FWD_CASE(bf16_t, 64)
+    CPLA_FWD_CASE(bf16_t, 128)
+  } else {
+    CPLA_FWD_CASE(float, 16)
+    CPLA_FWD_CASE(float, 64)
+  }
+#undef CPLA_FWD_CASE
+  return nullptr;
+}
+
+template <bool APPLY>
+bwd_fn pick_bwd(int dtype, int D, int decay) {
+#define CPLA_BWD_CASE(E, DD)                                              \
+  if (D == DD) {                                                          \
+    if (decay == 0) return bwd_walk<E, DD, DD, 0, APPLY>;                 \
+    if (decay == 1) return bwd_walk<E, DD, DD, 1, APPLY>;                 \
+    return bwd_walk<E, DD, DD, 2, APPLY>;                                 \
+  }
+  if (dtype == CPLA_BF16) {
+    CPLA_BWD_CASE(bf16_t, 16)
+    CPLA_BWD_CASE(bf16_t, 64)
+    CPLA_BWD_CASE(bf16_t, 128)
+  } else {
+    CPLA_BWD_CASE(float, 16)
+    CPLA_BWD_CASE(float, 64)
+  }
+#undef CPLA_BWD_CASE
+  return nullptr;
+}
+
+int next_pow2(int x) {
+  int g = 1;
+  while (g < x) g <<= 1;
+  return g;
+}
+
+cpla_status launch_scan(const cpla_problem* p, const float* summary, const int32_t* slice, const float* init,
+                        float* out, float* fin, int reverse, hipStream_t stream) {
+  ScanArgs s;
+  s.BH = p->B * p->H;
+  s.W = cpla_summary_width(p);
+  s.dk = (int)p->dk;
+  s.dv = (int)p->dv;
+  s.n_elem = s.BH * p->dk * p->dv;
+  s.P = p->num_shards;
+  s.m_slot = (int)m_slot_of(p);
+  s.diag = p->decay == CPLA_DECAY_DIAG;
+  s.reverse = reverse;
+  s.group = next_pow2(p->num_shards);
+  s.summary = summary;
+  s.slice = slice;
+  s.init = init;
+  s.out = out;
+  s.fin = fin;
+  const int64_t threads = s.n_elem * s.group;
+  const int64_t blocks = (threads + 255) / 256;
+  hipLaunchKernelGGL(affine_scan, dim3((unsigned)blocks), dim3(256), 0, stream, s);
+  return launched("affine_scan");
+}
+
+}  // namespace
+}  // namespace cpla
+
+using namespace cpla;
+
+extern "C" const char* cpla_last_error(void) { return last_error_buf(); }
+extern "C" int cpla_abi_version(void) { return CPLA_ABI_VERSION; }
+
+extern "C" int64_t cpla_summary_width(const cpla_problem* p) {
+  if (!p) return -1;
+  return m_slot_of(p) + p->dk * p->dv;
+}
+
+extern "C" int64_t cpla_chunk_states_bytes(const cpla_problem* p) {
+  if (!p || p->chunk <= 0) return -1;
+  return p->B * p->H * (p->T / p->chunk) * p->dk * p->dv * (int64_t)sizeof(float);
+}
+
+extern "C" cpla_status cp_forward_prepare(const cpla_problem* p, const cpla_packed* packed, const void* k,
+                                          const void* v, const float* g, float* fwd_summary, hipStream_t stream) {
+  clear_error();
+  cpla_status st;
+  if ((st = check_problem(p)) != CPLA_OK) return st;
+  if ((st = check_packed(p, packed, false, false)) != CPLA_OK) return st;
+  if ((st = check_ptr(k, "k", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(v, "v", true)) != CPLA_OK) return st;
+  if ((st = check_decay_ptr(p, g, "g")) != CPLA_OK) return st;
+  if ((st = check_ptr(fwd_summary, "fwd_summary", true)) != CPLA_OK) return st;
+  FwdArgs a = {};
+  a.B = p->B; a.T = p->T; a.H = p->H; a.W = cpla_summary_width(p);
+  a.P = p->num_shards; a.rank_begin = p->rank_begin; a.m_slot = (int)m_slot_of(p);
+  a.k = k; a.v = v; a.g = g;
+  a.seq_idx = packed ? packed->seq_idx : nullptr;
+  a.summary = fwd_summary;
+  fwd_fn fn = pick_fwd<false>(p->dtype, (int)p->dk, p->decay);
+  if (!fn) return fail(CPLA_E_UNSUPPORTED, "no forward kernel for this configuration");
+  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(NTHR), 0, stream, a);
+  return launched("cp_forward_prepare");
+}
+
+extern "C" cpla_status cp_forward_apply(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                        const void* k, const void* v, const float* g, const float* fwd_summary,
+                                        const float* initial_state, void* o, float* shard_in_state,
+                                        float* final_state, void* chunk_states, hipStream_t stream) {
+  clear_error();
+  cpla_status st;
+  if ((st = check_problem(p)) != CPLA_OK) return st;
+  if ((st = check_packed(p, packed, true, false)) != CPLA_OK) return st;
+  if ((st = check_ptr(q, "q", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(k, "k", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(v, "v", true)) != CPLA_OK) return st;
+  if ((st = check_decay_ptr(p, g, "g")) != CPLA_OK) return st;
+  if ((st = check_ptr(fwd_summary, "fwd_summary", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(initial_state, "initial_state", false)) != CPLA_OK) return st;
+  if ((st = check_ptr(o, "o", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(shard_in_state, "shard_in_state", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(final_state, "final_state", false)) != CPLA_OK) return st;
+  if ((st = check_ptr(chunk_states, "chunk_states", false)) != CPLA_OK) return st;
+  if (packed && initial_state) return fail(CPLA_E_INVALID, "initial_state must be NULL with packed sequences");
+  st = launch_scan(p, fwd_summary, packed ? packed->preceding_rank_start : nullptr, initial_state, shard_in_state,
+                   final_state, 0, stream);
+  if (st != CPLA_OK) return st;
+  FwdArgs a = {};
+  a.B = p->B; a.T = p->T; a.H = p->H; a.W = cpla_summary_width(p);
+  a.P = p->num_shards; a.rank_begin = p->rank_begin; a.m_slot = (int)m_slot_of(p);
+  a.q = q; a.k = k; a.v = v; a.g = g;
+  a.seq_idx = packed ? packed->seq_idx : nullptr;
+  a.state_in = shard_in_state;
+  a.out = o;
+  a.chunk_states = reinterpret_cast<float*>(chunk_states);
+  fwd_fn fn = pick_fwd<true>(p->dtype, (int)p->dk, p->decay);
+  if (!fn) return fail(CPLA_E_UNSUPPORTED, "no forward kernel for this configuration");
+  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(NTHR), 0, stream, a);
+  return launched("cp_forward_apply");
+}
+
+extern "C" cpla_status cp_backward_prepare(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                           const float* g, const void* dO, float* bwd_summary, hipStream_t stream) {
+  clear_error();
+  cpla_status st;
+  if ((st = check_problem(p)) != CPLA_OK) return st;
+  if ((st = check_packed(p, packed, false, false)) != CPLA_OK) return st;
+  if ((st = check_ptr(q, "q", true)) != CPLA_OK) return st;
+  if ((st = check_decay_ptr(p, g, "g")) != CPLA_OK) return st;
+  if ((st = check_ptr(dO, "dO", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(bwd_summary, "bwd_summary", true)) != CPLA_OK) return st;
+  BwdArgs a = {};
+  a.B = p->B; a.T = p->T; a.H = p->H; a.W = cpla_summary_width(p);
+  a.P = p->num_shards; a.rank_begin = p->rank_begin; a.m_slot = (int)m_slot_of(p);
+  a.q = q; a.g = g; a.dO = dO;
+  a.seq_idx = packed ? packed->seq_idx : nullptr;
+  a.summary = bwd_summary;
+  bwd_fn fn = pick_bwd<false>(p->dtype, (int)p->dk, p->decay);
+  if (!fn) return fail(CPLA_E_UNSUPPORTED, "no backward kernel for this configuration");
+  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(NTHR), 0, stream, a);
+  return launched("cp_backward_prepare");
+}
+
+extern "C" cpla_status cp_backward_apply(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                         const void* k, const void* v, const float* g, const void* dO,
+                                         const void* chunk_states, const float* bwd_summary,
+                                         const float* d_final_state, void* dq, void* dk, void* dv, float* dg,
+                                         float* shard_out_grad, float* d_initial_state, hipStream_t stream) {
+  clear_error();
+  cpla_status st;
+  if ((st = check_problem(p)) != CPLA_OK) return st;
+  if ((st = check_packed(p, packed, false, true)) != CPLA_OK) return st;
+  if ((st = check_ptr(q, "q", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(k, "k", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(v, "v", true)) != CPLA_OK) return st;
+  if ((st = check_decay_ptr(p, g, "g")) != CPLA_OK) return st;
+  if ((st = check_ptr(dO, "dO", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(chunk_states, "chunk_states", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(bwd_summary, "bwd_summary", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(d_final_state, "d_final_state", false)) != CPLA_OK) return st;
+  if ((st = check_ptr(dq, "dq", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(dk, "dk", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(dv, "dv", true)) != CPLA_OK) return st;
+  if ((st = check_decay_ptr(p, dg, "dg")) != CPLA_OK) return st;
+  if ((st = check_ptr(shard_out_grad, "shard_out_grad", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(d_initial_state, "d_initial_state", false)) != CPLA_OK) return st;
+  if (packed && (d_final_state || d_initial_state))
+    return fail(CPLA_E_INVALID, "d_final_state and d_initial_state must be NULL with packed sequences");
+  st = launch_scan(p, bwd_summary, packed ? packed->following_rank_stop : nullptr, d_final_state, shard_out_grad,
+                   d_initial_state, 1, stream);
+  if (st != CPLA_OK) return st;
+  BwdArgs a = {};
+  a.B = p->B; a.T = p->T; a.H = p->H; a.W = cpla_summary_width(p);
+  a.P = p->num_shards; a.rank_begin = p->rank_begin; a.m_slot = (int)m_slot_of(p);
+  a.q = q; a.k = k; a.v = v; a.g = g; a.dO = dO;
+  a.seq_idx = packed ? packed->seq_idx : nullptr;
+  a.chunk_states = reinterpret_cast<const float*>(chunk_states);
+  a.grad_in = shard_out_grad;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
+  bwd_fn fn = pick_bwd<true>(p->dtype, (int)p->dk, p->decay);
+  if (!fn) return fail(CPLA_E_UNSUPPORTED, "no backward kernel for this configuration");
+  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(NTHR), 0, stream, a);
+  return launched("cp_backward_apply");
+}

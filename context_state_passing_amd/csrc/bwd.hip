@@ -1,0 +1,623 @@
+// Backward shard walks: cp_backward_prepare (APPLY = false) and the local part of
+// cp_backward_apply (APPLY = true).
+//
+// One workgroup walks one (shard, b, h) from its last chunk to its first,
+// carrying dS (gradient w.r.t. the state at the current chunk's end, d_k x d_v,
+// fp32) in MFMA accumulators twice: dS with wave w owning d_v tiles w, w+4, ...,
+// and its transpose with wave w owning d_k tiles w, w+4, ... (the two feed the
+// contractions over d_k and over d_v). The state entering each chunk, S0, is
+// read (fp32) from the chunk states the forward saved.
+//
+// Per chunk (Gam, live, tail as in chunk_common.hpp; A = masked decayed scores,
+// dA_ij = [same sequence, i >= j] (dO_i . v_j) (* exp(Gam_i - Gam_j) for a scalar decay)):
+//   dq_i = live_i exp(Gam_i) * S0 dO_i + sum_j dA_ij exp(Gam_i - Gam_j) * k_j
+//   dk_j = sum_i dA_ij exp(Gam_i - Gam_j) * q_i + tail_j exp(Gam_last - Gam_j) * dS v_j
+//   dv_j = sum_i A_ij dO_i + tail_j dS^T (k_j * exp(Gam_last - Gam_j))
+//   dS  <- [no start] diag(exp(Gam_last)) dS + sum_i live_i (q_i * exp(Gam_i)) dO_i^T
+//   dg_t = a_t rowsum(dS_t * S_{t-1}) as four non-cancelling parts:
+//     T1 = live part of sum_{i >= t} q_i exp(Gam_i) * (S0 dO_i)
+//     T2 = sum_{i >= t > j} exp(Gam_i - Gam_j) q_i * k_j (dO_i . v_j)
+//     T3 = [no start] exp(Gam_last) * rowsum(dS * S0)
+//     T4 = tail part of sum_{j < t} exp(Gam_last - Gam_j) k_j * (dS v_j)
+//   diagonal decay: T1 + T2 = suffix sums of Q~ * (dq before exp(Gam)) - K~ * (intra dk),
+//   per key dim; scalar decay: T2 from the fp32 product of the score and
+//   score-gradient tiles (row sums left of the diagonal minus column sums below
+//   it, suffix-summed), all parts summed over the key dim; dg = 0 at starts.
+//
+// Every fp32 intermediate that feeds an MFMA (scores, score gradients, S0, dS,
+// exp-scaled q/k tiles) is split into bf16 hi + lo parts; inputs are exact.
+#include "chunk_common.hpp"
+#include "kernels.hpp"
+
+namespace cpla {
+
+template <typename E, int DK, int DV, int DECAY, bool APPLY>
+__global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
+  using G = Geo<E, DK, DV>;
+  constexpr bool SP = Split<E>::on;
+  constexpr bool DIAG = DECAY == DECAY_DIAG, SCAL = DECAY == DECAY_SCALAR;
+  constexpr int NA = APPLY ? 1 : 0;
+  constexpr bool HAS_DG = APPLY && DECAY != DECAY_NONE;
+  // q tile (hi) and its lo part: diagonal decay stores Q~ = Q exp(Gam)
+  constexpr int QLO = (DIAG && SP) ? 1 : 0;
+  // k tile only in apply; lo part for the diagonal decay
+  constexpr int KLO = (APPLY && DIAG && SP) ? 1 : 0;
+  // Q^ = q exp(Gam_i) live_i (scalar decay), split
+  constexpr int QH = SCAL ? 1 : 0;
+  constexpr int QHL = (SCAL && SP) ? 1 : 0;
+  // region: Gam (diag, fp32) during staging, then A/dA hi/lo and the scalar P tile
+  constexpr int GAM_BYTES = DIAG ? CH * DK * 4 : 0;
+  constexpr int AT_BYTES = APPLY ? (SP ? 4 : 2) * G::TILE_A * (int)sizeof(E) : 0;
+  constexpr int P_BYTES = (APPLY && SCAL) ? CH * (CH + 1) * 4 : 0;
+  constexpr int REG_BYTES = (GAM_BYTES > AT_BYTES + P_BYTES ? GAM_BYTES : AT_BYTES + P_BYTES) + 16;
+
+  __shared__ __attribute__((aligned(16))) E s_q[G::TILE_K];
+  __shared__ __attribute__((aligned(16))) E s_ql[QLO * G::TILE_K + 8];
+  __shared__ __attribute__((aligned(16))) E s_k[NA * G::TILE_K + 8];
+  __shared__ __attribute__((aligned(16))) E s_kl[KLO * G::TILE_K + 8];
+  __shared__ __attribute__((aligned(16))) E s_v[NA * G::TILE_V + 8];
+  __shared__ __attribute__((aligned(16))) E s_do[G::TILE_V];
+  __shared__ __attribute__((aligned(16))) E s_qh[QH * G::TILE_K + 8];
+  __shared__ __attribute__((aligned(16))) E s_qhl[QHL * G::TILE_K + 8];
+  __shared__ __attribute__((aligned(16))) char s_reg[REG_BYTES];
+  __shared__ float s_gs[CH], s_fq[CH], s_fk[CH], s_red[NTHR], s_glast[G::DKP];
+  __shared__ float s_t3[G::DKP];
+  __shared__ float s_u1[NWAVE * CH], s_u4[NWAVE * CH];
+
+  float* s_gam = DIAG ? reinterpret_cast<float*>(s_reg) : s_gs;
+  E* s_ah = reinterpret_cast<E*>(s_reg);
+  E* s_al = s_ah + G::TILE_A;
+  E* s_dah = s_ah + (SP ? 2 : 1) * G::TILE_A;
+  E* s_dal = s_dah + G::TILE_A;
+  float* s_p = reinterpret_cast<float*>(s_reg + AT_BYTES);
+  // the tile Q^ is read from in the dS update: scalar -> s_qh, else the q tile
+  const E* qhat_h = SCAL ? s_qh : s_q;
+  const E* qhat_l = SCAL ? s_qhl : s_ql;
+
+  const int w = wave_id(), l = lane_id(), g = l >> 4, i16 = l & 15;
+  const int r = a.rank_begin + blockIdx.x;
+  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t L = a.T / a.P, tshard = r * L;
+  const int nc = (int)(L / CH);
+  const int64_t nct = a.T / CH;
+
+  // dS: rows = all d_k tiles, columns = owned d_v tiles.  dT = dS^T: rows = all
+  // d_v tiles, columns = owned d_k tiles (lane-fixed d).
+  f32x4 dS[G::NKT][G::CPWV];
+  f32x4 dT[APPLY ? G::NVT : 1][G::CPWK];
+  {
+    const float* gin = APPLY ? a.grad_in + (int64_t)(r * a.B * a.H + bh) * DK * DV : nullptr;
+#pragma unroll
+    for (int m = 0; m < G::NKT; ++m)
+#pragma unroll
+      for (int cc = 0; cc < G::CPWV; ++cc) {
+        const int c = w + NWAVE * cc;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d = 16 * m + 4 * g + rr, n = 16 * c + i16;
+          dS[m][cc][rr] = (APPLY && c < G::NVT && d < DK && n < DV) ? gin[d * DV + n] : 0.f;
+        }
+      }
+    if constexpr (APPLY) {
+#pragma unroll
+      for (int nt = 0; nt < G::NVT; ++nt)
+#pragma unroll
+        for (int cc = 0; cc < G::CPWK; ++cc) {
+          const int cm = w + NWAVE * cc;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int n = 16 * nt + 4 * g + rr, d = 16 * cm + i16;
+            dT[nt][cc][rr] = (cm < G::NKT && d < DK && n < DV) ? gin[d * DV + n] : 0.f;
+          }
+        }
+    }
+  }
+
+  const E* q = reinterpret_cast<const E*>(a.q);
+  const E* k = reinterpret_cast<const E*>(a.k);
+  const E* v = reinterpret_cast<const E*>(a.v);
+  const E* dO = reinterpret_cast<const E*>(a.dO);
+  float gsum = 0.f;
+  bool any_start = false;
+
+  for (int c = nc - 1; c >= 0; --c) {
+    const int64_t t0 = tshard + (int64_t)c * CH;
+    const ChunkSeg seg = chunk_seg(a.seq_idx, t0);
+    any_start |= seg.any();
+    const float keep = seg.any() ? 0.f : 1.f;
+    stage_gamma<DK, DECAY>(a.g, b, h, t0, a.T, a.H, seg, s_gam, s_fq, s_fk, s_red);
+
+    // ---- stage tiles ----------------------------------------------------------------
+    if constexpr (DIAG) {
+      if (threadIdx.x < DK) {
+        const float gl = s_gam[(CH - 1) * DK + threadIdx.x];
+        gsum += gl;
+        s_glast[threadIdx.x] = gl;
+      }
+      stage_tile_split<E, DK, G::DKP, G::LDK, 1, DK>(q, b, h, t0, a.T, a.H, s_q, s_ql, s_gam, nullptr);
+      if constexpr (APPLY) stage_tile_split<E, DK, G::DKP, G::LDK, 2, DK>(k, b, h, t0, a.T, a.H, s_k, s_kl, s_gam, nullptr);
+    } else {
+      if constexpr (SCAL) {
+        if (threadIdx.x == 0) gsum += s_gam[CH - 1];
+        stage_tile_split<E, DK, G::DKP, G::LDK, 3, DK>(q, b, h, t0, a.T, a.H, s_qh, s_qhl, s_gam, s_fq);
+      }
+      if constexpr (APPLY || !SCAL) stage_tile<E, DK, G::DKP, G::LDK, 0, DK>(q, b, h, t0, a.T, a.H, s_q, s_gam);
+      if constexpr (APPLY) stage_tile<E, DK, G::DKP, G::LDK, 0, DK>(k, b, h, t0, a.T, a.H, s_k, s_gam);
+    }
+    stage_tile<E, DV, G::DVP, G::LDV, 0, DK>(dO, b, h, t0, a.T, a.H, s_do, s_gam);
+    if constexpr (APPLY) stage_tile<E, DV, G::DVP, G::LDV, 0, DK>(v, b, h, t0, a.T, a.H, s_v, s_gam);
+    __syncthreads();
+
+    // Gam at this wave's dq/dk output positions (diagonal), before the region is reused
+    float gq[G::CPWK][4][4];
+    if constexpr (APPLY && DIAG) {
+#pragma unroll
+      for (int cc = 0; cc < G::CPWK; ++cc)
+#pragma unroll
+        for (int I = 0; I < 4; ++I)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            const int d = 16 * (w + NWAVE * cc) + 4 * g + rr;
+            gq[cc][I][rr] = (w + NWAVE * cc < G::NKT && d < DK) ? s_gam[(16 * I + i16) * DK + d] : 0.f;
+          }
+      __syncthreads();
+    }
+
+    if constexpr (APPLY) {
+      // ---- scores and score gradients (hi/lo) for the wave's tiles -------------------
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        const int idx = score_tile(w, s);
+        const int I = idx >> 2, J = idx & 3;
+        f32x4 xa = {0.f, 0.f, 0.f, 0.f}, xd = {0.f, 0.f, 0.f, 0.f};
+        if (!score_tile_zero(idx)) {
+#pragma unroll
+          for (int kd = 0; kd < G::DKP / 32; ++kd) {
+            Frag<E> fa, fb, fal, fbl;
+            frag_direct(fa, s_q, G::LDK, 16 * I + i16, 32 * kd);
+            frag_direct(fb, s_k, G::LDK, 16 * J + i16, 32 * kd);
+            if constexpr (DIAG && SP) {
+              frag_direct(fal, s_ql, G::LDK, 16 * I + i16, 32 * kd);
+              frag_direct(fbl, s_kl, G::LDK, 16 * J + i16, 32 * kd);
+              mma3(xa, fa, fal, fb, fbl);
+            } else {
+              mma(xa, fa, fb);
+            }
+          }
+#pragma unroll
+          for (int kn = 0; kn < G::DVP / 32; ++kn) {
+            Frag<E> fa, fb;
+            frag_direct(fa, s_do, G::LDV, 16 * I + i16, 32 * kn);
+            frag_direct(fb, s_v, G::LDV, 16 * J + i16, 32 * kn);
+            mma(xd, fa, fb);
+          }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int i = 16 * I + 4 * g + rr, j = 16 * J + i16;
+          float va = 0.f, vd = 0.f, pp = 0.f;
+          if (seg.same(i, j)) {
+            va = xa[rr];
+            vd = xd[rr];
+            if constexpr (SCAL) {
+              const float dec = __expf(s_gam[i] - s_gam[j]);
+              pp = va * vd * dec;      // one decay factor: exp(Gam_i - Gam_j) (q_i.k_j)(dO_i.v_j)
+              va *= dec;
+              vd *= dec;
+            }
+          }
+          store_split(s_ah, s_al, i * G::LDA + j, va);
+          store_split(s_dah, s_dal, i * G::LDA + j, vd);
+          if constexpr (SCAL) s_p[i * (CH + 1) + j] = pp;
+        }
+      }
+      __syncthreads();
+
+      // ---- dv^T tiles: rows = owned d_v tiles, columns = tokens j ---------------------
+      E* dvp = reinterpret_cast<E*>(a.dv);
+#pragma unroll
+      for (int cc = 0; cc < G::CPWV; ++cc) {
+        const int cn = w + NWAVE * cc;
+        if (cn >= G::NVT) continue;
+        Frag<E> fs[G::DKP / 32], fsl[G::DKP / 32];
+#pragma unroll
+        for (int kb = 0; kb < G::DKP / 32; ++kb) {
+          f32x4 lo = dS[2 * kb][cc], hi = dS[2 * kb + 1][cc];
+          if constexpr (DIAG) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int d0 = 32 * kb + 4 * g + rr, d1 = d0 + 16;
+              lo[rr] *= d0 < DK ? __expf(s_glast[d0]) : 0.f;
+              hi[rr] *= d1 < DK ? __expf(s_glast[d1]) : 0.f;
+            }
+          }
+          acc_to_frag_split(fs[kb], fsl[kb], lo, hi);
+        }
+        Frag<E> fdo[2];
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) frag_tr(fdo[ib], s_do, G::LDV, 32 * ib, 16 * cn);
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          const int tj = 16 * J + i16;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < G::DKP / 32; ++kb) {
+            Frag<E> fb, fbl;
+            frag_direct_perm(fb, s_k, G::LDK, tj, 32 * kb);
+            if constexpr (DIAG && SP) {
+              frag_direct_perm(fbl, s_kl, G::LDK, tj, 32 * kb);
+              mma3(acc, fs[kb], fsl[kb], fb, fbl);
+            } else {
+              mma2a(acc, fs[kb], fsl[kb], fb);
+            }
+          }
+          acc *= s_fk[tj];
+#pragma unroll
+          for (int ib = 0; ib < 2; ++ib) {
+            if (ib == 0 && J >= 2) continue;
+            Frag<E> fb, fbl;
+            frag_tr(fb, s_ah, G::LDA, 32 * ib, 16 * J);
+            if constexpr (SP) frag_tr(fbl, s_al, G::LDA, 32 * ib, 16 * J);
+            mma2b(acc, fdo[ib], fb, fbl);
+          }
+          const int n0 = 16 * cn + 4 * g;
+          if (n0 < DV) store4(dvp + tok_off(b, t0 + tj, h, a.T, a.H, DV) + n0, acc);
+        }
+      }
+
+      // ---- dq^T and dk^T tiles: rows = owned d_k tiles, columns = tokens ---------------
+      E* dqp = reinterpret_cast<E*>(a.dq);
+      E* dkp = reinterpret_cast<E*>(a.dk);
+      const float* cs = a.chunk_states + ((bh * nct + t0 / CH) * DK) * (int64_t)DV;
+      float u1p[4] = {0.f, 0.f, 0.f, 0.f}, u4p[4] = {0.f, 0.f, 0.f, 0.f};  // scalar: per-I token partials
+      float t3p = 0.f;                                                      // scalar: T3 partial
+      f32x4 wv[G::CPWK][4], zv[G::CPWK][4];                                 // diagonal: dg parts
+#pragma unroll
+      for (int cc = 0; cc < G::CPWK; ++cc) {
+        const int cm = w + NWAVE * cc;
+        if (cm >= G::NKT) continue;
+        const int dl = 16 * cm + i16;        // lane-fixed key dim of the S0 / dS^T fragments
+        // S0 and dS^T fragments over d_v in the permuted order {32kn + 4g + e, 32kn + 16 + 4g + e}
+        Frag<E> fs0[G::DVP / 32], fs0l[G::DVP / 32], fdt[G::DVP / 32], fdtl[G::DVP / 32];
+        float t3 = 0.f;
+        const float eL = (DIAG && dl < DK) ? __expf(s_glast[dl]) : 1.f;
+#pragma unroll
+        for (int kn = 0; kn < G::DVP / 32; ++kn) {
+          float x[8], y[8];
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int n0 = 32 * kn + 16 * hh + 4 * g;
+            f32x4 sv = {0.f, 0.f, 0.f, 0.f};
+            if (dl < DK && n0 < DV) sv = *reinterpret_cast<const f32x4*>(cs + dl * DV + n0);
+            const f32x4 tv = dT[2 * kn + hh][cc];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              x[4 * hh + e] = sv[e];
+              y[4 * hh + e] = tv[e] * eL;
+              t3 += sv[e] * tv[e];
+            }
+          }
+          split_frag(fs0[kn], fs0l[kn], x);
+          split_frag(fdt[kn], fdtl[kn], y);
+        }
+        if constexpr (HAS_DG) {
+          t3 += __shfl_xor(t3, 16, 64);
+          t3 += __shfl_xor(t3, 32, 64);
+          if constexpr (DIAG) {
+            if (g == 0) s_t3[dl] = t3 * eL;
+          } else {
+            if (g == 0) t3p += t3;
+          }
+        }
+        Frag<E> fkt[2], fktl[2], fqt[2], fqtl[2];
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          frag_tr(fkt[jb], s_k, G::LDK, 32 * jb, 16 * cm);
+          frag_tr(fqt[jb], s_q, G::LDK, 32 * jb, 16 * cm);
+          if constexpr (DIAG && SP) {
+            frag_tr(fktl[jb], s_kl, G::LDK, 32 * jb, 16 * cm);
+            frag_tr(fqtl[jb], s_ql, G::LDK, 32 * jb, 16 * cm);
+          }
+        }
+        // dq^T
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          const int ti = 16 * I + i16;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kn = 0; kn < G::DVP / 32; ++kn) {
+            Frag<E> fb;
+            frag_direct_perm(fb, s_do, G::LDV, ti, 32 * kn);
+            mma2a(acc, fs0[kn], fs0l[kn], fb);
+          }
+          if constexpr (SCAL) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) u1p[I] += to_f(s_q[ti * G::LDK + 16 * cm + 4 * g + rr]) * acc[rr];
+          }
+          acc *= s_fq[ti];
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb) {
+            if (jb == 1 && I < 2) continue;
+            Frag<E> fb, fbl;
+            frag_direct(fb, s_dah, G::LDA, ti, 32 * jb);
+            if constexpr (SP) frag_direct(fbl, s_dal, G::LDA, ti, 32 * jb);
+            if constexpr (DIAG && SP) mma3(acc, fkt[jb], fktl[jb], fb, fbl);
+            else mma2b(acc, fkt[jb], fb, fbl);
+          }
+          const int d0 = 16 * cm + 4 * g;
+          if constexpr (DIAG) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int d = d0 + rr;
+              const bool ok = d < DK;
+              float qt = to_f(s_q[ti * G::LDK + d]);
+              if constexpr (SP) qt += to_f(s_ql[ti * G::LDK + d]);
+              wv[cc][I][rr] = ok ? qt * acc[rr] : 0.f;
+              acc[rr] *= ok ? __expf(gq[cc][I][rr]) : 0.f;
+            }
+          }
+          if (d0 < DK) store4(dqp + tok_off(b, t0 + ti, h, a.T, a.H, DK) + d0, acc);
+        }
+        // dk^T
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+          const int tj = 16 * J + i16;
+          f32x4 ay = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kn = 0; kn < G::DVP / 32; ++kn) {
+            Frag<E> fb;
+            frag_direct_perm(fb, s_v, G::LDV, tj, 32 * kn);
+            mma2a(ay, fdt[kn], fdtl[kn], fb);
+          }
+          ay *= s_fk[tj];
+          if constexpr (SCAL) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) u4p[J] += to_f(s_k[tj * G::LDK + 16 * cm + 4 * g + rr]) * ay[rr];
+          }
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ib = 0; ib < 2; ++ib) {
+            if (ib == 0 && J >= 2) continue;
+            Frag<E> fb, fbl;
+            frag_tr(fb, s_dah, G::LDA, 32 * ib, 16 * J);
+            if constexpr (SP) frag_tr(fbl, s_dal, G::LDA, 32 * ib, 16 * J);
+            if constexpr (DIAG && SP) mma3(acc, fqt[ib], fqtl[ib], fb, fbl);
+            else mma2b(acc, fqt[ib], fb, fbl);
+          }
+          const int d0 = 16 * cm + 4 * g;
+          if constexpr (DIAG) {
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int d = d0 + rr;
+              const bool ok = d < DK;
+              float kt = ok ? to_f(s_k[tj * G::LDK + d]) : 0.f;
+              if constexpr (SP) kt += ok ? to_f(s_kl[tj * G::LDK + d]) : 0.f;
+              wv[cc][J][rr] -= kt * acc[rr];
+              zv[cc][J][rr] = kt * ay[rr];
+              acc[rr] = ok ? (acc[rr] + ay[rr]) * __expf(-gq[cc][J][rr]) : 0.f;
+            }
+          } else {
+            acc += ay;
+          }
+          if (d0 < DK) store4(dkp + tok_off(b, t0 + tj, h, a.T, a.H, DK) + d0, acc);
+        }
+      }
+
+      if constexpr (DIAG) {
+        __syncthreads();  // s_t3 complete
+#pragma unroll
+        for (int cc = 0; cc < G::CPWK; ++cc) {
+          const int cm = w + NWAVE * cc;
+          if (cm >= G::NKT) continue;
+          const int d0 = 16 * cm + 4 * g;
+          f32x4 t3v;
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) t3v[rr] = (d0 + rr < DK) ? keep * s_t3[d0 + rr] : 0.f;
+          // suffix sums of wv and exclusive prefix sums of zv over the 64 tokens (I, i16)
+          f32x4 suf_tot = {0.f, 0.f, 0.f, 0.f}, pre_tot = {0.f, 0.f, 0.f, 0.f};
+          f32x4 sufI[4], preI[4];
+#pragma unroll
+          for (int I = 3; I >= 0; --I) {
+            f32x4 x = wv[cc][I];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const float y = __shfl_down(x[rr], off, 16);
+                if (i16 + off < 16) x[rr] += y;
+              }
+            }
+            sufI[I] = x + suf_tot;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) suf_tot[rr] += __shfl(x[rr], 0, 16);
+          }
+#pragma unroll
+          for (int I = 0; I < 4; ++I) {
+            f32x4 x = zv[cc][I];
+            const f32x4 own = x;
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const float y = __shfl_up(x[rr], off, 16);
+                if (i16 >= off) x[rr] += y;
+              }
+            }
+            preI[I] = x - own + pre_tot;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) pre_tot[rr] += __shfl(x[rr], 15, 16);
+          }
+          if (d0 < DK) {
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+              const int t = 16 * I + i16;
+              f32x4 dgv = sufI[I] + preI[I] + t3v;
+              if ((seg.starts >> t) & 1ull) dgv = f32x4{0.f, 0.f, 0.f, 0.f};
+              store4(a.dg + tok_off(b, t0 + t, h, a.T, a.H, DK) + d0, dgv);
+            }
+          }
+        }
+      }
+
+      if constexpr (SCAL) {
+        // token partials: reduce over the lane groups, then across waves
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          float x1 = u1p[I], x4 = u4p[I];
+          x1 += __shfl_xor(x1, 16, 64);
+          x1 += __shfl_xor(x1, 32, 64);
+          x4 += __shfl_xor(x4, 16, 64);
+          x4 += __shfl_xor(x4, 32, 64);
+          if (g == 0) {
+            s_u1[w * CH + 16 * I + i16] = x1;
+            s_u4[w * CH + 16 * I + i16] = x4;
+          }
+        }
+        t3p = wave_sum(g == 0 ? t3p : 0.f);
+        if (l == 0) s_red[w] = t3p;
+        __syncthreads();
+        if (w == 0) {
+          const int t = l;
+          float u1 = 0.f, u4 = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < NWAVE; ++ww) {
+            u1 += s_u1[ww * CH + t];
+            u4 += s_u4[ww * CH + t];
+          }
+          u1 *= s_fq[t];
+          // T2 step: row t left of the diagonal minus column t below it
+          float rowl = 0.f, colb = 0.f;
+          for (int j = 0; j < t; ++j) rowl += s_p[t * (CH + 1) + j];
+          for (int i = t + 1; i < CH; ++i) colb += s_p[i * (CH + 1) + t];
+          float x = u1 + rowl - colb;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_down(x, off, 64);
+            if (t + off < 64) x += y;
+          }
+          float y4 = u4;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(y4, off, 64);
+            if (t >= off) y4 += y;
+          }
+          y4 -= u4;
+          const float t3 = keep * __expf(s_gam[CH - 1]) * (s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+          float dgv = x + y4 + t3;
+          if ((seg.starts >> t) & 1ull) dgv = 0.f;
+          a.dg[(b * a.T + t0 + t) * a.H + h] = dgv;
+        }
+      }
+    }
+
+    // ---- dS <- [no start] diag(exp(Gam_last)) dS + sum_i live_i Q^_i dO_i^T ----------
+    // (and the same for dS^T)
+    {
+#pragma unroll
+      for (int m = 0; m < G::NKT; ++m)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d = 16 * m + 4 * g + rr;
+          float f = keep;
+          if constexpr (DIAG) f = d < DK ? keep * __expf(s_glast[d]) : 0.f;
+          if constexpr (SCAL) f = keep * __expf(s_gam[CH - 1]);
+#pragma unroll
+          for (int cc = 0; cc < G::CPWV; ++cc) dS[m][cc][rr] *= f;
+        }
+      if constexpr (APPLY) {
+#pragma unroll
+        for (int cc = 0; cc < G::CPWK; ++cc) {
+          const int d = 16 * (w + NWAVE * cc) + i16;
+          float f = keep;
+          if constexpr (DIAG) f = d < DK ? keep * __expf(s_glast[d]) : 0.f;
+          if constexpr (SCAL) f = keep * __expf(s_gam[CH - 1]);
+#pragma unroll
+          for (int nt = 0; nt < G::NVT; ++nt) dT[nt][cc] *= f;
+        }
+      }
+      // token mask for Q^ where it is not baked into a tile (diagonal / no decay, packed chunks)
+      const bool mask_tok = !SCAL && seg.any();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        Frag<E> fdo[G::CPWV];
+#pragma unroll
+        for (int cc = 0; cc < G::CPWV; ++cc) {
+          const int cn = w + NWAVE * cc;
+          if (cn < G::NVT) frag_tr(fdo[cc], s_do, G::LDV, 32 * kb, 16 * cn);
+        }
+        Frag<E> fdoa[APPLY ? G::NVT : 1];
+        if constexpr (APPLY) {
+#pragma unroll
+          for (int nt = 0; nt < G::NVT; ++nt) frag_tr(fdoa[nt], s_do, G::LDV, 32 * kb, 16 * nt);
+        }
+#pragma unroll
+        for (int m = 0; m < G::NKT; ++m) {
+          Frag<E> fa, fal;
+          frag_tr(fa, qhat_h, G::LDK, 32 * kb, 16 * m);
+          if constexpr (SP && (DIAG || SCAL)) frag_tr(fal, qhat_l, G::LDK, 32 * kb, 16 * m);
+          else frag_zero(fal);
+          if (mask_tok) {
+            frag_scale_tokens(fa, s_fq, 32 * kb, false);
+            frag_scale_tokens(fal, s_fq, 32 * kb, false);
+          }
+#pragma unroll
+          for (int cc = 0; cc < G::CPWV; ++cc)
+            if (w + NWAVE * cc < G::NVT) {
+              if constexpr (SP && (DIAG || SCAL)) mma2a(dS[m][cc], fa, fal, fdo[cc]);
+              else mma(dS[m][cc], fa, fdo[cc]);
+            }
+          if constexpr (APPLY) {
+            // dS^T columns owned by this wave: d tile m == w + 4 cc
+#pragma unroll
+            for (int cc = 0; cc < G::CPWK; ++cc)
+              if (m == w + NWAVE * cc) {
+#pragma unroll
+                for (int nt = 0; nt < G::NVT; ++nt) {
+                  if constexpr (SP && (DIAG || SCAL)) mma2b(dT[nt][cc], fdoa[nt], fa, fal);
+                  else mma(dT[nt][cc], fdoa[nt], fa);
+                }
+              }
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if constexpr (!APPLY) {
+    float* rec = a.summary + (int64_t)(r * a.B * a.H + bh) * a.W;
+    const float keep = any_start ? 0.f : 1.f;
+    if constexpr (DIAG) {
+      if (threadIdx.x < DK) rec[threadIdx.x] = keep * __expf(gsum);
+    } else {
+      if (threadIdx.x < 4) {
+        float mval = SCAL ? __expf(gsum) : 1.f;
+        rec[threadIdx.x] = threadIdx.x == 0 ? keep * mval : 0.f;
+      }
+    }
+    float* gm = rec + a.m_slot;
+#pragma unroll
+    for (int m = 0; m < G::NKT; ++m)
+#pragma unroll
+      for (int cc = 0; cc < G::CPWV; ++cc) {
+        const int cn = w + NWAVE * cc;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d = 16 * m + 4 * g + rr, n = 16 * cn + i16;
+          if (cn < G::NVT && d < DK && n < DV) gm[d * DV + n] = dS[m][cc][rr];
+        }
+      }
+  }
+}
+
+#define CPLA_INST_BWD(E, D, DEC)                                                   \
+  template __global__ void bwd_walk<E, D, D, DEC, false>(BwdArgs);                \
+  template __global__ void bwd_walk<E, D, D, DEC, true>(BwdArgs);
+#define CPLA_INST_BWD3(E, D) CPLA_INST_BWD(E, D, 0) CPLA_INST_BWD(E, D, 1) CPLA_INST_BWD(E, D, 2)
+CPLA_INST_BWD3(bf16_t, 16)
+CPLA_INST_BWD3(bf16_t, 64)
+CPLA_INST_BWD3(bf16_t, 128)
+CPLA_INST_BWD3(float, 16)
+CPLA_INST_BWD3(float, 64)
+
+}  // namespace cpla

@@ -1,0 +1,239 @@
+// Device primitives for the chunkwise linear-attention kernels (gfx950 only).
+//
+// MFMA: v_mfma_f32_16x16x32_bf16 (bf16 operands) and v_mfma_f32_16x16x4_f32
+// (fp32 operands, eight issues per 32-deep step). A "fragment" is the 8 values a
+// lane contributes to one 16x16x32 step: lane l holds operand row/column l%16
+// and the 8 contraction indices {8g + e} (g = l/16), or a permuted set when the
+// fragment is rebuilt from accumulators (see acc_to_frag). The fp32 form splits
+// the same 8 indices over eight 16x16x4 issues, so both element types share
+// every layout below.
+//
+// LDS tiles are token-major (as the inputs sit in HBM) with 16 bytes of padding
+// per row. Contractions over features read fragments directly; contractions over
+// tokens read them with the gfx950 transpose load ds_read_b64_tr_b16, where lane
+// c = 4r + s of each 16-lane group names row r / columns 4s..4s+3 of a 4x16
+// block and lane i receives column i.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpla {
+
+typedef __bf16 bf16_t;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 64;      // chunk length (tokens)
+constexpr int NWAVE = 4;    // waves per workgroup
+constexpr int NTHR = 256;   // threads per workgroup
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+// ---- element traits -------------------------------------------------------------
+
+template <typename E> struct Frag;
+template <> struct Frag<bf16_t> { bf16x8 v; };
+template <> struct Frag<float> { float v[8]; };
+
+template <typename E> __device__ __forceinline__ E to_e(float x);
+template <> __device__ __forceinline__ bf16_t to_e<bf16_t>(float x) { return (bf16_t)x; }
+template <> __device__ __forceinline__ float to_e<float>(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16_t x) { return (float)x; }
+__device__ __forceinline__ float to_f(float x) { return x; }
+
+template <typename E> constexpr int lds_pad() { return 16 / (int)sizeof(E); }
+
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], acc, 0, 0, 0);
+}
+
+template <typename E> __device__ __forceinline__ void frag_zero(Frag<E>& f) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = to_e<E>(0.f);
+}
+template <typename E> __device__ __forceinline__ float frag_get(const Frag<E>& f, int e) { return to_f(f.v[e]); }
+template <typename E> __device__ __forceinline__ void frag_set(Frag<E>& f, int e, float x) { f.v[e] = to_e<E>(x); }
+
+// ---- fragment loads from LDS tiles ----------------------------------------------
+// Tile: row-major, `ld` elements per row. All offsets in elements.
+
+// lane-fixed row `row`, contraction indices k0 + 8g + e (16 contiguous bytes for bf16)
+__device__ __forceinline__ void frag_direct(Frag<bf16_t>& f, const bf16_t* t, int ld, int row, int k0) {
+  const int g = lane_id() >> 4;
+  f.v = *reinterpret_cast<const bf16x8*>(t + row * ld + k0 + 8 * g);
+}
+__device__ __forceinline__ void frag_direct(Frag<float>& f, const float* t, int ld, int row, int k0) {
+  const int g = lane_id() >> 4;
+  const f32x4* p = reinterpret_cast<const f32x4*>(t + row * ld + k0 + 8 * g);
+  f32x4 a = p[0], b = p[1];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
+}
+// lane-fixed row, permuted contraction indices {k0 + 4g + e, k0 + 16 + 4g + e}
+__device__ __forceinline__ void frag_direct_perm(Frag<bf16_t>& f, const bf16_t* t, int ld, int row, int k0) {
+  const int g = lane_id() >> 4;
+  bf16x4 a = *reinterpret_cast<const bf16x4*>(t + row * ld + k0 + 4 * g);
+  bf16x4 b = *reinterpret_cast<const bf16x4*>(t + row * ld + k0 + 16 + 4 * g);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
+}
+__device__ __forceinline__ void frag_direct_perm(Frag<float>& f, const float* t, int ld, int row, int k0) {
+  const int g = lane_id() >> 4;
+  f32x4 a = *reinterpret_cast<const f32x4*>(t + row * ld + k0 + 4 * g);
+  f32x4 b = *reinterpret_cast<const f32x4*>(t + row * ld + k0 + 16 + 4 * g);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
+}
+
+// lane-fixed column col0 + l%16, contraction over rows k0 + 8g + e (transpose load)
+__device__ __forceinline__ s16x4 ds_tr16(const bf16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+}
+__device__ __forceinline__ void frag_tr(Frag<bf16_t>& f, const bf16_t* t, int ld, int k0, int col0) {
+  const int l = lane_id(), g = l >> 4, i = l & 15;
+  s16x4 a = ds_tr16(t + (k0 + 8 * g + (i >> 2)) * ld + col0 + 4 * (i & 3));
+  s16x4 b = ds_tr16(t + (k0 + 8 * g + 4 + (i >> 2)) * ld + col0 + 4 * (i & 3));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 c;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { c[e] = a[e]; c[4 + e] = b[e]; }
+  f.v = __builtin_bit_cast(bf16x8, c);
+}
+__device__ __forceinline__ void frag_tr(Frag<float>& f, const float* t, int ld, int k0, int col0) {
+  const int l = lane_id(), g = l >> 4, i = l & 15;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f.v[e] = t[(k0 + 8 * g + e) * ld + col0 + i];
+}
+// permuted rows {k0 + 4g + e, k0 + 16 + 4g + e}
+__device__ __forceinline__ void frag_tr_perm(Frag<bf16_t>& f, const bf16_t* t, int ld, int k0, int col0) {
+  const int l = lane_id(), g = l >> 4, i = l & 15;
+  s16x4 a = ds_tr16(t + (k0 + 4 * g + (i >> 2)) * ld + col0 + 4 * (i & 3));
+  s16x4 b = ds_tr16(t + (k0 + 16 + 4 * g + (i >> 2)) * ld + col0 + 4 * (i & 3));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  s16x8 c;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { c[e] = a[e]; c[4 + e] = b[e]; }
+  f.v = __builtin_bit_cast(bf16x8, c);
+}
+__device__ __forceinline__ void frag_tr_perm(Frag<float>& f, const float* t, int ld, int k0, int col0) {
+  const int l = lane_id(), g = l >> 4, i = l & 15;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    f.v[e] = t[(k0 + 4 * g + e) * ld + col0 + i];
+    f.v[4 + e] = t[(k0 + 16 + 4 * g + e) * ld + col0 + i];
+  }
+}
+// contraction index of fragment slot e for the plain and the permuted orders
+__device__ __forceinline__ int kidx(int e) { return 8 * (lane_id() >> 4) + e; }
+__device__ __forceinline__ int kidx_perm(int e) { return 4 * (lane_id() >> 4) + (e & 3) + ((e >> 2) << 4); }
+
+// Two 16x16 accumulator tiles stacked along their row index (rows r0..r0+31,
+// lane-fixed column) as one operand fragment contracting over those rows, in the
+// permuted order {r0 + 4g + e, r0 + 16 + 4g + e}. `s0`, `s1` scale rows.
+template <typename E>
+__device__ __forceinline__ void acc_to_frag(Frag<E>& f, const f32x4& lo, const f32x4& hi) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { f.v[e] = to_e<E>(lo[e]); f.v[4 + e] = to_e<E>(hi[e]); }
+}
+
+// ---- split bf16 arithmetic ---------------------------------------------------------
+// An fp32 intermediate x feeds bf16 MFMAs as hi = bf16(x), lo = bf16(x - hi); a
+// product then takes hi*b + lo*b (and + hi*b_lo when the other operand is split
+// too), which keeps its error near fp32 rounding instead of bf16 rounding. The
+// kernel inputs themselves are exact in bf16 and need no split. With fp32
+// operands the lo parts are zero and their MFMAs are skipped.
+template <typename E> struct Split { static constexpr bool on = sizeof(E) == 2; };
+
+template <typename E>
+__device__ __forceinline__ void split_frag(Frag<E>& hi, Frag<E>& lo, const float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    hi.v[e] = to_e<E>(x[e]);
+    if constexpr (Split<E>::on) lo.v[e] = to_e<E>(x[e] - to_f(hi.v[e]));
+  }
+}
+// acc += (a_hi + a_lo) (b_hi + b_lo), dropping lo*lo
+template <typename E>
+__device__ __forceinline__ void mma3(f32x4& acc, const Frag<E>& ah, const Frag<E>& al, const Frag<E>& bh,
+                                     const Frag<E>& bl) {
+  mma(acc, ah, bh);
+  if constexpr (Split<E>::on) {
+    mma(acc, ah, bl);
+    mma(acc, al, bh);
+  }
+}
+// acc += (a_hi + a_lo) b
+template <typename E>
+__device__ __forceinline__ void mma2a(f32x4& acc, const Frag<E>& ah, const Frag<E>& al, const Frag<E>& b) {
+  mma(acc, ah, b);
+  if constexpr (Split<E>::on) mma(acc, al, b);
+}
+// acc += a (b_hi + b_lo)
+template <typename E>
+__device__ __forceinline__ void mma2b(f32x4& acc, const Frag<E>& a, const Frag<E>& bh, const Frag<E>& bl) {
+  mma(acc, a, bh);
+  if constexpr (Split<E>::on) mma(acc, a, bl);
+}
+// Two accumulator tiles (see acc_to_frag) as split hi/lo fragments.
+template <typename E>
+__device__ __forceinline__ void acc_to_frag_split(Frag<E>& hi, Frag<E>& lo, const f32x4& a, const f32x4& b) {
+  float x[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+  split_frag(hi, lo, x);
+}
+// Store x as hi (and lo) into two LDS tiles at the same offset.
+template <typename E>
+__device__ __forceinline__ void store_split(E* hi, E* lo, int off, float x) {
+  const E h = to_e<E>(x);
+  hi[off] = h;
+  if constexpr (Split<E>::on) lo[off] = to_e<E>(x - to_f(h));
+}
+
+// ---- per-chunk token structure ---------------------------------------------------
+// Bit i of `starts` is set when chunk token i starts a packed sequence.
+struct ChunkSeg {
+  uint64_t starts;
+  __device__ __forceinline__ bool any() const { return starts != 0ull; }
+  // first start position (64 if none): tokens before it still see the incoming state
+  __device__ __forceinline__ int first() const { return starts ? __builtin_ctzll(starts) : CH; }
+  // last start position (0 if none): tokens from it on reach the outgoing state
+  __device__ __forceinline__ int last() const { return starts ? 63 - __builtin_clzll(starts) : 0; }
+  __device__ __forceinline__ bool live(int i) const { return i < first(); }
+  __device__ __forceinline__ bool tail(int i) const { return i >= last(); }
+  // i >= j and no start in (j, i]
+  __device__ __forceinline__ bool same(int i, int j) const {
+    if (i < j) return false;
+    if (!starts) return true;
+    uint64_t hi = (i >= 63) ? ~0ull : ((2ull << i) - 1ull);
+    uint64_t lo = (2ull << j) - 1ull;
+    return (starts & (hi & ~lo)) == 0ull;
+  }
+};
+
+// Every wave computes the same mask from the global sequence ids (uniform).
+__device__ __forceinline__ ChunkSeg chunk_seg(const int32_t* seq_idx, int64_t t0) {
+  ChunkSeg s;
+  if (!seq_idx) { s.starts = 0ull; return s; }
+  const int i = lane_id();
+  const int64_t t = t0 + i;
+  bool st = (t == 0) ? true : (seq_idx[t] != seq_idx[t - 1]);
+  s.starts = __ballot(st);
+  return s;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+}  // namespace cpla

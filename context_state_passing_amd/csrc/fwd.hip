@@ -1,0 +1,258 @@
+// Forward shard walks: cp_forward_prepare (APPLY = false) and the local part of
+// cp_forward_apply (APPLY = true).
+//
+// One workgroup walks one (shard, b, h): 64-token chunks in order, carrying the
+// d_k x d_v fp32 state in MFMA accumulators. Wave w owns the state's d_v tiles
+// w, w+4, ... (all d_k rows), so the state never leaves registers.
+//
+// Per chunk (see chunk_common.hpp for Gam, live, tail):
+//   scores  A_ij = [same sequence, i >= j] * sum_d Q*_i[d] K*_j[d] (* exp(Gam_i - Gam_j)
+//           for a scalar decay), Q* / K* = exp(+-Gam)-scaled tiles for a diagonal decay;
+//   output  o_i = sum_j A_ij v_j + live_i * S0^T (q_i * exp(Gam_i))          (APPLY)
+//   state   S  = diag(exp(Gam_last)) [no start] S0 + sum_{j tail} diag(exp(Gam_last - Gam_j)) k_j v_j^T
+// which is the chunk algebra of S_t = diag(a_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t.
+#include "chunk_common.hpp"
+#include "kernels.hpp"
+
+namespace cpla {
+
+// S <- diag(exp(Gam_last)) keep*S + K^T V with the tail/decay token factors.
+template <typename E, int DK, int DV, int DECAY, int NKT_, int CPWV_>
+__device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* Kt, const E* Vt,
+                                             const float* gam, const float* fk, const ChunkSeg& seg) {
+  using G = Geo<E, DK, DV>;
+  const int w = wave_id(), l = lane_id(), g = l >> 4;
+  const float keep = seg.any() ? 0.f : 1.f;
+  if constexpr (DECAY == DECAY_SCALAR) {
+    const float sc = keep * __expf(gam[CH - 1]);
+#pragma unroll
+    for (int m = 0; m < G::NKT; ++m)
+#pragma unroll
+      for (int cc = 0; cc < G::CPWV; ++cc) S[m][cc] *= sc;
+  } else {
+#pragma unroll
+    for (int m = 0; m < G::NKT; ++m)
+#pragma unroll
+      for (int cc = 0; cc < G::CPWV; ++cc) S[m][cc] *= keep;
+  }
+  Frag<E> bv[2][G::CPWV];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int cc = 0; cc < G::CPWV; ++cc) {
+      const int c = w + NWAVE * cc;
+      if (c < G::NVT) frag_tr(bv[kb][cc], Vt, G::LDV, 32 * kb, 16 * c);
+    }
+  const bool scale_tok = (DECAY == DECAY_SCALAR) || seg.any();
+#pragma unroll
+  for (int m = 0; m < G::NKT; ++m) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      Frag<E> a;
+      frag_tr(a, Kt, G::LDK, 32 * kb, 16 * m);
+      if (scale_tok) frag_scale_tokens(a, fk, 32 * kb, false);
+#pragma unroll
+      for (int cc = 0; cc < G::CPWV; ++cc)
+        if (w + NWAVE * cc < G::NVT) mma(S[m][cc], a, bv[kb][cc]);
+    }
+  }
+  if constexpr (DECAY == DECAY_DIAG) {
+    // K* = K exp(-Gam): restore exp(Gam_last - Gam_j) with a row factor exp(Gam_last[d])
+#pragma unroll
+    for (int m = 0; m < G::NKT; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = 16 * m + 4 * g + r;
+        const float f = d < DK ? __expf(gam[(CH - 1) * DK + d]) : 0.f;
+#pragma unroll
+        for (int cc = 0; cc < G::CPWV; ++cc) S[m][cc][r] *= f;
+      }
+  }
+}
+
+template <typename E, int DK, int DV, int DECAY, bool APPLY>
+__global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
+  using G = Geo<E, DK, DV>;
+  constexpr int GAM = (DECAY == DECAY_DIAG) ? CH * DK : CH;
+  constexpr int NQT = APPLY ? 1 : 0;
+  __shared__ __attribute__((aligned(16))) E s_q[NQT * G::TILE_K + 8];
+  __shared__ __attribute__((aligned(16))) E s_k[G::TILE_K];
+  __shared__ __attribute__((aligned(16))) E s_v[G::TILE_V];
+  constexpr int NAL = (APPLY && Split<E>::on) ? 1 : 0;
+  __shared__ __attribute__((aligned(16))) E s_a[NQT * G::TILE_A + 8];    // scores, hi part
+  __shared__ __attribute__((aligned(16))) E s_al[NAL * G::TILE_A + 8];   // scores, lo part
+  __shared__ float s_gam[GAM], s_fq[CH], s_fk[CH], s_red[NTHR];
+
+  const int w = wave_id(), l = lane_id(), g = l >> 4, i16 = l & 15;
+  const int r = a.rank_begin + blockIdx.x;
+  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t L = a.T / a.P, tshard = r * L;
+  const int nc = (int)(L / CH);
+
+  f32x4 S[G::NKT][G::CPWV];
+#pragma unroll
+  for (int m = 0; m < G::NKT; ++m)
+#pragma unroll
+    for (int cc = 0; cc < G::CPWV; ++cc) {
+      const int c = w + NWAVE * cc;
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        float x = 0.f;
+        if constexpr (APPLY) {
+          const int d = 16 * m + 4 * g + rr, n = 16 * c + i16;
+          if (c < G::NVT && d < DK && n < DV)
+            x = a.state_in[((int64_t)(r * a.B * a.H + bh) * DK + d) * DV + n];
+        }
+        S[m][cc][rr] = x;
+      }
+    }
+
+  const E* q = reinterpret_cast<const E*>(a.q);
+  const E* k = reinterpret_cast<const E*>(a.k);
+  const E* v = reinterpret_cast<const E*>(a.v);
+  float gsum = 0.f;          // total log-decay of the shard (diag: column tid; else thread 0)
+  bool any_start = false;
+
+  for (int c = 0; c < nc; ++c) {
+    const int64_t t0 = tshard + (int64_t)c * CH;
+    const ChunkSeg seg = chunk_seg(a.seq_idx, t0);
+    any_start |= seg.any();
+    stage_gamma<DK, DECAY>(a.g, b, h, t0, a.T, a.H, seg, s_gam, s_fq, s_fk, s_red);
+    if constexpr (DECAY == DECAY_DIAG) {
+      if (threadIdx.x < DK) gsum += s_gam[(CH - 1) * DK + threadIdx.x];
+      stage_tile<E, DK, G::DKP, G::LDK, 2, DK>(k, b, h, t0, a.T, a.H, s_k, s_gam);
+      if constexpr (APPLY) stage_tile<E, DK, G::DKP, G::LDK, 1, DK>(q, b, h, t0, a.T, a.H, s_q, s_gam);
+    } else {
+      if constexpr (DECAY == DECAY_SCALAR)
+        if (threadIdx.x == 0) gsum += s_gam[CH - 1];
+      stage_tile<E, DK, G::DKP, G::LDK, 0, DK>(k, b, h, t0, a.T, a.H, s_k, s_gam);
+      if constexpr (APPLY) stage_tile<E, DK, G::DKP, G::LDK, 0, DK>(q, b, h, t0, a.T, a.H, s_q, s_gam);
+    }
+    stage_tile<E, DV, G::DVP, G::LDV, 0, DK>(v, b, h, t0, a.T, a.H, s_v, s_gam);
+
+    if constexpr (APPLY) {
+      if (a.chunk_states) {
+        float* cs = a.chunk_states + ((bh * (a.T / CH) + t0 / CH) * DK) * (int64_t)DV;
+#pragma unroll
+        for (int m = 0; m < G::NKT; ++m)
+#pragma unroll
+          for (int cc = 0; cc < G::CPWV; ++cc) {
+            const int cn = w + NWAVE * cc;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int d = 16 * m + 4 * g + rr, n = 16 * cn + i16;
+              if (cn < G::NVT && d < DK && n < DV) cs[d * DV + n] = S[m][cc][rr];
+            }
+          }
+      }
+    }
+    __syncthreads();
+
+    if constexpr (APPLY) {
+      // ---- scores -> s_a (E), masked and decayed --------------------------------
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+        const int idx = score_tile(w, s);
+        const int I = idx >> 2, J = idx & 3;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (!score_tile_zero(idx)) {
+#pragma unroll
+          for (int kd = 0; kd < G::DKP / 32; ++kd) {
+            Frag<E> fa, fb;
+            frag_direct(fa, s_q, G::LDK, 16 * I + i16, 32 * kd);
+            frag_direct(fb, s_k, G::LDK, 16 * J + i16, 32 * kd);
+            mma(acc, fa, fb);
+          }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int i = 16 * I + 4 * g + rr, j = 16 * J + i16;
+          float x = 0.f;
+          if (seg.same(i, j)) {
+            x = acc[rr];
+            if constexpr (DECAY == DECAY_SCALAR) x *= __expf(s_gam[i] - s_gam[j]);
+          }
+          store_split(s_a, s_al, i * G::LDA + j, x);
+        }
+      }
+      __syncthreads();
+
+      // ---- o^T tiles: rows = d_v (owned tiles), columns = tokens ----------------
+      E* o = reinterpret_cast<E*>(a.out);
+#pragma unroll
+      for (int cc = 0; cc < G::CPWV; ++cc) {
+        const int cn = w + NWAVE * cc;
+        if (cn >= G::NVT) continue;
+        Frag<E> fs[G::DKP / 32], fsl[G::DKP / 32];
+#pragma unroll
+        for (int kb = 0; kb < G::DKP / 32; ++kb)
+          acc_to_frag_split(fs[kb], fsl[kb], S[2 * kb][cc], S[2 * kb + 1][cc]);
+        Frag<E> fvt[2];
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) frag_tr(fvt[jb], s_v, G::LDV, 32 * jb, 16 * cn);
+#pragma unroll
+        for (int I = 0; I < 4; ++I) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kb = 0; kb < G::DKP / 32; ++kb) {
+            Frag<E> fb;
+            frag_direct_perm(fb, s_q, G::LDK, 16 * I + i16, 32 * kb);
+            mma2a(acc, fs[kb], fsl[kb], fb);
+          }
+          acc *= s_fq[16 * I + i16];
+#pragma unroll
+          for (int jb = 0; jb < 2; ++jb) {
+            if (jb == 1 && I < 2) continue;
+            Frag<E> fb, fbl;
+            frag_direct(fb, s_a, G::LDA, 16 * I + i16, 32 * jb);
+            if constexpr (Split<E>::on) frag_direct(fbl, s_al, G::LDA, 16 * I + i16, 32 * jb);
+            mma2b(acc, fvt[jb], fb, fbl);
+          }
+          const int n0 = 16 * cn + 4 * g;
+          if (n0 < DV) store4(o + tok_off(b, t0 + 16 * I + i16, h, a.T, a.H, DV) + n0, acc);
+        }
+      }
+    }
+
+    state_update<E, DK, DV, DECAY>(S, s_k, s_v, s_gam, s_fk, seg);
+    __syncthreads();
+  }
+
+  if constexpr (!APPLY) {
+    // ---- summary record [M (m_slot) | delta_S (dk*dv)] -----------------------------
+    float* rec = a.summary + (int64_t)(r * a.B * a.H + bh) * a.W;
+    const float keep = any_start ? 0.f : 1.f;
+    if constexpr (DECAY == DECAY_DIAG) {
+      if (threadIdx.x < DK) rec[threadIdx.x] = keep * __expf(gsum);
+    } else {
+      if (threadIdx.x < 4) {
+        float mval = (DECAY == DECAY_SCALAR) ? __expf(gsum) : 1.f;
+        rec[threadIdx.x] = threadIdx.x == 0 ? keep * mval : 0.f;
+      }
+    }
+    float* ds = rec + a.m_slot;
+#pragma unroll
+    for (int m = 0; m < G::NKT; ++m)
+#pragma unroll
+      for (int cc = 0; cc < G::CPWV; ++cc) {
+        const int cn = w + NWAVE * cc;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int d = 16 * m + 4 * g + rr, n = 16 * cn + i16;
+          if (cn < G::NVT && d < DK && n < DV) ds[d * DV + n] = S[m][cc][rr];
+        }
+      }
+  }
+}
+
+#define CPLA_INST_FWD(E, D, DEC)                                                   \
+  template __global__ void fwd_walk<E, D, D, DEC, false>(FwdArgs);                \
+  template __global__ void fwd_walk<E, D, D, DEC, true>(FwdArgs);
+#define CPLA_INST_FWD3(E, D) CPLA_INST_FWD(E, D, 0) CPLA_INST_FWD(E, D, 1) CPLA_INST_FWD(E, D, 2)
+CPLA_INST_FWD3(bf16_t, 16)
+CPLA_INST_FWD3(bf16_t, 64)
+CPLA_INST_FWD3(bf16_t, 128)
+CPLA_INST_FWD3(float, 16)
+CPLA_INST_FWD3(float, 64)
+
+}  // namespace cpla

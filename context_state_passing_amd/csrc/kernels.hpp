@@ -1,0 +1,59 @@
+// Kernel argument blocks and templates shared by the launchers (abi.cpp) and the
+// kernel translation units. Device code only ever sees these plain structs.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device.hpp"
+
+namespace cpla {
+
+struct FwdArgs {
+  int64_t B, T, H, W;        // W: floats per summary record
+  int P, rank_begin, m_slot;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const int32_t* seq_idx;    // packed sequences or null
+  const float* state_in;     // apply: incoming state of every shard [P,B,H,dk,dv]
+  float* summary;            // prepare: [P,B,H,W]
+  void* out;                 // apply: o
+  float* chunk_states;       // apply: state entering every chunk (fp32), or null
+};
+
+struct BwdArgs {
+  int64_t B, T, H, W;
+  int P, rank_begin, m_slot;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const void* dO;
+  const int32_t* seq_idx;
+  const float* chunk_states; // apply: saved forward states (fp32)
+  const float* grad_in;      // apply: gradient arriving at every shard's end [P,B,H,dk,dv]
+  float* summary;            // prepare: [P,B,H,W]
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+};
+
+struct ScanArgs {
+  int64_t BH, W, n_elem;     // n_elem = B*H*dk*dv
+  int dk, dv, P, m_slot, diag, reverse, group;
+  const float* summary;      // [P,B,H,W]
+  const int32_t* slice;      // preceding_rank_start (forward) / following_rank_stop (reverse), or null
+  const float* init;         // S_init (forward) / dS_final (reverse), or null
+  float* out;                // [P,B,H,dk,dv]
+  float* fin;                // final state (forward) / dS_init (reverse), or null
+};
+
+template <typename E, int DK, int DV, int DECAY, bool APPLY>
+__global__ void fwd_walk(FwdArgs a);
+template <typename E, int DK, int DV, int DECAY, bool APPLY>
+__global__ void bwd_walk(BwdArgs a);
+__global__ void affine_scan(ScanArgs a);
+
+}  // namespace cpla

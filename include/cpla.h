@@ -1,0 +1,181 @@
+/*
+ * cpla.h -- C ABI of the chunkwise context-parallel linear-attention library
+ * (libcpla.so, gfx950 / MI355X).
+ *
+ * The calls follow the local-backend protocol of the Megatron-Core API page
+ * "core.ssm.context_parallel.chunkwise" (class LinearAttentionCPBackend):
+ *   cp_forward_prepare   - the state summary of each contiguous shard with zero
+ *                          incoming state (S_out = M S_in + delta_S);
+ *   cp_forward_apply     - compose the preceding summaries, then compute the
+ *                          local output;
+ *   cp_backward_prepare  - gamma of each shard with zero outgoing-state gradient
+ *                          (dS_in = M^T dS_out + gamma);
+ *   cp_backward_apply    - compose the reverse-causal suffix, then finish the
+ *                          local input gradients;
+ * plus build_packed_sequence_cp_metadata (same page, function of that name and
+ * class PackedSequenceCPMetadata).
+ *
+ * On one GPU the CP "ranks" are P contiguous segments of the same sequence in
+ * the same HBM; one call handles the shards [rank_begin, rank_end) of every
+ * (b, h) row. The library performs no communication.
+ *
+ * Method (per (b, h) row; g is the log-decay, a_t = exp(g_t)):
+ *   S_t = diag(a_t) S_{t-1} + k_t v_t^T,  o_t = S_t^T q_t,  S_{-1} = S_init,
+ *   and S_{t-1} := 0 where token t starts a packed sequence.
+ *
+ * Conventions shared by every call
+ *   - Every pointer is caller-owned. Device pointers point to HBM; the library
+ *     allocates nothing, keeps no pointer after returning, and enqueues all
+ *     device work on `stream` without synchronising the host.
+ *   - Tensors are dense row-major with the last index fastest:
+ *       q, k      [B, T, H, dk]   dtype (bf16 or fp32)
+ *       v, o, dO  [B, T, H, dv]   dtype
+ *       g, dg     scalar decay [B, T, H] fp32; diagonal decay [B, T, H, dk]
+ *                 fp32; no decay: NULL
+ *       states    [B, H, dk, dv] fp32 (S_init, final state and their grads)
+ *       summaries [P, B, H, W] fp32, W = cpla_summary_width(): the first
+ *                 m_slot entries hold the transition M (dk values for a
+ *                 diagonal decay, else one value followed by 3 zero pads),
+ *                 then dk*dv entries hold delta_S (or gamma), row = key dim.
+ *                 M is 0 for a shard that contains a packed-sequence start.
+ *       per-shard states [P, B, H, dk, dv] fp32
+ *       chunk states [B, H, T/chunk, dk, dv] fp32: the state entering every
+ *                 chunk (saved by the forward for the backward)
+ *   - Shard r covers tokens [r*T/P, (r+1)*T/P) of every row.
+ *   - Alignment: every device pointer 16-byte aligned.
+ *   - Validation happens on the host before any launch. On failure a call
+ *     returns a non-zero cpla_status, launches nothing, and sets a message
+ *     readable through cpla_last_error(). Kernel launch failures return
+ *     CPLA_E_HIP. Device kernels trust packed metadata produced by
+ *     build_packed_sequence_cp_metadata / cpla_packed_rank_slices.
+ */
+#ifndef CPLA_H
+#define CPLA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+#define CPLA_ABI_VERSION 1
+
+typedef enum {
+  CPLA_OK = 0,
+  CPLA_E_INVALID = 1,      /* null pointer where one is required, bad enum  */
+  CPLA_E_SHAPE = 2,        /* sizes inconsistent or not divisible           */
+  CPLA_E_DTYPE = 3,        /* unknown dtype                                  */
+  CPLA_E_ALIGN = 4,        /* a pointer is not 16-byte aligned               */
+  CPLA_E_UNSUPPORTED = 5,  /* valid request this build does not implement   */
+  CPLA_E_METADATA = 6,     /* malformed packed-sequence metadata             */
+  CPLA_E_HIP = 7           /* a HIP launch or runtime call failed            */
+} cpla_status;
+
+typedef enum { CPLA_F32 = 0, CPLA_BF16 = 1 } cpla_dtype;
+typedef enum { CPLA_DECAY_NONE = 0, CPLA_DECAY_SCALAR = 1, CPLA_DECAY_DIAG = 2 } cpla_decay;
+
+typedef struct {
+  int64_t B, T, H, dk, dv;   /* packed sequences: B == 1 and T is the stream length   */
+  int32_t num_shards;        /* P: T % P == 0 and (T / P) % chunk == 0                 */
+  int32_t chunk;             /* chunk length C; this build supports 64 only            */
+  int32_t rank_begin;        /* shards handled by this call: [rank_begin, rank_end)    */
+  int32_t rank_end;          /*   (0 and P on one GPU)                                  */
+  int32_t dtype;             /* cpla_dtype of q, k, v, o, dO, dq, dk, dv                */
+  int32_t decay;             /* cpla_decay                                              */
+} cpla_problem;
+
+/* Packed sequences. Passing NULL for the whole struct means "not packed": every
+ * row is one sequence that starts from S_init, the forward prefix of rank r is
+ * [0, r) and the backward suffix is (r, P). Device pointers. */
+typedef struct {
+  const int32_t* seq_idx;               /* [T] global sequence id of each token       */
+  const int32_t* preceding_rank_start;  /* [P] inclusive start of rank r's prefix      */
+  const int32_t* following_rank_stop;   /* [P] exclusive end of rank r's suffix        */
+} cpla_packed;
+
+/* Floats per (shard, b, h) summary record: m_slot + dk*dv (see layout above). */
+int64_t cpla_summary_width(const cpla_problem* p);
+
+/* Bytes of the chunk-state buffer the forward saves for the backward. */
+int64_t cpla_chunk_states_bytes(const cpla_problem* p);
+
+/* cp_forward_prepare: for every handled shard, run the shard from a zero state
+ * and write its map (M, delta_S) to fwd_summary[r]. With packed sequences the
+ * summary covers the shard's last sequence segment. Reads k, v, g. */
+cpla_status cp_forward_prepare(const cpla_problem* p, const cpla_packed* packed,
+                               const void* k, const void* v, const float* g,
+                               float* fwd_summary, hipStream_t stream);
+
+/* cp_forward_apply: compose the summaries of the preceding shards (the prefix
+ * [preceding_rank_start, r), started from initial_state when it starts at rank 0,
+ * else from zero) into shard_in_state[r], then run every handled shard from its
+ * incoming state and write o. final_state (nullable) receives the state after
+ * the last shard. chunk_states (nullable) receives the state entering every
+ * chunk; it is required later by cp_backward_apply. initial_state must be NULL
+ * with packed sequences. */
+cpla_status cp_forward_apply(const cpla_problem* p, const cpla_packed* packed,
+                             const void* q, const void* k, const void* v, const float* g,
+                             const float* fwd_summary, const float* initial_state,
+                             void* o, float* shard_in_state, float* final_state,
+                             void* chunk_states, hipStream_t stream);
+
+/* cp_backward_prepare: for every handled shard, the gradient w.r.t. its
+ * incoming state when no gradient arrives at its end (gamma), and its
+ * transition, into bwd_summary[r]. With packed sequences it covers the shard's
+ * first sequence segment. Reads q, g, dO. */
+cpla_status cp_backward_prepare(const cpla_problem* p, const cpla_packed* packed,
+                                const void* q, const float* g, const void* dO,
+                                float* bwd_summary, hipStream_t stream);
+
+/* cp_backward_apply: compose the reverse-causal suffix (r, following_rank_stop)
+ * of backward summaries, started from d_final_state (nullable = zero; must be
+ * NULL with packed sequences) when it reaches the last rank, into
+ * shard_out_grad[r]; then walk every handled shard backwards from it and write
+ * dq, dk, dv and dg (fp32, like g; NULL iff no decay). d_initial_state
+ * (nullable, unpacked only) receives the gradient w.r.t. S_init. chunk_states
+ * is the buffer cp_forward_apply filled. */
+cpla_status cp_backward_apply(const cpla_problem* p, const cpla_packed* packed,
+                              const void* q, const void* k, const void* v, const float* g,
+                              const void* dO, const void* chunk_states,
+                              const float* bwd_summary, const float* d_final_state,
+                              void* dq, void* dk, void* dv, float* dg,
+                              float* shard_out_grad, float* d_initial_state,
+                              hipStream_t stream);
+
+/* build_packed_sequence_cp_metadata (host memory, pure, thread-safe): rank-local
+ * packed metadata from the global per-token sequence ids (length T, starting at
+ * 0, each step 0 or 1, T % cp_size == 0). local_seq_idx [T/cp_size] receives the
+ * rank's ids rebased to start at 0; local_cu_seqlens (capacity T/cp_size + 1)
+ * receives 0, each interior id change and T/cp_size, and *num_local_seqs its
+ * number of sequences; *preceding_rank_start is the rank holding the first token
+ * of the sequence live at the rank's first token, *following_rank_stop one past
+ * the rank holding the last token of the sequence live at its last token.
+ * Malformed ids return CPLA_E_METADATA. */
+cpla_status build_packed_sequence_cp_metadata(const int32_t* global_seq_idx, int64_t T,
+                                              int32_t cp_rank, int32_t cp_size,
+                                              int32_t* local_seq_idx, int32_t* local_cu_seqlens,
+                                              int32_t* num_local_seqs,
+                                              int32_t* preceding_rank_start,
+                                              int32_t* following_rank_stop);
+
+/* preceding_rank_start and following_rank_stop of every rank at once (host). */
+cpla_status cpla_packed_rank_slices(const int32_t* global_seq_idx, int64_t T, int32_t cp_size,
+                                    int32_t* preceding_rank_start, int32_t* following_rank_stop);
+
+/* Sequence id of every token from cu_seqlens [n_seqs + 1] (host): strictly
+ * increasing, 0 first, T last. */
+cpla_status cpla_seq_idx_from_cu_seqlens(const int32_t* cu_seqlens, int32_t n_seqs, int64_t T,
+                                         int32_t* seq_idx);
+
+/* Message of the last failure on the calling thread; valid until its next call. */
+const char* cpla_last_error(void);
+
+int cpla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CPLA_H */

@@ -1,0 +1,84 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs, element by element, for outputs, gradients and the
+intermediate summaries / composed states.
+
+Small cases keep every workload's distributions and head size but shrink B, T,
+H so the oracle finishes in seconds; they still span several chunks per shard,
+several shards, and packed sequences with boundaries inside chunks. Full-size
+cases run the exact benchmark shapes on the GPU and compare sampled heads, which
+the oracle computes independently.
+"""
+import sys
+
+import pytest
+import torch
+
+import workloads
+from _parity import compare, gpu_run, oracle_run
+
+pytestmark = pytest.mark.gpu
+
+
+def _announce(name):
+    print(f"[gpu-case] {name}", file=sys.stderr, flush=True)
+
+
+SMALL = {
+    # name: (workload, overrides, backward)
+    "identity_fwd_full": ("identity_fwd", {}, False),
+    "identity_fp32_bwd": ("identity_fwd", {"backward": True}, True),
+    "identity_fp32_bwd_T1024_P8": ("identity_fwd", {"backward": True, "T": 1024, "num_shards": 8}, True),
+    "scalar_small_fwd": ("scalar_fwd", {"B": 2, "H": 2, "T": 1024, "num_shards": 4}, False),
+    "scalar_small_bwd": ("scalar_fwd", {"B": 1, "H": 2, "T": 1024, "num_shards": 4, "backward": True}, True),
+    "scalar_weak_bwd": ("scalar_fwd", {"B": 1, "H": 2, "T": 1024, "num_shards": 4, "backward": True,
+                                       "decay_scale": 1e-3}, True),
+    "diag_small_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 512, "num_shards": 4}, True),
+    "diag_weak_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 512, "num_shards": 4, "decay_scale": 1e-3}, True),
+    "diag_d64_bwd": ("diag_fwdbwd", {"B": 2, "H": 1, "T": 512, "d": 64, "num_shards": 2}, True),
+    "packed_small_bwd": ("packed_fwdbwd", {"T": 2048, "H": 2, "num_shards": 4, "len_range": (100, 700)}, True),
+    "packed_short_seqs_bwd": ("packed_fwdbwd", {"T": 1024, "H": 2, "num_shards": 4, "len_range": (1, 70)}, True),
+    "packed_weak_bwd": ("packed_fwdbwd", {"T": 2048, "H": 2, "num_shards": 8, "len_range": (100, 900),
+                                          "decay_scale": 1e-3}, True),
+    "long_small_bwd": ("long_fwdbwd", {"T": 1024, "H": 2, "num_shards": 4}, True),
+    "long_weak_bwd": ("long_fwdbwd", {"T": 1024, "H": 2, "num_shards": 4, "decay_scale": 1e-3}, True),
+    "single_shard_bwd": ("diag_fwdbwd", {"B": 1, "H": 1, "T": 256, "num_shards": 1}, True),
+    "scalar_d16_bf16_bwd": ("scalar_fwd", {"B": 1, "H": 2, "T": 512, "d": 16, "num_shards": 2,
+                                           "backward": True}, True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_small_parity(case, gpu_available):
+    name, ov, bwd = SMALL[case]
+    _announce(case)
+    wl = workloads.make(name, **ov)
+    got = gpu_run(wl, backward=bwd)
+    ref = oracle_run(wl, backward=bwd)
+    compare(wl, got, ref, backward=bwd)
+
+
+def test_d_final_state(gpu_available):
+    _announce("diag_small_dfinal")
+    wl = workloads.make("diag_fwdbwd", B=1, H=2, T=512, num_shards=4, decay_scale=1e-2)
+    dSf = torch.randn(1, 2, 128, 128, generator=torch.Generator().manual_seed(7))
+    got = gpu_run(wl, backward=True, d_final_state=dSf)
+    ref = oracle_run(wl, backward=True, d_final_state=dSf)
+    compare(wl, got, ref, backward=True)
+
+
+def test_scalar_fwd_full_size(gpu_available):
+    _announce("scalar_fwd_full")
+    wl = workloads.make("scalar_fwd")
+    got = gpu_run(wl, backward=False)
+    ref = oracle_run(wl, backward=False)
+    compare(wl, got, ref, backward=False)
+
+
+def test_deterministic(gpu_available):
+    _announce("determinism")
+    wl = workloads.make("packed_fwdbwd", T=2048, H=2, num_shards=4, len_range=(100, 700))
+    a = gpu_run(wl, backward=True)
+    b = gpu_run(wl, backward=True)
+    for key in a:
+        if a[key] is not None:
+            assert (a[key] == b[key]).all(), key
