@@ -1,0 +1,254 @@
+"""Benchmark: fwd+bwd tokens/s of chunkwise context-parallel linear attention.
+
+Workload (default): diagonal (per-key-dim) gated decay, B=4, H=16, T=8192,
+d_k=d_v=128, bf16 q/k/v/dO, fp32 log-decay, chunk 64, 8 simulated shards of 1024
+tokens, seeded synthetic inputs already resident in HBM. One step = the whole
+hot path: cp_forward_prepare, cp_forward_apply (prefix scan + local output),
+cp_backward_prepare, cp_backward_apply (suffix scan + local gradients).
+
+Prints ONE JSON line. `roofline` is for the dominant kernel (the backward shard
+walk inside cp_backward_apply): algorithmic bytes per launch / its average
+duration from HIP events recorded on the launch stream around that call (the
+call also runs the small suffix-scan kernel). `traffic` comes from the committed
+rocprofv3 counter summary in profiles/, and is null if the kernel sources changed
+since it was taken. `cpu_baseline` times the fp64 oracle on a bounded sample,
+before the GPU is touched.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+bwd tokens/s, chunkwise linear attn H16 d128 T8k bf16; % MFMA/HBM peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+KERNEL_SOURCES = ["bwd.hip", "chunk_common.hpp", "device.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_walk_diag_B4_H16_T8192_d128.txt")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="diag_fwdbwd")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="rows (b,h) in the oracle sample (0 = auto)")
+    return ap.parse_args()
+
+
+# ---- algorithmic counts (per token-head, chunk C, head size d) ------------------------
+
+def algorithmic(wl):
+    """Bytes and flops per token-head of the method's minimum: every input read
+    once, every output written once; flops of the chunkwise form."""
+    d, C = wl.d, wl.chunk
+    e = 2 if str(wl.dtype) == "torch.bfloat16" else 4
+    gbytes = {"none": 0, "scalar": 4, "diag": 4 * d}[wl.decay]
+    fwd = 3 * d * e + gbytes + d * e                    # q, k, v, g in; o out
+    bwd = 4 * d * e + gbytes + 3 * d * e + gbytes       # q, k, v, dO, g in; dq, dk, dv, dg out
+    flops_f = 4 * C * d + 4 * d * d
+    flops_b = 8 * C * d + 8 * d * d
+    return {"bytes_fwd": fwd, "bytes_bwd_apply": bwd, "flops_fwd": flops_f, "flops_bwd": flops_b}
+
+
+def sources_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "context_state_passing_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic():
+    """(bytes per launch, note) from the committed counter summary, or (None, why)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter summary"
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("sources_sha256_16") != sources_hash():
+        return None, "kernel changed since counters were taken"
+    try:
+        return float(vals["hbm_bytes_per_launch"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-kernel calibrated"
+    except (KeyError, ValueError):
+        return None, "summary incomplete"
+
+
+# ---- CPU baseline: the fp64 oracle on a bounded sample ----------------------------------
+
+_WL = None  # workload shared with forked workers (copy-on-write)
+
+
+def _oracle_row(args):
+    h, b = args
+    from threadpoolctl import threadpool_limits
+    from oracle import cp as ocp
+    wl = _WL
+    sl = lambda x: None if x is None else x[b:b + 1, :, h:h + 1]  # noqa: E731
+    S0 = None if wl.initial_state is None else wl.initial_state[b:b + 1, h:h + 1]
+    seq = None
+    if wl.cu_seqlens is not None:
+        from oracle import metadata as omd
+        seq = omd.seq_idx_from_cu_seqlens(wl.cu_seqlens.numpy(), wl.T)
+    with threadpool_limits(1):
+        t = time.perf_counter()
+        ocp.cp_backward(sl(wl.q), sl(wl.k), sl(wl.v), sl(wl.g), wl.decay, sl(wl.dO), wl.num_shards,
+                        initial_state=S0, seq_idx=seq)
+        return time.perf_counter() - t
+
+
+def cpu_baseline(wl, rows_req):
+    """Oracle fwd+bwd on a few full-length (b, h) rows, one single-threaded
+    worker process per row, forked before the GPU is initialised."""
+    global _WL
+    import multiprocessing as mp
+    _WL = wl
+    avail = len(os.sched_getaffinity(0))
+    rows = rows_req or min(16, avail)
+    workers = min(rows, avail, 16)
+    pairs = [(r % wl.H, (r // wl.H) % wl.B) for r in range(rows)]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        per = pool.map(_oracle_row, pairs)
+    wall = time.perf_counter() - t0
+    tok_heads = rows * wl.T
+    return {"value": tok_heads / wl.H / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"fp64 oracle CP fwd+bwd (summaries, composition, per-token recurrence and adjoint) on "
+                      f"{rows} of the {wl.B * wl.H} (b,h) rows at full T={wl.T}, {wl.num_shards} shards; "
+                      f"{workers} single-threaded processes, wall {wall:.1f}s, {sum(per):.1f} CPU-s; "
+                      f"value = row-tokens/s / H",
+            "cpu_seconds": round(sum(per), 2)}
+
+
+# ---- GPU run --------------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "summary exchange is not built", file=sys.stderr)
+        sys.exit(2)
+    rank = int(os.environ.get("RANK", "0"))
+    import torch
+    import workloads
+    wl = workloads.make(args.workload)
+    cpu = None
+    if rank == 0 and not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_rows)
+
+    from context_state_passing_amd import _lib
+    from context_state_passing_amd.api import _ptr, make_problem, packed_meta
+
+    dev = torch.device("cuda:0")
+    q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
+    g = None if wl.g is None else wl.g.to(dev)
+    dO = wl.dO.to(dev)
+    S0 = None if wl.initial_state is None else wl.initial_state.to(dev)
+    decay = {"none": 0, "scalar": 1, "diag": 2}[wl.decay]
+    p = make_problem(q, v, wl.num_shards, decay)
+    L = _lib.lib()
+    B, T, H, d = wl.B, wl.T, wl.H, wl.d
+    P = wl.num_shards
+    W = L.cpla_summary_width(ctypes.byref(p))
+    f32 = dict(device=dev, dtype=torch.float32)
+    fsum = torch.empty((P, B, H, W), **f32)
+    bsum = torch.empty((P, B, H, W), **f32)
+    s_in = torch.empty((P, B, H, d, d), **f32)
+    s_out = torch.empty((P, B, H, d, d), **f32)
+    fin = torch.empty((B, H, d, d), **f32)
+    dS0 = torch.empty((B, H, d, d), **f32) if wl.cu_seqlens is None else None
+    cs = torch.empty((B, H, T // 64, d, d), **f32)
+    o = torch.empty_like(v)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = None if g is None else torch.empty_like(g)
+    pk = None
+    if wl.cu_seqlens is not None:
+        meta = packed_meta(wl.cu_seqlens, T, P, dev)
+        pk = ctypes.byref(meta.c())
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    pp = ctypes.byref(p)
+    chk = _lib.check
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        chk(L.cp_forward_prepare(pp, pk, _ptr(k), _ptr(v), _ptr(g), _ptr(fsum), sp))
+        if ev: ev[1].record(stream)
+        chk(L.cp_forward_apply(pp, pk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(fsum), _ptr(S0), _ptr(o),
+                               _ptr(s_in), _ptr(fin), _ptr(cs), sp))
+        if ev: ev[2].record(stream)
+        chk(L.cp_backward_prepare(pp, pk, _ptr(q), _ptr(g), _ptr(dO), _ptr(bsum), sp))
+        if ev: ev[3].record(stream)
+        chk(L.cp_backward_apply(pp, pk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dO), _ptr(cs), _ptr(bsum),
+                                None, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(s_out), _ptr(dS0), sp))
+        if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    parts = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(4)]
+    names = ["cp_forward_prepare", "cp_forward_apply", "cp_backward_prepare", "cp_backward_apply"]
+
+    tokens = B * T
+    th = tokens * H
+    alg = algorithmic(wl)
+    dom_ms = parts[3]
+    dom_bytes = alg["bytes_bwd_apply"] * th
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic, tnote = read_traffic()
+    step_bytes = (alg["bytes_fwd"] + alg["bytes_bwd_apply"]) * th
+    step_flops = (alg["flops_fwd"] + alg["flops_bwd"]) * th
+    out = {
+        "metric": METRIC,
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "dk": d, "dv": d, "chunk": wl.chunk,
+                   "shards": P, "decay": wl.decay, "parallelism": "single-gpu (shards simulated in HBM)"},
+        "roofline": {"bound": "hbm", "kernel": "bwd_walk (cp_backward_apply)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "traffic_note": tnote,
+                     "algorithmic_bytes_per_launch": dom_bytes, "launch_ms": dom_ms},
+        "step_breakdown_ms": dict(zip(names, parts)),
+        "step_roofline": {"algorithmic_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+                          "hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                          "mfma_TFLOPs": step_flops / (ms_step * 1e-3) / 1e12,
+                          "mfma_frac": step_flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "fwd_tokens_per_s": tokens / ((parts[0] + parts[1]) * 1e-3),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,8 +17,9 @@
 namespace cpla {
 
 // S <- diag(exp(Gam_last)) keep*S + K^T V with the tail/decay token factors.
+// K^ = K exp(Gam_last - Gam) tail enters the MFMA split into hi + lo parts.
 template <typename E, int DK, int DV, int DECAY, int NKT_, int CPWV_>
-__device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* Kt, const E* Vt,
+__device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* Kt, const E* Ktl, const E* Vt,
                                              const float* gam, const float* fk, const ChunkSeg& seg) {
   using G = Geo<E, DK, DV>;
   const int w = wave_id(), l = lane_id(), g = l >> 4;
@@ -48,12 +49,29 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* K
   for (int m = 0; m < G::NKT; ++m) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      Frag<E> a;
+      Frag<E> a, al;
       frag_tr(a, Kt, G::LDK, 32 * kb, 16 * m);
-      if (scale_tok) frag_scale_tokens(a, fk, 32 * kb, false);
+      if constexpr (DECAY == DECAY_DIAG && Split<E>::on) {
+        frag_tr(al, Ktl, G::LDK, 32 * kb, 16 * m);
+        if (scale_tok) {
+          frag_scale_tokens(a, fk, 32 * kb, false);
+          frag_scale_tokens(al, fk, 32 * kb, false);
+        }
+      } else if constexpr (DECAY == DECAY_SCALAR) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = to_f(a.v[e]) * fk[32 * kb + kidx(e)];
+        split_frag(a, al, x);
+      } else {
+        if (scale_tok) frag_scale_tokens(a, fk, 32 * kb, false);
+        frag_zero(al);
+      }
 #pragma unroll
       for (int cc = 0; cc < G::CPWV; ++cc)
-        if (w + NWAVE * cc < G::NVT) mma(S[m][cc], a, bv[kb][cc]);
+        if (w + NWAVE * cc < G::NVT) {
+          if constexpr (DECAY == DECAY_NONE || !Split<E>::on) mma(S[m][cc], a, bv[kb][cc]);
+          else mma2a(S[m][cc], a, al, bv[kb][cc]);
+        }
     }
   }
   if constexpr (DECAY == DECAY_DIAG) {
@@ -75,8 +93,11 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
   using G = Geo<E, DK, DV>;
   constexpr int GAM = (DECAY == DECAY_DIAG) ? CH * DK : CH;
   constexpr int NQT = APPLY ? 1 : 0;
+  constexpr int DSP = (DECAY == DECAY_DIAG && Split<E>::on) ? 1 : 0;   // exp-scaled tiles split
   __shared__ __attribute__((aligned(16))) E s_q[NQT * G::TILE_K + 8];
+  __shared__ __attribute__((aligned(16))) E s_ql[NQT * DSP * G::TILE_K + 8];
   __shared__ __attribute__((aligned(16))) E s_k[G::TILE_K];
+  __shared__ __attribute__((aligned(16))) E s_kl[DSP * G::TILE_K + 8];
   __shared__ __attribute__((aligned(16))) E s_v[G::TILE_V];
   constexpr int NAL = (APPLY && Split<E>::on) ? 1 : 0;
   __shared__ __attribute__((aligned(16))) E s_a[NQT * G::TILE_A + 8];    // scores, hi part
@@ -120,8 +141,9 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
     stage_gamma<DK, DECAY>(a.g, b, h, t0, a.T, a.H, seg, s_gam, s_fq, s_fk, s_red);
     if constexpr (DECAY == DECAY_DIAG) {
       if (threadIdx.x < DK) gsum += s_gam[(CH - 1) * DK + threadIdx.x];
-      stage_tile<E, DK, G::DKP, G::LDK, 2, DK>(k, b, h, t0, a.T, a.H, s_k, s_gam);
-      if constexpr (APPLY) stage_tile<E, DK, G::DKP, G::LDK, 1, DK>(q, b, h, t0, a.T, a.H, s_q, s_gam);
+      stage_tile_split<E, DK, G::DKP, G::LDK, 2, DK>(k, b, h, t0, a.T, a.H, s_k, s_kl, s_gam, nullptr);
+      if constexpr (APPLY)
+        stage_tile_split<E, DK, G::DKP, G::LDK, 1, DK>(q, b, h, t0, a.T, a.H, s_q, s_ql, s_gam, nullptr);
     } else {
       if constexpr (DECAY == DECAY_SCALAR)
         if (threadIdx.x == 0) gsum += s_gam[CH - 1];
@@ -158,10 +180,16 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
         if (!score_tile_zero(idx)) {
 #pragma unroll
           for (int kd = 0; kd < G::DKP / 32; ++kd) {
-            Frag<E> fa, fb;
+            Frag<E> fa, fb, fal, fbl;
             frag_direct(fa, s_q, G::LDK, 16 * I + i16, 32 * kd);
             frag_direct(fb, s_k, G::LDK, 16 * J + i16, 32 * kd);
-            mma(acc, fa, fb);
+            if constexpr (DSP) {
+              frag_direct(fal, s_ql, G::LDK, 16 * I + i16, 32 * kd);
+              frag_direct(fbl, s_kl, G::LDK, 16 * J + i16, 32 * kd);
+              mma3(acc, fa, fal, fb, fbl);
+            } else {
+              mma(acc, fa, fb);
+            }
           }
         }
 #pragma unroll
@@ -195,9 +223,14 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < G::DKP / 32; ++kb) {
-            Frag<E> fb;
+            Frag<E> fb, fbl;
             frag_direct_perm(fb, s_q, G::LDK, 16 * I + i16, 32 * kb);
-            mma2a(acc, fs[kb], fsl[kb], fb);
+            if constexpr (DSP) {
+              frag_direct_perm(fbl, s_ql, G::LDK, 16 * I + i16, 32 * kb);
+              mma3(acc, fs[kb], fsl[kb], fb, fbl);
+            } else {
+              mma2a(acc, fs[kb], fsl[kb], fb);
+            }
           }
           acc *= s_fq[16 * I + i16];
 #pragma unroll
@@ -214,7 +247,7 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
       }
     }
 
-    state_update<E, DK, DV, DECAY>(S, s_k, s_v, s_gam, s_fk, seg);
+    state_update<E, DK, DV, DECAY>(S, s_k, s_kl, s_v, s_gam, s_fk, seg);
     __syncthreads();
   }
 

@@ -36,7 +36,19 @@ def _np(t):
     return None if t is None else t.detach().float().cpu().double().numpy()
 
 
-def gpu_run(wl, backward=True, device="cuda:0", d_final_state=None):
+def _select(key, t, heads):
+    """Keep the sampled heads of a device tensor before it is copied to the host."""
+    if t is None or heads is None:
+        return t
+    idx = torch.as_tensor(heads, device=t.device)
+    if key in ("final_state", "d_initial_state"):           # [B,H,...]
+        return t.index_select(1, idx)
+    if key in ("fwd_summary", "bwd_summary", "shard_in_state", "shard_out_grad"):   # [P,B,H,...]
+        return t.index_select(2, idx)
+    return t.index_select(2, idx)                            # [B,T,H,...]
+
+
+def gpu_run(wl, backward=True, device="cuda:0", d_final_state=None, heads=None):
     import context_state_passing_amd as cpla
     dev = torch.device(device)
     q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
@@ -52,7 +64,7 @@ def gpu_run(wl, backward=True, device="cuda:0", d_final_state=None):
                                                      want_intermediates=True)
         out.update(dq=dq, dk=dk, dv=dv, dg=dg, d_initial_state=dS0, **inter)
     torch.cuda.synchronize(dev)
-    return {key: _np(val) for key, val in out.items()}
+    return {key: _np(_select(key, val, heads)) for key, val in out.items()}
 
 
 def _rows(x, heads):

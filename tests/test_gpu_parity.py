@@ -27,7 +27,10 @@ SMALL = {
     # name: (workload, overrides, backward)
     "identity_fwd_full": ("identity_fwd", {}, False),
     "identity_fp32_bwd": ("identity_fwd", {"backward": True}, True),
-    "identity_fp32_bwd_T1024_P8": ("identity_fwd", {"backward": True, "T": 1024, "num_shards": 8}, True),
+    "scalar_fp32_d64_bwd": ("scalar_fwd", {"B": 1, "H": 2, "T": 512, "num_shards": 4, "backward": True,
+                                           "dtype": torch.float32}, True),
+    "diag_fp32_d64_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 256, "d": 64, "num_shards": 2,
+                                         "dtype": torch.float32}, True),
     "scalar_small_fwd": ("scalar_fwd", {"B": 2, "H": 2, "T": 1024, "num_shards": 4}, False),
     "scalar_small_bwd": ("scalar_fwd", {"B": 1, "H": 2, "T": 1024, "num_shards": 4, "backward": True}, True),
     "scalar_weak_bwd": ("scalar_fwd", {"B": 1, "H": 2, "T": 1024, "num_shards": 4, "backward": True,
@@ -82,3 +85,21 @@ def test_deterministic(gpu_available):
     for key in a:
         if a[key] is not None:
             assert (a[key] == b[key]).all(), key
+
+
+FULL = [
+    # full benchmark shapes; the oracle recomputes the sampled heads of every batch row
+    ("diag_fwdbwd", [0, 15]),
+    ("packed_fwdbwd", [0, 15]),
+    ("long_fwdbwd", [7]),
+]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,heads", FULL)
+def test_full_size_sampled_heads(name, heads, gpu_available):
+    _announce(f"full {name} heads {heads}")
+    wl = workloads.make(name)
+    got = gpu_run(wl, backward=True, heads=heads)
+    ref = oracle_run(wl, backward=True, heads=heads)
+    compare(wl, got, ref, backward=True)

@@ -33,7 +33,8 @@ to nearest even by ``Tensor.to(torch.bfloat16)``.
 
 ``make(name, **overrides)`` returns a ``Workload`` whose shapes may be shrunk
 (``B``, ``T``, ``H``, ``d``, ``num_shards``) for fast tests while keeping the
-distributions; ``decay_scale`` multiplies g (weak-decay coverage variants).
+distributions; ``decay_scale`` multiplies g (weak-decay coverage variants); ``dtype`` overrides
+the storage dtype of q/k/v/dO (same fp32 draws, different rounding).
 """
 from __future__ import annotations
 
@@ -115,7 +116,7 @@ def make(name: str, *, B: Optional[int] = None, T: Optional[int] = None,
          num_shards: Optional[int] = None, decay_scale: float = 1.0,
          seed_offset: int = 0, len_range: Optional[tuple] = None,
          with_initial_state: Optional[bool] = None,
-         backward: Optional[bool] = None) -> Workload:
+         backward: Optional[bool] = None, dtype: Optional[torch.dtype] = None) -> Workload:
     spec = SPECS[name]
     B = spec.B if B is None else B
     T = spec.T if T is None else T
@@ -161,7 +162,7 @@ def make(name: str, *, B: Optional[int] = None, T: Optional[int] = None,
     dO = randn(B, T, H, d) if bwd else None
     S0 = randn(B, H, d, d) * 0.1 if init else None
 
-    dt = spec.dtype
+    dt = spec.dtype if dtype is None else dtype
     return Workload(
         name=name, B=B, T=T, H=H, d=d, dtype=dt, decay=spec.decay, num_shards=P,
         chunk=CHUNK,
