@@ -128,6 +128,10 @@ bwd_fn pick_bwd(int dtype, int D, int decay) {
   return nullptr;
 }
 
+unsigned threads_for(const cpla_problem* p) {
+  return 64u * (unsigned)waves_for(p->dk < 32 ? 32 : (int)p->dk);
+}
+
 int next_pow2(int x) {
   int g = 1;
   while (g < x) g <<= 1;
@@ -194,7 +198,7 @@ extern "C" cpla_status cp_forward_prepare(const cpla_problem* p, const cpla_pack
   a.summary = fwd_summary;
   fwd_fn fn = pick_fwd<false>(p->dtype, (int)p->dk, p->decay);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no forward kernel for this configuration");
-  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(NTHR), 0, stream, a);
+  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(threads_for(p)), 0, stream, a);
   return launched("cp_forward_prepare");
 }
 
@@ -230,7 +234,7 @@ extern "C" cpla_status cp_forward_apply(const cpla_problem* p, const cpla_packed
   a.chunk_states = reinterpret_cast<float*>(chunk_states);
   fwd_fn fn = pick_fwd<true>(p->dtype, (int)p->dk, p->decay);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no forward kernel for this configuration");
-  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(NTHR), 0, stream, a);
+  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(threads_for(p)), 0, stream, a);
   return launched("cp_forward_apply");
 }
 
@@ -252,7 +256,7 @@ extern "C" cpla_status cp_backward_prepare(const cpla_problem* p, const cpla_pac
   a.summary = bwd_summary;
   bwd_fn fn = pick_bwd<false>(p->dtype, (int)p->dk, p->decay);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no backward kernel for this configuration");
-  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(NTHR), 0, stream, a);
+  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(threads_for(p)), 0, stream, a);
   return launched("cp_backward_prepare");
 }
 
@@ -294,6 +298,6 @@ extern "C" cpla_status cp_backward_apply(const cpla_problem* p, const cpla_packe
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
   bwd_fn fn = pick_bwd<true>(p->dtype, (int)p->dk, p->decay);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no backward kernel for this configuration");
-  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(NTHR), 0, stream, a);
+  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(threads_for(p)), 0, stream, a);
   return launched("cp_backward_apply");
 }

@@ -32,7 +32,7 @@
 namespace cpla {
 
 template <typename E, int DK, int DV, int DECAY, bool APPLY>
-__global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
+__global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
   using G = Geo<E, DK, DV>;
   constexpr bool SP = Split<E>::on;
   constexpr bool DIAG = DECAY == DECAY_DIAG, SCAL = DECAY == DECAY_SCALAR;
@@ -60,9 +60,11 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) E s_qh[QH * G::TILE_K + 8];
   __shared__ __attribute__((aligned(16))) E s_qhl[QHL * G::TILE_K + 8];
   __shared__ __attribute__((aligned(16))) char s_reg[REG_BYTES];
-  __shared__ float s_gs[CH], s_fq[CH], s_fk[CH], s_red[NTHR], s_glast[G::DKP];
-  __shared__ float s_t3[G::DKP];
-  __shared__ float s_u1[NWAVE * CH], s_u4[NWAVE * CH];
+  constexpr int NRED = DIAG ? G::NT : G::NW;                     // column-scan partials / T3 partials
+  constexpr int NU = (APPLY && SCAL) ? G::NW * CH : 1;           // scalar dg token partials
+  __shared__ float s_gs[DIAG ? 1 : CH], s_fq[CH], s_fk[CH], s_red[NRED], s_el[DIAG ? G::DKP : 1];
+  __shared__ float s_t3[(APPLY && DIAG) ? G::DKP : 1];
+  __shared__ float s_u1[NU], s_u4[NU];
 
   float* s_gam = DIAG ? reinterpret_cast<float*>(s_reg) : s_gs;
   E* s_ah = reinterpret_cast<E*>(s_reg);
@@ -91,7 +93,7 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
     for (int m = 0; m < G::NKT; ++m)
 #pragma unroll
       for (int cc = 0; cc < G::CPWV; ++cc) {
-        const int c = w + NWAVE * cc;
+        const int c = w + G::NW * cc;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int d = 16 * m + 4 * g + rr, n = 16 * c + i16;
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
       for (int nt = 0; nt < G::NVT; ++nt)
 #pragma unroll
         for (int cc = 0; cc < G::CPWK; ++cc) {
-          const int cm = w + NWAVE * cc;
+          const int cm = w + G::NW * cc;
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             const int n = 16 * nt + 4 * g + rr, d = 16 * cm + i16;
@@ -125,27 +127,27 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
     const ChunkSeg seg = chunk_seg(a.seq_idx, t0);
     any_start |= seg.any();
     const float keep = seg.any() ? 0.f : 1.f;
-    stage_gamma<DK, DECAY>(a.g, b, h, t0, a.T, a.H, seg, s_gam, s_fq, s_fk, s_red);
+    stage_gamma<DK, DECAY, G::NT>(a.g, b, h, t0, a.T, a.H, seg, s_gam, s_fq, s_fk, s_red);
 
     // ---- stage tiles ----------------------------------------------------------------
     if constexpr (DIAG) {
       if (threadIdx.x < DK) {
         const float gl = s_gam[(CH - 1) * DK + threadIdx.x];
         gsum += gl;
-        s_glast[threadIdx.x] = gl;
+        s_el[threadIdx.x] = __expf(gl);   // exp(Gam_last[d]), read by every row scaling below
       }
-      stage_tile_split<E, DK, G::DKP, G::LDK, 1, DK>(q, b, h, t0, a.T, a.H, s_q, s_ql, s_gam, nullptr);
-      if constexpr (APPLY) stage_tile_split<E, DK, G::DKP, G::LDK, 2, DK>(k, b, h, t0, a.T, a.H, s_k, s_kl, s_gam, nullptr);
+      stage_tile_split<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(q, b, h, t0, a.T, a.H, s_q, s_ql, s_gam, nullptr);
+      if constexpr (APPLY) stage_tile_split<E, DK, G::DKP, G::LDK, 2, DK, G::NT>(k, b, h, t0, a.T, a.H, s_k, s_kl, s_gam, nullptr);
     } else {
       if constexpr (SCAL) {
         if (threadIdx.x == 0) gsum += s_gam[CH - 1];
-        stage_tile_split<E, DK, G::DKP, G::LDK, 3, DK>(q, b, h, t0, a.T, a.H, s_qh, s_qhl, s_gam, s_fq);
+        stage_tile_split<E, DK, G::DKP, G::LDK, 3, DK, G::NT>(q, b, h, t0, a.T, a.H, s_qh, s_qhl, s_gam, s_fq);
       }
-      if constexpr (APPLY || !SCAL) stage_tile<E, DK, G::DKP, G::LDK, 0, DK>(q, b, h, t0, a.T, a.H, s_q, s_gam);
-      if constexpr (APPLY) stage_tile<E, DK, G::DKP, G::LDK, 0, DK>(k, b, h, t0, a.T, a.H, s_k, s_gam);
+      if constexpr (APPLY || !SCAL) stage_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(q, b, h, t0, a.T, a.H, s_q, s_gam);
+      if constexpr (APPLY) stage_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(k, b, h, t0, a.T, a.H, s_k, s_gam);
     }
-    stage_tile<E, DV, G::DVP, G::LDV, 0, DK>(dO, b, h, t0, a.T, a.H, s_do, s_gam);
-    if constexpr (APPLY) stage_tile<E, DV, G::DVP, G::LDV, 0, DK>(v, b, h, t0, a.T, a.H, s_v, s_gam);
+    stage_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(dO, b, h, t0, a.T, a.H, s_do, s_gam);
+    if constexpr (APPLY) stage_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(v, b, h, t0, a.T, a.H, s_v, s_gam);
     __syncthreads();
 
     // Gam at this wave's dq/dk output positions (diagonal), before the region is reused
@@ -157,8 +159,8 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
         for (int I = 0; I < 4; ++I)
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
-            const int d = 16 * (w + NWAVE * cc) + 4 * g + rr;
-            gq[cc][I][rr] = (w + NWAVE * cc < G::NKT && d < DK) ? s_gam[(16 * I + i16) * DK + d] : 0.f;
+            const int d = 16 * (w + G::NW * cc) + 4 * g + rr;
+            gq[cc][I][rr] = (w + G::NW * cc < G::NKT && d < DK) ? s_gam[(16 * I + i16) * DK + d] : 0.f;
           }
       __syncthreads();
     }
@@ -166,8 +168,9 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
     if constexpr (APPLY) {
       // ---- scores and score gradients (hi/lo) for the wave's tiles -------------------
 #pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        const int idx = score_tile(w, s);
+      for (int s = 0; s < (N_SCORE_TILES + G::NW - 1) / G::NW; ++s) {
+        if (s * G::NW + w >= N_SCORE_TILES) continue;
+        const int idx = score_tile(s * G::NW + w);
         const int I = idx >> 2, J = idx & 3;
         f32x4 xa = {0.f, 0.f, 0.f, 0.f}, xd = {0.f, 0.f, 0.f, 0.f};
         if (!score_tile_zero(idx)) {
@@ -217,7 +220,7 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
       E* dvp = reinterpret_cast<E*>(a.dv);
 #pragma unroll
       for (int cc = 0; cc < G::CPWV; ++cc) {
-        const int cn = w + NWAVE * cc;
+        const int cn = w + G::NW * cc;
         if (cn >= G::NVT) continue;
         Frag<E> fs[G::DKP / 32], fsl[G::DKP / 32];
 #pragma unroll
@@ -227,8 +230,8 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int d0 = 32 * kb + 4 * g + rr, d1 = d0 + 16;
-              lo[rr] *= d0 < DK ? __expf(s_glast[d0]) : 0.f;
-              hi[rr] *= d1 < DK ? __expf(s_glast[d1]) : 0.f;
+              lo[rr] *= d0 < DK ? s_el[d0] : 0.f;
+              hi[rr] *= d1 < DK ? s_el[d1] : 0.f;
             }
           }
           acc_to_frag_split(fs[kb], fsl[kb], lo, hi);
@@ -274,16 +277,17 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
       f32x4 wv[G::CPWK][4], zv[G::CPWK][4];                                 // diagonal: dg parts
 #pragma unroll
       for (int cc = 0; cc < G::CPWK; ++cc) {
-        const int cm = w + NWAVE * cc;
+        const int cm = w + G::NW * cc;
         if (cm >= G::NKT) continue;
         const int dl = 16 * cm + i16;        // lane-fixed key dim of the S0 / dS^T fragments
-        // S0 and dS^T fragments over d_v in the permuted order {32kn + 4g + e, 32kn + 16 + 4g + e}
-        Frag<E> fs0[G::DVP / 32], fs0l[G::DVP / 32], fdt[G::DVP / 32], fdtl[G::DVP / 32];
+        // S0 over d_v in the permuted order {32kn + 4g + e, 32kn + 16 + 4g + e}; the
+        // dS^T accumulators hold the same positions, so T3 is an elementwise product
         float t3 = 0.f;
-        const float eL = (DIAG && dl < DK) ? __expf(s_glast[dl]) : 1.f;
+        const float eL = (DIAG && dl < DK) ? s_el[dl] : 1.f;
+        Frag<E> fs0[G::DVP / 32], fs0l[G::DVP / 32];
 #pragma unroll
         for (int kn = 0; kn < G::DVP / 32; ++kn) {
-          float x[8], y[8];
+          float x[8];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int n0 = 32 * kn + 16 * hh + 4 * g;
@@ -293,12 +297,10 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               x[4 * hh + e] = sv[e];
-              y[4 * hh + e] = tv[e] * eL;
               t3 += sv[e] * tv[e];
             }
           }
           split_frag(fs0[kn], fs0l[kn], x);
-          split_frag(fdt[kn], fdtl[kn], y);
         }
         if constexpr (HAS_DG) {
           t3 += __shfl_xor(t3, 16, 64);
@@ -309,15 +311,11 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
             if (g == 0) t3p += t3;
           }
         }
-        Frag<E> fkt[2], fktl[2], fqt[2], fqtl[2];
+        Frag<E> fkt[2], fktl[2];
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
           frag_tr(fkt[jb], s_k, G::LDK, 32 * jb, 16 * cm);
-          frag_tr(fqt[jb], s_q, G::LDK, 32 * jb, 16 * cm);
-          if constexpr (DIAG && SP) {
-            frag_tr(fktl[jb], s_kl, G::LDK, 32 * jb, 16 * cm);
-            frag_tr(fqtl[jb], s_ql, G::LDK, 32 * jb, 16 * cm);
-          }
+          if constexpr (DIAG && SP) frag_tr(fktl[jb], s_kl, G::LDK, 32 * jb, 16 * cm);
         }
         // dq^T
 #pragma unroll
@@ -358,7 +356,23 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
           }
           if (d0 < DK) store4(dqp + tok_off(b, t0 + ti, h, a.T, a.H, DK) + d0, acc);
         }
-        // dk^T
+        // dk^T: dS^T (scaled by exp(Gam_last[d]) for a diagonal decay) as split fragments
+        Frag<E> fdt[G::DVP / 32], fdtl[G::DVP / 32], fqt[2], fqtl[2];
+#pragma unroll
+        for (int kn = 0; kn < G::DVP / 32; ++kn) {
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            y[e] = dT[2 * kn][cc][e] * eL;
+            y[4 + e] = dT[2 * kn + 1][cc][e] * eL;
+          }
+          split_frag(fdt[kn], fdtl[kn], y);
+        }
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+          frag_tr(fqt[jb], s_q, G::LDK, 32 * jb, 16 * cm);
+          if constexpr (DIAG && SP) frag_tr(fqtl[jb], s_ql, G::LDK, 32 * jb, 16 * cm);
+        }
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
           const int tj = 16 * J + i16;
@@ -407,7 +421,7 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
         __syncthreads();  // s_t3 complete
 #pragma unroll
         for (int cc = 0; cc < G::CPWK; ++cc) {
-          const int cm = w + NWAVE * cc;
+          const int cm = w + G::NW * cc;
           if (cm >= G::NKT) continue;
           const int d0 = 16 * cm + 4 * g;
           f32x4 t3v;
@@ -480,7 +494,7 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
           const int t = l;
           float u1 = 0.f, u4 = 0.f;
 #pragma unroll
-          for (int ww = 0; ww < NWAVE; ++ww) {
+          for (int ww = 0; ww < G::NW; ++ww) {
             u1 += s_u1[ww * CH + t];
             u4 += s_u4[ww * CH + t];
           }
@@ -502,7 +516,10 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
             if (t >= off) y4 += y;
           }
           y4 -= u4;
-          const float t3 = keep * __expf(s_gam[CH - 1]) * (s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+          float t3s = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < G::NW; ++ww) t3s += s_red[ww];
+          const float t3 = keep * __expf(s_gam[CH - 1]) * t3s;
           float dgv = x + y4 + t3;
           if ((seg.starts >> t) & 1ull) dgv = 0.f;
           a.dg[(b * a.T + t0 + t) * a.H + h] = dgv;
@@ -519,7 +536,7 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
         for (int rr = 0; rr < 4; ++rr) {
           const int d = 16 * m + 4 * g + rr;
           float f = keep;
-          if constexpr (DIAG) f = d < DK ? keep * __expf(s_glast[d]) : 0.f;
+          if constexpr (DIAG) f = d < DK ? keep * s_el[d] : 0.f;
           if constexpr (SCAL) f = keep * __expf(s_gam[CH - 1]);
 #pragma unroll
           for (int cc = 0; cc < G::CPWV; ++cc) dS[m][cc][rr] *= f;
@@ -527,9 +544,9 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
       if constexpr (APPLY) {
 #pragma unroll
         for (int cc = 0; cc < G::CPWK; ++cc) {
-          const int d = 16 * (w + NWAVE * cc) + i16;
+          const int d = 16 * (w + G::NW * cc) + i16;
           float f = keep;
-          if constexpr (DIAG) f = d < DK ? keep * __expf(s_glast[d]) : 0.f;
+          if constexpr (DIAG) f = d < DK ? keep * s_el[d] : 0.f;
           if constexpr (SCAL) f = keep * __expf(s_gam[CH - 1]);
 #pragma unroll
           for (int nt = 0; nt < G::NVT; ++nt) dT[nt][cc] *= f;
@@ -542,7 +559,7 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
         Frag<E> fdo[G::CPWV];
 #pragma unroll
         for (int cc = 0; cc < G::CPWV; ++cc) {
-          const int cn = w + NWAVE * cc;
+          const int cn = w + G::NW * cc;
           if (cn < G::NVT) frag_tr(fdo[cc], s_do, G::LDV, 32 * kb, 16 * cn);
         }
         Frag<E> fdoa[APPLY ? G::NVT : 1];
@@ -562,7 +579,7 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
           }
 #pragma unroll
           for (int cc = 0; cc < G::CPWV; ++cc)
-            if (w + NWAVE * cc < G::NVT) {
+            if (w + G::NW * cc < G::NVT) {
               if constexpr (SP && (DIAG || SCAL)) mma2a(dS[m][cc], fa, fal, fdo[cc]);
               else mma(dS[m][cc], fa, fdo[cc]);
             }
@@ -570,7 +587,7 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
             // dS^T columns owned by this wave: d tile m == w + 4 cc
 #pragma unroll
             for (int cc = 0; cc < G::CPWK; ++cc)
-              if (m == w + NWAVE * cc) {
+              if (m == w + G::NW * cc) {
 #pragma unroll
                 for (int nt = 0; nt < G::NVT; ++nt) {
                   if constexpr (SP && (DIAG || SCAL)) mma2b(dT[nt][cc], fdoa[nt], fa, fal);
@@ -600,7 +617,7 @@ __global__ __launch_bounds__(NTHR) void bwd_walk(BwdArgs a) {
     for (int m = 0; m < G::NKT; ++m)
 #pragma unroll
       for (int cc = 0; cc < G::CPWV; ++cc) {
-        const int cn = w + NWAVE * cc;
+        const int cn = w + G::NW * cc;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int d = 16 * m + 4 * g + rr, n = 16 * cn + i16;

@@ -27,19 +27,23 @@ struct Geo {
   static constexpr int LDA = CH + PAD;            // LDS row stride of 64x64 tiles
   static constexpr int NKT = DKP / 16;            // 16-wide tiles along dk
   static constexpr int NVT = DVP / 16;
-  static constexpr int CPWK = (NKT + NWAVE - 1) / NWAVE;  // dk tiles owned per wave
-  static constexpr int CPWV = (NVT + NWAVE - 1) / NWAVE;
+  static constexpr int NW = waves_for(DKP);       // waves per workgroup
+  static constexpr int NT = 64 * NW;              // threads per workgroup
+  static constexpr int CPWK = (NKT + NW - 1) / NW;  // dk tiles owned per wave
+  static constexpr int CPWV = (NVT + NW - 1) / NW;
   static constexpr int TILE_K = CH * LDK;         // elements
   static constexpr int TILE_V = CH * LDV;
   static constexpr int TILE_A = CH * LDA;
 };
 
-// Score tiles (I, J) of the 64x64 lower triangle handed to each wave; index
-// I*4 + J. Entries 1 = (0,1) and 11 = (2,3) are upper tiles that are read by
-// 32-deep token contractions and must hold zeros.
-__device__ __forceinline__ int score_tile(int w, int s) {
-  constexpr int T[4][3] = {{0, 9, 14}, {4, 10, 15}, {5, 12, 1}, {8, 13, 11}};
-  return T[w][s];
+// Score tiles (I, J) of the 64x64 lower triangle, index I*4 + J, dealt round
+// robin to the waves: wave w takes entries w, w + NW, ... of this list. Entries
+// 1 = (0,1) and 11 = (2,3) are upper tiles that are read by 32-deep token
+// contractions and must hold zeros.
+constexpr int N_SCORE_TILES = 12;
+__device__ __forceinline__ int score_tile(int k) {
+  constexpr int T[N_SCORE_TILES] = {0, 4, 5, 8, 9, 10, 12, 13, 14, 15, 1, 11};
+  return T[k];
 }
 __device__ __forceinline__ bool score_tile_zero(int idx) { return idx == 1 || idx == 11; }
 
@@ -53,8 +57,8 @@ __device__ __forceinline__ int64_t tok_off(int64_t b, int64_t t, int64_t h, int6
 // Then the per-token factors
 //   fq[i] = live_i * (scalar ? exp(Gam_i) : 1)
 //   fk[j] = tail_j * (scalar ? exp(Gam_last - Gam_j) : 1)
-// `red` is NTHR floats of scratch. Ends with a barrier.
-template <int DK, int DECAY>
+// `red` is NT floats of scratch. Ends with a barrier.
+template <int DK, int DECAY, int NT>
 __device__ __forceinline__ void stage_gamma(const float* __restrict__ g, int64_t b, int64_t h, int64_t t0,
                                             int64_t T, int64_t H, const ChunkSeg& seg,
                                             float* gam, float* fq, float* fk, float* red) {
@@ -74,7 +78,7 @@ __device__ __forceinline__ void stage_gamma(const float* __restrict__ g, int64_t
     }
   } else {
     if constexpr (DECAY == DECAY_DIAG) {
-      constexpr int TPC = NTHR / DK;       // threads per key column
+      constexpr int TPC = NT / DK;         // threads per key column
       constexpr int TOK = CH / TPC;        // tokens per thread
       const int d = tid % DK, part = tid / DK;
       float v[TOK];
@@ -101,14 +105,14 @@ __device__ __forceinline__ void stage_gamma(const float* __restrict__ g, int64_t
 // Stage a [64][D] token-major tile of the input into LDS (row stride LD),
 // zero-filling columns D..DP-1. MODE 0: copy; 1: multiply by exp(Gam[i][d]);
 // 2: multiply by exp(-Gam[i][d]) (diagonal decay only). No barrier.
-template <typename E, int D, int DP, int LD, int MODE, int DK>
+template <typename E, int D, int DP, int LD, int MODE, int DK, int NT>
 __device__ __forceinline__ void stage_tile(const E* __restrict__ src, int64_t b, int64_t h, int64_t t0,
                                            int64_t T, int64_t H, E* dst, const float* gam) {
   constexpr int VEC = 16 / (int)sizeof(E);   // elements per 16-byte load
   constexpr int VPR = D / VEC;               // vectors per row
   constexpr int NV = CH * VPR;
   const int tid = threadIdx.x;
-  for (int v = tid; v < NV; v += NTHR) {
+  for (int v = tid; v < NV; v += NT) {
     const int i = v / VPR, c = (v % VPR) * VEC;
     const E* s = src + tok_off(b, t0 + i, h, T, H, D) + c;
     E* d = dst + i * LD + c;
@@ -135,7 +139,7 @@ __device__ __forceinline__ void stage_tile(const E* __restrict__ src, int64_t b,
     }
   }
   if constexpr (DP > D) {
-    for (int v = tid; v < CH * (DP - D); v += NTHR) {
+    for (int v = tid; v < CH * (DP - D); v += NT) {
       const int i = v / (DP - D), c = D + v % (DP - D);
       dst[i * LD + c] = to_e<E>(0.f);
     }
@@ -144,7 +148,7 @@ __device__ __forceinline__ void stage_tile(const E* __restrict__ src, int64_t b,
 
 // Stage a [64][D] tile as split hi/lo parts (lo skipped for fp32). MODE 1:
 // x * exp(Gam[i][d]); 2: x * exp(-Gam[i][d]) (diagonal decay); 3: x * fac[i]. No barrier.
-template <typename E, int D, int DP, int LD, int MODE, int DK>
+template <typename E, int D, int DP, int LD, int MODE, int DK, int NT>
 __device__ __forceinline__ void stage_tile_split(const E* __restrict__ src, int64_t b, int64_t h, int64_t t0,
                                                  int64_t T, int64_t H, E* hi, E* lo, const float* gam,
                                                  const float* fac) {
@@ -152,7 +156,7 @@ __device__ __forceinline__ void stage_tile_split(const E* __restrict__ src, int6
   constexpr int VPR = D / VEC;
   constexpr int NV = CH * VPR;
   const int tid = threadIdx.x;
-  for (int v = tid; v < NV; v += NTHR) {
+  for (int v = tid; v < NV; v += NT) {
     const int i = v / VPR, c = (v % VPR) * VEC;
     const E* s = src + tok_off(b, t0 + i, h, T, H, D) + c;
     float x[VEC];
@@ -185,7 +189,7 @@ __device__ __forceinline__ void stage_tile_split(const E* __restrict__ src, int6
     }
   }
   if constexpr (DP > D) {
-    for (int v = tid; v < CH * (DP - D); v += NTHR) {
+    for (int v = tid; v < CH * (DP - D); v += NT) {
       const int i = v / (DP - D), c = D + v % (DP - D);
       hi[i * LD + c] = to_e<E>(0.f);
       if constexpr (sizeof(E) == 2) lo[i * LD + c] = to_e<E>(0.f);

@@ -26,8 +26,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;      // chunk length (tokens)
-constexpr int NWAVE = 4;    // waves per workgroup
-constexpr int NTHR = 256;   // threads per workgroup
+// Waves per workgroup for a (padded) head size: 8 at 128 (two per SIMD, so one
+// wave's memory or LDS wait overlaps the other's work), 4 below.
+constexpr int waves_for(int dpad) { return dpad >= 128 ? 8 : 4; }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }

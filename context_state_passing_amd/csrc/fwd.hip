@@ -20,7 +20,8 @@ namespace cpla {
 // K^ = K exp(Gam_last - Gam) tail enters the MFMA split into hi + lo parts.
 template <typename E, int DK, int DV, int DECAY, int NKT_, int CPWV_>
 __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* Kt, const E* Ktl, const E* Vt,
-                                             const float* gam, const float* fk, const ChunkSeg& seg) {
+                                             const float* gam, const float* el, const float* fk,
+                                             const ChunkSeg& seg) {
   using G = Geo<E, DK, DV>;
   const int w = wave_id(), l = lane_id(), g = l >> 4;
   const float keep = seg.any() ? 0.f : 1.f;
@@ -41,7 +42,7 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* K
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int cc = 0; cc < G::CPWV; ++cc) {
-      const int c = w + NWAVE * cc;
+      const int c = w + G::NW * cc;
       if (c < G::NVT) frag_tr(bv[kb][cc], Vt, G::LDV, 32 * kb, 16 * c);
     }
   const bool scale_tok = (DECAY == DECAY_SCALAR) || seg.any();
@@ -68,7 +69,7 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* K
       }
 #pragma unroll
       for (int cc = 0; cc < G::CPWV; ++cc)
-        if (w + NWAVE * cc < G::NVT) {
+        if (w + G::NW * cc < G::NVT) {
           if constexpr (DECAY == DECAY_NONE || !Split<E>::on) mma(S[m][cc], a, bv[kb][cc]);
           else mma2a(S[m][cc], a, al, bv[kb][cc]);
         }
@@ -81,7 +82,7 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* K
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int d = 16 * m + 4 * g + r;
-        const float f = d < DK ? __expf(gam[(CH - 1) * DK + d]) : 0.f;
+        const float f = d < DK ? el[d] : 0.f;
 #pragma unroll
         for (int cc = 0; cc < G::CPWV; ++cc) S[m][cc][r] *= f;
       }
@@ -89,7 +90,7 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* K
 }
 
 template <typename E, int DK, int DV, int DECAY, bool APPLY>
-__global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
+__global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
   using G = Geo<E, DK, DV>;
   constexpr int GAM = (DECAY == DECAY_DIAG) ? CH * DK : CH;
   constexpr int NQT = APPLY ? 1 : 0;
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
   constexpr int NAL = (APPLY && Split<E>::on) ? 1 : 0;
   __shared__ __attribute__((aligned(16))) E s_a[NQT * G::TILE_A + 8];    // scores, hi part
   __shared__ __attribute__((aligned(16))) E s_al[NAL * G::TILE_A + 8];   // scores, lo part
-  __shared__ float s_gam[GAM], s_fq[CH], s_fk[CH], s_red[NTHR];
+  __shared__ float s_gam[GAM], s_fq[CH], s_fk[CH], s_red[G::NT], s_el[G::DKP];
 
   const int w = wave_id(), l = lane_id(), g = l >> 4, i16 = l & 15;
   const int r = a.rank_begin + blockIdx.x;
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
   for (int m = 0; m < G::NKT; ++m)
 #pragma unroll
     for (int cc = 0; cc < G::CPWV; ++cc) {
-      const int c = w + NWAVE * cc;
+      const int c = w + G::NW * cc;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         float x = 0.f;
@@ -138,19 +139,23 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
     const int64_t t0 = tshard + (int64_t)c * CH;
     const ChunkSeg seg = chunk_seg(a.seq_idx, t0);
     any_start |= seg.any();
-    stage_gamma<DK, DECAY>(a.g, b, h, t0, a.T, a.H, seg, s_gam, s_fq, s_fk, s_red);
+    stage_gamma<DK, DECAY, G::NT>(a.g, b, h, t0, a.T, a.H, seg, s_gam, s_fq, s_fk, s_red);
     if constexpr (DECAY == DECAY_DIAG) {
-      if (threadIdx.x < DK) gsum += s_gam[(CH - 1) * DK + threadIdx.x];
-      stage_tile_split<E, DK, G::DKP, G::LDK, 2, DK>(k, b, h, t0, a.T, a.H, s_k, s_kl, s_gam, nullptr);
+      if (threadIdx.x < DK) {
+        const float gl = s_gam[(CH - 1) * DK + threadIdx.x];
+        gsum += gl;
+        s_el[threadIdx.x] = __expf(gl);   // exp(Gam_last[d]) for the state's row scaling
+      }
+      stage_tile_split<E, DK, G::DKP, G::LDK, 2, DK, G::NT>(k, b, h, t0, a.T, a.H, s_k, s_kl, s_gam, nullptr);
       if constexpr (APPLY)
-        stage_tile_split<E, DK, G::DKP, G::LDK, 1, DK>(q, b, h, t0, a.T, a.H, s_q, s_ql, s_gam, nullptr);
+        stage_tile_split<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(q, b, h, t0, a.T, a.H, s_q, s_ql, s_gam, nullptr);
     } else {
       if constexpr (DECAY == DECAY_SCALAR)
         if (threadIdx.x == 0) gsum += s_gam[CH - 1];
-      stage_tile<E, DK, G::DKP, G::LDK, 0, DK>(k, b, h, t0, a.T, a.H, s_k, s_gam);
-      if constexpr (APPLY) stage_tile<E, DK, G::DKP, G::LDK, 0, DK>(q, b, h, t0, a.T, a.H, s_q, s_gam);
+      stage_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(k, b, h, t0, a.T, a.H, s_k, s_gam);
+      if constexpr (APPLY) stage_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(q, b, h, t0, a.T, a.H, s_q, s_gam);
     }
-    stage_tile<E, DV, G::DVP, G::LDV, 0, DK>(v, b, h, t0, a.T, a.H, s_v, s_gam);
+    stage_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(v, b, h, t0, a.T, a.H, s_v, s_gam);
 
     if constexpr (APPLY) {
       if (a.chunk_states) {
@@ -159,7 +164,7 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
         for (int m = 0; m < G::NKT; ++m)
 #pragma unroll
           for (int cc = 0; cc < G::CPWV; ++cc) {
-            const int cn = w + NWAVE * cc;
+            const int cn = w + G::NW * cc;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int d = 16 * m + 4 * g + rr, n = 16 * cn + i16;
@@ -173,8 +178,9 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
     if constexpr (APPLY) {
       // ---- scores -> s_a (E), masked and decayed --------------------------------
 #pragma unroll
-      for (int s = 0; s < 3; ++s) {
-        const int idx = score_tile(w, s);
+      for (int s = 0; s < (N_SCORE_TILES + G::NW - 1) / G::NW; ++s) {
+        if (s * G::NW + w >= N_SCORE_TILES) continue;
+        const int idx = score_tile(s * G::NW + w);
         const int I = idx >> 2, J = idx & 3;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (!score_tile_zero(idx)) {
@@ -209,7 +215,7 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
       E* o = reinterpret_cast<E*>(a.out);
 #pragma unroll
       for (int cc = 0; cc < G::CPWV; ++cc) {
-        const int cn = w + NWAVE * cc;
+        const int cn = w + G::NW * cc;
         if (cn >= G::NVT) continue;
         Frag<E> fs[G::DKP / 32], fsl[G::DKP / 32];
 #pragma unroll
@@ -247,7 +253,7 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
       }
     }
 
-    state_update<E, DK, DV, DECAY>(S, s_k, s_kl, s_v, s_gam, s_fk, seg);
+    state_update<E, DK, DV, DECAY>(S, s_k, s_kl, s_v, s_gam, s_el, s_fk, seg);
     __syncthreads();
   }
 
@@ -268,7 +274,7 @@ __global__ __launch_bounds__(NTHR) void fwd_walk(FwdArgs a) {
     for (int m = 0; m < G::NKT; ++m)
 #pragma unroll
       for (int cc = 0; cc < G::CPWV; ++cc) {
-        const int cn = w + NWAVE * cc;
+        const int cn = w + G::NW * cc;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int d = 16 * m + 4 * g + rr, n = 16 * cn + i16;
