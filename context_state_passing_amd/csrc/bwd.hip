@@ -122,12 +122,35 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
   float gsum = 0.f;
   bool any_start = false;
 
+  // prefetch registers for the next chunk's inputs (walk goes backwards)
+  SegRegs rseg;
+  GamRegs<DK, DECAY, G::NT> rgam;
+  TileRegs<E, DK, G::NT> rq;
+  TileRegs<E, DV, G::NT> rdo;
+  auto prefetch = [&](int c) {
+    const int64_t t = tshard + (int64_t)c * CH;
+    rseg.load(a.seq_idx, t);
+    rgam.load(a.g, b, h, t, a.T, a.H);
+    rq.load(q, b, h, t, a.T, a.H);
+    rdo.load(dO, b, h, t, a.T, a.H);
+  };
+  // The prepare walk overlaps the next chunk's loads with its compute; the apply
+  // walk is register-bound and stages each chunk straight from global memory.
+  if constexpr (!APPLY) prefetch(nc - 1);
+
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t t0 = tshard + (int64_t)c * CH;
-    const ChunkSeg seg = chunk_seg(a.seq_idx, t0);
+    ChunkSeg seg;
+    if constexpr (APPLY) {
+      // direct global -> LDS staging (the apply walk has no registers to spare)
+      seg = chunk_seg(a.seq_idx, t0);
+      stage_gamma<DK, DECAY, G::NT>(a.g, b, h, t0, a.T, a.H, seg, s_gam, s_fq, s_fk, s_red);
+    } else {
+      seg = rseg.finish(a.seq_idx);
+      finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk, s_red);
+    }
     any_start |= seg.any();
     const float keep = seg.any() ? 0.f : 1.f;
-    stage_gamma<DK, DECAY, G::NT>(a.g, b, h, t0, a.T, a.H, seg, s_gam, s_fq, s_fk, s_red);
 
     // ---- stage tiles ----------------------------------------------------------------
     if constexpr (DIAG) {
@@ -136,19 +159,30 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
         gsum += gl;
         s_el[threadIdx.x] = __expf(gl);   // exp(Gam_last[d]), read by every row scaling below
       }
-      stage_tile_split<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(q, b, h, t0, a.T, a.H, s_q, s_ql, s_gam, nullptr);
-      if constexpr (APPLY) stage_tile_split<E, DK, G::DKP, G::LDK, 2, DK, G::NT>(k, b, h, t0, a.T, a.H, s_k, s_kl, s_gam, nullptr);
-    } else {
-      if constexpr (SCAL) {
-        if (threadIdx.x == 0) gsum += s_gam[CH - 1];
-        stage_tile_split<E, DK, G::DKP, G::LDK, 3, DK, G::NT>(q, b, h, t0, a.T, a.H, s_qh, s_qhl, s_gam, s_fq);
-      }
-      if constexpr (APPLY || !SCAL) stage_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(q, b, h, t0, a.T, a.H, s_q, s_gam);
-      if constexpr (APPLY) stage_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(k, b, h, t0, a.T, a.H, s_k, s_gam);
+    } else if constexpr (SCAL) {
+      if (threadIdx.x == 0) gsum += s_gam[CH - 1];
     }
-    stage_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(dO, b, h, t0, a.T, a.H, s_do, s_gam);
-    if constexpr (APPLY) stage_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(v, b, h, t0, a.T, a.H, s_v, s_gam);
+    if constexpr (APPLY) {
+      if constexpr (DIAG) {
+        stage_tile_split<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(q, b, h, t0, a.T, a.H, s_q, s_ql, s_gam, nullptr);
+        stage_tile_split<E, DK, G::DKP, G::LDK, 2, DK, G::NT>(k, b, h, t0, a.T, a.H, s_k, s_kl, s_gam, nullptr);
+      } else {
+        if constexpr (SCAL)
+          stage_tile_split<E, DK, G::DKP, G::LDK, 3, DK, G::NT>(q, b, h, t0, a.T, a.H, s_qh, s_qhl, s_gam, s_fq);
+        stage_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(q, b, h, t0, a.T, a.H, s_q, s_gam);
+        stage_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(k, b, h, t0, a.T, a.H, s_k, s_gam);
+      }
+      stage_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(dO, b, h, t0, a.T, a.H, s_do, s_gam);
+      stage_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(v, b, h, t0, a.T, a.H, s_v, s_gam);
+    } else {
+      if constexpr (DIAG) store_tile<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(rq, s_q, s_ql, s_gam, nullptr);
+      else if constexpr (SCAL) store_tile<E, DK, G::DKP, G::LDK, 3, DK, G::NT>(rq, s_qh, s_qhl, s_gam, s_fq);
+      else store_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(rq, s_q, nullptr, s_gam, nullptr);
+      store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(rdo, s_do, nullptr, s_gam, nullptr);
+    }
     __syncthreads();
+    if constexpr (!APPLY)
+      if (c > 0) prefetch(c - 1);
 
     // Gam at this wave's dq/dk output positions (diagonal), before the region is reused
     float gq[G::CPWK][4][4];

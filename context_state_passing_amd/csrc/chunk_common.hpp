@@ -197,6 +197,164 @@ __device__ __forceinline__ void stage_tile_split(const E* __restrict__ src, int6
   }
 }
 
+// ---- register prefetch ------------------------------------------------------------
+// A walk issues the next chunk's global loads into these registers before it
+// computes the current chunk, and writes them to LDS afterwards, so HBM latency
+// overlaps MFMA and LDS work instead of stalling every chunk.
+
+// Sequence ids of the chunk's tokens (packed sequences): one token per lane.
+struct SegRegs {
+  int cur, prev;
+  __device__ __forceinline__ void load(const int32_t* seq_idx, int64_t t0) {
+    if (!seq_idx) return;
+    const int64_t t = t0 + lane_id();
+    cur = seq_idx[t];
+    prev = t > 0 ? seq_idx[t - 1] : cur - 1;
+  }
+  __device__ __forceinline__ ChunkSeg finish(const int32_t* seq_idx) const {
+    ChunkSeg s;
+    s.starts = seq_idx ? (uint64_t)__ballot(cur != prev) : 0ull;
+    return s;
+  }
+};
+
+// Log-decays of one chunk: diagonal -> thread (d = tid % DK, part = tid / DK)
+// holds TOK consecutive tokens of key column d; scalar -> thread tid < 64 holds
+// token tid.
+template <int DK, int DECAY, int NT>
+struct GamRegs {
+  static constexpr int TPC = (DECAY == DECAY_DIAG) ? NT / DK : 1;
+  static constexpr int TOK = (DECAY == DECAY_DIAG) ? CH / TPC : 1;
+  float v[TOK];
+  __device__ __forceinline__ void load(const float* __restrict__ g, int64_t b, int64_t h, int64_t t0, int64_t T,
+                                       int64_t H) {
+    const int tid = threadIdx.x;
+    if constexpr (DECAY == DECAY_DIAG) {
+      const int d = tid % DK, part = tid / DK;
+      const float* src = g + ((b * T + t0 + part * TOK) * H + h) * DK + d;
+#pragma unroll
+      for (int s = 0; s < TOK; ++s) v[s] = src[(int64_t)s * H * DK];
+    } else if constexpr (DECAY == DECAY_SCALAR) {
+      if (tid < CH) v[0] = g[(b * T + t0 + tid) * H + h];
+    }
+  }
+};
+
+// Cumulative log-decay and per-token factors from prefetched registers (same
+// outputs as stage_gamma). Ends with a barrier.
+template <int DK, int DECAY, int NT>
+__device__ __forceinline__ void finish_gamma(GamRegs<DK, DECAY, NT>& R, const ChunkSeg& seg, float* gam,
+                                             float* fq, float* fk, float* red) {
+  const int tid = threadIdx.x;
+  if constexpr (DECAY == DECAY_SCALAR) {
+    if (tid < CH) {
+      float x = R.v[0];
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (tid >= off) x += y;
+      }
+      gam[tid] = x;
+      const float last = __shfl(x, 63, 64);
+      fq[tid] = seg.live(tid) ? __expf(x) : 0.f;
+      fk[tid] = seg.tail(tid) ? __expf(last - x) : 0.f;
+    }
+  } else {
+    if constexpr (DECAY == DECAY_DIAG) {
+      constexpr int TOK = GamRegs<DK, DECAY, NT>::TOK;
+      const int d = tid % DK, part = tid / DK;
+#pragma unroll
+      for (int s = 1; s < TOK; ++s) R.v[s] += R.v[s - 1];
+      red[part * DK + d] = R.v[TOK - 1];
+      __syncthreads();
+      float off = 0.f;
+      for (int pp = 0; pp < part; ++pp) off += red[pp * DK + d];
+#pragma unroll
+      for (int s = 0; s < TOK; ++s) gam[(part * TOK + s) * DK + d] = R.v[s] + off;
+    }
+    if (tid < CH) {
+      fq[tid] = seg.live(tid) ? 1.f : 0.f;
+      fk[tid] = seg.tail(tid) ? 1.f : 0.f;
+    }
+  }
+  __syncthreads();
+}
+
+// One [64][D] input tile as raw 16-byte vectors, dealt round robin to threads.
+template <typename E, int D, int NT>
+struct TileRegs {
+  static constexpr int VEC = 16 / (int)sizeof(E);
+  static constexpr int VPR = D / VEC;
+  static constexpr int NV = CH * VPR;
+  static constexpr int PER = (NV + NT - 1) / NT;
+  f32x4 r[PER];
+  __device__ __forceinline__ void load(const E* __restrict__ src, int64_t b, int64_t h, int64_t t0, int64_t T,
+                                       int64_t H) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int v = threadIdx.x + p * NT;
+      if (v < NV) {
+        const int i = v / VPR, c = (v % VPR) * VEC;
+        r[p] = *reinterpret_cast<const f32x4*>(src + tok_off(b, t0 + i, h, T, H, D) + c);
+      }
+    }
+  }
+};
+
+// Write prefetched vectors to LDS (row stride LD), zero-filling columns D..DP-1.
+// MODE 0: copy into `hi`; 1: x*exp(Gam[i][d]); 2: x*exp(-Gam[i][d]); 3: x*fac[i] --
+// scaled modes are stored split (hi, and lo for bf16). No barrier.
+template <typename E, int D, int DP, int LD, int MODE, int DK, int NT>
+__device__ __forceinline__ void store_tile(const TileRegs<E, D, NT>& R, E* hi, E* lo, const float* gam,
+                                           const float* fac) {
+  using TR = TileRegs<E, D, NT>;
+  constexpr int VEC = TR::VEC;
+#pragma unroll
+  for (int p = 0; p < TR::PER; ++p) {
+    const int v = threadIdx.x + p * NT;
+    if (v >= TR::NV) continue;
+    const int i = v / TR::VPR, c = (v % TR::VPR) * VEC;
+    if constexpr (MODE == 0) {
+      *reinterpret_cast<f32x4*>(hi + i * LD + c) = R.r[p];
+      continue;
+    }
+    float x[VEC];
+    if constexpr (sizeof(E) == 2) {
+      const bf16x8 y = __builtin_bit_cast(bf16x8, R.r[p]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = (float)y[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = R.r[p][e];
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if constexpr (MODE == 1) x[e] *= __expf(gam[i * DK + c + e]);
+      if constexpr (MODE == 2) x[e] *= __expf(-gam[i * DK + c + e]);
+      if constexpr (MODE == 3) x[e] *= fac[i];
+    }
+    if constexpr (sizeof(E) == 2) {
+      bf16x8 yh, yl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        yh[e] = (bf16_t)x[e];
+        yl[e] = (bf16_t)(x[e] - (float)yh[e]);
+      }
+      *reinterpret_cast<bf16x8*>(hi + i * LD + c) = yh;
+      *reinterpret_cast<bf16x8*>(lo + i * LD + c) = yl;
+    } else {
+      *reinterpret_cast<f32x4*>(hi + i * LD + c) = f32x4{x[0], x[1], x[2], x[3]};
+    }
+  }
+  if constexpr (DP > D) {
+    for (int v = threadIdx.x; v < CH * (DP - D); v += NT) {
+      const int i = v / (DP - D), c = D + v % (DP - D);
+      hi[i * LD + c] = to_e<E>(0.f);
+      if constexpr (MODE != 0 && sizeof(E) == 2) lo[i * LD + c] = to_e<E>(0.f);
+    }
+  }
+}
+
 // Multiply fragment slot e by fac[token(e)] (token-contracted operands).
 template <typename E>
 __device__ __forceinline__ void frag_scale_tokens(Frag<E>& f, const float* fac, int k0, bool perm) {

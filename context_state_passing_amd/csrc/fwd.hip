@@ -135,27 +135,42 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
   float gsum = 0.f;          // total log-decay of the shard (diag: column tid; else thread 0)
   bool any_start = false;
 
+  // prefetch registers for the next chunk's inputs
+  SegRegs rseg;
+  GamRegs<DK, DECAY, G::NT> rgam;
+  TileRegs<E, DK, G::NT> rk, rq;
+  TileRegs<E, DV, G::NT> rv;
+  auto prefetch = [&](int c) {
+    const int64_t t = tshard + (int64_t)c * CH;
+    rseg.load(a.seq_idx, t);
+    rgam.load(a.g, b, h, t, a.T, a.H);
+    rk.load(k, b, h, t, a.T, a.H);
+    if constexpr (APPLY) rq.load(q, b, h, t, a.T, a.H);
+    rv.load(v, b, h, t, a.T, a.H);
+  };
+  prefetch(0);
+
   for (int c = 0; c < nc; ++c) {
     const int64_t t0 = tshard + (int64_t)c * CH;
-    const ChunkSeg seg = chunk_seg(a.seq_idx, t0);
+    const ChunkSeg seg = rseg.finish(a.seq_idx);
     any_start |= seg.any();
-    stage_gamma<DK, DECAY, G::NT>(a.g, b, h, t0, a.T, a.H, seg, s_gam, s_fq, s_fk, s_red);
+    finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk, s_red);
     if constexpr (DECAY == DECAY_DIAG) {
       if (threadIdx.x < DK) {
         const float gl = s_gam[(CH - 1) * DK + threadIdx.x];
         gsum += gl;
         s_el[threadIdx.x] = __expf(gl);   // exp(Gam_last[d]) for the state's row scaling
       }
-      stage_tile_split<E, DK, G::DKP, G::LDK, 2, DK, G::NT>(k, b, h, t0, a.T, a.H, s_k, s_kl, s_gam, nullptr);
-      if constexpr (APPLY)
-        stage_tile_split<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(q, b, h, t0, a.T, a.H, s_q, s_ql, s_gam, nullptr);
+      store_tile<E, DK, G::DKP, G::LDK, 2, DK, G::NT>(rk, s_k, s_kl, s_gam, nullptr);
+      if constexpr (APPLY) store_tile<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(rq, s_q, s_ql, s_gam, nullptr);
     } else {
       if constexpr (DECAY == DECAY_SCALAR)
         if (threadIdx.x == 0) gsum += s_gam[CH - 1];
-      stage_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(k, b, h, t0, a.T, a.H, s_k, s_gam);
-      if constexpr (APPLY) stage_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(q, b, h, t0, a.T, a.H, s_q, s_gam);
+      store_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(rk, s_k, nullptr, s_gam, nullptr);
+      if constexpr (APPLY) store_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(rq, s_q, nullptr, s_gam, nullptr);
     }
-    stage_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(v, b, h, t0, a.T, a.H, s_v, s_gam);
+    store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(rv, s_v, nullptr, s_gam, nullptr);
+    if (c + 1 < nc) prefetch(c + 1);
 
     if constexpr (APPLY) {
       if (a.chunk_states) {

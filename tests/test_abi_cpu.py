@@ -1,0 +1,176 @@
+"""CPU tests of the C ABI: symbol exports, host-side validation (every case fails
+before any launch, so no GPU is touched), the packed-metadata builder against
+the oracle's brute-force twin (bit-exact), and product/oracle independence."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from context_state_passing_amd import _lib
+from context_state_passing_amd._lib import Packed, Problem
+import context_state_passing_amd as cpla
+from oracle import metadata as omd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = _lib.lib()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "cpla.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[\w\*]+\s+\**\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("typedef",)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = header_functions()
+    assert len(names) >= 11
+    assert sorted(names) == sorted(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version():
+    assert L.cpla_abi_version() == 1
+
+
+def prob(**kw):
+    base = dict(B=1, T=1024, H=2, dk=128, dv=128, num_shards=4, chunk=64, rank_begin=0, rank_end=4,
+                dtype=_lib.BF16, decay=_lib.DECAY_SCALAR)
+    base.update(kw)
+    return Problem(**base)
+
+
+FAKE = 0x10000            # aligned, never dereferenced: validation fails before any launch
+MISALIGNED = 0x10004
+
+
+def fwd_prepare(p, k=FAKE, v=FAKE, g=FAKE, out=FAKE, packed=None):
+    return L.cp_forward_prepare(ctypes.byref(p) if p is not None else None, packed, k, v, g, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(dtype=7), 3), (dict(decay=5), 1), (dict(chunk=32), 5),
+    (dict(T=1000), 2), (dict(T=1024, num_shards=8 * 3), 2), (dict(T=64 * 65, num_shards=65), 5),
+    (dict(rank_begin=2, rank_end=2), 1), (dict(rank_end=5), 1), (dict(dv=64), 5), (dict(dk=32, dv=32), 5),
+    (dict(dtype=_lib.F32), 5), (dict(num_shards=0), 2),
+])
+def test_problem_validation(kw, status):
+    assert fwd_prepare(prob(**kw)) == status
+    assert L.cpla_last_error()
+
+
+def test_pointer_validation():
+    p = prob()
+    assert fwd_prepare(None) == 1
+    assert fwd_prepare(p, k=None) == 1
+    assert fwd_prepare(p, v=MISALIGNED) == 4
+    assert fwd_prepare(p, g=None) == 1                              # scalar decay needs g
+    assert fwd_prepare(prob(decay=_lib.DECAY_NONE), g=FAKE) == 1     # no decay: g must be NULL
+    assert fwd_prepare(p, out=None) == 1
+    assert b"NULL" in L.cpla_last_error() or L.cpla_last_error()
+
+
+def test_packed_validation():
+    pk = Packed(FAKE, FAKE, FAKE)
+    assert fwd_prepare(prob(B=2), packed=ctypes.byref(pk)) == 2     # packed needs B == 1
+    assert fwd_prepare(prob(), packed=ctypes.byref(Packed(None, FAKE, FAKE))) == 1
+    p = prob()
+    # initial_state with packed sequences
+    st = L.cp_forward_apply(ctypes.byref(p), ctypes.byref(pk), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                            FAKE, FAKE, None)
+    assert st == 1
+    # d_final_state with packed sequences
+    st = L.cp_backward_apply(ctypes.byref(p), ctypes.byref(pk), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                             FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == 1
+
+
+def test_backward_requires_chunk_states_and_dg():
+    p = prob()
+    st = L.cp_backward_apply(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None,
+                             FAKE, FAKE, FAKE, FAKE, FAKE, None, None)
+    assert st == 1 and b"chunk_states" in L.cpla_last_error()
+    st = L.cp_backward_apply(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                             FAKE, FAKE, FAKE, None, FAKE, None, None)
+    assert st == 1 and b"dg" in L.cpla_last_error()
+
+
+def test_sizes():
+    p = prob(decay=_lib.DECAY_DIAG)
+    assert L.cpla_summary_width(ctypes.byref(p)) == 128 + 128 * 128
+    p = prob(decay=_lib.DECAY_SCALAR)
+    assert L.cpla_summary_width(ctypes.byref(p)) == 4 + 128 * 128
+    assert L.cpla_chunk_states_bytes(ctypes.byref(p)) == 1 * 2 * (1024 // 64) * 128 * 128 * 4
+
+
+# ---- packed metadata: C++ builder == oracle twin, bit-exact --------------------------------
+
+def random_stream(rng, T, lo, hi):
+    lens = []
+    while sum(lens) < T:
+        lens.append(int(rng.integers(lo, hi + 1)))
+    lens[-1] -= sum(lens) - T
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    return cu
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_metadata_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    T, P = 4096, 16
+    cu = random_stream(rng, T, [1, 128, 64][seed % 3], [300, 4096, 64][seed % 3])
+    s_c = cpla.seq_idx_from_cu_seqlens(cu, T)
+    s_o = omd.seq_idx_from_cu_seqlens(cu, T)
+    assert np.array_equal(s_c, s_o)
+    prs, frs = cpla.packed_rank_slices(s_c, P)
+    prs_o, frs_o = omd.rank_slices(s_o, P)
+    assert np.array_equal(prs, prs_o) and np.array_equal(frs, frs_o)
+    for r in range(P):
+        a = cpla.build_packed_sequence_cp_metadata(s_c, r, P)
+        b = omd.build_packed_sequence_cp_metadata(s_o, r, P)
+        assert np.array_equal(a["local_seq_idx"], b["local_seq_idx"])
+        assert np.array_equal(a["local_cu_seqlens"], b["local_cu_seqlens"])
+        assert a["preceding_rank_start"] == b["preceding_rank_start"]
+        assert a["following_rank_stop"] == b["following_rank_stop"]
+
+
+def test_metadata_edge_cases_match_oracle():
+    cases = [np.zeros(64, np.int32),                                 # one sequence everywhere
+             np.repeat(np.arange(4), 16).astype(np.int32),           # starts exactly at rank starts
+             np.arange(64).astype(np.int32),                         # every token its own sequence
+             np.concatenate([np.zeros(63), [1]]).astype(np.int32)]   # last sequence of length 1
+    for s in cases:
+        for r in range(4):
+            a = cpla.build_packed_sequence_cp_metadata(s, r, 4)
+            b = omd.build_packed_sequence_cp_metadata(s, r, 4)
+            for key in a:
+                assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("bad", [[1, 1, 1, 1], [0, 2, 2, 2], [0, 1, 0, 1], [0, 0, 0]])
+def test_metadata_rejects_malformed(bad):
+    with pytest.raises(cpla.CplaError) as e:
+        cpla.build_packed_sequence_cp_metadata(np.array(bad, np.int32), 0, 2)
+    assert e.value.status == 6
+
+
+def test_cu_seqlens_rejects_malformed():
+    with pytest.raises(cpla.CplaError):
+        cpla.seq_idx_from_cu_seqlens([0, 3, 3, 8], 8)
+    with pytest.raises(cpla.CplaError):
+        cpla.seq_idx_from_cu_seqlens([1, 8], 8)
+
+
+# ---- independence ------------------------------------------------------------------------
+
+def test_product_does_not_use_oracle():
+    pkg = os.path.join(ROOT, "context_state_passing_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), f
+                assert "oracle/" not in text, f
