@@ -42,7 +42,23 @@ def parse():
     ap.add_argument("--workload", default="diag_fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows (b,h) in the oracle sample (0 = auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device-to-device copy of known size: under rocprofv3 --pmc, its
+    FETCH_SIZE / WRITE_SIZE per dispatch divided by 1 GiB gives the scale that
+    turns those counters into bytes."""
+    import torch
+    n = (1 << 30) // 4
+    x = torch.randn(n, device="cuda:0")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "dispatches": 3}), flush=True)
 
 
 # ---- algorithmic counts (per token-head, chunk C, head size d) ------------------------
@@ -136,6 +152,9 @@ def cpu_baseline(wl, rows_req):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (got --gpus {args.gpus}); the multi-GPU "
               "summary exchange is not built", file=sys.stderr)

@@ -308,17 +308,24 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       const float* cs = a.chunk_states + ((bh * nct + t0 / CH) * DK) * (int64_t)DV;
       float u1p[4] = {0.f, 0.f, 0.f, 0.f}, u4p[4] = {0.f, 0.f, 0.f, 0.f};  // scalar: per-I token partials
       float t3p = 0.f;                                                      // scalar: T3 partial
-      f32x4 wv[G::CPWK][4], zv[G::CPWK][4];                                 // diagonal: dg parts
+      // diagonal dg: wv holds w_t = Q~*(dq before exp(Gam)) - K~*(intra dk) after the dq
+      // loop, then r_t = z_t - w_t with z_t = K~*(tail Y'); dg_t = sum_s w_s + T3 +
+      // sum_{s<t} r_s (suffix sums of w plus prefix sums of z, rearranged)
+      f32x4 wv[G::CPWK][4], wtot[G::CPWK];
 #pragma unroll
       for (int cc = 0; cc < G::CPWK; ++cc) {
         const int cm = w + G::NW * cc;
         if (cm >= G::NKT) continue;
         const int dl = 16 * cm + i16;        // lane-fixed key dim of the S0 / dS^T fragments
-        // S0 over d_v in the permuted order {32kn + 4g + e, 32kn + 16 + 4g + e}; the
-        // dS^T accumulators hold the same positions, so T3 is an elementwise product
+        // X^T = S0 dO^T for the four token blocks, contracting over d_v in 32-wide
+        // steps (outer) so only one split S0 fragment is live at a time. S0 is read
+        // in the permuted order {32kn + 4g + e, 32kn + 16 + 4g + e}, the positions the
+        // dS^T accumulators hold, so T3 is an elementwise product on the way.
         float t3 = 0.f;
         const float eL = (DIAG && dl < DK) ? s_el[dl] : 1.f;
-        Frag<E> fs0[G::DVP / 32], fs0l[G::DVP / 32];
+        f32x4 ax[4];
+#pragma unroll
+        for (int I = 0; I < 4; ++I) ax[I] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kn = 0; kn < G::DVP / 32; ++kn) {
           float x[8];
@@ -334,7 +341,14 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
               t3 += sv[e] * tv[e];
             }
           }
-          split_frag(fs0[kn], fs0l[kn], x);
+          Frag<E> fs0, fs0l;
+          split_frag(fs0, fs0l, x);
+#pragma unroll
+          for (int I = 0; I < 4; ++I) {
+            Frag<E> fb;
+            frag_direct_perm(fb, s_do, G::LDV, 16 * I + i16, 32 * kn);
+            mma2a(ax[I], fs0, fs0l, fb);
+          }
         }
         if constexpr (HAS_DG) {
           t3 += __shfl_xor(t3, 16, 64);
@@ -345,53 +359,52 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
             if (g == 0) t3p += t3;
           }
         }
-        Frag<E> fkt[2], fktl[2];
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-          frag_tr(fkt[jb], s_k, G::LDK, 32 * jb, 16 * cm);
-          if constexpr (DIAG && SP) frag_tr(fktl[jb], s_kl, G::LDK, 32 * jb, 16 * cm);
-        }
-        // dq^T
-#pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          const int ti = 16 * I + i16;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kn = 0; kn < G::DVP / 32; ++kn) {
-            Frag<E> fb;
-            frag_direct_perm(fb, s_do, G::LDV, ti, 32 * kn);
-            mma2a(acc, fs0[kn], fs0l[kn], fb);
-          }
-          if constexpr (SCAL) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) u1p[I] += to_f(s_q[ti * G::LDK + 16 * cm + 4 * g + rr]) * acc[rr];
-          }
-          acc *= s_fq[ti];
+        // dq^T = (live X^T) + intra, per token block
+        {
+          Frag<E> fkt[2], fktl[2];
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb) {
-            if (jb == 1 && I < 2) continue;
-            Frag<E> fb, fbl;
-            frag_direct(fb, s_dah, G::LDA, ti, 32 * jb);
-            if constexpr (SP) frag_direct(fbl, s_dal, G::LDA, ti, 32 * jb);
-            if constexpr (DIAG && SP) mma3(acc, fkt[jb], fktl[jb], fb, fbl);
-            else mma2b(acc, fkt[jb], fb, fbl);
+            frag_tr(fkt[jb], s_k, G::LDK, 32 * jb, 16 * cm);
+            if constexpr (DIAG && SP) frag_tr(fktl[jb], s_kl, G::LDK, 32 * jb, 16 * cm);
           }
-          const int d0 = 16 * cm + 4 * g;
-          if constexpr (DIAG) {
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int d = d0 + rr;
-              const bool ok = d < DK;
-              float qt = to_f(s_q[ti * G::LDK + d]);
-              if constexpr (SP) qt += to_f(s_ql[ti * G::LDK + d]);
-              wv[cc][I][rr] = ok ? qt * acc[rr] : 0.f;
-              acc[rr] *= ok ? __expf(gq[cc][I][rr]) : 0.f;
+          for (int I = 0; I < 4; ++I) {
+            const int ti = 16 * I + i16;
+            f32x4 acc = ax[I];
+            if constexpr (SCAL) {
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) u1p[I] += to_f(s_q[ti * G::LDK + 16 * cm + 4 * g + rr]) * acc[rr];
             }
+            acc *= s_fq[ti];
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+              if (jb == 1 && I < 2) continue;
+              Frag<E> fb, fbl;
+              frag_direct(fb, s_dah, G::LDA, ti, 32 * jb);
+              if constexpr (SP) frag_direct(fbl, s_dal, G::LDA, ti, 32 * jb);
+              if constexpr (DIAG && SP) mma3(acc, fkt[jb], fktl[jb], fb, fbl);
+              else mma2b(acc, fkt[jb], fb, fbl);
+            }
+            const int d0 = 16 * cm + 4 * g;
+            if constexpr (DIAG) {
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const int d = d0 + rr;
+                const bool ok = d < DK;
+                float qt = to_f(s_q[ti * G::LDK + d]);
+                if constexpr (SP) qt += to_f(s_ql[ti * G::LDK + d]);
+                wv[cc][I][rr] = ok ? qt * acc[rr] : 0.f;
+                acc[rr] *= ok ? __expf(gq[cc][I][rr]) : 0.f;
+              }
+            }
+            if (d0 < DK) store4(dqp + tok_off(b, t0 + ti, h, a.T, a.H, DK) + d0, acc);
           }
-          if (d0 < DK) store4(dqp + tok_off(b, t0 + ti, h, a.T, a.H, DK) + d0, acc);
         }
-        // dk^T: dS^T (scaled by exp(Gam_last[d]) for a diagonal decay) as split fragments
-        Frag<E> fdt[G::DVP / 32], fdtl[G::DVP / 32], fqt[2], fqtl[2];
+        // Y'^T = dS'^T V^T (dS' = dS scaled by exp(Gam_last[d]) for a diagonal decay),
+        // contracting over d_v outer as above
+        f32x4 ay[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) ay[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kn = 0; kn < G::DVP / 32; ++kn) {
           float y[8];
@@ -400,54 +413,60 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
             y[e] = dT[2 * kn][cc][e] * eL;
             y[4 + e] = dT[2 * kn + 1][cc][e] * eL;
           }
-          split_frag(fdt[kn], fdtl[kn], y);
-        }
+          Frag<E> fdt, fdtl;
+          split_frag(fdt, fdtl, y);
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-          frag_tr(fqt[jb], s_q, G::LDK, 32 * jb, 16 * cm);
-          if constexpr (DIAG && SP) frag_tr(fqtl[jb], s_ql, G::LDK, 32 * jb, 16 * cm);
-        }
-#pragma unroll
-        for (int J = 0; J < 4; ++J) {
-          const int tj = 16 * J + i16;
-          f32x4 ay = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kn = 0; kn < G::DVP / 32; ++kn) {
+          for (int J = 0; J < 4; ++J) {
             Frag<E> fb;
-            frag_direct_perm(fb, s_v, G::LDV, tj, 32 * kn);
-            mma2a(ay, fdt[kn], fdtl[kn], fb);
+            frag_direct_perm(fb, s_v, G::LDV, 16 * J + i16, 32 * kn);
+            mma2a(ay[J], fdt, fdtl, fb);
           }
-          ay *= s_fk[tj];
-          if constexpr (SCAL) {
+        }
+        // dk^T = tail Y'^T + intra, per token block
+        if constexpr (DIAG) wtot[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+          Frag<E> fqt[2], fqtl[2];
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) u4p[J] += to_f(s_k[tj * G::LDK + 16 * cm + 4 * g + rr]) * ay[rr];
+          for (int jb = 0; jb < 2; ++jb) {
+            frag_tr(fqt[jb], s_q, G::LDK, 32 * jb, 16 * cm);
+            if constexpr (DIAG && SP) frag_tr(fqtl[jb], s_ql, G::LDK, 32 * jb, 16 * cm);
           }
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int ib = 0; ib < 2; ++ib) {
-            if (ib == 0 && J >= 2) continue;
-            Frag<E> fb, fbl;
-            frag_tr(fb, s_dah, G::LDA, 32 * ib, 16 * J);
-            if constexpr (SP) frag_tr(fbl, s_dal, G::LDA, 32 * ib, 16 * J);
-            if constexpr (DIAG && SP) mma3(acc, fqt[ib], fqtl[ib], fb, fbl);
-            else mma2b(acc, fqt[ib], fb, fbl);
-          }
-          const int d0 = 16 * cm + 4 * g;
-          if constexpr (DIAG) {
+          for (int J = 0; J < 4; ++J) {
+            const int tj = 16 * J + i16;
+            f32x4 yv = ay[J] * s_fk[tj];
+            if constexpr (SCAL) {
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int d = d0 + rr;
-              const bool ok = d < DK;
-              float kt = ok ? to_f(s_k[tj * G::LDK + d]) : 0.f;
-              if constexpr (SP) kt += ok ? to_f(s_kl[tj * G::LDK + d]) : 0.f;
-              wv[cc][J][rr] -= kt * acc[rr];
-              zv[cc][J][rr] = kt * ay[rr];
-              acc[rr] = ok ? (acc[rr] + ay[rr]) * __expf(-gq[cc][J][rr]) : 0.f;
+              for (int rr = 0; rr < 4; ++rr) u4p[J] += to_f(s_k[tj * G::LDK + 16 * cm + 4 * g + rr]) * yv[rr];
             }
-          } else {
-            acc += ay;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib) {
+              if (ib == 0 && J >= 2) continue;
+              Frag<E> fb, fbl;
+              frag_tr(fb, s_dah, G::LDA, 32 * ib, 16 * J);
+              if constexpr (SP) frag_tr(fbl, s_dal, G::LDA, 32 * ib, 16 * J);
+              if constexpr (DIAG && SP) mma3(acc, fqt[ib], fqtl[ib], fb, fbl);
+              else mma2b(acc, fqt[ib], fb, fbl);
+            }
+            const int d0 = 16 * cm + 4 * g;
+            if constexpr (DIAG) {
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) {
+                const int d = d0 + rr;
+                const bool ok = d < DK;
+                float kt = ok ? to_f(s_k[tj * G::LDK + d]) : 0.f;
+                if constexpr (SP) kt += ok ? to_f(s_kl[tj * G::LDK + d]) : 0.f;
+                const float wfull = wv[cc][J][rr] - kt * acc[rr];
+                wtot[cc][rr] += wfull;
+                wv[cc][J][rr] = kt * yv[rr] - wfull;
+                acc[rr] = ok ? (acc[rr] + yv[rr]) * __expf(-gq[cc][J][rr]) : 0.f;
+              }
+            } else {
+              acc += yv;
+            }
+            if (d0 < DK) store4(dkp + tok_off(b, t0 + tj, h, a.T, a.H, DK) + d0, acc);
           }
-          if (d0 < DK) store4(dkp + tok_off(b, t0 + tj, h, a.T, a.H, DK) + d0, acc);
         }
       }
 
@@ -461,27 +480,18 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
           f32x4 t3v;
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) t3v[rr] = (d0 + rr < DK) ? keep * s_t3[d0 + rr] : 0.f;
-          // suffix sums of wv and exclusive prefix sums of zv over the 64 tokens (I, i16)
-          f32x4 suf_tot = {0.f, 0.f, 0.f, 0.f}, pre_tot = {0.f, 0.f, 0.f, 0.f};
-          f32x4 sufI[4], preI[4];
+          // total of w over the 64 tokens, and exclusive prefix sums of r over them
+          f32x4 base = wtot[cc];
 #pragma unroll
-          for (int I = 3; I >= 0; --I) {
-            f32x4 x = wv[cc][I];
+          for (int off = 1; off < 16; off <<= 1)
 #pragma unroll
-            for (int off = 1; off < 16; off <<= 1) {
-#pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                const float y = __shfl_down(x[rr], off, 16);
-                if (i16 + off < 16) x[rr] += y;
-              }
-            }
-            sufI[I] = x + suf_tot;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) suf_tot[rr] += __shfl(x[rr], 0, 16);
-          }
+            for (int rr = 0; rr < 4; ++rr) base[rr] += __shfl_xor(base[rr], off, 16);
+          base += t3v;
+          f32x4 pre_tot = {0.f, 0.f, 0.f, 0.f};
+          f32x4 preI[4];
 #pragma unroll
           for (int I = 0; I < 4; ++I) {
-            f32x4 x = zv[cc][I];
+            f32x4 x = wv[cc][I];
             const f32x4 own = x;
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) {
@@ -499,7 +509,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
               const int t = 16 * I + i16;
-              f32x4 dgv = sufI[I] + preI[I] + t3v;
+              f32x4 dgv = base + preI[I];
               if ((seg.starts >> t) & 1ull) dgv = f32x4{0.f, 0.f, 0.f, 0.f};
               store4(a.dg + tok_off(b, t0 + t, h, a.T, a.H, DK) + d0, dgv);
             }
