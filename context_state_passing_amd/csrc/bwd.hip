@@ -256,7 +256,11 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       for (int cc = 0; cc < G::CPWV; ++cc) {
         const int cn = w + G::NW * cc;
         if (cn >= G::NVT) continue;
-        Frag<E> fs[G::DKP / 32], fsl[G::DKP / 32];
+        // inter part K^ dS' for the four token blocks, contracting over d_k in
+        // 32-wide steps (outer) so one split dS fragment is live at a time
+        f32x4 av[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) av[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < G::DKP / 32; ++kb) {
           f32x4 lo = dS[2 * kb][cc], hi = dS[2 * kb + 1][cc];
@@ -268,7 +272,19 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
               hi[rr] *= d1 < DK ? s_el[d1] : 0.f;
             }
           }
-          acc_to_frag_split(fs[kb], fsl[kb], lo, hi);
+          Frag<E> fs, fsl;
+          acc_to_frag_split(fs, fsl, lo, hi);
+#pragma unroll
+          for (int J = 0; J < 4; ++J) {
+            Frag<E> fb, fbl;
+            frag_direct_perm(fb, s_k, G::LDK, 16 * J + i16, 32 * kb);
+            if constexpr (DIAG && SP) {
+              frag_direct_perm(fbl, s_kl, G::LDK, 16 * J + i16, 32 * kb);
+              mma3(av[J], fs, fsl, fb, fbl);
+            } else {
+              mma2a(av[J], fs, fsl, fb);
+            }
+          }
         }
         Frag<E> fdo[2];
 #pragma unroll
@@ -276,19 +292,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
           const int tj = 16 * J + i16;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int kb = 0; kb < G::DKP / 32; ++kb) {
-            Frag<E> fb, fbl;
-            frag_direct_perm(fb, s_k, G::LDK, tj, 32 * kb);
-            if constexpr (DIAG && SP) {
-              frag_direct_perm(fbl, s_kl, G::LDK, tj, 32 * kb);
-              mma3(acc, fs[kb], fsl[kb], fb, fbl);
-            } else {
-              mma2a(acc, fs[kb], fsl[kb], fb);
-            }
-          }
-          acc *= s_fk[tj];
+          f32x4 acc = av[J] * s_fk[tj];
 #pragma unroll
           for (int ib = 0; ib < 2; ++ib) {
             if (ib == 0 && J >= 2) continue;
