@@ -31,6 +31,32 @@
 
 namespace cpla {
 
+// Row shift within the 16 lanes of a DPP row; lanes with no source read 0.
+template <int OFF>
+__device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 | OFF,
+                                                               0xf, 0xf, true));
+}
+
+// Gam at token 16 I + (lane % 16) of the current block and key dims d0 .. d0+3
+// (the calling lane's), recomputed from g in global memory: an inclusive prefix
+// sum over the 16 lanes of the row, plus the total of the earlier blocks held in
+// carry (updated for the next block). Lanes with ok = false (dims past d_k) get 0.
+__device__ __forceinline__ f32x4 lane_gamma(const float* __restrict__ gp, bool ok, f32x4& carry) {
+  f32x4 x = ok ? *reinterpret_cast<const f32x4*>(gp) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    x[rr] += row_shr<1>(x[rr]);
+    x[rr] += row_shr<2>(x[rr]);
+    x[rr] += row_shr<4>(x[rr]);
+    x[rr] += row_shr<8>(x[rr]);
+  }
+  const f32x4 out = x + carry;
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) carry[rr] += __shfl(x[rr], 15, 16);
+  return out;
+}
+
 template <typename E, int DK, int DV, int DECAY, bool APPLY>
 __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
   using G = Geo<E, DK, DV>;
@@ -60,6 +86,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) E s_qh[QH * G::TILE_K + 8];
   __shared__ __attribute__((aligned(16))) E s_qhl[QHL * G::TILE_K + 8];
   __shared__ __attribute__((aligned(16))) char s_reg[REG_BYTES];
+  // diagonal apply: exp(Gam) of the chunk in bf16, for the dq / dk output scaling
+  // (adds at most 2^-9 relative error to outputs that are rounded to bf16 anyway)
   constexpr int NRED = DIAG ? G::NT : G::NW;                     // column-scan partials / T3 partials
   constexpr int NU = (APPLY && SCAL) ? G::NW * CH : 1;           // scalar dg token partials
   __shared__ float s_gs[DIAG ? 1 : CH], s_fq[CH], s_fk[CH], s_red[NRED], s_el[DIAG ? G::DKP : 1];
@@ -183,21 +211,6 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
     __syncthreads();
     if constexpr (!APPLY)
       if (c > 0) prefetch(c - 1);
-
-    // Gam at this wave's dq/dk output positions (diagonal), before the region is reused
-    float gq[G::CPWK][4][4];
-    if constexpr (APPLY && DIAG) {
-#pragma unroll
-      for (int cc = 0; cc < G::CPWK; ++cc)
-#pragma unroll
-        for (int I = 0; I < 4; ++I)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            const int d = 16 * (w + G::NW * cc) + 4 * g + rr;
-            gq[cc][I][rr] = (w + G::NW * cc < G::NKT && d < DK) ? s_gam[(16 * I + i16) * DK + d] : 0.f;
-          }
-      __syncthreads();
-    }
 
     if constexpr (APPLY) {
       // ---- scores and score gradients (hi/lo) for the wave's tiles -------------------
@@ -365,6 +378,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
         }
         // dq^T = (live X^T) + intra, per token block
         {
+          f32x4 gcar = {0.f, 0.f, 0.f, 0.f};
           Frag<E> fkt[2], fktl[2];
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb) {
@@ -391,6 +405,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
             }
             const int d0 = 16 * cm + 4 * g;
             if constexpr (DIAG) {
+              const f32x4 gm = lane_gamma(a.g + tok_off(b, t0 + ti, h, a.T, a.H, DK) + d0, d0 < DK, gcar);
 #pragma unroll
               for (int rr = 0; rr < 4; ++rr) {
                 const int d = d0 + rr;
@@ -398,7 +413,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
                 float qt = to_f(s_q[ti * G::LDK + d]);
                 if constexpr (SP) qt += to_f(s_ql[ti * G::LDK + d]);
                 wv[cc][I][rr] = ok ? qt * acc[rr] : 0.f;
-                acc[rr] *= ok ? __expf(gq[cc][I][rr]) : 0.f;
+                acc[rr] *= ok ? __expf(gm[rr]) : 0.f;
               }
             }
             if (d0 < DK) store4(dqp + tok_off(b, t0 + ti, h, a.T, a.H, DK) + d0, acc);
@@ -429,6 +444,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
         // dk^T = tail Y'^T + intra, per token block
         if constexpr (DIAG) wtot[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
         {
+          f32x4 gcar = {0.f, 0.f, 0.f, 0.f};
           Frag<E> fqt[2], fqtl[2];
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb) {
@@ -455,6 +471,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
             }
             const int d0 = 16 * cm + 4 * g;
             if constexpr (DIAG) {
+              const f32x4 gm = lane_gamma(a.g + tok_off(b, t0 + tj, h, a.T, a.H, DK) + d0, d0 < DK, gcar);
 #pragma unroll
               for (int rr = 0; rr < 4; ++rr) {
                 const int d = d0 + rr;
@@ -464,7 +481,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
                 const float wfull = wv[cc][J][rr] - kt * acc[rr];
                 wtot[cc][rr] += wfull;
                 wv[cc][J][rr] = kt * yv[rr] - wfull;
-                acc[rr] = ok ? (acc[rr] + yv[rr]) * __expf(-gq[cc][J][rr]) : 0.f;
+                acc[rr] = ok ? (acc[rr] + yv[rr]) * __expf(-gm[rr]) : 0.f;
               }
             } else {
               acc += yv;
@@ -492,7 +509,6 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
             for (int rr = 0; rr < 4; ++rr) base[rr] += __shfl_xor(base[rr], off, 16);
           base += t3v;
           f32x4 pre_tot = {0.f, 0.f, 0.f, 0.f};
-          f32x4 preI[4];
 #pragma unroll
           for (int I = 0; I < 4; ++I) {
             f32x4 x = wv[cc][I];
@@ -505,18 +521,12 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
                 if (i16 >= off) x[rr] += y;
               }
             }
-            preI[I] = x - own + pre_tot;
+            f32x4 dgv = base + (x - own) + pre_tot;
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) pre_tot[rr] += __shfl(x[rr], 15, 16);
-          }
-          if (d0 < DK) {
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-              const int t = 16 * I + i16;
-              f32x4 dgv = base + preI[I];
-              if ((seg.starts >> t) & 1ull) dgv = f32x4{0.f, 0.f, 0.f, 0.f};
-              store4(a.dg + tok_off(b, t0 + t, h, a.T, a.H, DK) + d0, dgv);
-            }
+            const int t = 16 * I + i16;
+            if ((seg.starts >> t) & 1ull) dgv = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (d0 < DK) store4(a.dg + tok_off(b, t0 + t, h, a.T, a.H, DK) + d0, dgv);
           }
         }
       }
@@ -602,6 +612,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       }
       // token mask for Q^ where it is not baked into a tile (diagonal / no decay, packed chunks)
       const bool mask_tok = !SCAL && seg.any();
+      constexpr bool QSPLIT = SP && (DIAG || SCAL);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         Frag<E> fdo[G::CPWV];
@@ -610,16 +621,12 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
           const int cn = w + G::NW * cc;
           if (cn < G::NVT) frag_tr(fdo[cc], s_do, G::LDV, 32 * kb, 16 * cn);
         }
-        Frag<E> fdoa[APPLY ? G::NVT : 1];
-        if constexpr (APPLY) {
-#pragma unroll
-          for (int nt = 0; nt < G::NVT; ++nt) frag_tr(fdoa[nt], s_do, G::LDV, 32 * kb, 16 * nt);
-        }
+        // dS[d][n] += sum_i Q^[i][d] dO[i][n]   (rows: every d tile; columns: owned n tiles)
 #pragma unroll
         for (int m = 0; m < G::NKT; ++m) {
           Frag<E> fa, fal;
           frag_tr(fa, qhat_h, G::LDK, 32 * kb, 16 * m);
-          if constexpr (SP && (DIAG || SCAL)) frag_tr(fal, qhat_l, G::LDK, 32 * kb, 16 * m);
+          if constexpr (QSPLIT) frag_tr(fal, qhat_l, G::LDK, 32 * kb, 16 * m);
           else frag_zero(fal);
           if (mask_tok) {
             frag_scale_tokens(fa, s_fq, 32 * kb, false);
@@ -628,20 +635,31 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
 #pragma unroll
           for (int cc = 0; cc < G::CPWV; ++cc)
             if (w + G::NW * cc < G::NVT) {
-              if constexpr (SP && (DIAG || SCAL)) mma2a(dS[m][cc], fa, fal, fdo[cc]);
+              if constexpr (QSPLIT) mma2a(dS[m][cc], fa, fal, fdo[cc]);
               else mma(dS[m][cc], fa, fdo[cc]);
             }
-          if constexpr (APPLY) {
-            // dS^T columns owned by this wave: d tile m == w + 4 cc
+        }
+        // dS^T[n][d] += sum_i dO[i][n] Q^[i][d]   (rows: every n tile; columns: owned d tiles)
+        if constexpr (APPLY) {
 #pragma unroll
-            for (int cc = 0; cc < G::CPWK; ++cc)
-              if (m == w + G::NW * cc) {
+          for (int cc = 0; cc < G::CPWK; ++cc) {
+            const int cm = w + G::NW * cc;
+            if (cm >= G::NKT) continue;
+            Frag<E> qa, qal;
+            frag_tr(qa, qhat_h, G::LDK, 32 * kb, 16 * cm);
+            if constexpr (QSPLIT) frag_tr(qal, qhat_l, G::LDK, 32 * kb, 16 * cm);
+            else frag_zero(qal);
+            if (mask_tok) {
+              frag_scale_tokens(qa, s_fq, 32 * kb, false);
+              frag_scale_tokens(qal, s_fq, 32 * kb, false);
+            }
 #pragma unroll
-                for (int nt = 0; nt < G::NVT; ++nt) {
-                  if constexpr (SP && (DIAG || SCAL)) mma2b(dT[nt][cc], fdoa[nt], fa, fal);
-                  else mma(dT[nt][cc], fdoa[nt], fa);
-                }
-              }
+            for (int nt = 0; nt < G::NVT; ++nt) {
+              Frag<E> fd;
+              frag_tr(fd, s_do, G::LDV, 32 * kb, 16 * nt);
+              if constexpr (QSPLIT) mma2b(dT[nt][cc], fd, qa, qal);
+              else mma(dT[nt][cc], fd, qa);
+            }
           }
         }
       }
