@@ -169,10 +169,23 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t t0 = tshard + (int64_t)c * CH;
     ChunkSeg seg;
+    // apply walk: every global load of the chunk's inputs is issued before the
+    // first use, so the chunk waits on memory once; the registers are free again
+    // once the tiles are in LDS (the walk's compute needs them)
+    SegRegs aseg;
+    GamRegs<DK, DECAY, G::NT> agam;
+    TileRegs<E, DK, G::NT> aq, ak;
+    TileRegs<E, DV, G::NT> av_, ado;
+    const int tidf = tid_pick<APPLY>();
     if constexpr (APPLY) {
-      // direct global -> LDS staging (the apply walk has no registers to spare)
-      seg = chunk_seg(a.seq_idx, t0);
-      stage_gamma<DK, DECAY, G::NT>(a.g, b, h, t0, a.T, a.H, seg, s_gam, s_fq, s_fk, s_red);
+      aseg.load(a.seq_idx, t0, tidf & 63);
+      agam.load(a.g, b, h, t0, a.T, a.H, tidf);
+      aq.load(q, b, h, t0, a.T, a.H, tidf);
+      ak.load(k, b, h, t0, a.T, a.H, tidf);
+      av_.load(v, b, h, t0, a.T, a.H, tidf);
+      ado.load(dO, b, h, t0, a.T, a.H, tidf);
+      seg = aseg.finish(a.seq_idx);
+      finish_gamma<DK, DECAY, G::NT>(agam, seg, s_gam, s_fq, s_fk, s_red, tidf);
     } else {
       seg = rseg.finish(a.seq_idx);
       finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk, s_red);
@@ -192,21 +205,20 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
     }
     if constexpr (APPLY) {
       if constexpr (DIAG) {
-        stage_tile_split<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(q, b, h, t0, a.T, a.H, s_q, s_ql, s_gam, nullptr);
-        stage_tile_split<E, DK, G::DKP, G::LDK, 2, DK, G::NT>(k, b, h, t0, a.T, a.H, s_k, s_kl, s_gam, nullptr);
+        store_tile<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(aq, s_q, s_ql, s_gam, nullptr, tidf);
+        store_tile<E, DK, G::DKP, G::LDK, 2, DK, G::NT>(ak, s_k, s_kl, s_gam, nullptr, tidf);
       } else {
-        if constexpr (SCAL)
-          stage_tile_split<E, DK, G::DKP, G::LDK, 3, DK, G::NT>(q, b, h, t0, a.T, a.H, s_qh, s_qhl, s_gam, s_fq);
-        stage_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(q, b, h, t0, a.T, a.H, s_q, s_gam);
-        stage_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(k, b, h, t0, a.T, a.H, s_k, s_gam);
+        if constexpr (SCAL) store_tile<E, DK, G::DKP, G::LDK, 3, DK, G::NT>(aq, s_qh, s_qhl, s_gam, s_fq, tidf);
+        store_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(aq, s_q, nullptr, s_gam, nullptr, tidf);
+        store_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(ak, s_k, nullptr, s_gam, nullptr, tidf);
       }
-      stage_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(dO, b, h, t0, a.T, a.H, s_do, s_gam);
-      stage_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(v, b, h, t0, a.T, a.H, s_v, s_gam);
+      store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(ado, s_do, nullptr, s_gam, nullptr, tidf);
+      store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(av_, s_v, nullptr, s_gam, nullptr, tidf);
     } else {
-      if constexpr (DIAG) store_tile<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(rq, s_q, s_ql, s_gam, nullptr);
-      else if constexpr (SCAL) store_tile<E, DK, G::DKP, G::LDK, 3, DK, G::NT>(rq, s_qh, s_qhl, s_gam, s_fq);
-      else store_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(rq, s_q, nullptr, s_gam, nullptr);
-      store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(rdo, s_do, nullptr, s_gam, nullptr);
+      if constexpr (DIAG) store_tile<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(rq, s_q, s_ql, s_gam, nullptr, tidf);
+      else if constexpr (SCAL) store_tile<E, DK, G::DKP, G::LDK, 3, DK, G::NT>(rq, s_qh, s_qhl, s_gam, s_fq, tidf);
+      else store_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(rq, s_q, nullptr, s_gam, nullptr, tidf);
+      store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(rdo, s_do, nullptr, s_gam, nullptr, tidf);
     }
     __syncthreads();
     if constexpr (!APPLY)
@@ -216,6 +228,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       // ---- scores and score gradients (hi/lo) for the wave's tiles -------------------
 #pragma unroll
       for (int s = 0; s < (N_SCORE_TILES + G::NW - 1) / G::NW; ++s) {
+        const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
         if (s * G::NW + w >= N_SCORE_TILES) continue;
         const int idx = score_tile(s * G::NW + w);
         const int I = idx >> 2, J = idx & 3;
@@ -224,11 +237,11 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
 #pragma unroll
           for (int kd = 0; kd < G::DKP / 32; ++kd) {
             Frag<E> fa, fb, fal, fbl;
-            frag_direct(fa, s_q, G::LDK, 16 * I + i16, 32 * kd);
-            frag_direct(fb, s_k, G::LDK, 16 * J + i16, 32 * kd);
+            frag_direct(fa, s_q, G::LDK, 16 * I + i16, 32 * kd, l);
+            frag_direct(fb, s_k, G::LDK, 16 * J + i16, 32 * kd, l);
             if constexpr (DIAG && SP) {
-              frag_direct(fal, s_ql, G::LDK, 16 * I + i16, 32 * kd);
-              frag_direct(fbl, s_kl, G::LDK, 16 * J + i16, 32 * kd);
+              frag_direct(fal, s_ql, G::LDK, 16 * I + i16, 32 * kd, l);
+              frag_direct(fbl, s_kl, G::LDK, 16 * J + i16, 32 * kd, l);
               mma3(xa, fa, fal, fb, fbl);
             } else {
               mma(xa, fa, fb);
@@ -237,8 +250,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
 #pragma unroll
           for (int kn = 0; kn < G::DVP / 32; ++kn) {
             Frag<E> fa, fb;
-            frag_direct(fa, s_do, G::LDV, 16 * I + i16, 32 * kn);
-            frag_direct(fb, s_v, G::LDV, 16 * J + i16, 32 * kn);
+            frag_direct(fa, s_do, G::LDV, 16 * I + i16, 32 * kn, l);
+            frag_direct(fb, s_v, G::LDV, 16 * J + i16, 32 * kn, l);
             mma(xd, fa, fb);
           }
         }
@@ -267,6 +280,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       E* dvp = reinterpret_cast<E*>(a.dv);
 #pragma unroll
       for (int cc = 0; cc < G::CPWV; ++cc) {
+        const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
         const int cn = w + G::NW * cc;
         if (cn >= G::NVT) continue;
         // inter part K^ dS' for the four token blocks, contracting over d_k in
@@ -290,9 +304,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
             Frag<E> fb, fbl;
-            frag_direct_perm(fb, s_k, G::LDK, 16 * J + i16, 32 * kb);
+            frag_direct_perm(fb, s_k, G::LDK, 16 * J + i16, 32 * kb, l);
             if constexpr (DIAG && SP) {
-              frag_direct_perm(fbl, s_kl, G::LDK, 16 * J + i16, 32 * kb);
+              frag_direct_perm(fbl, s_kl, G::LDK, 16 * J + i16, 32 * kb, l);
               mma3(av[J], fs, fsl, fb, fbl);
             } else {
               mma2a(av[J], fs, fsl, fb);
@@ -301,7 +315,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
         }
         Frag<E> fdo[2];
 #pragma unroll
-        for (int ib = 0; ib < 2; ++ib) frag_tr(fdo[ib], s_do, G::LDV, 32 * ib, 16 * cn);
+        for (int ib = 0; ib < 2; ++ib) frag_tr(fdo[ib], s_do, G::LDV, 32 * ib, 16 * cn, l);
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
           const int tj = 16 * J + i16;
@@ -310,8 +324,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
           for (int ib = 0; ib < 2; ++ib) {
             if (ib == 0 && J >= 2) continue;
             Frag<E> fb, fbl;
-            frag_tr(fb, s_ah, G::LDA, 32 * ib, 16 * J);
-            if constexpr (SP) frag_tr(fbl, s_al, G::LDA, 32 * ib, 16 * J);
+            frag_tr(fb, s_ah, G::LDA, 32 * ib, 16 * J, l);
+            if constexpr (SP) frag_tr(fbl, s_al, G::LDA, 32 * ib, 16 * J, l);
             mma2b(acc, fdo[ib], fb, fbl);
           }
           const int n0 = 16 * cn + 4 * g;
@@ -331,6 +345,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       f32x4 wv[G::CPWK][4], wtot[G::CPWK];
 #pragma unroll
       for (int cc = 0; cc < G::CPWK; ++cc) {
+        const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
         const int cm = w + G::NW * cc;
         if (cm >= G::NKT) continue;
         const int dl = 16 * cm + i16;        // lane-fixed key dim of the S0 / dS^T fragments
@@ -363,7 +378,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
 #pragma unroll
           for (int I = 0; I < 4; ++I) {
             Frag<E> fb;
-            frag_direct_perm(fb, s_do, G::LDV, 16 * I + i16, 32 * kn);
+            frag_direct_perm(fb, s_do, G::LDV, 16 * I + i16, 32 * kn, l);
             mma2a(ax[I], fs0, fs0l, fb);
           }
         }
@@ -382,8 +397,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
           Frag<E> fkt[2], fktl[2];
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb) {
-            frag_tr(fkt[jb], s_k, G::LDK, 32 * jb, 16 * cm);
-            if constexpr (DIAG && SP) frag_tr(fktl[jb], s_kl, G::LDK, 32 * jb, 16 * cm);
+            frag_tr(fkt[jb], s_k, G::LDK, 32 * jb, 16 * cm, l);
+            if constexpr (DIAG && SP) frag_tr(fktl[jb], s_kl, G::LDK, 32 * jb, 16 * cm, l);
           }
 #pragma unroll
           for (int I = 0; I < 4; ++I) {
@@ -398,8 +413,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
             for (int jb = 0; jb < 2; ++jb) {
               if (jb == 1 && I < 2) continue;
               Frag<E> fb, fbl;
-              frag_direct(fb, s_dah, G::LDA, ti, 32 * jb);
-              if constexpr (SP) frag_direct(fbl, s_dal, G::LDA, ti, 32 * jb);
+              frag_direct(fb, s_dah, G::LDA, ti, 32 * jb, l);
+              if constexpr (SP) frag_direct(fbl, s_dal, G::LDA, ti, 32 * jb, l);
               if constexpr (DIAG && SP) mma3(acc, fkt[jb], fktl[jb], fb, fbl);
               else mma2b(acc, fkt[jb], fb, fbl);
             }
@@ -437,7 +452,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
             Frag<E> fb;
-            frag_direct_perm(fb, s_v, G::LDV, 16 * J + i16, 32 * kn);
+            frag_direct_perm(fb, s_v, G::LDV, 16 * J + i16, 32 * kn, l);
             mma2a(ay[J], fdt, fdtl, fb);
           }
         }
@@ -448,8 +463,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
           Frag<E> fqt[2], fqtl[2];
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb) {
-            frag_tr(fqt[jb], s_q, G::LDK, 32 * jb, 16 * cm);
-            if constexpr (DIAG && SP) frag_tr(fqtl[jb], s_ql, G::LDK, 32 * jb, 16 * cm);
+            frag_tr(fqt[jb], s_q, G::LDK, 32 * jb, 16 * cm, l);
+            if constexpr (DIAG && SP) frag_tr(fqtl[jb], s_ql, G::LDK, 32 * jb, 16 * cm, l);
           }
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
@@ -464,8 +479,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
             for (int ib = 0; ib < 2; ++ib) {
               if (ib == 0 && J >= 2) continue;
               Frag<E> fb, fbl;
-              frag_tr(fb, s_dah, G::LDA, 32 * ib, 16 * J);
-              if constexpr (SP) frag_tr(fbl, s_dal, G::LDA, 32 * ib, 16 * J);
+              frag_tr(fb, s_dah, G::LDA, 32 * ib, 16 * J, l);
+              if constexpr (SP) frag_tr(fbl, s_dal, G::LDA, 32 * ib, 16 * J, l);
               if constexpr (DIAG && SP) mma3(acc, fqt[ib], fqtl[ib], fb, fbl);
               else mma2b(acc, fqt[ib], fb, fbl);
             }
@@ -495,6 +510,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
         __syncthreads();  // s_t3 complete
 #pragma unroll
         for (int cc = 0; cc < G::CPWK; ++cc) {
+          const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
           const int cm = w + G::NW * cc;
           if (cm >= G::NKT) continue;
           const int d0 = 16 * cm + 4 * g;
@@ -586,6 +602,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
     }
 
     // ---- dS <- [no start] diag(exp(Gam_last)) dS + sum_i live_i Q^_i dO_i^T ----------
+      const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
     // (and the same for dS^T)
     {
 #pragma unroll
@@ -619,18 +636,18 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
 #pragma unroll
         for (int cc = 0; cc < G::CPWV; ++cc) {
           const int cn = w + G::NW * cc;
-          if (cn < G::NVT) frag_tr(fdo[cc], s_do, G::LDV, 32 * kb, 16 * cn);
+          if (cn < G::NVT) frag_tr(fdo[cc], s_do, G::LDV, 32 * kb, 16 * cn, l);
         }
         // dS[d][n] += sum_i Q^[i][d] dO[i][n]   (rows: every d tile; columns: owned n tiles)
 #pragma unroll
         for (int m = 0; m < G::NKT; ++m) {
           Frag<E> fa, fal;
-          frag_tr(fa, qhat_h, G::LDK, 32 * kb, 16 * m);
-          if constexpr (QSPLIT) frag_tr(fal, qhat_l, G::LDK, 32 * kb, 16 * m);
+          frag_tr(fa, qhat_h, G::LDK, 32 * kb, 16 * m, l);
+          if constexpr (QSPLIT) frag_tr(fal, qhat_l, G::LDK, 32 * kb, 16 * m, l);
           else frag_zero(fal);
           if (mask_tok) {
-            frag_scale_tokens(fa, s_fq, 32 * kb, false);
-            frag_scale_tokens(fal, s_fq, 32 * kb, false);
+            frag_scale_tokens(fa, s_fq, 32 * kb, false, l);
+            frag_scale_tokens(fal, s_fq, 32 * kb, false, l);
           }
 #pragma unroll
           for (int cc = 0; cc < G::CPWV; ++cc)
@@ -646,17 +663,17 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
             const int cm = w + G::NW * cc;
             if (cm >= G::NKT) continue;
             Frag<E> qa, qal;
-            frag_tr(qa, qhat_h, G::LDK, 32 * kb, 16 * cm);
-            if constexpr (QSPLIT) frag_tr(qal, qhat_l, G::LDK, 32 * kb, 16 * cm);
+            frag_tr(qa, qhat_h, G::LDK, 32 * kb, 16 * cm, l);
+            if constexpr (QSPLIT) frag_tr(qal, qhat_l, G::LDK, 32 * kb, 16 * cm, l);
             else frag_zero(qal);
             if (mask_tok) {
-              frag_scale_tokens(qa, s_fq, 32 * kb, false);
-              frag_scale_tokens(qal, s_fq, 32 * kb, false);
+              frag_scale_tokens(qa, s_fq, 32 * kb, false, l);
+              frag_scale_tokens(qal, s_fq, 32 * kb, false, l);
             }
 #pragma unroll
             for (int nt = 0; nt < G::NVT; ++nt) {
               Frag<E> fd;
-              frag_tr(fd, s_do, G::LDV, 32 * kb, 16 * nt);
+              frag_tr(fd, s_do, G::LDV, 32 * kb, 16 * nt, l);
               if constexpr (QSPLIT) mma2b(dT[nt][cc], fd, qa, qal);
               else mma(dT[nt][cc], fd, qa);
             }

@@ -205,9 +205,9 @@ __device__ __forceinline__ void stage_tile_split(const E* __restrict__ src, int6
 // Sequence ids of the chunk's tokens (packed sequences): one token per lane.
 struct SegRegs {
   int cur, prev;
-  __device__ __forceinline__ void load(const int32_t* seq_idx, int64_t t0) {
+  __device__ __forceinline__ void load(const int32_t* seq_idx, int64_t t0, int l = lane_id()) {
     if (!seq_idx) return;
-    const int64_t t = t0 + lane_id();
+    const int64_t t = t0 + l;
     cur = seq_idx[t];
     prev = t > 0 ? seq_idx[t - 1] : cur - 1;
   }
@@ -227,8 +227,7 @@ struct GamRegs {
   static constexpr int TOK = (DECAY == DECAY_DIAG) ? CH / TPC : 1;
   float v[TOK];
   __device__ __forceinline__ void load(const float* __restrict__ g, int64_t b, int64_t h, int64_t t0, int64_t T,
-                                       int64_t H) {
-    const int tid = threadIdx.x;
+                                       int64_t H, int tid = threadIdx.x) {
     if constexpr (DECAY == DECAY_DIAG) {
       const int d = tid % DK, part = tid / DK;
       const float* src = g + ((b * T + t0 + part * TOK) * H + h) * DK + d;
@@ -244,8 +243,7 @@ struct GamRegs {
 // outputs as stage_gamma). Ends with a barrier.
 template <int DK, int DECAY, int NT>
 __device__ __forceinline__ void finish_gamma(GamRegs<DK, DECAY, NT>& R, const ChunkSeg& seg, float* gam,
-                                             float* fq, float* fk, float* red) {
-  const int tid = threadIdx.x;
+                                             float* fq, float* fk, float* red, int tid = threadIdx.x) {
   if constexpr (DECAY == DECAY_SCALAR) {
     if (tid < CH) {
       float x = R.v[0];
@@ -289,10 +287,10 @@ struct TileRegs {
   static constexpr int PER = (NV + NT - 1) / NT;
   f32x4 r[PER];
   __device__ __forceinline__ void load(const E* __restrict__ src, int64_t b, int64_t h, int64_t t0, int64_t T,
-                                       int64_t H) {
+                                       int64_t H, int tid = threadIdx.x) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int v = threadIdx.x + p * NT;
+      const int v = tid + p * NT;
       if (v < NV) {
         const int i = v / VPR, c = (v % VPR) * VEC;
         r[p] = *reinterpret_cast<const f32x4*>(src + tok_off(b, t0 + i, h, T, H, D) + c);
@@ -306,12 +304,12 @@ struct TileRegs {
 // scaled modes are stored split (hi, and lo for bf16). No barrier.
 template <typename E, int D, int DP, int LD, int MODE, int DK, int NT>
 __device__ __forceinline__ void store_tile(const TileRegs<E, D, NT>& R, E* hi, E* lo, const float* gam,
-                                           const float* fac) {
+                                           const float* fac, int tid = threadIdx.x) {
   using TR = TileRegs<E, D, NT>;
   constexpr int VEC = TR::VEC;
 #pragma unroll
   for (int p = 0; p < TR::PER; ++p) {
-    const int v = threadIdx.x + p * NT;
+    const int v = tid + p * NT;
     if (v >= TR::NV) continue;
     const int i = v / TR::VPR, c = (v % TR::VPR) * VEC;
     if constexpr (MODE == 0) {
@@ -347,7 +345,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<E, D, NT>& R, E* hi, E
     }
   }
   if constexpr (DP > D) {
-    for (int v = threadIdx.x; v < CH * (DP - D); v += NT) {
+    for (int v = tid; v < CH * (DP - D); v += NT) {
       const int i = v / (DP - D), c = D + v % (DP - D);
       hi[i * LD + c] = to_e<E>(0.f);
       if constexpr (MODE != 0 && sizeof(E) == 2) lo[i * LD + c] = to_e<E>(0.f);
@@ -357,10 +355,11 @@ __device__ __forceinline__ void store_tile(const TileRegs<E, D, NT>& R, E* hi, E
 
 // Multiply fragment slot e by fac[token(e)] (token-contracted operands).
 template <typename E>
-__device__ __forceinline__ void frag_scale_tokens(Frag<E>& f, const float* fac, int k0, bool perm) {
+__device__ __forceinline__ void frag_scale_tokens(Frag<E>& f, const float* fac, int k0, bool perm,
+                                                  int l = lane_id()) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const int tok = k0 + (perm ? kidx_perm(e) : kidx(e));
+    const int tok = k0 + (perm ? kidx_perm(e, l) : kidx(e, l));
     f.v[e] = to_e<E>(to_f(f.v[e]) * fac[tok]);
   }
 }

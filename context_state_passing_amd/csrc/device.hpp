@@ -31,6 +31,24 @@ constexpr int CH = 64;      // chunk length (tokens)
 constexpr int waves_for(int dpad) { return dpad >= 128 ? 8 : 4; }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+// The lane (thread) index behind an empty asm statement, so that the values a
+// loop body derives from it are computed inside the body: in the long chunk
+// walks the compiler would otherwise hoist every lane-dependent LDS and global
+// address out of the chunk loop and hold each in a register for the whole walk.
+// Take one per phase and pass it to the loaders below.
+__device__ __forceinline__ int lane_fresh() {
+  int l = threadIdx.x & 63;
+  asm volatile("" : "+v"(l));
+  return l;
+}
+__device__ __forceinline__ int tid_fresh() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+// fresh (FRESH = true) or plain indices, for walks that share code
+template <bool FRESH> __device__ __forceinline__ int lane_pick() { return FRESH ? lane_fresh() : lane_id(); }
+template <bool FRESH> __device__ __forceinline__ int tid_pick() { return FRESH ? tid_fresh() : (int)threadIdx.x; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // ---- element traits -------------------------------------------------------------
@@ -66,27 +84,26 @@ template <typename E> __device__ __forceinline__ void frag_set(Frag<E>& f, int e
 // Tile: row-major, `ld` elements per row. All offsets in elements.
 
 // lane-fixed row `row`, contraction indices k0 + 8g + e (16 contiguous bytes for bf16)
-__device__ __forceinline__ void frag_direct(Frag<bf16_t>& f, const bf16_t* t, int ld, int row, int k0) {
-  const int g = lane_id() >> 4;
+__device__ __forceinline__ void frag_direct(Frag<bf16_t>& f, const bf16_t* t, int ld, int row, int k0, int l = lane_id()) {
+  const int g = l >> 4;
   f.v = *reinterpret_cast<const bf16x8*>(t + row * ld + k0 + 8 * g);
 }
-__device__ __forceinline__ void frag_direct(Frag<float>& f, const float* t, int ld, int row, int k0) {
-  const int g = lane_id() >> 4;
+__device__ __forceinline__ void frag_direct(Frag<float>& f, const float* t, int ld, int row, int k0, int l = lane_id()) {
+  const int g = l >> 4;
   const f32x4* p = reinterpret_cast<const f32x4*>(t + row * ld + k0 + 8 * g);
   f32x4 a = p[0], b = p[1];
 #pragma unroll
   for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
 }
 // lane-fixed row, permuted contraction indices {k0 + 4g + e, k0 + 16 + 4g + e}
-__device__ __forceinline__ void frag_direct_perm(Frag<bf16_t>& f, const bf16_t* t, int ld, int row, int k0) {
-  const int g = lane_id() >> 4;
-  bf16x4 a = *reinterpret_cast<const bf16x4*>(t + row * ld + k0 + 4 * g);
-  bf16x4 b = *reinterpret_cast<const bf16x4*>(t + row * ld + k0 + 16 + 4 * g);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
+__device__ __forceinline__ void frag_direct_perm(Frag<bf16_t>& f, const bf16_t* t, int ld, int row, int k0, int l = lane_id()) {
+  const int g = l >> 4;
+  const bf16x4 a = *reinterpret_cast<const bf16x4*>(t + row * ld + k0 + 4 * g);
+  const bf16x4 b = *reinterpret_cast<const bf16x4*>(t + row * ld + k0 + 16 + 4 * g);
+  f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
-__device__ __forceinline__ void frag_direct_perm(Frag<float>& f, const float* t, int ld, int row, int k0) {
-  const int g = lane_id() >> 4;
+__device__ __forceinline__ void frag_direct_perm(Frag<float>& f, const float* t, int ld, int row, int k0, int l = lane_id()) {
+  const int g = l >> 4;
   f32x4 a = *reinterpret_cast<const f32x4*>(t + row * ld + k0 + 4 * g);
   f32x4 b = *reinterpret_cast<const f32x4*>(t + row * ld + k0 + 16 + 4 * g);
 #pragma unroll
@@ -98,34 +115,30 @@ __device__ __forceinline__ s16x4 ds_tr16(const bf16_t* p) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
-__device__ __forceinline__ void frag_tr(Frag<bf16_t>& f, const bf16_t* t, int ld, int k0, int col0) {
-  const int l = lane_id(), g = l >> 4, i = l & 15;
+__device__ __forceinline__ void frag_tr(Frag<bf16_t>& f, const bf16_t* t, int ld, int k0, int col0, int l = lane_id()) {
+  const int g = l >> 4, i = l & 15;
   s16x4 a = ds_tr16(t + (k0 + 8 * g + (i >> 2)) * ld + col0 + 4 * (i & 3));
   s16x4 b = ds_tr16(t + (k0 + 8 * g + 4 + (i >> 2)) * ld + col0 + 4 * (i & 3));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
-  s16x8 c;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { c[e] = a[e]; c[4 + e] = b[e]; }
+  const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   f.v = __builtin_bit_cast(bf16x8, c);
 }
-__device__ __forceinline__ void frag_tr(Frag<float>& f, const float* t, int ld, int k0, int col0) {
-  const int l = lane_id(), g = l >> 4, i = l & 15;
+__device__ __forceinline__ void frag_tr(Frag<float>& f, const float* t, int ld, int k0, int col0, int l = lane_id()) {
+  const int g = l >> 4, i = l & 15;
 #pragma unroll
   for (int e = 0; e < 8; ++e) f.v[e] = t[(k0 + 8 * g + e) * ld + col0 + i];
 }
 // permuted rows {k0 + 4g + e, k0 + 16 + 4g + e}
-__device__ __forceinline__ void frag_tr_perm(Frag<bf16_t>& f, const bf16_t* t, int ld, int k0, int col0) {
-  const int l = lane_id(), g = l >> 4, i = l & 15;
+__device__ __forceinline__ void frag_tr_perm(Frag<bf16_t>& f, const bf16_t* t, int ld, int k0, int col0, int l = lane_id()) {
+  const int g = l >> 4, i = l & 15;
   s16x4 a = ds_tr16(t + (k0 + 4 * g + (i >> 2)) * ld + col0 + 4 * (i & 3));
   s16x4 b = ds_tr16(t + (k0 + 16 + 4 * g + (i >> 2)) * ld + col0 + 4 * (i & 3));
   typedef short s16x8 __attribute__((ext_vector_type(8)));
-  s16x8 c;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) { c[e] = a[e]; c[4 + e] = b[e]; }
+  const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   f.v = __builtin_bit_cast(bf16x8, c);
 }
-__device__ __forceinline__ void frag_tr_perm(Frag<float>& f, const float* t, int ld, int k0, int col0) {
-  const int l = lane_id(), g = l >> 4, i = l & 15;
+__device__ __forceinline__ void frag_tr_perm(Frag<float>& f, const float* t, int ld, int k0, int col0, int l = lane_id()) {
+  const int g = l >> 4, i = l & 15;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     f.v[e] = t[(k0 + 4 * g + e) * ld + col0 + i];
@@ -133,8 +146,8 @@ __device__ __forceinline__ void frag_tr_perm(Frag<float>& f, const float* t, int
   }
 }
 // contraction index of fragment slot e for the plain and the permuted orders
-__device__ __forceinline__ int kidx(int e) { return 8 * (lane_id() >> 4) + e; }
-__device__ __forceinline__ int kidx_perm(int e) { return 4 * (lane_id() >> 4) + (e & 3) + ((e >> 2) << 4); }
+__device__ __forceinline__ int kidx(int e, int l = lane_id()) { return 8 * (l >> 4) + e; }
+__device__ __forceinline__ int kidx_perm(int e, int l = lane_id()) { return 4 * (l >> 4) + (e & 3) + ((e >> 2) << 4); }
 
 // Two 16x16 accumulator tiles stacked along their row index (rows r0..r0+31,
 // lane-fixed column) as one operand fragment contracting over those rows, in the
