@@ -38,12 +38,8 @@ __device__ __forceinline__ float row_shr(float x) {
                                                                0xf, 0xf, true));
 }
 
-// Gam at token 16 I + (lane % 16) of the current block and key dims d0 .. d0+3
-// (the calling lane's), recomputed from g in global memory: an inclusive prefix
-// sum over the 16 lanes of the row, plus the total of the earlier blocks held in
-// carry (updated for the next block). Lanes with ok = false (dims past d_k) get 0.
-__device__ __forceinline__ f32x4 lane_gamma(const float* __restrict__ gp, bool ok, f32x4& carry) {
-  f32x4 x = ok ? *reinterpret_cast<const f32x4*>(gp) : f32x4{0.f, 0.f, 0.f, 0.f};
+// Inclusive prefix sums over the 16 lanes of each DPP row, per component.
+__device__ __forceinline__ f32x4 row_scan(f32x4 x) {
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) {
     x[rr] += row_shr<1>(x[rr]);
@@ -51,9 +47,25 @@ __device__ __forceinline__ f32x4 lane_gamma(const float* __restrict__ gp, bool o
     x[rr] += row_shr<4>(x[rr]);
     x[rr] += row_shr<8>(x[rr]);
   }
-  const f32x4 out = x + carry;
+  return x;
+}
+
+// Value of the row's last lane (lane 15 of each group of 16), per component.
+__device__ __forceinline__ f32x4 row_last(const f32x4& x) {
+  f32x4 y;
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) carry[rr] += __shfl(x[rr], 15, 16);
+  for (int rr = 0; rr < 4; ++rr) y[rr] = __shfl(x[rr], 15, 16);
+  return y;
+}
+
+// Gam at token 16 I + (lane % 16) of the current block and key dims d0 .. d0+3
+// (the calling lane's) from the lane's raw log-decays x of that block: the
+// prefix sum over the row plus the total of the earlier blocks held in carry
+// (updated for the next block).
+__device__ __forceinline__ f32x4 lane_gamma(f32x4 x, f32x4& carry) {
+  x = row_scan(x);
+  const f32x4 out = x + carry;
+  carry += row_last(x);
   return out;
 }
 
@@ -276,6 +288,36 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       }
       __syncthreads();
 
+      // S0 rows of the owned d_k tiles (fp32, columns 16j + 4g .. +3), read here so
+      // that the load overlaps the dv phase
+      const float* cs = a.chunk_states + ((bh * nct + t0 / CH) * DK) * (int64_t)DV;
+      f32x4 s0r[G::CPWK][G::DVP / 16];
+      // diagonal: the lane's log-decays g[t0 + 16 I + i16][16 cm + 4g .. +3] for
+      // the dq/dk scaling, turned into Gam in the dq phase
+      f32x4 gl[DIAG ? G::CPWK : 1][4];
+      {
+        const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
+#pragma unroll
+        for (int cc = 0; cc < G::CPWK; ++cc) {
+          const int dl = 16 * (w + G::NW * cc) + i16;
+#pragma unroll
+          for (int j = 0; j < G::DVP / 16; ++j) {
+            const int n0 = 16 * j + 4 * g;
+            s0r[cc][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (dl < DK && n0 < DV) s0r[cc][j] = *reinterpret_cast<const f32x4*>(cs + dl * DV + n0);
+          }
+          if constexpr (DIAG) {
+            const int d0 = 16 * (w + G::NW * cc) + 4 * g;
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+              gl[cc][I] = f32x4{0.f, 0.f, 0.f, 0.f};
+              if (d0 < DK)
+                gl[cc][I] = *reinterpret_cast<const f32x4*>(a.g + tok_off(b, t0 + 16 * I + i16, h, a.T, a.H, DK) + d0);
+            }
+          }
+        }
+      }
+
       // ---- dv^T tiles: rows = owned d_v tiles, columns = tokens j ---------------------
       E* dvp = reinterpret_cast<E*>(a.dv);
 #pragma unroll
@@ -336,7 +378,6 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       // ---- dq^T and dk^T tiles: rows = owned d_k tiles, columns = tokens ---------------
       E* dqp = reinterpret_cast<E*>(a.dq);
       E* dkp = reinterpret_cast<E*>(a.dk);
-      const float* cs = a.chunk_states + ((bh * nct + t0 / CH) * DK) * (int64_t)DV;
       float u1p[4] = {0.f, 0.f, 0.f, 0.f}, u4p[4] = {0.f, 0.f, 0.f, 0.f};  // scalar: per-I token partials
       float t3p = 0.f;                                                      // scalar: T3 partial
       // diagonal dg: wv holds w_t = Q~*(dq before exp(Gam)) - K~*(intra dk) after the dq
@@ -363,9 +404,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
           float x[8];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const int n0 = 32 * kn + 16 * hh + 4 * g;
-            f32x4 sv = {0.f, 0.f, 0.f, 0.f};
-            if (dl < DK && n0 < DV) sv = *reinterpret_cast<const f32x4*>(cs + dl * DV + n0);
+            const f32x4 sv = s0r[cc][2 * kn + hh];
             const f32x4 tv = dT[2 * kn + hh][cc];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -405,8 +444,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
             const int ti = 16 * I + i16;
             f32x4 acc = ax[I];
             if constexpr (SCAL) {
+              const f32x4 q4 = load4f(s_q + ti * G::LDK + 16 * cm + 4 * g);
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) u1p[I] += to_f(s_q[ti * G::LDK + 16 * cm + 4 * g + rr]) * acc[rr];
+              for (int rr = 0; rr < 4; ++rr) u1p[I] += q4[rr] * acc[rr];
             }
             acc *= s_fq[ti];
 #pragma unroll
@@ -420,14 +460,16 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
             }
             const int d0 = 16 * cm + 4 * g;
             if constexpr (DIAG) {
-              const f32x4 gm = lane_gamma(a.g + tok_off(b, t0 + ti, h, a.T, a.H, DK) + d0, d0 < DK, gcar);
+              const f32x4 gm = lane_gamma(gl[cc][I], gcar);
+              gl[cc][I] = gm;
+              // Q~ (hi + lo) at the lane's four dims; columns past d_k hold zeros
+              f32x4 q4 = load4f(s_q + ti * G::LDK + d0);
+              if constexpr (SP) q4 += load4f(s_ql + ti * G::LDK + d0);
 #pragma unroll
               for (int rr = 0; rr < 4; ++rr) {
                 const int d = d0 + rr;
                 const bool ok = d < DK;
-                float qt = to_f(s_q[ti * G::LDK + d]);
-                if constexpr (SP) qt += to_f(s_ql[ti * G::LDK + d]);
-                wv[cc][I][rr] = ok ? qt * acc[rr] : 0.f;
+                wv[cc][I][rr] = ok ? q4[rr] * acc[rr] : 0.f;
                 acc[rr] *= ok ? __expf(gm[rr]) : 0.f;
               }
             }
@@ -459,7 +501,6 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
         // dk^T = tail Y'^T + intra, per token block
         if constexpr (DIAG) wtot[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
         {
-          f32x4 gcar = {0.f, 0.f, 0.f, 0.f};
           Frag<E> fqt[2], fqtl[2];
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb) {
@@ -471,8 +512,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
             const int tj = 16 * J + i16;
             f32x4 yv = ay[J] * s_fk[tj];
             if constexpr (SCAL) {
+              const f32x4 k4 = load4f(s_k + tj * G::LDK + 16 * cm + 4 * g);
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) u4p[J] += to_f(s_k[tj * G::LDK + 16 * cm + 4 * g + rr]) * yv[rr];
+              for (int rr = 0; rr < 4; ++rr) u4p[J] += k4[rr] * yv[rr];
             }
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -486,13 +528,14 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
             }
             const int d0 = 16 * cm + 4 * g;
             if constexpr (DIAG) {
-              const f32x4 gm = lane_gamma(a.g + tok_off(b, t0 + tj, h, a.T, a.H, DK) + d0, d0 < DK, gcar);
+              const f32x4 gm = gl[cc][J];
+              f32x4 k4 = load4f(s_k + tj * G::LDK + d0);
+              if constexpr (SP) k4 += load4f(s_kl + tj * G::LDK + d0);
 #pragma unroll
               for (int rr = 0; rr < 4; ++rr) {
                 const int d = d0 + rr;
                 const bool ok = d < DK;
-                float kt = ok ? to_f(s_k[tj * G::LDK + d]) : 0.f;
-                if constexpr (SP) kt += ok ? to_f(s_kl[tj * G::LDK + d]) : 0.f;
+                const float kt = ok ? k4[rr] : 0.f;
                 const float wfull = wv[cc][J][rr] - kt * acc[rr];
                 wtot[cc][rr] += wfull;
                 wv[cc][J][rr] = kt * yv[rr] - wfull;
@@ -518,28 +561,16 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) t3v[rr] = (d0 + rr < DK) ? keep * s_t3[d0 + rr] : 0.f;
           // total of w over the 64 tokens, and exclusive prefix sums of r over them
-          f32x4 base = wtot[cc];
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) base[rr] += __shfl_xor(base[rr], off, 16);
-          base += t3v;
+          const f32x4 base = row_last(row_scan(wtot[cc])) + t3v;
           f32x4 pre_tot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int I = 0; I < 4; ++I) {
-            f32x4 x = wv[cc][I];
-            const f32x4 own = x;
+            const f32x4 x = row_scan(wv[cc][I]);
+            f32x4 ex;
 #pragma unroll
-            for (int off = 1; off < 16; off <<= 1) {
-#pragma unroll
-              for (int rr = 0; rr < 4; ++rr) {
-                const float y = __shfl_up(x[rr], off, 16);
-                if (i16 >= off) x[rr] += y;
-              }
-            }
-            f32x4 dgv = base + (x - own) + pre_tot;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) pre_tot[rr] += __shfl(x[rr], 15, 16);
+            for (int rr = 0; rr < 4; ++rr) ex[rr] = row_shr<1>(x[rr]);
+            f32x4 dgv = base + ex + pre_tot;
+            pre_tot += row_last(x);
             const int t = 16 * I + i16;
             if ((seg.starts >> t) & 1ull) dgv = f32x4{0.f, 0.f, 0.f, 0.f};
             if (d0 < DK) store4(a.dg + tok_off(b, t0 + t, h, a.T, a.H, DK) + d0, dgv);

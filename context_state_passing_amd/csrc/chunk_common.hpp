@@ -364,6 +364,13 @@ __device__ __forceinline__ void frag_scale_tokens(Frag<E>& f, const float* fac, 
   }
 }
 
+// Load 4 consecutive tile elements (8-byte aligned for bf16, 16 for fp32) as fp32.
+__device__ __forceinline__ f32x4 load4f(const bf16_t* p) {
+  const bf16x4 y = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)y[0], (float)y[1], (float)y[2], (float)y[3]};
+}
+__device__ __forceinline__ f32x4 load4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+
 // Store 4 consecutive values (output feature 4g..4g+3 of a 16-wide tile).
 __device__ __forceinline__ void store4(bf16_t* p, const f32x4& x) {
   bf16x4 y;
