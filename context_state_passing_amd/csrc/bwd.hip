@@ -188,7 +188,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
     GamRegs<DK, DECAY, G::NT> agam;
     TileRegs<E, DK, G::NT> aq, ak;
     TileRegs<E, DV, G::NT> av_, ado;
-    const int tidf = tid_pick<APPLY>();
+    const int tidf = tid_pick<APPLY, G::NT>();
     if constexpr (APPLY) {
       aseg.load(a.seq_idx, t0, tidf & 63);
       agam.load(a.g, b, h, t0, a.T, a.H, tidf);
@@ -211,6 +211,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
         const float gl = s_gam[(CH - 1) * DK + threadIdx.x];
         gsum += gl;
         s_el[threadIdx.x] = __expf(gl);   // exp(Gam_last[d]), read by every row scaling below
+      } else if (threadIdx.x < G::DKP) {
+        s_el[threadIdx.x] = 0.f;           // padded key dims: their state rows stay zero
       }
     } else if constexpr (SCAL) {
       if (threadIdx.x == 0) gsum += s_gam[CH - 1];
@@ -235,6 +237,26 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
     __syncthreads();
     if constexpr (!APPLY)
       if (c > 0) prefetch(c - 1);
+
+    if constexpr (DIAG) {
+      // dS' = diag(exp(Gam_last)) dS, the adjoint as the chunk's tail tokens see it
+      // (dv, Y' and T3 below) and the carried part of the update at the end
+      const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
+#pragma unroll
+      for (int m = 0; m < G::NKT; ++m) {
+        const f32x4 el = load4f(s_el + 16 * m + 4 * g);
+#pragma unroll
+        for (int cc = 0; cc < G::CPWV; ++cc) dS[m][cc] *= el;
+      }
+      if constexpr (APPLY) {
+#pragma unroll
+        for (int cc = 0; cc < G::CPWK; ++cc) {
+          const float f = s_el[16 * (w + G::NW * cc) + i16];
+#pragma unroll
+          for (int nt = 0; nt < G::NVT; ++nt) dT[nt][cc] *= f;
+        }
+      }
+    }
 
     if constexpr (APPLY) {
       // ---- scores and score gradients (hi/lo) for the wave's tiles -------------------
@@ -332,15 +354,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
         for (int J = 0; J < 4; ++J) av[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < G::DKP / 32; ++kb) {
-          f32x4 lo = dS[2 * kb][cc], hi = dS[2 * kb + 1][cc];
-          if constexpr (DIAG) {
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int d0 = 32 * kb + 4 * g + rr, d1 = d0 + 16;
-              lo[rr] *= d0 < DK ? s_el[d0] : 0.f;
-              hi[rr] *= d1 < DK ? s_el[d1] : 0.f;
-            }
-          }
+          const f32x4 lo = dS[2 * kb][cc], hi = dS[2 * kb + 1][cc];
           Frag<E> fs, fsl;
           acc_to_frag_split(fs, fsl, lo, hi);
 #pragma unroll
@@ -395,7 +409,6 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
         // in the permuted order {32kn + 4g + e, 32kn + 16 + 4g + e}, the positions the
         // dS^T accumulators hold, so T3 is an elementwise product on the way.
         float t3 = 0.f;
-        const float eL = (DIAG && dl < DK) ? s_el[dl] : 1.f;
         f32x4 ax[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) ax[I] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -425,7 +438,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
           t3 += __shfl_xor(t3, 16, 64);
           t3 += __shfl_xor(t3, 32, 64);
           if constexpr (DIAG) {
-            if (g == 0) s_t3[dl] = t3 * eL;
+            if (g == 0) s_t3[dl] = t3;   // dS^T already carries exp(Gam_last[d])
           } else {
             if (g == 0) t3p += t3;
           }
@@ -486,8 +499,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
           float y[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            y[e] = dT[2 * kn][cc][e] * eL;
-            y[4 + e] = dT[2 * kn + 1][cc][e] * eL;
+            y[e] = dT[2 * kn][cc][e];
+            y[4 + e] = dT[2 * kn + 1][cc][e];
           }
           Frag<E> fdt, fdtl;
           split_frag(fdt, fdtl, y);
@@ -636,26 +649,19 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
     // (and the same for dS^T)
     {
+      // carried part: keep * dS' (diagonal: already scaled), keep * exp(Gam_last) dS
+      // (scalar), keep * dS (none); keep = 0 when the chunk holds a start
+      const float f = SCAL ? keep * __expf(s_gam[CH - 1]) : keep;
+      if (SCAL || seg.any()) {
 #pragma unroll
-      for (int m = 0; m < G::NKT; ++m)
+        for (int m = 0; m < G::NKT; ++m)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int d = 16 * m + 4 * g + rr;
-          float f = keep;
-          if constexpr (DIAG) f = d < DK ? keep * s_el[d] : 0.f;
-          if constexpr (SCAL) f = keep * __expf(s_gam[CH - 1]);
+          for (int cc = 0; cc < G::CPWV; ++cc) dS[m][cc] *= f;
+        if constexpr (APPLY) {
 #pragma unroll
-          for (int cc = 0; cc < G::CPWV; ++cc) dS[m][cc][rr] *= f;
-        }
-      if constexpr (APPLY) {
+          for (int cc = 0; cc < G::CPWK; ++cc)
 #pragma unroll
-        for (int cc = 0; cc < G::CPWK; ++cc) {
-          const int d = 16 * (w + G::NW * cc) + i16;
-          float f = keep;
-          if constexpr (DIAG) f = d < DK ? keep * s_el[d] : 0.f;
-          if constexpr (SCAL) f = keep * __expf(s_gam[CH - 1]);
-#pragma unroll
-          for (int nt = 0; nt < G::NVT; ++nt) dT[nt][cc] *= f;
+            for (int nt = 0; nt < G::NVT; ++nt) dT[nt][cc] *= f;
         }
       }
       // token mask for Q^ where it is not baked into a tile (diagonal / no decay, packed chunks)

@@ -52,151 +52,6 @@ __device__ __forceinline__ int64_t tok_off(int64_t b, int64_t t, int64_t h, int6
   return ((b * T + t) * H + h) * (int64_t)D;
 }
 
-// Stage the chunk's cumulative log-decay.
-//   scalar: gam[i] (64 floats);  diagonal: gam[i * DK + d];  none: nothing.
-// Then the per-token factors
-//   fq[i] = live_i * (scalar ? exp(Gam_i) : 1)
-//   fk[j] = tail_j * (scalar ? exp(Gam_last - Gam_j) : 1)
-// `red` is NT floats of scratch. Ends with a barrier.
-template <int DK, int DECAY, int NT>
-__device__ __forceinline__ void stage_gamma(const float* __restrict__ g, int64_t b, int64_t h, int64_t t0,
-                                            int64_t T, int64_t H, const ChunkSeg& seg,
-                                            float* gam, float* fq, float* fk, float* red) {
-  const int tid = threadIdx.x;
-  if constexpr (DECAY == DECAY_SCALAR) {
-    if (tid < CH) {
-      float x = g[(b * T + t0 + tid) * H + h];
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        float y = __shfl_up(x, off, 64);
-        if (tid >= off) x += y;
-      }
-      gam[tid] = x;
-      const float last = __shfl(x, 63, 64);
-      fq[tid] = seg.live(tid) ? __expf(x) : 0.f;
-      fk[tid] = seg.tail(tid) ? __expf(last - x) : 0.f;
-    }
-  } else {
-    if constexpr (DECAY == DECAY_DIAG) {
-      constexpr int TPC = NT / DK;         // threads per key column
-      constexpr int TOK = CH / TPC;        // tokens per thread
-      const int d = tid % DK, part = tid / DK;
-      float v[TOK];
-      const float* src = g + ((b * T + t0 + part * TOK) * H + h) * DK + d;
-#pragma unroll
-      for (int s = 0; s < TOK; ++s) v[s] = src[(int64_t)s * H * DK];
-#pragma unroll
-      for (int s = 1; s < TOK; ++s) v[s] += v[s - 1];
-      red[part * DK + d] = v[TOK - 1];
-      __syncthreads();
-      float off = 0.f;
-      for (int pp = 0; pp < part; ++pp) off += red[pp * DK + d];
-#pragma unroll
-      for (int s = 0; s < TOK; ++s) gam[(part * TOK + s) * DK + d] = v[s] + off;
-    }
-    if (tid < CH) {
-      fq[tid] = seg.live(tid) ? 1.f : 0.f;
-      fk[tid] = seg.tail(tid) ? 1.f : 0.f;
-    }
-  }
-  __syncthreads();
-}
-
-// Stage a [64][D] token-major tile of the input into LDS (row stride LD),
-// zero-filling columns D..DP-1. MODE 0: copy; 1: multiply by exp(Gam[i][d]);
-// 2: multiply by exp(-Gam[i][d]) (diagonal decay only). No barrier.
-template <typename E, int D, int DP, int LD, int MODE, int DK, int NT>
-__device__ __forceinline__ void stage_tile(const E* __restrict__ src, int64_t b, int64_t h, int64_t t0,
-                                           int64_t T, int64_t H, E* dst, const float* gam) {
-  constexpr int VEC = 16 / (int)sizeof(E);   // elements per 16-byte load
-  constexpr int VPR = D / VEC;               // vectors per row
-  constexpr int NV = CH * VPR;
-  const int tid = threadIdx.x;
-  for (int v = tid; v < NV; v += NT) {
-    const int i = v / VPR, c = (v % VPR) * VEC;
-    const E* s = src + tok_off(b, t0 + i, h, T, H, D) + c;
-    E* d = dst + i * LD + c;
-    if constexpr (sizeof(E) == 2) {
-      bf16x8 x = *reinterpret_cast<const bf16x8*>(s);
-      if constexpr (MODE != 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float gm = gam[i * DK + c + e];
-          x[e] = (bf16_t)((float)x[e] * __expf(MODE == 1 ? gm : -gm));
-        }
-      }
-      *reinterpret_cast<bf16x8*>(d) = x;
-    } else {
-      f32x4 x = *reinterpret_cast<const f32x4*>(s);
-      if constexpr (MODE != 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float gm = gam[i * DK + c + e];
-          x[e] = x[e] * __expf(MODE == 1 ? gm : -gm);
-        }
-      }
-      *reinterpret_cast<f32x4*>(d) = x;
-    }
-  }
-  if constexpr (DP > D) {
-    for (int v = tid; v < CH * (DP - D); v += NT) {
-      const int i = v / (DP - D), c = D + v % (DP - D);
-      dst[i * LD + c] = to_e<E>(0.f);
-    }
-  }
-}
-
-// Stage a [64][D] tile as split hi/lo parts (lo skipped for fp32). MODE 1:
-// x * exp(Gam[i][d]); 2: x * exp(-Gam[i][d]) (diagonal decay); 3: x * fac[i]. No barrier.
-template <typename E, int D, int DP, int LD, int MODE, int DK, int NT>
-__device__ __forceinline__ void stage_tile_split(const E* __restrict__ src, int64_t b, int64_t h, int64_t t0,
-                                                 int64_t T, int64_t H, E* hi, E* lo, const float* gam,
-                                                 const float* fac) {
-  constexpr int VEC = 16 / (int)sizeof(E);
-  constexpr int VPR = D / VEC;
-  constexpr int NV = CH * VPR;
-  const int tid = threadIdx.x;
-  for (int v = tid; v < NV; v += NT) {
-    const int i = v / VPR, c = (v % VPR) * VEC;
-    const E* s = src + tok_off(b, t0 + i, h, T, H, D) + c;
-    float x[VEC];
-    if constexpr (sizeof(E) == 2) {
-      bf16x8 y = *reinterpret_cast<const bf16x8*>(s);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = (float)y[e];
-    } else {
-      f32x4 y = *reinterpret_cast<const f32x4*>(s);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = y[e];
-    }
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      if constexpr (MODE == 1) x[e] *= __expf(gam[i * DK + c + e]);
-      if constexpr (MODE == 2) x[e] *= __expf(-gam[i * DK + c + e]);
-      if constexpr (MODE == 3) x[e] *= fac[i];
-    }
-    if constexpr (sizeof(E) == 2) {
-      bf16x8 yh, yl;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        yh[e] = (bf16_t)x[e];
-        yl[e] = (bf16_t)(x[e] - (float)yh[e]);
-      }
-      *reinterpret_cast<bf16x8*>(hi + i * LD + c) = yh;
-      *reinterpret_cast<bf16x8*>(lo + i * LD + c) = yl;
-    } else {
-      *reinterpret_cast<f32x4*>(hi + i * LD + c) = f32x4{x[0], x[1], x[2], x[3]};
-    }
-  }
-  if constexpr (DP > D) {
-    for (int v = tid; v < CH * (DP - D); v += NT) {
-      const int i = v / (DP - D), c = D + v % (DP - D);
-      hi[i * LD + c] = to_e<E>(0.f);
-      if constexpr (sizeof(E) == 2) lo[i * LD + c] = to_e<E>(0.f);
-    }
-  }
-}
-
 // ---- register prefetch ------------------------------------------------------------
 // A walk issues the next chunk's global loads into these registers before it
 // computes the current chunk, and writes them to LDS afterwards, so HBM latency
@@ -239,8 +94,12 @@ struct GamRegs {
   }
 };
 
-// Cumulative log-decay and per-token factors from prefetched registers (same
-// outputs as stage_gamma). Ends with a barrier.
+// The chunk's cumulative log-decay from the loaded registers, into LDS:
+//   scalar: gam[i] (64 floats);  diagonal: gam[i * DK + d];  none: nothing.
+// and the per-token factors
+//   fq[i] = live_i * (scalar ? exp(Gam_i) : 1)
+//   fk[j] = tail_j * (scalar ? exp(Gam_last - Gam_j) : 1)
+// `red` is NT floats of scratch. Ends with a barrier.
 template <int DK, int DECAY, int NT>
 __device__ __forceinline__ void finish_gamma(GamRegs<DK, DECAY, NT>& R, const ChunkSeg& seg, float* gam,
                                              float* fq, float* fk, float* red, int tid = threadIdx.x) {
@@ -332,14 +191,10 @@ __device__ __forceinline__ void store_tile(const TileRegs<E, D, NT>& R, E* hi, E
       if constexpr (MODE == 3) x[e] *= fac[i];
     }
     if constexpr (sizeof(E) == 2) {
-      bf16x8 yh, yl;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        yh[e] = (bf16_t)x[e];
-        yl[e] = (bf16_t)(x[e] - (float)yh[e]);
-      }
-      *reinterpret_cast<bf16x8*>(hi + i * LD + c) = yh;
-      *reinterpret_cast<bf16x8*>(lo + i * LD + c) = yl;
+      Frag<bf16_t> yh, yl;
+      split_frag(yh, yl, x);
+      *reinterpret_cast<bf16x8*>(hi + i * LD + c) = yh.v;
+      *reinterpret_cast<bf16x8*>(lo + i * LD + c) = yl.v;
     } else {
       *reinterpret_cast<f32x4*>(hi + i * LD + c) = f32x4{x[0], x[1], x[2], x[3]};
     }

@@ -39,16 +39,20 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int lane_fresh() {
   int l = threadIdx.x & 63;
   asm volatile("" : "+v"(l));
+  __builtin_assume(l >= 0 && l < 64);
   return l;
 }
-__device__ __forceinline__ int tid_fresh() {
+template <int NT> __device__ __forceinline__ int tid_fresh() {
   int t = threadIdx.x;
   asm volatile("" : "+v"(t));
+  __builtin_assume(t >= 0 && t < NT);
   return t;
 }
 // fresh (FRESH = true) or plain indices, for walks that share code
 template <bool FRESH> __device__ __forceinline__ int lane_pick() { return FRESH ? lane_fresh() : lane_id(); }
-template <bool FRESH> __device__ __forceinline__ int tid_pick() { return FRESH ? tid_fresh() : (int)threadIdx.x; }
+template <bool FRESH, int NT> __device__ __forceinline__ int tid_pick() {
+  return FRESH ? tid_fresh<NT>() : (int)threadIdx.x;
+}
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 
 // ---- element traits -------------------------------------------------------------
@@ -166,13 +170,25 @@ __device__ __forceinline__ void acc_to_frag(Frag<E>& f, const f32x4& lo, const f
 // operands the lo parts are zero and their MFMAs are skipped.
 template <typename E> struct Split { static constexpr bool on = sizeof(E) == 2; };
 
-template <typename E>
-__device__ __forceinline__ void split_frag(Frag<E>& hi, Frag<E>& lo, const float (&x)[8]) {
+__device__ __forceinline__ void split_frag(Frag<float>& hi, Frag<float>& lo, const float (&x)[8]) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    hi.v[e] = to_e<E>(x[e]);
-    if constexpr (Split<E>::on) lo.v[e] = to_e<E>(x[e] - to_f(hi.v[e]));
+  for (int e = 0; e < 8; ++e) hi.v[e] = x[e];
+}
+// bf16: hi converted in pairs; hi's fp32 values are read back from the packed
+// pairs with a shift / mask instead of a second conversion
+__device__ __forceinline__ void split_frag(Frag<bf16_t>& hi, Frag<bf16_t>& lo, const float (&x)[8]) {
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  hi.v = __builtin_convertvector(v, bf16x8);
+  const u32x4 hb = __builtin_bit_cast(u32x4, hi.v);
+  f32x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = x[2 * i] - __builtin_bit_cast(float, hb[i] << 16);
+    r[2 * i + 1] = x[2 * i + 1] - __builtin_bit_cast(float, hb[i] & 0xffff0000u);
   }
+  lo.v = __builtin_convertvector(r, bf16x8);
 }
 // acc += (a_hi + a_lo) (b_hi + b_lo), dropping lo*lo
 template <typename E>
@@ -232,17 +248,6 @@ struct ChunkSeg {
     return (starts & (hi & ~lo)) == 0ull;
   }
 };
-
-// Every wave computes the same mask from the global sequence ids (uniform).
-__device__ __forceinline__ ChunkSeg chunk_seg(const int32_t* seq_idx, int64_t t0) {
-  ChunkSeg s;
-  if (!seq_idx) { s.starts = 0ull; return s; }
-  const int i = lane_id();
-  const int64_t t = t0 + i;
-  bool st = (t == 0) ? true : (seq_idx[t] != seq_idx[t - 1]);
-  s.starts = __ballot(st);
-  return s;
-}
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
