@@ -41,10 +41,11 @@ struct Geo {
 // 1 = (0,1) and 11 = (2,3) are upper tiles that are read by 32-deep token
 // contractions and must hold zeros.
 constexpr int N_SCORE_TILES = 12;
-__device__ __forceinline__ int score_tile(int k) {
-  constexpr int T[N_SCORE_TILES] = {0, 4, 5, 8, 9, 10, 12, 13, 14, 15, 1, 11};
-  return T[k];
-}
+// The list {0, 4, 5, 8, 9, 10, 12, 13, 14, 15, 1, 11} packed as 4-bit fields, so
+// the lookup is register arithmetic rather than a load from a constant table
+// (a global load inside the chunk loop would make the wave wait for every
+// outstanding memory operation).
+__device__ __forceinline__ int score_tile(int k) { return (int)((0xB1FEDCA98540ull >> (4 * k)) & 15ull); }
 __device__ __forceinline__ bool score_tile_zero(int idx) { return idx == 1 || idx == 11; }
 
 // Row base offset of token t of row (b, h) in a [B, T, H, D] tensor.

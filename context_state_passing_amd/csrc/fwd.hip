@@ -21,9 +21,9 @@ namespace cpla {
 template <typename E, int DK, int DV, int DECAY, int NKT_, int CPWV_>
 __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* Kt, const E* Ktl, const E* Vt,
                                              const float* gam, const float* el, const float* fk,
-                                             const ChunkSeg& seg) {
+                                             const ChunkSeg& seg, int l) {
   using G = Geo<E, DK, DV>;
-  const int w = wave_id(), l = lane_id(), g = l >> 4;
+  const int w = wave_id(), g = l >> 4;
   const float keep = seg.any() ? 0.f : 1.f;
   if constexpr (DECAY == DECAY_SCALAR) {
     const float sc = keep * __expf(gam[CH - 1]);
@@ -43,7 +43,7 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* K
 #pragma unroll
     for (int cc = 0; cc < G::CPWV; ++cc) {
       const int c = w + G::NW * cc;
-      if (c < G::NVT) frag_tr(bv[kb][cc], Vt, G::LDV, 32 * kb, 16 * c);
+      if (c < G::NVT) frag_tr(bv[kb][cc], Vt, G::LDV, 32 * kb, 16 * c, l);
     }
   const bool scale_tok = (DECAY == DECAY_SCALAR) || seg.any();
 #pragma unroll
@@ -51,20 +51,20 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* K
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       Frag<E> a, al;
-      frag_tr(a, Kt, G::LDK, 32 * kb, 16 * m);
+      frag_tr(a, Kt, G::LDK, 32 * kb, 16 * m, l);
       if constexpr (DECAY == DECAY_DIAG && Split<E>::on) {
-        frag_tr(al, Ktl, G::LDK, 32 * kb, 16 * m);
+        frag_tr(al, Ktl, G::LDK, 32 * kb, 16 * m, l);
         if (scale_tok) {
-          frag_scale_tokens(a, fk, 32 * kb, false);
-          frag_scale_tokens(al, fk, 32 * kb, false);
+          frag_scale_tokens(a, fk, 32 * kb, false, l);
+          frag_scale_tokens(al, fk, 32 * kb, false, l);
         }
       } else if constexpr (DECAY == DECAY_SCALAR) {
         float x[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = to_f(a.v[e]) * fk[32 * kb + kidx(e)];
+        for (int e = 0; e < 8; ++e) x[e] = to_f(a.v[e]) * fk[32 * kb + kidx(e, l)];
         split_frag(a, al, x);
       } else {
-        if (scale_tok) frag_scale_tokens(a, fk, 32 * kb, false);
+        if (scale_tok) frag_scale_tokens(a, fk, 32 * kb, false, l);
         frag_zero(al);
       }
 #pragma unroll
@@ -172,28 +172,13 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
     store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(rv, s_v, nullptr, s_gam, nullptr);
     if (c + 1 < nc) prefetch(c + 1);
 
-    if constexpr (APPLY) {
-      if (a.chunk_states) {
-        float* cs = a.chunk_states + ((bh * (a.T / CH) + t0 / CH) * DK) * (int64_t)DV;
-#pragma unroll
-        for (int m = 0; m < G::NKT; ++m)
-#pragma unroll
-          for (int cc = 0; cc < G::CPWV; ++cc) {
-            const int cn = w + G::NW * cc;
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              const int d = 16 * m + 4 * g + rr, n = 16 * cn + i16;
-              if (cn < G::NVT && d < DK && n < DV) cs[d * DV + n] = S[m][cc][rr];
-            }
-          }
-      }
-    }
     __syncthreads();
 
     if constexpr (APPLY) {
       // ---- scores -> s_a (E), masked and decayed --------------------------------
 #pragma unroll
       for (int s = 0; s < (N_SCORE_TILES + G::NW - 1) / G::NW; ++s) {
+        const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
         if (s * G::NW + w >= N_SCORE_TILES) continue;
         const int idx = score_tile(s * G::NW + w);
         const int I = idx >> 2, J = idx & 3;
@@ -202,11 +187,11 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
 #pragma unroll
           for (int kd = 0; kd < G::DKP / 32; ++kd) {
             Frag<E> fa, fb, fal, fbl;
-            frag_direct(fa, s_q, G::LDK, 16 * I + i16, 32 * kd);
-            frag_direct(fb, s_k, G::LDK, 16 * J + i16, 32 * kd);
+            frag_direct(fa, s_q, G::LDK, 16 * I + i16, 32 * kd, l);
+            frag_direct(fb, s_k, G::LDK, 16 * J + i16, 32 * kd, l);
             if constexpr (DSP) {
-              frag_direct(fal, s_ql, G::LDK, 16 * I + i16, 32 * kd);
-              frag_direct(fbl, s_kl, G::LDK, 16 * J + i16, 32 * kd);
+              frag_direct(fal, s_ql, G::LDK, 16 * I + i16, 32 * kd, l);
+              frag_direct(fbl, s_kl, G::LDK, 16 * J + i16, 32 * kd, l);
               mma3(acc, fa, fal, fb, fbl);
             } else {
               mma(acc, fa, fb);
@@ -230,6 +215,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
       E* o = reinterpret_cast<E*>(a.out);
 #pragma unroll
       for (int cc = 0; cc < G::CPWV; ++cc) {
+        const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
         const int cn = w + G::NW * cc;
         if (cn >= G::NVT) continue;
         Frag<E> fs[G::DKP / 32], fsl[G::DKP / 32];
@@ -238,16 +224,16 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
           acc_to_frag_split(fs[kb], fsl[kb], S[2 * kb][cc], S[2 * kb + 1][cc]);
         Frag<E> fvt[2];
 #pragma unroll
-        for (int jb = 0; jb < 2; ++jb) frag_tr(fvt[jb], s_v, G::LDV, 32 * jb, 16 * cn);
+        for (int jb = 0; jb < 2; ++jb) frag_tr(fvt[jb], s_v, G::LDV, 32 * jb, 16 * cn, l);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int kb = 0; kb < G::DKP / 32; ++kb) {
             Frag<E> fb, fbl;
-            frag_direct_perm(fb, s_q, G::LDK, 16 * I + i16, 32 * kb);
+            frag_direct_perm(fb, s_q, G::LDK, 16 * I + i16, 32 * kb, l);
             if constexpr (DSP) {
-              frag_direct_perm(fbl, s_ql, G::LDK, 16 * I + i16, 32 * kb);
+              frag_direct_perm(fbl, s_ql, G::LDK, 16 * I + i16, 32 * kb, l);
               mma3(acc, fs[kb], fsl[kb], fb, fbl);
             } else {
               mma2a(acc, fs[kb], fsl[kb], fb);
@@ -258,8 +244,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
           for (int jb = 0; jb < 2; ++jb) {
             if (jb == 1 && I < 2) continue;
             Frag<E> fb, fbl;
-            frag_direct(fb, s_a, G::LDA, 16 * I + i16, 32 * jb);
-            if constexpr (Split<E>::on) frag_direct(fbl, s_al, G::LDA, 16 * I + i16, 32 * jb);
+            frag_direct(fb, s_a, G::LDA, 16 * I + i16, 32 * jb, l);
+            if constexpr (Split<E>::on) frag_direct(fbl, s_al, G::LDA, 16 * I + i16, 32 * jb, l);
             mma2b(acc, fvt[jb], fb, fbl);
           }
           const int n0 = 16 * cn + 4 * g;
@@ -268,7 +254,26 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
       }
     }
 
-    state_update<E, DK, DV, DECAY>(S, s_k, s_kl, s_v, s_gam, s_el, s_fk, seg);
+    // the state entering the chunk, saved for the backward walk: written after
+    // the output tiles and before the update overwrites S (issuing these stores
+    // at the start of the chunk measured slower)
+    if constexpr (APPLY) {
+      if (a.chunk_states) {
+        float* cs = a.chunk_states + ((bh * (a.T / CH) + t0 / CH) * DK) * (int64_t)DV;
+#pragma unroll
+        for (int m = 0; m < G::NKT; ++m)
+#pragma unroll
+          for (int cc = 0; cc < G::CPWV; ++cc) {
+            const int cn = w + G::NW * cc;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int d = 16 * m + 4 * g + rr, n = 16 * cn + i16;
+              if (cn < G::NVT && d < DK && n < DV) cs[d * DV + n] = S[m][cc][rr];
+            }
+          }
+      }
+    }
+    state_update<E, DK, DV, DECAY>(S, s_k, s_kl, s_v, s_gam, s_el, s_fk, seg, lane_pick<APPLY>());
     __syncthreads();
   }
 
