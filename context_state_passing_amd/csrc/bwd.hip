@@ -117,6 +117,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
   const E* qhat_l = SCAL ? s_qhl : s_ql;
 
   const int w = wave_id(), l = lane_id(), g = l >> 4, i16 = l & 15;
+  __builtin_assume(w >= 0 && w < G::NW);
   const int r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int64_t L = a.T / a.P, tshard = r * L;

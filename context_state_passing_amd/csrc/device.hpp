@@ -53,7 +53,8 @@ template <bool FRESH> __device__ __forceinline__ int lane_pick() { return FRESH 
 template <bool FRESH, int NT> __device__ __forceinline__ int tid_pick() {
   return FRESH ? tid_fresh<NT>() : (int)threadIdx.x;
 }
-__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// wave index within the workgroup, uniform (scalar register)
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
 // ---- element traits -------------------------------------------------------------
 

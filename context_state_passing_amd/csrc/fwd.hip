@@ -24,6 +24,7 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* K
                                              const ChunkSeg& seg, int l) {
   using G = Geo<E, DK, DV>;
   const int w = wave_id(), g = l >> 4;
+  __builtin_assume(w >= 0 && w < G::NW);
   const float keep = seg.any() ? 0.f : 1.f;
   if constexpr (DECAY == DECAY_SCALAR) {
     const float sc = keep * __expf(gam[CH - 1]);
@@ -106,6 +107,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
   __shared__ float s_gam[GAM], s_fq[CH], s_fk[CH], s_red[G::NT], s_el[G::DKP];
 
   const int w = wave_id(), l = lane_id(), g = l >> 4, i16 = l & 15;
+  __builtin_assume(w >= 0 && w < G::NW);
   const int r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   const int64_t L = a.T / a.P, tshard = r * L;
