@@ -132,11 +132,6 @@ unsigned threads_for(const cpla_problem* p) {
   return 64u * (unsigned)waves_for(p->dk < 32 ? 32 : (int)p->dk);
 }
 
-int next_pow2(int x) {
-  int g = 1;
-  while (g < x) g <<= 1;
-  return g;
-}
 
 cpla_status launch_scan(const cpla_problem* p, const float* summary, const int32_t* slice, const float* init,
                         float* out, float* fin, int reverse, hipStream_t stream) {
@@ -150,14 +145,12 @@ cpla_status launch_scan(const cpla_problem* p, const float* summary, const int32
   s.m_slot = (int)m_slot_of(p);
   s.diag = p->decay == CPLA_DECAY_DIAG;
   s.reverse = reverse;
-  s.group = next_pow2(p->num_shards);
   s.summary = summary;
   s.slice = slice;
   s.init = init;
   s.out = out;
   s.fin = fin;
-  const int64_t threads = s.n_elem * s.group;
-  const int64_t blocks = (threads + 255) / 256;
+  const int64_t blocks = (s.n_elem + 255) / 256;
   hipLaunchKernelGGL(affine_scan, dim3((unsigned)blocks), dim3(256), 0, stream, s);
   return launched("affine_scan");
 }

@@ -42,7 +42,7 @@ struct BwdArgs {
 
 struct ScanArgs {
   int64_t BH, W, n_elem;     // n_elem = B*H*dk*dv
-  int dk, dv, P, m_slot, diag, reverse, group;
+  int dk, dv, P, m_slot, diag, reverse;
   const float* summary;      // [P,B,H,W]
   const int32_t* slice;      // preceding_rank_start (forward) / following_rank_stop (reverse), or null
   const float* init;         // S_init (forward) / dS_final (reverse), or null

@@ -1,68 +1,61 @@
-// Composition of shard summaries: a wavefront-level segmented associative scan
-// of the affine maps F_r(S) = M_r S + delta_S_r (Megatron-Core page
+// Composition of shard summaries: the exclusive scan of the affine maps
+// F_r(S) = M_r S + delta_S_r over the shards (Megatron-Core page
 // core.ssm.context_parallel.chunkwise: classes CPForward*Summary /
 // CPBackward*Summary and functions chunkwise_cp_forward / chunkwise_cp_backward).
 //
-// Maps compose as (M2, D2) o (M1, D1) = (M2 M1, M2 D1 + D2); M is diagonal (one
-// value per key row), so every state element (d, n) scans independently. A group
-// of `group` = next_pow2(P) lanes holds one element's maps, one shard per lane,
-// and runs a Hillis-Steele scan with segment heads:
-//   forward:  shard r gets fold over [prs_r, r) of the maps, from S_init when the
-//             prefix reaches rank 0 unpacked, else from zero; heads are ranks
-//             with prs_r == r;
-//   reverse:  shard r gets fold over (r, frs_r) taken backwards, from dS_final
-//             when the suffix reaches the last rank unpacked; heads are ranks with
-//             frs_r == r + 1.
-// A shard containing a sequence start has M == 0, so a segment that begins
-// before the slice start yields the same value as the slice itself.
-// The last lane also yields the final state (forward) or dS_init (reverse).
+// M is diagonal (one value per key row d), so every state element (d, n) of
+// every (b, h) composes independently: one thread per element folds the maps
+// in shard order, reading each shard's record with loads that are contiguous
+// across the threads (the element index runs fastest), P of them in flight
+// per batch.
+//   forward:  shard r gets the fold over [prs_r, r), started from S_init at
+//             rank 0 (unpacked) and from zero at ranks with prs_r == r;
+//   reverse:  shard r gets the fold over (r, frs_r) taken backwards, started
+//             from dS_final at the last rank (unpacked) and from zero at ranks
+//             with frs_r == r + 1.
+// A shard that holds a sequence start has M == 0, so carrying the fold through
+// it equals restarting the fold there. After the last shard the running value
+// is the final state (forward) or dS_init (reverse).
 #include "kernels.hpp"
 
 namespace cpla {
 
 __global__ __launch_bounds__(256) void affine_scan(ScanArgs a) {
-  const int64_t gt = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int G = a.group;
-  const int s = (int)(gt % G);
-  const int64_t elem = gt / G;
-  const bool active = elem < a.n_elem;
+  constexpr int BATCH = 8;
+  const int64_t elem = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (elem >= a.n_elem) return;
   const int64_t per = (int64_t)a.dk * a.dv;
-  const int64_t bh = active ? elem / per : 0;
-  const int64_t e = active ? elem % per : 0;
-  const int d = (int)(e / a.dv);
-  const int q = a.reverse ? (a.P - 1 - s) : s;
-  const bool real = active && s < a.P;
+  const int64_t bh = elem / per, e = elem % per;
+  const int m_off = a.diag ? (int)(e / a.dv) : 0;
+  const int64_t rec_stride = a.BH * a.W, out_stride = a.BH * per;
+  const float* rec0 = a.summary + bh * a.W;
+  float* out0 = a.out + bh * per + e;
 
-  float m = 1.f, x = 0.f;
-  int head = 0;
-  if (real) {
-    const float* rec = a.summary + ((int64_t)q * a.BH + bh) * a.W;
-    m = rec[a.diag ? d : 0];
-    x = rec[a.m_slot + e];
-    head = (s == 0);
-    if (a.slice) head |= a.reverse ? (a.slice[q] == q + 1) : (a.slice[q] == q);
-  }
-  const float init = (active && a.init) ? a.init[bh * per + e] : 0.f;
-
-  int f = head;
-  for (int off = 1; off < G; off <<= 1) {
-    const float m2 = __shfl_up(m, off, G);
-    const float x2 = __shfl_up(x, off, G);
-    const int f2 = __shfl_up(f, off, G);
-    if (s >= off && !f) {
-      x = m * x2 + x;
-      m = m * m2;
-      f = f2;
+  float run = a.init ? a.init[bh * per + e] : 0.f;
+  for (int s0 = 0; s0 < a.P; s0 += BATCH) {
+    float m[BATCH], x[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int s = s0 + j;
+      if (s < a.P) {
+        const int q = a.reverse ? a.P - 1 - s : s;
+        const float* rec = rec0 + q * rec_stride;
+        m[j] = rec[m_off];
+        x[j] = rec[a.m_slot + e];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int s = s0 + j;
+      if (s < a.P) {
+        const int q = a.reverse ? a.P - 1 - s : s;
+        if (s > 0 && a.slice && a.slice[q] == (a.reverse ? q + 1 : q)) run = 0.f;
+        out0[q * out_stride] = run;
+        run = m[j] * run + x[j];
+      }
     }
   }
-  // value after applying the inclusive map of lane s to the stream's initial value
-  const float applied = x + m * init;
-  const float prev = __shfl_up(applied, 1, G);
-  if (real) {
-    const float outv = head ? (s == 0 ? init : 0.f) : prev;
-    a.out[((int64_t)q * a.BH + bh) * per + e] = outv;
-    if (a.fin && s == a.P - 1) a.fin[bh * per + e] = applied;
-  }
+  if (a.fin) a.fin[bh * per + e] = run;
 }
 
 }  // namespace cpla
