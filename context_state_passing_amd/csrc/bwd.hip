@@ -100,7 +100,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) char s_reg[REG_BYTES];
   // diagonal apply: exp(Gam) of the chunk in bf16, for the dq / dk output scaling
   // (adds at most 2^-9 relative error to outputs that are rounded to bf16 anyway)
-  constexpr int NRED = DIAG ? G::NT : G::NW;                     // column-scan partials / T3 partials
+  constexpr int NRED = SCAL ? G::NW : 1;                          // scalar decay: per-wave T3 partials
   constexpr int NU = (APPLY && SCAL) ? G::NW * CH : 1;           // scalar dg token partials
   __shared__ float s_gs[DIAG ? 1 : CH], s_fq[CH], s_fk[CH], s_red[NRED], s_el[DIAG ? G::DKP : 1];
   __shared__ float s_t3[(APPLY && DIAG) ? G::DKP : 1];
@@ -198,10 +198,10 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       av_.load(v, b, h, t0, a.T, a.H, tidf);
       ado.load(dO, b, h, t0, a.T, a.H, tidf);
       seg = aseg.finish(a.seq_idx);
-      finish_gamma<DK, DECAY, G::NT>(agam, seg, s_gam, s_fq, s_fk, s_red, tidf);
+      finish_gamma<DK, DECAY, G::NT>(agam, seg, s_gam, s_fq, s_fk, tidf);
     } else {
       seg = rseg.finish(a.seq_idx);
-      finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk, s_red);
+      finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk);
     }
     any_start |= seg.any();
     const float keep = seg.any() ? 0.f : 1.f;

@@ -79,14 +79,22 @@ struct SegRegs {
 // token tid.
 template <int DK, int DECAY, int NT>
 struct GamRegs {
+  // diagonal: TPC threads share a key column, each holding TOK consecutive
+  // tokens; the TPC parts of a column sit in one wave (lane = part * CPW + j,
+  // column = wave * CPW + j), so the running totals pass between parts by
+  // shuffles instead of through LDS
   static constexpr int TPC = (DECAY == DECAY_DIAG) ? NT / DK : 1;
   static constexpr int TOK = (DECAY == DECAY_DIAG) ? CH / TPC : 1;
+  static constexpr int CPW = 64 / TPC;
+  static_assert(DECAY != DECAY_DIAG || (TPC <= 64 && 64 % TPC == 0), "column split must fit a wave");
   float v[TOK];
+  __device__ __forceinline__ static int column(int tid) { return (tid >> 6) * CPW + (tid & 63) % CPW; }
+  __device__ __forceinline__ static int part(int tid) { return (tid & 63) / CPW; }
   __device__ __forceinline__ void load(const float* __restrict__ g, int64_t b, int64_t h, int64_t t0, int64_t T,
                                        int64_t H, int tid = threadIdx.x) {
     if constexpr (DECAY == DECAY_DIAG) {
-      const int d = tid % DK, part = tid / DK;
-      const float* src = g + ((b * T + t0 + part * TOK) * H + h) * DK + d;
+      const int d = column(tid);
+      const float* src = g + ((b * T + t0 + part(tid) * TOK) * H + h) * DK + d;
 #pragma unroll
       for (int s = 0; s < TOK; ++s) v[s] = src[(int64_t)s * H * DK];
     } else if constexpr (DECAY == DECAY_SCALAR) {
@@ -100,10 +108,10 @@ struct GamRegs {
 // and the per-token factors
 //   fq[i] = live_i * (scalar ? exp(Gam_i) : 1)
 //   fk[j] = tail_j * (scalar ? exp(Gam_last - Gam_j) : 1)
-// `red` is NT floats of scratch. Ends with a barrier.
+// Ends with a barrier.
 template <int DK, int DECAY, int NT>
 __device__ __forceinline__ void finish_gamma(GamRegs<DK, DECAY, NT>& R, const ChunkSeg& seg, float* gam,
-                                             float* fq, float* fk, float* red, int tid = threadIdx.x) {
+                                             float* fq, float* fk, int tid = threadIdx.x) {
   if constexpr (DECAY == DECAY_SCALAR) {
     if (tid < CH) {
       float x = R.v[0];
@@ -119,14 +127,18 @@ __device__ __forceinline__ void finish_gamma(GamRegs<DK, DECAY, NT>& R, const Ch
     }
   } else {
     if constexpr (DECAY == DECAY_DIAG) {
-      constexpr int TOK = GamRegs<DK, DECAY, NT>::TOK;
-      const int d = tid % DK, part = tid / DK;
+      using GR = GamRegs<DK, DECAY, NT>;
+      constexpr int TOK = GR::TOK;
+      const int d = GR::column(tid), part = GR::part(tid), j = (tid & 63) % GR::CPW;
 #pragma unroll
       for (int s = 1; s < TOK; ++s) R.v[s] += R.v[s - 1];
-      red[part * DK + d] = R.v[TOK - 1];
-      __syncthreads();
+      // totals of the earlier parts of this column (lanes p * CPW + j of this wave)
       float off = 0.f;
-      for (int pp = 0; pp < part; ++pp) off += red[pp * DK + d];
+#pragma unroll
+      for (int p = 0; p + 1 < GR::TPC; ++p) {
+        const float tp = __shfl(R.v[TOK - 1], p * GR::CPW + j, 64);
+        if (p < part) off += tp;
+      }
 #pragma unroll
       for (int s = 0; s < TOK; ++s) gam[(part * TOK + s) * DK + d] = R.v[s] + off;
     }

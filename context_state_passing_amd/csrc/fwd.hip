@@ -104,7 +104,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
   constexpr int NAL = (APPLY && Split<E>::on) ? 1 : 0;
   __shared__ __attribute__((aligned(16))) E s_a[NQT * G::TILE_A + 8];    // scores, hi part
   __shared__ __attribute__((aligned(16))) E s_al[NAL * G::TILE_A + 8];   // scores, lo part
-  __shared__ float s_gam[GAM], s_fq[CH], s_fk[CH], s_red[G::NT], s_el[G::DKP];
+  __shared__ float s_gam[GAM], s_fq[CH], s_fk[CH], s_el[G::DKP];
 
   const int w = wave_id(), l = lane_id(), g = l >> 4, i16 = l & 15;
   __builtin_assume(w >= 0 && w < G::NW);
@@ -156,7 +156,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
     const int64_t t0 = tshard + (int64_t)c * CH;
     const ChunkSeg seg = rseg.finish(a.seq_idx);
     any_start |= seg.any();
-    finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk, s_red);
+    finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk);
     if constexpr (DECAY == DECAY_DIAG) {
       if (threadIdx.x < DK) {
         const float gl = s_gam[(CH - 1) * DK + threadIdx.x];
