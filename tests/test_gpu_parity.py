@@ -47,6 +47,24 @@ SMALL = {
     "single_shard_bwd": ("diag_fwdbwd", {"B": 1, "H": 1, "T": 256, "num_shards": 1}, True),
     "scalar_d16_bf16_bwd": ("scalar_fwd", {"B": 1, "H": 2, "T": 512, "d": 16, "num_shards": 2,
                                            "backward": True}, True),
+    # edge cases: one chunk per shard; the largest shard count; no decay at d=128 bf16;
+    # diagonal decay at d=16 in both dtypes; many (b, h) rows
+    "one_chunk_shards_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 256, "num_shards": 4}, True),
+    "max_shards_bwd": ("scalar_fwd", {"B": 1, "H": 1, "T": 4096, "d": 16, "num_shards": 64,
+                                      "backward": True}, True),
+    "identity_d128_bf16_bwd": ("identity_fwd", {"B": 1, "H": 2, "T": 512, "d": 128, "num_shards": 2,
+                                                "backward": True, "dtype": torch.bfloat16}, True),
+    "diag_d16_bf16_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 512, "d": 16, "num_shards": 4}, True),
+    "diag_d16_fp32_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 256, "d": 16, "num_shards": 2,
+                                          "dtype": torch.float32}, True),
+    "many_rows_bwd": ("scalar_fwd", {"B": 3, "H": 40, "T": 128, "d": 16, "num_shards": 2,
+                                     "backward": True}, True),
+    # packed edge cases: every start on a chunk (and shard) boundary; one token per
+    # sequence (every chunk holds 64 starts); one sequence covering the whole stream
+    "packed_aligned_bwd": ("packed_fwdbwd", {"T": 1024, "H": 2, "num_shards": 4, "len_range": (128, 128)}, True),
+    "packed_len1_bwd": ("packed_fwdbwd", {"T": 256, "H": 1, "num_shards": 2, "len_range": (1, 1)}, True),
+    "packed_one_seq_bwd": ("packed_fwdbwd", {"T": 1024, "H": 2, "num_shards": 4, "len_range": (4096, 4096)},
+                           True),
 }
 
 
