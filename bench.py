@@ -120,8 +120,12 @@ def _oracle_row(args):
         seq = omd.seq_idx_from_cu_seqlens(wl.cu_seqlens.numpy(), wl.T)
     with threadpool_limits(1):
         t = time.perf_counter()
-        ocp.cp_backward(sl(wl.q), sl(wl.k), sl(wl.v), sl(wl.g), wl.decay, sl(wl.dO), wl.num_shards,
-                        initial_state=S0, seq_idx=seq)
+        if wl.dO is None:
+            ocp.cp_forward(sl(wl.q), sl(wl.k), sl(wl.v), sl(wl.g), wl.decay, wl.num_shards,
+                           initial_state=S0, seq_idx=seq)
+        else:
+            ocp.cp_backward(sl(wl.q), sl(wl.k), sl(wl.v), sl(wl.g), wl.decay, sl(wl.dO), wl.num_shards,
+                            initial_state=S0, seq_idx=seq)
         return time.perf_counter() - t
 
 
@@ -141,7 +145,8 @@ def cpu_baseline(wl, rows_req):
     wall = time.perf_counter() - t0
     tok_heads = rows * wl.T
     return {"value": tok_heads / wl.H / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-            "sample": f"fp64 oracle CP fwd+bwd (summaries, composition, per-token recurrence and adjoint) on "
+            "sample": f"fp64 oracle CP {'fwd' if wl.dO is None else 'fwd+bwd'} (summaries, composition, "
+                      f"per-token recurrence{'' if wl.dO is None else ' and adjoint'}) on "
                       f"{rows} of the {wl.B * wl.H} (b,h) rows at full T={wl.T}, {wl.num_shards} shards; "
                       f"{workers} single-threaded processes, wall {wall:.1f}s, {sum(per):.1f} CPU-s; "
                       f"value = row-tokens/s / H",
@@ -173,7 +178,7 @@ def main():
     dev = torch.device("cuda:0")
     q, k, v = wl.q.to(dev), wl.k.to(dev), wl.v.to(dev)
     g = None if wl.g is None else wl.g.to(dev)
-    dO = wl.dO.to(dev)
+    dO = None if wl.dO is None else wl.dO.to(dev)
     S0 = None if wl.initial_state is None else wl.initial_state.to(dev)
     decay = {"none": 0, "scalar": 1, "diag": 2}[wl.decay]
     p = make_problem(q, v, wl.num_shards, decay)
@@ -201,23 +206,27 @@ def main():
     pp = ctypes.byref(p)
     chk = _lib.check
 
+    backward = dO is not None
+
     def step(ev=None):
         if ev: ev[0].record(stream)
         chk(L.cp_forward_prepare(pp, pk, _ptr(k), _ptr(v), _ptr(g), _ptr(fsum), sp))
         if ev: ev[1].record(stream)
         chk(L.cp_forward_apply(pp, pk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(fsum), _ptr(S0), _ptr(o),
-                               _ptr(s_in), _ptr(fin), _ptr(cs), sp))
+                               _ptr(s_in), _ptr(fin), _ptr(cs) if backward else None, sp))
         if ev: ev[2].record(stream)
-        chk(L.cp_backward_prepare(pp, pk, _ptr(q), _ptr(g), _ptr(dO), _ptr(bsum), sp))
-        if ev: ev[3].record(stream)
-        chk(L.cp_backward_apply(pp, pk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dO), _ptr(cs), _ptr(bsum),
-                                None, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(s_out), _ptr(dS0), sp))
-        if ev: ev[4].record(stream)
+        if backward:
+            chk(L.cp_backward_prepare(pp, pk, _ptr(q), _ptr(g), _ptr(dO), _ptr(bsum), sp))
+            if ev: ev[3].record(stream)
+            chk(L.cp_backward_apply(pp, pk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(dO), _ptr(cs), _ptr(bsum),
+                                    None, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(s_out), _ptr(dS0), sp))
+            if ev: ev[4].record(stream)
 
+    nev = 5 if backward else 3
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -227,20 +236,39 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    parts = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(4)]
-    names = ["cp_forward_prepare", "cp_forward_apply", "cp_backward_prepare", "cp_backward_apply"]
+    parts = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(nev - 1)]
+    names = ["cp_forward_prepare", "cp_forward_apply", "cp_backward_prepare", "cp_backward_apply"][:nev - 1]
+
+    # Cold caches: before each of a few steps (outside the timed region) write a
+    # 512 MiB scratch buffer so that no input is still resident in L2 or the MALL.
+    cold = []
+    flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
+    for i in range(min(args.steps, 10)):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cold.append(e0.elapsed_time(e1))
+    cold.sort()
+    del flush
 
     tokens = B * T
     th = tokens * H
     alg = algorithmic(wl)
-    dom_ms = parts[3]
-    dom_bytes = alg["bytes_bwd_apply"] * th
+    if backward:
+        dom_ms, dom_bytes, dom_name = parts[3], alg["bytes_bwd_apply"] * th, "bwd_walk (cp_backward_apply)"
+        traffic, tnote = read_traffic()
+    else:
+        dom_ms, dom_bytes, dom_name = parts[1], alg["bytes_fwd"] * th, "fwd_walk (cp_forward_apply)"
+        traffic, tnote = None, "counters are taken for the backward walk of the default workload"
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic, tnote = read_traffic()
-    step_bytes = (alg["bytes_fwd"] + alg["bytes_bwd_apply"]) * th
-    step_flops = (alg["flops_fwd"] + alg["flops_bwd"]) * th
+    step_bytes = (alg["bytes_fwd"] + (alg["bytes_bwd_apply"] if backward else 0)) * th
+    step_flops = (alg["flops_fwd"] + (alg["flops_bwd"] if backward else 0)) * th
     out = {
-        "metric": METRIC,
+        "metric": METRIC if wl.name == "diag_fwdbwd" else
+                  f"{'fwd+bwd' if backward else 'fwd'} tokens/s, {wl.name} (B{B} H{H} T{T} d{d} {wl.decay} decay)",
         "value": tokens / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -254,7 +282,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "dk": d, "dv": d, "chunk": wl.chunk,
                    "shards": P, "decay": wl.decay, "parallelism": "single-gpu (shards simulated in HBM)"},
-        "roofline": {"bound": "hbm", "kernel": "bwd_walk (cp_backward_apply)", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "traffic_note": tnote,
                      "algorithmic_bytes_per_launch": dom_bytes, "launch_ms": dom_ms},
@@ -264,6 +292,9 @@ def main():
                           "mfma_TFLOPs": step_flops / (ms_step * 1e-3) / 1e12,
                           "mfma_frac": step_flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "fwd_tokens_per_s": tokens / ((parts[0] + parts[1]) * 1e-3),
+        "cold_cache": {"ms_per_step_median": cold[len(cold) // 2], "ms_per_step_min": cold[0],
+                       "tokens_per_s": tokens / (cold[len(cold) // 2] * 1e-3), "steps": len(cold),
+                       "note": "512 MiB written before each step (outside the timed region) to evict L2 and MALL"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
