@@ -31,7 +31,11 @@
  *       q, k      [B, T, H, dk]   dtype (bf16 or fp32)
  *       v, o, dO  [B, T, H, dv]   dtype
  *       g, dg     scalar decay [B, T, H] fp32; diagonal decay [B, T, H, dk]
- *                 fp32; no decay: NULL
+ *                 fp32; no decay: NULL. g <= 0 (log of a decay in (0, 1]).
+ *                 Diagonal decay: within every 64-token chunk the running
+ *                 sum of g per key dim must stay above about -80 (the kernels
+ *                 factor the decay into exp(+-sum) that must stay finite in
+ *                 fp32); stronger decays are outside the supported range.
  *       states    [B, H, dk, dv] fp32 (S_init, final state and their grads)
  *       summaries [P, B, H, W] fp32, W = cpla_summary_width(): the first
  *                 m_slot entries hold the transition M (dk values for a
