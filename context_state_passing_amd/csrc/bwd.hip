@@ -103,7 +103,6 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
   constexpr int NRED = SCAL ? G::NW : 1;                          // scalar decay: per-wave T3 partials
   constexpr int NU = (APPLY && SCAL) ? G::NW * CH : 1;           // scalar dg token partials
   __shared__ float s_gs[DIAG ? 1 : CH], s_fq[CH], s_fk[CH], s_red[NRED], s_el[DIAG ? G::DKP : 1];
-  __shared__ float s_t3[(APPLY && DIAG) ? G::DKP : 1];
   __shared__ float s_u1[NU], s_u4[NU];
 
   float* s_gam = DIAG ? reinterpret_cast<float*>(s_reg) : s_gs;
@@ -399,6 +398,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       // loop, then r_t = z_t - w_t with z_t = K~*(tail Y'); dg_t = sum_s w_s + T3 +
       // sum_{s<t} r_s (suffix sums of w plus prefix sums of z, rearranged)
       f32x4 wv[G::CPWK][4], wtot[G::CPWK];
+      float t3r[DIAG ? G::CPWK : 1];   // diagonal: T3 of the lane's key dim 16 cm + i16
 #pragma unroll
       for (int cc = 0; cc < G::CPWK; ++cc) {
         const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
@@ -439,7 +439,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
           t3 += __shfl_xor(t3, 16, 64);
           t3 += __shfl_xor(t3, 32, 64);
           if constexpr (DIAG) {
-            if (g == 0) s_t3[dl] = t3;   // dS^T already carries exp(Gam_last[d])
+            t3r[cc] = t3;   // for key dim dl in every lane of column i16; dS^T carries exp(Gam_last[d])
           } else {
             if (g == 0) t3p += t3;
           }
@@ -564,7 +564,6 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       }
 
       if constexpr (DIAG) {
-        __syncthreads();  // s_t3 complete
 #pragma unroll
         for (int cc = 0; cc < G::CPWK; ++cc) {
           const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
@@ -573,7 +572,10 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
           const int d0 = 16 * cm + 4 * g;
           f32x4 t3v;
 #pragma unroll
-          for (int rr = 0; rr < 4; ++rr) t3v[rr] = (d0 + rr < DK) ? keep * s_t3[d0 + rr] : 0.f;
+          for (int rr = 0; rr < 4; ++rr) {
+            const float t3 = __shfl(t3r[cc], 4 * g + rr, 64);   // lane 4g + rr holds key dim d0 + rr
+            t3v[rr] = (d0 + rr < DK) ? keep * t3 : 0.f;
+          }
           // total of w over the 64 tokens, and exclusive prefix sums of r over them
           const f32x4 base = row_last(row_scan(wtot[cc])) + t3v;
           f32x4 pre_tot = {0.f, 0.f, 0.f, 0.f};
