@@ -70,7 +70,7 @@ __device__ __forceinline__ f32x4 lane_gamma(f32x4 x, f32x4& carry) {
 }
 
 template <typename E, int DK, int DV, int DECAY, bool APPLY>
-__global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
+__global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_walk(BwdArgs a) {
   using G = Geo<E, DK, DV>;
   constexpr bool SP = Split<E>::on;
   constexpr bool DIAG = DECAY == DECAY_DIAG, SCAL = DECAY == DECAY_SCALAR;
@@ -83,8 +83,11 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
   // Q^ = q exp(Gam_i) live_i (scalar decay), split
   constexpr int QH = SCAL ? 1 : 0;
   constexpr int QHL = (SCAL && SP) ? 1 : 0;
-  // region: Gam (diag, fp32) during staging, then A/dA hi/lo and the scalar P tile
-  constexpr int GAM_BYTES = DIAG ? CH * DK * 4 : 0;
+  // region: Gam (diag, fp32) during staging, then A/dA hi/lo and the scalar P tile.
+  // The prepare walk (two workgroups per CU) stages Gam rows 32..63 in the dO
+  // tile's buffer, written after the q tile is scaled.
+  constexpr bool GSPLIT = !APPLY && DIAG;
+  constexpr int GAM_BYTES = DIAG ? (GSPLIT ? CH / 2 : CH) * DK * 4 : 0;
   constexpr int AT_BYTES = APPLY ? (SP ? 4 : 2) * G::TILE_A * (int)sizeof(E) : 0;
   constexpr int P_BYTES = (APPLY && SCAL) ? CH * (CH + 1) * 4 : 0;
   constexpr int REG_BYTES = (GAM_BYTES > AT_BYTES + P_BYTES ? GAM_BYTES : AT_BYTES + P_BYTES) + 16;
@@ -98,8 +101,6 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) E s_qh[QH * G::TILE_K + 8];
   __shared__ __attribute__((aligned(16))) E s_qhl[QHL * G::TILE_K + 8];
   __shared__ __attribute__((aligned(16))) char s_reg[REG_BYTES];
-  // diagonal apply: exp(Gam) of the chunk in bf16, for the dq / dk output scaling
-  // (adds at most 2^-9 relative error to outputs that are rounded to bf16 anyway)
   constexpr int NRED = SCAL ? G::NW : 1;                          // scalar decay: per-wave T3 partials
   constexpr int NU = (APPLY && SCAL) ? G::NW * CH : 1;           // scalar dg token partials
   __shared__ float s_gs[DIAG ? 1 : CH], s_fq[CH], s_fk[CH], s_red[NRED], s_el[DIAG ? G::DKP : 1];
@@ -114,6 +115,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
   // the tile Q^ is read from in the dS update: scalar -> s_qh, else the q tile
   const E* qhat_h = SCAL ? s_qh : s_q;
   const E* qhat_l = SCAL ? s_qhl : s_ql;
+  float* const gam_hi = GSPLIT ? reinterpret_cast<float*>(s_do) : nullptr;
+  const float* const gam_last = GSPLIT ? gam_hi + (CH / 2 - 1) * DK : s_gam + (CH - 1) * DK;
 
   const int w = wave_id(), l = lane_id(), g = l >> 4, i16 = l & 15;
   __builtin_assume(w >= 0 && w < G::NW);
@@ -162,53 +165,35 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
   float gsum = 0.f;
   bool any_start = false;
 
-  // prefetch registers for the next chunk's inputs (walk goes backwards)
-  SegRegs rseg;
-  GamRegs<DK, DECAY, G::NT> rgam;
-  TileRegs<E, DK, G::NT> rq;
-  TileRegs<E, DV, G::NT> rdo;
-  auto prefetch = [&](int c) {
-    const int64_t t = tshard + (int64_t)c * CH;
-    rseg.load(a.seq_idx, t);
-    rgam.load(a.g, b, h, t, a.T, a.H);
-    rq.load(q, b, h, t, a.T, a.H);
-    rdo.load(dO, b, h, t, a.T, a.H);
-  };
-  // The prepare walk overlaps the next chunk's loads with its compute; the apply
-  // walk is register-bound and stages each chunk straight from global memory.
-  if constexpr (!APPLY) prefetch(nc - 1);
-
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t t0 = tshard + (int64_t)c * CH;
     ChunkSeg seg;
-    // apply walk: every global load of the chunk's inputs is issued before the
-    // first use, so the chunk waits on memory once; the registers are free again
-    // once the tiles are in LDS (the walk's compute needs them)
+    // Every global load of the chunk's inputs is issued before the first use, so
+    // the chunk waits on memory once; the registers are free again once the tiles
+    // are in LDS (the apply walk's compute needs them; the prepare walk runs two
+    // workgroups per CU, which cover each other's waits).
     SegRegs aseg;
     GamRegs<DK, DECAY, G::NT> agam;
     TileRegs<E, DK, G::NT> aq, ak;
     TileRegs<E, DV, G::NT> av_, ado;
     const int tidf = tid_pick<APPLY, G::NT>();
+    aseg.load(a.seq_idx, t0, tidf & 63);
+    agam.load(a.g, b, h, t0, a.T, a.H, tidf);
+    aq.load(q, b, h, t0, a.T, a.H, tidf);
     if constexpr (APPLY) {
-      aseg.load(a.seq_idx, t0, tidf & 63);
-      agam.load(a.g, b, h, t0, a.T, a.H, tidf);
-      aq.load(q, b, h, t0, a.T, a.H, tidf);
       ak.load(k, b, h, t0, a.T, a.H, tidf);
       av_.load(v, b, h, t0, a.T, a.H, tidf);
-      ado.load(dO, b, h, t0, a.T, a.H, tidf);
-      seg = aseg.finish(a.seq_idx);
-      finish_gamma<DK, DECAY, G::NT>(agam, seg, s_gam, s_fq, s_fk, tidf);
-    } else {
-      seg = rseg.finish(a.seq_idx);
-      finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk);
     }
+    ado.load(dO, b, h, t0, a.T, a.H, tidf);
+    seg = aseg.finish(a.seq_idx);
+    finish_gamma<DK, DECAY, G::NT>(agam, seg, s_gam, s_fq, s_fk, tidf, gam_hi);
     any_start |= seg.any();
     const float keep = seg.any() ? 0.f : 1.f;
 
     // ---- stage tiles ----------------------------------------------------------------
     if constexpr (DIAG) {
       if (threadIdx.x < DK) {
-        const float gl = s_gam[(CH - 1) * DK + threadIdx.x];
+        const float gl = gam_last[threadIdx.x];
         gsum += gl;
         s_el[threadIdx.x] = __expf(gl);   // exp(Gam_last[d]), read by every row scaling below
       } else if (threadIdx.x < G::DKP) {
@@ -229,14 +214,17 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void bwd_walk(BwdArgs a) {
       store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(ado, s_do, nullptr, s_gam, nullptr, tidf);
       store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(av_, s_v, nullptr, s_gam, nullptr, tidf);
     } else {
-      if constexpr (DIAG) store_tile<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(rq, s_q, s_ql, s_gam, nullptr, tidf);
-      else if constexpr (SCAL) store_tile<E, DK, G::DKP, G::LDK, 3, DK, G::NT>(rq, s_qh, s_qhl, s_gam, s_fq, tidf);
-      else store_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(rq, s_q, nullptr, s_gam, nullptr, tidf);
-      store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(rdo, s_do, nullptr, s_gam, nullptr, tidf);
+      if constexpr (DIAG) {
+        store_tile<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(aq, s_q, s_ql, s_gam, nullptr, tidf, gam_hi);
+        __syncthreads();   // the dO tile overwrites Gam rows 32..63
+      } else if constexpr (SCAL) {
+        store_tile<E, DK, G::DKP, G::LDK, 3, DK, G::NT>(aq, s_qh, s_qhl, s_gam, s_fq, tidf);
+      } else {
+        store_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(aq, s_q, nullptr, s_gam, nullptr, tidf);
+      }
+      store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(ado, s_do, nullptr, s_gam, nullptr, tidf);
     }
     __syncthreads();
-    if constexpr (!APPLY)
-      if (c > 0) prefetch(c - 1);
 
     if constexpr (DIAG) {
       // dS' = diag(exp(Gam_last)) dS, the adjoint as the chunk's tail tokens see it

@@ -104,14 +104,18 @@ struct GamRegs {
 };
 
 // The chunk's cumulative log-decay from the loaded registers, into LDS:
-//   scalar: gam[i] (64 floats);  diagonal: gam[i * DK + d];  none: nothing.
+//   scalar: gam[i] (64 floats);  diagonal: rows i < 32 at gam[i * DK + d] and
+//   rows i >= 32 at gam_hi[(i - 32) * DK + d] (gam_hi = gam + 32 * DK when null:
+//   one contiguous tile; a walk short of LDS passes a buffer it reuses later);
+//   none: nothing.
 // and the per-token factors
 //   fq[i] = live_i * (scalar ? exp(Gam_i) : 1)
 //   fk[j] = tail_j * (scalar ? exp(Gam_last - Gam_j) : 1)
 // Ends with a barrier.
 template <int DK, int DECAY, int NT>
 __device__ __forceinline__ void finish_gamma(GamRegs<DK, DECAY, NT>& R, const ChunkSeg& seg, float* gam,
-                                             float* fq, float* fk, int tid = threadIdx.x) {
+                                             float* fq, float* fk, int tid = threadIdx.x,
+                                             float* gam_hi = nullptr) {
   if constexpr (DECAY == DECAY_SCALAR) {
     if (tid < CH) {
       float x = R.v[0];
@@ -139,8 +143,12 @@ __device__ __forceinline__ void finish_gamma(GamRegs<DK, DECAY, NT>& R, const Ch
         const float tp = __shfl(R.v[TOK - 1], p * GR::CPW + j, 64);
         if (p < part) off += tp;
       }
+      float* const g1 = gam_hi ? gam_hi - 32 * DK : gam;
 #pragma unroll
-      for (int s = 0; s < TOK; ++s) gam[(part * TOK + s) * DK + d] = R.v[s] + off;
+      for (int s = 0; s < TOK; ++s) {
+        const int t = part * TOK + s;
+        (t < 32 ? gam : g1)[t * DK + d] = R.v[s] + off;
+      }
     }
     if (tid < CH) {
       fq[tid] = seg.live(tid) ? 1.f : 0.f;
@@ -173,12 +181,15 @@ struct TileRegs {
 
 // Write prefetched vectors to LDS (row stride LD), zero-filling columns D..DP-1.
 // MODE 0: copy into `hi`; 1: x*exp(Gam[i][d]); 2: x*exp(-Gam[i][d]); 3: x*fac[i] --
-// scaled modes are stored split (hi, and lo for bf16). No barrier.
+// scaled modes are stored split (hi, and lo for bf16). Gam rows as finish_gamma
+// wrote them (gam_hi: rows 32..63, null for one contiguous tile). No barrier.
 template <typename E, int D, int DP, int LD, int MODE, int DK, int NT>
 __device__ __forceinline__ void store_tile(const TileRegs<E, D, NT>& R, E* hi, E* lo, const float* gam,
-                                           const float* fac, int tid = threadIdx.x) {
+                                           const float* fac, int tid = threadIdx.x,
+                                           const float* gam_hi = nullptr) {
   using TR = TileRegs<E, D, NT>;
   constexpr int VEC = TR::VEC;
+  const float* const g1 = gam_hi ? gam_hi - 32 * DK : gam;
 #pragma unroll
   for (int p = 0; p < TR::PER; ++p) {
     const int v = tid + p * NT;
@@ -197,10 +208,11 @@ __device__ __forceinline__ void store_tile(const TileRegs<E, D, NT>& R, E* hi, E
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = R.r[p][e];
     }
+    const float* const grow = (i < 32 ? gam : g1) + i * DK + c;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      if constexpr (MODE == 1) x[e] *= __expf(gam[i * DK + c + e]);
-      if constexpr (MODE == 2) x[e] *= __expf(-gam[i * DK + c + e]);
+      if constexpr (MODE == 1) x[e] *= __expf(grow[e]);
+      if constexpr (MODE == 2) x[e] *= __expf(-grow[e]);
       if constexpr (MODE == 3) x[e] *= fac[i];
     }
     if constexpr (sizeof(E) == 2) {

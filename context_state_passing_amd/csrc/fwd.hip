@@ -91,9 +91,12 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* K
 }
 
 template <typename E, int DK, int DV, int DECAY, bool APPLY>
-__global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
+__global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_walk(FwdArgs a) {
   using G = Geo<E, DK, DV>;
-  constexpr int GAM = (DECAY == DECAY_DIAG) ? CH * DK : CH;
+  // diagonal decay: the prepare walk stages Gam rows 32..63 in the v tile's buffer
+  // (written after the k tile is scaled), so two workgroups fit in a CU's LDS
+  constexpr bool GSPLIT = !APPLY && DECAY == DECAY_DIAG;
+  constexpr int GAM = (DECAY == DECAY_DIAG) ? (GSPLIT ? CH / 2 : CH) * DK : CH;
   constexpr int NQT = APPLY ? 1 : 0;
   constexpr int DSP = (DECAY == DECAY_DIAG && Split<E>::on) ? 1 : 0;   // exp-scaled tiles split
   __shared__ __attribute__((aligned(16))) E s_q[NQT * G::TILE_K + 8];
@@ -105,6 +108,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) E s_a[NQT * G::TILE_A + 8];    // scores, hi part
   __shared__ __attribute__((aligned(16))) E s_al[NAL * G::TILE_A + 8];   // scores, lo part
   __shared__ float s_gam[GAM], s_fq[CH], s_fk[CH], s_el[G::DKP];
+
+  float* const gam_hi = GSPLIT ? reinterpret_cast<float*>(s_v) : nullptr;
+  const float* const gam_last = GSPLIT ? gam_hi + (CH / 2 - 1) * DK : s_gam + (CH - 1) * DK;
 
   const int w = wave_id(), l = lane_id(), g = l >> 4, i16 = l & 15;
   __builtin_assume(w >= 0 && w < G::NW);
@@ -137,7 +143,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
   float gsum = 0.f;          // total log-decay of the shard (diag: column tid; else thread 0)
   bool any_start = false;
 
-  // prefetch registers for the next chunk's inputs
+  // prefetch registers for the next chunk's inputs (apply); the prepare walk runs
+  // two workgroups per CU and loads each chunk when it starts it
   SegRegs rseg;
   GamRegs<DK, DECAY, G::NT> rgam;
   TileRegs<E, DK, G::NT> rk, rq;
@@ -150,21 +157,23 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
     if constexpr (APPLY) rq.load(q, b, h, t, a.T, a.H);
     rv.load(v, b, h, t, a.T, a.H);
   };
-  prefetch(0);
+  if constexpr (APPLY) prefetch(0);
 
   for (int c = 0; c < nc; ++c) {
     const int64_t t0 = tshard + (int64_t)c * CH;
+    if constexpr (!APPLY) prefetch(c);
     const ChunkSeg seg = rseg.finish(a.seq_idx);
     any_start |= seg.any();
-    finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk);
+    finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk, threadIdx.x, gam_hi);
     if constexpr (DECAY == DECAY_DIAG) {
       if (threadIdx.x < DK) {
-        const float gl = s_gam[(CH - 1) * DK + threadIdx.x];
+        const float gl = gam_last[threadIdx.x];
         gsum += gl;
         s_el[threadIdx.x] = __expf(gl);   // exp(Gam_last[d]) for the state's row scaling
       }
-      store_tile<E, DK, G::DKP, G::LDK, 2, DK, G::NT>(rk, s_k, s_kl, s_gam, nullptr);
+      store_tile<E, DK, G::DKP, G::LDK, 2, DK, G::NT>(rk, s_k, s_kl, s_gam, nullptr, threadIdx.x, gam_hi);
       if constexpr (APPLY) store_tile<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(rq, s_q, s_ql, s_gam, nullptr);
+      if constexpr (GSPLIT) __syncthreads();   // the v tile overwrites Gam rows 32..63
     } else {
       if constexpr (DECAY == DECAY_SCALAR)
         if (threadIdx.x == 0) gsum += s_gam[CH - 1];
@@ -172,7 +181,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT)) void fwd_walk(FwdArgs a) {
       if constexpr (APPLY) store_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(rq, s_q, nullptr, s_gam, nullptr);
     }
     store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(rv, s_v, nullptr, s_gam, nullptr);
-    if (c + 1 < nc) prefetch(c + 1);
+    if constexpr (APPLY)
+      if (c + 1 < nc) prefetch(c + 1);
 
     __syncthreads();
 
