@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="diag_fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra steps timed one by one after evicting L2 and the MALL (0 = skip)")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows (b,h) in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
@@ -242,8 +244,8 @@ def main():
     # Cold caches: before each of a few steps (outside the timed region) write a
     # 512 MiB scratch buffer so that no input is still resident in L2 or the MALL.
     cold = []
-    flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
-    for i in range(min(args.steps, 10)):
+    flush = torch.empty(512 << 18, dtype=torch.float32, device=dev) if args.cold_steps > 0 else None
+    for i in range(args.cold_steps):
         flush.fill_(float(i))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -292,9 +294,10 @@ def main():
                           "mfma_TFLOPs": step_flops / (ms_step * 1e-3) / 1e12,
                           "mfma_frac": step_flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
         "fwd_tokens_per_s": tokens / ((parts[0] + parts[1]) * 1e-3),
-        "cold_cache": {"ms_per_step_median": cold[len(cold) // 2], "ms_per_step_min": cold[0],
-                       "tokens_per_s": tokens / (cold[len(cold) // 2] * 1e-3), "steps": len(cold),
-                       "note": "512 MiB written before each step (outside the timed region) to evict L2 and MALL"},
+        "cold_cache": None if not cold else {
+            "ms_per_step_median": cold[len(cold) // 2], "ms_per_step_min": cold[0],
+            "tokens_per_s": tokens / (cold[len(cold) // 2] * 1e-3), "steps": len(cold),
+            "note": "512 MiB written before each step (outside the timed region) to evict L2 and MALL"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
