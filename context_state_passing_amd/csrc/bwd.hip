@@ -277,24 +277,28 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
             mma(xd, fa, fb);
           }
         }
+        // the tiles are stored transposed (row = key token j, column = query token
+        // i): the lane's four rows i become one 8-byte write per part
+        f32x4 va = {0.f, 0.f, 0.f, 0.f}, vd = {0.f, 0.f, 0.f, 0.f};
+        const int j = 16 * J + i16;
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int i = 16 * I + 4 * g + rr, j = 16 * J + i16;
-          float va = 0.f, vd = 0.f, pp = 0.f;
+          const int i = 16 * I + 4 * g + rr;
+          float pp = 0.f;
           if (seg.same(i, j)) {
-            va = xa[rr];
-            vd = xd[rr];
+            va[rr] = xa[rr];
+            vd[rr] = xd[rr];
             if constexpr (SCAL) {
               const float dec = __expf(s_gam[i] - s_gam[j]);
-              pp = va * vd * dec;      // one decay factor: exp(Gam_i - Gam_j) (q_i.k_j)(dO_i.v_j)
-              va *= dec;
-              vd *= dec;
+              pp = va[rr] * vd[rr] * dec;   // one decay factor: exp(Gam_i - Gam_j) (q_i.k_j)(dO_i.v_j)
+              va[rr] *= dec;
+              vd[rr] *= dec;
             }
           }
-          store_split(s_ah, s_al, i * G::LDA + j, va);
-          store_split(s_dah, s_dal, i * G::LDA + j, vd);
           if constexpr (SCAL) s_p[i * (CH + 1) + j] = pp;
         }
+        store_split4(s_ah, s_al, j * G::LDA + 16 * I + 4 * g, va);
+        store_split4(s_dah, s_dal, j * G::LDA + 16 * I + 4 * g, vd);
       }
       __syncthreads();
 
@@ -368,8 +372,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
           for (int ib = 0; ib < 2; ++ib) {
             if (ib == 0 && J >= 2) continue;
             Frag<E> fb, fbl;
-            frag_tr(fb, s_ah, G::LDA, 32 * ib, 16 * J, l);
-            if constexpr (SP) frag_tr(fbl, s_al, G::LDA, 32 * ib, 16 * J, l);
+            frag_direct(fb, s_ah, G::LDA, tj, 32 * ib, l);
+            if constexpr (SP) frag_direct(fbl, s_al, G::LDA, tj, 32 * ib, l);
             mma2b(acc, fdo[ib], fb, fbl);
           }
           const int n0 = 16 * cn + 4 * g;
@@ -455,8 +459,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
             for (int jb = 0; jb < 2; ++jb) {
               if (jb == 1 && I < 2) continue;
               Frag<E> fb, fbl;
-              frag_direct(fb, s_dah, G::LDA, ti, 32 * jb, l);
-              if constexpr (SP) frag_direct(fbl, s_dal, G::LDA, ti, 32 * jb, l);
+              frag_tr(fb, s_dah, G::LDA, 32 * jb, 16 * I, l);
+              if constexpr (SP) frag_tr(fbl, s_dal, G::LDA, 32 * jb, 16 * I, l);
               if constexpr (DIAG && SP) mma3(acc, fkt[jb], fktl[jb], fb, fbl);
               else mma2b(acc, fkt[jb], fb, fbl);
             }
@@ -523,8 +527,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
             for (int ib = 0; ib < 2; ++ib) {
               if (ib == 0 && J >= 2) continue;
               Frag<E> fb, fbl;
-              frag_tr(fb, s_dah, G::LDA, 32 * ib, 16 * J, l);
-              if constexpr (SP) frag_tr(fbl, s_dal, G::LDA, 32 * ib, 16 * J, l);
+              frag_direct(fb, s_dah, G::LDA, tj, 32 * ib, l);
+              if constexpr (SP) frag_direct(fbl, s_dal, G::LDA, tj, 32 * ib, l);
               if constexpr (DIAG && SP) mma3(acc, fqt[ib], fqtl[ib], fb, fbl);
               else mma2b(acc, fqt[ib], fb, fbl);
             }

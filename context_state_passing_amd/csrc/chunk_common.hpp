@@ -251,6 +251,21 @@ __device__ __forceinline__ f32x4 load4f(const bf16_t* p) {
 }
 __device__ __forceinline__ f32x4 load4f(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
+// Store 4 consecutive values as hi (and lo) parts into two LDS tiles at the same
+// offset (8-byte aligned for bf16, 16 for fp32).
+__device__ __forceinline__ void store_split4(bf16_t* hi, bf16_t* lo, int off, const f32x4& x) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const bf16x4 h = __builtin_convertvector(x, bf16x4);
+  const u32x2 hb = __builtin_bit_cast(u32x2, h);
+  const f32x4 r = {x[0] - __builtin_bit_cast(float, hb[0] << 16), x[1] - __builtin_bit_cast(float, hb[0] & 0xffff0000u),
+                   x[2] - __builtin_bit_cast(float, hb[1] << 16), x[3] - __builtin_bit_cast(float, hb[1] & 0xffff0000u)};
+  *reinterpret_cast<bf16x4*>(hi + off) = h;
+  *reinterpret_cast<bf16x4*>(lo + off) = __builtin_convertvector(r, bf16x4);
+}
+__device__ __forceinline__ void store_split4(float* hi, float*, int off, const f32x4& x) {
+  *reinterpret_cast<f32x4*>(hi + off) = x;
+}
+
 // Store 4 consecutive values (output feature 4g..4g+3 of a 16-wide tile).
 __device__ __forceinline__ void store4(bf16_t* p, const f32x4& x) {
   bf16x4 y;
