@@ -38,7 +38,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # The clocks of a freshly idle MI355X settle after ~25 steps of the default
+    # workload (per-dispatch kernel traces: the backward apply goes 630 -> 790 ->
+    # 578 us), so the default warmup covers that ramp.
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="diag_fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10,
