@@ -91,6 +91,12 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
   constexpr int AT_BYTES = APPLY ? (SP ? 4 : 2) * G::TILE_A * (int)sizeof(E) : 0;
   constexpr int P_BYTES = (APPLY && SCAL) ? CH * (CH + 1) * 4 : 0;
   constexpr int REG_BYTES = (GAM_BYTES > AT_BYTES + P_BYTES ? GAM_BYTES : AT_BYTES + P_BYTES) + 16;
+  // Apply walk, bf16 with a diagonal decay: the next chunk's raw inputs are copied
+  // into LDS by DMA once the dk phase is done (q into a buffer of its own; k, v,
+  // dO and g into the k, v, k-lo and score-tile regions, dead from there to the
+  // end of the chunk), so their HBM latency overlaps dg and the dS update.
+  constexpr bool PF = APPLY && DIAG && SP;
+  static_assert(!PF || GamRegs<DK, DECAY, G::NT>::DMA_FLOATS * 4 <= REG_BYTES, "raw g must fit");
 
   __shared__ __attribute__((aligned(16))) E s_q[G::TILE_K];
   __shared__ __attribute__((aligned(16))) E s_ql[QLO * G::TILE_K + 8];
@@ -101,6 +107,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
   __shared__ __attribute__((aligned(16))) E s_qh[QH * G::TILE_K + 8];
   __shared__ __attribute__((aligned(16))) E s_qhl[QHL * G::TILE_K + 8];
   __shared__ __attribute__((aligned(16))) char s_reg[REG_BYTES];
+  __shared__ __attribute__((aligned(16))) E s_pq[PF ? CH * DK : 8];
   constexpr int NRED = SCAL ? G::NW : 1;                          // scalar decay: per-wave T3 partials
   constexpr int NU = (APPLY && SCAL) ? G::NW * CH : 1;           // scalar dg token partials
   __shared__ float s_gs[DIAG ? 1 : CH], s_fq[CH], s_fk[CH], s_red[NRED], s_el[DIAG ? G::DKP : 1];
@@ -165,6 +172,31 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
   float gsum = 0.f;
   bool any_start = false;
 
+  using GamR = GamRegs<DK, DECAY, G::NT>;
+  using TileK = TileRegs<E, DK, G::NT>;
+  using TileV = TileRegs<E, DV, G::NT>;
+  float* const pf_g = reinterpret_cast<float*>(s_reg);
+  E* const pf_do = s_kl;
+  // raw inputs of the chunk starting at tn, by DMA into the regions above
+  auto prefetch = [&](int64_t tn, int tid) {
+    const int wv = wave_id();
+    GamR::dma(a.g, b, h, tn, a.T, a.H, pf_g, tid, wv);
+    TileK::dma(q, b, h, tn, a.T, a.H, s_pq, tid, wv);
+    TileK::dma(k, b, h, tn, a.T, a.H, s_k, tid, wv);
+    TileV::dma(v, b, h, tn, a.T, a.H, s_v, tid, wv);
+    TileV::dma(dO, b, h, tn, a.T, a.H, pf_do, tid, wv);
+  };
+  SegRegs nseg;   // sequence ids of the prefetched chunk
+  // the lane's log-decays for dq/dk come from the DMA buffer (d_k 64 / 128: one
+  // key tile per wave, 16-token parts) instead of a second read from HBM
+  constexpr bool GL_LDS = PF && GamR::TOK == 16 && GamR::CPW == 16 && G::CPWK == 1 && G::NKT == G::NW;
+  if constexpr (PF) {
+    const int tidf = tid_pick<APPLY, G::NT>();
+    const int64_t tn = tshard + (int64_t)(nc - 1) * CH;
+    prefetch(tn, tidf);
+    nseg.load(a.seq_idx, tn, tidf & 63);
+  }
+
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t t0 = tshard + (int64_t)c * CH;
     ChunkSeg seg;
@@ -173,18 +205,36 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
     // are in LDS (the apply walk's compute needs them; the prepare walk runs two
     // workgroups per CU, which cover each other's waits).
     SegRegs aseg;
-    GamRegs<DK, DECAY, G::NT> agam;
-    TileRegs<E, DK, G::NT> aq, ak;
-    TileRegs<E, DV, G::NT> av_, ado;
+    GamR agam;
+    TileK aq, ak;
+    TileV av_, ado;
     const int tidf = tid_pick<APPLY, G::NT>();
-    aseg.load(a.seq_idx, t0, tidf & 63);
-    agam.load(a.g, b, h, t0, a.T, a.H, tidf);
-    aq.load(q, b, h, t0, a.T, a.H, tidf);
-    if constexpr (APPLY) {
-      ak.load(k, b, h, t0, a.T, a.H, tidf);
-      av_.load(v, b, h, t0, a.T, a.H, tidf);
+    // diagonal: the lane's raw log-decays g[t0 + 16 I + i16][16 cm + 4g .. +3] for
+    // the dq/dk scaling, turned into Gam in the dq phase
+    f32x4 gl[HAS_DG && DIAG ? G::CPWK : 1][4];
+    if constexpr (PF) {
+      aseg = nseg;
+      if constexpr (GL_LDS) {
+        const int l = lane_pick<APPLY>();
+#pragma unroll
+        for (int I = 0; I < 4; ++I) gl[0][I] = GamR::lane_block(pf_g, w, I, l);
+      }
+      agam.load_lds(pf_g, tidf);
+      aq.load_lds(s_pq, tidf);
+      ak.load_lds(s_k, tidf);
+      av_.load_lds(s_v, tidf);
+      ado.load_lds(pf_do, tidf);
+      __syncthreads();   // the raw regions are overwritten from here on
+    } else {
+      aseg.load(a.seq_idx, t0, tidf & 63);
+      agam.load(a.g, b, h, t0, a.T, a.H, tidf);
+      aq.load(q, b, h, t0, a.T, a.H, tidf);
+      if constexpr (APPLY) {
+        ak.load(k, b, h, t0, a.T, a.H, tidf);
+        av_.load(v, b, h, t0, a.T, a.H, tidf);
+      }
+      ado.load(dO, b, h, t0, a.T, a.H, tidf);
     }
-    ado.load(dO, b, h, t0, a.T, a.H, tidf);
     seg = aseg.finish(a.seq_idx);
     finish_gamma<DK, DECAY, G::NT>(agam, seg, s_gam, s_fq, s_fk, tidf, gam_hi);
     any_start |= seg.any();
@@ -306,9 +356,6 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
       // that the load overlaps the dv phase
       const float* cs = a.chunk_states + ((bh * nct + t0 / CH) * DK) * (int64_t)DV;
       f32x4 s0r[G::CPWK][G::DVP / 16];
-      // diagonal: the lane's log-decays g[t0 + 16 I + i16][16 cm + 4g .. +3] for
-      // the dq/dk scaling, turned into Gam in the dq phase
-      f32x4 gl[DIAG ? G::CPWK : 1][4];
       {
         const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
 #pragma unroll
@@ -320,7 +367,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
             s0r[cc][j] = f32x4{0.f, 0.f, 0.f, 0.f};
             if (dl < DK && n0 < DV) s0r[cc][j] = *reinterpret_cast<const f32x4*>(cs + dl * DV + n0);
           }
-          if constexpr (DIAG) {
+          if constexpr (DIAG && !GL_LDS) {
             const int d0 = 16 * (w + G::NW * cc) + 4 * g;
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
@@ -552,6 +599,15 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
             }
             if (d0 < DK) store4(dkp + tok_off(b, t0 + tj, h, a.T, a.H, DK) + d0, acc);
           }
+        }
+      }
+
+      if constexpr (PF) {
+        __syncthreads();   // every wave is past its last read of k, k-lo, v and the score tiles
+        if (c > 0) {
+          const int tidp = tid_pick<APPLY, G::NT>();
+          prefetch(t0 - CH, tidp);
+          nseg.load(a.seq_idx, t0 - CH, tidp & 63);
         }
       }
 

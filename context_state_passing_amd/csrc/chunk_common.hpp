@@ -65,7 +65,7 @@ struct SegRegs {
     if (!seq_idx) return;
     const int64_t t = t0 + l;
     cur = seq_idx[t];
-    prev = t > 0 ? seq_idx[t - 1] : cur - 1;
+    prev = t > 0 ? seq_idx[t - 1] : -1;   // sequence ids are >= 0: token 0 starts one
   }
   __device__ __forceinline__ ChunkSeg finish(const int32_t* seq_idx) const {
     ChunkSeg s;
@@ -100,6 +100,43 @@ struct GamRegs {
     } else if constexpr (DECAY == DECAY_SCALAR) {
       if (tid < CH) v[0] = g[(b * T + t0 + tid) * H + h];
     }
+  }
+  // The values load() reads, copied by LDS DMA instead. Diagonal: value s of
+  // lane l of wave w lands at buf[lds_row(w, s) + l], one 64-float row per
+  // (w, s), each row shifted by lds_shift(s) < 64 words so that the lane-layout
+  // reads below are bank-conflict free (rows of 64 words all start in bank 0
+  // otherwise); a wave's rows take (TOK + 1) * 64 floats, the last 64 absorbing
+  // the shifts, so the buffer holds NT / 64 * (TOK + 1) * 64 floats. Scalar:
+  // token t at buf[t].
+  static constexpr int DMA_FLOATS = (DECAY == DECAY_DIAG) ? NT / 64 * (TOK + 1) * 64 : CH;
+  __device__ __forceinline__ static constexpr int lds_shift(int s) { return (s & 3) + 16 * ((s >> 2) & 3); }
+  __device__ __forceinline__ static int lds_row(int w, int s) { return w * (TOK + 1) * 64 + s * 64 + lds_shift(s); }
+  __device__ __forceinline__ static void dma(const float* __restrict__ g, int64_t b, int64_t h, int64_t t0,
+                                             int64_t T, int64_t H, float* buf, int tid, int w) {
+    if constexpr (DECAY == DECAY_DIAG) {
+      const float* src = g + ((b * T + t0 + part(tid) * TOK) * H + h) * DK + column(tid);
+#pragma unroll
+      for (int s = 0; s < TOK; ++s) lds_dma<4>(src + (int64_t)s * H * DK, buf + lds_row(w, s));
+    } else if constexpr (DECAY == DECAY_SCALAR) {
+      if (tid < CH) lds_dma<4>(g + (b * T + t0 + tid) * H + h, buf + 64 * w);
+    }
+  }
+  __device__ __forceinline__ void load_lds(const float* buf, int tid) {
+    if constexpr (DECAY == DECAY_DIAG) {
+      const int w = tid >> 6, l = tid & 63;
+#pragma unroll
+      for (int s = 0; s < TOK; ++s) v[s] = buf[lds_row(w, s) + l];
+    } else if constexpr (DECAY == DECAY_SCALAR) {
+      if (tid < CH) v[0] = buf[tid];
+    }
+  }
+  // Diagonal, TOK == CPW == 16 (d_k of 64 or 128): the raw log-decay of token
+  // 16 I + (l % 16) at key dims 16 w + 4 (l / 16) + rr (rr = 0..3), the MFMA
+  // accumulator layout of wave w's key tile, from the DMA buffer.
+  __device__ __forceinline__ static f32x4 lane_block(const float* buf, int w, int I, int l) {
+    static_assert(DECAY == DECAY_DIAG && TOK == 16 && CPW == 16, "lane layout needs 16-token parts of 16 columns");
+    const float* p = buf + lds_row(w, l & 15) + 16 * I + 4 * (l >> 4);
+    return f32x4{p[0], p[1], p[2], p[3]};
   }
 };
 
@@ -176,6 +213,25 @@ struct TileRegs {
         r[p] = *reinterpret_cast<const f32x4*>(src + tok_off(b, t0 + i, h, T, H, D) + c);
       }
     }
+  }
+  // The vectors load() reads, copied by LDS DMA instead: vector p of thread tid
+  // lands at buf[(p * NT + tid) * VEC], one contiguous kilobyte per wave and p
+  // (w = the calling wave); load_lds reads them back. buf holds CH * D elements.
+  __device__ __forceinline__ static void dma(const E* __restrict__ src, int64_t b, int64_t h, int64_t t0, int64_t T,
+                                             int64_t H, E* buf, int tid, int w) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int v = tid + p * NT;
+      if (v < NV) {
+        const int i = v / VPR, c = (v % VPR) * VEC;
+        lds_dma<16>(src + tok_off(b, t0 + i, h, T, H, D) + c, buf + (p * NT + 64 * w) * VEC);
+      }
+    }
+  }
+  __device__ __forceinline__ void load_lds(const E* buf, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+      if (tid + p * NT < NV) r[p] = *reinterpret_cast<const f32x4*>(buf + (p * NT + tid) * VEC);
   }
 };
 
@@ -257,8 +313,11 @@ __device__ __forceinline__ void store_split4(bf16_t* hi, bf16_t* lo, int off, co
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
   const bf16x4 h = __builtin_convertvector(x, bf16x4);
   const u32x2 hb = __builtin_bit_cast(u32x2, h);
-  const f32x4 r = {x[0] - __builtin_bit_cast(float, hb[0] << 16), x[1] - __builtin_bit_cast(float, hb[0] & 0xffff0000u),
-                   x[2] - __builtin_bit_cast(float, hb[1] << 16), x[3] - __builtin_bit_cast(float, hb[1] & 0xffff0000u)};
+  f32x4 r = x;
+  float r0 = r[0], r1 = r[1], r2 = r[2], r3 = r[3];
+  bf16_residual_pair(hb[0], r0, r1);
+  bf16_residual_pair(hb[1], r2, r3);
+  r = f32x4{r0, r1, r2, r3};
   *reinterpret_cast<bf16x4*>(hi + off) = h;
   *reinterpret_cast<bf16x4*>(lo + off) = __builtin_convertvector(r, bf16x4);
 }

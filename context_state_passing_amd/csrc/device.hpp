@@ -115,6 +115,18 @@ __device__ __forceinline__ void frag_direct_perm(Frag<float>& f, const float* t,
   for (int e = 0; e < 4; ++e) { f.v[e] = a[e]; f.v[4 + e] = b[e]; }
 }
 
+// Direct global -> LDS copy (the gfx950 LDS DMA form of a vector load): lane i of
+// the wave copies BYTES bytes from src to lds_wave + i * BYTES, without passing
+// through registers. lds_wave must be the same for every lane of the wave.
+// Completion is counted like any vector-memory load (vmcnt).
+template <int BYTES>
+__device__ __forceinline__ void lds_dma(const void* src, void* lds_wave) {
+  static_assert(BYTES == 4 || BYTES == 16, "LDS DMA copies 4 or 16 bytes per lane here");
+  typedef __attribute__((address_space(3))) void lds_void;
+  if constexpr (BYTES == 16) __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_wave, 16, 0, 0);
+  else __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_wave, 4, 0, 0);
+}
+
 // lane-fixed column col0 + l%16, contraction over rows k0 + 8g + e (transpose load)
 __device__ __forceinline__ s16x4 ds_tr16(const bf16_t* p) {
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
@@ -175,19 +187,33 @@ __device__ __forceinline__ void split_frag(Frag<float>& hi, Frag<float>& lo, con
 #pragma unroll
   for (int e = 0; e < 8; ++e) hi.v[e] = x[e];
 }
-// bf16: hi converted in pairs; hi's fp32 values are read back from the packed
-// pairs with a shift / mask instead of a second conversion
+// Residuals of a pair (x0, x1) after rounding to the packed bf16 pair h:
+// x0 - h[0] and x1 - h[1], each one v_dot2c_f32_bf16 (x + h . m with m = (-1, 0)
+// or (0, -1): the products are exact and the difference is representable, so the
+// result is exact), instead of unpacking h and subtracting. The multipliers are
+// passed in scalar registers: as an inline constant, the pair (-1, 0) is encoded
+// as fp32 -1.0, whose bits are the pair (0, -1).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void bf16_residual_pair(unsigned h, float& x0, float& x1) {
+  unsigned m0 = 0x0000bf80u, m1 = 0xbf800000u;
+  asm("" : "+s"(m0), "+s"(m1));
+  const bf16x2 hp = __builtin_bit_cast(bf16x2, h);
+  x0 = __builtin_amdgcn_fdot2_f32_bf16(hp, __builtin_bit_cast(bf16x2, m0), x0, false);
+  x1 = __builtin_amdgcn_fdot2_f32_bf16(hp, __builtin_bit_cast(bf16x2, m1), x1, false);
+}
+// bf16: hi converted in pairs, lo = bf16 of the exact residuals
 __device__ __forceinline__ void split_frag(Frag<bf16_t>& hi, Frag<bf16_t>& lo, const float (&x)[8]) {
   typedef float f32x8 __attribute__((ext_vector_type(8)));
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const f32x8 v = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
-  hi.v = __builtin_convertvector(v, bf16x8);
+  f32x8 r = {x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]};
+  hi.v = __builtin_convertvector(r, bf16x8);
   const u32x4 hb = __builtin_bit_cast(u32x4, hi.v);
-  f32x8 r;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    r[2 * i] = x[2 * i] - __builtin_bit_cast(float, hb[i] << 16);
-    r[2 * i + 1] = x[2 * i + 1] - __builtin_bit_cast(float, hb[i] & 0xffff0000u);
+    float a = r[2 * i], b = r[2 * i + 1];
+    bf16_residual_pair(hb[i], a, b);
+    r[2 * i] = a;
+    r[2 * i + 1] = b;
   }
   lo.v = __builtin_convertvector(r, bf16x8);
 }

@@ -94,7 +94,8 @@ typedef struct {
  * row is one sequence that starts from S_init, the forward prefix of rank r is
  * [0, r) and the backward suffix is (r, P). Device pointers. */
 typedef struct {
-  const int32_t* seq_idx;               /* [T] global sequence id of each token       */
+  const int32_t* seq_idx;               /* [T] global sequence id of each token (>= 0,
+                                           as cpla_seq_idx_from_cu_seqlens writes) */
   const int32_t* preceding_rank_start;  /* [P] inclusive start of rank r's prefix      */
   const int32_t* following_rank_stop;   /* [P] exclusive end of rank r's suffix        */
 } cpla_packed;
