@@ -1,0 +1,96 @@
+"""Pins for the Mamba2 (SSD) oracle: against things other than itself.
+
+* the O(T^2) quadratic form of the selective state space (brute force, tiny T);
+* central finite differences of a scalar loss, for every input (initial state
+  and packed sequences included);
+* the linear-attention oracle, an independent implementation, under the map
+  q = C[group], k = B[group], v = dt x, g = A dt — forward and, through the
+  chain rule, backward.
+"""
+import numpy as np
+import pytest
+
+from oracle import metadata, recurrence as rec, ssd
+
+
+def _inputs(rng, Bt=2, T=9, H=4, G=2, N=3, init=False):
+    x = rng.standard_normal((Bt, T, H, N))
+    dt = np.log1p(np.exp(rng.standard_normal((Bt, T, H)) - 1.0))
+    A = -np.exp(rng.uniform(0.0, 1.5, H))
+    B = rng.standard_normal((Bt, T, G, N))
+    C = rng.standard_normal((Bt, T, G, N))
+    h0 = rng.standard_normal((Bt, H, N, N)) * 0.5 if init else None
+    return x, dt, A, B, C, h0
+
+
+def test_forward_matches_quadratic_form():
+    rng = np.random.default_rng(7)
+    x, dt, A, B, C, _ = _inputs(rng)
+    y, _ = ssd.ssd_forward(x, dt, A, B, C)
+    y2 = ssd.ssd_matrix_form(x, dt, A, B, C)
+    np.testing.assert_allclose(y, y2, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("init,packed", [(False, False), (True, False), (False, True)])
+def test_backward_matches_finite_differences(init, packed):
+    rng = np.random.default_rng(11 + 2 * init + packed)
+    Bt = 1 if packed else 2
+    x, dt, A, B, C, h0 = _inputs(rng, Bt=Bt, T=8, init=init)
+    seq = metadata.seq_idx_from_cu_seqlens(np.array([0, 3, 8]), 8) if packed else None
+    W = rng.standard_normal(x.shape)
+    Wf = rng.standard_normal((Bt, x.shape[2], 3, 3))
+
+    def loss(x_, dt_, A_, B_, C_, h0_):
+        y, hT = ssd.ssd_forward(x_, dt_, A_, B_, C_, h_init=h0_, seq_idx=seq)
+        return float(np.sum(y * W) + np.sum(hT * Wf))
+
+    grads = ssd.ssd_backward(x, dt, A, B, C, W, h_init=h0, seq_idx=seq, dh_final=Wf)
+    args = [x, dt, A, B, C, h0]
+    eps = 1e-6
+    for i, gexp in enumerate(grads):
+        if args[i] is None:
+            assert gexp is None
+            continue
+        num = np.zeros_like(args[i])
+        it = np.nditer(args[i], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            hi = [a.copy() if a is not None else None for a in args]
+            lo = [a.copy() if a is not None else None for a in args]
+            hi[i][idx] += eps
+            lo[i][idx] -= eps
+            num[idx] = (loss(*hi) - loss(*lo)) / (2 * eps)
+        np.testing.assert_allclose(gexp, num, rtol=1e-6, atol=1e-7, err_msg=f"input {i}")
+
+
+@pytest.mark.parametrize("init,packed", [(False, False), (True, False), (False, True)])
+def test_matches_linear_attention_oracle(init, packed):
+    rng = np.random.default_rng(23 + 2 * init + packed)
+    Bt = 1 if packed else 2
+    x, dt, A, B, C, h0 = _inputs(rng, Bt=Bt, T=21, H=4, G=2, N=4, init=init)
+    seq = metadata.seq_idx_from_cu_seqlens(np.array([0, 5, 6, 21]), 21) if packed else None
+    H, G = x.shape[2], B.shape[2]
+    grp = np.arange(H) // (H // G)
+    q, k = C[:, :, grp], B[:, :, grp]
+    v = dt[..., None] * x
+    g = A[None, None, :] * dt
+    y, hT = ssd.ssd_forward(x, dt, A, B, C, h_init=h0, seq_idx=seq)
+    o, ST = rec.forward(q, k, v, g, "scalar", initial_state=h0, seq_idx=seq)
+    np.testing.assert_allclose(y, o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(hT, ST, rtol=1e-12, atol=1e-12)
+
+    dy = rng.standard_normal(y.shape)
+    dx, ddt, dA, dB, dC, dh0 = ssd.ssd_backward(x, dt, A, B, C, dy, h_init=h0, seq_idx=seq)
+    dq, dk, dv, dg, dS0 = rec.backward(q, k, v, g, "scalar", dO=dy, initial_state=h0, seq_idx=seq)
+    np.testing.assert_allclose(dx, dt[..., None] * dv, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(ddt, np.sum(dv * x, axis=-1) + A[None, None, :] * dg, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dA, np.sum(dt * dg, axis=(0, 1)), rtol=1e-10, atol=1e-12)
+    dB2 = np.zeros_like(B)
+    dC2 = np.zeros_like(C)
+    for h in range(H):
+        dB2[:, :, grp[h]] += dk[:, :, h]
+        dC2[:, :, grp[h]] += dq[:, :, h]
+    np.testing.assert_allclose(dB, dB2, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dC, dC2, rtol=1e-10, atol=1e-12)
+    if init:
+        np.testing.assert_allclose(dh0, dS0, rtol=1e-10, atol=1e-12)
