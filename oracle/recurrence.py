@@ -24,6 +24,10 @@ loss with respect to S_t from tokens >= t:
              the key dimension for a scalar decay; 0 at a sequence start)
     dS_init = diag(a_0) dS_0
 
+With a per-token input weight w (scalar decay; the recurrence becomes
+S_t = diag(a_t) S_{t-1} + w_t k_t v_t^T) the same chain rule gives
+dk_t = w_t dS_t v_t, dv_t = w_t dS_t^T k_t and dw_t = k_t^T dS_t v_t.
+
 These are the chain rule applied to the definition above, written out plainly.
 Everything is vectorised over rows only; the token loop is a Python loop.
 """
@@ -77,26 +81,31 @@ def starts_from_seq_idx(seq_idx, T):
     return st
 
 
-def run_forward_rows(q, k, v, a, resets, S0):
-    """Rows form. q, k: [R,T,dk]; v: [R,T,dv]; a: [R,T,dk]; resets: [T] bool; S0: [R,dk,dv].
+def run_forward_rows(q, k, v, a, resets, S0, wr=None):
+    """Rows form. q, k: [R,T,dk]; v: [R,T,dv]; a: [R,T,dk]; resets: [T] bool; S0: [R,dk,dv];
+    wr: per-token input weights [R,T] or None.
 
     Returns o [R,T,dv] and the final state [R,dk,dv]."""
     R, T, dk = q.shape
     S = S0.copy()
     o = np.empty((R, T, v.shape[2]))
+    wr = np.ones((R, T)) if wr is None else wr
     for t in range(T):
         if resets[t]:
             S[:] = 0.0
-        S = a[:, t, :, None] * S + k[:, t, :, None] * v[:, t, None, :]
+        S = a[:, t, :, None] * S + wr[:, t, None, None] * k[:, t, :, None] * v[:, t, None, :]
         o[:, t] = np.einsum("rkv,rk->rv", S, q[:, t])
     return o, S
 
 
-def run_backward_rows(q, k, v, a, resets, S0, dO, dSf, decay):
+def run_backward_rows(q, k, v, a, resets, S0, dO, dSf, decay, wr=None):
     """Rows form of the adjoint. Returns dq, dk, dv, dg_rows [R,T,dk] (per key
-    dim; summed by the caller for a scalar decay) and dS_init [R,dk,dv]."""
+    dim; summed by the caller for a scalar decay), dS_init [R,dk,dv] and dw [R,T]
+    (the input-weight gradient; zeros without weights)."""
     R, T, dk = q.shape
     dv_ = v.shape[2]
+    wr = np.ones((R, T)) if wr is None else wr
+    dw = np.zeros((R, T))
     # forward sweep storing the state before every CKPT-th token
     nblk = (T + CKPT - 1) // CKPT
     ck = np.empty((nblk, R, dk, dv_))
@@ -106,7 +115,7 @@ def run_backward_rows(q, k, v, a, resets, S0, dO, dSf, decay):
             ck[t // CKPT] = S
         if resets[t]:
             S[:] = 0.0
-        S = a[:, t, :, None] * S + k[:, t, :, None] * v[:, t, None, :]
+        S = a[:, t, :, None] * S + wr[:, t, None, None] * k[:, t, :, None] * v[:, t, None, :]
 
     dq = np.empty((R, T, dk))
     dk_ = np.empty((R, T, dk))
@@ -120,22 +129,23 @@ def run_backward_rows(q, k, v, a, resets, S0, dO, dSf, decay):
         S = ck[b].copy()
         for t in range(t0, t1):
             Sp = np.zeros_like(S) if resets[t] else S
-            S = a[:, t, :, None] * Sp + k[:, t, :, None] * v[:, t, None, :]
+            S = a[:, t, :, None] * Sp + wr[:, t, None, None] * k[:, t, :, None] * v[:, t, None, :]
             prev.append(Sp)
             cur.append(S)
         for t in range(t1 - 1, t0 - 1, -1):
             i = t - t0
             dS = G + q[:, t, :, None] * dO[:, t, None, :]
             dq[:, t] = np.einsum("rkv,rv->rk", cur[i], dO[:, t])
-            dk_[:, t] = np.einsum("rkv,rv->rk", dS, v[:, t])
-            dvv[:, t] = np.einsum("rkv,rk->rv", dS, k[:, t])
+            dk_[:, t] = wr[:, t, None] * np.einsum("rkv,rv->rk", dS, v[:, t])
+            dvv[:, t] = wr[:, t, None] * np.einsum("rkv,rk->rv", dS, k[:, t])
+            dw[:, t] = np.einsum("rkv,rk,rv->r", dS, k[:, t], v[:, t])
             if resets[t]:
                 G = np.zeros_like(G)
             else:
                 if decay != "none":
                     dg[:, t] = a[:, t] * np.einsum("rkv,rkv->rk", dS, prev[i])
                 G = a[:, t, :, None] * dS
-    return dq, dk_, dvv, dg, G
+    return dq, dk_, dvv, dg, G, dw
 
 
 def _prep(q, k, v, g, decay, initial_state, seq_idx, resets):
@@ -154,28 +164,35 @@ def _prep(q, k, v, g, decay, initial_state, seq_idx, resets):
     return q, k, v, B, T, H, dk, dv, R, resets, S0, a
 
 
-def forward(q, k, v, g=None, decay="none", initial_state=None, seq_idx=None, resets=None):
+def forward(q, k, v, g=None, decay="none", initial_state=None, seq_idx=None, resets=None, w=None):
     """o [B,T,H,dv] and final state [B,H,dk,dv], fp64.
 
     ``seq_idx`` (int [T], B == 1) marks packed sequences: the state resets at each
     start, token 0 included. ``resets`` may be given instead (bool [T]) to reset
-    only at chosen tokens, e.g. a shard whose first token continues a sequence."""
+    only at chosen tokens, e.g. a shard whose first token continues a sequence.
+    ``w`` [B,T,H]: per-token input weights (S_t = a_t S_{t-1} + w_t k_t v_t^T)."""
     q, k, v, B, T, H, dk, dv, R, resets, S0, a = _prep(q, k, v, g, decay, initial_state, seq_idx, resets)
-    o, S = run_forward_rows(to_rows(q), to_rows(k), to_rows(v), a, resets, S0)
+    wr = None if w is None else to_rows(_np(w))
+    o, S = run_forward_rows(to_rows(q), to_rows(k), to_rows(v), a, resets, S0, wr)
     return from_rows(o, B, H), S.reshape(B, H, dk, dv)
 
 
 def backward(q, k, v, g=None, decay="none", dO=None, initial_state=None, seq_idx=None,
-             d_final_state=None, resets=None):
-    """dq, dk, dv (like q, k, v), dg (like g, or None), dS_init [B,H,dk,dv], all fp64."""
+             d_final_state=None, resets=None, w=None):
+    """dq, dk, dv (like q, k, v), dg (like g, or None), dS_init [B,H,dk,dv], all fp64;
+    with input weights ``w`` [B,T,H], also dw [B,T,H] as a sixth element."""
     q, k, v, B, T, H, dk, dv, R, resets, S0, a = _prep(q, k, v, g, decay, initial_state, seq_idx, resets)
     dO = to_rows(_np(dO))
     dSf = np.zeros((R, dk, dv)) if d_final_state is None else _np(d_final_state).reshape(R, dk, dv).copy()
-    dq, dk_, dv_, dg, dS0 = run_backward_rows(to_rows(q), to_rows(k), to_rows(v), a, resets, S0, dO, dSf, decay)
+    wr = None if w is None else to_rows(_np(w))
+    dq, dk_, dv_, dg, dS0, dw = run_backward_rows(to_rows(q), to_rows(k), to_rows(v), a, resets, S0, dO, dSf,
+                                                  decay, wr)
     dgo = None
     if decay == "diag":
         dgo = from_rows(dg, B, H)
     elif decay == "scalar":
         dgo = from_rows(dg.sum(axis=2), B, H)
-    return (from_rows(dq, B, H), from_rows(dk_, B, H), from_rows(dv_, B, H), dgo,
-            dS0.reshape(B, H, dk, dv))
+    res = (from_rows(dq, B, H), from_rows(dk_, B, H), from_rows(dv_, B, H), dgo, dS0.reshape(B, H, dk, dv))
+    if w is not None:
+        res = res + (from_rows(dw, B, H),)
+    return res

@@ -4,8 +4,10 @@
 * central finite differences of a scalar loss, for every input (initial state
   and packed sequences included);
 * the linear-attention oracle, an independent implementation, under the map
-  q = C[group], k = B[group], v = dt x, g = A dt — forward and, through the
-  chain rule, backward.
+  q = C[group], k = B[group], v = x, input weight w = dt, g = A dt — forward and,
+  through the chain rule, backward;
+* and the linear-attention oracle's input-weight gradients against central
+  finite differences.
 """
 import numpy as np
 import pytest
@@ -72,18 +74,17 @@ def test_matches_linear_attention_oracle(init, packed):
     H, G = x.shape[2], B.shape[2]
     grp = np.arange(H) // (H // G)
     q, k = C[:, :, grp], B[:, :, grp]
-    v = dt[..., None] * x
     g = A[None, None, :] * dt
     y, hT = ssd.ssd_forward(x, dt, A, B, C, h_init=h0, seq_idx=seq)
-    o, ST = rec.forward(q, k, v, g, "scalar", initial_state=h0, seq_idx=seq)
+    o, ST = rec.forward(q, k, x, g, "scalar", initial_state=h0, seq_idx=seq, w=dt)
     np.testing.assert_allclose(y, o, rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(hT, ST, rtol=1e-12, atol=1e-12)
 
     dy = rng.standard_normal(y.shape)
     dx, ddt, dA, dB, dC, dh0 = ssd.ssd_backward(x, dt, A, B, C, dy, h_init=h0, seq_idx=seq)
-    dq, dk, dv, dg, dS0 = rec.backward(q, k, v, g, "scalar", dO=dy, initial_state=h0, seq_idx=seq)
-    np.testing.assert_allclose(dx, dt[..., None] * dv, rtol=1e-10, atol=1e-12)
-    np.testing.assert_allclose(ddt, np.sum(dv * x, axis=-1) + A[None, None, :] * dg, rtol=1e-10, atol=1e-12)
+    dq, dk, dv, dg, dS0, dw = rec.backward(q, k, x, g, "scalar", dO=dy, initial_state=h0, seq_idx=seq, w=dt)
+    np.testing.assert_allclose(dx, dv, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(ddt, dw + A[None, None, :] * dg, rtol=1e-10, atol=1e-12)
     np.testing.assert_allclose(dA, np.sum(dt * dg, axis=(0, 1)), rtol=1e-10, atol=1e-12)
     dB2 = np.zeros_like(B)
     dC2 = np.zeros_like(C)
@@ -94,3 +95,35 @@ def test_matches_linear_attention_oracle(init, packed):
     np.testing.assert_allclose(dC, dC2, rtol=1e-10, atol=1e-12)
     if init:
         np.testing.assert_allclose(dh0, dS0, rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_weighted_linear_attention_matches_finite_differences(packed):
+    rng = np.random.default_rng(31 + packed)
+    Bt, T, H, d = (1, 10, 2, 3) if packed else (2, 9, 2, 3)
+    q, k, v = (rng.standard_normal((Bt, T, H, d)) for _ in range(3))
+    g = -np.log1p(np.exp(rng.standard_normal((Bt, T, H))))
+    w = np.exp(rng.standard_normal((Bt, T, H)) * 0.5)
+    S0 = None if packed else rng.standard_normal((Bt, H, d, d)) * 0.3
+    seq = metadata.seq_idx_from_cu_seqlens(np.array([0, 4, 10]), 10) if packed else None
+    W = rng.standard_normal((Bt, T, H, d))
+
+    def loss(q_, k_, v_, g_, w_):
+        o, _ = rec.forward(q_, k_, v_, g_, "scalar", initial_state=S0, seq_idx=seq, w=w_)
+        return float(np.sum(o * W))
+
+    got = rec.backward(q, k, v, g, "scalar", dO=W, initial_state=S0, seq_idx=seq, w=w)
+    grads = {"q": got[0], "k": got[1], "v": got[2], "g": got[3], "w": got[5]}
+    args = {"q": q, "k": k, "v": v, "g": g, "w": w}
+    eps = 1e-6
+    for name, gexp in grads.items():
+        num = np.zeros_like(args[name])
+        it = np.nditer(args[name], flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            hi = {n: a.copy() for n, a in args.items()}
+            lo = {n: a.copy() for n, a in args.items()}
+            hi[name][idx] += eps
+            lo[name][idx] -= eps
+            num[idx] = (loss(**{n + "_": a for n, a in hi.items()}) - loss(**{n + "_": a for n, a in lo.items()})) / (2 * eps)
+        np.testing.assert_allclose(gexp, num, rtol=1e-6, atol=1e-7, err_msg=name)
