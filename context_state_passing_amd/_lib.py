@@ -20,6 +20,8 @@ EXPORTS = [
     "cpla_summary_width", "cpla_chunk_states_bytes", "cp_forward_prepare", "cp_forward_apply",
     "cp_backward_prepare", "cp_backward_apply", "build_packed_sequence_cp_metadata",
     "cpla_packed_rank_slices", "cpla_seq_idx_from_cu_seqlens", "cpla_last_error", "cpla_abi_version",
+    "cpla_ssd_inputs", "cpla_ssd_input_grads", "cp_forward_prepare_weighted", "cp_forward_apply_weighted",
+    "cp_backward_apply_weighted",
 ]
 
 
@@ -35,6 +37,11 @@ class Problem(ctypes.Structure):
                 ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("num_shards", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("rank_begin", ctypes.c_int32), ("rank_end", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("decay", ctypes.c_int32)]
+
+
+class SsdProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64), ("G", ctypes.c_int64),
+                ("N", ctypes.c_int64), ("dtype", ctypes.c_int32)]
 
 
 class Packed(ctypes.Structure):
@@ -71,6 +78,16 @@ def lib() -> ctypes.CDLL:
         L.cpla_packed_rank_slices.restype = ctypes.c_int
         L.cpla_seq_idx_from_cu_seqlens.argtypes = [pi32, I32, I64, pi32]
         L.cpla_seq_idx_from_cu_seqlens.restype = ctypes.c_int
+        SP = ctypes.POINTER(SsdProblem)
+        L.cpla_ssd_inputs.argtypes = [SP, V, V, V, V, V, V, V, V]
+        L.cpla_ssd_inputs.restype = ctypes.c_int
+        L.cpla_ssd_input_grads.argtypes = [SP, V, V, V, V, V, V, V, V, V, V, V, V, V]
+        L.cpla_ssd_input_grads.restype = ctypes.c_int
+        L.cp_forward_prepare_weighted.argtypes = [P, PK, V, V, V, V, V, V]
+        L.cp_forward_apply_weighted.argtypes = [P, PK, V, V, V, V, V, V, V, V, V, V, V, V]
+        L.cp_backward_apply_weighted.argtypes = [P, PK, V, V, V, V, V, V, V, V, V, V, V, V, V, V, V, V, I32, V]
+        for fn in ["cp_forward_prepare_weighted", "cp_forward_apply_weighted", "cp_backward_apply_weighted"]:
+            getattr(L, fn).restype = ctypes.c_int
         L.cpla_last_error.restype = ctypes.c_char_p
         L.cpla_abi_version.restype = ctypes.c_int
         _lib = L

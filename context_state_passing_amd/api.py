@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import CplaError, Packed, Problem, check
+from ._lib import CplaError, Packed, Problem, SsdProblem, check
 
 _DTYPE = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
 
@@ -102,6 +102,7 @@ class Context:
     final_state: torch.Tensor
     chunk_states: Optional[torch.Tensor]
     has_initial_state: bool
+    w: Optional[torch.Tensor] = None     # per-token input weights (scalar decay)
 
 
 def _decay_of(g: Optional[torch.Tensor], q: torch.Tensor) -> int:
@@ -126,9 +127,10 @@ def make_problem(q, v, num_shards: int, decay: int, chunk: int = 64, rank_range=
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor] = None, *,
             num_shards: int, initial_state: Optional[torch.Tensor] = None, cu_seqlens=None,
             packed: Optional[PackedMeta] = None, save_for_backward: bool = True, chunk: int = 64,
-            out: Optional[torch.Tensor] = None):
-    """o [B,T,H,dv] (dtype of q) and a Context for ``backward``."""
-    for t in (q, k, v, g, initial_state):
+            out: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None):
+    """o [B,T,H,dv] (dtype of q) and a Context for ``backward``. ``w`` [B,T,H] fp32:
+    per-token input weights (scalar decay): S_t = exp(g_t) S_{t-1} + w_t k_t v_t^T."""
+    for t in (q, k, v, g, initial_state, w):
         if t is not None and not t.is_contiguous():
             raise CplaError(1, "inputs must be contiguous")
     decay = _decay_of(g, q)
@@ -149,17 +151,25 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
     o = torch.empty(v.shape, device=dev, dtype=q.dtype) if out is None else out
     pk = ctypes.byref(packed.c()) if packed is not None else None
     st = _stream()
-    check(L.cp_forward_prepare(ctypes.byref(p), pk, _ptr(k), _ptr(v), _ptr(g), _ptr(fsum), st))
-    check(L.cp_forward_apply(ctypes.byref(p), pk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(fsum),
-                             _ptr(initial_state), _ptr(o), _ptr(s_in), _ptr(fin), _ptr(cs), st))
-    ctx = Context(p, decay, q, k, v, g, packed, fsum, s_in, fin, cs, initial_state is not None)
+    if w is None:
+        check(L.cp_forward_prepare(ctypes.byref(p), pk, _ptr(k), _ptr(v), _ptr(g), _ptr(fsum), st))
+        check(L.cp_forward_apply(ctypes.byref(p), pk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(fsum),
+                                 _ptr(initial_state), _ptr(o), _ptr(s_in), _ptr(fin), _ptr(cs), st))
+    else:
+        check(L.cp_forward_prepare_weighted(ctypes.byref(p), pk, _ptr(k), _ptr(v), _ptr(g), _ptr(w), _ptr(fsum), st))
+        check(L.cp_forward_apply_weighted(ctypes.byref(p), pk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(w),
+                                          _ptr(fsum), _ptr(initial_state), _ptr(o), _ptr(s_in), _ptr(fin), _ptr(cs),
+                                          st))
+    ctx = Context(p, decay, q, k, v, g, packed, fsum, s_in, fin, cs, initial_state is not None, w)
     return o, ctx
 
 
 def backward(dO: torch.Tensor, ctx: Context, d_final_state: Optional[torch.Tensor] = None,
-             want_intermediates: bool = False):
+             want_intermediates: bool = False, grad_dtype: Optional[torch.dtype] = None):
     """(dq, dk, dv, dg, d_initial_state); dg is None without decay, d_initial_state
-    None with packed sequences."""
+    None with packed sequences. With input weights (``w`` given to ``forward``) a
+    sixth element dw [B,T,H] fp32 follows, and ``grad_dtype=torch.float32`` gives dq,
+    dk, dv in fp32 (bf16 inputs, scalar decay)."""
     if ctx.chunk_states is None:
         raise CplaError(1, "forward was run with save_for_backward=False")
     if not dO.is_contiguous():
@@ -173,9 +183,12 @@ def backward(dO: torch.Tensor, ctx: Context, d_final_state: Optional[torch.Tenso
     W = L.cpla_summary_width(ctypes.byref(p))
     bsum = torch.empty((P, B, H, W), device=dev, dtype=torch.float32)
     s_out = torch.empty((P, B, H, dk, dv), device=dev, dtype=torch.float32)
-    dq = torch.empty_like(ctx.q)
-    dk_ = torch.empty_like(ctx.k)
-    dv_ = torch.empty_like(ctx.v)
+    gdt = ctx.q.dtype if grad_dtype is None else grad_dtype
+    if gdt != ctx.q.dtype and ctx.w is None:
+        raise CplaError(3, "fp32 gradients are available through the weighted backward only")
+    dq = torch.empty(ctx.q.shape, device=dev, dtype=gdt)
+    dk_ = torch.empty(ctx.k.shape, device=dev, dtype=gdt)
+    dv_ = torch.empty(ctx.v.shape, device=dev, dtype=gdt)
     dg = None if ctx.g is None else torch.empty_like(ctx.g)
     dS0 = None
     if ctx.packed is None:
@@ -183,10 +196,18 @@ def backward(dO: torch.Tensor, ctx: Context, d_final_state: Optional[torch.Tenso
     pk = ctypes.byref(ctx.packed.c()) if ctx.packed is not None else None
     st = _stream()
     check(L.cp_backward_prepare(ctypes.byref(p), pk, _ptr(ctx.q), _ptr(ctx.g), _ptr(dO), _ptr(bsum), st))
-    check(L.cp_backward_apply(ctypes.byref(p), pk, _ptr(ctx.q), _ptr(ctx.k), _ptr(ctx.v), _ptr(ctx.g),
-                              _ptr(dO), _ptr(ctx.chunk_states), _ptr(bsum), _ptr(d_final_state), _ptr(dq),
-                              _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(s_out), _ptr(dS0), st))
-    res = (dq, dk_, dv_, dg, dS0)
+    if ctx.w is None:
+        check(L.cp_backward_apply(ctypes.byref(p), pk, _ptr(ctx.q), _ptr(ctx.k), _ptr(ctx.v), _ptr(ctx.g),
+                                  _ptr(dO), _ptr(ctx.chunk_states), _ptr(bsum), _ptr(d_final_state), _ptr(dq),
+                                  _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(s_out), _ptr(dS0), st))
+        res = (dq, dk_, dv_, dg, dS0)
+    else:
+        dw = torch.empty_like(ctx.w)
+        check(L.cp_backward_apply_weighted(ctypes.byref(p), pk, _ptr(ctx.q), _ptr(ctx.k), _ptr(ctx.v), _ptr(ctx.g),
+                                           _ptr(ctx.w), _ptr(dO), _ptr(ctx.chunk_states), _ptr(bsum),
+                                           _ptr(d_final_state), _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dg), _ptr(dw),
+                                           _ptr(s_out), _ptr(dS0), _DTYPE[gdt], st))
+        res = (dq, dk_, dv_, dg, dS0, dw)
     if want_intermediates:
         return res, {"bwd_summary": bsum, "shard_out_grad": s_out}
     return res
@@ -211,3 +232,84 @@ class ChunkwiseLinearAttention(torch.autograd.Function):
 
 def chunkwise_linear_attention(q, k, v, g=None, initial_state=None, *, num_shards: int = 1, cu_seqlens=None):
     return ChunkwiseLinearAttention.apply(q, k, v, g, initial_state, num_shards, cu_seqlens)
+
+
+# ---- Mamba2 (SSD) parametrisation ---------------------------------------------------------
+# Mamba2's selective state space runs through the weighted scalar-decay path:
+# cpla_ssd_inputs writes per-head q = C[group], k = B[group] and g = A dt; the CP
+# calls take v = x and input weights w = dt; cpla_ssd_input_grads takes the
+# gradients back (see include/cpla.h). dx is the dv of the CP backward.
+
+@dataclasses.dataclass
+class SsdContext:
+    problem: SsdProblem
+    dt: torch.Tensor
+    A: torch.Tensor
+    la: Context
+
+
+def _ssd_problem(x, B) -> SsdProblem:
+    Bt, T, H, N = x.shape
+    if x.dtype not in _DTYPE:
+        raise CplaError(3, f"dtype {x.dtype} unsupported")
+    return SsdProblem(Bt, T, H, B.shape[2], N, _DTYPE[x.dtype])
+
+
+def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *,
+                num_shards: int, initial_state: Optional[torch.Tensor] = None, cu_seqlens=None,
+                packed: Optional[PackedMeta] = None):
+    """y [Bt,T,H,N] (dtype of x) and an SsdContext for ``ssd_backward``. x [Bt,T,H,N];
+    dt [Bt,T,H] and A [H] fp32; B, C [Bt,T,G,N] like x; initial_state [Bt,H,N,N] fp32."""
+    for t in (x, dt, A, B, C):
+        if not t.is_contiguous():
+            raise CplaError(1, "inputs must be contiguous")
+    sp = _ssd_problem(x, B)
+    q = torch.empty_like(x)
+    k = torch.empty_like(x)
+    g = torch.empty(dt.shape, device=x.device, dtype=torch.float32)
+    check(_lib.lib().cpla_ssd_inputs(ctypes.byref(sp), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(q), _ptr(k),
+                                     _ptr(g), _stream()))
+    y, la = forward(q, k, x, g, num_shards=num_shards, initial_state=initial_state, cu_seqlens=cu_seqlens,
+                    packed=packed, w=dt)
+    return y, SsdContext(sp, dt, A, la)
+
+
+def ssd_backward(dy: torch.Tensor, ctx: SsdContext, d_final_state: Optional[torch.Tensor] = None):
+    """(dx, d_dt, dA, dB, dC, d_initial_state); d_initial_state is None with packed
+    sequences."""
+    dq, dk, dv, dg, dS0, dw = backward(dy, ctx.la, d_final_state, grad_dtype=torch.float32)
+    sp = ctx.problem
+    dev = dy.device
+    xdt = ctx.la.v.dtype
+    dx = torch.empty(ctx.la.v.shape, device=dev, dtype=xdt)
+    ddt = torch.empty(ctx.dt.shape, device=dev, dtype=torch.float32)
+    dA = torch.empty(ctx.A.shape, device=dev, dtype=torch.float32)
+    Bshape = (sp.B, sp.T, sp.G, sp.N)
+    dB = torch.empty(Bshape, device=dev, dtype=xdt)
+    dC = torch.empty(Bshape, device=dev, dtype=xdt)
+    check(_lib.lib().cpla_ssd_input_grads(ctypes.byref(sp), _ptr(ctx.dt), _ptr(ctx.A), _ptr(dq), _ptr(dk),
+                                          _ptr(dv), _ptr(dg), _ptr(dw), _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB),
+                                          _ptr(dC), _stream()))
+    return dx, ddt, dA, dB, dC, dS0
+
+
+class Mamba2SSD(torch.autograd.Function):
+    """Autograd adapter: y = SSD(x, dt, A, B, C, h_init) with shards simulated on one GPU."""
+
+    @staticmethod
+    def forward(fctx, x, dt, A, B, C, initial_state, num_shards, cu_seqlens):
+        y, c = ssd_forward(x, dt, A, B, C, num_shards=num_shards, initial_state=initial_state,
+                           cu_seqlens=cu_seqlens)
+        fctx.cpla = c
+        return y
+
+    @staticmethod
+    def backward(fctx, dy):
+        dx, ddt, dA, dB, dC, dS0 = ssd_backward(dy.contiguous(), fctx.cpla)
+        if not fctx.cpla.la.has_initial_state:
+            dS0 = None
+        return dx, ddt, dA, dB, dC, dS0, None, None
+
+
+def mamba2_ssd(x, dt, A, B, C, initial_state=None, *, num_shards: int = 1, cu_seqlens=None):
+    return Mamba2SSD.apply(x, dt, A, B, C, initial_state, num_shards, cu_seqlens)

@@ -109,12 +109,19 @@ fwd_fn pick_fwd(int dtype, int D, int decay) {
 }
 
 template <bool APPLY>
-bwd_fn pick_bwd(int dtype, int D, int decay) {
+bwd_fn pick_bwd(int dtype, int D, int decay, bool grad_f32 = false) {
+  if (grad_f32) {   // fp32 gradients from bf16 inputs: scalar decay only
+    if (!APPLY || dtype != CPLA_BF16 || decay != CPLA_DECAY_SCALAR) return nullptr;
+    if (D == 16) return bwd_walk<bf16_t, 16, 16, 1, true, true>;
+    if (D == 64) return bwd_walk<bf16_t, 64, 64, 1, true, true>;
+    if (D == 128) return bwd_walk<bf16_t, 128, 128, 1, true, true>;
+    return nullptr;
+  }
 #define CPLA_BWD_CASE(E, DD)                                              \
   if (D == DD) {                                                          \
-    if (decay == 0) return bwd_walk<E, DD, DD, 0, APPLY>;                 \
-    if (decay == 1) return bwd_walk<E, DD, DD, 1, APPLY>;                 \
-    return bwd_walk<E, DD, DD, 2, APPLY>;                                 \
+    if (decay == 0) return bwd_walk<E, DD, DD, 0, APPLY, false>;          \
+    if (decay == 1) return bwd_walk<E, DD, DD, 1, APPLY, false>;          \
+    return bwd_walk<E, DD, DD, 2, APPLY, false>;                          \
   }
   if (dtype == CPLA_BF16) {
     CPLA_BWD_CASE(bf16_t, 16)
@@ -173,11 +180,25 @@ extern "C" int64_t cpla_chunk_states_bytes(const cpla_problem* p) {
   return p->B * p->H * (p->T / p->chunk) * p->dk * p->dv * (int64_t)sizeof(float);
 }
 
-extern "C" cpla_status cp_forward_prepare(const cpla_problem* p, const cpla_packed* packed, const void* k,
-                                          const void* v, const float* g, float* fwd_summary, hipStream_t stream) {
+namespace cpla {
+namespace {
+// The optional per-token input weight w (and its gradient dw) of the scalar decay.
+cpla_status check_weight(const cpla_problem* p, const float* w, const float* dw) {
+  if (!w && !dw) return CPLA_OK;
+  if (p->decay != CPLA_DECAY_SCALAR) return fail(CPLA_E_INVALID, "input weights need a scalar decay");
+  if (!w) return fail(CPLA_E_INVALID, "dw needs w");
+  return check_ptr(w, "w", true);
+}
+}  // namespace
+}  // namespace cpla
+
+static cpla_status forward_prepare(const cpla_problem* p, const cpla_packed* packed, const void* k,
+                                   const void* v, const float* g, const float* w, float* fwd_summary,
+                                   hipStream_t stream) {
   clear_error();
   cpla_status st;
   if ((st = check_problem(p)) != CPLA_OK) return st;
+  if ((st = check_weight(p, w, nullptr)) != CPLA_OK) return st;
   if ((st = check_packed(p, packed, false, false)) != CPLA_OK) return st;
   if ((st = check_ptr(k, "k", true)) != CPLA_OK) return st;
   if ((st = check_ptr(v, "v", true)) != CPLA_OK) return st;
@@ -186,7 +207,7 @@ extern "C" cpla_status cp_forward_prepare(const cpla_problem* p, const cpla_pack
   FwdArgs a = {};
   a.B = p->B; a.T = p->T; a.H = p->H; a.W = cpla_summary_width(p);
   a.P = p->num_shards; a.rank_begin = p->rank_begin; a.m_slot = (int)m_slot_of(p);
-  a.k = k; a.v = v; a.g = g;
+  a.k = k; a.v = v; a.g = g; a.w = w;
   a.seq_idx = packed ? packed->seq_idx : nullptr;
   a.summary = fwd_summary;
   fwd_fn fn = pick_fwd<false>(p->dtype, (int)p->dk, p->decay);
@@ -195,13 +216,25 @@ extern "C" cpla_status cp_forward_prepare(const cpla_problem* p, const cpla_pack
   return launched("cp_forward_prepare");
 }
 
-extern "C" cpla_status cp_forward_apply(const cpla_problem* p, const cpla_packed* packed, const void* q,
-                                        const void* k, const void* v, const float* g, const float* fwd_summary,
-                                        const float* initial_state, void* o, float* shard_in_state,
-                                        float* final_state, void* chunk_states, hipStream_t stream) {
+extern "C" cpla_status cp_forward_prepare(const cpla_problem* p, const cpla_packed* packed, const void* k,
+                                          const void* v, const float* g, float* fwd_summary, hipStream_t stream) {
+  return forward_prepare(p, packed, k, v, g, nullptr, fwd_summary, stream);
+}
+
+extern "C" cpla_status cp_forward_prepare_weighted(const cpla_problem* p, const cpla_packed* packed, const void* k,
+                                                   const void* v, const float* g, const float* w,
+                                                   float* fwd_summary, hipStream_t stream) {
+  return forward_prepare(p, packed, k, v, g, w, fwd_summary, stream);
+}
+
+static cpla_status forward_apply(const cpla_problem* p, const cpla_packed* packed, const void* q, const void* k,
+                                 const void* v, const float* g, const float* w, const float* fwd_summary,
+                                 const float* initial_state, void* o, float* shard_in_state, float* final_state,
+                                 void* chunk_states, hipStream_t stream) {
   clear_error();
   cpla_status st;
   if ((st = check_problem(p)) != CPLA_OK) return st;
+  if ((st = check_weight(p, w, nullptr)) != CPLA_OK) return st;
   if ((st = check_packed(p, packed, true, false)) != CPLA_OK) return st;
   if ((st = check_ptr(q, "q", true)) != CPLA_OK) return st;
   if ((st = check_ptr(k, "k", true)) != CPLA_OK) return st;
@@ -220,7 +253,7 @@ extern "C" cpla_status cp_forward_apply(const cpla_problem* p, const cpla_packed
   FwdArgs a = {};
   a.B = p->B; a.T = p->T; a.H = p->H; a.W = cpla_summary_width(p);
   a.P = p->num_shards; a.rank_begin = p->rank_begin; a.m_slot = (int)m_slot_of(p);
-  a.q = q; a.k = k; a.v = v; a.g = g;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.w = w;
   a.seq_idx = packed ? packed->seq_idx : nullptr;
   a.state_in = shard_in_state;
   a.out = o;
@@ -229,6 +262,23 @@ extern "C" cpla_status cp_forward_apply(const cpla_problem* p, const cpla_packed
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no forward kernel for this configuration");
   hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(threads_for(p)), 0, stream, a);
   return launched("cp_forward_apply");
+}
+
+extern "C" cpla_status cp_forward_apply(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                        const void* k, const void* v, const float* g, const float* fwd_summary,
+                                        const float* initial_state, void* o, float* shard_in_state,
+                                        float* final_state, void* chunk_states, hipStream_t stream) {
+  return forward_apply(p, packed, q, k, v, g, nullptr, fwd_summary, initial_state, o, shard_in_state, final_state,
+                       chunk_states, stream);
+}
+
+extern "C" cpla_status cp_forward_apply_weighted(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                                 const void* k, const void* v, const float* g, const float* w,
+                                                 const float* fwd_summary, const float* initial_state, void* o,
+                                                 float* shard_in_state, float* final_state, void* chunk_states,
+                                                 hipStream_t stream) {
+  return forward_apply(p, packed, q, k, v, g, w, fwd_summary, initial_state, o, shard_in_state, final_state,
+                       chunk_states, stream);
 }
 
 extern "C" cpla_status cp_backward_prepare(const cpla_problem* p, const cpla_packed* packed, const void* q,
@@ -253,14 +303,19 @@ extern "C" cpla_status cp_backward_prepare(const cpla_problem* p, const cpla_pac
   return launched("cp_backward_prepare");
 }
 
-extern "C" cpla_status cp_backward_apply(const cpla_problem* p, const cpla_packed* packed, const void* q,
-                                         const void* k, const void* v, const float* g, const void* dO,
-                                         const void* chunk_states, const float* bwd_summary,
-                                         const float* d_final_state, void* dq, void* dk, void* dv, float* dg,
-                                         float* shard_out_grad, float* d_initial_state, hipStream_t stream) {
+static cpla_status backward_apply(const cpla_problem* p, const cpla_packed* packed, const void* q, const void* k,
+                                  const void* v, const float* g, const float* w, const void* dO,
+                                  const void* chunk_states, const float* bwd_summary, const float* d_final_state,
+                                  void* dq, void* dk, void* dv, float* dg, float* dw, float* shard_out_grad,
+                                  float* d_initial_state, int32_t grad_dtype, hipStream_t stream) {
   clear_error();
   cpla_status st;
   if ((st = check_problem(p)) != CPLA_OK) return st;
+  if (grad_dtype != p->dtype && grad_dtype != CPLA_F32)
+    return fail(CPLA_E_DTYPE, "grad_dtype must be the input dtype or CPLA_F32");
+  const bool grad_f32 = grad_dtype != p->dtype;
+  if ((st = check_weight(p, w, dw)) != CPLA_OK) return st;
+  if ((st = check_ptr(dw, "dw", false)) != CPLA_OK) return st;
   if ((st = check_packed(p, packed, false, true)) != CPLA_OK) return st;
   if ((st = check_ptr(q, "q", true)) != CPLA_OK) return st;
   if ((st = check_ptr(k, "k", true)) != CPLA_OK) return st;
@@ -284,13 +339,33 @@ extern "C" cpla_status cp_backward_apply(const cpla_problem* p, const cpla_packe
   BwdArgs a = {};
   a.B = p->B; a.T = p->T; a.H = p->H; a.W = cpla_summary_width(p);
   a.P = p->num_shards; a.rank_begin = p->rank_begin; a.m_slot = (int)m_slot_of(p);
-  a.q = q; a.k = k; a.v = v; a.g = g; a.dO = dO;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.w = w; a.dO = dO;
   a.seq_idx = packed ? packed->seq_idx : nullptr;
   a.chunk_states = reinterpret_cast<const float*>(chunk_states);
   a.grad_in = shard_out_grad;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg;
-  bwd_fn fn = pick_bwd<true>(p->dtype, (int)p->dk, p->decay);
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dw = dw;
+  bwd_fn fn = pick_bwd<true>(p->dtype, (int)p->dk, p->decay, grad_f32);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no backward kernel for this configuration");
   hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(threads_for(p)), 0, stream, a);
   return launched("cp_backward_apply");
+}
+
+extern "C" cpla_status cp_backward_apply(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                         const void* k, const void* v, const float* g, const void* dO,
+                                         const void* chunk_states, const float* bwd_summary,
+                                         const float* d_final_state, void* dq, void* dk, void* dv, float* dg,
+                                         float* shard_out_grad, float* d_initial_state, hipStream_t stream) {
+  return backward_apply(p, packed, q, k, v, g, nullptr, dO, chunk_states, bwd_summary, d_final_state, dq, dk, dv,
+                        dg, nullptr, shard_out_grad, d_initial_state, p ? p->dtype : 0, stream);
+}
+
+extern "C" cpla_status cp_backward_apply_weighted(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                                  const void* k, const void* v, const float* g, const float* w,
+                                                  const void* dO, const void* chunk_states,
+                                                  const float* bwd_summary, const float* d_final_state, void* dq,
+                                                  void* dk, void* dv, float* dg, float* dw,
+                                                  float* shard_out_grad, float* d_initial_state,
+                                                  int32_t grad_dtype, hipStream_t stream) {
+  return backward_apply(p, packed, q, k, v, g, w, dO, chunk_states, bwd_summary, d_final_state, dq, dk, dv, dg, dw,
+                        shard_out_grad, d_initial_state, grad_dtype, stream);
 }

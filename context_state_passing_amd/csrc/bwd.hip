@@ -26,6 +26,8 @@
 //
 // Every fp32 intermediate that feeds an MFMA (scores, score gradients, S0, dS,
 // exp-scaled q/k tiles) is split into bf16 hi + lo parts; inputs are exact.
+#include <type_traits>
+
 #include "chunk_common.hpp"
 #include "kernels.hpp"
 
@@ -69,9 +71,12 @@ __device__ __forceinline__ f32x4 lane_gamma(f32x4 x, f32x4& carry) {
   return out;
 }
 
-template <typename E, int DK, int DV, int DECAY, bool APPLY>
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32>
 __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_walk(BwdArgs a) {
   using G = Geo<E, DK, DV>;
+  // dq, dk, dv in the input dtype, or in fp32 (GF32: for callers that sum them
+  // further, e.g. over the heads sharing an input)
+  using GE = typename std::conditional<GF32, float, E>::type;
   constexpr bool SP = Split<E>::on;
   constexpr bool DIAG = DECAY == DECAY_DIAG, SCAL = DECAY == DECAY_SCALAR;
   constexpr int NA = APPLY ? 1 : 0;
@@ -112,6 +117,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
   constexpr int NU = (APPLY && SCAL) ? G::NW * CH : 1;           // scalar dg token partials
   __shared__ float s_gs[DIAG ? 1 : CH], s_fq[CH], s_fk[CH], s_red[NRED], s_el[DIAG ? G::DKP : 1];
   __shared__ float s_u1[NU], s_u4[NU];
+  __shared__ float s_w[SCAL ? CH : 1];   // per-token input weights (scalar decay)
 
   float* s_gam = DIAG ? reinterpret_cast<float*>(s_reg) : s_gs;
   E* s_ah = reinterpret_cast<E*>(s_reg);
@@ -228,6 +234,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
     } else {
       aseg.load(a.seq_idx, t0, tidf & 63);
       agam.load(a.g, b, h, t0, a.T, a.H, tidf);
+      if constexpr (APPLY) agam.load_w(a.w, b, h, t0, a.T, a.H, tidf);
       aq.load(q, b, h, t0, a.T, a.H, tidf);
       if constexpr (APPLY) {
         ak.load(k, b, h, t0, a.T, a.H, tidf);
@@ -236,7 +243,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
       ado.load(dO, b, h, t0, a.T, a.H, tidf);
     }
     seg = aseg.finish(a.seq_idx);
-    finish_gamma<DK, DECAY, G::NT>(agam, seg, s_gam, s_fq, s_fk, tidf, gam_hi);
+    finish_gamma<DK, DECAY, G::NT>(agam, seg, s_gam, s_fq, s_fk, tidf, gam_hi, SCAL ? s_w : nullptr);
     any_start |= seg.any();
     const float keep = seg.any() ? 0.f : 1.f;
 
@@ -339,8 +346,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
             va[rr] = xa[rr];
             vd[rr] = xd[rr];
             if constexpr (SCAL) {
-              const float dec = __expf(s_gam[i] - s_gam[j]);
-              pp = va[rr] * vd[rr] * dec;   // one decay factor: exp(Gam_i - Gam_j) (q_i.k_j)(dO_i.v_j)
+              // exp(Gam_i - Gam_j) and the input weight of token j, applied once
+              const float dec = __expf(s_gam[i] - s_gam[j]) * s_w[j];
+              pp = va[rr] * vd[rr] * dec;   // exp(Gam_i - Gam_j) w_j (q_i.k_j)(dO_i.v_j)
               va[rr] *= dec;
               vd[rr] *= dec;
             }
@@ -380,7 +388,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
       }
 
       // ---- dv^T tiles: rows = owned d_v tiles, columns = tokens j ---------------------
-      E* dvp = reinterpret_cast<E*>(a.dv);
+      GE* dvp = reinterpret_cast<GE*>(a.dv);
 #pragma unroll
       for (int cc = 0; cc < G::CPWV; ++cc) {
         const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
@@ -429,8 +437,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
       }
 
       // ---- dq^T and dk^T tiles: rows = owned d_k tiles, columns = tokens ---------------
-      E* dqp = reinterpret_cast<E*>(a.dq);
-      E* dkp = reinterpret_cast<E*>(a.dk);
+      GE* dqp = reinterpret_cast<GE*>(a.dq);
+      GE* dkp = reinterpret_cast<GE*>(a.dk);
       float u1p[4] = {0.f, 0.f, 0.f, 0.f}, u4p[4] = {0.f, 0.f, 0.f, 0.f};  // scalar: per-I token partials
       float t3p = 0.f;                                                      // scalar: T3 partial
       // diagonal dg: wv holds w_t = Q~*(dq before exp(Gam)) - K~*(intra dk) after the dq
@@ -692,6 +700,10 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
           float dgv = x + y4 + t3;
           if ((seg.starts >> t) & 1ull) dgv = 0.f;
           a.dg[(b * a.T + t0 + t) * a.H + h] = dgv;
+          // input-weight gradient dw_t = k_t^T dS_t v_t: the intra part is column t
+          // of the P tile on and below the diagonal, the tail part is u4; both carry
+          // w_t (in the score decay and the tail factor), divided out here
+          if (a.dw) a.dw[(b * a.T + t0 + t) * a.H + h] = (colb + s_p[t * (CH + 1) + t] + u4) / s_w[t];
         }
       }
     }
@@ -799,12 +811,16 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
 }
 
 #define CPLA_INST_BWD(E, D, DEC)                                                   \
-  template __global__ void bwd_walk<E, D, D, DEC, false>(BwdArgs);                \
-  template __global__ void bwd_walk<E, D, D, DEC, true>(BwdArgs);
+  template __global__ void bwd_walk<E, D, D, DEC, false, false>(BwdArgs);         \
+  template __global__ void bwd_walk<E, D, D, DEC, true, false>(BwdArgs);
 #define CPLA_INST_BWD3(E, D) CPLA_INST_BWD(E, D, 0) CPLA_INST_BWD(E, D, 1) CPLA_INST_BWD(E, D, 2)
 CPLA_INST_BWD3(bf16_t, 16)
 CPLA_INST_BWD3(bf16_t, 64)
 CPLA_INST_BWD3(bf16_t, 128)
+// fp32 gradients from bf16 inputs: the scalar decay (the Mamba2 parametrisation)
+template __global__ void bwd_walk<bf16_t, 16, 16, 1, true, true>(BwdArgs);
+template __global__ void bwd_walk<bf16_t, 64, 64, 1, true, true>(BwdArgs);
+template __global__ void bwd_walk<bf16_t, 128, 128, 1, true, true>(BwdArgs);
 CPLA_INST_BWD3(float, 16)
 CPLA_INST_BWD3(float, 64)
 

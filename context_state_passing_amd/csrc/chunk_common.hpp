@@ -88,7 +88,14 @@ struct GamRegs {
   static constexpr int CPW = 64 / TPC;
   static_assert(DECAY != DECAY_DIAG || (TPC <= 64 && 64 % TPC == 0), "column split must fit a wave");
   float v[TOK];
+  float wt = 1.f;   // scalar decay: the token's input weight (1 without one)
   __device__ __forceinline__ static int column(int tid) { return (tid >> 6) * CPW + (tid & 63) % CPW; }
+  // scalar decay with a per-token input weight: thread tid < 64 holds token tid's
+  __device__ __forceinline__ void load_w(const float* __restrict__ w, int64_t b, int64_t h, int64_t t0, int64_t T,
+                                         int64_t H, int tid = threadIdx.x) {
+    if constexpr (DECAY == DECAY_SCALAR)
+      if (w && tid < CH) wt = w[(b * T + t0 + tid) * H + h];
+  }
   __device__ __forceinline__ static int part(int tid) { return (tid & 63) / CPW; }
   __device__ __forceinline__ void load(const float* __restrict__ g, int64_t b, int64_t h, int64_t t0, int64_t T,
                                        int64_t H, int tid = threadIdx.x) {
@@ -147,12 +154,13 @@ struct GamRegs {
 //   none: nothing.
 // and the per-token factors
 //   fq[i] = live_i * (scalar ? exp(Gam_i) : 1)
-//   fk[j] = tail_j * (scalar ? exp(Gam_last - Gam_j) : 1)
+//   fk[j] = tail_j * (scalar ? exp(Gam_last - Gam_j) * w_j : 1)
+// and, for a scalar decay, the input weights w_j (1 without them) into wl.
 // Ends with a barrier.
 template <int DK, int DECAY, int NT>
 __device__ __forceinline__ void finish_gamma(GamRegs<DK, DECAY, NT>& R, const ChunkSeg& seg, float* gam,
                                              float* fq, float* fk, int tid = threadIdx.x,
-                                             float* gam_hi = nullptr) {
+                                             float* gam_hi = nullptr, float* wl = nullptr) {
   if constexpr (DECAY == DECAY_SCALAR) {
     if (tid < CH) {
       float x = R.v[0];
@@ -164,7 +172,8 @@ __device__ __forceinline__ void finish_gamma(GamRegs<DK, DECAY, NT>& R, const Ch
       gam[tid] = x;
       const float last = __shfl(x, 63, 64);
       fq[tid] = seg.live(tid) ? __expf(x) : 0.f;
-      fk[tid] = seg.tail(tid) ? __expf(last - x) : 0.f;
+      fk[tid] = seg.tail(tid) ? __expf(last - x) * R.wt : 0.f;
+      if (wl) wl[tid] = R.wt;
     }
   } else {
     if constexpr (DECAY == DECAY_DIAG) {

@@ -108,6 +108,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
   __shared__ __attribute__((aligned(16))) E s_a[NQT * G::TILE_A + 8];    // scores, hi part
   __shared__ __attribute__((aligned(16))) E s_al[NAL * G::TILE_A + 8];   // scores, lo part
   __shared__ float s_gam[GAM], s_fq[CH], s_fk[CH], s_el[G::DKP];
+  __shared__ float s_w[DECAY == DECAY_SCALAR ? CH : 1];   // per-token input weights
 
   float* const gam_hi = GSPLIT ? reinterpret_cast<float*>(s_v) : nullptr;
   const float* const gam_last = GSPLIT ? gam_hi + (CH / 2 - 1) * DK : s_gam + (CH - 1) * DK;
@@ -153,6 +154,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
     const int64_t t = tshard + (int64_t)c * CH;
     rseg.load(a.seq_idx, t);
     rgam.load(a.g, b, h, t, a.T, a.H);
+    rgam.load_w(a.w, b, h, t, a.T, a.H);
     rk.load(k, b, h, t, a.T, a.H);
     if constexpr (APPLY) rq.load(q, b, h, t, a.T, a.H);
     rv.load(v, b, h, t, a.T, a.H);
@@ -164,7 +166,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
     if constexpr (!APPLY) prefetch(c);
     const ChunkSeg seg = rseg.finish(a.seq_idx);
     any_start |= seg.any();
-    finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk, threadIdx.x, gam_hi);
+    finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk, threadIdx.x, gam_hi,
+                                   DECAY == DECAY_SCALAR ? s_w : nullptr);
     if constexpr (DECAY == DECAY_DIAG) {
       if (threadIdx.x < DK) {
         const float gl = gam_last[threadIdx.x];
@@ -216,7 +219,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
           float x = 0.f;
           if (seg.same(i, j)) {
             x = acc[rr];
-            if constexpr (DECAY == DECAY_SCALAR) x *= __expf(s_gam[i] - s_gam[j]);
+            if constexpr (DECAY == DECAY_SCALAR) x *= __expf(s_gam[i] - s_gam[j]) * s_w[j];
           }
           store_split(s_a, s_al, i * G::LDA + j, x);
         }

@@ -15,6 +15,7 @@ struct FwdArgs {
   const void* k;
   const void* v;
   const float* g;
+  const float* w;            // scalar decay: per-token input weight [B,T,H] (fp32), or null (1)
   const int32_t* seq_idx;    // packed sequences or null
   const float* state_in;     // apply: incoming state of every shard [P,B,H,dk,dv]
   float* summary;            // prepare: [P,B,H,W]
@@ -29,6 +30,7 @@ struct BwdArgs {
   const void* k;
   const void* v;
   const float* g;
+  const float* w;            // scalar decay: per-token input weight, or null (1)
   const void* dO;
   const int32_t* seq_idx;
   const float* chunk_states; // apply: saved forward states (fp32)
@@ -38,6 +40,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* dg;
+  float* dw;                 // apply, with w: gradient w.r.t. w [B,T,H] (fp32)
 };
 
 struct ScanArgs {
@@ -52,7 +55,7 @@ struct ScanArgs {
 
 template <typename E, int DK, int DV, int DECAY, bool APPLY>
 __global__ void fwd_walk(FwdArgs a);
-template <typename E, int DK, int DV, int DECAY, bool APPLY>
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32>
 __global__ void bwd_walk(BwdArgs a);
 __global__ void affine_scan(ScanArgs a);
 

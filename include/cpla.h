@@ -64,7 +64,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;
 
-#define CPLA_ABI_VERSION 1
+#define CPLA_ABI_VERSION 2
 
 typedef enum {
   CPLA_OK = 0,
@@ -149,6 +149,35 @@ cpla_status cp_backward_apply(const cpla_problem* p, const cpla_packed* packed,
                               float* shard_out_grad, float* d_initial_state,
                               hipStream_t stream);
 
+/* Weighted variants (scalar decay only): each token's input k_t v_t^T enters the
+ * state weighted by w_t > 0, w [B,T,H] fp32 (device; NULL = 1):
+ *   S_t = exp(g_t) S_{t-1} + w_t k_t v_t^T.
+ * The weight is applied in fp32 inside the walks (in the score tile and the
+ * tail factor of the state update), never folded into the bf16 k or v. With w,
+ * cp_backward_apply_weighted also writes dw [B,T,H] fp32 (nullable): dw_t =
+ * k_t^T dS_t v_t, formed as (dv_t . v_t) / w_t from dv in fp32 before its
+ * rounding. cp_backward_prepare does not depend on w. Mamba2's dt is such a
+ * weight (see the SSD calls below). grad_dtype is the cpla_dtype of dq, dk, dv:
+ * the input dtype, or CPLA_F32 with bf16 inputs and a scalar decay (gradients a
+ * caller sums further before rounding). Errors as for the unweighted calls; a
+ * weight with another decay is CPLA_E_INVALID, another grad_dtype
+ * CPLA_E_DTYPE. */
+cpla_status cp_forward_prepare_weighted(const cpla_problem* p, const cpla_packed* packed,
+                                        const void* k, const void* v, const float* g, const float* w,
+                                        float* fwd_summary, hipStream_t stream);
+cpla_status cp_forward_apply_weighted(const cpla_problem* p, const cpla_packed* packed,
+                                      const void* q, const void* k, const void* v, const float* g,
+                                      const float* w, const float* fwd_summary,
+                                      const float* initial_state, void* o, float* shard_in_state,
+                                      float* final_state, void* chunk_states, hipStream_t stream);
+cpla_status cp_backward_apply_weighted(const cpla_problem* p, const cpla_packed* packed,
+                                       const void* q, const void* k, const void* v, const float* g,
+                                       const float* w, const void* dO, const void* chunk_states,
+                                       const float* bwd_summary, const float* d_final_state,
+                                       void* dq, void* dk, void* dv, float* dg, float* dw,
+                                       float* shard_out_grad, float* d_initial_state,
+                                       int32_t grad_dtype, hipStream_t stream);
+
 /* build_packed_sequence_cp_metadata (host memory, pure, thread-safe): rank-local
  * packed metadata from the global per-token sequence ids (length T, starting at
  * 0, each step 0 or 1, T % cp_size == 0). local_seq_idx [T/cp_size] receives the
@@ -173,6 +202,43 @@ cpla_status cpla_packed_rank_slices(const int32_t* global_seq_idx, int64_t T, in
  * increasing, 0 first, T last. */
 cpla_status cpla_seq_idx_from_cu_seqlens(const int32_t* cu_seqlens, int32_t n_seqs, int64_t T,
                                          int32_t* seq_idx);
+
+/* ---- Mamba2 (SSD) parametrisation of the scalar-decay path ------------------------
+ * The axolotl-ringmaster README (Status table, Layout) runs Mamba2 SSM context
+ * parallelism through the same exact CP linear scan as linear attention. Mamba2's
+ * selective state space, for head h of group gr = h / (H / G):
+ *   h_t = exp(dt_t A_h) h_{t-1} + dt_t B_t x_t^T   (state N x P),   y_t = h_t^T C_t
+ * is the weighted scalar-decay recurrence above with q = C[gr], k = B[gr], v = x,
+ * g = A dt and w = dt: run cpla_ssd_inputs, the weighted cp_* calls (and
+ * cp_backward_prepare) with v = x and w = dt, then cpla_ssd_input_grads.
+ * Shapes: x, q, k [B,T,H,N] and B, C [B,T,G,N] in `dtype`; dt, g [B,T,H] and A [H]
+ * fp32 (dt already positive: any softplus or bias is the caller's); the head dim
+ * P equals the state size N here (the cp_* calls need dk == dv). All pointers
+ * are device memory owned by the caller, 16-byte aligned; work is enqueued on
+ * `stream`; invalid arguments return an error and launch nothing. */
+typedef struct {
+  int64_t B, T, H;           /* batch, tokens, heads                                   */
+  int64_t G;                 /* groups sharing B and C: H % G == 0                     */
+  int64_t N;                 /* state size = head dim: a multiple of 4, N/4 a power of
+                                two up to 64                                          */
+  int32_t dtype;             /* cpla_dtype of B, C, q, k, dq, dk, dB, dC               */
+} cpla_ssd_problem;
+
+/* q[b,t,h] = C[b,t,gr], k[b,t,h] = B[b,t,gr] (copies) and g = A dt (fp32). */
+cpla_status cpla_ssd_inputs(const cpla_ssd_problem* p, const float* dt, const float* A,
+                            const void* B, const void* C, void* q, void* k, float* g,
+                            hipStream_t stream);
+
+/* The chain rule from the gradients of cp_backward_apply_weighted, run with
+ * grad_dtype CPLA_F32 (dq, dk, dv, dg, dw all fp32), to the Mamba2 inputs:
+ * dx = dv (dtype [B,T,H,N]), d_dt = dw + A dg (fp32 [B,T,H]), dA = sum over
+ * (b, t) of dt dg (fp32 [H], summed in a fixed order: the same on every run),
+ * dB = sum over the group's heads of dk and dC of dq (dtype [B,T,G,N], summed in
+ * fp32 and rounded once). */
+cpla_status cpla_ssd_input_grads(const cpla_ssd_problem* p, const float* dt, const float* A,
+                                 const float* dq, const float* dk, const float* dv, const float* dg,
+                                 const float* dw, void* dx, float* d_dt, float* dA, void* dB, void* dC,
+                                 hipStream_t stream);
 
 /* Message of the last failure on the calling thread; valid until its next call. */
 const char* cpla_last_error(void);

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert L.cpla_abi_version() == 1
+    assert L.cpla_abi_version() == 2
 
 
 def prob(**kw):

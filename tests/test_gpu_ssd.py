@@ -1,0 +1,153 @@
+"""GPU parity for the Mamba2 (SSD) parametrisation: cpla_ssd_inputs, the four CP
+calls (scalar decay) and cpla_ssd_input_grads, through the C ABI, against the
+fp64 SSD oracle (oracle/ssd.py: the recurrence in Mamba2's own terms) on the
+same seeded inputs, element by element, for y and every input gradient.
+
+Cases span several chunks per shard and several shards, groups shared by 1, 2
+and 4 heads, state sizes 16, 64 and 128, an initial state, and packed
+sequences with boundaries inside chunks. Tolerances are those of the
+linear-attention parity tests (fp32 rtol 1e-4 / atol 1e-5, bf16 rtol 2e-2 /
+atol 2e-3), plus, for d_dt only, the accumulation error of its two terms:
+d_dt = dw + A dg is a difference of fp32 quantities, each formed from
+chunk-wide sums (suffix sums over the chunk's 64 tokens of products over the
+state size), which cancel to results thousands of times smaller than
+themselves on some tokens; the bound added is 64 * 2^-24 * s, with s the
+largest |dw| + |A dg| in the token's 64-token chunk (terms from the oracle).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from _parity import assert_close, tolerances
+from oracle import metadata as omd, recurrence as orec, ssd as ossd
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: make_ssd overrides
+    "bf16_n64_g2": dict(B=2, T=512, H=8, G=2, N=64, num_shards=4),
+    "bf16_n128_init": dict(B=1, T=512, H=4, G=1, N=128, num_shards=2, with_initial_state=True),
+    "bf16_n64_packed": dict(B=1, T=1024, H=4, G=2, N=64, num_shards=4, packed=True, len_range=(40, 300)),
+    "fp32_n16_g4": dict(B=2, T=256, H=4, G=4, N=16, num_shards=4, dtype=torch.float32),
+    "fp32_n64_init": dict(B=1, T=384, H=2, G=1, N=64, num_shards=3, dtype=torch.float32,
+                          with_initial_state=True),
+}
+
+
+def _np(t):
+    return None if t is None else t.detach().float().cpu().double().numpy()
+
+
+def _run_gpu(wl):
+    import context_state_passing_amd as cpla
+    dev = torch.device("cuda:0")
+    x, dt, A, Bm, Cm, dy = (t.to(dev) for t in (wl.x, wl.dt, wl.A, wl.Bm, wl.Cm, wl.dy))
+    h0 = None if wl.initial_state is None else wl.initial_state.to(dev)
+    y, ctx = cpla.ssd_forward(x, dt, A, Bm, Cm, num_shards=wl.num_shards, initial_state=h0,
+                              cu_seqlens=wl.cu_seqlens)
+    dx, ddt, dA, dB, dC, dh0 = cpla.ssd_backward(dy, ctx)
+    torch.cuda.synchronize()
+    out = {"y": y, "dx": dx, "d_dt": ddt, "dA": dA, "dB": dB, "dC": dC}
+    if h0 is not None:
+        out["d_initial_state"] = dh0
+    return {k: v.detach().cpu() for k, v in out.items()}
+
+
+def _run_oracle(wl):
+    seq = None
+    if wl.cu_seqlens is not None:
+        seq = omd.seq_idx_from_cu_seqlens(wl.cu_seqlens.numpy(), wl.T)
+    args = [_np(t) for t in (wl.x, wl.dt, wl.A, wl.Bm, wl.Cm)]
+    h0 = _np(wl.initial_state)
+    y, _ = ossd.ssd_forward(*args, h_init=h0, seq_idx=seq)
+    dx, ddt, dA, dB, dC, dh0 = ossd.ssd_backward(*args, _np(wl.dy), h_init=h0, seq_idx=seq)
+    out = {"y": y, "dx": dx, "d_dt": ddt, "dA": dA, "dB": dB, "dC": dC}
+    if h0 is not None:
+        out["d_initial_state"] = dh0
+    return out
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_ssd_parity(case, gpu_available):
+    print(f"[gpu-case] ssd {case}", file=sys.stderr, flush=True)
+    wl = workloads.make_ssd(**CASES[case])
+    got = _run_gpu(wl)
+    ref = _run_oracle(wl)
+    rtol, atol = tolerances(wl.dtype)
+    for name in ref:
+        if name == "d_dt":
+            continue
+        assert_close(name, _np(got[name]), ref[name], rtol, atol)
+    scale = _ddt_term_scale(wl)
+    err = np.abs(_np(got["d_dt"]) - ref["d_dt"])
+    lim = atol + rtol * np.abs(ref["d_dt"]) + 64 * 2.0 ** -24 * scale
+    assert np.all(err <= lim), f"d_dt: {int((err > lim).sum())}/{err.size} outside; worst excess {(err - lim).max():.3e}"
+
+
+def _ddt_term_scale(wl):
+    """|dw| + |A dg| per (b, t, h) from the linear-attention oracle under the SSD map."""
+    seq = None
+    if wl.cu_seqlens is not None:
+        seq = omd.seq_idx_from_cu_seqlens(wl.cu_seqlens.numpy(), wl.T)
+    x, dt, A, Bm, Cm = (_np(t) for t in (wl.x, wl.dt, wl.A, wl.Bm, wl.Cm))
+    grp = np.arange(wl.H) // (wl.H // wl.G)
+    g = A[None, None, :] * dt
+    res = orec.backward(Cm[:, :, grp], Bm[:, :, grp], x, g, "scalar", dO=_np(wl.dy),
+                        initial_state=_np(wl.initial_state), seq_idx=seq, w=dt)
+    term = np.abs(res[5]) + np.abs(A[None, None, :] * res[3])             # [B, T, H]
+    B_, T_, H_ = term.shape
+    nc = (T_ + 63) // 64
+    pad = np.zeros((B_, nc * 64, H_))
+    pad[:, :T_] = term
+    cmax = pad.reshape(B_, nc, 64, H_).max(axis=2, keepdims=True)
+    return np.broadcast_to(cmax, (B_, nc, 64, H_)).reshape(B_, nc * 64, H_)[:, :T_]
+
+
+def test_ssd_deterministic(gpu_available):
+    print("[gpu-case] ssd determinism", file=sys.stderr, flush=True)
+    wl = workloads.make_ssd(**CASES["bf16_n64_g2"])
+    a = _run_gpu(wl)
+    b = _run_gpu(wl)
+    for name in a:
+        assert torch.equal(a[name], b[name]), name
+
+
+# ---- the weighted scalar-decay calls on their own ----------------------------------------
+WEIGHTED = {
+    # name: (workload, overrides)
+    "w_bf16_d128": ("packed_fwdbwd", dict(T=1024, H=2, num_shards=4, len_range=(40, 400))),
+    "w_bf16_d64_init": ("long_fwdbwd", dict(T=512, H=2, d=64, num_shards=4)),
+    "w_fp32_d64": ("scalar_fwd", dict(B=1, H=2, T=512, num_shards=4, backward=True, dtype=torch.float32)),
+}
+
+
+@pytest.mark.parametrize("case", sorted(WEIGHTED))
+def test_weighted_parity(case, gpu_available):
+    import context_state_passing_amd as cpla
+    print(f"[gpu-case] weighted {case}", file=sys.stderr, flush=True)
+    name, ov = WEIGHTED[case]
+    wl = workloads.make(name, **ov)
+    gen = torch.Generator().manual_seed(77)
+    w = torch.exp(0.5 * torch.randn(wl.B, wl.T, wl.H, generator=gen)).contiguous()
+    dev = torch.device("cuda:0")
+    S0 = None if wl.initial_state is None else wl.initial_state.to(dev)
+    o, ctx = cpla.forward(wl.q.to(dev), wl.k.to(dev), wl.v.to(dev), wl.g.to(dev), num_shards=wl.num_shards,
+                          initial_state=S0, cu_seqlens=wl.cu_seqlens, w=w.to(dev))
+    dq, dk, dv, dg, dS0, dw = cpla.backward(wl.dO.to(dev), ctx)
+    torch.cuda.synchronize()
+    seq = None if wl.cu_seqlens is None else omd.seq_idx_from_cu_seqlens(wl.cu_seqlens.numpy(), wl.T)
+    args = [_np(t) for t in (wl.q, wl.k, wl.v, wl.g)]
+    ref_o, ref_S = orec.forward(*args, "scalar", initial_state=_np(wl.initial_state), seq_idx=seq, w=_np(w))
+    ref = orec.backward(*args, "scalar", dO=_np(wl.dO), initial_state=_np(wl.initial_state), seq_idx=seq,
+                        w=_np(w))
+    rtol, atol = tolerances(wl.dtype)
+    got = {"o": o, "final_state": ctx.final_state, "dq": dq, "dk": dk, "dv": dv, "dg": dg, "dw": dw}
+    want = {"o": ref_o, "final_state": ref_S, "dq": ref[0], "dk": ref[1], "dv": ref[2], "dg": ref[3], "dw": ref[5]}
+    if S0 is not None:
+        got["d_initial_state"] = dS0
+        want["d_initial_state"] = ref[4]
+    for n in want:
+        assert_close(n, _np(got[n]), want[n], rtol, atol)

@@ -171,3 +171,87 @@ def make(name: str, *, B: Optional[int] = None, T: Optional[int] = None,
         dO=None if dO is None else dO.to(dt).contiguous(),
         initial_state=None if S0 is None else S0.contiguous(),
         cu_seqlens=cu)
+
+
+# ---- Mamba2 (SSD) inputs --------------------------------------------------------------------
+# Shapes of a Mamba2 layer whose head dim equals its state size (the library's
+# linear-attention path needs dk == dv): x [B,T,H,N], dt [B,T,H], A [H], and B, C
+# [B,T,G,N] shared by the H/G heads of a group. Distributions follow Mamba2's
+# parameter initialisation: dt log-uniform in [1e-3, 1e-1] (as dt after its
+# softplus), A = -U[1, 16] per head; x ~ N(0,1); B, C ~ N(0,1) / N^(1/4) so that
+# C_t . B_s is of order one; dy ~ N(0,1); h_init ~ N(0, 0.1^2).
+
+@dataclasses.dataclass(frozen=True)
+class SsdSpec:
+    index: int
+    B: int
+    T: int
+    H: int
+    G: int
+    N: int
+    dtype: torch.dtype
+    num_shards: int
+
+
+SSD_SPECS = {
+    "ssd_fwdbwd": SsdSpec(6, 2, 4096, 8, 2, 64, torch.bfloat16, 8),
+}
+
+
+@dataclasses.dataclass
+class SsdWorkload:
+    name: str
+    B: int
+    T: int
+    H: int
+    G: int
+    N: int
+    dtype: torch.dtype
+    num_shards: int
+    x: torch.Tensor
+    dt: torch.Tensor
+    A: torch.Tensor
+    Bm: torch.Tensor
+    Cm: torch.Tensor
+    dy: torch.Tensor
+    initial_state: Optional[torch.Tensor]
+    cu_seqlens: Optional[torch.Tensor]
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+
+def make_ssd(name: str = "ssd_fwdbwd", *, B: Optional[int] = None, T: Optional[int] = None,
+             H: Optional[int] = None, G: Optional[int] = None, N: Optional[int] = None,
+             num_shards: Optional[int] = None, packed: bool = False, len_range: tuple = (64, 1024),
+             with_initial_state: bool = False, dtype: Optional[torch.dtype] = None,
+             seed_offset: int = 0) -> SsdWorkload:
+    spec = SSD_SPECS[name]
+    B = spec.B if B is None else B
+    T = spec.T if T is None else T
+    H = spec.H if H is None else H
+    G = spec.G if G is None else G
+    N = spec.N if N is None else N
+    P = spec.num_shards if num_shards is None else num_shards
+    gen = torch.Generator().manual_seed(1000 + spec.index + seed_offset)
+    cu = _lengths(gen, B * T, len_range[0], len_range[1]) if packed else None
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, dtype=torch.float32)
+
+    def rand(*shape):
+        return torch.rand(*shape, generator=gen, dtype=torch.float32)
+
+    x = randn(B, T, H, N)
+    dt = torch.exp(math.log(1e-3) + rand(B, T, H) * (math.log(1e-1) - math.log(1e-3)))
+    A = -(1.0 + 15.0 * rand(H))
+    Bm = randn(B, T, G, N) / N ** 0.25
+    Cm = randn(B, T, G, N) / N ** 0.25
+    dy = randn(B, T, H, N)
+    h0 = randn(B, H, N, N) * 0.1 if with_initial_state else None
+    dtp = spec.dtype if dtype is None else dtype
+    return SsdWorkload(name=name, B=B, T=T, H=H, G=G, N=N, dtype=dtp, num_shards=P,
+                       x=x.to(dtp).contiguous(), dt=dt.contiguous(), A=A.contiguous(),
+                       Bm=Bm.to(dtp).contiguous(), Cm=Cm.to(dtp).contiguous(), dy=dy.to(dtp).contiguous(),
+                       initial_state=None if h0 is None else h0.contiguous(), cu_seqlens=cu)
