@@ -158,6 +158,144 @@ def cpu_baseline(wl, rows_req):
             "cpu_seconds": round(sum(per), 2)}
 
 
+# ---- Mamba2 (SSD) workload ----------------------------------------------------------------
+
+def _ssd_oracle_row(args):
+    h, b = args
+    from threadpoolctl import threadpool_limits
+    from oracle import ssd as ossd
+    wl = _WL
+    gr = h // (wl.H // wl.G)
+    sl = lambda x, i: x[b:b + 1, :, i:i + 1].double().numpy()  # noqa: E731
+    with threadpool_limits(1):
+        t = time.perf_counter()
+        x, dt, B, C, dy = sl(wl.x, h), sl(wl.dt, h), sl(wl.Bm, gr), sl(wl.Cm, gr), sl(wl.dy, h)
+        A = wl.A[h:h + 1].double().numpy()
+        ossd.ssd_forward(x, dt, A, B, C)
+        ossd.ssd_backward(x, dt, A, B, C, dy)
+        return time.perf_counter() - t
+
+
+def ssd_cpu_baseline(wl, rows_req):
+    global _WL
+    import multiprocessing as mp
+    _WL = wl
+    avail = len(os.sched_getaffinity(0))
+    rows = rows_req or min(16, avail)
+    workers = min(rows, avail, 16)
+    pairs = [(r % wl.H, (r // wl.H) % wl.B) for r in range(rows)]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        per = pool.map(_ssd_oracle_row, pairs)
+    wall = time.perf_counter() - t0
+    return {"value": rows * wl.T / wl.H / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"fp64 Mamba2 SSD oracle (per-token recurrence and adjoint) fwd+bwd on {rows} of the "
+                      f"{wl.B * wl.H} (b,h) rows at full T={wl.T}; {workers} single-threaded processes, "
+                      f"wall {wall:.1f}s, {sum(per):.1f} CPU-s; value = row-tokens/s / H",
+            "cpu_seconds": round(sum(per), 2)}
+
+
+def main_ssd(args, rank):
+    """One step = cpla_ssd_inputs, the weighted CP forward (prepare, apply), the CP
+    backward (prepare, weighted apply with fp32 gradients), cpla_ssd_input_grads."""
+    import torch
+    import workloads
+    wl = workloads.make_ssd(args.workload)
+    cpu = None
+    if rank == 0 and not args.no_cpu_baseline:
+        cpu = ssd_cpu_baseline(wl, args.cpu_rows)
+    from context_state_passing_amd import _lib
+    from context_state_passing_amd._lib import SsdProblem
+    from context_state_passing_amd.api import _ptr, make_problem
+
+    dev = torch.device("cuda:0")
+    x, dt, A, Bm, Cm, dy = (t.to(dev) for t in (wl.x, wl.dt, wl.A, wl.Bm, wl.Cm, wl.dy))
+    B, T, H, G, N, P = wl.B, wl.T, wl.H, wl.G, wl.N, wl.num_shards
+    sp_ = SsdProblem(B, T, H, G, N, _lib.BF16 if wl.dtype == torch.bfloat16 else _lib.F32)
+    q = torch.empty_like(x)
+    k = torch.empty_like(x)
+    g = torch.empty_like(dt)
+    p = make_problem(q, x, P, _lib.DECAY_SCALAR)
+    L = _lib.lib()
+    W = L.cpla_summary_width(ctypes.byref(p))
+    f32 = dict(device=dev, dtype=torch.float32)
+    fsum, bsum = torch.empty((P, B, H, W), **f32), torch.empty((P, B, H, W), **f32)
+    s_in, s_out = torch.empty((P, B, H, N, N), **f32), torch.empty((P, B, H, N, N), **f32)
+    fin = torch.empty((B, H, N, N), **f32)
+    cs = torch.empty((B, H, T // 64, N, N), **f32)
+    y = torch.empty_like(x)
+    dq, dk, dv = (torch.empty((B, T, H, N), **f32) for _ in range(3))
+    dg, dw, ddt = torch.empty_like(dt), torch.empty_like(dt), torch.empty_like(dt)
+    dA = torch.empty_like(A)
+    dx = torch.empty_like(x)
+    dB, dC = torch.empty_like(Bm), torch.empty_like(Cm)
+    stream = torch.cuda.current_stream()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    pp, sp = ctypes.byref(p), ctypes.byref(sp_)
+    chk = _lib.check
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        chk(L.cpla_ssd_inputs(sp, _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(q), _ptr(k), _ptr(g), st))
+        if ev: ev[1].record(stream)
+        chk(L.cp_forward_prepare_weighted(pp, None, _ptr(k), _ptr(x), _ptr(g), _ptr(dt), _ptr(fsum), st))
+        if ev: ev[2].record(stream)
+        chk(L.cp_forward_apply_weighted(pp, None, _ptr(q), _ptr(k), _ptr(x), _ptr(g), _ptr(dt), _ptr(fsum), None,
+                                        _ptr(y), _ptr(s_in), _ptr(fin), _ptr(cs), st))
+        if ev: ev[3].record(stream)
+        chk(L.cp_backward_prepare(pp, None, _ptr(q), _ptr(g), _ptr(dy), _ptr(bsum), st))
+        if ev: ev[4].record(stream)
+        chk(L.cp_backward_apply_weighted(pp, None, _ptr(q), _ptr(k), _ptr(x), _ptr(g), _ptr(dt), _ptr(dy),
+                                         _ptr(cs), _ptr(bsum), None, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg),
+                                         _ptr(dw), _ptr(s_out), None, _lib.F32, st))
+        if ev: ev[5].record(stream)
+        chk(L.cpla_ssd_input_grads(sp, _ptr(dt), _ptr(A), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dw),
+                                   _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB), _ptr(dC), st))
+        if ev: ev[6].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    parts = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(6)]
+    names = ["cpla_ssd_inputs", "cp_forward_prepare_weighted", "cp_forward_apply_weighted", "cp_backward_prepare",
+             "cp_backward_apply_weighted", "cpla_ssd_input_grads"]
+    tokens = B * T
+    th = tokens * H
+    e = 2 if wl.dtype == torch.bfloat16 else 4
+    # dominant kernel: the weighted backward apply (q, k, v, dO, g, w in; fp32 dq, dk, dv and dg, dw out)
+    dom_bytes = (4 * N * e + 8 + 3 * N * 4 + 8) * th
+    dom_ms = parts[4]
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    # the SSD's own minimum per token-head: x, dy, dt in and dx, d_dt out, y out; B, C, dB, dC per group
+    step_bytes = (4 * N * e + 8 + 4 * N * e * G / H) * th
+    out = {
+        "metric": f"fwd+bwd tokens/s, Mamba2 SSD {wl.name} (B{B} H{H} G{G} T{T} N=P={N})",
+        "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16" if e == 2 else "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "G": G, "N": N, "chunk": 64, "shards": P,
+                   "decay": "scalar (A dt) with input weight dt",
+                   "parallelism": "single-gpu (shards simulated in HBM)"},
+        "roofline": {"bound": "hbm", "kernel": "bwd_walk<scalar, fp32 grads> (cp_backward_apply_weighted)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": None, "traffic_note": "counters are taken for the default workload",
+                     "algorithmic_bytes_per_launch": dom_bytes, "launch_ms": dom_ms},
+        "step_breakdown_ms": dict(zip(names, parts)),
+        "step_roofline": {"algorithmic_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
+                          "hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 # ---- GPU run --------------------------------------------------------------------------------
 
 def main():
@@ -172,6 +310,9 @@ def main():
     rank = int(os.environ.get("RANK", "0"))
     import torch
     import workloads
+    if args.workload in workloads.SSD_SPECS:
+        main_ssd(args, rank)
+        return
     wl = workloads.make(args.workload)
     cpu = None
     if rank == 0 and not args.no_cpu_baseline:

@@ -110,15 +110,24 @@ __global__ __launch_bounds__(256) void ssd_grads(SsdArgs a) {
 }
 
 // One workgroup per head: dA_h = sum over (b, t) of dt * dg in a fixed order
-// (strided partial sums, then a tree), so the result is the same on every run.
-__global__ __launch_bounds__(256) void ssd_dA(SsdArgs a) {
-  __shared__ float red[256];
+// (four strided partial sums per thread, so their loads are in flight together,
+// then a tree), so the result is the same on every run.
+constexpr int DA_THREADS = 1024;
+__global__ __launch_bounds__(DA_THREADS) void ssd_dA(SsdArgs a) {
+  __shared__ float red[DA_THREADS];
   const int64_t h = blockIdx.x, n = a.B * a.T;
-  float s = 0.f;
-  for (int64_t bt = threadIdx.x; bt < n; bt += 256) s += a.dt[bt * a.H + h] * a.dg[bt * a.H + h];
-  red[threadIdx.x] = s;
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f;
+  int64_t bt = threadIdx.x;
+  for (; bt + 3 * DA_THREADS < n; bt += 4 * DA_THREADS) {
+    s0 += a.dt[bt * a.H + h] * a.dg[bt * a.H + h];
+    s1 += a.dt[(bt + DA_THREADS) * a.H + h] * a.dg[(bt + DA_THREADS) * a.H + h];
+    s2 += a.dt[(bt + 2 * DA_THREADS) * a.H + h] * a.dg[(bt + 2 * DA_THREADS) * a.H + h];
+    s3 += a.dt[(bt + 3 * DA_THREADS) * a.H + h] * a.dg[(bt + 3 * DA_THREADS) * a.H + h];
+  }
+  for (; bt < n; bt += DA_THREADS) s0 += a.dt[bt * a.H + h] * a.dg[bt * a.H + h];
+  red[threadIdx.x] = (s0 + s1) + (s2 + s3);
   __syncthreads();
-  for (int w = 128; w >= 1; w >>= 1) {
+  for (int w = DA_THREADS / 2; w >= 1; w >>= 1) {
     if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
@@ -188,7 +197,7 @@ extern "C" cpla_status cpla_ssd_input_grads(const cpla_ssd_problem* p, const flo
   const unsigned nb = blocks_for(p->B * p->T * p->G * (p->N / 4));
   if (p->dtype == CPLA_BF16) hipLaunchKernelGGL(ssd_grads<bf16_t>, dim3(nb), dim3(256), 0, stream, a);
   else hipLaunchKernelGGL(ssd_grads<float>, dim3(nb), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(ssd_dA, dim3((unsigned)p->H), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(ssd_dA, dim3((unsigned)p->H), dim3(DA_THREADS), 0, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(CPLA_E_HIP, "ssd gradient launch: %s", hipGetErrorString(e));
   return CPLA_OK;
