@@ -21,7 +21,10 @@ token included) forgets its incoming state, so its M is exactly 0; with packed
 sequences rank r composes from zero over ranks [preceding_rank_start, r) and
 the suffix from zero over (r, following_rank_stop); without packing the prefix
 starts at rank 0 from S_init and the suffix ends at the last rank from
-dS_final.
+dS_final. Shards follow torch.chunk: ceil(T / P) tokens each, the last
+non-empty one shorter when P does not divide T, and trailing shards empty when
+the stream is too short (the graceful division the mixle page relies on, in
+place of failing fast); an empty shard's map is the identity.
 """
 from __future__ import annotations
 
@@ -35,35 +38,38 @@ def _np(x):
     return rec._np(x)
 
 
-def shard_len(T, P):
-    if P <= 0 or T % P != 0:
-        raise ValueError("T must be a multiple of the number of shards")
-    return T // P
+def shard_bounds(T, P):
+    """[start, end) of every shard: torch.chunk's split of T tokens into P parts."""
+    if P <= 0 or T <= 0:
+        raise ValueError("T and the number of shards must be positive")
+    s = -(-T // P)
+    return [(min(r * s, T), min((r + 1) * s, T)) for r in range(P)]
 
 
-def _local_resets(global_starts, r, L):
-    return global_starts[r * L:(r + 1) * L].copy()
+def _local_resets(global_starts, bounds):
+    a, e = bounds
+    return global_starts[a:e].copy()
 
 
 def transitions(g, decay, B, T, H, dk, P, global_starts):
     """M_r for every shard: [P, B, H, m] with m = dk (diag) or 1."""
-    L = shard_len(T, P)
     m = dk if decay == "diag" else 1
     out = np.zeros((P, B, H, m))
-    for r in range(P):
-        if global_starts[r * L:(r + 1) * L].any():
+    for r, (a, e) in enumerate(shard_bounds(T, P)):
+        if global_starts[a:e].any():
             continue  # forgets its incoming state: M = 0
         if decay == "none":
             out[r] = 1.0
         elif decay == "scalar":
-            out[r, :, :, 0] = np.exp(_np(g)[:, r * L:(r + 1) * L, :].sum(axis=1))
+            out[r, :, :, 0] = np.exp(_np(g)[:, a:e, :].sum(axis=1))
         else:
-            out[r] = np.exp(_np(g)[:, r * L:(r + 1) * L, :, :].sum(axis=1))
+            out[r] = np.exp(_np(g)[:, a:e, :, :].sum(axis=1))
     return out
 
 
-def _shard(x, r, L):
-    return None if x is None else _np(x)[:, r * L:(r + 1) * L]
+def _shard(x, bounds):
+    a, e = bounds
+    return None if x is None else _np(x)[:, a:e]
 
 
 def forward_summaries(k, v, g, decay, P, seq_idx=None):
@@ -71,13 +77,12 @@ def forward_summaries(k, v, g, decay, P, seq_idx=None):
     k, v = _np(k), _np(v)
     B, T, H, dk = k.shape
     dv = v.shape[3]
-    L = shard_len(T, P)
     starts = rec.starts_from_seq_idx(seq_idx, T)
     dS = np.zeros((P, B, H, dk, dv))
-    for r in range(P):
-        zq = np.zeros((B, L, H, dk))
-        _, fin = rec.forward(zq, _shard(k, r, L), _shard(v, r, L), _shard(g, r, L), decay,
-                             resets=_local_resets(starts, r, L))
+    for r, bd in enumerate(shard_bounds(T, P)):
+        zq = np.zeros((B, bd[1] - bd[0], H, dk))
+        _, fin = rec.forward(zq, _shard(k, bd), _shard(v, bd), _shard(g, bd), decay,
+                             resets=_local_resets(starts, bd))
         dS[r] = fin
     return transitions(g, decay, B, T, H, dk, P, starts), dS
 
@@ -86,14 +91,14 @@ def backward_summaries(q, dO, g, decay, P, dv, seq_idx=None):
     """(M [P,B,H,m], gamma [P,B,H,dk,dv]) — each shard's adjoint with zero outgoing gradient."""
     q, dO = _np(q), _np(dO)
     B, T, H, dk = q.shape
-    L = shard_len(T, P)
     starts = rec.starts_from_seq_idx(seq_idx, T)
     gam = np.zeros((P, B, H, dk, dv))
-    for r in range(P):
+    for r, bd in enumerate(shard_bounds(T, P)):
+        L = bd[1] - bd[0]
         z = np.zeros((B, L, H, dk))
         zv = np.zeros((B, L, H, dv))
-        *_, dS0 = rec.backward(_shard(q, r, L), z, zv, _shard(g, r, L), decay, _shard(dO, r, L),
-                               resets=_local_resets(starts, r, L))
+        *_, dS0 = rec.backward(_shard(q, bd), z, zv, _shard(g, bd), decay, _shard(dO, bd),
+                               resets=_local_resets(starts, bd))
         gam[r] = dS0
     return transitions(g, decay, B, T, H, dk, P, starts), gam
 
@@ -147,16 +152,15 @@ def cp_forward(q, k, v, g, decay, P, initial_state=None, seq_idx=None):
     final state, and the intermediates (M, delta_S, S_in)."""
     q, k, v = _np(q), _np(k), _np(v)
     B, T, H, dk = q.shape
-    L = shard_len(T, P)
     starts = rec.starts_from_seq_idx(seq_idx, T)
     M, dS = forward_summaries(k, v, g, decay, P, seq_idx)
     prs, _ = slices(P, seq_idx)
     S_in, final = compose_prefix(M, dS, initial_state, prs)
     o = np.zeros((B, T, H, v.shape[3]))
-    for r in range(P):
-        o_r, _ = rec.forward(_shard(q, r, L), _shard(k, r, L), _shard(v, r, L), _shard(g, r, L), decay,
-                             initial_state=S_in[r], resets=_local_resets(starts, r, L))
-        o[:, r * L:(r + 1) * L] = o_r
+    for r, bd in enumerate(shard_bounds(T, P)):
+        o_r, _ = rec.forward(_shard(q, bd), _shard(k, bd), _shard(v, bd), _shard(g, bd), decay,
+                             initial_state=S_in[r], resets=_local_resets(starts, bd))
+        o[:, bd[0]:bd[1]] = o_r
     return {"o": o, "final_state": final, "M": M, "delta_S": dS, "S_in": S_in}
 
 
@@ -166,7 +170,6 @@ def cp_backward(q, k, v, g, decay, dO, P, initial_state=None, seq_idx=None, d_fi
     q, k, v, dO = _np(q), _np(k), _np(v), _np(dO)
     B, T, H, dk = q.shape
     dv = v.shape[3]
-    L = shard_len(T, P)
     starts = rec.starts_from_seq_idx(seq_idx, T)
     M, gam = backward_summaries(q, dO, g, decay, P, dv, seq_idx)
     _, frs = slices(P, seq_idx)
@@ -175,15 +178,15 @@ def cp_backward(q, k, v, g, decay, dO, P, initial_state=None, seq_idx=None, d_fi
     dk_ = np.zeros_like(k)
     dv_ = np.zeros_like(v)
     dg = None if g is None else np.zeros_like(_np(g))
-    for r in range(P):
-        a, b, c, e, _ = rec.backward(_shard(q, r, L), _shard(k, r, L), _shard(v, r, L), _shard(g, r, L), decay,
-                                     _shard(dO, r, L), initial_state=fw["S_in"][r], d_final_state=dS_out[r],
-                                     resets=_local_resets(starts, r, L))
-        dq[:, r * L:(r + 1) * L] = a
-        dk_[:, r * L:(r + 1) * L] = b
-        dv_[:, r * L:(r + 1) * L] = c
+    for r, bd in enumerate(shard_bounds(T, P)):
+        a, b, c, e, _ = rec.backward(_shard(q, bd), _shard(k, bd), _shard(v, bd), _shard(g, bd), decay,
+                                     _shard(dO, bd), initial_state=fw["S_in"][r], d_final_state=dS_out[r],
+                                     resets=_local_resets(starts, bd))
+        dq[:, bd[0]:bd[1]] = a
+        dk_[:, bd[0]:bd[1]] = b
+        dv_[:, bd[0]:bd[1]] = c
         if dg is not None:
-            dg[:, r * L:(r + 1) * L] = e
+            dg[:, bd[0]:bd[1]] = e
     if seq_idx is not None:
         d_init = None
     return {"dq": dq, "dk": dk_, "dv": dv_, "dg": dg, "d_initial_state": d_init,

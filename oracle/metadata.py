@@ -12,8 +12,12 @@ fields are:
 * ``following_rank_stop``   exclusive end of the ranks whose backward summaries
   rank r composes (the suffix runs over ranks (r, stop)).
 
-Readings where the page is silent: shards are the cp_size equal contiguous
-slices of the stream (fail fast if it does not divide); local ids are rebased so
+Readings where the page is silent: shards are the cp_size contiguous slices of
+the stream that torch.chunk makes (ceil(T / cp_size) tokens each, the last
+non-empty one shorter, trailing ones empty when the stream is short — the
+graceful division the mixle page relies on); an empty shard has no local
+tokens, local_cu_seqlens [0, 0], and composes nothing (prefix start r, suffix
+stop r + 1); local ids are rebased so
 the shard's first token has id 0; local_cu_seqlens lists 0, every interior
 position where the id changes, and the shard length; the prefix starts at the
 rank holding the first token of the sequence that is live at the shard's first
@@ -47,8 +51,8 @@ def seq_idx_from_cu_seqlens(cu_seqlens, T):
 def validate_global_seq_idx(global_seq_idx, cp_size):
     s = [int(x) for x in np.asarray(global_seq_idx).tolist()]
     T = len(s)
-    if cp_size <= 0 or T == 0 or T % cp_size != 0:
-        raise MetadataError("stream length must be a positive multiple of cp_size")
+    if cp_size <= 0 or T == 0:
+        raise MetadataError("stream length and cp_size must be positive")
     if s[0] != 0:
         raise MetadataError("global_seq_idx must start at 0")
     for t in range(1, T):
@@ -62,8 +66,12 @@ def build_packed_sequence_cp_metadata(global_seq_idx, cp_rank, cp_size):
     if not 0 <= cp_rank < cp_size:
         raise MetadataError("cp_rank out of range")
     T = len(s)
-    L = T // cp_size
-    a = cp_rank * L
+    size = -(-T // cp_size)                  # torch.chunk's part size
+    a = min(cp_rank * size, T)
+    L = min(size, T - a)
+    if L == 0:
+        return {"local_seq_idx": np.zeros(0, dtype=np.int32), "local_cu_seqlens": np.zeros(2, dtype=np.int32),
+                "preceding_rank_start": cp_rank, "following_rank_stop": cp_rank + 1}
     e = a + L - 1
     local = [s[t] - s[a] for t in range(a, a + L)]
     cu = [0]
@@ -76,8 +84,8 @@ def build_packed_sequence_cp_metadata(global_seq_idx, cp_rank, cp_size):
     return {
         "local_seq_idx": np.array(local, dtype=np.int32),
         "local_cu_seqlens": np.array(cu, dtype=np.int32),
-        "preceding_rank_start": first_of // L,
-        "following_rank_stop": last_of // L + 1,
+        "preceding_rank_start": first_of // size,
+        "following_rank_stop": last_of // size + 1,
     }
 
 

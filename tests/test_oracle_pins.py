@@ -164,8 +164,11 @@ def test_adjoint_identity_and_starts():
 # --- sharded == unsharded ---------------------------------------------------
 
 @pytest.mark.parametrize("decay", ["none", "scalar", "diag"])
-@pytest.mark.parametrize("P", [1, 2, 4, 8])
+@pytest.mark.parametrize("P", [1, 2, 4, 8, 3, 5, 7, 40])
 def test_sharded_equals_unsharded(decay, P):
+    # P = 3, 5, 7: torch.chunk's uneven split of 32 tokens (the last shard shorter,
+    # or empty: 7 parts of ceil(32/7) = 5 leave the seventh with 2); P = 40: shards
+    # of one token and eight empty ones
     rng = np.random.default_rng(10 + P)
     B, T, H, dk, dv = 2, 32, 2, 3, 4
     q, k, v, g, S0 = _rand(rng, B, T, H, dk, dv, decay, init=True, gscale=0.1)
@@ -188,8 +191,7 @@ def test_sharded_packed_equals_whole_stream(lengths):
     rng = np.random.default_rng(5)
     seq, cu = _packed_seq_idx(lengths)
     T = int(cu[-1])
-    P = 5 if T % 5 == 0 else 4
-    for decay in ["none", "scalar", "diag"]:
+    for decay, P in [("none", 5 if T % 5 == 0 else 4), ("scalar", 3), ("diag", 7)]:
         q, k, v, g, _ = _rand(rng, 1, T, 2, 3, 2, decay, gscale=0.1)
         dO = rng.standard_normal((1, T, 2, 2))
         o, fin = oracle.forward(q, k, v, g, decay, seq_idx=seq)
@@ -206,10 +208,11 @@ def test_sharded_packed_equals_whole_stream(lengths):
         # start) gives the same incoming states as the sliced prefixes, except at ranks
         # that begin with a start: their incoming state is never read (the slice gives 0)
         S_in_all, _ = cp.compose_prefix(f["M"], f["delta_S"], None, None)
-        L = T // P
         starts = rec.starts_from_seq_idx(seq, T)
-        for r in range(P):
-            if starts[r * L]:
+        for r, (a, e) in enumerate(cp.shard_bounds(T, P)):
+            if a == e:
+                continue                                    # empty shard: nothing reads its state
+            if starts[a]:
                 assert np.all(f["S_in"][r] == 0.0)
             else:
                 np.testing.assert_allclose(S_in_all[r], f["S_in"][r], atol=1e-12)
@@ -278,9 +281,26 @@ def test_metadata_edge_cases():
     seq = np.repeat(np.arange(4), 8).astype(np.int32)
     prs, frs = metadata.rank_slices(seq, 4)
     assert prs.tolist() == [0, 1, 2, 3] and frs.tolist() == [1, 2, 3, 4]
+    # uneven division (torch.chunk): 3 tokens on 2 ranks are [0, 2) and [2, 3)
+    m = metadata.build_packed_sequence_cp_metadata(np.array([0, 0, 0]), 1, 2)
+    assert m["local_seq_idx"].tolist() == [0] and m["local_cu_seqlens"].tolist() == [0, 1]
+    assert m["preceding_rank_start"] == 0 and m["following_rank_stop"] == 2
+    # 5 tokens on 8 ranks: ranks 5..7 are empty and compose nothing
+    seq = np.array([0, 0, 1, 1, 1], dtype=np.int32)
+    prs, frs = metadata.rank_slices(seq, 8)
+    assert prs.tolist() == [0, 0, 2, 2, 2, 5, 6, 7] and frs.tolist() == [2, 2, 5, 5, 5, 6, 7, 8]
     # malformed inputs fail
-    for bad in [np.array([1, 1, 1, 1]), np.array([0, 2, 2, 2]), np.array([0, 1, 0, 1]), np.array([0, 0, 0])]:
+    for bad in [np.array([1, 1, 1, 1]), np.array([0, 2, 2, 2]), np.array([0, 1, 0, 1])]:
         with pytest.raises(metadata.MetadataError):
             metadata.build_packed_sequence_cp_metadata(bad, 0, 2)
     with pytest.raises(metadata.MetadataError):
         metadata.seq_idx_from_cu_seqlens([0, 3, 3, 5], 5)
+
+
+def test_shard_bounds_follow_torch_chunk():
+    import torch
+    for T in [1, 5, 9, 10, 32, 100, 4097]:
+        for P in [1, 2, 3, 4, 7, 8, 40]:
+            want = [len(c) for c in torch.arange(T).chunk(P)]
+            got = [e - a for a, e in cp.shard_bounds(T, P)]
+            assert got[:len(want)] == want and all(n == 0 for n in got[len(want):]), (T, P)
