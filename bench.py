@@ -222,7 +222,7 @@ def main_ssd(args, rank):
     fsum, bsum = torch.empty((P, B, H, W), **f32), torch.empty((P, B, H, W), **f32)
     s_in, s_out = torch.empty((P, B, H, N, N), **f32), torch.empty((P, B, H, N, N), **f32)
     fin = torch.empty((B, H, N, N), **f32)
-    cs = torch.empty((B, H, T // 64, N, N), **f32)
+    cs = torch.empty((L.cpla_chunk_states_bytes(ctypes.byref(p)) // 4,), **f32)
     y = torch.empty_like(x)
     dq, dk, dv = (torch.empty((B, T, H, N), **f32) for _ in range(3))
     dg, dw, ddt = torch.empty_like(dt), torch.empty_like(dt), torch.empty_like(dt)
@@ -339,7 +339,7 @@ def main():
     s_out = torch.empty((P, B, H, d, d), **f32)
     fin = torch.empty((B, H, d, d), **f32)
     dS0 = torch.empty((B, H, d, d), **f32) if wl.cu_seqlens is None else None
-    cs = torch.empty((B, H, T // 64, d, d), **f32)
+    cs = torch.empty((L.cpla_chunk_states_bytes(ctypes.byref(p)) // 4,), **f32)
     o = torch.empty_like(v)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     dg = None if g is None else torch.empty_like(g)

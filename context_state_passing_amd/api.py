@@ -37,6 +37,15 @@ def _i32p(a: np.ndarray):
 
 # ---- packed-sequence metadata (host, in the library) --------------------------------
 
+def shard_len(T: int, P: int, r: int) -> int:
+    """Tokens of shard r when T tokens are divided among P shards the way
+    torch.chunk divides them (the library's division; see include/cpla.h)."""
+    if P <= 0 or T <= 0 or not 0 <= r < P:
+        return 0
+    size = -(-T // P)
+    return max(0, min(size, T - r * size))
+
+
 def seq_idx_from_cu_seqlens(cu_seqlens, T: int) -> np.ndarray:
     cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32))
     out = np.empty(T, dtype=np.int32)
@@ -54,7 +63,7 @@ def packed_rank_slices(global_seq_idx: np.ndarray, cp_size: int):
 
 def build_packed_sequence_cp_metadata(global_seq_idx, cp_rank: int, cp_size: int) -> dict:
     s = np.ascontiguousarray(np.asarray(global_seq_idx), dtype=np.int32)
-    L = len(s) // cp_size if cp_size > 0 else 0
+    L = shard_len(len(s), cp_size, cp_rank)
     local = np.empty(max(L, 1), dtype=np.int32)
     cu = np.empty(max(L, 1) + 1, dtype=np.int32)
     n = ctypes.c_int32()
@@ -147,7 +156,8 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
     fin = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
     cs = None
     if save_for_backward:
-        cs = torch.empty((B, H, T // chunk, dk, dv), device=dev, dtype=torch.float32)
+        n_chunks = L.cpla_chunk_states_bytes(ctypes.byref(p)) // (B * H * dk * dv * 4)
+        cs = torch.empty((B, H, n_chunks, dk, dv), device=dev, dtype=torch.float32)
     o = torch.empty(v.shape, device=dev, dtype=q.dtype) if out is None else out
     pk = ctypes.byref(packed.c()) if packed is not None else None
     st = _stream()

@@ -15,6 +15,7 @@
 #include "cpla.h"
 #include "errors.hpp"
 #include "kernels.hpp"
+#include "shards.hpp"
 
 namespace cpla {
 
@@ -37,11 +38,7 @@ cpla_status check_problem(const cpla_problem* p) {
   if (p->decay < CPLA_DECAY_NONE || p->decay > CPLA_DECAY_DIAG) return fail(CPLA_E_INVALID, "unknown decay %d", p->decay);
   if (p->chunk != 64) return fail(CPLA_E_UNSUPPORTED, "chunk %d unsupported (64 only)", p->chunk);
   if (p->num_shards <= 0) return fail(CPLA_E_SHAPE, "num_shards must be positive");
-  if (p->T % p->num_shards != 0)
-    return fail(CPLA_E_SHAPE, "T=%lld is not divisible by num_shards=%d", (long long)p->T, p->num_shards);
-  if ((p->T / p->num_shards) % p->chunk != 0)
-    return fail(CPLA_E_SHAPE, "shard length %lld is not a multiple of chunk %d", (long long)(p->T / p->num_shards),
-                p->chunk);
+  // any T and num_shards: torch.chunk's division (shards.hpp), partial last chunks
   if (p->num_shards > 64) return fail(CPLA_E_UNSUPPORTED, "num_shards=%d > 64 unsupported", p->num_shards);
   if (p->rank_begin < 0 || p->rank_end > p->num_shards || p->rank_begin >= p->rank_end)
     return fail(CPLA_E_INVALID, "rank range [%d, %d) outside [0, %d)", p->rank_begin, p->rank_end, p->num_shards);
@@ -88,13 +85,20 @@ cpla_status launched(const char* what) {
 typedef void (*fwd_fn)(FwdArgs);
 typedef void (*bwd_fn)(BwdArgs);
 
-template <bool APPLY>
-fwd_fn pick_fwd(int dtype, int D, int decay) {
+// some shard's length is not a multiple of the 64-token chunk
+bool needs_tail(const cpla_problem* p) {
+  for (int r = 0; r < p->num_shards; ++r)
+    if (shard_len(p->T, p->num_shards, r) % 64 != 0) return true;
+  return false;
+}
+
+template <bool APPLY, bool TAIL>
+fwd_fn pick_fwd_t(int dtype, int D, int decay) {
 #define CPLA_FWD_CASE(E, DD)                                              \
   if (D == DD) {                                                          \
-    if (decay == 0) return fwd_walk<E, DD, DD, 0, APPLY>;                 \
-    if (decay == 1) return fwd_walk<E, DD, DD, 1, APPLY>;                 \
-    return fwd_walk<E, DD, DD, 2, APPLY>;                                 \
+    if (decay == 0) return fwd_walk<E, DD, DD, 0, APPLY, TAIL>;           \
+    if (decay == 1) return fwd_walk<E, DD, DD, 1, APPLY, TAIL>;           \
+    return fwd_walk<E, DD, DD, 2, APPLY, TAIL>;                           \
   }
   if (dtype == CPLA_BF16) {
     CPLA_FWD_CASE(bf16_t, 16)
@@ -108,20 +112,20 @@ fwd_fn pick_fwd(int dtype, int D, int decay) {
   return nullptr;
 }
 
-template <bool APPLY>
-bwd_fn pick_bwd(int dtype, int D, int decay, bool grad_f32 = false) {
+template <bool APPLY, bool TAIL>
+bwd_fn pick_bwd_t(int dtype, int D, int decay, bool grad_f32) {
   if (grad_f32) {   // fp32 gradients from bf16 inputs: scalar decay only
     if (!APPLY || dtype != CPLA_BF16 || decay != CPLA_DECAY_SCALAR) return nullptr;
-    if (D == 16) return bwd_walk<bf16_t, 16, 16, 1, true, true>;
-    if (D == 64) return bwd_walk<bf16_t, 64, 64, 1, true, true>;
-    if (D == 128) return bwd_walk<bf16_t, 128, 128, 1, true, true>;
+    if (D == 16) return bwd_walk<bf16_t, 16, 16, 1, true, true, TAIL>;
+    if (D == 64) return bwd_walk<bf16_t, 64, 64, 1, true, true, TAIL>;
+    if (D == 128) return bwd_walk<bf16_t, 128, 128, 1, true, true, TAIL>;
     return nullptr;
   }
 #define CPLA_BWD_CASE(E, DD)                                              \
   if (D == DD) {                                                          \
-    if (decay == 0) return bwd_walk<E, DD, DD, 0, APPLY, false>;          \
-    if (decay == 1) return bwd_walk<E, DD, DD, 1, APPLY, false>;          \
-    return bwd_walk<E, DD, DD, 2, APPLY, false>;                          \
+    if (decay == 0) return bwd_walk<E, DD, DD, 0, APPLY, false, TAIL>;    \
+    if (decay == 1) return bwd_walk<E, DD, DD, 1, APPLY, false, TAIL>;    \
+    return bwd_walk<E, DD, DD, 2, APPLY, false, TAIL>;                    \
   }
   if (dtype == CPLA_BF16) {
     CPLA_BWD_CASE(bf16_t, 16)
@@ -133,6 +137,18 @@ bwd_fn pick_bwd(int dtype, int D, int decay, bool grad_f32 = false) {
   }
 #undef CPLA_BWD_CASE
   return nullptr;
+}
+
+// the kernel for a problem: the TAIL variant only when some shard ends inside a chunk
+template <bool APPLY>
+fwd_fn pick_fwd(const cpla_problem* p) {
+  return needs_tail(p) ? pick_fwd_t<APPLY, true>(p->dtype, (int)p->dk, p->decay)
+                       : pick_fwd_t<APPLY, false>(p->dtype, (int)p->dk, p->decay);
+}
+template <bool APPLY>
+bwd_fn pick_bwd(const cpla_problem* p, bool grad_f32 = false) {
+  return needs_tail(p) ? pick_bwd_t<APPLY, true>(p->dtype, (int)p->dk, p->decay, grad_f32)
+                       : pick_bwd_t<APPLY, false>(p->dtype, (int)p->dk, p->decay, grad_f32);
 }
 
 unsigned threads_for(const cpla_problem* p) {
@@ -176,8 +192,8 @@ extern "C" int64_t cpla_summary_width(const cpla_problem* p) {
 }
 
 extern "C" int64_t cpla_chunk_states_bytes(const cpla_problem* p) {
-  if (!p || p->chunk <= 0) return -1;
-  return p->B * p->H * (p->T / p->chunk) * p->dk * p->dv * (int64_t)sizeof(float);
+  if (!p || p->chunk != 64 || p->T <= 0 || p->num_shards <= 0) return -1;
+  return p->B * p->H * row_chunks(p->T, p->num_shards) * p->dk * p->dv * (int64_t)sizeof(float);
 }
 
 namespace cpla {
@@ -210,7 +226,7 @@ static cpla_status forward_prepare(const cpla_problem* p, const cpla_packed* pac
   a.k = k; a.v = v; a.g = g; a.w = w;
   a.seq_idx = packed ? packed->seq_idx : nullptr;
   a.summary = fwd_summary;
-  fwd_fn fn = pick_fwd<false>(p->dtype, (int)p->dk, p->decay);
+  fwd_fn fn = pick_fwd<false>(p);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no forward kernel for this configuration");
   hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(threads_for(p)), 0, stream, a);
   return launched("cp_forward_prepare");
@@ -258,7 +274,7 @@ static cpla_status forward_apply(const cpla_problem* p, const cpla_packed* packe
   a.state_in = shard_in_state;
   a.out = o;
   a.chunk_states = reinterpret_cast<float*>(chunk_states);
-  fwd_fn fn = pick_fwd<true>(p->dtype, (int)p->dk, p->decay);
+  fwd_fn fn = pick_fwd<true>(p);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no forward kernel for this configuration");
   hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(threads_for(p)), 0, stream, a);
   return launched("cp_forward_apply");
@@ -297,7 +313,7 @@ extern "C" cpla_status cp_backward_prepare(const cpla_problem* p, const cpla_pac
   a.q = q; a.g = g; a.dO = dO;
   a.seq_idx = packed ? packed->seq_idx : nullptr;
   a.summary = bwd_summary;
-  bwd_fn fn = pick_bwd<false>(p->dtype, (int)p->dk, p->decay);
+  bwd_fn fn = pick_bwd<false>(p);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no backward kernel for this configuration");
   hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(threads_for(p)), 0, stream, a);
   return launched("cp_backward_prepare");
@@ -344,7 +360,7 @@ static cpla_status backward_apply(const cpla_problem* p, const cpla_packed* pack
   a.chunk_states = reinterpret_cast<const float*>(chunk_states);
   a.grad_in = shard_out_grad;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dw = dw;
-  bwd_fn fn = pick_bwd<true>(p->dtype, (int)p->dk, p->decay, grad_f32);
+  bwd_fn fn = pick_bwd<true>(p, grad_f32);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no backward kernel for this configuration");
   hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(threads_for(p)), 0, stream, a);
   return launched("cp_backward_apply");

@@ -71,7 +71,7 @@ __device__ __forceinline__ f32x4 lane_gamma(f32x4 x, f32x4& carry) {
   return out;
 }
 
-template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32>
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAIL>
 __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_walk(BwdArgs a) {
   using G = Geo<E, DK, DV>;
   // dq, dk, dv in the input dtype, or in fp32 (GF32: for callers that sum them
@@ -135,9 +135,12 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
   __builtin_assume(w >= 0 && w < G::NW);
   const int r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
-  const int64_t L = a.T / a.P, tshard = r * L;
-  const int nc = (int)(L / CH);
-  const int64_t nct = a.T / CH;
+  // the shard's tokens [tshard, tshard + slen): torch.chunk's division of T into P
+  const int64_t tshard = shard_begin(a.T, a.P, r), slen = shard_len(a.T, a.P, r);
+  const int nc = (int)chunks_of(slen);
+  const int64_t nct = row_chunks(a.T, a.P), cbase = shard_chunk_base(a.T, a.P, r);
+  // tokens of chunk c inside the shard (the last chunk may be partial)
+  auto valid = [&](int c) { return (int)(slen - (int64_t)c * CH < CH ? slen - (int64_t)c * CH : CH); };
 
   // dS: rows = all d_k tiles, columns = owned d_v tiles.  dT = dS^T: rows = all
   // d_v tiles, columns = owned d_k tiles (lane-fixed d).
@@ -184,27 +187,34 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
   float* const pf_g = reinterpret_cast<float*>(s_reg);
   E* const pf_do = s_kl;
   // raw inputs of the chunk starting at tn, by DMA into the regions above
-  auto prefetch = [&](int64_t tn, int tid) {
+  // raw inputs of the chunk starting at tn (n of its tokens inside the shard)
+  auto prefetch = [&](int64_t tn, int tid, int n, auto tail) {
+    constexpr bool TL = decltype(tail)::value;
     const int wv = wave_id();
-    GamR::dma(a.g, b, h, tn, a.T, a.H, pf_g, tid, wv);
-    TileK::dma(q, b, h, tn, a.T, a.H, s_pq, tid, wv);
-    TileK::dma(k, b, h, tn, a.T, a.H, s_k, tid, wv);
-    TileV::dma(v, b, h, tn, a.T, a.H, s_v, tid, wv);
-    TileV::dma(dO, b, h, tn, a.T, a.H, pf_do, tid, wv);
+    GamR::template dma<TL>(a.g, b, h, tn, a.T, a.H, pf_g, tid, wv, n);
+    TileK::template dma<TL>(q, b, h, tn, a.T, a.H, s_pq, tid, wv, n);
+    TileK::template dma<TL>(k, b, h, tn, a.T, a.H, s_k, tid, wv, n);
+    TileV::template dma<TL>(v, b, h, tn, a.T, a.H, s_v, tid, wv, n);
+    TileV::template dma<TL>(dO, b, h, tn, a.T, a.H, pf_do, tid, wv, n);
   };
   SegRegs nseg;   // sequence ids of the prefetched chunk
   // the lane's log-decays for dq/dk come from the DMA buffer (d_k 64 / 128: one
   // key tile per wave, 16-token parts) instead of a second read from HBM
   constexpr bool GL_LDS = PF && GamR::TOK == 16 && GamR::CPW == 16 && G::CPWK == 1 && G::NKT == G::NW;
   if constexpr (PF) {
-    const int tidf = tid_pick<APPLY, G::NT>();
-    const int64_t tn = tshard + (int64_t)(nc - 1) * CH;
-    prefetch(tn, tidf);
-    nseg.load(a.seq_idx, tn, tidf & 63);
+    if (nc > 0) {
+      const int tidf = tid_pick<APPLY, G::NT>();
+      const int64_t tn = tshard + (int64_t)(nc - 1) * CH;
+      const int n = TAIL ? valid(nc - 1) : CH;
+      prefetch(tn, tidf, n, std::integral_constant<bool, TAIL>{});
+      nseg.template load<TAIL>(a.seq_idx, tn, tidf & 63, n);
+    }
   }
 
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t t0 = tshard + (int64_t)c * CH;
+    const int nv = TAIL ? valid(c) : CH;
+    const bool full = !TAIL || nv >= CH;   // only a shard's last chunk is partial
     ChunkSeg seg;
     // Every global load of the chunk's inputs is issued before the first use, so
     // the chunk waits on memory once; the registers are free again once the tiles
@@ -219,28 +229,33 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
     // the dq/dk scaling, turned into Gam in the dq phase
     f32x4 gl[HAS_DG && DIAG ? G::CPWK : 1][4];
     if constexpr (PF) {
+      // this wave's DMA copies must have landed before it reads them back (each
+      // lane reads only bytes its own DMA lane wrote); the wait is explicit
+      // because the compiler's own tracking of LDS DMA does not cover every path
+      // into the loop
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       aseg = nseg;
       if constexpr (GL_LDS) {
         const int l = lane_pick<APPLY>();
 #pragma unroll
-        for (int I = 0; I < 4; ++I) gl[0][I] = GamR::lane_block(pf_g, w, I, l);
+        for (int I = 0; I < 4; ++I) gl[0][I] = GamR::template lane_block<TAIL>(pf_g, w, I, l, nv);
       }
-      agam.load_lds(pf_g, tidf);
-      aq.load_lds(s_pq, tidf);
-      ak.load_lds(s_k, tidf);
-      av_.load_lds(s_v, tidf);
-      ado.load_lds(pf_do, tidf);
+      agam.template load_lds<TAIL>(pf_g, tidf, nv);
+      aq.template load_lds<TAIL>(s_pq, tidf, nv);
+      ak.template load_lds<TAIL>(s_k, tidf, nv);
+      av_.template load_lds<TAIL>(s_v, tidf, nv);
+      ado.template load_lds<TAIL>(pf_do, tidf, nv);
       __syncthreads();   // the raw regions are overwritten from here on
     } else {
-      aseg.load(a.seq_idx, t0, tidf & 63);
-      agam.load(a.g, b, h, t0, a.T, a.H, tidf);
-      if constexpr (APPLY) agam.load_w(a.w, b, h, t0, a.T, a.H, tidf);
-      aq.load(q, b, h, t0, a.T, a.H, tidf);
+      aseg.template load<TAIL>(a.seq_idx, t0, tidf & 63, nv);
+      agam.template load<TAIL>(a.g, b, h, t0, a.T, a.H, tidf, nv);
+      if constexpr (APPLY) agam.template load_w<TAIL>(a.w, b, h, t0, a.T, a.H, tidf, nv);
+      aq.template load<TAIL>(q, b, h, t0, a.T, a.H, tidf, nv);
       if constexpr (APPLY) {
-        ak.load(k, b, h, t0, a.T, a.H, tidf);
-        av_.load(v, b, h, t0, a.T, a.H, tidf);
+        ak.template load<TAIL>(k, b, h, t0, a.T, a.H, tidf, nv);
+        av_.template load<TAIL>(v, b, h, t0, a.T, a.H, tidf, nv);
       }
-      ado.load(dO, b, h, t0, a.T, a.H, tidf);
+      ado.template load<TAIL>(dO, b, h, t0, a.T, a.H, tidf, nv);
     }
     seg = aseg.finish(a.seq_idx);
     finish_gamma<DK, DECAY, G::NT>(agam, seg, s_gam, s_fq, s_fk, tidf, gam_hi, SCAL ? s_w : nullptr);
@@ -362,7 +377,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
 
       // S0 rows of the owned d_k tiles (fp32, columns 16j + 4g .. +3), read here so
       // that the load overlaps the dv phase
-      const float* cs = a.chunk_states + ((bh * nct + t0 / CH) * DK) * (int64_t)DV;
+      const float* cs = a.chunk_states + ((bh * nct + cbase + c) * DK) * (int64_t)DV;
       f32x4 s0r[G::CPWK][G::DVP / 16];
       {
         const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
@@ -380,7 +395,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
 #pragma unroll
             for (int I = 0; I < 4; ++I) {
               gl[cc][I] = f32x4{0.f, 0.f, 0.f, 0.f};
-              if (d0 < DK)
+              if (d0 < DK && (full || 16 * I + i16 < nv))
                 gl[cc][I] = *reinterpret_cast<const f32x4*>(a.g + tok_off(b, t0 + 16 * I + i16, h, a.T, a.H, DK) + d0);
             }
           }
@@ -432,7 +447,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
             mma2b(acc, fdo[ib], fb, fbl);
           }
           const int n0 = 16 * cn + 4 * g;
-          if (n0 < DV) store4(dvp + tok_off(b, t0 + tj, h, a.T, a.H, DV) + n0, acc);
+          if (n0 < DV && (full || tj < nv)) store4(dvp + tok_off(b, t0 + tj, h, a.T, a.H, DV) + n0, acc);
         }
       }
 
@@ -534,7 +549,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
                 acc[rr] *= ok ? __expf(gm[rr]) : 0.f;
               }
             }
-            if (d0 < DK) store4(dqp + tok_off(b, t0 + ti, h, a.T, a.H, DK) + d0, acc);
+            if (d0 < DK && (full || ti < nv)) store4(dqp + tok_off(b, t0 + ti, h, a.T, a.H, DK) + d0, acc);
           }
         }
         // Y'^T = dS'^T V^T (dS' = dS scaled by exp(Gam_last[d]) for a diagonal decay),
@@ -605,7 +620,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
             } else {
               acc += yv;
             }
-            if (d0 < DK) store4(dkp + tok_off(b, t0 + tj, h, a.T, a.H, DK) + d0, acc);
+            if (d0 < DK && (full || tj < nv)) store4(dkp + tok_off(b, t0 + tj, h, a.T, a.H, DK) + d0, acc);
           }
         }
       }
@@ -614,7 +629,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
         __syncthreads();   // every wave is past its last read of k, k-lo, v and the score tiles
         if (c > 0) {
           const int tidp = tid_pick<APPLY, G::NT>();
-          prefetch(t0 - CH, tidp);
+          prefetch(t0 - CH, tidp, CH, std::false_type{});   // every chunk but a shard's last is full
           nseg.load(a.seq_idx, t0 - CH, tidp & 63);
         }
       }
@@ -645,7 +660,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
             pre_tot += row_last(x);
             const int t = 16 * I + i16;
             if ((seg.starts >> t) & 1ull) dgv = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (d0 < DK) store4(a.dg + tok_off(b, t0 + t, h, a.T, a.H, DK) + d0, dgv);
+            if (d0 < DK && (full || t < nv)) store4(a.dg + tok_off(b, t0 + t, h, a.T, a.H, DK) + d0, dgv);
           }
         }
       }
@@ -699,11 +714,11 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
           const float t3 = keep * __expf(s_gam[CH - 1]) * t3s;
           float dgv = x + y4 + t3;
           if ((seg.starts >> t) & 1ull) dgv = 0.f;
-          a.dg[(b * a.T + t0 + t) * a.H + h] = dgv;
+          if (t < nv) a.dg[(b * a.T + t0 + t) * a.H + h] = dgv;
           // input-weight gradient dw_t = k_t^T dS_t v_t: the intra part is column t
           // of the P tile on and below the diagonal, the tail part is u4; both carry
           // w_t (in the score decay and the tail factor), divided out here
-          if (a.dw) a.dw[(b * a.T + t0 + t) * a.H + h] = (colb + s_p[t * (CH + 1) + t] + u4) / s_w[t];
+          if (a.dw && t < nv) a.dw[(b * a.T + t0 + t) * a.H + h] = (colb + s_p[t * (CH + 1) + t] + u4) / s_w[t];
         }
       }
     }
@@ -811,16 +826,21 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
 }
 
 #define CPLA_INST_BWD(E, D, DEC)                                                   \
-  template __global__ void bwd_walk<E, D, D, DEC, false, false>(BwdArgs);         \
-  template __global__ void bwd_walk<E, D, D, DEC, true, false>(BwdArgs);
+  template __global__ void bwd_walk<E, D, D, DEC, false, false, false>(BwdArgs);  \
+  template __global__ void bwd_walk<E, D, D, DEC, true, false, false>(BwdArgs);   \
+  template __global__ void bwd_walk<E, D, D, DEC, false, false, true>(BwdArgs);   \
+  template __global__ void bwd_walk<E, D, D, DEC, true, false, true>(BwdArgs);
 #define CPLA_INST_BWD3(E, D) CPLA_INST_BWD(E, D, 0) CPLA_INST_BWD(E, D, 1) CPLA_INST_BWD(E, D, 2)
 CPLA_INST_BWD3(bf16_t, 16)
 CPLA_INST_BWD3(bf16_t, 64)
 CPLA_INST_BWD3(bf16_t, 128)
 // fp32 gradients from bf16 inputs: the scalar decay (the Mamba2 parametrisation)
-template __global__ void bwd_walk<bf16_t, 16, 16, 1, true, true>(BwdArgs);
-template __global__ void bwd_walk<bf16_t, 64, 64, 1, true, true>(BwdArgs);
-template __global__ void bwd_walk<bf16_t, 128, 128, 1, true, true>(BwdArgs);
+#define CPLA_INST_BWD_GF32(D)                                                      \
+  template __global__ void bwd_walk<bf16_t, D, D, 1, true, true, false>(BwdArgs); \
+  template __global__ void bwd_walk<bf16_t, D, D, 1, true, true, true>(BwdArgs);
+CPLA_INST_BWD_GF32(16)
+CPLA_INST_BWD_GF32(64)
+CPLA_INST_BWD_GF32(128)
 CPLA_INST_BWD3(float, 16)
 CPLA_INST_BWD3(float, 64)
 

@@ -12,6 +12,7 @@
 // exponentiate a positive exponent.
 #pragma once
 #include "device.hpp"
+#include "shards.hpp"
 
 namespace cpla {
 
@@ -61,11 +62,18 @@ __device__ __forceinline__ int64_t tok_off(int64_t b, int64_t t, int64_t h, int6
 // Sequence ids of the chunk's tokens (packed sequences): one token per lane.
 struct SegRegs {
   int cur, prev;
-  __device__ __forceinline__ void load(const int32_t* seq_idx, int64_t t0, int l = lane_id()) {
+  // TAIL: n = tokens of the chunk inside the shard (fewer than 64 only in a
+  // shard's last chunk); the rows past them continue the last sequence (no start)
+  template <bool TAIL = false>
+  __device__ __forceinline__ void load(const int32_t* seq_idx, int64_t t0, int l = lane_id(), int n = CH) {
     if (!seq_idx) return;
     const int64_t t = t0 + l;
-    cur = seq_idx[t];
-    prev = t > 0 ? seq_idx[t - 1] : -1;   // sequence ids are >= 0: token 0 starts one
+    if (!TAIL || l < n) {
+      cur = seq_idx[t];
+      prev = t > 0 ? seq_idx[t - 1] : -1;   // sequence ids are >= 0: token 0 starts one
+    } else {
+      cur = prev = 0;
+    }
   }
   __device__ __forceinline__ ChunkSeg finish(const int32_t* seq_idx) const {
     ChunkSeg s;
@@ -91,21 +99,32 @@ struct GamRegs {
   float wt = 1.f;   // scalar decay: the token's input weight (1 without one)
   __device__ __forceinline__ static int column(int tid) { return (tid >> 6) * CPW + (tid & 63) % CPW; }
   // scalar decay with a per-token input weight: thread tid < 64 holds token tid's
+  template <bool TAIL = false>
   __device__ __forceinline__ void load_w(const float* __restrict__ w, int64_t b, int64_t h, int64_t t0, int64_t T,
-                                         int64_t H, int tid = threadIdx.x) {
+                                         int64_t H, int tid = threadIdx.x, int n = CH) {
     if constexpr (DECAY == DECAY_SCALAR)
-      if (w && tid < CH) wt = w[(b * T + t0 + tid) * H + h];
+      if (w && tid < (TAIL ? n : CH)) wt = w[(b * T + t0 + tid) * H + h];
   }
   __device__ __forceinline__ static int part(int tid) { return (tid & 63) / CPW; }
+  // TAIL: n = tokens of the chunk inside the shard; the rows past them read as g = 0
+  template <bool TAIL = false>
   __device__ __forceinline__ void load(const float* __restrict__ g, int64_t b, int64_t h, int64_t t0, int64_t T,
-                                       int64_t H, int tid = threadIdx.x) {
+                                       int64_t H, int tid = threadIdx.x, int n = CH) {
     if constexpr (DECAY == DECAY_DIAG) {
-      const int d = column(tid);
-      const float* src = g + ((b * T + t0 + part(tid) * TOK) * H + h) * DK + d;
+      const int d = column(tid), i0 = part(tid) * TOK;
+      const float* src = g + ((b * T + t0 + i0) * H + h) * DK + d;
 #pragma unroll
-      for (int s = 0; s < TOK; ++s) v[s] = src[(int64_t)s * H * DK];
+      for (int s = 0; s < TOK; ++s) {
+        if constexpr (!TAIL) {
+          v[s] = src[(int64_t)s * H * DK];
+        } else {   // rows past the shard: load the last valid row (in bounds), then 0
+          const int row = i0 + s < n ? s : n - 1 - i0;
+          const float x = src[(int64_t)row * H * DK];
+          v[s] = i0 + s < n ? x : 0.f;
+        }
+      }
     } else if constexpr (DECAY == DECAY_SCALAR) {
-      if (tid < CH) v[0] = g[(b * T + t0 + tid) * H + h];
+      if (tid < CH) v[0] = (!TAIL || tid < n) ? g[(b * T + t0 + tid) * H + h] : 0.f;
     }
   }
   // The values load() reads, copied by LDS DMA instead. Diagonal: value s of
@@ -118,32 +137,45 @@ struct GamRegs {
   static constexpr int DMA_FLOATS = (DECAY == DECAY_DIAG) ? NT / 64 * (TOK + 1) * 64 : CH;
   __device__ __forceinline__ static constexpr int lds_shift(int s) { return (s & 3) + 16 * ((s >> 2) & 3); }
   __device__ __forceinline__ static int lds_row(int w, int s) { return w * (TOK + 1) * 64 + s * 64 + lds_shift(s); }
+  // TAIL: with n < CH (a shard's partial last chunk) lanes past the shard copy
+  // nothing and load_lds returns 0 for them
+  template <bool TAIL = false>
   __device__ __forceinline__ static void dma(const float* __restrict__ g, int64_t b, int64_t h, int64_t t0,
-                                             int64_t T, int64_t H, float* buf, int tid, int w) {
+                                             int64_t T, int64_t H, float* buf, int tid, int w, int n = CH) {
     if constexpr (DECAY == DECAY_DIAG) {
-      const float* src = g + ((b * T + t0 + part(tid) * TOK) * H + h) * DK + column(tid);
+      const int i0 = part(tid) * TOK;
+      const float* src = g + ((b * T + t0 + i0) * H + h) * DK + column(tid);
 #pragma unroll
-      for (int s = 0; s < TOK; ++s) lds_dma<4>(src + (int64_t)s * H * DK, buf + lds_row(w, s));
+      for (int s = 0; s < TOK; ++s)
+        if (!TAIL || i0 + s < n) lds_dma<4>(src + (int64_t)s * H * DK, buf + lds_row(w, s));
     } else if constexpr (DECAY == DECAY_SCALAR) {
-      if (tid < CH) lds_dma<4>(g + (b * T + t0 + tid) * H + h, buf + 64 * w);
+      if (tid < (TAIL ? n : CH)) lds_dma<4>(g + (b * T + t0 + tid) * H + h, buf + 64 * w);
     }
   }
-  __device__ __forceinline__ void load_lds(const float* buf, int tid) {
+  template <bool TAIL = false>
+  __device__ __forceinline__ void load_lds(const float* buf, int tid, int n = CH) {
     if constexpr (DECAY == DECAY_DIAG) {
-      const int w = tid >> 6, l = tid & 63;
+      const int w = tid >> 6, l = tid & 63, i0 = part(tid) * TOK;
 #pragma unroll
       for (int s = 0; s < TOK; ++s) v[s] = buf[lds_row(w, s) + l];
+      if constexpr (TAIL) {
+#pragma unroll
+        for (int s = 0; s < TOK; ++s) v[s] = i0 + s < n ? v[s] : 0.f;
+      }
     } else if constexpr (DECAY == DECAY_SCALAR) {
-      if (tid < CH) v[0] = buf[tid];
+      if (tid < CH) v[0] = (!TAIL || tid < n) ? buf[tid] : 0.f;
     }
   }
   // Diagonal, TOK == CPW == 16 (d_k of 64 or 128): the raw log-decay of token
   // 16 I + (l % 16) at key dims 16 w + 4 (l / 16) + rr (rr = 0..3), the MFMA
   // accumulator layout of wave w's key tile, from the DMA buffer.
-  __device__ __forceinline__ static f32x4 lane_block(const float* buf, int w, int I, int l) {
+  template <bool TAIL = false>
+  __device__ __forceinline__ static f32x4 lane_block(const float* buf, int w, int I, int l, int n = CH) {
     static_assert(DECAY == DECAY_DIAG && TOK == 16 && CPW == 16, "lane layout needs 16-token parts of 16 columns");
     const float* p = buf + lds_row(w, l & 15) + 16 * I + 4 * (l >> 4);
-    return f32x4{p[0], p[1], p[2], p[3]};
+    const f32x4 x = {p[0], p[1], p[2], p[3]};
+    if constexpr (!TAIL) return x;
+    return 16 * I + (l & 15) >= n ? f32x4{0.f, 0.f, 0.f, 0.f} : x;
   }
 };
 
@@ -212,35 +244,48 @@ struct TileRegs {
   static constexpr int NV = CH * VPR;
   static constexpr int PER = (NV + NT - 1) / NT;
   f32x4 r[PER];
+  // TAIL: n = tokens of the chunk inside the shard; the rows past them read as zeros
+  template <bool TAIL = false>
   __device__ __forceinline__ void load(const E* __restrict__ src, int64_t b, int64_t h, int64_t t0, int64_t T,
-                                       int64_t H, int tid = threadIdx.x) {
+                                       int64_t H, int tid = threadIdx.x, int n = CH) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int v = tid + p * NT;
       if (v < NV) {
         const int i = v / VPR, c = (v % VPR) * VEC;
-        r[p] = *reinterpret_cast<const f32x4*>(src + tok_off(b, t0 + i, h, T, H, D) + c);
+        if constexpr (!TAIL) {
+          r[p] = *reinterpret_cast<const f32x4*>(src + tok_off(b, t0 + i, h, T, H, D) + c);
+        } else {   // rows past the shard: load the last valid row (in bounds), then 0
+          const f32x4 x = *reinterpret_cast<const f32x4*>(src + tok_off(b, t0 + (i < n ? i : n - 1), h, T, H, D) + c);
+          r[p] = i < n ? x : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
       }
     }
   }
   // The vectors load() reads, copied by LDS DMA instead: vector p of thread tid
   // lands at buf[(p * NT + tid) * VEC], one contiguous kilobyte per wave and p
   // (w = the calling wave); load_lds reads them back. buf holds CH * D elements.
+  template <bool TAIL = false>
   __device__ __forceinline__ static void dma(const E* __restrict__ src, int64_t b, int64_t h, int64_t t0, int64_t T,
-                                             int64_t H, E* buf, int tid, int w) {
+                                             int64_t H, E* buf, int tid, int w, int n = CH) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int v = tid + p * NT;
-      if (v < NV) {
-        const int i = v / VPR, c = (v % VPR) * VEC;
+      const int i = v / VPR, c = (v % VPR) * VEC;
+      if (v < NV && (!TAIL || i < n))
         lds_dma<16>(src + tok_off(b, t0 + i, h, T, H, D) + c, buf + (p * NT + 64 * w) * VEC);
-      }
     }
   }
-  __device__ __forceinline__ void load_lds(const E* buf, int tid) {
+  template <bool TAIL = false>
+  __device__ __forceinline__ void load_lds(const E* buf, int tid, int n = CH) {
 #pragma unroll
     for (int p = 0; p < PER; ++p)
       if (tid + p * NT < NV) r[p] = *reinterpret_cast<const f32x4*>(buf + (p * NT + tid) * VEC);
+    if constexpr (TAIL) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p)
+        if ((tid + p * NT) / VPR >= n) r[p] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
 };
 

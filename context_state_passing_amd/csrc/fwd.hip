@@ -90,7 +90,7 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* K
   }
 }
 
-template <typename E, int DK, int DV, int DECAY, bool APPLY>
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL>
 __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_walk(FwdArgs a) {
   using G = Geo<E, DK, DV>;
   // diagonal decay: the prepare walk stages Gam rows 32..63 in the v tile's buffer
@@ -117,8 +117,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
   __builtin_assume(w >= 0 && w < G::NW);
   const int r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
-  const int64_t L = a.T / a.P, tshard = r * L;
-  const int nc = (int)(L / CH);
+  // the shard's tokens [tshard, tshard + slen): torch.chunk's division of T into P
+  const int64_t tshard = shard_begin(a.T, a.P, r), slen = shard_len(a.T, a.P, r);
+  const int nc = (int)chunks_of(slen);
 
   f32x4 S[G::NKT][G::CPWV];
 #pragma unroll
@@ -150,19 +151,24 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
   GamRegs<DK, DECAY, G::NT> rgam;
   TileRegs<E, DK, G::NT> rk, rq;
   TileRegs<E, DV, G::NT> rv;
+  // tokens of chunk c inside the shard (the last chunk may be partial)
+  auto valid = [&](int c) { return (int)(slen - (int64_t)c * CH < CH ? slen - (int64_t)c * CH : CH); };
   auto prefetch = [&](int c) {
     const int64_t t = tshard + (int64_t)c * CH;
-    rseg.load(a.seq_idx, t);
-    rgam.load(a.g, b, h, t, a.T, a.H);
-    rgam.load_w(a.w, b, h, t, a.T, a.H);
-    rk.load(k, b, h, t, a.T, a.H);
-    if constexpr (APPLY) rq.load(q, b, h, t, a.T, a.H);
-    rv.load(v, b, h, t, a.T, a.H);
+    const int n = TAIL ? valid(c) : CH;
+    rseg.template load<TAIL>(a.seq_idx, t, lane_id(), n);
+    rgam.template load<TAIL>(a.g, b, h, t, a.T, a.H, threadIdx.x, n);
+    rgam.template load_w<TAIL>(a.w, b, h, t, a.T, a.H, threadIdx.x, n);
+    rk.template load<TAIL>(k, b, h, t, a.T, a.H, threadIdx.x, n);
+    if constexpr (APPLY) rq.template load<TAIL>(q, b, h, t, a.T, a.H, threadIdx.x, n);
+    rv.template load<TAIL>(v, b, h, t, a.T, a.H, threadIdx.x, n);
   };
   if constexpr (APPLY) prefetch(0);
 
   for (int c = 0; c < nc; ++c) {
     const int64_t t0 = tshard + (int64_t)c * CH;
+    const int nv = TAIL ? valid(c) : CH;
+    const bool full = !TAIL || nv >= CH;   // only a shard's last chunk is partial
     if constexpr (!APPLY) prefetch(c);
     const ChunkSeg seg = rseg.finish(a.seq_idx);
     any_start |= seg.any();
@@ -264,7 +270,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
             mma2b(acc, fvt[jb], fb, fbl);
           }
           const int n0 = 16 * cn + 4 * g;
-          if (n0 < DV) store4(o + tok_off(b, t0 + 16 * I + i16, h, a.T, a.H, DV) + n0, acc);
+          if (n0 < DV && (full || 16 * I + i16 < nv)) store4(o + tok_off(b, t0 + 16 * I + i16, h, a.T, a.H, DV) + n0, acc);
         }
       }
     }
@@ -274,7 +280,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
     // at the start of the chunk measured slower)
     if constexpr (APPLY) {
       if (a.chunk_states) {
-        float* cs = a.chunk_states + ((bh * (a.T / CH) + t0 / CH) * DK) * (int64_t)DV;
+        float* cs = a.chunk_states +
+                    ((bh * row_chunks(a.T, a.P) + shard_chunk_base(a.T, a.P, r) + c) * DK) * (int64_t)DV;
 #pragma unroll
         for (int m = 0; m < G::NKT; ++m)
 #pragma unroll
@@ -320,8 +327,10 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
 }
 
 #define CPLA_INST_FWD(E, D, DEC)                                                   \
-  template __global__ void fwd_walk<E, D, D, DEC, false>(FwdArgs);                \
-  template __global__ void fwd_walk<E, D, D, DEC, true>(FwdArgs);
+  template __global__ void fwd_walk<E, D, D, DEC, false, false>(FwdArgs);         \
+  template __global__ void fwd_walk<E, D, D, DEC, true, false>(FwdArgs);          \
+  template __global__ void fwd_walk<E, D, D, DEC, false, true>(FwdArgs);          \
+  template __global__ void fwd_walk<E, D, D, DEC, true, true>(FwdArgs);
 #define CPLA_INST_FWD3(E, D) CPLA_INST_FWD(E, D, 0) CPLA_INST_FWD(E, D, 1) CPLA_INST_FWD(E, D, 2)
 CPLA_INST_FWD3(bf16_t, 16)
 CPLA_INST_FWD3(bf16_t, 64)

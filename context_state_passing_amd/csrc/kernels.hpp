@@ -53,9 +53,11 @@ struct ScanArgs {
   float* fin;                // final state (forward) / dS_init (reverse), or null
 };
 
-template <typename E, int DK, int DV, int DECAY, bool APPLY>
+// TAIL: some shard's length is not a multiple of the chunk (a partial last chunk
+// to mask); without it every guard compiles away
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL>
 __global__ void fwd_walk(FwdArgs a);
-template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32>
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAIL>
 __global__ void bwd_walk(BwdArgs a);
 __global__ void affine_scan(ScanArgs a);
 

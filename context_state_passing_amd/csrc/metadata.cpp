@@ -5,7 +5,9 @@
 // rank-local per-token sequence ids, rank-local sequence boundaries, the
 // inclusive start of the ranks whose forward summaries the rank composes, and
 // the exclusive end of the ranks whose backward summaries it composes. Shards
-// are the cp_size equal contiguous slices of the stream.
+// are torch.chunk's cp_size contiguous slices of the stream (shards.hpp): an
+// empty trailing shard has no local tokens and no sequences (local_cu_seqlens
+// {0}), and composes nothing (preceding_rank_start r, following_rank_stop r + 1).
 //
 // One O(T) sweep finds, for every token, the first and last index of its
 // sequence; the per-rank fields follow from the rank's first and last token.
@@ -15,15 +17,15 @@
 
 #include "cpla.h"
 #include "errors.hpp"
+#include "shards.hpp"
 
 namespace {
 
 // Valid ids start at 0 and step by 0 or 1 (the form cu_seqlens produces).
 cpla_status check_ids(const int32_t* s, int64_t T, int32_t cp_size) {
   if (!s) return cpla::fail(CPLA_E_INVALID, "global_seq_idx is NULL");
-  if (cp_size <= 0 || T <= 0 || T % cp_size != 0)
-    return cpla::fail(CPLA_E_METADATA, "stream length %lld is not a positive multiple of cp_size %d",
-                      (long long)T, cp_size);
+  if (cp_size <= 0 || T <= 0)
+    return cpla::fail(CPLA_E_METADATA, "stream length %lld and cp_size %d must be positive", (long long)T, cp_size);
   if (s[0] != 0) return cpla::fail(CPLA_E_METADATA, "global_seq_idx[0] is %d, expected 0", s[0]);
   for (int64_t t = 1; t < T; ++t) {
     const int32_t step = s[t] - s[t - 1];
@@ -65,7 +67,15 @@ extern "C" cpla_status build_packed_sequence_cp_metadata(const int32_t* global_s
     return cpla::fail(CPLA_E_INVALID, "cp_rank %d outside [0, %d)", cp_rank, cp_size);
   if (!local_seq_idx || !local_cu_seqlens || !num_local_seqs || !preceding_rank_start || !following_rank_stop)
     return cpla::fail(CPLA_E_INVALID, "an output pointer is NULL");
-  const int64_t L = T / cp_size, a = (int64_t)cp_rank * L, e = a + L - 1;
+  const int64_t size = cpla::shard_size(T, cp_size), a = cpla::shard_begin(T, cp_size, cp_rank);
+  const int64_t L = cpla::shard_len(T, cp_size, cp_rank), e = a + L - 1;
+  if (L == 0) {
+    local_cu_seqlens[0] = 0;
+    *num_local_seqs = 0;
+    *preceding_rank_start = cp_rank;
+    *following_rank_stop = cp_rank + 1;
+    return CPLA_OK;
+  }
   const int32_t* s = global_seq_idx;
   int32_t n = 0;
   local_cu_seqlens[n++] = 0;
@@ -80,8 +90,8 @@ extern "C" cpla_status build_packed_sequence_cp_metadata(const int32_t* global_s
   while (f > 0 && s[f - 1] == s[a]) --f;
   int64_t z = e;
   while (z < T - 1 && s[z + 1] == s[e]) ++z;
-  *preceding_rank_start = (int32_t)(f / L);
-  *following_rank_stop = (int32_t)(z / L + 1);
+  *preceding_rank_start = (int32_t)(f / size);
+  *following_rank_stop = (int32_t)(z / size + 1);
   return CPLA_OK;
 }
 
@@ -93,11 +103,17 @@ extern "C" cpla_status cpla_packed_rank_slices(const int32_t* global_seq_idx, in
   if (!preceding_rank_start || !following_rank_stop) return cpla::fail(CPLA_E_INVALID, "an output pointer is NULL");
   std::vector<int64_t> first, last;
   seq_bounds(global_seq_idx, T, first, last);
-  const int64_t L = T / cp_size;
+  const int64_t size = cpla::shard_size(T, cp_size);
   for (int32_t r = 0; r < cp_size; ++r) {
-    const int64_t a = (int64_t)r * L, e = a + L - 1;
-    preceding_rank_start[r] = (int32_t)(first[a] / L);
-    following_rank_stop[r] = (int32_t)(last[e] / L + 1);
+    const int64_t a = cpla::shard_begin(T, cp_size, r), L = cpla::shard_len(T, cp_size, r);
+    if (L == 0) {   // empty trailing shard: composes nothing
+      preceding_rank_start[r] = r;
+      following_rank_stop[r] = r + 1;
+      continue;
+    }
+    const int64_t e = a + L - 1;
+    preceding_rank_start[r] = (int32_t)(first[a] / size);
+    following_rank_stop[r] = (int32_t)(last[e] / size + 1);
   }
   return CPLA_OK;
 }

@@ -69,7 +69,7 @@ typedef struct ihipStream_t* hipStream_t;
 typedef enum {
   CPLA_OK = 0,
   CPLA_E_INVALID = 1,      /* null pointer where one is required, bad enum  */
-  CPLA_E_SHAPE = 2,        /* sizes inconsistent or not divisible           */
+  CPLA_E_SHAPE = 2,        /* sizes not positive or inconsistent            */
   CPLA_E_DTYPE = 3,        /* unknown dtype                                  */
   CPLA_E_ALIGN = 4,        /* a pointer is not 16-byte aligned               */
   CPLA_E_UNSUPPORTED = 5,  /* valid request this build does not implement   */
@@ -82,7 +82,10 @@ typedef enum { CPLA_DECAY_NONE = 0, CPLA_DECAY_SCALAR = 1, CPLA_DECAY_DIAG = 2 }
 
 typedef struct {
   int64_t B, T, H, dk, dv;   /* packed sequences: B == 1 and T is the stream length   */
-  int32_t num_shards;        /* P: T % P == 0 and (T / P) % chunk == 0                 */
+  int32_t num_shards;        /* P <= 64 shards of any T: torch.chunk's division (shard
+                                size ceil(T/P), the last non-empty shard shorter, trailing
+                                shards empty when T is short; a shard's last chunk may be
+                                partial), the graceful division the mixle page relies on */
   int32_t chunk;             /* chunk length C; this build supports 64 only            */
   int32_t rank_begin;        /* shards handled by this call: [rank_begin, rank_end)    */
   int32_t rank_end;          /*   (0 and P on one GPU)                                  */
@@ -103,7 +106,9 @@ typedef struct {
 /* Floats per (shard, b, h) summary record: m_slot + dk*dv (see layout above). */
 int64_t cpla_summary_width(const cpla_problem* p);
 
-/* Bytes of the chunk-state buffer the forward saves for the backward. */
+/* Bytes of the chunk-state buffer the forward saves for the backward: one fp32
+ * dk x dv state per (b, h) and per 64-token chunk of every shard, the shards'
+ * chunks in order ([B,H,n_chunks,dk,dv]). -1 for an invalid problem. */
 int64_t cpla_chunk_states_bytes(const cpla_problem* p);
 
 /* cp_forward_prepare: for every handled shard, run the shard from a zero state
@@ -180,13 +185,16 @@ cpla_status cp_backward_apply_weighted(const cpla_problem* p, const cpla_packed*
 
 /* build_packed_sequence_cp_metadata (host memory, pure, thread-safe): rank-local
  * packed metadata from the global per-token sequence ids (length T, starting at
- * 0, each step 0 or 1, T % cp_size == 0). local_seq_idx [T/cp_size] receives the
- * rank's ids rebased to start at 0; local_cu_seqlens (capacity T/cp_size + 1)
- * receives 0, each interior id change and T/cp_size, and *num_local_seqs its
- * number of sequences; *preceding_rank_start is the rank holding the first token
- * of the sequence live at the rank's first token, *following_rank_stop one past
- * the rank holding the last token of the sequence live at its last token.
- * Malformed ids return CPLA_E_METADATA. */
+ * 0, each step 0 or 1), the rank's shard being torch.chunk's slice (see
+ * cpla_problem.num_shards; L = its length, at most ceil(T/cp_size)).
+ * local_seq_idx [L] receives the rank's ids rebased to start at 0;
+ * local_cu_seqlens (capacity L + 1) receives 0, each interior id
+ * change and L, and *num_local_seqs its number of sequences; *preceding_rank_start
+ * is the rank holding the first token of the sequence live at the rank's first
+ * token, *following_rank_stop one past the rank holding the last token of the
+ * sequence live at its last token. An empty shard gets local_cu_seqlens {0},
+ * no sequences and the slice [r, r + 1) (it composes nothing). Malformed ids
+ * return CPLA_E_METADATA. */
 cpla_status build_packed_sequence_cp_metadata(const int32_t* global_seq_idx, int64_t T,
                                               int32_t cp_rank, int32_t cp_size,
                                               int32_t* local_seq_idx, int32_t* local_cu_seqlens,

@@ -16,8 +16,8 @@ Readings where the page is silent: shards are the cp_size contiguous slices of
 the stream that torch.chunk makes (ceil(T / cp_size) tokens each, the last
 non-empty one shorter, trailing ones empty when the stream is short — the
 graceful division the mixle page relies on); an empty shard has no local
-tokens, local_cu_seqlens [0, 0], and composes nothing (prefix start r, suffix
-stop r + 1); local ids are rebased so
+tokens and no sequences (local_cu_seqlens [0]), and composes nothing (prefix
+start r, suffix stop r + 1); local ids are rebased so
 the shard's first token has id 0; local_cu_seqlens lists 0, every interior
 position where the id changes, and the shard length; the prefix starts at the
 rank holding the first token of the sequence that is live at the shard's first
@@ -70,7 +70,7 @@ def build_packed_sequence_cp_metadata(global_seq_idx, cp_rank, cp_size):
     a = min(cp_rank * size, T)
     L = min(size, T - a)
     if L == 0:
-        return {"local_seq_idx": np.zeros(0, dtype=np.int32), "local_cu_seqlens": np.zeros(2, dtype=np.int32),
+        return {"local_seq_idx": np.zeros(0, dtype=np.int32), "local_cu_seqlens": np.zeros(1, dtype=np.int32),
                 "preceding_rank_start": cp_rank, "following_rank_stop": cp_rank + 1}
     e = a + L - 1
     local = [s[t] - s[a] for t in range(a, a + L)]

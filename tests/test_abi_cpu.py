@@ -52,8 +52,8 @@ def fwd_prepare(p, k=FAKE, v=FAKE, g=FAKE, out=FAKE, packed=None):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(B=0), 2), (dict(dtype=7), 3), (dict(decay=5), 1), (dict(chunk=32), 5),
-    (dict(T=1000), 2), (dict(T=1024, num_shards=8 * 3), 2), (dict(T=64 * 65, num_shards=65), 5),
+    (dict(B=0), 2), (dict(dtype=7), 3), (dict(decay=5), 1), (dict(chunk=32), 5), (dict(T=0), 2),
+    (dict(T=64 * 65, num_shards=65), 5),
     (dict(rank_begin=2, rank_end=2), 1), (dict(rank_end=5), 1), (dict(dv=64), 5), (dict(dk=32, dv=32), 5),
     (dict(dtype=_lib.F32), 5), (dict(num_shards=0), 2),
 ])
@@ -104,6 +104,18 @@ def test_sizes():
     p = prob(decay=_lib.DECAY_SCALAR)
     assert L.cpla_summary_width(ctypes.byref(p)) == 4 + 128 * 128
     assert L.cpla_chunk_states_bytes(ctypes.byref(p)) == 1 * 2 * (1024 // 64) * 128 * 128 * 4
+    # uneven division: 1000 tokens on 3 shards are 334 + 334 + 332 -> 6 + 6 + 6 chunks;
+    # 200 tokens on 64 shards are 50 shards of 4 (one chunk each) and 14 empty ones
+    for T, P, chunks in [(1000, 3, 18), (200, 64, 50), (1000, 1, 16), (65, 2, 2)]:
+        p = prob(T=T, num_shards=P, rank_end=P)
+        assert L.cpla_chunk_states_bytes(ctypes.byref(p)) == 2 * chunks * 128 * 128 * 4, (T, P)
+
+
+def test_uneven_division_is_accepted():
+    for T, P in [(1000, 3), (200, 64), (7, 4), (1, 8)]:
+        # validation passes, so the call reaches the (absent) pointers' checks
+        assert fwd_prepare(prob(T=T, num_shards=P, rank_end=P), k=None) == 1
+        assert b"k is NULL" in L.cpla_last_error()
 
 
 # ---- packed metadata: C++ builder == oracle twin, bit-exact --------------------------------
@@ -137,6 +149,21 @@ def test_metadata_matches_oracle(seed):
         assert a["following_rank_stop"] == b["following_rank_stop"]
 
 
+@pytest.mark.parametrize("T,P", [(4000, 16), (4000, 7), (10, 4), (9, 4), (5, 8), (130, 64)])
+def test_metadata_uneven_matches_oracle(T, P):
+    rng = np.random.default_rng(T + P)
+    cu = random_stream(rng, T, 1, max(2, T // 5))
+    s = cpla.seq_idx_from_cu_seqlens(cu, T)
+    prs, frs = cpla.packed_rank_slices(s, P)
+    prs_o, frs_o = omd.rank_slices(s, P)
+    assert np.array_equal(prs, prs_o) and np.array_equal(frs, frs_o)
+    for r in range(P):
+        a = cpla.build_packed_sequence_cp_metadata(s, r, P)
+        b = omd.build_packed_sequence_cp_metadata(s, r, P)
+        for key in a:
+            assert np.array_equal(a[key], b[key]), (key, r)
+
+
 def test_metadata_edge_cases_match_oracle():
     cases = [np.zeros(64, np.int32),                                 # one sequence everywhere
              np.repeat(np.arange(4), 16).astype(np.int32),           # starts exactly at rank starts
@@ -150,7 +177,7 @@ def test_metadata_edge_cases_match_oracle():
                 assert np.array_equal(a[key], b[key]), key
 
 
-@pytest.mark.parametrize("bad", [[1, 1, 1, 1], [0, 2, 2, 2], [0, 1, 0, 1], [0, 0, 0]])
+@pytest.mark.parametrize("bad", [[1, 1, 1, 1], [0, 2, 2, 2], [0, 1, 0, 1]])
 def test_metadata_rejects_malformed(bad):
     with pytest.raises(cpla.CplaError) as e:
         cpla.build_packed_sequence_cp_metadata(np.array(bad, np.int32), 0, 2)

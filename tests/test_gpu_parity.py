@@ -65,6 +65,23 @@ SMALL = {
     "packed_len1_bwd": ("packed_fwdbwd", {"T": 256, "H": 1, "num_shards": 2, "len_range": (1, 1)}, True),
     "packed_one_seq_bwd": ("packed_fwdbwd", {"T": 1024, "H": 2, "num_shards": 4, "len_range": (4096, 4096)},
                            True),
+    # uneven division (torch.chunk) and partial last chunks: shards of 167/167/166
+    # tokens; weak decay so the composition across the uneven shards matters;
+    # shards shorter than one chunk (63 tokens, the last 55); 64 shards of 4 tokens
+    # with 14 empty; a single shard of 100 tokens (64 + 36); packed streams with
+    # shards of 143 tokens; d = 64 / 16 in both dtypes
+    "uneven_diag_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 500, "num_shards": 3}, True),
+    "uneven_diag_weak_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 700, "num_shards": 5,
+                                             "decay_scale": 1e-3}, True),
+    "uneven_subchunk_shards_bwd": ("diag_fwdbwd", {"B": 1, "H": 1, "T": 1000, "num_shards": 16}, True),
+    "uneven_empty_shards_bwd": ("scalar_fwd", {"B": 1, "H": 2, "T": 200, "num_shards": 64, "backward": True,
+                                               "decay_scale": 1e-2}, True),
+    "tail_identity_fp32_bwd": ("identity_fwd", {"T": 100, "num_shards": 1, "backward": True}, True),
+    "uneven_packed_bwd": ("packed_fwdbwd", {"T": 1000, "H": 2, "num_shards": 7, "len_range": (40, 300)}, True),
+    "uneven_diag_d64_bwd": ("diag_fwdbwd", {"B": 2, "H": 1, "T": 450, "d": 64, "num_shards": 2}, True),
+    "uneven_diag_d16_fp32_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 300, "d": 16, "num_shards": 4,
+                                                 "dtype": torch.float32}, True),
+    "uneven_long_init_bwd": ("long_fwdbwd", {"T": 777, "H": 2, "num_shards": 3}, True),
 }
 
 

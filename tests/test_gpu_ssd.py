@@ -34,6 +34,7 @@ CASES = {
     "fp32_n16_g4": dict(B=2, T=256, H=4, G=4, N=16, num_shards=4, dtype=torch.float32),
     "fp32_n64_init": dict(B=1, T=384, H=2, G=1, N=64, num_shards=3, dtype=torch.float32,
                           with_initial_state=True),
+    "bf16_n64_uneven": dict(B=1, T=1000, H=4, G=2, N=64, num_shards=3),
 }
 
 
