@@ -64,6 +64,8 @@ def forward(q, k, v, g=None, decay="none", initial_state=None, seq_idx=None, chu
     R = B * H
     qr, kr, vr = rec.to_rows(q), rec.to_rows(k), rec.to_rows(v)
     lg = _log_decay_rows(g, decay, R, T, dk)
+    if seq_idx is not None and np.ndim(seq_idx) != 1:
+        raise ValueError("the chunked form takes one packing shared by the batch ([T] seq_idx)")
     resets = rec.starts_from_seq_idx(seq_idx, T)
     S = np.zeros((R, dk, dv)) if initial_state is None else rec._np(initial_state).reshape(R, dk, dv).copy()
     o = np.zeros((R, T, dv))
@@ -89,6 +91,8 @@ def backward(q, k, v, g=None, decay="none", dO=None, initial_state=None, seq_idx
     R = B * H
     qr, kr, vr, dOr = rec.to_rows(q), rec.to_rows(k), rec.to_rows(v), rec.to_rows(rec._np(dO))
     lg = _log_decay_rows(g, decay, R, T, dk)
+    if seq_idx is not None and np.ndim(seq_idx) != 1:
+        raise ValueError("the chunked form takes one packing shared by the batch ([T] seq_idx)")
     resets = rec.starts_from_seq_idx(seq_idx, T)
     # forward pass: state entering every chunk
     S = np.zeros((R, dk, dv)) if initial_state is None else rec._np(initial_state).reshape(R, dk, dv).copy()

@@ -24,7 +24,9 @@ starts at rank 0 from S_init and the suffix ends at the last rank from
 dS_final. Shards follow torch.chunk: ceil(T / P) tokens each, the last
 non-empty one shorter when P does not divide T, and trailing shards empty when
 the stream is too short (the graceful division the mixle page relies on, in
-place of failing fast); an empty shard's map is the identity.
+place of failing fast); an empty shard's map is the identity. With one
+packing per batch row (``seq_idx`` [B, T]) the rows are independent problems,
+each with its own rank slices, and are run one after the other.
 """
 from __future__ import annotations
 
@@ -147,11 +149,40 @@ def compose_suffix(M, gam, d_final_state=None, frs=None):
     return dS_out, d_init
 
 
+def _per_row(seq_idx):
+    return seq_idx is not None and np.ndim(seq_idx) == 2
+
+
+def _row(x, b):
+    return None if x is None else _np(x)[b:b + 1]
+
+
+def _stack(parts, shard_major):
+    """Concatenate per-row results: batch axis 1 for the per-shard arrays named
+    in ``shard_major``, axis 0 otherwise."""
+    out = {}
+    for key, first in parts[0].items():
+        if first is None:
+            out[key] = None
+        elif isinstance(first, dict):
+            out[key] = _stack([p[key] for p in parts], shard_major)
+        else:
+            out[key] = np.concatenate([p[key] for p in parts], axis=1 if key in shard_major else 0)
+    return out
+
+
+_SHARD_MAJOR = ("M", "delta_S", "S_in", "gamma", "dS_out")
+
+
 def cp_forward(q, k, v, g, decay, P, initial_state=None, seq_idx=None):
     """The method end to end: prepare (summaries), compose, apply. Returns o,
     final state, and the intermediates (M, delta_S, S_in)."""
     q, k, v = _np(q), _np(k), _np(v)
     B, T, H, dk = q.shape
+    if _per_row(seq_idx):
+        return _stack([cp_forward(_row(q, b), _row(k, b), _row(v, b), _row(g, b), decay, P,
+                                  _row(initial_state, b), np.asarray(seq_idx)[b]) for b in range(B)],
+                      _SHARD_MAJOR)
     starts = rec.starts_from_seq_idx(seq_idx, T)
     M, dS = forward_summaries(k, v, g, decay, P, seq_idx)
     prs, _ = slices(P, seq_idx)
@@ -166,6 +197,11 @@ def cp_forward(q, k, v, g, decay, P, initial_state=None, seq_idx=None):
 
 def cp_backward(q, k, v, g, decay, dO, P, initial_state=None, seq_idx=None, d_final_state=None):
     """Backward through summaries: gamma, reverse-causal composition, local finish."""
+    if _per_row(seq_idx):
+        B = np.shape(q)[0]
+        return _stack([cp_backward(_row(q, b), _row(k, b), _row(v, b), _row(g, b), decay, _row(dO, b), P,
+                                   _row(initial_state, b), np.asarray(seq_idx)[b], _row(d_final_state, b))
+                       for b in range(B)], _SHARD_MAJOR)
     fw = cp_forward(q, k, v, g, decay, P, initial_state, seq_idx)
     q, k, v, dO = _np(q), _np(k), _np(v), _np(dO)
     B, T, H, dk = q.shape

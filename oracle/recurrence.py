@@ -71,18 +71,27 @@ def decay_rows(g, decay, R, T, dk):
 
 
 def starts_from_seq_idx(seq_idx, T):
-    """Boolean [T]: True where a packed sequence starts (token 0 always does)."""
+    """Boolean [T] (or [B, T] for one packing per batch row): True where a packed
+    sequence starts (token 0 always does)."""
     if seq_idx is None:
         return np.zeros(T, dtype=bool)
     s = np.asarray(seq_idx).astype(np.int64)
-    st = np.zeros(T, dtype=bool)
-    st[0] = True
-    st[1:] = s[1:] != s[:-1]
+    st = np.zeros(s.shape, dtype=bool)
+    st[..., 0] = True
+    st[..., 1:] = s[..., 1:] != s[..., :-1]
     return st
 
 
+def resets_per_row(resets, B, H):
+    """[T] (shared by every batch row) or [B, T] -> [B*H, T], rows ordered as to_rows."""
+    r = np.asarray(resets, dtype=bool)
+    if r.ndim == 1:
+        return np.broadcast_to(r, (B * H, r.shape[0]))
+    return np.repeat(r, H, axis=0)
+
+
 def run_forward_rows(q, k, v, a, resets, S0, wr=None):
-    """Rows form. q, k: [R,T,dk]; v: [R,T,dv]; a: [R,T,dk]; resets: [T] bool; S0: [R,dk,dv];
+    """Rows form. q, k: [R,T,dk]; v: [R,T,dv]; a: [R,T,dk]; resets: [R,T] bool; S0: [R,dk,dv];
     wr: per-token input weights [R,T] or None.
 
     Returns o [R,T,dv] and the final state [R,dk,dv]."""
@@ -91,8 +100,7 @@ def run_forward_rows(q, k, v, a, resets, S0, wr=None):
     o = np.empty((R, T, v.shape[2]))
     wr = np.ones((R, T)) if wr is None else wr
     for t in range(T):
-        if resets[t]:
-            S[:] = 0.0
+        S = np.where(resets[:, t, None, None], 0.0, S)
         S = a[:, t, :, None] * S + wr[:, t, None, None] * k[:, t, :, None] * v[:, t, None, :]
         o[:, t] = np.einsum("rkv,rk->rv", S, q[:, t])
     return o, S
@@ -113,8 +121,7 @@ def run_backward_rows(q, k, v, a, resets, S0, dO, dSf, decay, wr=None):
     for t in range(T):
         if t % CKPT == 0:
             ck[t // CKPT] = S
-        if resets[t]:
-            S[:] = 0.0
+        S = np.where(resets[:, t, None, None], 0.0, S)
         S = a[:, t, :, None] * S + wr[:, t, None, None] * k[:, t, :, None] * v[:, t, None, :]
 
     dq = np.empty((R, T, dk))
@@ -128,7 +135,7 @@ def run_backward_rows(q, k, v, a, resets, S0, dO, dSf, decay, wr=None):
         cur = []    # S_t
         S = ck[b].copy()
         for t in range(t0, t1):
-            Sp = np.zeros_like(S) if resets[t] else S
+            Sp = np.where(resets[:, t, None, None], 0.0, S)
             S = a[:, t, :, None] * Sp + wr[:, t, None, None] * k[:, t, :, None] * v[:, t, None, :]
             prev.append(Sp)
             cur.append(S)
@@ -139,12 +146,10 @@ def run_backward_rows(q, k, v, a, resets, S0, dO, dSf, decay, wr=None):
             dk_[:, t] = wr[:, t, None] * np.einsum("rkv,rv->rk", dS, v[:, t])
             dvv[:, t] = wr[:, t, None] * np.einsum("rkv,rk->rv", dS, k[:, t])
             dw[:, t] = np.einsum("rkv,rk,rv->r", dS, k[:, t], v[:, t])
-            if resets[t]:
-                G = np.zeros_like(G)
-            else:
-                if decay != "none":
-                    dg[:, t] = a[:, t] * np.einsum("rkv,rkv->rk", dS, prev[i])
-                G = a[:, t, :, None] * dS
+            keep = ~resets[:, t]          # rows where token t continues its sequence
+            if decay != "none":
+                dg[:, t] = np.where(keep[:, None], a[:, t] * np.einsum("rkv,rkv->rk", dS, prev[i]), 0.0)
+            G = np.where(keep[:, None, None], a[:, t, :, None] * dS, 0.0)
     return dq, dk_, dvv, dg, G, dw
 
 
@@ -155,7 +160,7 @@ def _prep(q, k, v, g, decay, initial_state, seq_idx, resets):
     R = B * H
     if resets is None:
         resets = starts_from_seq_idx(seq_idx, T)
-    resets = np.asarray(resets, dtype=bool)
+    resets = resets_per_row(resets, B, H)
     if initial_state is None:
         S0 = np.zeros((R, dk, dv))
     else:
@@ -167,9 +172,10 @@ def _prep(q, k, v, g, decay, initial_state, seq_idx, resets):
 def forward(q, k, v, g=None, decay="none", initial_state=None, seq_idx=None, resets=None, w=None):
     """o [B,T,H,dv] and final state [B,H,dk,dv], fp64.
 
-    ``seq_idx`` (int [T], B == 1) marks packed sequences: the state resets at each
-    start, token 0 included. ``resets`` may be given instead (bool [T]) to reset
-    only at chosen tokens, e.g. a shard whose first token continues a sequence.
+    ``seq_idx`` (int [T], or [B, T] for one packing per batch row) marks packed
+    sequences: the state resets at each start, token 0 included. ``resets`` may
+    be given instead (bool [T] or [B, T]) to reset only at chosen tokens, e.g. a
+    shard whose first token continues a sequence.
     ``w`` [B,T,H]: per-token input weights (S_t = a_t S_{t-1} + w_t k_t v_t^T)."""
     q, k, v, B, T, H, dk, dv, R, resets, S0, a = _prep(q, k, v, g, decay, initial_state, seq_idx, resets)
     wr = None if w is None else to_rows(_np(w))

@@ -46,14 +46,14 @@ def _np(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _starts(seq_idx, T):
-    if seq_idx is None:
-        st = np.zeros(T, dtype=bool)
-    else:
-        s = np.asarray(seq_idx)
-        st = np.concatenate([[True], s[1:] != s[:-1]])
-    st[0] = False   # token 0 starts from h_init (zero in packed use)
-    return st
+def _starts(seq_idx, Bt, T):
+    """[Bt, T] bool: True where a packed sequence starts after token 0. ``seq_idx``
+    is [T] (one packing for every batch row) or [Bt, T] (one per row)."""
+    st = np.zeros((Bt, T), dtype=bool)
+    if seq_idx is not None:
+        s = np.broadcast_to(np.asarray(seq_idx), (Bt, T))
+        st[:, 1:] = s[:, 1:] != s[:, :-1]
+    return st   # token 0 starts from h_init (zero in packed use)
 
 
 def ssd_forward(x, dt, A, B, C, h_init=None, seq_idx=None):
@@ -62,12 +62,11 @@ def ssd_forward(x, dt, A, B, C, h_init=None, seq_idx=None):
     Bt, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     grp = np.arange(H) // (H // G)
-    st = _starts(seq_idx, T)
+    st = _starts(seq_idx, Bt, T)
     h = np.zeros((Bt, H, N, P)) if h0 is None else h0.copy()
     y = np.zeros((Bt, T, H, P))
     for t in range(T):
-        if st[t]:
-            h[:] = 0.0
+        h = np.where(st[:, t, None, None, None], 0.0, h)
         a = np.exp(dt[:, t, :] * A[None, :])                       # [Bt, H]
         Bt_ = B[:, t, grp, :]                                      # [Bt, H, N]
         Ct_ = C[:, t, grp, :]
@@ -82,13 +81,13 @@ def ssd_backward(x, dt, A, B, C, dy, h_init=None, seq_idx=None, dh_final=None):
     Bt, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     grp = np.arange(H) // (H // G)
-    st = _starts(seq_idx, T)
+    st = _starts(seq_idx, Bt, T)
     a = np.exp(dt * A[None, None, :])                              # [Bt, T, H]
     # states h_{t-1} for every t (T is small in tests)
     hs = np.zeros((T + 1, Bt, H, N, P))
     hs[0] = 0.0 if h0 is None else h0
     for t in range(T):
-        prev = np.zeros((Bt, H, N, P)) if st[t] else hs[t]
+        prev = np.where(st[:, t, None, None, None], 0.0, hs[t])
         hs[t + 1] = a[:, t, :, None, None] * prev + dt[:, t, :, None, None] * \
             B[:, t, grp, :][:, :, :, None] * x[:, t, :, None, :]
     dx = np.zeros_like(x)
@@ -104,13 +103,11 @@ def ssd_backward(x, dt, A, B, C, dy, h_init=None, seq_idx=None, dh_final=None):
         np.add.at(dC, (slice(None), t, grp), np.einsum("bhnp,bhp->bhn", hs[t + 1], dy[:, t]))
         np.add.at(dB, (slice(None), t, grp), dt[:, t, :, None] * np.einsum("bhnp,bhp->bhn", dh, x[:, t]))
         dx[:, t] = dt[:, t, :, None] * np.einsum("bhnp,bhn->bhp", dh, Bt_)
-        prev = np.zeros((Bt, H, N, P)) if st[t] else hs[t]
+        prev = np.where(st[:, t, None, None, None], 0.0, hs[t])
         da = np.einsum("bhnp,bhnp->bh", dh, prev)
         ddt[:, t] = np.einsum("bhnp,bhn,bhp->bh", dh, Bt_, x[:, t]) + da * a[:, t] * A[None, :]
         dA += np.sum(da * a[:, t] * dt[:, t], axis=0)
-        dh = a[:, t, :, None, None] * dh
-        if st[t]:
-            dh = np.zeros_like(dh)
+        dh = np.where(st[:, t, None, None, None], 0.0, a[:, t, :, None, None] * dh)
     dh0 = None if h0 is None else dh
     return dx, ddt, dA, dB, dC, dh0
 

@@ -2,7 +2,7 @@
 
 * O(T^2) closed forms (identity decay: tril(Q K^T) V; decayed: explicit double sum);
 * central finite differences of a scalar loss (backward);
-* packed stream == each sequence run alone;
+* packed stream == each sequence run alone (one packing for the batch, or one per row);
 * sharded (summaries + composition) == unsharded, packed and unpacked;
 * chunk algebra == per-token recurrence at chunk lengths 1, 7, 64;
 * the adjoint identity sum_t (q*dq - k*dk) == 0 over a sequence with zero
@@ -97,6 +97,41 @@ def test_packed_equals_separate():
                 np.testing.assert_allclose(dg[:, a:b], r[3], rtol=0, atol=1e-13)
                 assert np.all(dg[:, a] == 0.0)       # a start never sees its decay
         np.testing.assert_allclose(fin, fin_s, rtol=0, atol=1e-13)
+
+
+ROW_LENGTHS = [[5, 1, 17, 9, 2, 30], [64], [30, 34], [1, 1, 62]]   # one packing per batch row, T = 64
+
+
+def _row_packing(lengths_per_row):
+    seqs, cus = zip(*(_packed_seq_idx(L) for L in lengths_per_row))
+    return np.stack(seqs), cus
+
+
+def test_per_row_packing_equals_separate():
+    """seq_idx [B, T]: every row keeps its own boundaries; each sequence of each
+    row equals that sequence run alone, forward and backward."""
+    rng = np.random.default_rng(12)
+    seq, cus = _row_packing(ROW_LENGTHS)
+    B, T = seq.shape
+    for decay in ["none", "scalar", "diag"]:
+        q, k, v, g, _ = _rand(rng, B, T, 2, 4, 3, decay)
+        o, fin = oracle.forward(q, k, v, g, decay, seq_idx=seq)
+        dO = rng.standard_normal(o.shape)
+        dq, dk, dv, dg, _ = oracle.backward(q, k, v, g, decay, dO, seq_idx=seq)
+        for b, cu in enumerate(cus):
+            for s in range(len(cu) - 1):
+                a, e = int(cu[s]), int(cu[s + 1])
+                sl = (slice(b, b + 1), slice(a, e))
+                gs = None if g is None else g[sl]
+                o_s, fin_s = oracle.forward(q[sl], k[sl], v[sl], gs, decay)
+                np.testing.assert_allclose(o[sl], o_s, rtol=0, atol=1e-13)
+                r = oracle.backward(q[sl], k[sl], v[sl], gs, decay, dO[sl])
+                for got, want in [(dq, r[0]), (dk, r[1]), (dv, r[2])]:
+                    np.testing.assert_allclose(got[sl], want, rtol=0, atol=1e-13)
+                if dg is not None:
+                    np.testing.assert_allclose(dg[sl], r[3], rtol=0, atol=1e-13)
+                    assert np.all(dg[b, a] == 0.0)
+            np.testing.assert_allclose(fin[b:b + 1], fin_s, rtol=0, atol=1e-13)
 
 
 # --- backward: finite differences ---------------------------------------------
@@ -216,6 +251,33 @@ def test_sharded_packed_equals_whole_stream(lengths):
                 assert np.all(f["S_in"][r] == 0.0)
             else:
                 np.testing.assert_allclose(S_in_all[r], f["S_in"][r], atol=1e-12)
+
+
+@pytest.mark.parametrize("P", [3, 4, 7])
+def test_sharded_per_row_packing_equals_whole_stream(P):
+    """One packing per batch row: each row gets its own rank slices, and the
+    sharded method equals the per-token recurrence on every row."""
+    rng = np.random.default_rng(50 + P)
+    seq, _ = _row_packing(ROW_LENGTHS)
+    B, T = seq.shape
+    for decay in ["scalar", "diag"]:
+        q, k, v, g, _ = _rand(rng, B, T, 2, 3, 2, decay, gscale=0.1)
+        dO = rng.standard_normal((B, T, 2, 2))
+        o, fin = oracle.forward(q, k, v, g, decay, seq_idx=seq)
+        dq, dk_, dv_, dg, _ = oracle.backward(q, k, v, g, decay, dO, seq_idx=seq)
+        f = cp.cp_forward(q, k, v, g, decay, P, seq_idx=seq)
+        np.testing.assert_allclose(f["o"], o, atol=1e-12)
+        np.testing.assert_allclose(f["final_state"], fin, atol=1e-12)
+        assert f["S_in"].shape == (P, B, 2, 3, 2)
+        r = cp.cp_backward(q, k, v, g, decay, dO, P, seq_idx=seq)
+        for a, b in [(r["dq"], dq), (r["dk"], dk_), (r["dv"], dv_), (r["dg"], dg)]:
+            np.testing.assert_allclose(a, b, atol=1e-12)
+        # a row's slices depend on that row only
+        for b in range(B):
+            prs, frs = metadata.rank_slices(seq[b], P)
+            one = cp.cp_forward(q[b:b + 1], k[b:b + 1], v[b:b + 1], g[b:b + 1], decay, P, seq_idx=seq[b])
+            np.testing.assert_array_equal(one["S_in"][:, 0], f["S_in"][:, b])
+            assert prs.shape == frs.shape == (P,)
 
 
 # --- chunk algebra ------------------------------------------------------------

@@ -2,7 +2,7 @@
 
 * the O(T^2) quadratic form of the selective state space (brute force, tiny T);
 * central finite differences of a scalar loss, for every input (initial state
-  and packed sequences included);
+  and packed sequences, one packing for the batch or one per row, included);
 * the linear-attention oracle, an independent implementation, under the map
   q = C[group], k = B[group], v = x, input weight w = dt, g = A dt — forward and,
   through the chain rule, backward;
@@ -33,12 +33,22 @@ def test_forward_matches_quadratic_form():
     np.testing.assert_allclose(y, y2, rtol=1e-12, atol=1e-12)
 
 
-@pytest.mark.parametrize("init,packed", [(False, False), (True, False), (False, True)])
+def _seq(packed, Bt, cu, T):
+    """packed: 0 none, 1 one packing for the batch (Bt = 1), 2 one per row."""
+    if packed == 1:
+        return metadata.seq_idx_from_cu_seqlens(np.array(cu), T)
+    if packed == 2:
+        rows = [cu, [0, T]] + [[0, 1, T]] * (Bt - 2)
+        return np.stack([metadata.seq_idx_from_cu_seqlens(np.array(c), T) for c in rows[:Bt]])
+    return None
+
+
+@pytest.mark.parametrize("init,packed", [(False, 0), (True, 0), (False, 1), (False, 2)])
 def test_backward_matches_finite_differences(init, packed):
     rng = np.random.default_rng(11 + 2 * init + packed)
-    Bt = 1 if packed else 2
+    Bt = 1 if packed == 1 else 2
     x, dt, A, B, C, h0 = _inputs(rng, Bt=Bt, T=8, init=init)
-    seq = metadata.seq_idx_from_cu_seqlens(np.array([0, 3, 8]), 8) if packed else None
+    seq = _seq(packed, Bt, [0, 3, 8], 8)
     W = rng.standard_normal(x.shape)
     Wf = rng.standard_normal((Bt, x.shape[2], 3, 3))
 
@@ -65,12 +75,12 @@ def test_backward_matches_finite_differences(init, packed):
         np.testing.assert_allclose(gexp, num, rtol=1e-6, atol=1e-7, err_msg=f"input {i}")
 
 
-@pytest.mark.parametrize("init,packed", [(False, False), (True, False), (False, True)])
+@pytest.mark.parametrize("init,packed", [(False, 0), (True, 0), (False, 1), (False, 2)])
 def test_matches_linear_attention_oracle(init, packed):
     rng = np.random.default_rng(23 + 2 * init + packed)
-    Bt = 1 if packed else 2
+    Bt = 1 if packed == 1 else 3
     x, dt, A, B, C, h0 = _inputs(rng, Bt=Bt, T=21, H=4, G=2, N=4, init=init)
-    seq = metadata.seq_idx_from_cu_seqlens(np.array([0, 5, 6, 21]), 21) if packed else None
+    seq = _seq(packed, Bt, [0, 5, 6, 21], 21)
     H, G = x.shape[2], B.shape[2]
     grp = np.arange(H) // (H // G)
     q, k = C[:, :, grp], B[:, :, grp]
