@@ -122,7 +122,7 @@ def _oracle_row(args):
     seq = None
     if wl.cu_seqlens is not None:
         from oracle import metadata as omd
-        seq = omd.seq_idx_from_cu_seqlens(wl.cu_seqlens.numpy(), wl.T)
+        seq = omd.seq_idx_rows(wl.cu_seqlens, wl.T)
     with threadpool_limits(1):
         t = time.perf_counter()
         if wl.dO is None:
@@ -345,7 +345,7 @@ def main():
     dg = None if g is None else torch.empty_like(g)
     pk = None
     if wl.cu_seqlens is not None:
-        meta = packed_meta(wl.cu_seqlens, T, P, dev)
+        meta = packed_meta(wl.cu_seqlens, T, P, dev, B)
         pk = ctypes.byref(meta.c())
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)

@@ -79,20 +79,42 @@ def build_packed_sequence_cp_metadata(global_seq_idx, cp_rank: int, cp_size: int
 
 @dataclasses.dataclass
 class PackedMeta:
-    seq_idx: torch.Tensor                 # device int32 [T]
-    preceding_rank_start: torch.Tensor    # device int32 [P]
-    following_rank_stop: torch.Tensor     # device int32 [P]
+    seq_idx: torch.Tensor                 # device int32 [B, T]: each batch row packed on its own
+    preceding_rank_start: torch.Tensor    # device int32 [B, P]
+    following_rank_stop: torch.Tensor     # device int32 [B, P]
 
     def c(self) -> Packed:
         return Packed(self.seq_idx.data_ptr(), self.preceding_rank_start.data_ptr(),
                       self.following_rank_stop.data_ptr())
 
 
-def packed_meta(cu_seqlens, T: int, num_shards: int, device) -> PackedMeta:
-    s = seq_idx_from_cu_seqlens(cu_seqlens, T)
-    prs, frs = packed_rank_slices(s, num_shards)
+def _cu_rows(cu_seqlens, B: int):
+    """cu_seqlens of every batch row: one 1-D cu_seqlens (B == 1), or one per row
+    (a sequence of B of them, or a 2-D array when the rows hold equally many)."""
+    if torch.is_tensor(cu_seqlens):
+        cu_seqlens = cu_seqlens.detach().cpu().numpy()
+    if isinstance(cu_seqlens, np.ndarray):
+        rows = [cu_seqlens] if cu_seqlens.ndim == 1 else list(cu_seqlens)
+    else:
+        items = list(cu_seqlens)
+        rows = [np.asarray(items)] if items and np.ndim(items[0]) == 0 else [
+            c.detach().cpu().numpy() if torch.is_tensor(c) else np.asarray(c) for c in items]
+    if len(rows) != B:
+        raise CplaError(2, f"cu_seqlens describes {len(rows)} packed rows for B={B}")
+    return rows
+
+
+def packed_meta(cu_seqlens, T: int, num_shards: int, device, B: int = 1) -> PackedMeta:
+    """Device metadata for B packed rows of T tokens (``cu_seqlens`` as ``_cu_rows`` reads it)."""
+    seqs, prss, frss = [], [], []
+    for cu in _cu_rows(cu_seqlens, B):
+        s = seq_idx_from_cu_seqlens(cu, T)
+        prs, frs = packed_rank_slices(s, num_shards)
+        seqs.append(s)
+        prss.append(prs)
+        frss.append(frs)
     dev = torch.device(device)
-    return PackedMeta(torch.from_numpy(s).to(dev), torch.from_numpy(prs).to(dev), torch.from_numpy(frs).to(dev))
+    return PackedMeta(*(torch.from_numpy(np.stack(x)).to(dev) for x in (seqs, prss, frss)))
 
 
 # ---- forward / backward ----------------------------------------------------------------
@@ -145,7 +167,7 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
     decay = _decay_of(g, q)
     p = make_problem(q, v, num_shards, decay, chunk)
     if cu_seqlens is not None and packed is None:
-        packed = packed_meta(cu_seqlens, q.shape[1], num_shards, q.device)
+        packed = packed_meta(cu_seqlens, q.shape[1], num_shards, q.device, q.shape[0])
     L = _lib.lib()
     B, T, H, dk = q.shape
     dv = v.shape[-1]

@@ -59,7 +59,6 @@ cpla_status check_ptr(const void* ptr, const char* name, bool required) {
 
 cpla_status check_packed(const cpla_problem* p, const cpla_packed* pk, bool need_prs, bool need_frs) {
   if (!pk) return CPLA_OK;
-  if (p->B != 1) return fail(CPLA_E_SHAPE, "packed sequences need B == 1 (got %lld)", (long long)p->B);
   cpla_status st;
   if ((st = check_ptr(pk->seq_idx, "packed->seq_idx", true)) != CPLA_OK) return st;
   if ((st = check_ptr(pk->preceding_rank_start, "packed->preceding_rank_start", need_prs)) != CPLA_OK) return st;
@@ -163,6 +162,7 @@ cpla_status launch_scan(const cpla_problem* p, const float* summary, const int32
   s.W = cpla_summary_width(p);
   s.dk = (int)p->dk;
   s.dv = (int)p->dv;
+  s.H = (int)p->H;
   s.n_elem = s.BH * p->dk * p->dv;
   s.P = p->num_shards;
   s.m_slot = (int)m_slot_of(p);

@@ -135,6 +135,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
   __builtin_assume(w >= 0 && w < G::NW);
   const int r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  // packed sequences: row b's sequence ids (one packing per batch row)
+  const int32_t* const seq_row = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
   // the shard's tokens [tshard, tshard + slen): torch.chunk's division of T into P
   const int64_t tshard = shard_begin(a.T, a.P, r), slen = shard_len(a.T, a.P, r);
   const int nc = (int)chunks_of(slen);
@@ -207,7 +209,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
       const int64_t tn = tshard + (int64_t)(nc - 1) * CH;
       const int n = TAIL ? valid(nc - 1) : CH;
       prefetch(tn, tidf, n, std::integral_constant<bool, TAIL>{});
-      nseg.template load<TAIL>(a.seq_idx, tn, tidf & 63, n);
+      nseg.template load<TAIL>(seq_row, tn, tidf & 63, n);
     }
   }
 
@@ -247,7 +249,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
       ado.template load_lds<TAIL>(pf_do, tidf, nv);
       __syncthreads();   // the raw regions are overwritten from here on
     } else {
-      aseg.template load<TAIL>(a.seq_idx, t0, tidf & 63, nv);
+      aseg.template load<TAIL>(seq_row, t0, tidf & 63, nv);
       agam.template load<TAIL>(a.g, b, h, t0, a.T, a.H, tidf, nv);
       if constexpr (APPLY) agam.template load_w<TAIL>(a.w, b, h, t0, a.T, a.H, tidf, nv);
       aq.template load<TAIL>(q, b, h, t0, a.T, a.H, tidf, nv);
@@ -257,7 +259,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
       }
       ado.template load<TAIL>(dO, b, h, t0, a.T, a.H, tidf, nv);
     }
-    seg = aseg.finish(a.seq_idx);
+    seg = aseg.finish(seq_row);
     finish_gamma<DK, DECAY, G::NT>(agam, seg, s_gam, s_fq, s_fk, tidf, gam_hi, SCAL ? s_w : nullptr);
     any_start |= seg.any();
     const float keep = seg.any() ? 0.f : 1.f;
@@ -351,24 +353,24 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
         }
         // the tiles are stored transposed (row = key token j, column = query token
         // i): the lane's four rows i become one 8-byte write per part
-        f32x4 va = {0.f, 0.f, 0.f, 0.f}, vd = {0.f, 0.f, 0.f, 0.f};
+        // causal, same-sequence mask as selects on the sequence counts (a branch per
+        // element here was compiled into code that dropped some of them)
+        f32x4 va, vd;
         const int j = 16 * J + i16;
+        const int sj = seg.index(j);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int i = 16 * I + 4 * g + rr;
-          float pp = 0.f;
-          if (seg.same(i, j)) {
-            va[rr] = xa[rr];
-            vd[rr] = xd[rr];
-            if constexpr (SCAL) {
-              // exp(Gam_i - Gam_j) and the input weight of token j, applied once
-              const float dec = __expf(s_gam[i] - s_gam[j]) * s_w[j];
-              pp = va[rr] * vd[rr] * dec;   // exp(Gam_i - Gam_j) w_j (q_i.k_j)(dO_i.v_j)
-              va[rr] *= dec;
-              vd[rr] *= dec;
-            }
+          const bool ok = i >= j && seg.index(i) == sj;
+          va[rr] = ok ? xa[rr] : 0.f;
+          vd[rr] = ok ? xd[rr] : 0.f;
+          if constexpr (SCAL) {
+            // exp(Gam_i - Gam_j) and the input weight of token j, applied once
+            const float dec = ok ? __expf(s_gam[i] - s_gam[j]) * s_w[j] : 0.f;
+            s_p[i * (CH + 1) + j] = va[rr] * vd[rr] * dec;   // exp(Gam_i - Gam_j) w_j (q_i.k_j)(dO_i.v_j)
+            va[rr] *= dec;
+            vd[rr] *= dec;
           }
-          if constexpr (SCAL) s_p[i * (CH + 1) + j] = pp;
         }
         store_split4(s_ah, s_al, j * G::LDA + 16 * I + 4 * g, va);
         store_split4(s_dah, s_dal, j * G::LDA + 16 * I + 4 * g, vd);
@@ -630,7 +632,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
         if (c > 0) {
           const int tidp = tid_pick<APPLY, G::NT>();
           prefetch(t0 - CH, tidp, CH, std::false_type{});   // every chunk but a shard's last is full
-          nseg.load(a.seq_idx, t0 - CH, tidp & 63);
+          nseg.load(seq_row, t0 - CH, tidp & 63);
         }
       }
 

@@ -266,6 +266,9 @@ struct ChunkSeg {
   __device__ __forceinline__ int last() const { return starts ? 63 - __builtin_clzll(starts) : 0; }
   __device__ __forceinline__ bool live(int i) const { return i < first(); }
   __device__ __forceinline__ bool tail(int i) const { return i >= last(); }
+  // number of starts at or before token t: tokens i >= j share a sequence iff
+  // their counts are equal
+  __device__ __forceinline__ int index(int t) const { return __popcll(starts & ((2ull << t) - 1ull)); }
   // i >= j and no start in (j, i]
   __device__ __forceinline__ bool same(int i, int j) const {
     if (i < j) return false;

@@ -117,6 +117,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
   __builtin_assume(w >= 0 && w < G::NW);
   const int r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  // packed sequences: row b's sequence ids (one packing per batch row)
+  const int32_t* const seq_row = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
   // the shard's tokens [tshard, tshard + slen): torch.chunk's division of T into P
   const int64_t tshard = shard_begin(a.T, a.P, r), slen = shard_len(a.T, a.P, r);
   const int nc = (int)chunks_of(slen);
@@ -156,7 +158,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
   auto prefetch = [&](int c) {
     const int64_t t = tshard + (int64_t)c * CH;
     const int n = TAIL ? valid(c) : CH;
-    rseg.template load<TAIL>(a.seq_idx, t, lane_id(), n);
+    rseg.template load<TAIL>(seq_row, t, lane_id(), n);
     rgam.template load<TAIL>(a.g, b, h, t, a.T, a.H, threadIdx.x, n);
     rgam.template load_w<TAIL>(a.w, b, h, t, a.T, a.H, threadIdx.x, n);
     rk.template load<TAIL>(k, b, h, t, a.T, a.H, threadIdx.x, n);
@@ -170,7 +172,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
     const int nv = TAIL ? valid(c) : CH;
     const bool full = !TAIL || nv >= CH;   // only a shard's last chunk is partial
     if constexpr (!APPLY) prefetch(c);
-    const ChunkSeg seg = rseg.finish(a.seq_idx);
+    const ChunkSeg seg = rseg.finish(seq_row);
     any_start |= seg.any();
     finish_gamma<DK, DECAY, G::NT>(rgam, seg, s_gam, s_fq, s_fk, threadIdx.x, gam_hi,
                                    DECAY == DECAY_SCALAR ? s_w : nullptr);

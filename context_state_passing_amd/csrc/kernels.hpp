@@ -45,13 +45,60 @@ struct BwdArgs {
 
 struct ScanArgs {
   int64_t BH, W, n_elem;     // n_elem = B*H*dk*dv
-  int dk, dv, P, m_slot, diag, reverse;
+  int dk, dv, H, P, m_slot, diag, reverse;
   const float* summary;      // [P,B,H,W]
-  const int32_t* slice;      // preceding_rank_start (forward) / following_rank_stop (reverse), or null
+  const int32_t* slice;      // [B,P] preceding_rank_start (forward) / following_rank_stop (reverse), or null
   const float* init;         // S_init (forward) / dS_final (reverse), or null
   float* out;                // [P,B,H,dk,dv]
   float* fin;                // final state (forward) / dS_init (reverse), or null
 };
+
+// The gated delta rule (dense transition), d_k = d_v = D. Workspace tensors are
+// fp32: ws_ut, ws_w, ws_u, ws_du [B,T,H,D]; chunk states and ws_dsc (the gradient
+// at every chunk's end) [B,H,row_chunks,D,D].
+struct DeltaArgs {
+  int64_t B, T, H;
+  int P, rank_begin;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dO;
+  const float* g;            // [B,T,H] log-decay
+  const float* beta;         // [B,T,H] write strength
+  const int32_t* seq_idx;    // [B,T] packed sequences or null
+  const float* state_in;     // forward apply: S_in [P,B,H,D,D]; backward apply: dS_out
+  const float* fwd_summary;  // backward prepare: the forward records (M is copied)
+  float* summary;            // prepare: [P,B,H,2 D^2] records [M | delta_S or gamma]
+  void* out;                 // o
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dg;
+  float* dbeta;
+  float* chunk_states;
+  float* ws_ut;
+  float* ws_w;
+  float* ws_u;
+  float* ws_du;
+  float* ws_dsc;
+};
+
+struct DeltaScanArgs {
+  int64_t BH, H;
+  int P, reverse;
+  const float* summary;      // [P,B,H,2 D^2]
+  const int32_t* slice;      // [B,P] or null
+  const float* init;         // S_init / dS_final, or null
+  float* out;                // [P,B,H,D,D]
+  float* fin;                // final state / dS_init, or null
+};
+
+template <typename E, int D> __global__ void delta_wy(DeltaArgs a);
+template <typename E, int D, bool APPLY> __global__ void delta_fwalk(DeltaArgs a);
+template <int D> __global__ void delta_scan(DeltaScanArgs a);
+template <typename E, int D> __global__ void delta_out(DeltaArgs a);
+template <typename E, int D, bool APPLY> __global__ void delta_bwalk(DeltaArgs a);
+template <typename E, int D> __global__ void delta_grad(DeltaArgs a);
 
 // TAIL: some shard's length is not a multiple of the chunk (a partial last chunk
 // to mask); without it every guard compiles away

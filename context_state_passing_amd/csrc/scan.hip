@@ -8,6 +8,7 @@
 // in shard order, reading each shard's record with loads that are contiguous
 // across the threads (the element index runs fastest), P of them in flight
 // per batch.
+// With packed sequences each batch row has its own slices prs / frs ([B, P]).
 //   forward:  shard r gets the fold over [prs_r, r), started from S_init at
 //             rank 0 (unpacked) and from zero at ranks with prs_r == r;
 //   reverse:  shard r gets the fold over (r, frs_r) taken backwards, started
@@ -31,6 +32,7 @@ __global__ __launch_bounds__(256) void affine_scan(ScanArgs a) {
   const float* rec0 = a.summary + bh * a.W;
   float* out0 = a.out + bh * per + e;
 
+  const int32_t* slice = a.slice ? a.slice + (bh / a.H) * a.P : nullptr;   // row b's rank slices
   float run = a.init ? a.init[bh * per + e] : 0.f;
   for (int s0 = 0; s0 < a.P; s0 += BATCH) {
     float m[BATCH], x[BATCH];
@@ -49,7 +51,7 @@ __global__ __launch_bounds__(256) void affine_scan(ScanArgs a) {
       const int s = s0 + j;
       if (s < a.P) {
         const int q = a.reverse ? a.P - 1 - s : s;
-        if (s > 0 && a.slice && a.slice[q] == (a.reverse ? q + 1 : q)) run = 0.f;
+        if (s > 0 && slice && slice[q] == (a.reverse ? q + 1 : q)) run = 0.f;
         out0[q * out_stride] = run;
         run = m[j] * run + x[j];
       }

@@ -64,7 +64,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;
 
-#define CPLA_ABI_VERSION 2
+#define CPLA_ABI_VERSION 3
 
 typedef enum {
   CPLA_OK = 0,
@@ -81,7 +81,8 @@ typedef enum { CPLA_F32 = 0, CPLA_BF16 = 1 } cpla_dtype;
 typedef enum { CPLA_DECAY_NONE = 0, CPLA_DECAY_SCALAR = 1, CPLA_DECAY_DIAG = 2 } cpla_decay;
 
 typedef struct {
-  int64_t B, T, H, dk, dv;   /* packed sequences: B == 1 and T is the stream length   */
+  int64_t B, T, H, dk, dv;   /* packed sequences: each of the B rows is a stream of T
+                                tokens with its own packing                           */
   int32_t num_shards;        /* P <= 64 shards of any T: torch.chunk's division (shard
                                 size ceil(T/P), the last non-empty shard shorter, trailing
                                 shards empty when T is short; a shard's last chunk may be
@@ -95,12 +96,16 @@ typedef struct {
 
 /* Packed sequences. Passing NULL for the whole struct means "not packed": every
  * row is one sequence that starts from S_init, the forward prefix of rank r is
- * [0, r) and the backward suffix is (r, P). Device pointers. */
+ * [0, r) and the backward suffix is (r, P). Device pointers, row-major with one
+ * row per batch row b: each row is packed on its own (B == 1 is the usual
+ * single packed stream), and its slices are those cpla_packed_rank_slices gives
+ * for that row's ids. */
 typedef struct {
-  const int32_t* seq_idx;               /* [T] global sequence id of each token (>= 0,
-                                           as cpla_seq_idx_from_cu_seqlens writes) */
-  const int32_t* preceding_rank_start;  /* [P] inclusive start of rank r's prefix      */
-  const int32_t* following_rank_stop;   /* [P] exclusive end of rank r's suffix        */
+  const int32_t* seq_idx;               /* [B, T] global sequence id of each token in
+                                           its row (>= 0, as cpla_seq_idx_from_cu_seqlens
+                                           writes)                                       */
+  const int32_t* preceding_rank_start;  /* [B, P] inclusive start of rank r's prefix   */
+  const int32_t* following_rank_stop;   /* [B, P] exclusive end of rank r's suffix     */
 } cpla_packed;
 
 /* Floats per (shard, b, h) summary record: m_slot + dk*dv (see layout above). */

@@ -48,6 +48,14 @@ def seq_idx_from_cu_seqlens(cu_seqlens, T):
     return out
 
 
+def seq_idx_rows(cu_seqlens, T):
+    """[T] ids from one cu_seqlens, or [B, T] from a list of B of them (one
+    packing per batch row)."""
+    if isinstance(cu_seqlens, (list, tuple)) and len(cu_seqlens) and np.ndim(cu_seqlens[0]) == 1:
+        return np.stack([seq_idx_from_cu_seqlens(np.asarray(c), T) for c in cu_seqlens])
+    return seq_idx_from_cu_seqlens(np.asarray(cu_seqlens), T)
+
+
 def validate_global_seq_idx(global_seq_idx, cp_size):
     s = [int(x) for x in np.asarray(global_seq_idx).tolist()]
     T = len(s)

@@ -81,7 +81,7 @@ def oracle_run(wl, backward=True, heads=None, d_final_state=None):
     dSf = d_final_state if (d_final_state is None or heads is None) else d_final_state[:, heads]
     seq = None
     if wl.cu_seqlens is not None:
-        seq = omd.seq_idx_from_cu_seqlens(wl.cu_seqlens.numpy(), wl.T)
+        seq = omd.seq_idx_rows(wl.cu_seqlens, wl.T)
     if backward:
         dO = _rows(wl.dO, heads)
         r = ocp.cp_backward(q, k, v, g, wl.decay, dO, wl.num_shards, initial_state=S0, seq_idx=seq,

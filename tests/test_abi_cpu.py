@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert L.cpla_abi_version() == 2
+    assert L.cpla_abi_version() == 3
 
 
 def prob(**kw):
@@ -75,9 +75,10 @@ def test_pointer_validation():
 
 def test_packed_validation():
     pk = Packed(FAKE, FAKE, FAKE)
-    assert fwd_prepare(prob(B=2), packed=ctypes.byref(pk)) == 2     # packed needs B == 1
     assert fwd_prepare(prob(), packed=ctypes.byref(Packed(None, FAKE, FAKE))) == 1
-    p = prob()
+    # B > 1 is accepted (one packing per row): the checks reach the same errors
+    assert fwd_prepare(prob(B=2), packed=ctypes.byref(Packed(None, FAKE, FAKE))) == 1
+    p = prob(B=3)
     # initial_state with packed sequences
     st = L.cp_forward_apply(ctypes.byref(p), ctypes.byref(pk), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                             FAKE, FAKE, None)
@@ -201,3 +202,24 @@ def test_product_does_not_use_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), f
                 assert "oracle/" not in text, f
+
+
+def test_per_row_packed_metadata_matches_oracle():
+    """packed_meta with one cu_seqlens per batch row: [B, T] ids and [B, P] slices,
+    each row equal to the oracle's metadata for that row alone."""
+    from context_state_passing_amd.api import packed_meta
+    T, P = 300, 7
+    cus = [[0, 5, 120, 300], [0, 300], [0, 1, 2, 3, 299, 300]]
+    m = packed_meta(cus, T, P, "cpu", B=3)
+    assert tuple(m.seq_idx.shape) == (3, T) and tuple(m.preceding_rank_start.shape) == (3, P)
+    for b, cu in enumerate(cus):
+        s = omd.seq_idx_from_cu_seqlens(np.array(cu), T)
+        prs, frs = omd.rank_slices(s, P)
+        assert np.array_equal(m.seq_idx[b].numpy(), s)
+        assert np.array_equal(m.preceding_rank_start[b].numpy(), prs)
+        assert np.array_equal(m.following_rank_stop[b].numpy(), frs)
+    assert np.array_equal(omd.seq_idx_rows(cus, T), m.seq_idx.numpy())
+    one = packed_meta(np.array(cus[0]), T, P, "cpu")
+    assert tuple(one.seq_idx.shape) == (1, T)
+    with pytest.raises(cpla.CplaError):
+        packed_meta(cus, T, P, "cpu", B=2)

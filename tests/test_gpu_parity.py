@@ -82,6 +82,23 @@ SMALL = {
     "uneven_diag_d16_fp32_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 300, "d": 16, "num_shards": 4,
                                                  "dtype": torch.float32}, True),
     "uneven_long_init_bwd": ("long_fwdbwd", {"T": 777, "H": 2, "num_shards": 3}, True),
+    # one packing per batch row: rows with different boundaries (and slices); with
+    # uneven shards and sequences of 1..200 tokens; the diagonal decay packed
+    "rows_packed_bwd": ("packed_fwdbwd", {"B": 3, "T": 1024, "H": 2, "num_shards": 4, "len_range": (40, 400)},
+                        True),
+    "rows_packed_uneven_bwd": ("packed_fwdbwd", {"B": 2, "T": 1000, "H": 2, "num_shards": 5,
+                                                 "len_range": (1, 200)}, True),
+    "rows_packed_diag_bwd": ("diag_fwdbwd", {"B": 2, "T": 768, "H": 2, "num_shards": 4, "packed": True,
+                                             "len_range": (30, 300)}, True),
+    # the diagonal decay over packed sequences: one stream, bf16 d_k 128 / fp32 d_k 64,
+    # and a single sequence (its only start is token 0)
+    "packed_diag_bwd": ("diag_fwdbwd", {"B": 1, "T": 1024, "H": 2, "num_shards": 4, "packed": True,
+                                        "len_range": (30, 300)}, True),
+    "packed_diag_d64_fp32_bwd": ("diag_fwdbwd", {"B": 1, "T": 512, "H": 2, "d": 64, "num_shards": 2,
+                                                 "packed": True, "len_range": (20, 200),
+                                                 "dtype": torch.float32}, True),
+    "packed_diag_one_seq_bwd": ("diag_fwdbwd", {"B": 1, "T": 256, "H": 1, "d": 64, "num_shards": 1,
+                                                "packed": True, "len_range": (256, 256)}, True),
 }
 
 

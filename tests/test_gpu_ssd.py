@@ -35,6 +35,7 @@ CASES = {
     "fp32_n64_init": dict(B=1, T=384, H=2, G=1, N=64, num_shards=3, dtype=torch.float32,
                           with_initial_state=True),
     "bf16_n64_uneven": dict(B=1, T=1000, H=4, G=2, N=64, num_shards=3),
+    "bf16_n64_rows_packed": dict(B=2, T=512, H=4, G=2, N=64, num_shards=4, packed=True, len_range=(40, 300)),
 }
 
 
@@ -60,7 +61,7 @@ def _run_gpu(wl):
 def _run_oracle(wl):
     seq = None
     if wl.cu_seqlens is not None:
-        seq = omd.seq_idx_from_cu_seqlens(wl.cu_seqlens.numpy(), wl.T)
+        seq = omd.seq_idx_rows(wl.cu_seqlens, wl.T)
     args = [_np(t) for t in (wl.x, wl.dt, wl.A, wl.Bm, wl.Cm)]
     h0 = _np(wl.initial_state)
     y, _ = ossd.ssd_forward(*args, h_init=h0, seq_idx=seq)
@@ -92,7 +93,7 @@ def _ddt_term_scale(wl):
     """|dw| + |A dg| per (b, t, h) from the linear-attention oracle under the SSD map."""
     seq = None
     if wl.cu_seqlens is not None:
-        seq = omd.seq_idx_from_cu_seqlens(wl.cu_seqlens.numpy(), wl.T)
+        seq = omd.seq_idx_rows(wl.cu_seqlens, wl.T)
     x, dt, A, Bm, Cm = (_np(t) for t in (wl.x, wl.dt, wl.A, wl.Bm, wl.Cm))
     grp = np.arange(wl.H) // (wl.H // wl.G)
     g = A[None, None, :] * dt
@@ -139,7 +140,7 @@ def test_weighted_parity(case, gpu_available):
                           initial_state=S0, cu_seqlens=wl.cu_seqlens, w=w.to(dev))
     dq, dk, dv, dg, dS0, dw = cpla.backward(wl.dO.to(dev), ctx)
     torch.cuda.synchronize()
-    seq = None if wl.cu_seqlens is None else omd.seq_idx_from_cu_seqlens(wl.cu_seqlens.numpy(), wl.T)
+    seq = None if wl.cu_seqlens is None else omd.seq_idx_rows(wl.cu_seqlens, wl.T)
     args = [_np(t) for t in (wl.q, wl.k, wl.v, wl.g)]
     ref_o, ref_S = orec.forward(*args, "scalar", initial_state=_np(wl.initial_state), seq_idx=seq, w=_np(w))
     ref = orec.backward(*args, "scalar", dO=_np(wl.dO), initial_state=_np(wl.initial_state), seq_idx=seq,

@@ -28,6 +28,19 @@ def test_packed_lengths():
     assert all(128 <= n <= 4096 for n in lens[:-1]) and 1 <= lens[-1] <= 4096
 
 
+def test_per_row_packing():
+    wl = workloads.make("packed_fwdbwd", B=3, H=1, T=1000, len_range=(10, 300))
+    assert isinstance(wl.cu_seqlens, list) and len(wl.cu_seqlens) == 3
+    for cu in wl.cu_seqlens:
+        c = cu.tolist()
+        assert c[0] == 0 and c[-1] == 1000 and all(b > a for a, b in zip(c[:-1], c[1:]))
+    assert wl.cu_seqlens[0].tolist() != wl.cu_seqlens[1].tolist()
+    d = workloads.make("diag_fwdbwd", B=2, T=512, H=1, packed=True, len_range=(30, 300))
+    assert len(d.cu_seqlens) == 2
+    s = workloads.make_ssd(B=2, T=512, packed=True, len_range=(40, 300))
+    assert len(s.cu_seqlens) == 2
+
+
 def test_seeded_and_scaled():
     a = workloads.make("scalar_fwd", T=256, H=1, B=1)
     b = workloads.make("scalar_fwd", T=256, H=1, B=1)

@@ -89,7 +89,7 @@ class Workload:
     g: Optional[torch.Tensor]
     dO: Optional[torch.Tensor]
     initial_state: Optional[torch.Tensor]
-    cu_seqlens: Optional[torch.Tensor]   # int32 [N+1] (packed only)
+    cu_seqlens: Optional[object]         # packed only: int32 [N+1] (B == 1), or a list of B of them
 
     @property
     def tokens(self) -> int:
@@ -111,12 +111,20 @@ def _lengths(gen: torch.Generator, T: int, lo: int, hi: int) -> torch.Tensor:
     return torch.tensor(cu, dtype=torch.int32)
 
 
+def _packing(gen: torch.Generator, B: int, T: int, lo: int, hi: int):
+    """One packed stream (B == 1) or one packing per batch row, each of T tokens."""
+    if B == 1:
+        return _lengths(gen, T, lo, hi)
+    return [_lengths(gen, T, lo, hi) for _ in range(B)]
+
+
 def make(name: str, *, B: Optional[int] = None, T: Optional[int] = None,
          H: Optional[int] = None, d: Optional[int] = None,
          num_shards: Optional[int] = None, decay_scale: float = 1.0,
          seed_offset: int = 0, len_range: Optional[tuple] = None,
          with_initial_state: Optional[bool] = None,
-         backward: Optional[bool] = None, dtype: Optional[torch.dtype] = None) -> Workload:
+         backward: Optional[bool] = None, dtype: Optional[torch.dtype] = None,
+         packed: Optional[bool] = None) -> Workload:
     spec = SPECS[name]
     B = spec.B if B is None else B
     T = spec.T if T is None else T
@@ -128,9 +136,9 @@ def make(name: str, *, B: Optional[int] = None, T: Optional[int] = None,
     gen = torch.Generator().manual_seed(1000 + spec.index + seed_offset)
 
     cu = None
-    if spec.packed:
+    if spec.packed if packed is None else packed:
         lo, hi = (128, 4096) if len_range is None else len_range
-        cu = _lengths(gen, B * T, lo, hi)
+        cu = _packing(gen, B, T, lo, hi)
 
     def randn(*shape):
         return torch.randn(*shape, generator=gen, dtype=torch.float32)
@@ -215,7 +223,7 @@ class SsdWorkload:
     Cm: torch.Tensor
     dy: torch.Tensor
     initial_state: Optional[torch.Tensor]
-    cu_seqlens: Optional[torch.Tensor]
+    cu_seqlens: Optional[object]         # as Workload.cu_seqlens
 
     @property
     def tokens(self) -> int:
@@ -235,7 +243,7 @@ def make_ssd(name: str = "ssd_fwdbwd", *, B: Optional[int] = None, T: Optional[i
     N = spec.N if N is None else N
     P = spec.num_shards if num_shards is None else num_shards
     gen = torch.Generator().manual_seed(1000 + spec.index + seed_offset)
-    cu = _lengths(gen, B * T, len_range[0], len_range[1]) if packed else None
+    cu = _packing(gen, B, T, len_range[0], len_range[1]) if packed else None
 
     def randn(*shape):
         return torch.randn(*shape, generator=gen, dtype=torch.float32)
