@@ -6,7 +6,8 @@ library and fails loudly if it has not been built.
 """
 from ._lib import CplaError, lib  # noqa: F401
 from .api import (  # noqa: F401
-    Context, PackedMeta, SsdContext, backward, build_packed_sequence_cp_metadata, chunkwise_linear_attention,
-    forward, mamba2_ssd, packed_meta, packed_rank_slices, seq_idx_from_cu_seqlens, ssd_backward, ssd_forward)
+    Context, DeltaContext, PackedMeta, SsdContext, backward, build_packed_sequence_cp_metadata,
+    chunkwise_linear_attention, delta_backward, delta_forward, forward, gated_delta_rule, mamba2_ssd, packed_meta,
+    packed_rank_slices, seq_idx_from_cu_seqlens, ssd_backward, ssd_forward)
 
 lib()

@@ -12,7 +12,7 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcpla.so")
 
 F32, BF16 = 0, 1
-DECAY_NONE, DECAY_SCALAR, DECAY_DIAG = 0, 1, 2
+DECAY_NONE, DECAY_SCALAR, DECAY_DIAG, DECAY_DELTA = 0, 1, 2, 3
 STATUS = {0: "OK", 1: "INVALID", 2: "SHAPE", 3: "DTYPE", 4: "ALIGN", 5: "UNSUPPORTED", 6: "METADATA", 7: "HIP"}
 
 # every function the header include/cpla.h declares
@@ -21,7 +21,8 @@ EXPORTS = [
     "cp_backward_prepare", "cp_backward_apply", "build_packed_sequence_cp_metadata",
     "cpla_packed_rank_slices", "cpla_seq_idx_from_cu_seqlens", "cpla_last_error", "cpla_abi_version",
     "cpla_ssd_inputs", "cpla_ssd_input_grads", "cp_forward_prepare_weighted", "cp_forward_apply_weighted",
-    "cp_backward_apply_weighted",
+    "cp_backward_apply_weighted", "cpla_delta_workspace_bytes", "cp_forward_prepare_delta",
+    "cp_forward_apply_delta", "cp_backward_prepare_delta", "cp_backward_apply_delta",
 ]
 
 
@@ -87,6 +88,15 @@ def lib() -> ctypes.CDLL:
         L.cp_forward_apply_weighted.argtypes = [P, PK, V, V, V, V, V, V, V, V, V, V, V, V]
         L.cp_backward_apply_weighted.argtypes = [P, PK, V, V, V, V, V, V, V, V, V, V, V, V, V, V, V, V, I32, V]
         for fn in ["cp_forward_prepare_weighted", "cp_forward_apply_weighted", "cp_backward_apply_weighted"]:
+            getattr(L, fn).restype = ctypes.c_int
+        L.cpla_delta_workspace_bytes.argtypes = [P]
+        L.cpla_delta_workspace_bytes.restype = ctypes.c_int64
+        L.cp_forward_prepare_delta.argtypes = [P, PK] + [V] * 7
+        L.cp_forward_apply_delta.argtypes = [P, PK] + [V] * 12
+        L.cp_backward_prepare_delta.argtypes = [P, PK] + [V] * 9
+        L.cp_backward_apply_delta.argtypes = [P, PK] + [V] * 17
+        for fn in ["cp_forward_prepare_delta", "cp_forward_apply_delta", "cp_backward_prepare_delta",
+                   "cp_backward_apply_delta"]:
             getattr(L, fn).restype = ctypes.c_int
         L.cpla_last_error.restype = ctypes.c_char_p
         L.cpla_abi_version.restype = ctypes.c_int

@@ -345,3 +345,106 @@ class Mamba2SSD(torch.autograd.Function):
 
 def mamba2_ssd(x, dt, A, B, C, initial_state=None, *, num_shards: int = 1, cu_seqlens=None):
     return Mamba2SSD.apply(x, dt, A, B, C, initial_state, num_shards, cu_seqlens)
+
+
+# ---- the gated delta rule (dense transition) ---------------------------------------------
+
+@dataclasses.dataclass
+class DeltaContext:
+    problem: Problem
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+    packed: Optional[PackedMeta]
+    fwd_summary: torch.Tensor
+    shard_in_state: torch.Tensor
+    final_state: torch.Tensor
+    workspace: torch.Tensor             # the local context of the four calls (fp32 scratch)
+    has_initial_state: bool
+
+
+def delta_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, *,
+                  num_shards: int, initial_state: Optional[torch.Tensor] = None, cu_seqlens=None,
+                  packed: Optional[PackedMeta] = None):
+    """Gated delta rule o [B,T,H,d] and a DeltaContext: S_t = exp(g_t)(I - beta_t k_t k_t^T) S_{t-1}
+    + beta_t k_t v_t^T, o_t = S_t^T q_t; g, beta [B,T,H] fp32."""
+    for t in (q, k, v, g, beta, initial_state):
+        if t is not None and not t.is_contiguous():
+            raise CplaError(1, "inputs must be contiguous")
+    p = make_problem(q, v, num_shards, _lib.DECAY_DELTA)
+    if cu_seqlens is not None and packed is None:
+        packed = packed_meta(cu_seqlens, q.shape[1], num_shards, q.device, q.shape[0])
+    L = _lib.lib()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    nb = L.cpla_delta_workspace_bytes(ctypes.byref(p))
+    if nb < 0:
+        check(L.cp_forward_prepare_delta(ctypes.byref(p), None, None, None, None, None, None, None, None))
+    dev = q.device
+    W = L.cpla_summary_width(ctypes.byref(p))
+    ws = torch.empty((nb // 4,), device=dev, dtype=torch.float32)
+    fsum = torch.empty((num_shards, B, H, W), device=dev, dtype=torch.float32)
+    s_in = torch.empty((num_shards, B, H, dk, dv), device=dev, dtype=torch.float32)
+    fin = torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+    o = torch.empty(v.shape, device=dev, dtype=q.dtype)
+    pk = ctypes.byref(packed.c()) if packed is not None else None
+    st = _stream()
+    check(L.cp_forward_prepare_delta(ctypes.byref(p), pk, _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(fsum),
+                                     _ptr(ws), st))
+    check(L.cp_forward_apply_delta(ctypes.byref(p), pk, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(fsum),
+                                   _ptr(initial_state), _ptr(o), _ptr(s_in), _ptr(fin), _ptr(ws), st))
+    return o, DeltaContext(p, q, k, v, g, beta, packed, fsum, s_in, fin, ws, initial_state is not None)
+
+
+def delta_backward(dO: torch.Tensor, ctx: DeltaContext, d_final_state: Optional[torch.Tensor] = None,
+                   want_intermediates: bool = False):
+    """(dq, dk, dv, dg, dbeta, d_initial_state); d_initial_state is None with packed sequences."""
+    if not dO.is_contiguous():
+        raise CplaError(1, "dO must be contiguous")
+    L = _lib.lib()
+    p = ctx.problem
+    B, T, H, dk = ctx.q.shape
+    dv = ctx.v.shape[-1]
+    P = p.num_shards
+    dev = dO.device
+    W = L.cpla_summary_width(ctypes.byref(p))
+    bsum = torch.empty((P, B, H, W), device=dev, dtype=torch.float32)
+    s_out = torch.empty((P, B, H, dk, dv), device=dev, dtype=torch.float32)
+    dq, dk_, dv_ = torch.empty_like(ctx.q), torch.empty_like(ctx.k), torch.empty_like(ctx.v)
+    dg, db = torch.empty_like(ctx.g), torch.empty_like(ctx.beta)
+    dS0 = None if ctx.packed is not None else torch.empty((B, H, dk, dv), device=dev, dtype=torch.float32)
+    pk = ctypes.byref(ctx.packed.c()) if ctx.packed is not None else None
+    st = _stream()
+    check(L.cp_backward_prepare_delta(ctypes.byref(p), pk, _ptr(ctx.q), _ptr(ctx.k), _ptr(ctx.g), _ptr(ctx.beta),
+                                      _ptr(dO), _ptr(ctx.fwd_summary), _ptr(bsum), _ptr(ctx.workspace), st))
+    check(L.cp_backward_apply_delta(ctypes.byref(p), pk, _ptr(ctx.q), _ptr(ctx.k), _ptr(ctx.v), _ptr(ctx.g),
+                                    _ptr(ctx.beta), _ptr(dO), _ptr(bsum), _ptr(d_final_state), _ptr(dq), _ptr(dk_),
+                                    _ptr(dv_), _ptr(dg), _ptr(db), _ptr(s_out), _ptr(dS0), _ptr(ctx.workspace), st))
+    res = (dq, dk_, dv_, dg, db, dS0)
+    if want_intermediates:
+        return res, {"bwd_summary": bsum, "shard_out_grad": s_out}
+    return res
+
+
+class GatedDeltaRule(torch.autograd.Function):
+    """Autograd adapter for the gated delta rule, shards simulated on one GPU."""
+
+    @staticmethod
+    def forward(fctx, q, k, v, g, beta, initial_state, num_shards, cu_seqlens):
+        o, c = delta_forward(q, k, v, g, beta, num_shards=num_shards, initial_state=initial_state,
+                             cu_seqlens=cu_seqlens)
+        fctx.cpla = c
+        return o
+
+    @staticmethod
+    def backward(fctx, dO):
+        dq, dk, dv, dg, db, dS0 = delta_backward(dO.contiguous(), fctx.cpla)
+        if not fctx.cpla.has_initial_state:
+            dS0 = None
+        return dq, dk, dv, dg, db, dS0, None, None
+
+
+def gated_delta_rule(q, k, v, g, beta, initial_state=None, *, num_shards: int = 1, cu_seqlens=None):
+    return GatedDeltaRule.apply(q, k, v, g, beta, initial_state, num_shards, cu_seqlens)

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcpla.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["abi.hip", "fwd.hip", "bwd.hip", "scan.hip", "ssd.hip", "metadata.cpp"]
+SOURCES = ["abi.hip", "fwd.hip", "bwd.hip", "scan.hip", "ssd.hip", "delta.hip", "metadata.cpp"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -35,6 +35,7 @@ cpla_status check_problem(const cpla_problem* p) {
   if (p->B <= 0 || p->T <= 0 || p->H <= 0 || p->dk <= 0 || p->dv <= 0)
     return fail(CPLA_E_SHAPE, "B, T, H, dk, dv must be positive");
   if (p->dtype != CPLA_F32 && p->dtype != CPLA_BF16) return fail(CPLA_E_DTYPE, "unknown dtype %d", p->dtype);
+  if (p->decay == CPLA_DECAY_DELTA) return fail(CPLA_E_INVALID, "the delta rule goes through the _delta calls");
   if (p->decay < CPLA_DECAY_NONE || p->decay > CPLA_DECAY_DIAG) return fail(CPLA_E_INVALID, "unknown decay %d", p->decay);
   if (p->chunk != 64) return fail(CPLA_E_UNSUPPORTED, "chunk %d unsupported (64 only)", p->chunk);
   if (p->num_shards <= 0) return fail(CPLA_E_SHAPE, "num_shards must be positive");
@@ -188,6 +189,7 @@ extern "C" int cpla_abi_version(void) { return CPLA_ABI_VERSION; }
 
 extern "C" int64_t cpla_summary_width(const cpla_problem* p) {
   if (!p) return -1;
+  if (p->decay == CPLA_DECAY_DELTA) return p->dk * p->dk + p->dk * p->dv;   // [M | delta_S or gamma]
   return m_slot_of(p) + p->dk * p->dv;
 }
 
@@ -384,4 +386,223 @@ extern "C" cpla_status cp_backward_apply_weighted(const cpla_problem* p, const c
                                                   int32_t grad_dtype, hipStream_t stream) {
   return backward_apply(p, packed, q, k, v, g, w, dO, chunk_states, bwd_summary, d_final_state, dq, dk, dv, dg, dw,
                         shard_out_grad, d_initial_state, grad_dtype, stream);
+}
+
+// ---- the gated delta rule (dense transition) ------------------------------------------------
+namespace cpla {
+namespace {
+
+cpla_status check_delta(const cpla_problem* p) {
+  if (!p) return fail(CPLA_E_INVALID, "problem is NULL");
+  if (p->B <= 0 || p->T <= 0 || p->H <= 0 || p->dk <= 0 || p->dv <= 0)
+    return fail(CPLA_E_SHAPE, "B, T, H, dk, dv must be positive");
+  if (p->dtype != CPLA_F32 && p->dtype != CPLA_BF16) return fail(CPLA_E_DTYPE, "unknown dtype %d", p->dtype);
+  if (p->decay != CPLA_DECAY_DELTA) return fail(CPLA_E_INVALID, "the _delta calls need decay CPLA_DECAY_DELTA");
+  if (p->chunk != 64) return fail(CPLA_E_UNSUPPORTED, "chunk %d unsupported (64 only)", p->chunk);
+  if (p->num_shards <= 0) return fail(CPLA_E_SHAPE, "num_shards must be positive");
+  if (p->num_shards > 64) return fail(CPLA_E_UNSUPPORTED, "num_shards=%d > 64 unsupported", p->num_shards);
+  if (p->rank_begin < 0 || p->rank_end > p->num_shards || p->rank_begin >= p->rank_end)
+    return fail(CPLA_E_INVALID, "rank range [%d, %d) outside [0, %d)", p->rank_begin, p->rank_end, p->num_shards);
+  if (p->dk != p->dv) return fail(CPLA_E_UNSUPPORTED, "dk != dv unsupported");
+  if (!(p->dk == 16 || p->dk == 32 || p->dk == 64))
+    return fail(CPLA_E_UNSUPPORTED, "head dim %lld unsupported for the delta rule (16, 32, 64)", (long long)p->dk);
+  if (p->B * p->H > 65535) return fail(CPLA_E_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)(p->B * p->H));
+  return CPLA_OK;
+}
+
+// workspace: U~, W, U, dU [B,T,H,D] then the chunk states and chunk-end gradients
+// [B,H,row_chunks,D,D], all fp32
+int64_t delta_ws_floats(const cpla_problem* p) {
+  const int64_t tok = p->B * p->T * p->H * p->dk, ch = p->B * p->H * row_chunks(p->T, p->num_shards) * p->dk * p->dk;
+  return 4 * tok + 2 * ch;
+}
+
+void bind_ws(const cpla_problem* p, void* ws, DeltaArgs& a) {
+  const int64_t tok = p->B * p->T * p->H * p->dk, ch = p->B * p->H * row_chunks(p->T, p->num_shards) * p->dk * p->dk;
+  float* f = static_cast<float*>(ws);
+  a.ws_ut = f;
+  a.ws_w = f + tok;
+  a.ws_u = f + 2 * tok;
+  a.ws_du = f + 3 * tok;
+  a.chunk_states = f + 4 * tok;
+  a.ws_dsc = f + 4 * tok + ch;
+}
+
+DeltaArgs delta_args(const cpla_problem* p, const cpla_packed* packed, void* ws) {
+  DeltaArgs a = {};
+  a.B = p->B; a.T = p->T; a.H = p->H;
+  a.P = p->num_shards; a.rank_begin = p->rank_begin;
+  const int64_t nsc = chunks_of(shard_size(p->T, p->num_shards));
+  a.chunk_begin = p->rank_begin * nsc;
+  a.seq_idx = packed ? packed->seq_idx : nullptr;
+  bind_ws(p, ws, a);
+  return a;
+}
+
+// chunks of the launch's ranks (row-local indices [chunk_begin, chunk_end))
+unsigned delta_chunks(const cpla_problem* p) {
+  const int64_t nsc = chunks_of(shard_size(p->T, p->num_shards));
+  int64_t end = (int64_t)p->rank_end * nsc;
+  const int64_t nct = row_chunks(p->T, p->num_shards);
+  if (end > nct) end = nct;
+  const int64_t beg = (int64_t)p->rank_begin * nsc;
+  return (unsigned)(end > beg ? end - beg : 0);
+}
+
+enum DeltaPhase { DP_FWD_PREPARE, DP_FWD_APPLY_WALK, DP_FWD_OUT, DP_BWD_PREPARE, DP_BWD_APPLY_WALK, DP_BWD_GRAD };
+
+template <typename E, int D>
+void delta_launch(DeltaPhase ph, const cpla_problem* p, const DeltaArgs& a, hipStream_t stream) {
+  const dim3 ranks(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), chunks(delta_chunks(p), (unsigned)(p->B * p->H));
+  const dim3 nt(256);
+  switch (ph) {
+    case DP_FWD_PREPARE:
+      if (chunks.x) hipLaunchKernelGGL((delta_wy<E, D>), chunks, nt, 0, stream, a);
+      hipLaunchKernelGGL((delta_fwalk<E, D, false>), ranks, nt, 0, stream, a);
+      break;
+    case DP_FWD_APPLY_WALK: hipLaunchKernelGGL((delta_fwalk<E, D, true>), ranks, nt, 0, stream, a); break;
+    case DP_FWD_OUT:
+      if (chunks.x) hipLaunchKernelGGL((delta_out<E, D>), chunks, nt, 0, stream, a);
+      break;
+    case DP_BWD_PREPARE: hipLaunchKernelGGL((delta_bwalk<E, D, false>), ranks, nt, 0, stream, a); break;
+    case DP_BWD_APPLY_WALK: hipLaunchKernelGGL((delta_bwalk<E, D, true>), ranks, nt, 0, stream, a); break;
+    case DP_BWD_GRAD:
+      if (chunks.x) hipLaunchKernelGGL((delta_grad<E, D>), chunks, nt, 0, stream, a);
+      break;
+  }
+}
+
+template <typename E>
+void delta_launch_d(DeltaPhase ph, const cpla_problem* p, const DeltaArgs& a, hipStream_t stream) {
+  if (p->dk == 16) delta_launch<E, 16>(ph, p, a, stream);
+  else if (p->dk == 32) delta_launch<E, 32>(ph, p, a, stream);
+  else delta_launch<E, 64>(ph, p, a, stream);
+}
+
+cpla_status delta_run(DeltaPhase ph, const cpla_problem* p, const DeltaArgs& a, hipStream_t stream, const char* what) {
+  if (p->dtype == CPLA_BF16) delta_launch_d<bf16_t>(ph, p, a, stream);
+  else delta_launch_d<float>(ph, p, a, stream);
+  return launched(what);
+}
+
+cpla_status delta_scan_run(const cpla_problem* p, const float* summary, const int32_t* slice, const float* init,
+                           float* out, float* fin, int reverse, hipStream_t stream) {
+  DeltaScanArgs s = {};
+  s.BH = p->B * p->H;
+  s.H = p->H;
+  s.P = p->num_shards;
+  s.reverse = reverse;
+  s.summary = summary;
+  s.slice = slice;
+  s.init = init;
+  s.out = out;
+  s.fin = fin;
+  const dim3 grid((unsigned)s.BH);
+  if (p->dk == 16) hipLaunchKernelGGL(delta_scan<16>, grid, dim3(256), 0, stream, s);
+  else if (p->dk == 32) hipLaunchKernelGGL(delta_scan<32>, grid, dim3(256), 0, stream, s);
+  else hipLaunchKernelGGL(delta_scan<64>, grid, dim3(256), 0, stream, s);
+  return launched("delta_scan");
+}
+
+}  // namespace
+}  // namespace cpla
+
+extern "C" int64_t cpla_delta_workspace_bytes(const cpla_problem* p) {
+  if (check_delta(p) != CPLA_OK) return -1;
+  return delta_ws_floats(p) * (int64_t)sizeof(float);
+}
+
+extern "C" cpla_status cp_forward_prepare_delta(const cpla_problem* p, const cpla_packed* packed, const void* k,
+                                                const void* v, const float* g, const float* beta,
+                                                float* fwd_summary, void* workspace, hipStream_t stream) {
+  clear_error();
+  cpla_status st;
+  if ((st = check_delta(p)) != CPLA_OK) return st;
+  if ((st = check_packed(p, packed, false, false)) != CPLA_OK) return st;
+  if ((st = check_ptr(k, "k", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(v, "v", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(g, "g", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(beta, "beta", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(fwd_summary, "fwd_summary", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(workspace, "workspace", true)) != CPLA_OK) return st;
+  DeltaArgs a = delta_args(p, packed, workspace);
+  a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.summary = fwd_summary;
+  return delta_run(DP_FWD_PREPARE, p, a, stream, "cp_forward_prepare_delta");
+}
+
+extern "C" cpla_status cp_forward_apply_delta(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                              const void* k, const void* v, const float* g, const float* beta,
+                                              const float* fwd_summary, const float* initial_state, void* o,
+                                              float* shard_in_state, float* final_state, void* workspace,
+                                              hipStream_t stream) {
+  clear_error();
+  cpla_status st;
+  if ((st = check_delta(p)) != CPLA_OK) return st;
+  if ((st = check_packed(p, packed, true, false)) != CPLA_OK) return st;
+  const void* req[] = {q, k, v, g, beta, fwd_summary, o, shard_in_state, workspace};
+  const char* names[] = {"q", "k", "v", "g", "beta", "fwd_summary", "o", "shard_in_state", "workspace"};
+  for (int i = 0; i < 9; ++i)
+    if ((st = check_ptr(req[i], names[i], true)) != CPLA_OK) return st;
+  if ((st = check_ptr(initial_state, "initial_state", false)) != CPLA_OK) return st;
+  if ((st = check_ptr(final_state, "final_state", false)) != CPLA_OK) return st;
+  if (packed && initial_state) return fail(CPLA_E_INVALID, "initial_state must be NULL with packed sequences");
+  st = delta_scan_run(p, fwd_summary, packed ? packed->preceding_rank_start : nullptr, initial_state, shard_in_state,
+                      final_state, 0, stream);
+  if (st != CPLA_OK) return st;
+  DeltaArgs a = delta_args(p, packed, workspace);
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta;
+  a.state_in = shard_in_state;
+  a.out = o;
+  if ((st = delta_run(DP_FWD_APPLY_WALK, p, a, stream, "cp_forward_apply_delta (walk)")) != CPLA_OK) return st;
+  return delta_run(DP_FWD_OUT, p, a, stream, "cp_forward_apply_delta (output)");
+}
+
+extern "C" cpla_status cp_backward_prepare_delta(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                                 const void* k, const float* g, const float* beta, const void* dO,
+                                                 const float* fwd_summary, float* bwd_summary, void* workspace,
+                                                 hipStream_t stream) {
+  clear_error();
+  cpla_status st;
+  if ((st = check_delta(p)) != CPLA_OK) return st;
+  if ((st = check_packed(p, packed, false, false)) != CPLA_OK) return st;
+  const void* req[] = {q, k, g, beta, dO, fwd_summary, bwd_summary, workspace};
+  const char* names[] = {"q", "k", "g", "beta", "dO", "fwd_summary", "bwd_summary", "workspace"};
+  for (int i = 0; i < 8; ++i)
+    if ((st = check_ptr(req[i], names[i], true)) != CPLA_OK) return st;
+  DeltaArgs a = delta_args(p, packed, workspace);
+  a.q = q; a.k = k; a.g = g; a.beta = beta; a.dO = dO;
+  a.fwd_summary = fwd_summary;
+  a.summary = bwd_summary;
+  return delta_run(DP_BWD_PREPARE, p, a, stream, "cp_backward_prepare_delta");
+}
+
+extern "C" cpla_status cp_backward_apply_delta(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                               const void* k, const void* v, const float* g, const float* beta,
+                                               const void* dO, const float* bwd_summary,
+                                               const float* d_final_state, void* dq, void* dk, void* dv, float* dg,
+                                               float* dbeta, float* shard_out_grad, float* d_initial_state,
+                                               void* workspace, hipStream_t stream) {
+  clear_error();
+  cpla_status st;
+  if ((st = check_delta(p)) != CPLA_OK) return st;
+  if ((st = check_packed(p, packed, false, true)) != CPLA_OK) return st;
+  const void* req[] = {q, k, v, g, beta, dO, bwd_summary, dq, dk, dv, dg, dbeta, shard_out_grad, workspace};
+  const char* names[] = {"q", "k", "v", "g", "beta", "dO", "bwd_summary", "dq", "dk", "dv", "dg", "dbeta",
+                         "shard_out_grad", "workspace"};
+  for (int i = 0; i < 14; ++i)
+    if ((st = check_ptr(req[i], names[i], true)) != CPLA_OK) return st;
+  if ((st = check_ptr(d_final_state, "d_final_state", false)) != CPLA_OK) return st;
+  if ((st = check_ptr(d_initial_state, "d_initial_state", false)) != CPLA_OK) return st;
+  if (packed && (d_final_state || d_initial_state))
+    return fail(CPLA_E_INVALID, "d_final_state and d_initial_state must be NULL with packed sequences");
+  st = delta_scan_run(p, bwd_summary, packed ? packed->following_rank_stop : nullptr, d_final_state, shard_out_grad,
+                      d_initial_state, 1, stream);
+  if (st != CPLA_OK) return st;
+  DeltaArgs a = delta_args(p, packed, workspace);
+  a.q = q; a.k = k; a.v = v; a.g = g; a.beta = beta; a.dO = dO;
+  a.state_in = shard_out_grad;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta;
+  if ((st = delta_run(DP_BWD_APPLY_WALK, p, a, stream, "cp_backward_apply_delta (walk)")) != CPLA_OK) return st;
+  return delta_run(DP_BWD_GRAD, p, a, stream, "cp_backward_apply_delta (gradients)");
 }

@@ -1,0 +1,800 @@
+// The gated delta rule: a dense d_k x d_k state transition on the same
+// context-parallel protocol (Megatron-Core page core.ssm.context_parallel.chunkwise:
+// S_out = M S_in + delta_S and dS_in = M^T dS_out + gamma for a general M; the
+// axolotl-ringmaster README's Status table names gated-DeltaNet among the
+// linear-attention variants validated on it).
+//
+//   S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,  a_t = exp(g_t),
+//   o_t = S_t^T q_t,  S_{t-1} := 0 where token t starts a packed sequence.
+//
+// Chunk form (64 tokens; Gam = segment-local inclusive cumsum of g, live_i = no
+// start at or before i, D_ij = exp(Gam_i - Gam_j) for j <= i in one sequence):
+//   A = strict-lower(beta_i D_ij k_i.k_j),   [U~ | W] = (I + A)^{-1} [beta V | beta live e^Gam K]
+//   U = U~ - W S,   O = live e^Gam Q S + (tril(Q K^T) . D) U,
+//   S <- live_last e^{Gam_last} S + K~^T U,  K~_j = [j in the last sequence] e^{Gam_last - Gam_j} k_j.
+// The solve is the WY form of the product of the chunk's transitions: the
+// chunk's own map is M_c = live_last e^{Gam_last} I - K~^T W.
+//
+// Kernels (one workgroup of four waves each; every contraction is fp32 MFMA
+// 16x16x4 on fp32 LDS tiles, inputs widened on load):
+//   delta_wy      per chunk:  U~, W (triangular solve, one column per thread)
+//   delta_fwalk   per shard:  chunk walk of the state; prepare folds [delta_S | M]
+//                             from [0 | I], apply saves chunk states and U
+//   delta_scan    per (b,h):  composition S <- M S + delta_S over shards (or its
+//                             transpose backwards)
+//   delta_out     per chunk:  O
+//   delta_bwalk   per shard:  reverse walk of dS; prepare gives gamma, apply saves
+//                             the chunk-end gradients and dU
+//   delta_grad    per chunk:  dq, dk, dv, dg, dbeta
+// This build covers d_k = d_v in {16, 32, 64}.
+#include "kernels.hpp"
+#include "shards.hpp"
+
+namespace cpla {
+namespace {
+
+constexpr int NTH = 256, NWV = 4;
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// One 16 x 16 output tile: acc += sum_{k < K} a(i, k) b(k, j). Lane l supplies
+// A[l % 16][k0 + l / 16] and B[k0 + l / 16][l % 16]; the accumulator holds rows
+// 4 (l / 16) + r, column l % 16.
+template <class FA, class FB>
+__device__ __forceinline__ f32x4 tile_mm(int K, const FA& a, const FB& b, f32x4 acc) {
+  const int l = lane_id(), x = l & 15, kk = l >> 4;
+  for (int k0 = 0; k0 < K; k0 += 4) acc = mfma_f32(a(x, k0 + kk), b(k0 + kk, x), acc);
+  return acc;
+}
+
+template <int D> struct DGeo {
+  static constexpr int LD = D + 4;            // row stride of a [64][D] or [D][D] tile (floats)
+  static constexpr int LC = CH + 4;           // row stride of a [64][64] tile
+  static constexpr int NTC = D / 16;          // column tiles of a [*][D] tile
+  static constexpr int TILE = CH * LD;        // floats of a [64][D] tile
+  static constexpr int TILE_C = CH * LC;      // floats of a [64][64] tile
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }
+
+// [64][D] rows t0 .. t0 + 63 of a [B,T,H,D] tensor into an fp32 LDS tile; rows
+// past n read as zero.
+template <typename E, int D>
+__device__ __forceinline__ void load_rows(float* dst, const E* src, int64_t b, int64_t h, int64_t t0, int n,
+                                          int64_t T, int64_t H) {
+  using G = DGeo<D>;
+  constexpr int PER_ROW = D / 4;
+  for (int e = threadIdx.x; e < CH * PER_ROW; e += NTH) {
+    const int i = e / PER_ROW, c = 4 * (e % PER_ROW);
+    f32x4 x = {0.f, 0.f, 0.f, 0.f};
+    if (i < n) {
+      const E* p = src + ((b * T + t0 + i) * H + h) * D + c;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = to_f32(p[u]);
+    }
+    *reinterpret_cast<f32x4*>(dst + i * G::LD + c) = x;
+  }
+}
+
+// rows i < n of an fp32 LDS tile into a [B,T,H,D] tensor of type E
+template <typename E, int D>
+__device__ __forceinline__ void store_rows(E* dst, const float* src, int64_t b, int64_t h, int64_t t0, int n,
+                                           int64_t T, int64_t H) {
+  using G = DGeo<D>;
+  constexpr int PER_ROW = D / 4;
+  for (int e = threadIdx.x; e < CH * PER_ROW; e += NTH) {
+    const int i = e / PER_ROW, c = 4 * (e % PER_ROW);
+    if (i >= n) continue;
+    E* p = dst + ((b * T + t0 + i) * H + h) * D + c;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) p[u] = (E)src[i * G::LD + c + u];
+  }
+}
+
+// a [D][D] fp32 matrix between global (row-major) and an LDS tile
+template <int D>
+__device__ __forceinline__ void load_mat(float* dst, const float* src) {
+  for (int e = threadIdx.x; e < D * D / 4; e += NTH) {
+    const int i = e / (D / 4), c = 4 * (e % (D / 4));
+    *reinterpret_cast<f32x4*>(dst + i * DGeo<D>::LD + c) = *reinterpret_cast<const f32x4*>(src + i * D + c);
+  }
+}
+template <int D>
+__device__ __forceinline__ void store_mat(float* dst, const float* src) {
+  for (int e = threadIdx.x; e < D * D / 4; e += NTH) {
+    const int i = e / (D / 4), c = 4 * (e % (D / 4));
+    *reinterpret_cast<f32x4*>(dst + i * D + c) = *reinterpret_cast<const f32x4*>(src + i * DGeo<D>::LD + c);
+  }
+}
+
+// Per-chunk token terms in LDS: Gam, beta, the sequence count cnt (starts at or
+// before the token), eg = live e^Gam, el = tail e^{Gam_last - Gam}; sc[0] =
+// live_last e^{Gam_last}. Wave 0 computes them (lane = token); ends with a barrier.
+struct ChunkTerms {
+  float gam[CH], beta[CH], eg[CH], el[CH];
+  int cnt[CH];
+  float sc[4];
+};
+
+__device__ __forceinline__ void chunk_terms(ChunkTerms& s, const float* g, const float* beta, const int32_t* seq,
+                                            int64_t b, int64_t h, int64_t t0, int n, int64_t T, int64_t H) {
+  if (threadIdx.x < CH) {
+    const int l = threadIdx.x;
+    const bool ok = l < n;
+    const int64_t t = t0 + l;
+    const float gv = ok ? g[(b * T + t) * H + h] : 0.f;
+    const float bv = ok ? beta[(b * T + t) * H + h] : 0.f;
+    bool st = false;
+    if (seq && ok) st = seq[t] != (t > 0 ? seq[t - 1] : -1);
+    const uint64_t starts = __ballot(st);
+    const int cnt = __popcll(starts & ((2ull << l) - 1ull));
+    // segment-local inclusive scan: add the partial of lane l - off when it is in
+    // the same sequence (sequences are contiguous, so its partial is too)
+    float x = gv;
+#pragma unroll
+    for (int off = 1; off < CH; off <<= 1) {
+      const float y = __shfl_up(x, off, 64);
+      const int cy = __shfl_up(cnt, off, 64);
+      if (l >= off && cy == cnt) x += y;
+    }
+    const float last = __shfl(x, CH - 1, 64);
+    const int clast = __shfl(cnt, CH - 1, 64);
+    s.gam[l] = x;
+    s.beta[l] = bv;
+    s.cnt[l] = cnt;
+    s.eg[l] = cnt == 0 ? __expf(x) : 0.f;
+    s.el[l] = cnt == clast ? __expf(last - x) : 0.f;
+    if (l == 0) s.sc[0] = clast == 0 ? __expf(last) : 0.f;
+  }
+  __syncthreads();
+}
+
+// the chunk's tokens inside shard r: (start, valid count)
+__device__ __forceinline__ void chunk_of(int64_t T, int P, int64_t idx, int64_t& r, int64_t& c) {
+  const int64_t nsc = chunks_of(shard_size(T, P));
+  r = idx / nsc;
+  c = idx % nsc;
+}
+
+}  // namespace
+
+// ---- U~ and W per chunk ------------------------------------------------------------------
+template <typename E, int D>
+__global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
+  using G = DGeo<D>;
+  __shared__ __attribute__((aligned(16))) float s_k[G::TILE], s_v[G::TILE], s_a[G::TILE_C];
+  __shared__ ChunkTerms s_t;
+  int64_t r, c;
+  const int64_t idx = a.chunk_begin + blockIdx.x;
+  chunk_of(a.T, a.P, idx, r, c);
+  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t slen = shard_len(a.T, a.P, r);
+  const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
+  if (r >= a.P || n <= 0) return;
+  const int64_t t0 = shard_begin(a.T, a.P, r) + 64 * c;
+  const int32_t* seq = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
+  load_rows<E, D>(s_k, reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+  load_rows<E, D>(s_v, reinterpret_cast<const E*>(a.v), b, h, t0, n, a.T, a.H);
+  chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+
+  // A = strict-lower(beta_i D_ij k_i.k_j)
+  const int w = threadIdx.x >> 6, l = lane_id();
+  for (int t = w; t < 16; t += NWV) {
+    const int ti = t >> 2, tj = t & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (tj <= ti)
+      acc = tile_mm(D, [&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+                    [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+      const bool ok = j < i && s_t.cnt[i] == s_t.cnt[j];
+      s_a[i * G::LC + j] = ok ? s_t.beta[i] * __expf(s_t.gam[i] - s_t.gam[j]) * acc[q] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // forward substitution (I + A) X = [beta V | beta live e^Gam K], one column per
+  // thread, in place in the LDS tiles (a register-resident column made the
+  // compiler hold the hoisted rows of A in every register and spill)
+  const int col = threadIdx.x;
+  if (col < 2 * D) {
+    const bool isv = col < D;
+    const int cc = isv ? col : col - D;
+    float* xc = (isv ? s_v : s_k) + cc;
+    for (int i = 0; i < CH; ++i) xc[i * G::LD] *= isv ? s_t.beta[i] : s_t.beta[i] * s_t.eg[i];
+    for (int i = 1; i < CH; ++i) {
+      const float* ai = s_a + i * G::LC;
+      float acc = xc[i * G::LD];
+      int j = 0;
+      for (; j + 4 <= i; j += 4) {
+        const f32x4 av = *reinterpret_cast<const f32x4*>(ai + j);
+        acc -= av[0] * xc[j * G::LD] + av[1] * xc[(j + 1) * G::LD] + av[2] * xc[(j + 2) * G::LD] +
+               av[3] * xc[(j + 3) * G::LD];
+      }
+      for (; j < i; ++j) acc -= ai[j] * xc[j * G::LD];
+      xc[i * G::LD] = acc;
+    }
+    float* dst = isv ? a.ws_ut : a.ws_w;
+    for (int i = 0; i < n; ++i) dst[((b * a.T + t0 + i) * a.H + h) * D + cc] = xc[i * G::LD];
+  }
+}
+
+// ---- forward chunk walk of one shard ------------------------------------------------------
+// PREPARE: the augmented state Z = [delta_S | M] (D x 2D) from [0 | I], written to
+// the shard's record as [M | delta_S]. APPLY: S from the composed incoming state;
+// saves the state entering every chunk and U.
+template <typename E, int D, bool APPLY>
+__global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
+  using G = DGeo<D>;
+  constexpr int NZ = APPLY ? D : 2 * D;
+  constexpr int LZ = NZ + 4;
+  __shared__ __attribute__((aligned(16))) float s_z[D * LZ], s_u[CH * LZ], s_w[G::TILE], s_k[G::TILE];
+  __shared__ ChunkTerms s_t;
+  const int64_t r = a.rank_begin + blockIdx.x;
+  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t tshard = shard_begin(a.T, a.P, r), slen = shard_len(a.T, a.P, r);
+  const int nc = (int)chunks_of(slen);
+  const int64_t cbase = shard_chunk_base(a.T, a.P, r), nct = row_chunks(a.T, a.P);
+  const int32_t* seq = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
+  const int w = threadIdx.x >> 6, l = lane_id();
+
+  for (int e = threadIdx.x; e < D * NZ; e += NTH) {
+    const int d = e / NZ, m = e % NZ;
+    float x;
+    if constexpr (APPLY) x = a.state_in[((r * a.B * a.H + bh) * D + d) * D + m];
+    else x = (m == D + d) ? 1.f : 0.f;
+    s_z[d * LZ + m] = x;
+  }
+  for (int c = 0; c < nc; ++c) {
+    const int64_t t0 = tshard + 64 * c;
+    const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
+    load_rows<float, D>(s_w, a.ws_w, b, h, t0, n, a.T, a.H);
+    load_rows<E, D>(s_k, reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+    // U~ into the first D columns of s_u (the M part takes no input)
+    for (int e = threadIdx.x; e < CH * NZ; e += NTH) {
+      const int i = e / NZ, m = e % NZ;
+      s_u[i * LZ + m] = (m < D && i < n) ? a.ws_ut[((b * a.T + t0 + i) * a.H + h) * D + m] : 0.f;
+    }
+    chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    if constexpr (APPLY) {
+      float* cs = a.chunk_states + (bh * nct + cbase + c) * (int64_t)(D * D);
+      for (int e = threadIdx.x; e < D * D; e += NTH) cs[e] = s_z[(e / D) * LZ + e % D];
+    }
+    // U_Z = U~_Z - W Z
+    for (int t = w; t < 4 * (NZ / 16); t += NWV) {
+      const int ti = t / (NZ / 16), tj = t % (NZ / 16);
+      f32x4 acc = tile_mm(D, [&](int i, int k) { return s_w[(16 * ti + i) * G::LD + k]; },
+                          [&](int k, int j) { return s_z[k * LZ + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+        s_u[i * LZ + j] -= acc[q];
+      }
+    }
+    __syncthreads();
+    if constexpr (APPLY) {
+      for (int e = threadIdx.x; e < CH * D; e += NTH) {
+        const int i = e / D, m = e % D;
+        if (i < n) a.ws_u[((b * a.T + t0 + i) * a.H + h) * D + m] = s_u[i * LZ + m];
+      }
+    }
+    // Z <- live_last e^Gam_last Z + K~^T U_Z
+    const float sc = s_t.sc[0];
+    for (int t = w; t < (D / 16) * (NZ / 16); t += NWV) {
+      const int ti = t / (NZ / 16), tj = t % (NZ / 16);
+      f32x4 acc = tile_mm(CH, [&](int i, int k) { return s_k[k * G::LD + 16 * ti + i] * s_t.el[k]; },
+                          [&](int k, int j) { return s_u[k * LZ + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = 16 * ti + 4 * (l >> 4) + q, m = 16 * tj + (l & 15);
+        s_z[d * LZ + m] = sc * s_z[d * LZ + m] + acc[q];
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (!APPLY) {
+    float* rec = a.summary + (r * a.B * a.H + bh) * (int64_t)(2 * D * D);
+    for (int e = threadIdx.x; e < 2 * D * D; e += NTH) {
+      const int part = e / (D * D), f = e % (D * D), d = f / D, m = f % D;
+      rec[e] = part == 0 ? s_z[d * LZ + D + m] : s_z[d * LZ + m];
+    }
+  }
+}
+
+// ---- composition over shards ----------------------------------------------------------
+// forward: out[r] = fold of S <- M_j S + delta_S_j over [prs_r, r) (S_init at rank 0
+// unpacked); reverse: out[r] = fold of dS <- M_j^T dS + gamma_j over (r, frs_r)
+// backwards (dS_final at the last rank unpacked). A shard holding a start has
+// M = 0, so folding through it restarts the fold. The running value after the
+// last shard is the final state / dS_init.
+template <int D>
+__global__ __launch_bounds__(NTH) void delta_scan(DeltaScanArgs a) {
+  using G = DGeo<D>;
+  __shared__ __attribute__((aligned(16))) float s_s[D * G::LD], s_m[D * G::LD];
+  const int64_t bh = blockIdx.x;
+  const int w = threadIdx.x >> 6, l = lane_id();
+  const int32_t* slice = a.slice ? a.slice + (bh / a.H) * a.P : nullptr;
+  constexpr int64_t REC = 2 * D * D;
+  for (int e = threadIdx.x; e < D * D; e += NTH)
+    s_s[(e / D) * G::LD + e % D] = a.init ? a.init[bh * D * D + e] : 0.f;
+  __syncthreads();
+  for (int s = 0; s < a.P; ++s) {
+    const int q = a.reverse ? a.P - 1 - s : s;
+    if (s > 0 && slice && slice[q] == (a.reverse ? q + 1 : q)) {
+      for (int e = threadIdx.x; e < D * D; e += NTH) s_s[(e / D) * G::LD + e % D] = 0.f;
+      __syncthreads();
+    }
+    store_mat<D>(a.out + (q * a.BH + bh) * (int64_t)(D * D), s_s);
+    const float* rec = a.summary + (q * a.BH + bh) * REC;
+    load_mat<D>(s_m, rec);
+    __syncthreads();
+    constexpr int NT2 = (D / 16) * (D / 16), PW = (NT2 + NWV - 1) / NWV;
+    f32x4 res[PW];
+#pragma unroll
+    for (int m = 0; m < PW; ++m) {
+      const int t = w + NWV * m;
+      if (t >= NT2) continue;
+      const int ti = t / (D / 16), tj = t % (D / 16);
+      f32x4 acc = a.reverse
+          ? tile_mm(D, [&](int i, int k) { return s_m[k * G::LD + 16 * ti + i]; },
+                    [&](int k, int j) { return s_s[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f})
+          : tile_mm(D, [&](int i, int k) { return s_m[(16 * ti + i) * G::LD + k]; },
+                    [&](int k, int j) { return s_s[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = 16 * ti + 4 * (l >> 4) + u, j = 16 * tj + (l & 15);
+        acc[u] += rec[D * D + i * D + j];
+      }
+      res[m] = acc;
+    }
+    __syncthreads();   // every read of s_s is done
+#pragma unroll
+    for (int m = 0; m < PW; ++m) {
+      const int t = w + NWV * m;
+      if (t >= NT2) continue;
+      const int ti = t / (D / 16), tj = t % (D / 16);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s_s[(16 * ti + 4 * (l >> 4) + u) * G::LD + 16 * tj + (l & 15)] = res[m][u];
+    }
+    __syncthreads();
+  }
+  if (a.fin) store_mat<D>(a.fin + bh * (int64_t)(D * D), s_s);
+}
+
+// ---- output per chunk --------------------------------------------------------------------
+template <typename E, int D>
+__global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
+  using G = DGeo<D>;
+  __shared__ __attribute__((aligned(16))) float s_q[G::TILE], s_k[G::TILE], s_u[G::TILE], s_s[D * G::LD],
+      s_p[G::TILE_C];
+  __shared__ ChunkTerms s_t;
+  int64_t r, c;
+  const int64_t idx = a.chunk_begin + blockIdx.x;
+  chunk_of(a.T, a.P, idx, r, c);
+  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t slen = shard_len(a.T, a.P, r);
+  const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
+  if (r >= a.P || n <= 0) return;
+  const int64_t t0 = shard_begin(a.T, a.P, r) + 64 * c;
+  const int64_t nct = row_chunks(a.T, a.P);
+  const int32_t* seq = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
+  const int w = threadIdx.x >> 6, l = lane_id();
+  load_rows<E, D>(s_q, reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
+  load_rows<E, D>(s_k, reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+  load_rows<float, D>(s_u, a.ws_u, b, h, t0, n, a.T, a.H);
+  load_mat<D>(s_s, a.chunk_states + (bh * nct + idx) * (int64_t)(D * D));
+  chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+  for (int t = w; t < 16; t += NWV) {
+    const int ti = t >> 2, tj = t & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (tj <= ti)
+      acc = tile_mm(D, [&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+                    [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+      const bool ok = j <= i && s_t.cnt[i] == s_t.cnt[j];
+      s_p[i * G::LC + j] = ok ? __expf(s_t.gam[i] - s_t.gam[j]) * acc[q] : 0.f;
+    }
+  }
+  __syncthreads();
+  E* o = reinterpret_cast<E*>(a.out);
+  for (int t = w; t < 4 * G::NTC; t += NWV) {
+    const int ti = t / G::NTC, tj = t % G::NTC;
+    f32x4 x = tile_mm(D, [&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+                      [&](int k, int j) { return s_s[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+    f32x4 y = tile_mm(CH, [&](int i, int k) { return s_p[(16 * ti + i) * G::LC + k]; },
+                      [&](int k, int j) { return s_u[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+      if (i < n) o[((b * a.T + t0 + i) * a.H + h) * D + j] = (E)(s_t.eg[i] * x[q] + y[q]);
+    }
+  }
+}
+
+// ---- reverse chunk walk of one shard ------------------------------------------------------
+// dU = P^T dO + K~ dS, dS <- live_last e^Gam_last dS + (live e^Gam Q)^T dO - W^T dU,
+// from dS = 0 (PREPARE: gamma, written with a copy of the shard's M) or from the
+// composed gradient (APPLY: saves the gradient at every chunk's end and dU).
+template <typename E, int D, bool APPLY>
+__global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
+  using G = DGeo<D>;
+  __shared__ __attribute__((aligned(16))) float s_q[G::TILE], s_k[G::TILE], s_do[G::TILE], s_w[G::TILE],
+      s_du[G::TILE], s_ds[D * G::LD], s_p[G::TILE_C];
+  __shared__ ChunkTerms s_t;
+  const int64_t r = a.rank_begin + blockIdx.x;
+  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t tshard = shard_begin(a.T, a.P, r), slen = shard_len(a.T, a.P, r);
+  const int nc = (int)chunks_of(slen);
+  const int64_t cbase = shard_chunk_base(a.T, a.P, r), nct = row_chunks(a.T, a.P);
+  const int32_t* seq = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
+  const int w = threadIdx.x >> 6, l = lane_id();
+  for (int e = threadIdx.x; e < D * D; e += NTH)
+    s_ds[(e / D) * G::LD + e % D] = APPLY ? a.state_in[(r * a.B * a.H + bh) * (int64_t)(D * D) + e] : 0.f;
+  for (int c = nc - 1; c >= 0; --c) {
+    const int64_t t0 = tshard + 64 * c;
+    const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
+    load_rows<E, D>(s_q, reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
+    load_rows<E, D>(s_k, reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+    load_rows<E, D>(s_do, reinterpret_cast<const E*>(a.dO), b, h, t0, n, a.T, a.H);
+    load_rows<float, D>(s_w, a.ws_w, b, h, t0, n, a.T, a.H);
+    chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    if constexpr (APPLY) store_mat<D>(a.ws_dsc + (bh * nct + cbase + c) * (int64_t)(D * D), s_ds);
+    for (int t = w; t < 16; t += NWV) {
+      const int ti = t >> 2, tj = t & 3;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (tj <= ti)
+        acc = tile_mm(D, [&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+                      [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+        const bool ok = j <= i && s_t.cnt[i] == s_t.cnt[j];
+        s_p[i * G::LC + j] = ok ? __expf(s_t.gam[i] - s_t.gam[j]) * acc[q] : 0.f;
+      }
+    }
+    __syncthreads();
+    // dU = P^T dO + K~ dS
+    for (int t = w; t < 4 * G::NTC; t += NWV) {
+      const int ti = t / G::NTC, tj = t % G::NTC;
+      f32x4 acc = tile_mm(CH, [&](int i, int k) { return s_p[k * G::LC + 16 * ti + i]; },
+                          [&](int k, int j) { return s_do[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+      acc = tile_mm(D, [&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k] * s_t.el[16 * ti + i]; },
+                    [&](int k, int j) { return s_ds[k * G::LD + 16 * tj + j]; }, acc);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s_du[(16 * ti + 4 * (l >> 4) + q) * G::LD + 16 * tj + (l & 15)] = acc[q];
+    }
+    __syncthreads();
+    if constexpr (APPLY) store_rows<float, D>(a.ws_du, s_du, b, h, t0, n, a.T, a.H);
+    // dS <- sc dS + (eg Q)^T dO - W^T dU
+    const float sc = s_t.sc[0];
+    for (int t = w; t < G::NTC * G::NTC; t += NWV) {
+      const int ti = t / G::NTC, tj = t % G::NTC;
+      f32x4 x = tile_mm(CH, [&](int i, int k) { return s_q[k * G::LD + 16 * ti + i] * s_t.eg[k]; },
+                        [&](int k, int j) { return s_do[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 y = tile_mm(CH, [&](int i, int k) { return s_w[k * G::LD + 16 * ti + i]; },
+                        [&](int k, int j) { return s_du[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int d = 16 * ti + 4 * (l >> 4) + q, m = 16 * tj + (l & 15);
+        s_ds[d * G::LD + m] = sc * s_ds[d * G::LD + m] + x[q] - y[q];
+      }
+    }
+    __syncthreads();
+  }
+  if constexpr (!APPLY) {
+    float* rec = a.summary + (r * a.B * a.H + bh) * (int64_t)(2 * D * D);
+    const float* frec = a.fwd_summary + (r * a.B * a.H + bh) * (int64_t)(2 * D * D);
+    for (int e = threadIdx.x; e < D * D; e += NTH) {
+      rec[e] = frec[e];
+      rec[D * D + e] = s_ds[(e / D) * G::LD + e % D];
+    }
+  }
+}
+
+// ---- gradients per chunk --------------------------------------------------------------------
+// From S0 (state entering the chunk), dS (gradient at its end), U, dU, U~, W:
+//   dPr = (dO U^T) . D (causal, one sequence), dq = dPr K + eg (dO S0^T),
+//   dk  = dPr^T Q + el (U dS^T) + dAr K + dAr^T K + beta eg dBk,
+//   [dBv | dBk] = (I + A)^{-T} [dU | -dU S0^T],  dA = strict-lower(-(dBv U~^T + dBk W^T)),
+//   dAr = dA . D . beta_i,  dv = beta dBv,
+//   dbeta = rowsum(dA . D . KK^T) + rowsum(dBv . V) + eg rowsum(dBk . K),
+//   dGam = (row - column sums of dPr . QK^T and of dA . A) + eg rowsum(Q . dO S0^T)
+//          + beta eg rowsum(dBk . K) - tk + [last] (sum tk + sc <dS, S0>),
+//   tk_j = el_j rowsum(U dS^T . K)_j,  dg = suffix sums of dGam within each sequence.
+template <typename E, int D>
+__global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
+  using G = DGeo<D>;
+  // eight [64][64+4] slots (a [64][D] or [D][D] tile fits one)
+  __shared__ __attribute__((aligned(16))) float s_slot[8][G::TILE_C];
+  __shared__ ChunkTerms s_t;
+  __shared__ float s_rp[3][NWV][CH];   // per-wave row partials
+  __shared__ float s_cp[2][CH];        // column sums
+  __shared__ float s_red[NWV];
+  int64_t r, c;
+  const int64_t idx = a.chunk_begin + blockIdx.x;
+  chunk_of(a.T, a.P, idx, r, c);
+  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t slen = shard_len(a.T, a.P, r);
+  const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
+  if (r >= a.P || n <= 0) return;
+  const int64_t t0 = shard_begin(a.T, a.P, r) + 64 * c;
+  const int64_t nct = row_chunks(a.T, a.P);
+  const int32_t* seq = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
+  const int w = threadIdx.x >> 6, l = lane_id();
+  float *s_q = s_slot[0], *s_k = s_slot[1], *s_do = s_slot[2], *s_u = s_slot[3], *s_s0 = s_slot[4],
+        *s_ds = s_slot[5], *s_dp = s_slot[6], *s_dk = s_slot[7];
+  load_rows<E, D>(s_q, reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
+  load_rows<E, D>(s_k, reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+  load_rows<E, D>(s_do, reinterpret_cast<const E*>(a.dO), b, h, t0, n, a.T, a.H);
+  load_rows<float, D>(s_u, a.ws_u, b, h, t0, n, a.T, a.H);
+  load_mat<D>(s_s0, a.chunk_states + (bh * nct + idx) * (int64_t)(D * D));
+  load_mat<D>(s_ds, a.ws_dsc + (bh * nct + idx) * (int64_t)(D * D));
+  for (int e = threadIdx.x; e < 3 * NWV * CH; e += NTH) (&s_rp[0][0][0])[e] = 0.f;
+  chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+
+  // score tiles: dPr and the decay terms of dGam (rows of wave w's column tile tj = w)
+  {
+    float colacc[1] = {0.f};
+    for (int t = w; t < 16; t += NWV) {
+      const int ti = t >> 2, tj = t & 3;
+      f32x4 qk = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
+      if (tj <= ti) {
+        qk = tile_mm(D, [&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, qk);
+        du = tile_mm(D, [&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
+                     [&](int k, int j) { return s_u[(16 * tj + j) * G::LD + k]; }, du);
+      }
+      float rowp[4], colp = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+        const bool ok = j <= i && s_t.cnt[i] == s_t.cnt[j];
+        const float dpr = ok ? __expf(s_t.gam[i] - s_t.gam[j]) * du[q] : 0.f;
+        s_dp[i * G::LC + j] = dpr;
+        const float pa = dpr * qk[q];
+        rowp[q] = pa;
+        colp += pa;
+      }
+      // rows: sum over the 16 columns of the tile (lanes sharing l / 16)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float x = rowp[q];
+        x += __shfl_xor(x, 1, 64);
+        x += __shfl_xor(x, 2, 64);
+        x += __shfl_xor(x, 4, 64);
+        x += __shfl_xor(x, 8, 64);
+        if ((l & 15) == 0) s_rp[0][w][16 * ti + 4 * (l >> 4) + q] = x;
+      }
+      colp += __shfl_xor(colp, 16, 64);
+      colp += __shfl_xor(colp, 32, 64);
+      colacc[0] += colp;
+    }
+    if (l < 16) s_cp[0][16 * w + l] = colacc[0];   // column tile tj = w, summed over its row tiles
+  }
+  __syncthreads();
+
+  // dq = dPr K + eg (dO S0^T); dk (part) = dPr^T Q + el (U dS^T); row partials of
+  // Q . (dO S0^T) and el (U dS^T) . K
+  {
+    E* dq = reinterpret_cast<E*>(a.dq);
+    for (int t = w; t < 4 * G::NTC; t += NWV) {
+      const int ti = t / G::NTC, tj = t % G::NTC;
+      f32x4 x = tile_mm(CH, [&](int i, int k) { return s_dp[(16 * ti + i) * G::LC + k]; },
+                        [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 y = tile_mm(D, [&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
+                        [&](int k, int j) { return s_s0[(16 * tj + j) * G::LD + k]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 z = tile_mm(CH, [&](int i, int k) { return s_dp[k * G::LC + 16 * ti + i]; },
+                        [&](int k, int j) { return s_q[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 u = tile_mm(D, [&](int i, int k) { return s_u[(16 * ti + i) * G::LD + k]; },
+                        [&](int k, int j) { return s_ds[(16 * tj + j) * G::LD + k]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+        const float eg = s_t.eg[i], el = s_t.el[i];
+        if (i < n) dq[((b * a.T + t0 + i) * a.H + h) * D + j] = (E)(x[q] + eg * y[q]);
+        const float ue = el * u[q];
+        s_dk[i * G::LD + j] = z[q] + ue;
+        float p1 = eg * y[q] * s_q[i * G::LD + j];
+        float p2 = ue * s_k[i * G::LD + j];
+        p1 += __shfl_xor(p1, 1, 64);
+        p1 += __shfl_xor(p1, 2, 64);
+        p1 += __shfl_xor(p1, 4, 64);
+        p1 += __shfl_xor(p1, 8, 64);
+        p2 += __shfl_xor(p2, 1, 64);
+        p2 += __shfl_xor(p2, 2, 64);
+        p2 += __shfl_xor(p2, 4, 64);
+        p2 += __shfl_xor(p2, 8, 64);
+        if ((l & 15) == 0) {
+          s_rp[1][w][i] += p1;   // a wave may own several column tiles of one row
+          s_rp[2][w][i] += p2;
+        }
+      }
+    }
+    // <dS, S0>
+    float sp = 0.f;
+    for (int e = threadIdx.x; e < D * D; e += NTH) sp += s_ds[(e / D) * G::LD + e % D] * s_s0[(e / D) * G::LD + e % D];
+    sp = wave_sum(sp);
+    if (l == 0) s_red[w] = sp;
+  }
+  __syncthreads();
+  // dGam (partial) into s_cp[1]
+  if (threadIdx.x < CH) {
+    const int i = threadIdx.x;
+    float rowpa = 0.f, qdos = 0.f, tk = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) {
+      rowpa += s_rp[0][ww][i];
+      qdos += s_rp[1][ww][i];
+      tk += s_rp[2][ww][i];
+    }
+    float dgam = rowpa - s_cp[0][i] + qdos - tk;
+    float tks = tk;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tks += __shfl_xor(tks, off, 64);
+    if (i == CH - 1) dgam += tks + s_t.sc[0] * (s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+    s_cp[1][i] = dgam;
+  }
+  __syncthreads();
+
+  // phase 2: slots 0 V, 2 U~, 3 W, 6 dU; 1 K, 4 S0, 7 dk kept; 5 dW
+  float *s_v = s_slot[0], *s_ut = s_slot[2], *s_w = s_slot[3], *s_dU = s_slot[6], *s_dW = s_slot[5];
+  load_rows<E, D>(s_v, reinterpret_cast<const E*>(a.v), b, h, t0, n, a.T, a.H);
+  load_rows<float, D>(s_ut, a.ws_ut, b, h, t0, n, a.T, a.H);
+  load_rows<float, D>(s_w, a.ws_w, b, h, t0, n, a.T, a.H);
+  load_rows<float, D>(s_dU, a.ws_du, b, h, t0, n, a.T, a.H);
+  __syncthreads();
+  // dW = -dU S0^T
+  for (int t = w; t < 4 * G::NTC; t += NWV) {
+    const int ti = t / G::NTC, tj = t % G::NTC;
+    f32x4 x = tile_mm(D, [&](int i, int k) { return s_dU[(16 * ti + i) * G::LD + k]; },
+                      [&](int k, int j) { return s_s0[(16 * tj + j) * G::LD + k]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_dW[(16 * ti + 4 * (l >> 4) + q) * G::LD + 16 * tj + (l & 15)] = -x[q];
+  }
+  __syncthreads();
+  // A into slot 4 (S0 is dead)
+  float* s_a = s_slot[4];
+  for (int t = w; t < 16; t += NWV) {
+    const int ti = t >> 2, tj = t & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (tj <= ti)
+      acc = tile_mm(D, [&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+                    [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+      const bool ok = j < i && s_t.cnt[i] == s_t.cnt[j];
+      s_a[i * G::LC + j] = ok ? s_t.beta[i] * __expf(s_t.gam[i] - s_t.gam[j]) * acc[q] : 0.f;
+    }
+  }
+  __syncthreads();
+  // backward substitution (I + A)^T dB = [dU | dW], one column per thread, in place
+  if (threadIdx.x < 2 * D) {
+    const bool isv = threadIdx.x < D;
+    float* xc = (isv ? s_dU : s_dW) + (isv ? threadIdx.x : threadIdx.x - D);
+    for (int i = CH - 2; i >= 0; --i) {
+      float acc = xc[i * G::LD];
+      for (int j = i + 1; j < CH; ++j) acc -= s_a[j * G::LC + i] * xc[j * G::LD];
+      xc[i * G::LD] = acc;
+    }
+  }
+  __syncthreads();
+  // dA = strict-lower(-(dBv U~^T + dBk W^T)); dAr = dA . D . beta_i into slot 4;
+  // row sums of dA . D . KK^T (dbeta) and column sums of dA . A (dGam)
+  for (int e = threadIdx.x; e < 2 * NWV * CH; e += NTH) (&s_rp[0][0][0])[e] = 0.f;
+  __syncthreads();
+  {
+    float colacc = 0.f;
+    for (int t = w; t < 16; t += NWV) {
+      const int ti = t >> 2, tj = t & 3;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f}, kk = {0.f, 0.f, 0.f, 0.f};
+      if (tj <= ti) {
+        x = tile_mm(D, [&](int i, int k) { return s_dU[(16 * ti + i) * G::LD + k]; },
+                    [&](int k, int j) { return s_ut[(16 * tj + j) * G::LD + k]; }, x);
+        x = tile_mm(D, [&](int i, int k) { return s_dW[(16 * ti + i) * G::LD + k]; },
+                    [&](int k, int j) { return s_w[(16 * tj + j) * G::LD + k]; }, x);
+        kk = tile_mm(D, [&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, kk);
+      }
+      float colp = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+        const bool ok = j < i && s_t.cnt[i] == s_t.cnt[j];
+        const float dec = ok ? __expf(s_t.gam[i] - s_t.gam[j]) : 0.f;
+        const float da = ok ? -x[q] : 0.f;
+        const float r1 = da * dec * kk[q];          // dA . D . KK^T
+        s_a[i * G::LC + j] = da * dec * s_t.beta[i];
+        colp += r1 * s_t.beta[i];                   // column sums of dA . A
+        float x1 = r1;
+        x1 += __shfl_xor(x1, 1, 64);
+        x1 += __shfl_xor(x1, 2, 64);
+        x1 += __shfl_xor(x1, 4, 64);
+        x1 += __shfl_xor(x1, 8, 64);
+        if ((l & 15) == 0) s_rp[0][w][i] = x1;
+      }
+      colp += __shfl_xor(colp, 16, 64);
+      colp += __shfl_xor(colp, 32, 64);
+      colacc += colp;
+    }
+    if (l < 16) s_cp[0][16 * w + l] = colacc;
+  }
+  __syncthreads();
+  // dk = part + dAr K + dAr^T K + beta eg dBk; dv = beta dBv
+  {
+    E* dk = reinterpret_cast<E*>(a.dk);
+    E* dv = reinterpret_cast<E*>(a.dv);
+    for (int t = w; t < 4 * G::NTC; t += NWV) {
+      const int ti = t / G::NTC, tj = t % G::NTC;
+      f32x4 x = tile_mm(CH, [&](int i, int k) { return s_a[(16 * ti + i) * G::LC + k]; },
+                        [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+      x = tile_mm(CH, [&](int i, int k) { return s_a[k * G::LC + 16 * ti + i]; },
+                  [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, x);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+        if (i < n) {
+          const float bt = s_t.beta[i];
+          const int64_t off = ((b * a.T + t0 + i) * a.H + h) * D + j;
+          dk[off] = (E)(s_dk[i * G::LD + j] + x[q] + bt * s_t.eg[i] * s_dW[i * G::LD + j]);
+          dv[off] = (E)(bt * s_dU[i * G::LD + j]);
+        }
+      }
+    }
+  }
+  // dbeta and dg (wave 0, lane = token)
+  if (threadIdx.x < CH) {
+    const int i = threadIdx.x;
+    float r2 = 0.f, r3 = 0.f;
+    for (int j = 0; j < D; ++j) {
+      r2 += s_dU[i * G::LD + j] * s_v[i * G::LD + j];
+      r3 += s_dW[i * G::LD + j] * s_k[i * G::LD + j];
+    }
+    float r1 = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) r1 += s_rp[0][ww][i];
+    const float bt = s_t.beta[i], eg = s_t.eg[i];
+    const float dbeta = r1 + r2 + eg * r3;
+    const float dgam = s_cp[1][i] + bt * r1 - s_cp[0][i] + bt * eg * r3;
+    // suffix sums within the token's sequence: lanes i + off in the same sequence
+    const int cnt = s_t.cnt[i];
+    float x = dgam;
+#pragma unroll
+    for (int off = 1; off < CH; off <<= 1) {
+      const float y = __shfl_down(x, off, 64);
+      const int cy = __shfl_down(cnt, off, 64);
+      if (i + off < CH && cy == cnt) x += y;
+    }
+    const bool start = i == 0 ? (seq && cnt == 1) : cnt != s_t.cnt[i - 1];
+    if (i < n) {
+      a.dbeta[(b * a.T + t0 + i) * a.H + h] = dbeta;
+      a.dg[(b * a.T + t0 + i) * a.H + h] = start ? 0.f : x;
+    }
+  }
+}
+
+#define CPLA_INST_DELTA(E, D)                                                  \
+  template __global__ void delta_wy<E, D>(DeltaArgs);                          \
+  template __global__ void delta_fwalk<E, D, false>(DeltaArgs);                \
+  template __global__ void delta_fwalk<E, D, true>(DeltaArgs);                 \
+  template __global__ void delta_out<E, D>(DeltaArgs);                         \
+  template __global__ void delta_bwalk<E, D, false>(DeltaArgs);                \
+  template __global__ void delta_bwalk<E, D, true>(DeltaArgs);                 \
+  template __global__ void delta_grad<E, D>(DeltaArgs);
+CPLA_INST_DELTA(float, 16)
+CPLA_INST_DELTA(float, 32)
+CPLA_INST_DELTA(float, 64)
+CPLA_INST_DELTA(bf16_t, 16)
+CPLA_INST_DELTA(bf16_t, 32)
+CPLA_INST_DELTA(bf16_t, 64)
+template __global__ void delta_scan<16>(DeltaScanArgs);
+template __global__ void delta_scan<32>(DeltaScanArgs);
+template __global__ void delta_scan<64>(DeltaScanArgs);
+
+}  // namespace cpla

@@ -59,6 +59,7 @@ struct ScanArgs {
 struct DeltaArgs {
   int64_t B, T, H;
   int P, rank_begin;
+  int64_t chunk_begin;       // per-chunk kernels: first chunk (row-local index) of the launch
   const void* q;
   const void* k;
   const void* v;

@@ -64,7 +64,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;
 
-#define CPLA_ABI_VERSION 3
+#define CPLA_ABI_VERSION 4
 
 typedef enum {
   CPLA_OK = 0,
@@ -78,7 +78,8 @@ typedef enum {
 } cpla_status;
 
 typedef enum { CPLA_F32 = 0, CPLA_BF16 = 1 } cpla_dtype;
-typedef enum { CPLA_DECAY_NONE = 0, CPLA_DECAY_SCALAR = 1, CPLA_DECAY_DIAG = 2 } cpla_decay;
+typedef enum { CPLA_DECAY_NONE = 0, CPLA_DECAY_SCALAR = 1, CPLA_DECAY_DIAG = 2,
+               CPLA_DECAY_DELTA = 3 /* gated delta rule: the _delta calls below */ } cpla_decay;
 
 typedef struct {
   int64_t B, T, H, dk, dv;   /* packed sequences: each of the B rows is a stream of T
@@ -215,6 +216,48 @@ cpla_status cpla_packed_rank_slices(const int32_t* global_seq_idx, int64_t T, in
  * increasing, 0 first, T last. */
 cpla_status cpla_seq_idx_from_cu_seqlens(const int32_t* cu_seqlens, int32_t n_seqs, int64_t T,
                                          int32_t* seq_idx);
+
+/* ---- The gated delta rule: a dense state transition -------------------------------
+ * The Megatron-Core page core.ssm.context_parallel.chunkwise states the shard maps
+ * for a general transition M (classes CPForward*Summary: S_out = M S_in + delta_S;
+ * CPBackward*Summary: dS_in = M^T dS_out + gamma), and the axolotl-ringmaster
+ * README (Status table) validates gated-DeltaNet linear attention on that state
+ * passing. Here the recurrence is
+ *   S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,  a_t = exp(g_t),
+ *   o_t = S_t^T q_t,  S_{t-1} := 0 where token t starts a packed sequence,
+ * so M is a full d_k x d_k matrix (zero for a shard holding a start) and the
+ * composition multiplies matrices (M^T backwards). Problem: decay =
+ * CPLA_DECAY_DELTA, dk == dv in {16, 32, 64}, dtype fp32 or bf16; g and beta
+ * [B,T,H] fp32 (beta is the write strength, usually in (0, 1); keys are usually
+ * L2-normalised by the caller, and q carries any scale). Summary records
+ * (cpla_summary_width = dk*dk + dk*dv floats): [M (dk x dk, row-major) | delta_S
+ * (forward) or gamma (backward) (dk x dv)]. The four calls follow the protocol of
+ * the calls above; their local context lives in a caller-owned workspace of
+ * cpla_delta_workspace_bytes() bytes (16-byte aligned), which must be the same
+ * buffer, unchanged, across the four calls of one step: forward prepare fills the
+ * per-chunk solves, forward apply the chunk states, backward prepare reads them,
+ * backward apply writes the chunk-end gradients. Packing, rank ranges and error
+ * behaviour as for the calls above; the gradients dg and dbeta are fp32 [B,T,H],
+ * dq, dk, dv in the input dtype. */
+int64_t cpla_delta_workspace_bytes(const cpla_problem* p);   /* -1 for an invalid problem */
+
+cpla_status cp_forward_prepare_delta(const cpla_problem* p, const cpla_packed* packed, const void* k,
+                                     const void* v, const float* g, const float* beta, float* fwd_summary,
+                                     void* workspace, hipStream_t stream);
+cpla_status cp_forward_apply_delta(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                   const void* k, const void* v, const float* g, const float* beta,
+                                   const float* fwd_summary, const float* initial_state, void* o,
+                                   float* shard_in_state, float* final_state, void* workspace,
+                                   hipStream_t stream);
+cpla_status cp_backward_prepare_delta(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                      const void* k, const float* g, const float* beta, const void* dO,
+                                      const float* fwd_summary, float* bwd_summary, void* workspace,
+                                      hipStream_t stream);
+cpla_status cp_backward_apply_delta(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                    const void* k, const void* v, const float* g, const float* beta,
+                                    const void* dO, const float* bwd_summary, const float* d_final_state,
+                                    void* dq, void* dk, void* dv, float* dg, float* dbeta, float* shard_out_grad,
+                                    float* d_initial_state, void* workspace, hipStream_t stream);
 
 /* ---- Mamba2 (SSD) parametrisation of the scalar-decay path ------------------------
  * The axolotl-ringmaster README (Status table, Layout) runs Mamba2 SSM context

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert L.cpla_abi_version() == 3
+    assert L.cpla_abi_version() == 4
 
 
 def prob(**kw):
@@ -223,3 +223,26 @@ def test_per_row_packed_metadata_matches_oracle():
     assert tuple(one.seq_idx.shape) == (1, T)
     with pytest.raises(cpla.CplaError):
         packed_meta(cus, T, P, "cpu", B=2)
+
+
+def test_delta_validation():
+    """The _delta calls check their problem before any launch; the other calls
+    refuse the delta decay; the workspace size follows its layout."""
+    p = prob(dk=64, dv=64, dtype=_lib.F32, decay=_lib.DECAY_DELTA, T=1000, num_shards=3, rank_end=3)
+    nct = 3 * 6         # shards of 334, 334 and 332 tokens: 6 chunks each
+    tok = 1 * 1000 * 2 * 64
+    assert L.cpla_delta_workspace_bytes(ctypes.byref(p)) == 4 * (4 * tok + 2 * 1 * 2 * nct * 64 * 64)
+    assert L.cpla_summary_width(ctypes.byref(p)) == 2 * 64 * 64
+    for bad in [dict(dk=128, dv=128), dict(dk=64, dv=32), dict(decay=_lib.DECAY_DIAG), dict(chunk=32),
+                dict(num_shards=65, rank_end=65)]:
+        base = dict(dk=64, dv=64, dtype=_lib.F32, decay=_lib.DECAY_DELTA)
+        base.update(bad)
+        q = prob(**base)
+        assert L.cpla_delta_workspace_bytes(ctypes.byref(q)) == -1, bad
+        st = L.cp_forward_prepare_delta(ctypes.byref(q), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+        assert st in (1, 5), (bad, st)
+    # a NULL workspace or beta is refused before any launch
+    assert L.cp_forward_prepare_delta(ctypes.byref(p), None, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == 1
+    assert L.cp_forward_prepare_delta(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
+    # the linear-attention calls refuse the delta decay
+    assert fwd_prepare(p) == 1

@@ -1,0 +1,92 @@
+"""GPU parity for the gated delta rule (dense transition) through the C ABI: the
+four _delta calls against the fp64 oracle (oracle/delta.py, the per-token
+recurrence composed through dense shard summaries) on the same seeded inputs,
+element by element: o, final state, the forward summaries (M and delta_S), the
+composed incoming states, every gradient (dq, dk, dv, dg, dbeta, dS_init), the
+backward summaries (gamma) and the composed outgoing gradients.
+
+Cases span several chunks per shard and several shards, d = 16, 32, 64 in fp32
+and bf16, an initial state, uneven shards with partial last chunks and empty
+shards, and packed sequences (one stream, and one packing per batch row) with
+boundaries inside chunks. Tolerances are the linear-attention ones (fp32 rtol
+1e-4 / atol 1e-5, bf16 rtol 2e-2 / atol 2e-3).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from _parity import assert_close, tolerances
+from oracle import delta as odelta, metadata as omd
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "fp32_d16": dict(B=2, T=512, H=2, d=16, num_shards=4, dtype=torch.float32),
+    "fp32_d32_init": dict(B=1, T=384, H=2, d=32, num_shards=3, dtype=torch.float32, with_initial_state=True),
+    "fp32_d64": dict(B=1, T=512, H=2, d=64, num_shards=4, dtype=torch.float32, with_initial_state=True),
+    "bf16_d64": dict(B=2, T=1024, H=2, d=64, num_shards=4),
+    "fp32_d64_uneven": dict(B=1, T=500, H=2, d=64, num_shards=3, dtype=torch.float32),
+    "fp32_d32_empty_shards": dict(B=1, T=200, H=1, d=32, num_shards=64, dtype=torch.float32),
+    "fp32_d64_packed": dict(B=1, T=768, H=2, d=64, num_shards=4, packed=True, len_range=(30, 300),
+                            dtype=torch.float32),
+    "bf16_d64_rows_packed": dict(B=2, T=640, H=2, d=64, num_shards=5, packed=True, len_range=(1, 200)),
+}
+
+
+def _np(t):
+    return None if t is None else t.detach().float().cpu().double().numpy()
+
+
+def _run_gpu(wl):
+    import context_state_passing_amd as cpla
+    dev = torch.device("cuda:0")
+    q, k, v, g, beta, dO = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta, wl.dO))
+    S0 = None if wl.initial_state is None else wl.initial_state.to(dev)
+    o, ctx = cpla.delta_forward(q, k, v, g, beta, num_shards=wl.num_shards, initial_state=S0,
+                                cu_seqlens=wl.cu_seqlens)
+    (dq, dk, dv, dg, db, dS0), inter = cpla.delta_backward(dO, ctx, want_intermediates=True)
+    torch.cuda.synchronize()
+    D = wl.d
+    out = {"o": o, "final_state": ctx.final_state, "M": ctx.fwd_summary[..., :D * D].reshape(-1, wl.B, wl.H, D, D),
+           "delta_S": ctx.fwd_summary[..., D * D:].reshape(-1, wl.B, wl.H, D, D), "S_in": ctx.shard_in_state,
+           "gamma": inter["bwd_summary"][..., D * D:].reshape(-1, wl.B, wl.H, D, D),
+           "dS_out": inter["shard_out_grad"], "dq": dq, "dk": dk, "dv": dv, "dg": dg, "dbeta": db}
+    if S0 is not None:
+        out["d_initial_state"] = dS0
+    return {n: _np(t) for n, t in out.items()}
+
+
+def _run_oracle(wl):
+    seq = None if wl.cu_seqlens is None else omd.seq_idx_rows(wl.cu_seqlens, wl.T)
+    args = [_np(t) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta)]
+    r = odelta.cp_backward(*args, _np(wl.dO), wl.num_shards, initial_state=_np(wl.initial_state), seq_idx=seq)
+    fw = r["fwd"]
+    out = {"o": fw["o"], "final_state": fw["final_state"], "M": fw["M"], "delta_S": fw["delta_S"],
+           "S_in": fw["S_in"], "gamma": r["gamma"], "dS_out": r["dS_out"], "dq": r["dq"], "dk": r["dk"],
+           "dv": r["dv"], "dg": r["dg"], "dbeta": r["dbeta"]}
+    if wl.initial_state is not None:
+        out["d_initial_state"] = r["d_initial_state"]
+    return out
+
+
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_delta_parity(case, gpu_available):
+    print(f"[gpu-case] delta {case}", file=sys.stderr, flush=True)
+    wl = workloads.make_delta(**CASES[case])
+    got = _run_gpu(wl)
+    ref = _run_oracle(wl)
+    rtol, atol = tolerances(wl.dtype)
+    for name in ref:
+        assert_close(name, got[name], ref[name], rtol, atol)
+
+
+def test_delta_deterministic(gpu_available):
+    print("[gpu-case] delta determinism", file=sys.stderr, flush=True)
+    wl = workloads.make_delta(**CASES["bf16_d64"])
+    a = _run_gpu(wl)
+    b = _run_gpu(wl)
+    for name in a:
+        assert np.array_equal(a[name], b[name]), name

@@ -263,3 +263,76 @@ def make_ssd(name: str = "ssd_fwdbwd", *, B: Optional[int] = None, T: Optional[i
                        x=x.to(dtp).contiguous(), dt=dt.contiguous(), A=A.contiguous(),
                        Bm=Bm.to(dtp).contiguous(), Cm=Cm.to(dtp).contiguous(), dy=dy.to(dtp).contiguous(),
                        initial_state=None if h0 is None else h0.contiguous(), cu_seqlens=cu)
+
+
+# ---- gated delta rule inputs ------------------------------------------------------------------
+# A gated-DeltaNet layer's shapes: q, k L2-normalised per head (the usual setting,
+# keeping I - beta k k^T a contraction), v ~ N(0, 1), beta = sigmoid(N(0, 1)) and a
+# per-head log-decay g = logsigmoid(N(0, 1) + 3) (about -0.05 per token).
+@dataclasses.dataclass
+class DeltaSpec:
+    index: int
+    B: int
+    T: int
+    H: int
+    d: int
+    dtype: torch.dtype
+    num_shards: int
+
+
+DELTA_SPECS = {
+    "delta_fwdbwd": DeltaSpec(7, 2, 8192, 16, 64, torch.bfloat16, 8),
+}
+
+
+@dataclasses.dataclass
+class DeltaWorkload:
+    name: str
+    B: int
+    T: int
+    H: int
+    d: int
+    dtype: torch.dtype
+    num_shards: int
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+    dO: torch.Tensor
+    initial_state: Optional[torch.Tensor]
+    cu_seqlens: Optional[object]
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+
+def make_delta(name: str = "delta_fwdbwd", *, B: Optional[int] = None, T: Optional[int] = None,
+               H: Optional[int] = None, d: Optional[int] = None, num_shards: Optional[int] = None,
+               packed: bool = False, len_range: tuple = (64, 1024), with_initial_state: bool = False,
+               dtype: Optional[torch.dtype] = None, seed_offset: int = 0) -> DeltaWorkload:
+    spec = DELTA_SPECS[name]
+    B = spec.B if B is None else B
+    T = spec.T if T is None else T
+    H = spec.H if H is None else H
+    d = spec.d if d is None else d
+    P = spec.num_shards if num_shards is None else num_shards
+    gen = torch.Generator().manual_seed(1000 + spec.index + seed_offset)
+    cu = _packing(gen, B, T, len_range[0], len_range[1]) if packed else None
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=gen, dtype=torch.float32)
+
+    q = F.normalize(randn(B, T, H, d), dim=-1)
+    k = F.normalize(randn(B, T, H, d), dim=-1)
+    v = randn(B, T, H, d)
+    beta = torch.sigmoid(randn(B, T, H))
+    g = F.logsigmoid(randn(B, T, H) + 3.0)
+    dO = randn(B, T, H, d)
+    S0 = randn(B, H, d, d) * 0.1 if with_initial_state else None
+    dt = spec.dtype if dtype is None else dtype
+    return DeltaWorkload(name=name, B=B, T=T, H=H, d=d, dtype=dt, num_shards=P,
+                         q=q.to(dt).contiguous(), k=k.to(dt).contiguous(), v=v.to(dt).contiguous(),
+                         g=g.contiguous(), beta=beta.contiguous(), dO=dO.to(dt).contiguous(),
+                         initial_state=None if S0 is None else S0.contiguous(), cu_seqlens=cu)
