@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "fwd+bwd tokens/s, chunkwise linear attn H16 d128 T8k bf16; % MFMA/HBM peak"
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+FP32_MFMA_PEAK_TFLOPS = 157.3
 KERNEL_SOURCES = ["bwd.hip", "chunk_common.hpp", "device.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_walk_diag_B4_H16_T8192_d128.txt")
 
@@ -296,6 +297,148 @@ def main_ssd(args, rank):
     print(json.dumps(out), flush=True)
 
 
+# ---- gated delta rule workload -------------------------------------------------------------
+
+def _delta_oracle_row(args):
+    h, b = args
+    from threadpoolctl import threadpool_limits
+    from oracle import delta as odelta
+    wl = _WL
+    sl = lambda x: x[b:b + 1, :, h:h + 1].double().numpy()  # noqa: E731
+    with threadpool_limits(1):
+        t = time.perf_counter()
+        q, k, v, g, beta, dO = (sl(x) for x in (wl.q, wl.k, wl.v, wl.g, wl.beta, wl.dO))
+        odelta.forward(q, k, v, g, beta)
+        odelta.backward(q, k, v, g, beta, dO)
+        return time.perf_counter() - t
+
+
+def delta_cpu_baseline(wl, rows_req):
+    global _WL
+    import multiprocessing as mp
+    _WL = wl
+    avail = len(os.sched_getaffinity(0))
+    rows = rows_req or min(16, avail)
+    workers = min(rows, avail, 16)
+    pairs = [(r % wl.H, (r // wl.H) % wl.B) for r in range(rows)]
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(workers) as pool:
+        per = pool.map(_delta_oracle_row, pairs)
+    wall = time.perf_counter() - t0
+    return {"value": rows * wl.T / wl.H / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "sample": f"fp64 gated-delta-rule oracle (per-token recurrence and adjoint) fwd+bwd on {rows} of the "
+                      f"{wl.B * wl.H} (b,h) rows at full T={wl.T}; {workers} single-threaded processes, "
+                      f"wall {wall:.1f}s, {sum(per):.1f} CPU-s; value = row-tokens/s / H",
+            "cpu_seconds": round(sum(per), 2)}
+
+
+# MFMA flops per chunk (64 tokens) and (b, h) of each call, d = d_k = d_v: 2 m n k per
+# product; the causal 64 x 64 score products count their 10 lower tiles of 16.
+def delta_flops_per_chunk(d):
+    C = 64
+    full = 2 * C * C * d                 # a 64 x 64 x d (or 64 x d x 64) product
+    tri = full * 10 // 16                # causal score tile products
+    state = 2 * C * d * d                # a 64 x d x d (or d x 64 x d) product
+    return {
+        "cp_forward_prepare_delta": tri + 2 * (2 * C * d * 2 * d),    # K K^T; W Z and K~^T U_Z on Z = [dS | M]
+        "cp_forward_apply_delta": 2 * state + tri + state + full,     # W S, K~^T U; Q K^T, Q S, P U
+        "cp_backward_prepare_delta": tri + full + 3 * state,          # Q K^T; P^T dO; K~ dS, Q^T dO, W^T dU
+        "cp_backward_apply_delta": (tri + full + 3 * state)           # the reverse walk again, then the
+        + 2 * tri                                                     # gradients: Q K^T, dO U^T;
+        + 2 * full + 2 * state                                        # dPr K, dO S0^T, dPr^T Q, U dS^T;
+        + state + tri                                                 # dU S0^T; K K^T (A);
+        + 3 * tri + 2 * full,                                         # dA (two products, K K^T); dAr K, dAr^T K
+    }
+
+
+def main_delta(args, rank):
+    """One step = the four _delta calls (forward prepare, apply; backward prepare, apply)."""
+    import torch
+    import workloads
+    wl = workloads.make_delta(args.workload)
+    cpu = None
+    if rank == 0 and not args.no_cpu_baseline:
+        cpu = delta_cpu_baseline(wl, args.cpu_rows)
+    from context_state_passing_amd import _lib
+    from context_state_passing_amd.api import _ptr, make_problem
+
+    dev = torch.device("cuda:0")
+    q, k, v, g, beta, dO = (t.to(dev) for t in (wl.q, wl.k, wl.v, wl.g, wl.beta, wl.dO))
+    B, T, H, d, P = wl.B, wl.T, wl.H, wl.d, wl.num_shards
+    p = make_problem(q, v, P, _lib.DECAY_DELTA)
+    L = _lib.lib()
+    W = L.cpla_summary_width(ctypes.byref(p))
+    f32 = dict(device=dev, dtype=torch.float32)
+    ws = torch.empty((L.cpla_delta_workspace_bytes(ctypes.byref(p)) // 4,), **f32)
+    fsum, bsum = torch.empty((P, B, H, W), **f32), torch.empty((P, B, H, W), **f32)
+    s_in, s_out = torch.empty((P, B, H, d, d), **f32), torch.empty((P, B, H, d, d), **f32)
+    fin = torch.empty((B, H, d, d), **f32)
+    o = torch.empty_like(v)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg, db = torch.empty_like(g), torch.empty_like(beta)
+    stream = torch.cuda.current_stream()
+    st = ctypes.c_void_p(stream.cuda_stream)
+    pp = ctypes.byref(p)
+    chk = _lib.check
+
+    def step(ev=None):
+        if ev: ev[0].record(stream)
+        chk(L.cp_forward_prepare_delta(pp, None, _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(fsum), _ptr(ws), st))
+        if ev: ev[1].record(stream)
+        chk(L.cp_forward_apply_delta(pp, None, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(fsum), None,
+                                     _ptr(o), _ptr(s_in), _ptr(fin), _ptr(ws), st))
+        if ev: ev[2].record(stream)
+        chk(L.cp_backward_prepare_delta(pp, None, _ptr(q), _ptr(k), _ptr(g), _ptr(beta), _ptr(dO), _ptr(fsum),
+                                        _ptr(bsum), _ptr(ws), st))
+        if ev: ev[3].record(stream)
+        chk(L.cp_backward_apply_delta(pp, None, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(dO),
+                                      _ptr(bsum), None, _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(db),
+                                      _ptr(s_out), None, _ptr(ws), st))
+        if ev: ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    names = ["cp_forward_prepare_delta", "cp_forward_apply_delta", "cp_backward_prepare_delta",
+             "cp_backward_apply_delta"]
+    parts = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(4)]
+    tokens = B * T
+    chunks = B * H * (T // 64)
+    fl = delta_flops_per_chunk(d)
+    dom = "cp_backward_apply_delta"
+    dom_ms = parts[3]
+    dom_flops = fl[dom] * chunks
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    step_flops = sum(fl.values()) * chunks
+    out = {
+        "metric": f"fwd+bwd tokens/s, gated delta rule {wl.name} (B{B} H{H} T{T} d={d})",
+        "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "H": H, "dk": d, "dv": d, "chunk": 64, "shards": P,
+                   "decay": "gated delta rule (dense transition)", "inputs": "bf16" if wl.dtype == torch.bfloat16
+                   else "f32", "parallelism": "single-gpu (shards simulated in HBM)"},
+        "roofline": {"bound": "mfma", "kernel": "cp_backward_apply_delta (delta_scan, delta_bwalk, delta_grad)",
+                     "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
+                     "traffic_note": "counters are taken for the default workload",
+                     "algorithmic_flops_per_launch": dom_flops, "launch_ms": dom_ms},
+        "step_breakdown_ms": dict(zip(names, parts)),
+        "step_roofline": {"mfma_TFLOPs": step_flops / (ms_step * 1e-3) / 1e12,
+                          "mfma_frac": step_flops / (ms_step * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 # ---- GPU run --------------------------------------------------------------------------------
 
 def main():
@@ -312,6 +455,9 @@ def main():
     import workloads
     if args.workload in workloads.SSD_SPECS:
         main_ssd(args, rank)
+        return
+    if args.workload in workloads.DELTA_SPECS:
+        main_delta(args, rank)
         return
     wl = workloads.make(args.workload)
     cpu = None
