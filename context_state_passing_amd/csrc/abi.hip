@@ -454,7 +454,7 @@ enum DeltaPhase { DP_FWD_PREPARE, DP_FWD_APPLY_WALK, DP_FWD_OUT, DP_BWD_PREPARE,
 template <typename E, int D>
 void delta_launch(DeltaPhase ph, const cpla_problem* p, const DeltaArgs& a, hipStream_t stream) {
   const dim3 ranks(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), chunks(delta_chunks(p), (unsigned)(p->B * p->H));
-  const dim3 nt(256);
+  const dim3 nt(DELTA_THREADS);
   switch (ph) {
     case DP_FWD_PREPARE:
       if (chunks.x) hipLaunchKernelGGL((delta_wy<E, D>), chunks, nt, 0, stream, a);
@@ -498,9 +498,9 @@ cpla_status delta_scan_run(const cpla_problem* p, const float* summary, const in
   s.out = out;
   s.fin = fin;
   const dim3 grid((unsigned)s.BH);
-  if (p->dk == 16) hipLaunchKernelGGL(delta_scan<16>, grid, dim3(256), 0, stream, s);
-  else if (p->dk == 32) hipLaunchKernelGGL(delta_scan<32>, grid, dim3(256), 0, stream, s);
-  else hipLaunchKernelGGL(delta_scan<64>, grid, dim3(256), 0, stream, s);
+  if (p->dk == 16) hipLaunchKernelGGL(delta_scan<16>, grid, dim3(DELTA_THREADS), 0, stream, s);
+  else if (p->dk == 32) hipLaunchKernelGGL(delta_scan<32>, grid, dim3(DELTA_THREADS), 0, stream, s);
+  else hipLaunchKernelGGL(delta_scan<64>, grid, dim3(DELTA_THREADS), 0, stream, s);
   return launched("delta_scan");
 }
 

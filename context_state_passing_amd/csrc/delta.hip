@@ -15,7 +15,7 @@
 // The solve is the WY form of the product of the chunk's transitions: the
 // chunk's own map is M_c = live_last e^{Gam_last} I - K~^T W.
 //
-// Kernels (one workgroup of four waves each; every contraction is fp32 MFMA
+// Kernels (one workgroup of eight waves each; every contraction is fp32 MFMA
 // 16x16x4 on fp32 LDS tiles, inputs widened on load):
 //   delta_wy      per chunk:  U~, W (triangular solve, one column per thread)
 //   delta_fwalk   per shard:  chunk walk of the state; prepare folds [delta_S | M]
@@ -33,7 +33,8 @@
 namespace cpla {
 namespace {
 
-constexpr int NTH = 256, NWV = 4;
+constexpr int NTH = DELTA_THREADS, NWV = DELTA_THREADS / 64;
+static_assert(NWV % 4 == 0, "a wave's score tiles share one column tile");
 
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -197,29 +198,29 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
   }
   __syncthreads();
 
-  // forward substitution (I + A) X = [beta V | beta live e^Gam K], one column per
-  // thread, in place in the LDS tiles (a register-resident column made the
-  // compiler hold the hoisted rows of A in every register and spill)
-  const int col = threadIdx.x;
-  if (col < 2 * D) {
+  // forward substitution (I + A) X = [beta V | beta live e^Gam K] in place in the
+  // LDS tiles (a register-resident column made the compiler hold the hoisted rows
+  // of A in every register and spill): four lanes per column, each summing every
+  // fourth earlier row; lane 0 of the four updates the row. The lanes of a column
+  // sit in one wave, whose LDS accesses complete in order.
+  const int col = 16 * (threadIdx.x >> 6) + (lane_id() >> 2), part = lane_id() & 3;
+  if (col < 2 * D) {   // uniform per wave
     const bool isv = col < D;
     const int cc = isv ? col : col - D;
     float* xc = (isv ? s_v : s_k) + cc;
-    for (int i = 0; i < CH; ++i) xc[i * G::LD] *= isv ? s_t.beta[i] : s_t.beta[i] * s_t.eg[i];
+    for (int i = part; i < CH; i += 4) xc[i * G::LD] *= isv ? s_t.beta[i] : s_t.beta[i] * s_t.eg[i];
+    asm volatile("" ::: "memory");
     for (int i = 1; i < CH; ++i) {
       const float* ai = s_a + i * G::LC;
-      float acc = xc[i * G::LD];
-      int j = 0;
-      for (; j + 4 <= i; j += 4) {
-        const f32x4 av = *reinterpret_cast<const f32x4*>(ai + j);
-        acc -= av[0] * xc[j * G::LD] + av[1] * xc[(j + 1) * G::LD] + av[2] * xc[(j + 2) * G::LD] +
-               av[3] * xc[(j + 3) * G::LD];
-      }
-      for (; j < i; ++j) acc -= ai[j] * xc[j * G::LD];
-      xc[i * G::LD] = acc;
+      float acc = 0.f;
+      for (int j = part; j < i; j += 4) acc += ai[j] * xc[j * G::LD];
+      acc += __shfl_xor(acc, 1, 64);
+      acc += __shfl_xor(acc, 2, 64);
+      if (part == 0) xc[i * G::LD] -= acc;
+      asm volatile("" ::: "memory");   // later rows re-read what lane 0 wrote
     }
     float* dst = isv ? a.ws_ut : a.ws_w;
-    for (int i = 0; i < n; ++i) dst[((b * a.T + t0 + i) * a.H + h) * D + cc] = xc[i * G::LD];
+    for (int i = part; i < n; i += 4) dst[((b * a.T + t0 + i) * a.H + h) * D + cc] = xc[i * G::LD];
   }
 }
 
@@ -514,6 +515,7 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
   __shared__ __attribute__((aligned(16))) float s_slot[8][G::TILE_C];
   __shared__ ChunkTerms s_t;
   __shared__ float s_rp[3][NWV][CH];   // per-wave row partials
+  __shared__ float s_colp[NWV][CH];    // per-wave column partials
   __shared__ float s_cp[2][CH];        // column sums
   __shared__ float s_red[NWV];
   int64_t r, c;
@@ -536,6 +538,7 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
   load_mat<D>(s_s0, a.chunk_states + (bh * nct + idx) * (int64_t)(D * D));
   load_mat<D>(s_ds, a.ws_dsc + (bh * nct + idx) * (int64_t)(D * D));
   for (int e = threadIdx.x; e < 3 * NWV * CH; e += NTH) (&s_rp[0][0][0])[e] = 0.f;
+  for (int e = threadIdx.x; e < NWV * CH; e += NTH) (&s_colp[0][0])[e] = 0.f;
   chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
 
   // score tiles: dPr and the decay terms of dGam (rows of wave w's column tile tj = w)
@@ -575,9 +578,15 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
       colp += __shfl_xor(colp, 32, 64);
       colacc[0] += colp;
     }
-    if (l < 16) s_cp[0][16 * w + l] = colacc[0];   // column tile tj = w, summed over its row tiles
+    if (l < 16) s_colp[w][16 * (w & 3) + l] = colacc[0];   // the wave's column tile, over its row tiles
   }
   __syncthreads();
+  if (threadIdx.x < CH) {
+    float x = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) x += s_colp[ww][threadIdx.x];
+    s_cp[0][threadIdx.x] = x;
+  }
 
   // dq = dPr K + eg (dO S0^T); dk (part) = dPr^T Q + el (U dS^T); row partials of
   // Q . (dO S0^T) and el (U dS^T) . K
@@ -637,7 +646,12 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     float tks = tk;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) tks += __shfl_xor(tks, off, 64);
-    if (i == CH - 1) dgam += tks + s_t.sc[0] * (s_red[0] + s_red[1] + s_red[2] + s_red[3]);
+    if (i == CH - 1) {
+      float sp = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NWV; ++ww) sp += s_red[ww];
+      dgam += tks + s_t.sc[0] * sp;
+    }
     s_cp[1][i] = dgam;
   }
   __syncthreads();
@@ -674,20 +688,28 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     }
   }
   __syncthreads();
-  // backward substitution (I + A)^T dB = [dU | dW], one column per thread, in place
-  if (threadIdx.x < 2 * D) {
-    const bool isv = threadIdx.x < D;
-    float* xc = (isv ? s_dU : s_dW) + (isv ? threadIdx.x : threadIdx.x - D);
-    for (int i = CH - 2; i >= 0; --i) {
-      float acc = xc[i * G::LD];
-      for (int j = i + 1; j < CH; ++j) acc -= s_a[j * G::LC + i] * xc[j * G::LD];
-      xc[i * G::LD] = acc;
+  // backward substitution (I + A)^T dB = [dU | dW] in place, four lanes per column
+  // as in the forward solve
+  {
+    const int col = 16 * w + (l >> 2), part = l & 3;
+    if (col < 2 * D) {
+      const bool isv = col < D;
+      float* xc = (isv ? s_dU : s_dW) + (isv ? col : col - D);
+      for (int i = CH - 2; i >= 0; --i) {
+        float acc = 0.f;
+        for (int j = i + 1 + part; j < CH; j += 4) acc += s_a[j * G::LC + i] * xc[j * G::LD];
+        acc += __shfl_xor(acc, 1, 64);
+        acc += __shfl_xor(acc, 2, 64);
+        if (part == 0) xc[i * G::LD] -= acc;
+        asm volatile("" ::: "memory");
+      }
     }
   }
   __syncthreads();
   // dA = strict-lower(-(dBv U~^T + dBk W^T)); dAr = dA . D . beta_i into slot 4;
   // row sums of dA . D . KK^T (dbeta) and column sums of dA . A (dGam)
   for (int e = threadIdx.x; e < 2 * NWV * CH; e += NTH) (&s_rp[0][0][0])[e] = 0.f;
+  for (int e = threadIdx.x; e < NWV * CH; e += NTH) (&s_colp[0][0])[e] = 0.f;
   __syncthreads();
   {
     float colacc = 0.f;
@@ -723,7 +745,14 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
       colp += __shfl_xor(colp, 32, 64);
       colacc += colp;
     }
-    if (l < 16) s_cp[0][16 * w + l] = colacc;
+    if (l < 16) s_colp[w][16 * (w & 3) + l] = colacc;
+  }
+  __syncthreads();
+  if (threadIdx.x < CH) {
+    float x = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) x += s_colp[ww][threadIdx.x];
+    s_cp[0][threadIdx.x] = x;
   }
   __syncthreads();
   // dk = part + dAr K + dAr^T K + beta eg dBk; dv = beta dBv

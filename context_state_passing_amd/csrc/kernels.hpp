@@ -56,6 +56,8 @@ struct ScanArgs {
 // The gated delta rule (dense transition), d_k = d_v = D. Workspace tensors are
 // fp32: ws_ut, ws_w, ws_u, ws_du [B,T,H,D]; chunk states and ws_dsc (the gradient
 // at every chunk's end) [B,H,row_chunks,D,D].
+constexpr int DELTA_THREADS = 512;   // threads per workgroup of every delta-rule kernel
+
 struct DeltaArgs {
   int64_t B, T, H;
   int P, rank_begin;
