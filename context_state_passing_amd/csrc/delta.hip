@@ -41,12 +41,23 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
 }
 
 // One 16 x 16 output tile: acc += sum_{k < K} a(i, k) b(k, j). Lane l supplies
-// A[l % 16][k0 + l / 16] and B[k0 + l / 16][l % 16]; the accumulator holds rows
+// A[l % 16][k] and B[k][l % 16] for its k of the step; the accumulator holds rows
 // 4 (l / 16) + r, column l % 16.
-template <class FA, class FB>
-__device__ __forceinline__ f32x4 tile_mm(int K, const FA& a, const FB& b, f32x4 acc) {
+// The sum over k is split so that lane group kk = l / 16 supplies k = kk K/4 + s
+// at step s: a lane's operands then run over K/4 consecutive k, which row-major
+// tiles serve with 16-byte LDS reads.
+template <int K, class FA, class FB>
+__device__ __forceinline__ f32x4 tile_mm(const FA& a, const FB& b, f32x4 acc) {
+  constexpr int S = K / 4;
   const int l = lane_id(), x = l & 15, kk = l >> 4;
-  for (int k0 = 0; k0 < K; k0 += 4) acc = mfma_f32(a(x, k0 + kk), b(k0 + kk, x), acc);
+  float av[S], bv[S];
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    av[s] = a(x, kk * S + s);
+    bv[s] = b(kk * S + s, x);
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s) acc = mfma_f32(av[s], bv[s], acc);
   return acc;
 }
 
@@ -187,7 +198,7 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti)
-      acc = tile_mm(D, [&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+      acc = tile_mm<D>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -268,7 +279,7 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     // U_Z = U~_Z - W Z
     for (int t = w; t < 4 * (NZ / 16); t += NWV) {
       const int ti = t / (NZ / 16), tj = t % (NZ / 16);
-      f32x4 acc = tile_mm(D, [&](int i, int k) { return s_w[(16 * ti + i) * G::LD + k]; },
+      f32x4 acc = tile_mm<D>([&](int i, int k) { return s_w[(16 * ti + i) * G::LD + k]; },
                           [&](int k, int j) { return s_z[k * LZ + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -287,7 +298,7 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     const float sc = s_t.sc[0];
     for (int t = w; t < (D / 16) * (NZ / 16); t += NWV) {
       const int ti = t / (NZ / 16), tj = t % (NZ / 16);
-      f32x4 acc = tile_mm(CH, [&](int i, int k) { return s_k[k * G::LD + 16 * ti + i] * s_t.el[k]; },
+      f32x4 acc = tile_mm<CH>([&](int i, int k) { return s_k[k * G::LD + 16 * ti + i] * s_t.el[k]; },
                           [&](int k, int j) { return s_u[k * LZ + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -341,9 +352,9 @@ __global__ __launch_bounds__(NTH) void delta_scan(DeltaScanArgs a) {
       if (t >= NT2) continue;
       const int ti = t / (D / 16), tj = t % (D / 16);
       f32x4 acc = a.reverse
-          ? tile_mm(D, [&](int i, int k) { return s_m[k * G::LD + 16 * ti + i]; },
+          ? tile_mm<D>([&](int i, int k) { return s_m[k * G::LD + 16 * ti + i]; },
                     [&](int k, int j) { return s_s[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f})
-          : tile_mm(D, [&](int i, int k) { return s_m[(16 * ti + i) * G::LD + k]; },
+          : tile_mm<D>([&](int i, int k) { return s_m[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_s[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -393,7 +404,7 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti)
-      acc = tile_mm(D, [&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+      acc = tile_mm<D>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -406,9 +417,9 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
   E* o = reinterpret_cast<E*>(a.out);
   for (int t = w; t < 4 * G::NTC; t += NWV) {
     const int ti = t / G::NTC, tj = t % G::NTC;
-    f32x4 x = tile_mm(D, [&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+    f32x4 x = tile_mm<D>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                       [&](int k, int j) { return s_s[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-    f32x4 y = tile_mm(CH, [&](int i, int k) { return s_p[(16 * ti + i) * G::LC + k]; },
+    f32x4 y = tile_mm<CH>([&](int i, int k) { return s_p[(16 * ti + i) * G::LC + k]; },
                       [&](int k, int j) { return s_u[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -450,7 +461,7 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
       const int ti = t >> 2, tj = t & 3;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       if (tj <= ti)
-        acc = tile_mm(D, [&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+        acc = tile_mm<D>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                       [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -463,9 +474,9 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
     // dU = P^T dO + K~ dS
     for (int t = w; t < 4 * G::NTC; t += NWV) {
       const int ti = t / G::NTC, tj = t % G::NTC;
-      f32x4 acc = tile_mm(CH, [&](int i, int k) { return s_p[k * G::LC + 16 * ti + i]; },
+      f32x4 acc = tile_mm<CH>([&](int i, int k) { return s_p[k * G::LC + 16 * ti + i]; },
                           [&](int k, int j) { return s_do[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      acc = tile_mm(D, [&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k] * s_t.el[16 * ti + i]; },
+      acc = tile_mm<D>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k] * s_t.el[16 * ti + i]; },
                     [&](int k, int j) { return s_ds[k * G::LD + 16 * tj + j]; }, acc);
 #pragma unroll
       for (int q = 0; q < 4; ++q) s_du[(16 * ti + 4 * (l >> 4) + q) * G::LD + 16 * tj + (l & 15)] = acc[q];
@@ -476,9 +487,9 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
     const float sc = s_t.sc[0];
     for (int t = w; t < G::NTC * G::NTC; t += NWV) {
       const int ti = t / G::NTC, tj = t % G::NTC;
-      f32x4 x = tile_mm(CH, [&](int i, int k) { return s_q[k * G::LD + 16 * ti + i] * s_t.eg[k]; },
+      f32x4 x = tile_mm<CH>([&](int i, int k) { return s_q[k * G::LD + 16 * ti + i] * s_t.eg[k]; },
                         [&](int k, int j) { return s_do[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 y = tile_mm(CH, [&](int i, int k) { return s_w[k * G::LD + 16 * ti + i]; },
+      f32x4 y = tile_mm<CH>([&](int i, int k) { return s_w[k * G::LD + 16 * ti + i]; },
                         [&](int k, int j) { return s_du[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -548,9 +559,9 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
       const int ti = t >> 2, tj = t & 3;
       f32x4 qk = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
       if (tj <= ti) {
-        qk = tile_mm(D, [&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+        qk = tile_mm<D>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                      [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, qk);
-        du = tile_mm(D, [&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
+        du = tile_mm<D>([&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
                      [&](int k, int j) { return s_u[(16 * tj + j) * G::LD + k]; }, du);
       }
       float rowp[4], colp = 0.f;
@@ -594,13 +605,13 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     E* dq = reinterpret_cast<E*>(a.dq);
     for (int t = w; t < 4 * G::NTC; t += NWV) {
       const int ti = t / G::NTC, tj = t % G::NTC;
-      f32x4 x = tile_mm(CH, [&](int i, int k) { return s_dp[(16 * ti + i) * G::LC + k]; },
+      f32x4 x = tile_mm<CH>([&](int i, int k) { return s_dp[(16 * ti + i) * G::LC + k]; },
                         [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 y = tile_mm(D, [&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
+      f32x4 y = tile_mm<D>([&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
                         [&](int k, int j) { return s_s0[(16 * tj + j) * G::LD + k]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 z = tile_mm(CH, [&](int i, int k) { return s_dp[k * G::LC + 16 * ti + i]; },
+      f32x4 z = tile_mm<CH>([&](int i, int k) { return s_dp[k * G::LC + 16 * ti + i]; },
                         [&](int k, int j) { return s_q[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 u = tile_mm(D, [&](int i, int k) { return s_u[(16 * ti + i) * G::LD + k]; },
+      f32x4 u = tile_mm<D>([&](int i, int k) { return s_u[(16 * ti + i) * G::LD + k]; },
                         [&](int k, int j) { return s_ds[(16 * tj + j) * G::LD + k]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -666,7 +677,7 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
   // dW = -dU S0^T
   for (int t = w; t < 4 * G::NTC; t += NWV) {
     const int ti = t / G::NTC, tj = t % G::NTC;
-    f32x4 x = tile_mm(D, [&](int i, int k) { return s_dU[(16 * ti + i) * G::LD + k]; },
+    f32x4 x = tile_mm<D>([&](int i, int k) { return s_dU[(16 * ti + i) * G::LD + k]; },
                       [&](int k, int j) { return s_s0[(16 * tj + j) * G::LD + k]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int q = 0; q < 4; ++q) s_dW[(16 * ti + 4 * (l >> 4) + q) * G::LD + 16 * tj + (l & 15)] = -x[q];
@@ -678,7 +689,7 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti)
-      acc = tile_mm(D, [&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+      acc = tile_mm<D>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -717,11 +728,11 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
       const int ti = t >> 2, tj = t & 3;
       f32x4 x = {0.f, 0.f, 0.f, 0.f}, kk = {0.f, 0.f, 0.f, 0.f};
       if (tj <= ti) {
-        x = tile_mm(D, [&](int i, int k) { return s_dU[(16 * ti + i) * G::LD + k]; },
+        x = tile_mm<D>([&](int i, int k) { return s_dU[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_ut[(16 * tj + j) * G::LD + k]; }, x);
-        x = tile_mm(D, [&](int i, int k) { return s_dW[(16 * ti + i) * G::LD + k]; },
+        x = tile_mm<D>([&](int i, int k) { return s_dW[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_w[(16 * tj + j) * G::LD + k]; }, x);
-        kk = tile_mm(D, [&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+        kk = tile_mm<D>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
                      [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, kk);
       }
       float colp = 0.f;
@@ -761,9 +772,9 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     E* dv = reinterpret_cast<E*>(a.dv);
     for (int t = w; t < 4 * G::NTC; t += NWV) {
       const int ti = t / G::NTC, tj = t % G::NTC;
-      f32x4 x = tile_mm(CH, [&](int i, int k) { return s_a[(16 * ti + i) * G::LC + k]; },
+      f32x4 x = tile_mm<CH>([&](int i, int k) { return s_a[(16 * ti + i) * G::LC + k]; },
                         [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      x = tile_mm(CH, [&](int i, int k) { return s_a[k * G::LC + 16 * ti + i]; },
+      x = tile_mm<CH>([&](int i, int k) { return s_a[k * G::LC + 16 * ti + i]; },
                   [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, x);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
