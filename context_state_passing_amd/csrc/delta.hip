@@ -554,7 +554,7 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
 
   // score tiles: dPr and the decay terms of dGam (rows of wave w's column tile tj = w)
   {
-    float colacc[1] = {0.f};
+    float colacc = 0.f;
     for (int t = w; t < 16; t += NWV) {
       const int ti = t >> 2, tj = t & 3;
       f32x4 qk = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
@@ -587,9 +587,9 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
       }
       colp += __shfl_xor(colp, 16, 64);
       colp += __shfl_xor(colp, 32, 64);
-      colacc[0] += colp;
+      colacc += colp;
     }
-    if (l < 16) s_colp[w][16 * (w & 3) + l] = colacc[0];   // the wave's column tile, over its row tiles
+    if (l < 16) s_colp[w][16 * (w & 3) + l] = colacc;   // the wave's column tile, over its row tiles
   }
   __syncthreads();
   if (threadIdx.x < CH) {
