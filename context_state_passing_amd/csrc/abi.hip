@@ -43,11 +43,16 @@ cpla_status check_problem(const cpla_problem* p) {
   if (p->num_shards > 64) return fail(CPLA_E_UNSUPPORTED, "num_shards=%d > 64 unsupported", p->num_shards);
   if (p->rank_begin < 0 || p->rank_end > p->num_shards || p->rank_begin >= p->rank_end)
     return fail(CPLA_E_INVALID, "rank range [%d, %d) outside [0, %d)", p->rank_begin, p->rank_end, p->num_shards);
-  if (p->dk != p->dv) return fail(CPLA_E_UNSUPPORTED, "dk != dv unsupported");
   const bool bf = p->dtype == CPLA_BF16;
-  if (!(p->dk == 16 || p->dk == 64 || (bf && p->dk == 128)))
+  if (p->dk != p->dv) {
+    const bool mixed = bf && ((p->dk == 64 && p->dv == 128) || (p->dk == 128 && p->dv == 64));
+    if (!mixed)
+      return fail(CPLA_E_UNSUPPORTED, "dk=%lld, dv=%lld unsupported for dtype %s (dk != dv: bf16 64/128 or 128/64)",
+                  (long long)p->dk, (long long)p->dv, bf ? "bf16" : "fp32");
+  } else if (!(p->dk == 16 || p->dk == 64 || (bf && p->dk == 128))) {
     return fail(CPLA_E_UNSUPPORTED, "head dim %lld unsupported for dtype %s (bf16: 16, 64, 128; fp32: 16, 64)",
                 (long long)p->dk, bf ? "bf16" : "fp32");
+  }
   if (p->B * p->H > 65535) return fail(CPLA_E_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)(p->B * p->H));
   return CPLA_OK;
 }
@@ -93,47 +98,51 @@ bool needs_tail(const cpla_problem* p) {
 }
 
 template <bool APPLY, bool TAIL>
-fwd_fn pick_fwd_t(int dtype, int D, int decay) {
-#define CPLA_FWD_CASE(E, DD)                                              \
-  if (D == DD) {                                                          \
-    if (decay == 0) return fwd_walk<E, DD, DD, 0, APPLY, TAIL>;           \
-    if (decay == 1) return fwd_walk<E, DD, DD, 1, APPLY, TAIL>;           \
-    return fwd_walk<E, DD, DD, 2, APPLY, TAIL>;                           \
+fwd_fn pick_fwd_t(int dtype, int DK, int DV, int decay) {
+#define CPLA_FWD_CASE(E, KK, VV)                                          \
+  if (DK == KK && DV == VV) {                                             \
+    if (decay == 0) return fwd_walk<E, KK, VV, 0, APPLY, TAIL>;           \
+    if (decay == 1) return fwd_walk<E, KK, VV, 1, APPLY, TAIL>;           \
+    return fwd_walk<E, KK, VV, 2, APPLY, TAIL>;                           \
   }
   if (dtype == CPLA_BF16) {
-    CPLA_FWD_CASE(bf16_t, 16)
-    CPLA_FWD_CASE(bf16_t, 64)
-    CPLA_FWD_CASE(bf16_t, 128)
+    CPLA_FWD_CASE(bf16_t, 16, 16)
+    CPLA_FWD_CASE(bf16_t, 64, 64)
+    CPLA_FWD_CASE(bf16_t, 128, 128)
+    CPLA_FWD_CASE(bf16_t, 64, 128)
+    CPLA_FWD_CASE(bf16_t, 128, 64)
   } else {
-    CPLA_FWD_CASE(float, 16)
-    CPLA_FWD_CASE(float, 64)
+    CPLA_FWD_CASE(float, 16, 16)
+    CPLA_FWD_CASE(float, 64, 64)
   }
 #undef CPLA_FWD_CASE
   return nullptr;
 }
 
 template <bool APPLY, bool TAIL>
-bwd_fn pick_bwd_t(int dtype, int D, int decay, bool grad_f32) {
-  if (grad_f32) {   // fp32 gradients from bf16 inputs: scalar decay only
-    if (!APPLY || dtype != CPLA_BF16 || decay != CPLA_DECAY_SCALAR) return nullptr;
-    if (D == 16) return bwd_walk<bf16_t, 16, 16, 1, true, true, TAIL>;
-    if (D == 64) return bwd_walk<bf16_t, 64, 64, 1, true, true, TAIL>;
-    if (D == 128) return bwd_walk<bf16_t, 128, 128, 1, true, true, TAIL>;
+bwd_fn pick_bwd_t(int dtype, int DK, int DV, int decay, bool grad_f32) {
+  if (grad_f32) {   // fp32 gradients from bf16 inputs: scalar decay only, dk == dv
+    if (!APPLY || dtype != CPLA_BF16 || decay != CPLA_DECAY_SCALAR || DK != DV) return nullptr;
+    if (DK == 16) return bwd_walk<bf16_t, 16, 16, 1, true, true, TAIL>;
+    if (DK == 64) return bwd_walk<bf16_t, 64, 64, 1, true, true, TAIL>;
+    if (DK == 128) return bwd_walk<bf16_t, 128, 128, 1, true, true, TAIL>;
     return nullptr;
   }
-#define CPLA_BWD_CASE(E, DD)                                              \
-  if (D == DD) {                                                          \
-    if (decay == 0) return bwd_walk<E, DD, DD, 0, APPLY, false, TAIL>;    \
-    if (decay == 1) return bwd_walk<E, DD, DD, 1, APPLY, false, TAIL>;    \
-    return bwd_walk<E, DD, DD, 2, APPLY, false, TAIL>;                    \
+#define CPLA_BWD_CASE(E, KK, VV)                                          \
+  if (DK == KK && DV == VV) {                                             \
+    if (decay == 0) return bwd_walk<E, KK, VV, 0, APPLY, false, TAIL>;    \
+    if (decay == 1) return bwd_walk<E, KK, VV, 1, APPLY, false, TAIL>;    \
+    return bwd_walk<E, KK, VV, 2, APPLY, false, TAIL>;                    \
   }
   if (dtype == CPLA_BF16) {
-    CPLA_BWD_CASE(bf16_t, 16)
-    CPLA_BWD_CASE(bf16_t, 64)
-    CPLA_BWD_CASE(bf16_t, 128)
+    CPLA_BWD_CASE(bf16_t, 16, 16)
+    CPLA_BWD_CASE(bf16_t, 64, 64)
+    CPLA_BWD_CASE(bf16_t, 128, 128)
+    CPLA_BWD_CASE(bf16_t, 64, 128)
+    CPLA_BWD_CASE(bf16_t, 128, 64)
   } else {
-    CPLA_BWD_CASE(float, 16)
-    CPLA_BWD_CASE(float, 64)
+    CPLA_BWD_CASE(float, 16, 16)
+    CPLA_BWD_CASE(float, 64, 64)
   }
 #undef CPLA_BWD_CASE
   return nullptr;
@@ -142,13 +151,13 @@ bwd_fn pick_bwd_t(int dtype, int D, int decay, bool grad_f32) {
 // the kernel for a problem: the TAIL variant only when some shard ends inside a chunk
 template <bool APPLY>
 fwd_fn pick_fwd(const cpla_problem* p) {
-  return needs_tail(p) ? pick_fwd_t<APPLY, true>(p->dtype, (int)p->dk, p->decay)
-                       : pick_fwd_t<APPLY, false>(p->dtype, (int)p->dk, p->decay);
+  return needs_tail(p) ? pick_fwd_t<APPLY, true>(p->dtype, (int)p->dk, (int)p->dv, p->decay)
+                       : pick_fwd_t<APPLY, false>(p->dtype, (int)p->dk, (int)p->dv, p->decay);
 }
 template <bool APPLY>
 bwd_fn pick_bwd(const cpla_problem* p, bool grad_f32 = false) {
-  return needs_tail(p) ? pick_bwd_t<APPLY, true>(p->dtype, (int)p->dk, p->decay, grad_f32)
-                       : pick_bwd_t<APPLY, false>(p->dtype, (int)p->dk, p->decay, grad_f32);
+  return needs_tail(p) ? pick_bwd_t<APPLY, true>(p->dtype, (int)p->dk, (int)p->dv, p->decay, grad_f32)
+                       : pick_bwd_t<APPLY, false>(p->dtype, (int)p->dk, (int)p->dv, p->decay, grad_f32);
 }
 
 unsigned threads_for(const cpla_problem* p) {

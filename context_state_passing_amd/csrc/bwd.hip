@@ -90,8 +90,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
   constexpr int QHL = (SCAL && SP) ? 1 : 0;
   // region: Gam (diag, fp32) during staging, then A/dA hi/lo and the scalar P tile.
   // The prepare walk (two workgroups per CU) stages Gam rows 32..63 in the dO
-  // tile's buffer, written after the q tile is scaled.
-  constexpr bool GSPLIT = !APPLY && DIAG;
+  // tile's buffer, written after the q tile is scaled (when they fit there: not
+  // with d_v narrower than d_k).
+  constexpr bool GSPLIT = !APPLY && DIAG && G::TILE_V * (int)sizeof(E) >= (CH / 2) * DK * 4;
   constexpr int GAM_BYTES = DIAG ? (GSPLIT ? CH / 2 : CH) * DK * 4 : 0;
   constexpr int AT_BYTES = APPLY ? (SP ? 4 : 2) * G::TILE_A * (int)sizeof(E) : 0;
   constexpr int P_BYTES = (APPLY && SCAL) ? CH * (CH + 1) * 4 : 0;
@@ -99,8 +100,10 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
   // Apply walk, bf16 with a diagonal decay: the next chunk's raw inputs are copied
   // into LDS by DMA once the dk phase is done (q into a buffer of its own; k, v,
   // dO and g into the k, v, k-lo and score-tile regions, dead from there to the
-  // end of the chunk), so their HBM latency overlaps dg and the dS update.
-  constexpr bool PF = APPLY && DIAG && SP;
+  // end of the chunk), so their HBM latency overlaps dg and the dS update. The raw
+  // dO goes to the k-lo region, so this needs d_v <= d_k + pad; wider d_v loads
+  // each chunk at its start instead.
+  constexpr bool PF = APPLY && DIAG && SP && G::TILE_K >= CH * DV;
   static_assert(!PF || GamRegs<DK, DECAY, G::NT>::DMA_FLOATS * 4 <= REG_BYTES, "raw g must fit");
 
   __shared__ __attribute__((aligned(16))) E s_q[G::TILE_K];
@@ -827,15 +830,18 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
   }
 }
 
-#define CPLA_INST_BWD(E, D, DEC)                                                   \
-  template __global__ void bwd_walk<E, D, D, DEC, false, false, false>(BwdArgs);  \
-  template __global__ void bwd_walk<E, D, D, DEC, true, false, false>(BwdArgs);   \
-  template __global__ void bwd_walk<E, D, D, DEC, false, false, true>(BwdArgs);   \
-  template __global__ void bwd_walk<E, D, D, DEC, true, false, true>(BwdArgs);
-#define CPLA_INST_BWD3(E, D) CPLA_INST_BWD(E, D, 0) CPLA_INST_BWD(E, D, 1) CPLA_INST_BWD(E, D, 2)
+#define CPLA_INST_BWD(E, DK, DV, DEC)                                              \
+  template __global__ void bwd_walk<E, DK, DV, DEC, false, false, false>(BwdArgs); \
+  template __global__ void bwd_walk<E, DK, DV, DEC, true, false, false>(BwdArgs);  \
+  template __global__ void bwd_walk<E, DK, DV, DEC, false, false, true>(BwdArgs);  \
+  template __global__ void bwd_walk<E, DK, DV, DEC, true, false, true>(BwdArgs);
+#define CPLA_INST_BWD3(E, D) CPLA_INST_BWD(E, D, D, 0) CPLA_INST_BWD(E, D, D, 1) CPLA_INST_BWD(E, D, D, 2)
+#define CPLA_INST_BWD3X(E, DK, DV) CPLA_INST_BWD(E, DK, DV, 0) CPLA_INST_BWD(E, DK, DV, 1) CPLA_INST_BWD(E, DK, DV, 2)
 CPLA_INST_BWD3(bf16_t, 16)
 CPLA_INST_BWD3(bf16_t, 64)
 CPLA_INST_BWD3(bf16_t, 128)
+CPLA_INST_BWD3X(bf16_t, 64, 128)
+CPLA_INST_BWD3X(bf16_t, 128, 64)
 // fp32 gradients from bf16 inputs: the scalar decay (the Mamba2 parametrisation)
 #define CPLA_INST_BWD_GF32(D)                                                      \
   template __global__ void bwd_walk<bf16_t, D, D, 1, true, true, false>(BwdArgs); \

@@ -94,8 +94,9 @@ template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL>
 __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_walk(FwdArgs a) {
   using G = Geo<E, DK, DV>;
   // diagonal decay: the prepare walk stages Gam rows 32..63 in the v tile's buffer
-  // (written after the k tile is scaled), so two workgroups fit in a CU's LDS
-  constexpr bool GSPLIT = !APPLY && DECAY == DECAY_DIAG;
+  // (written after the k tile is scaled), so two workgroups fit in a CU's LDS;
+  // with d_v narrower than d_k those rows do not fit there and Gam stays whole
+  constexpr bool GSPLIT = !APPLY && DECAY == DECAY_DIAG && G::TILE_V * (int)sizeof(E) >= (CH / 2) * DK * 4;
   constexpr int GAM = (DECAY == DECAY_DIAG) ? (GSPLIT ? CH / 2 : CH) * DK : CH;
   constexpr int NQT = APPLY ? 1 : 0;
   constexpr int DSP = (DECAY == DECAY_DIAG && Split<E>::on) ? 1 : 0;   // exp-scaled tiles split
@@ -328,15 +329,18 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
   }
 }
 
-#define CPLA_INST_FWD(E, D, DEC)                                                   \
-  template __global__ void fwd_walk<E, D, D, DEC, false, false>(FwdArgs);         \
-  template __global__ void fwd_walk<E, D, D, DEC, true, false>(FwdArgs);          \
-  template __global__ void fwd_walk<E, D, D, DEC, false, true>(FwdArgs);          \
-  template __global__ void fwd_walk<E, D, D, DEC, true, true>(FwdArgs);
-#define CPLA_INST_FWD3(E, D) CPLA_INST_FWD(E, D, 0) CPLA_INST_FWD(E, D, 1) CPLA_INST_FWD(E, D, 2)
+#define CPLA_INST_FWD(E, DK, DV, DEC)                                              \
+  template __global__ void fwd_walk<E, DK, DV, DEC, false, false>(FwdArgs);       \
+  template __global__ void fwd_walk<E, DK, DV, DEC, true, false>(FwdArgs);        \
+  template __global__ void fwd_walk<E, DK, DV, DEC, false, true>(FwdArgs);        \
+  template __global__ void fwd_walk<E, DK, DV, DEC, true, true>(FwdArgs);
+#define CPLA_INST_FWD3(E, D) CPLA_INST_FWD(E, D, D, 0) CPLA_INST_FWD(E, D, D, 1) CPLA_INST_FWD(E, D, D, 2)
+#define CPLA_INST_FWD3X(E, DK, DV) CPLA_INST_FWD(E, DK, DV, 0) CPLA_INST_FWD(E, DK, DV, 1) CPLA_INST_FWD(E, DK, DV, 2)
 CPLA_INST_FWD3(bf16_t, 16)
 CPLA_INST_FWD3(bf16_t, 64)
 CPLA_INST_FWD3(bf16_t, 128)
+CPLA_INST_FWD3X(bf16_t, 64, 128)
+CPLA_INST_FWD3X(bf16_t, 128, 64)
 CPLA_INST_FWD3(float, 16)
 CPLA_INST_FWD3(float, 64)
 

@@ -83,7 +83,9 @@ typedef enum { CPLA_DECAY_NONE = 0, CPLA_DECAY_SCALAR = 1, CPLA_DECAY_DIAG = 2,
 
 typedef struct {
   int64_t B, T, H, dk, dv;   /* packed sequences: each of the B rows is a stream of T
-                                tokens with its own packing                           */
+                                tokens with its own packing. Head dims: dk == dv in
+                                {16, 64, 128} (bf16) or {16, 64} (fp32); dk != dv:
+                                bf16 (64, 128) or (128, 64); others CPLA_E_UNSUPPORTED */
   int32_t num_shards;        /* P <= 64 shards of any T: torch.chunk's division (shard
                                 size ceil(T/P), the last non-empty shard shorter, trailing
                                 shards empty when T is short; a shard's last chunk may be

@@ -118,7 +118,7 @@ def compare(wl, got, ref, heads=None, backward=True):
 
     assert_close("o", pick_bthd(got["o"]), ref["o"], rtol, atol)
     assert_close("final_state", pick_bh(got["final_state"]), ref["final_state"], rtol, atol)
-    M, dS = split_summary(got["fwd_summary"], wl.decay, wl.d, wl.d)
+    M, dS = split_summary(got["fwd_summary"], wl.decay, wl.d, wl.dv)
     assert_close("fwd_summary.M", pick_pbh(M), ref["M"], rtol, atol)
     assert_close("fwd_summary.delta_S", pick_pbh(dS), ref["delta_S"], rtol, atol)
     assert_close("shard_in_state", pick_pbh(got["shard_in_state"]), ref["shard_in_state"], rtol, atol)
@@ -130,7 +130,7 @@ def compare(wl, got, ref, heads=None, backward=True):
         assert_close("dg", pick_bthd(got["dg"]), ref["dg"], rtol, atol)
     if ref["d_initial_state"] is not None:
         assert_close("d_initial_state", pick_bh(got["d_initial_state"]), ref["d_initial_state"], rtol, atol)
-    Mb, gam = split_summary(got["bwd_summary"], wl.decay, wl.d, wl.d)
+    Mb, gam = split_summary(got["bwd_summary"], wl.decay, wl.d, wl.dv)
     assert_close("bwd_summary.M", pick_pbh(Mb), ref["M"], rtol, atol)
     assert_close("bwd_summary.gamma", pick_pbh(gam), ref["gamma"], rtol, atol)
     assert_close("shard_out_grad", pick_pbh(got["shard_out_grad"]), ref["shard_out_grad"], rtol, atol)

@@ -54,7 +54,8 @@ def fwd_prepare(p, k=FAKE, v=FAKE, g=FAKE, out=FAKE, packed=None):
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 2), (dict(dtype=7), 3), (dict(decay=5), 1), (dict(chunk=32), 5), (dict(T=0), 2),
     (dict(T=64 * 65, num_shards=65), 5),
-    (dict(rank_begin=2, rank_end=2), 1), (dict(rank_end=5), 1), (dict(dv=64), 5), (dict(dk=32, dv=32), 5),
+    (dict(rank_begin=2, rank_end=2), 1), (dict(rank_end=5), 1), (dict(dv=32), 5), (dict(dk=32, dv=32), 5),
+    (dict(dk=64, dv=16), 5), (dict(dk=64, dv=128, dtype=_lib.F32), 5), (dict(dk=16, dv=128), 5),
     (dict(dtype=_lib.F32), 5), (dict(num_shards=0), 2),
 ])
 def test_problem_validation(kw, status):

@@ -99,6 +99,32 @@ SMALL = {
                                                  "dtype": torch.float32}, True),
     "packed_diag_one_seq_bwd": ("diag_fwdbwd", {"B": 1, "T": 256, "H": 1, "d": 64, "num_shards": 1,
                                                 "packed": True, "len_range": (256, 256)}, True),
+    # d_k != d_v (bf16 64/128 and 128/64): every decay, uneven shards with partial
+    # last chunks, packed streams, a nonzero initial state, weak decay
+    "mixed_none_k64_v128_bwd": ("identity_fwd", {"B": 1, "H": 2, "T": 512, "d": 64, "dv": 128, "num_shards": 2,
+                                                 "backward": True, "dtype": torch.bfloat16}, True),
+    "mixed_none_k128_v64_bwd": ("identity_fwd", {"B": 1, "H": 2, "T": 500, "d": 128, "dv": 64, "num_shards": 3,
+                                                 "backward": True, "dtype": torch.bfloat16}, True),
+    "mixed_scalar_k64_v128_bwd": ("scalar_fwd", {"B": 2, "H": 1, "T": 700, "d": 64, "dv": 128, "num_shards": 3,
+                                                 "backward": True}, True),
+    "mixed_scalar_k128_v64_weak_bwd": ("scalar_fwd", {"B": 1, "H": 2, "T": 1024, "d": 128, "dv": 64,
+                                                      "num_shards": 4, "backward": True, "decay_scale": 1e-3},
+                                       True),
+    "mixed_diag_k64_v128_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 512, "d": 64, "dv": 128, "num_shards": 4},
+                                True),
+    "mixed_diag_k128_v64_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 600, "d": 128, "dv": 64, "num_shards": 3},
+                                True),
+    "mixed_diag_k128_v64_weak_bwd": ("diag_fwdbwd", {"B": 2, "H": 1, "T": 512, "d": 128, "dv": 64,
+                                                     "num_shards": 4, "decay_scale": 1e-3}, True),
+    "mixed_packed_k128_v64_bwd": ("packed_fwdbwd", {"T": 1024, "H": 2, "d": 128, "dv": 64, "num_shards": 4,
+                                                    "len_range": (30, 300)}, True),
+    "mixed_packed_diag_k64_v128_bwd": ("diag_fwdbwd", {"B": 2, "T": 512, "H": 1, "d": 64, "dv": 128,
+                                                       "num_shards": 3, "packed": True, "len_range": (20, 200)},
+                                       True),
+    "mixed_long_init_k128_v64_bwd": ("long_fwdbwd", {"T": 777, "H": 2, "d": 128, "dv": 64, "num_shards": 3},
+                                     True),
+    "mixed_long_init_k64_v128_bwd": ("long_fwdbwd", {"T": 512, "H": 2, "d": 64, "dv": 128, "num_shards": 2},
+                                     True),
 }
 
 

@@ -78,7 +78,7 @@ class Workload:
     B: int
     T: int
     H: int
-    d: int
+    d: int                               # d_k (q, k, g per key dim)
     dtype: torch.dtype
     decay: str
     num_shards: int
@@ -94,6 +94,10 @@ class Workload:
     @property
     def tokens(self) -> int:
         return self.B * self.T
+
+    @property
+    def dv(self) -> int:
+        return self.v.shape[-1]
 
 
 def _lengths(gen: torch.Generator, T: int, lo: int, hi: int) -> torch.Tensor:
@@ -119,7 +123,7 @@ def _packing(gen: torch.Generator, B: int, T: int, lo: int, hi: int):
 
 
 def make(name: str, *, B: Optional[int] = None, T: Optional[int] = None,
-         H: Optional[int] = None, d: Optional[int] = None,
+         H: Optional[int] = None, d: Optional[int] = None, dv: Optional[int] = None,
          num_shards: Optional[int] = None, decay_scale: float = 1.0,
          seed_offset: int = 0, len_range: Optional[tuple] = None,
          with_initial_state: Optional[bool] = None,
@@ -130,6 +134,7 @@ def make(name: str, *, B: Optional[int] = None, T: Optional[int] = None,
     T = spec.T if T is None else T
     H = spec.H if H is None else H
     d = spec.d if d is None else d
+    dv = d if dv is None else dv        # value head dim (d_v); d is d_k
     P = spec.num_shards if num_shards is None else num_shards
     bwd = spec.backward if backward is None else backward
     init = spec.initial_state if with_initial_state is None else with_initial_state
@@ -147,13 +152,13 @@ def make(name: str, *, B: Optional[int] = None, T: Optional[int] = None,
         q = randn(B, T, H, d)
         k = randn(B, T, H, d)
         k = k / k.norm(dim=-1, keepdim=True)
-        v = randn(B, T, H, d)
+        v = randn(B, T, H, dv)
     else:
         scale = {"identity_fwd": 1.0 / math.sqrt(16), "scalar_fwd": 1.0 / 8}.get(
             name, 1.0 / math.sqrt(128))
         q = randn(B, T, H, d) * scale
         k = randn(B, T, H, d) * scale
-        v = randn(B, T, H, d) * scale
+        v = randn(B, T, H, dv) * scale
 
     g = None
     if spec.decay == "scalar":
@@ -167,8 +172,8 @@ def make(name: str, *, B: Optional[int] = None, T: Optional[int] = None,
     if g is not None and decay_scale != 1.0:
         g = g * decay_scale
 
-    dO = randn(B, T, H, d) if bwd else None
-    S0 = randn(B, H, d, d) * 0.1 if init else None
+    dO = randn(B, T, H, dv) if bwd else None
+    S0 = randn(B, H, d, dv) * 0.1 if init else None
 
     dt = spec.dtype if dtype is None else dtype
     return Workload(
