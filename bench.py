@@ -238,7 +238,8 @@ def main_ssd(args, rank):
     dev = torch.device("cuda:0")
     x, dt, A, Bm, Cm, dy = (t.to(dev) for t in (wl.x, wl.dt, wl.A, wl.Bm, wl.Cm, wl.dy))
     B, T, H, G, N, P = wl.B, wl.T, wl.H, wl.G, wl.N, wl.num_shards
-    sp_ = SsdProblem(B, T, H, G, N, _lib.BF16 if wl.dtype == torch.bfloat16 else _lib.F32)
+    assert x.shape[-1] == N, "the SSD bench workload has its head dim equal to its state size"
+    sp_ = SsdProblem(B, T, H, G, N, N, _lib.BF16 if wl.dtype == torch.bfloat16 else _lib.F32)
     q = torch.empty_like(x)
     k = torch.empty_like(x)
     g = torch.empty_like(dt)

@@ -42,7 +42,7 @@ class Problem(ctypes.Structure):
 
 class SsdProblem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64), ("G", ctypes.c_int64),
-                ("N", ctypes.c_int64), ("dtype", ctypes.c_int32)]
+                ("N", ctypes.c_int64), ("P", ctypes.c_int64), ("dtype", ctypes.c_int32)]
 
 
 class Packed(ctypes.Structure):

@@ -281,23 +281,24 @@ class SsdContext:
 
 
 def _ssd_problem(x, B) -> SsdProblem:
-    Bt, T, H, N = x.shape
+    Bt, T, H, P = x.shape
     if x.dtype not in _DTYPE:
         raise CplaError(3, f"dtype {x.dtype} unsupported")
-    return SsdProblem(Bt, T, H, B.shape[2], N, _DTYPE[x.dtype])
+    return SsdProblem(Bt, T, H, B.shape[2], B.shape[3], P, _DTYPE[x.dtype])
 
 
 def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor, *,
                 num_shards: int, initial_state: Optional[torch.Tensor] = None, cu_seqlens=None,
                 packed: Optional[PackedMeta] = None):
-    """y [Bt,T,H,N] (dtype of x) and an SsdContext for ``ssd_backward``. x [Bt,T,H,N];
-    dt [Bt,T,H] and A [H] fp32; B, C [Bt,T,G,N] like x; initial_state [Bt,H,N,N] fp32."""
+    """y [Bt,T,H,P] (dtype of x) and an SsdContext for ``ssd_backward``. x [Bt,T,H,P];
+    dt [Bt,T,H] and A [H] fp32; B, C [Bt,T,G,N] like x; initial_state [Bt,H,N,P] fp32."""
     for t in (x, dt, A, B, C):
         if not t.is_contiguous():
             raise CplaError(1, "inputs must be contiguous")
     sp = _ssd_problem(x, B)
-    q = torch.empty_like(x)
-    k = torch.empty_like(x)
+    qk_shape = (x.shape[0], x.shape[1], x.shape[2], B.shape[3])
+    q = torch.empty(qk_shape, device=x.device, dtype=x.dtype)
+    k = torch.empty(qk_shape, device=x.device, dtype=x.dtype)
     g = torch.empty(dt.shape, device=x.device, dtype=torch.float32)
     check(_lib.lib().cpla_ssd_inputs(ctypes.byref(sp), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(q), _ptr(k),
                                      _ptr(g), _stream()))

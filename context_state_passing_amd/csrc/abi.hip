@@ -121,11 +121,13 @@ fwd_fn pick_fwd_t(int dtype, int DK, int DV, int decay) {
 
 template <bool APPLY, bool TAIL>
 bwd_fn pick_bwd_t(int dtype, int DK, int DV, int decay, bool grad_f32) {
-  if (grad_f32) {   // fp32 gradients from bf16 inputs: scalar decay only, dk == dv
-    if (!APPLY || dtype != CPLA_BF16 || decay != CPLA_DECAY_SCALAR || DK != DV) return nullptr;
-    if (DK == 16) return bwd_walk<bf16_t, 16, 16, 1, true, true, TAIL>;
-    if (DK == 64) return bwd_walk<bf16_t, 64, 64, 1, true, true, TAIL>;
-    if (DK == 128) return bwd_walk<bf16_t, 128, 128, 1, true, true, TAIL>;
+  if (grad_f32) {   // fp32 gradients from bf16 inputs: scalar decay only
+    if (!APPLY || dtype != CPLA_BF16 || decay != CPLA_DECAY_SCALAR) return nullptr;
+    if (DK == 16 && DV == 16) return bwd_walk<bf16_t, 16, 16, 1, true, true, TAIL>;
+    if (DK == 64 && DV == 64) return bwd_walk<bf16_t, 64, 64, 1, true, true, TAIL>;
+    if (DK == 128 && DV == 128) return bwd_walk<bf16_t, 128, 128, 1, true, true, TAIL>;
+    if (DK == 64 && DV == 128) return bwd_walk<bf16_t, 64, 128, 1, true, true, TAIL>;
+    if (DK == 128 && DV == 64) return bwd_walk<bf16_t, 128, 64, 1, true, true, TAIL>;
     return nullptr;
   }
 #define CPLA_BWD_CASE(E, KK, VV)                                          \

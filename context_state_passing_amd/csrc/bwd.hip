@@ -843,12 +843,14 @@ CPLA_INST_BWD3(bf16_t, 128)
 CPLA_INST_BWD3X(bf16_t, 64, 128)
 CPLA_INST_BWD3X(bf16_t, 128, 64)
 // fp32 gradients from bf16 inputs: the scalar decay (the Mamba2 parametrisation)
-#define CPLA_INST_BWD_GF32(D)                                                      \
-  template __global__ void bwd_walk<bf16_t, D, D, 1, true, true, false>(BwdArgs); \
-  template __global__ void bwd_walk<bf16_t, D, D, 1, true, true, true>(BwdArgs);
-CPLA_INST_BWD_GF32(16)
-CPLA_INST_BWD_GF32(64)
-CPLA_INST_BWD_GF32(128)
+#define CPLA_INST_BWD_GF32(DK, DV)                                                   \
+  template __global__ void bwd_walk<bf16_t, DK, DV, 1, true, true, false>(BwdArgs); \
+  template __global__ void bwd_walk<bf16_t, DK, DV, 1, true, true, true>(BwdArgs);
+CPLA_INST_BWD_GF32(16, 16)
+CPLA_INST_BWD_GF32(64, 64)
+CPLA_INST_BWD_GF32(128, 128)
+CPLA_INST_BWD_GF32(64, 128)
+CPLA_INST_BWD_GF32(128, 64)
 CPLA_INST_BWD3(float, 16)
 CPLA_INST_BWD3(float, 64)
 

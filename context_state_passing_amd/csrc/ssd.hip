@@ -28,7 +28,7 @@
 namespace cpla {
 
 struct SsdArgs {
-  int64_t B, T, H, G, N;
+  int64_t B, T, H, G, N, P;
   const float* dt;
   const float* A;
   const void* Bm;
@@ -85,28 +85,34 @@ __global__ __launch_bounds__(256) void ssd_inputs(SsdArgs a) {
   if (f == 0) a.g[bth] = a.A[h] * a.dt[bth];
 }
 
-// One thread per (b, t, group, four features): the group's dB and dC rows, its
-// heads' dx, and their d_dt (from the thread holding features 0..3).
+// One thread per (b, t, group, four features f of max(N, P)): the group's dB and
+// dC rows (f < N), its heads' dx (f < P), and their d_dt (from the thread
+// holding features 0..3).
 template <typename E>
 __global__ __launch_bounds__(256) void ssd_grads(SsdArgs a) {
-  const int64_t nv = a.N / 4;
+  const int64_t nv = (a.N > a.P ? a.N : a.P) / 4;
   const int64_t total = a.B * a.T * a.G * nv;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const int64_t btg = i / nv, f = (i % nv) * 4;
   const int64_t gr = btg % a.G, bt = btg / a.G;
   const int64_t hpg = a.H / a.G;
+  const bool in_n = f < a.N, in_p = f < a.P;
   f32x4 sb = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
   for (int64_t j = 0; j < hpg; ++j) {
-    const int64_t h = gr * hpg + j, bth = bt * a.H + h, off = bth * a.N + f;
-    sb += ld4(a.dk + off);
-    sc += ld4(a.dq + off);
-    st4(reinterpret_cast<E*>(a.dx) + off, ld4(a.dv + off));
+    const int64_t h = gr * hpg + j, bth = bt * a.H + h;
+    if (in_n) {
+      sb += ld4(a.dk + bth * a.N + f);
+      sc += ld4(a.dq + bth * a.N + f);
+    }
+    if (in_p) st4(reinterpret_cast<E*>(a.dx) + bth * a.P + f, ld4(a.dv + bth * a.P + f));
     if (f == 0) a.ddt[bth] = a.dw[bth] + a.A[h] * a.dg[bth];
   }
-  const int64_t off = btg * a.N + f;
-  st4(reinterpret_cast<E*>(a.dB) + off, sb);
-  st4(reinterpret_cast<E*>(a.dC) + off, sc);
+  if (in_n) {
+    const int64_t off = btg * a.N + f;
+    st4(reinterpret_cast<E*>(a.dB) + off, sb);
+    st4(reinterpret_cast<E*>(a.dC) + off, sc);
+  }
 }
 
 // One workgroup per head: dA_h = sum over (b, t) of dt * dg in a fixed order
@@ -143,6 +149,8 @@ cpla_status check_ssd(const cpla_ssd_problem* p) {
   const int64_t nv = p->N / 4;
   if (p->N % 4 != 0 || nv > 64 || (nv & (nv - 1)) != 0)
     return fail(CPLA_E_UNSUPPORTED, "N=%lld unsupported (4 times a power of two up to 256)", (long long)p->N);
+  if (p->P <= 0 || p->P % 4 != 0 || p->P > 256)
+    return fail(CPLA_E_UNSUPPORTED, "P=%lld unsupported (a positive multiple of 4 up to 256)", (long long)p->P);
   return CPLA_OK;
 }
 
@@ -169,7 +177,7 @@ extern "C" cpla_status cpla_ssd_inputs(const cpla_ssd_problem* p, const float* d
   for (int i = 0; i < 7; ++i)
     if ((st = ptr_ok(in[i], nm[i])) != CPLA_OK) return st;
   SsdArgs a{};
-  a.B = p->B; a.T = p->T; a.H = p->H; a.G = p->G; a.N = p->N;
+  a.B = p->B; a.T = p->T; a.H = p->H; a.G = p->G; a.N = p->N; a.P = p->P;
   a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm; a.q = q; a.k = k; a.g = g;
   const unsigned nb = blocks_for(p->B * p->T * p->H * (p->N / 4));
   if (p->dtype == CPLA_BF16) hipLaunchKernelGGL(ssd_inputs<bf16_t>, dim3(nb), dim3(256), 0, stream, a);
@@ -191,10 +199,10 @@ extern "C" cpla_status cpla_ssd_input_grads(const cpla_ssd_problem* p, const flo
   for (int i = 0; i < 12; ++i)
     if ((st = ptr_ok(in[i], nm[i])) != CPLA_OK) return st;
   SsdArgs a{};
-  a.B = p->B; a.T = p->T; a.H = p->H; a.G = p->G; a.N = p->N;
+  a.B = p->B; a.T = p->T; a.H = p->H; a.G = p->G; a.N = p->N; a.P = p->P;
   a.dt = dt; a.A = A; a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dw = dw;
   a.dx = dx; a.ddt = d_dt; a.dA = dA; a.dB = dB; a.dC = dC;
-  const unsigned nb = blocks_for(p->B * p->T * p->G * (p->N / 4));
+  const unsigned nb = blocks_for(p->B * p->T * p->G * ((p->N > p->P ? p->N : p->P) / 4));
   if (p->dtype == CPLA_BF16) hipLaunchKernelGGL(ssd_grads<bf16_t>, dim3(nb), dim3(256), 0, stream, a);
   else hipLaunchKernelGGL(ssd_grads<float>, dim3(nb), dim3(256), 0, stream, a);
   hipLaunchKernelGGL(ssd_dA, dim3((unsigned)p->H), dim3(DA_THREADS), 0, stream, a);

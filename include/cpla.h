@@ -64,7 +64,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;
 
-#define CPLA_ABI_VERSION 4
+#define CPLA_ABI_VERSION 5
 
 typedef enum {
   CPLA_OK = 0,
@@ -269,17 +269,20 @@ cpla_status cp_backward_apply_delta(const cpla_problem* p, const cpla_packed* pa
  * is the weighted scalar-decay recurrence above with q = C[gr], k = B[gr], v = x,
  * g = A dt and w = dt: run cpla_ssd_inputs, the weighted cp_* calls (and
  * cp_backward_prepare) with v = x and w = dt, then cpla_ssd_input_grads.
- * Shapes: x, q, k [B,T,H,N] and B, C [B,T,G,N] in `dtype`; dt, g [B,T,H] and A [H]
- * fp32 (dt already positive: any softplus or bias is the caller's); the head dim
- * P equals the state size N here (the cp_* calls need dk == dv). All pointers
+ * Shapes: q, k [B,T,H,N], x and y [B,T,H,P], B, C [B,T,G,N] in `dtype`; dt, g
+ * [B,T,H] and A [H] fp32 (dt already positive: any softplus or bias is the
+ * caller's); the state is N x P per head, so the cp_* calls run with dk = N and
+ * dv = P (bf16: N = P in {16, 64, 128} or (N, P) = (64, 128), (128, 64); fp32:
+ * N = P in {16, 64}; other pairs are rejected by those calls). All pointers
  * are device memory owned by the caller, 16-byte aligned; work is enqueued on
  * `stream`; invalid arguments return an error and launch nothing. */
 typedef struct {
   int64_t B, T, H;           /* batch, tokens, heads                                   */
   int64_t G;                 /* groups sharing B and C: H % G == 0                     */
-  int64_t N;                 /* state size = head dim: a multiple of 4, N/4 a power of
-                                two up to 64                                          */
-  int32_t dtype;             /* cpla_dtype of B, C, q, k, dq, dk, dB, dC               */
+  int64_t N;                 /* state size (B, C, q, k): a multiple of 4, N/4 a power
+                                of two up to 64                                       */
+  int64_t P;                 /* head dim (x, y): a multiple of 4, at most 256         */
+  int32_t dtype;             /* cpla_dtype of x, B, C, q, k, dx, dB, dC                */
 } cpla_ssd_problem;
 
 /* q[b,t,h] = C[b,t,gr], k[b,t,h] = B[b,t,gr] (copies) and g = A dt (fp32). */
@@ -289,7 +292,7 @@ cpla_status cpla_ssd_inputs(const cpla_ssd_problem* p, const float* dt, const fl
 
 /* The chain rule from the gradients of cp_backward_apply_weighted, run with
  * grad_dtype CPLA_F32 (dq, dk, dv, dg, dw all fp32), to the Mamba2 inputs:
- * dx = dv (dtype [B,T,H,N]), d_dt = dw + A dg (fp32 [B,T,H]), dA = sum over
+ * dx = dv (dtype [B,T,H,P]), d_dt = dw + A dg (fp32 [B,T,H]), dA = sum over
  * (b, t) of dt dg (fp32 [H], summed in a fixed order: the same on every run),
  * dB = sum over the group's heads of dk and dC of dq (dtype [B,T,G,N], summed in
  * fp32 and rounded once). */

@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_abi_version():
-    assert L.cpla_abi_version() == 4
+    assert L.cpla_abi_version() == 5
 
 
 def prob(**kw):
@@ -247,3 +247,27 @@ def test_delta_validation():
     assert L.cp_forward_prepare_delta(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1
     # the linear-attention calls refuse the delta decay
     assert fwd_prepare(p) == 1
+
+
+def ssd_prob(**kw):
+    base = dict(B=1, T=256, H=4, G=2, N=128, P=64, dtype=_lib.BF16)
+    base.update(kw)
+    return _lib.SsdProblem(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(B=0), 2), (dict(G=3), 2), (dict(dtype=9), 3), (dict(N=12), 5), (dict(N=512), 5),
+    (dict(P=0), 5), (dict(P=66), 5), (dict(P=260), 5),
+])
+def test_ssd_problem_validation(kw, status):
+    # state size N and head dim P are separate fields; bad shapes fail before any launch
+    p = ssd_prob(**kw)
+    assert L.cpla_ssd_inputs(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None) == status
+    assert L.cpla_last_error()
+    assert L.cpla_ssd_input_grads(ctypes.byref(p), *([FAKE] * 12), None) == status
+
+
+def test_ssd_pointer_validation():
+    p = ssd_prob()
+    assert L.cpla_ssd_inputs(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert L.cpla_ssd_inputs(ctypes.byref(p), FAKE, FAKE, FAKE, MISALIGNED, FAKE, FAKE, FAKE, None) == 4

@@ -36,6 +36,11 @@ CASES = {
                           with_initial_state=True),
     "bf16_n64_uneven": dict(B=1, T=1000, H=4, G=2, N=64, num_shards=3),
     "bf16_n64_rows_packed": dict(B=2, T=512, H=4, G=2, N=64, num_shards=4, packed=True, len_range=(40, 300)),
+    # state size N != head dim P (Mamba2's usual N = 128, P = 64, and the reverse)
+    "bf16_n128_p64_init": dict(B=1, T=700, H=4, G=2, N=128, P=64, num_shards=3, with_initial_state=True),
+    "bf16_n128_p64_packed": dict(B=1, T=1024, H=4, G=1, N=128, P=64, num_shards=4, packed=True,
+                                 len_range=(40, 300)),
+    "bf16_n64_p128_g2": dict(B=2, T=512, H=4, G=2, N=64, P=128, num_shards=4),
 }
 
 

@@ -15,19 +15,21 @@ import pytest
 from oracle import metadata, recurrence as rec, ssd
 
 
-def _inputs(rng, Bt=2, T=9, H=4, G=2, N=3, init=False):
-    x = rng.standard_normal((Bt, T, H, N))
+def _inputs(rng, Bt=2, T=9, H=4, G=2, N=3, init=False, P=None):
+    P = N if P is None else P           # head dim of x and y; N is the state size
+    x = rng.standard_normal((Bt, T, H, P))
     dt = np.log1p(np.exp(rng.standard_normal((Bt, T, H)) - 1.0))
     A = -np.exp(rng.uniform(0.0, 1.5, H))
     B = rng.standard_normal((Bt, T, G, N))
     C = rng.standard_normal((Bt, T, G, N))
-    h0 = rng.standard_normal((Bt, H, N, N)) * 0.5 if init else None
+    h0 = rng.standard_normal((Bt, H, N, P)) * 0.5 if init else None
     return x, dt, A, B, C, h0
 
 
-def test_forward_matches_quadratic_form():
+@pytest.mark.parametrize("N,P", [(3, 3), (3, 2), (2, 5)])
+def test_forward_matches_quadratic_form(N, P):
     rng = np.random.default_rng(7)
-    x, dt, A, B, C, _ = _inputs(rng)
+    x, dt, A, B, C, _ = _inputs(rng, N=N, P=P)
     y, _ = ssd.ssd_forward(x, dt, A, B, C)
     y2 = ssd.ssd_matrix_form(x, dt, A, B, C)
     np.testing.assert_allclose(y, y2, rtol=1e-12, atol=1e-12)
@@ -43,14 +45,16 @@ def _seq(packed, Bt, cu, T):
     return None
 
 
-@pytest.mark.parametrize("init,packed", [(False, 0), (True, 0), (False, 1), (False, 2)])
-def test_backward_matches_finite_differences(init, packed):
+@pytest.mark.parametrize("init,packed,P", [(False, 0, 3), (True, 0, 3), (False, 1, 3), (False, 2, 3),
+                                           (True, 0, 2), (False, 1, 4)])
+def test_backward_matches_finite_differences(init, packed, P):
+    # P != 3: a head dim different from the state size N = 3
     rng = np.random.default_rng(11 + 2 * init + packed)
     Bt = 1 if packed == 1 else 2
-    x, dt, A, B, C, h0 = _inputs(rng, Bt=Bt, T=8, init=init)
+    x, dt, A, B, C, h0 = _inputs(rng, Bt=Bt, T=8, init=init, P=P)
     seq = _seq(packed, Bt, [0, 3, 8], 8)
     W = rng.standard_normal(x.shape)
-    Wf = rng.standard_normal((Bt, x.shape[2], 3, 3))
+    Wf = rng.standard_normal((Bt, x.shape[2], 3, P))
 
     def loss(x_, dt_, A_, B_, C_, h0_):
         y, hT = ssd.ssd_forward(x_, dt_, A_, B_, C_, h_init=h0_, seq_idx=seq)
@@ -75,11 +79,12 @@ def test_backward_matches_finite_differences(init, packed):
         np.testing.assert_allclose(gexp, num, rtol=1e-6, atol=1e-7, err_msg=f"input {i}")
 
 
-@pytest.mark.parametrize("init,packed", [(False, 0), (True, 0), (False, 1), (False, 2)])
-def test_matches_linear_attention_oracle(init, packed):
+@pytest.mark.parametrize("init,packed,P", [(False, 0, 4), (True, 0, 4), (False, 1, 4), (False, 2, 4),
+                                           (True, 0, 6), (False, 2, 2)])
+def test_matches_linear_attention_oracle(init, packed, P):
     rng = np.random.default_rng(23 + 2 * init + packed)
     Bt = 1 if packed == 1 else 3
-    x, dt, A, B, C, h0 = _inputs(rng, Bt=Bt, T=21, H=4, G=2, N=4, init=init)
+    x, dt, A, B, C, h0 = _inputs(rng, Bt=Bt, T=21, H=4, G=2, N=4, init=init, P=P)
     seq = _seq(packed, Bt, [0, 5, 6, 21], 21)
     H, G = x.shape[2], B.shape[2]
     grp = np.arange(H) // (H // G)

@@ -187,8 +187,7 @@ def make(name: str, *, B: Optional[int] = None, T: Optional[int] = None,
 
 
 # ---- Mamba2 (SSD) inputs --------------------------------------------------------------------
-# Shapes of a Mamba2 layer whose head dim equals its state size (the library's
-# linear-attention path needs dk == dv): x [B,T,H,N], dt [B,T,H], A [H], and B, C
+# Shapes of a Mamba2 layer: x [B,T,H,P] (P = N unless given), dt [B,T,H], A [H], and B, C
 # [B,T,G,N] shared by the H/G heads of a group. Distributions follow Mamba2's
 # parameter initialisation: dt log-uniform in [1e-3, 1e-1] (as dt after its
 # softplus), A = -U[1, 16] per head; x ~ N(0,1); B, C ~ N(0,1) / N^(1/4) so that
@@ -237,6 +236,7 @@ class SsdWorkload:
 
 def make_ssd(name: str = "ssd_fwdbwd", *, B: Optional[int] = None, T: Optional[int] = None,
              H: Optional[int] = None, G: Optional[int] = None, N: Optional[int] = None,
+             P: Optional[int] = None,
              num_shards: Optional[int] = None, packed: bool = False, len_range: tuple = (64, 1024),
              with_initial_state: bool = False, dtype: Optional[torch.dtype] = None,
              seed_offset: int = 0) -> SsdWorkload:
@@ -246,6 +246,7 @@ def make_ssd(name: str = "ssd_fwdbwd", *, B: Optional[int] = None, T: Optional[i
     H = spec.H if H is None else H
     G = spec.G if G is None else G
     N = spec.N if N is None else N
+    hd = N if P is None else P          # head dim of x and y (Mamba2's P); N is the state size
     P = spec.num_shards if num_shards is None else num_shards
     gen = torch.Generator().manual_seed(1000 + spec.index + seed_offset)
     cu = _packing(gen, B, T, len_range[0], len_range[1]) if packed else None
@@ -256,13 +257,13 @@ def make_ssd(name: str = "ssd_fwdbwd", *, B: Optional[int] = None, T: Optional[i
     def rand(*shape):
         return torch.rand(*shape, generator=gen, dtype=torch.float32)
 
-    x = randn(B, T, H, N)
+    x = randn(B, T, H, hd)
     dt = torch.exp(math.log(1e-3) + rand(B, T, H) * (math.log(1e-1) - math.log(1e-3)))
     A = -(1.0 + 15.0 * rand(H))
     Bm = randn(B, T, G, N) / N ** 0.25
     Cm = randn(B, T, G, N) / N ** 0.25
-    dy = randn(B, T, H, N)
-    h0 = randn(B, H, N, N) * 0.1 if with_initial_state else None
+    dy = randn(B, T, H, hd)
+    h0 = randn(B, H, N, hd) * 0.1 if with_initial_state else None
     dtp = spec.dtype if dtype is None else dtype
     return SsdWorkload(name=name, B=B, T=T, H=H, G=G, N=N, dtype=dtp, num_shards=P,
                        x=x.to(dtp).contiguous(), dt=dt.contiguous(), A=A.contiguous(),
