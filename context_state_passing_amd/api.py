@@ -35,6 +35,47 @@ def _i32p(a: np.ndarray):
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
+# ---- argument checks ------------------------------------------------------------------
+# The C ABI takes plain device pointers and cannot see a tensor's size, dtype or
+# device, so every tensor is checked here against the shapes the call implies
+# before any pointer is handed over: a wrong one raises instead of reaching a
+# kernel. Shapes and dtypes are checked first, the device last.
+
+def _expect(name: str, t, shape, dtype, device=None, optional: bool = False):
+    if t is None:
+        if optional:
+            return
+        raise CplaError(1, f"{name} is required")
+    if not torch.is_tensor(t):
+        raise CplaError(1, f"{name} must be a tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise CplaError(2, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise CplaError(3, f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise CplaError(1, f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise CplaError(1, f"{name} is on {t.device}, expected {device}")
+
+
+def _expect_gpu(first: str, tensors: dict):
+    """Every given tensor on the GPU that holds the first one."""
+    dev = tensors[first].device
+    if dev.type != "cuda":
+        raise CplaError(1, f"{first} must be on a GPU (got {dev}); the library has no host path")
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise CplaError(1, f"{name} is on {t.device}, expected {dev}")
+
+
+def _check_packed(packed, B: int, T: int, P: int, device):
+    if packed is None:
+        return
+    _expect("packed.seq_idx", packed.seq_idx, (B, T), torch.int32, device)
+    _expect("packed.preceding_rank_start", packed.preceding_rank_start, (B, P), torch.int32, device)
+    _expect("packed.following_rank_stop", packed.following_rank_stop, (B, P), torch.int32, device)
+
+
 # ---- packed-sequence metadata (host, in the library) --------------------------------
 
 def shard_len(T: int, P: int, r: int) -> int:
@@ -161,9 +202,24 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
             out: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None):
     """o [B,T,H,dv] (dtype of q) and a Context for ``backward``. ``w`` [B,T,H] fp32:
     per-token input weights (scalar decay): S_t = exp(g_t) S_{t-1} + w_t k_t v_t^T."""
-    for t in (q, k, v, g, initial_state, w):
-        if t is not None and not t.is_contiguous():
-            raise CplaError(1, "inputs must be contiguous")
+    if not torch.is_tensor(q) or q.dim() != 4 or not torch.is_tensor(v) or v.dim() != 4:
+        raise CplaError(2, "q and v must be [B,T,H,d] tensors")
+    if q.dtype not in _DTYPE:
+        raise CplaError(3, f"dtype {q.dtype} unsupported")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _expect("q", q, (B, T, H, dk), q.dtype)
+    _expect("k", k, (B, T, H, dk), q.dtype)
+    _expect("v", v, (B, T, H, dv), q.dtype)
+    if g is not None and g.dim() == 4:
+        _expect("g", g, (B, T, H, dk), torch.float32)
+    else:
+        _expect("g", g, (B, T, H), torch.float32, optional=True)
+    _expect("initial_state", initial_state, (B, H, dk, dv), torch.float32, optional=True)
+    _expect("w", w, (B, T, H), torch.float32, optional=True)
+    _expect("out", out, (B, T, H, dv), q.dtype, optional=True)
+    _expect_gpu("q", dict(q=q, k=k, v=v, g=g, initial_state=initial_state, w=w, out=out))
+    _check_packed(packed, B, T, num_shards, q.device)
     decay = _decay_of(g, q)
     p = make_problem(q, v, num_shards, decay, chunk)
     if cu_seqlens is not None and packed is None:
@@ -204,12 +260,12 @@ def backward(dO: torch.Tensor, ctx: Context, d_final_state: Optional[torch.Tenso
     dk, dv in fp32 (bf16 inputs, scalar decay)."""
     if ctx.chunk_states is None:
         raise CplaError(1, "forward was run with save_for_backward=False")
-    if not dO.is_contiguous():
-        raise CplaError(1, "dO must be contiguous")
-    L = _lib.lib()
-    p = ctx.problem
     B, T, H, dk = ctx.q.shape
     dv = ctx.v.shape[-1]
+    _expect("dO", dO, (B, T, H, dv), ctx.q.dtype, ctx.q.device)
+    _expect("d_final_state", d_final_state, (B, H, dk, dv), torch.float32, ctx.q.device, optional=True)
+    L = _lib.lib()
+    p = ctx.problem
     P = p.num_shards
     dev = dO.device
     W = L.cpla_summary_width(ctypes.byref(p))
@@ -292,9 +348,17 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
                 packed: Optional[PackedMeta] = None):
     """y [Bt,T,H,P] (dtype of x) and an SsdContext for ``ssd_backward``. x [Bt,T,H,P];
     dt [Bt,T,H] and A [H] fp32; B, C [Bt,T,G,N] like x; initial_state [Bt,H,N,P] fp32."""
-    for t in (x, dt, A, B, C):
-        if not t.is_contiguous():
-            raise CplaError(1, "inputs must be contiguous")
+    if not torch.is_tensor(x) or x.dim() != 4 or not torch.is_tensor(B) or B.dim() != 4:
+        raise CplaError(2, "x and B must be [Bt,T,H,P] and [Bt,T,G,N] tensors")
+    Bt, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    _expect("x", x, (Bt, T, H, P), x.dtype)
+    _expect("dt", dt, (Bt, T, H), torch.float32)
+    _expect("A", A, (H,), torch.float32)
+    _expect("B", B, (Bt, T, G, N), x.dtype)
+    _expect("C", C, (Bt, T, G, N), x.dtype)
+    _expect("initial_state", initial_state, (Bt, H, N, P), torch.float32, optional=True)
+    _expect_gpu("x", dict(x=x, dt=dt, A=A, B=B, C=C, initial_state=initial_state))
     sp = _ssd_problem(x, B)
     qk_shape = (x.shape[0], x.shape[1], x.shape[2], B.shape[3])
     q = torch.empty(qk_shape, device=x.device, dtype=x.dtype)
@@ -310,6 +374,7 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
 def ssd_backward(dy: torch.Tensor, ctx: SsdContext, d_final_state: Optional[torch.Tensor] = None):
     """(dx, d_dt, dA, dB, dC, d_initial_state); d_initial_state is None with packed
     sequences."""
+    _expect("dy", dy, tuple(ctx.la.v.shape), ctx.la.v.dtype, ctx.la.v.device)
     dq, dk, dv, dg, dS0, dw = backward(dy, ctx.la, d_final_state, grad_dtype=torch.float32)
     sp = ctx.problem
     dev = dy.device
@@ -371,9 +436,20 @@ def delta_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   packed: Optional[PackedMeta] = None):
     """Gated delta rule o [B,T,H,d] and a DeltaContext: S_t = exp(g_t)(I - beta_t k_t k_t^T) S_{t-1}
     + beta_t k_t v_t^T, o_t = S_t^T q_t; g, beta [B,T,H] fp32."""
-    for t in (q, k, v, g, beta, initial_state):
-        if t is not None and not t.is_contiguous():
-            raise CplaError(1, "inputs must be contiguous")
+    if not torch.is_tensor(q) or q.dim() != 4 or not torch.is_tensor(v) or v.dim() != 4:
+        raise CplaError(2, "q and v must be [B,T,H,d] tensors")
+    if q.dtype not in _DTYPE:
+        raise CplaError(3, f"dtype {q.dtype} unsupported")
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    _expect("q", q, (B, T, H, dk), q.dtype)
+    _expect("k", k, (B, T, H, dk), q.dtype)
+    _expect("v", v, (B, T, H, dv), q.dtype)
+    _expect("g", g, (B, T, H), torch.float32)
+    _expect("beta", beta, (B, T, H), torch.float32)
+    _expect("initial_state", initial_state, (B, H, dk, dv), torch.float32, optional=True)
+    _expect_gpu("q", dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state))
+    _check_packed(packed, B, T, num_shards, q.device)
     p = make_problem(q, v, num_shards, _lib.DECAY_DELTA)
     if cu_seqlens is not None and packed is None:
         packed = packed_meta(cu_seqlens, q.shape[1], num_shards, q.device, q.shape[0])
@@ -402,12 +478,12 @@ def delta_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
 def delta_backward(dO: torch.Tensor, ctx: DeltaContext, d_final_state: Optional[torch.Tensor] = None,
                    want_intermediates: bool = False):
     """(dq, dk, dv, dg, dbeta, d_initial_state); d_initial_state is None with packed sequences."""
-    if not dO.is_contiguous():
-        raise CplaError(1, "dO must be contiguous")
-    L = _lib.lib()
-    p = ctx.problem
     B, T, H, dk = ctx.q.shape
     dv = ctx.v.shape[-1]
+    _expect("dO", dO, (B, T, H, dv), ctx.q.dtype, ctx.q.device)
+    _expect("d_final_state", d_final_state, (B, H, dk, dv), torch.float32, ctx.q.device, optional=True)
+    L = _lib.lib()
+    p = ctx.problem
     P = p.num_shards
     dev = dO.device
     W = L.cpla_summary_width(ctypes.byref(p))
