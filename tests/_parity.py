@@ -6,6 +6,8 @@ atol 1e-5; bf16 inputs rtol 2e-2, atol 2e-3. Integer metadata is compared with =
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -18,12 +20,22 @@ def tolerances(dtype):
     return (1e-4, 1e-5) if dtype == torch.float32 else (2e-2, 2e-3)
 
 
+# worst |got - ref| / (atol + rtol |ref|) of each compared output, keyed by the
+# running test and the output name (reported at the end of the session when
+# CPLA_MARGINS_OUT names a file; see conftest.py)
+MARGINS = {}
+
+
 def assert_close(name, got, ref, rtol, atol):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, f"{name}: shape {got.shape} != {ref.shape}"
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     err = np.abs(got - ref)
+    if err.size:
+        test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+        MARGINS[(test, name)] = max(MARGINS.get((test, name), 0.0),
+                                    float(np.max(err / (atol + rtol * np.abs(ref)))))
     bad = err > atol + rtol * np.abs(ref)
     if bad.any():
         idx = np.unravel_index(np.argmax(err - (atol + rtol * np.abs(ref))), err.shape)

@@ -19,3 +19,17 @@ def gpu_available():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     return True
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """With CPLA_MARGINS_OUT set, write the worst error of every compared output as
+    a fraction of its tolerance (1.0 = at the bound), one line per (test, output)."""
+    out = os.environ.get("CPLA_MARGINS_OUT")
+    if not out:
+        return
+    mod = sys.modules.get("_parity")
+    if mod is None or not mod.MARGINS:
+        return
+    with open(out, "w") as f:
+        for (test, name), r in sorted(mod.MARGINS.items(), key=lambda kv: -kv[1]):
+            f.write(f"{r:8.4f}  {test}  {name}\n")
