@@ -168,7 +168,7 @@ def cpu_baseline(wl, rows_req):
     import multiprocessing as mp
     _WL = wl
     avail = len(os.sched_getaffinity(0))
-    rows = rows_req or min(16, avail)
+    rows = rows_req or min(10, avail)   # ten full rows of the default workload: ~25 s of CPU work
     workers = min(rows, avail, 16)
     pairs = [(r % wl.H, (r // wl.H) % wl.B) for r in range(rows)]
     t0 = time.perf_counter()
@@ -208,7 +208,7 @@ def ssd_cpu_baseline(wl, rows_req):
     import multiprocessing as mp
     _WL = wl
     avail = len(os.sched_getaffinity(0))
-    rows = rows_req or min(16, avail)
+    rows = rows_req or min(10, avail)   # ten full rows of the default workload: ~25 s of CPU work
     workers = min(rows, avail, 16)
     pairs = [(r % wl.H, (r // wl.H) % wl.B) for r in range(rows)]
     t0 = time.perf_counter()
@@ -345,7 +345,7 @@ def delta_cpu_baseline(wl, rows_req):
     import multiprocessing as mp
     _WL = wl
     avail = len(os.sched_getaffinity(0))
-    rows = rows_req or min(16, avail)
+    rows = rows_req or min(10, avail)   # ten full rows of the default workload: ~25 s of CPU work
     workers = min(rows, avail, 16)
     pairs = [(r % wl.H, (r // wl.H) % wl.B) for r in range(rows)]
     t0 = time.perf_counter()
