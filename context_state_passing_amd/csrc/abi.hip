@@ -97,13 +97,20 @@ bool needs_tail(const cpla_problem* p) {
   return false;
 }
 
+template <typename E, int KK, int VV, int DEC, bool APPLY, bool TAIL>
+fwd_fn fwd_kernel(bool split) {
+  if constexpr (APPLY)
+    if (split) return fwd_walk<E, KK, VV, DEC, true, TAIL, true>;
+  return fwd_walk<E, KK, VV, DEC, APPLY, TAIL>;
+}
+
 template <bool APPLY, bool TAIL>
-fwd_fn pick_fwd_t(int dtype, int DK, int DV, int decay) {
+fwd_fn pick_fwd_t(int dtype, int DK, int DV, int decay, bool split) {
 #define CPLA_FWD_CASE(E, KK, VV)                                          \
   if (DK == KK && DV == VV) {                                             \
-    if (decay == 0) return fwd_walk<E, KK, VV, 0, APPLY, TAIL>;           \
-    if (decay == 1) return fwd_walk<E, KK, VV, 1, APPLY, TAIL>;           \
-    return fwd_walk<E, KK, VV, 2, APPLY, TAIL>;                           \
+    if (decay == 0) return fwd_kernel<E, KK, VV, 0, APPLY, TAIL>(split);  \
+    if (decay == 1) return fwd_kernel<E, KK, VV, 1, APPLY, TAIL>(split);  \
+    return fwd_kernel<E, KK, VV, 2, APPLY, TAIL>(split);                  \
   }
   if (dtype == CPLA_BF16) {
     CPLA_FWD_CASE(bf16_t, 16, 16)
@@ -152,9 +159,32 @@ bwd_fn pick_bwd_t(int dtype, int DK, int DV, int decay, bool grad_f32) {
 
 // the kernel for a problem: the TAIL variant only when some shard ends inside a chunk
 template <bool APPLY>
-fwd_fn pick_fwd(const cpla_problem* p) {
-  return needs_tail(p) ? pick_fwd_t<APPLY, true>(p->dtype, (int)p->dk, (int)p->dv, p->decay)
-                       : pick_fwd_t<APPLY, false>(p->dtype, (int)p->dk, (int)p->dv, p->decay);
+fwd_fn pick_fwd(const cpla_problem* p, bool split = false) {
+  return needs_tail(p) ? pick_fwd_t<APPLY, true>(p->dtype, (int)p->dk, (int)p->dv, p->decay, split)
+                       : pick_fwd_t<APPLY, false>(p->dtype, (int)p->dk, (int)p->dv, p->decay, split);
+}
+
+// Compute units of the current device (queried once per device).
+int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Workgroups per shard for the forward apply: two when one per (shard, row)
+// would leave more than half of the compute units idle and shards span two
+// chunks or more (the second replays the first half to reach its state), else one.
+unsigned apply_parts(const cpla_problem* p) {
+  const int64_t units = (int64_t)(p->rank_end - p->rank_begin) * p->B * p->H;
+  const int cus = device_cus();
+  if (cus <= 0 || 2 * units > cus) return 1;
+  return chunks_of(shard_len(p->T, p->num_shards, 0)) >= 2 ? 2u : 1u;
 }
 template <bool APPLY>
 bwd_fn pick_bwd(const cpla_problem* p, bool grad_f32 = false) {
@@ -287,9 +317,11 @@ static cpla_status forward_apply(const cpla_problem* p, const cpla_packed* packe
   a.state_in = shard_in_state;
   a.out = o;
   a.chunk_states = reinterpret_cast<float*>(chunk_states);
-  fwd_fn fn = pick_fwd<true>(p);
+  const unsigned parts = apply_parts(p);
+  fwd_fn fn = pick_fwd<true>(p, parts > 1);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no forward kernel for this configuration");
-  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(threads_for(p)), 0, stream, a);
+  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H), parts), dim3(threads_for(p)), 0,
+                     stream, a);
   return launched("cp_forward_apply");
 }
 

@@ -90,8 +90,9 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* K
   }
 }
 
-template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL>
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL, bool SPLIT>
 __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_walk(FwdArgs a) {
+  static_assert(APPLY || !SPLIT, "only the apply walk divides a shard");
   using G = Geo<E, DK, DV>;
   // diagonal decay: the prepare walk stages Gam rows 32..63 in the v tile's buffer
   // (written after the k tile is scaled), so two workgroups fit in a CU's LDS;
@@ -168,8 +169,14 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
   };
   if constexpr (APPLY) prefetch(0);
 
-  for (int c = 0; c < nc; ++c) {
+  // SPLIT: this workgroup emits chunks [c_emit, c_end) of the shard; the chunks
+  // before them only carry the state forward (every workgroup starts at chunk 0
+  // from the shard's incoming state, so the state it reaches at c_emit is exact)
+  const int c_emit = SPLIT ? (int)((blockIdx.z * (int64_t)nc) / gridDim.z) : 0;
+  const int c_end = SPLIT ? (int)(((blockIdx.z + 1) * (int64_t)nc) / gridDim.z) : nc;
+  for (int c = 0; c < c_end; ++c) {
     const int64_t t0 = tshard + (int64_t)c * CH;
+    const bool emit = !SPLIT || c >= c_emit;   // uniform across the workgroup
     const int nv = TAIL ? valid(c) : CH;
     const bool full = !TAIL || nv >= CH;   // only a shard's last chunk is partial
     if constexpr (!APPLY) prefetch(c);
@@ -194,11 +201,11 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
     }
     store_tile<E, DV, G::DVP, G::LDV, 0, DK, G::NT>(rv, s_v, nullptr, s_gam, nullptr);
     if constexpr (APPLY)
-      if (c + 1 < nc) prefetch(c + 1);
+      if (c + 1 < c_end) prefetch(c + 1);
 
     __syncthreads();
 
-    if constexpr (APPLY) {
+    if (APPLY && emit) {
       // ---- scores -> s_a (E), masked and decayed --------------------------------
 #pragma unroll
       for (int s = 0; s < (N_SCORE_TILES + G::NW - 1) / G::NW; ++s) {
@@ -281,7 +288,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
     // the state entering the chunk, saved for the backward walk: written after
     // the output tiles and before the update overwrites S (issuing these stores
     // at the start of the chunk measured slower)
-    if constexpr (APPLY) {
+    if (APPLY && emit) {
       if (a.chunk_states) {
         float* cs = a.chunk_states +
                     ((bh * row_chunks(a.T, a.P) + shard_chunk_base(a.T, a.P, r) + c) * DK) * (int64_t)DV;
@@ -333,7 +340,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
   template __global__ void fwd_walk<E, DK, DV, DEC, false, false>(FwdArgs);       \
   template __global__ void fwd_walk<E, DK, DV, DEC, true, false>(FwdArgs);        \
   template __global__ void fwd_walk<E, DK, DV, DEC, false, true>(FwdArgs);        \
-  template __global__ void fwd_walk<E, DK, DV, DEC, true, true>(FwdArgs);
+  template __global__ void fwd_walk<E, DK, DV, DEC, true, true>(FwdArgs);         \
+  template __global__ void fwd_walk<E, DK, DV, DEC, true, false, true>(FwdArgs);  \
+  template __global__ void fwd_walk<E, DK, DV, DEC, true, true, true>(FwdArgs);
 #define CPLA_INST_FWD3(E, D) CPLA_INST_FWD(E, D, D, 0) CPLA_INST_FWD(E, D, D, 1) CPLA_INST_FWD(E, D, D, 2)
 #define CPLA_INST_FWD3X(E, DK, DV) CPLA_INST_FWD(E, DK, DV, 0) CPLA_INST_FWD(E, DK, DV, 1) CPLA_INST_FWD(E, DK, DV, 2)
 CPLA_INST_FWD3(bf16_t, 16)

@@ -104,8 +104,11 @@ template <typename E, int D, bool APPLY> __global__ void delta_bwalk(DeltaArgs a
 template <typename E, int D> __global__ void delta_grad(DeltaArgs a);
 
 // TAIL: some shard's length is not a multiple of the chunk (a partial last chunk
-// to mask); without it every guard compiles away
-template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL>
+// to mask); without it every guard compiles away.
+// SPLIT (apply only): the shard's chunks are divided among gridDim.z workgroups;
+// workgroup z emits chunks [z nc / Z, (z + 1) nc / Z) after replaying the ones
+// before them from the shard's incoming state (staging and state update only).
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL, bool SPLIT = false>
 __global__ void fwd_walk(FwdArgs a);
 template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAIL>
 __global__ void bwd_walk(BwdArgs a);
