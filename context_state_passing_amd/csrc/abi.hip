@@ -126,22 +126,31 @@ fwd_fn pick_fwd_t(int dtype, int DK, int DV, int decay, bool split) {
   return nullptr;
 }
 
+// the divided (SPLIT) variants exist for the apply walk without decay or with a scalar decay
+template <typename E, int KK, int VV, int DEC, bool APPLY, bool GF, bool TAIL>
+bwd_fn bwd_kernel(bool split) {
+  if constexpr (APPLY && DEC != CPLA_DECAY_DIAG)
+    if (split) return bwd_walk<E, KK, VV, DEC, true, GF, TAIL, true>;
+  return bwd_walk<E, KK, VV, DEC, APPLY, GF, TAIL>;
+}
+
 template <bool APPLY, bool TAIL>
-bwd_fn pick_bwd_t(int dtype, int DK, int DV, int decay, bool grad_f32) {
+bwd_fn pick_bwd_t(int dtype, int DK, int DV, int decay, bool grad_f32, bool split) {
   if (grad_f32) {   // fp32 gradients from bf16 inputs: scalar decay only
-    if (!APPLY || dtype != CPLA_BF16 || decay != CPLA_DECAY_SCALAR) return nullptr;
-    if (DK == 16 && DV == 16) return bwd_walk<bf16_t, 16, 16, 1, true, true, TAIL>;
-    if (DK == 64 && DV == 64) return bwd_walk<bf16_t, 64, 64, 1, true, true, TAIL>;
-    if (DK == 128 && DV == 128) return bwd_walk<bf16_t, 128, 128, 1, true, true, TAIL>;
-    if (DK == 64 && DV == 128) return bwd_walk<bf16_t, 64, 128, 1, true, true, TAIL>;
-    if (DK == 128 && DV == 64) return bwd_walk<bf16_t, 128, 64, 1, true, true, TAIL>;
+    if constexpr (!APPLY) return nullptr;
+    if (dtype != CPLA_BF16 || decay != CPLA_DECAY_SCALAR) return nullptr;
+    if (DK == 16 && DV == 16) return bwd_kernel<bf16_t, 16, 16, 1, true, true, TAIL>(split);
+    if (DK == 64 && DV == 64) return bwd_kernel<bf16_t, 64, 64, 1, true, true, TAIL>(split);
+    if (DK == 128 && DV == 128) return bwd_kernel<bf16_t, 128, 128, 1, true, true, TAIL>(split);
+    if (DK == 64 && DV == 128) return bwd_kernel<bf16_t, 64, 128, 1, true, true, TAIL>(split);
+    if (DK == 128 && DV == 64) return bwd_kernel<bf16_t, 128, 64, 1, true, true, TAIL>(split);
     return nullptr;
   }
-#define CPLA_BWD_CASE(E, KK, VV)                                          \
-  if (DK == KK && DV == VV) {                                             \
-    if (decay == 0) return bwd_walk<E, KK, VV, 0, APPLY, false, TAIL>;    \
-    if (decay == 1) return bwd_walk<E, KK, VV, 1, APPLY, false, TAIL>;    \
-    return bwd_walk<E, KK, VV, 2, APPLY, false, TAIL>;                    \
+#define CPLA_BWD_CASE(E, KK, VV)                                               \
+  if (DK == KK && DV == VV) {                                                  \
+    if (decay == 0) return bwd_kernel<E, KK, VV, 0, APPLY, false, TAIL>(split); \
+    if (decay == 1) return bwd_kernel<E, KK, VV, 1, APPLY, false, TAIL>(split); \
+    return bwd_kernel<E, KK, VV, 2, APPLY, false, TAIL>(false);                \
   }
   if (dtype == CPLA_BF16) {
     CPLA_BWD_CASE(bf16_t, 16, 16)
@@ -187,9 +196,9 @@ unsigned apply_parts(const cpla_problem* p) {
   return chunks_of(shard_len(p->T, p->num_shards, 0)) >= 2 ? 2u : 1u;
 }
 template <bool APPLY>
-bwd_fn pick_bwd(const cpla_problem* p, bool grad_f32 = false) {
-  return needs_tail(p) ? pick_bwd_t<APPLY, true>(p->dtype, (int)p->dk, (int)p->dv, p->decay, grad_f32)
-                       : pick_bwd_t<APPLY, false>(p->dtype, (int)p->dk, (int)p->dv, p->decay, grad_f32);
+bwd_fn pick_bwd(const cpla_problem* p, bool grad_f32 = false, bool split = false) {
+  return needs_tail(p) ? pick_bwd_t<APPLY, true>(p->dtype, (int)p->dk, (int)p->dv, p->decay, grad_f32, split)
+                       : pick_bwd_t<APPLY, false>(p->dtype, (int)p->dk, (int)p->dv, p->decay, grad_f32, split);
 }
 
 unsigned threads_for(const cpla_problem* p) {
@@ -405,9 +414,12 @@ static cpla_status backward_apply(const cpla_problem* p, const cpla_packed* pack
   a.chunk_states = reinterpret_cast<const float*>(chunk_states);
   a.grad_in = shard_out_grad;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dw = dw;
-  bwd_fn fn = pick_bwd<true>(p, grad_f32);
+  // divided walks for small grids (no decay or a scalar decay)
+  const unsigned parts = p->decay == CPLA_DECAY_DIAG ? 1u : apply_parts(p);
+  bwd_fn fn = pick_bwd<true>(p, grad_f32, parts > 1);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no backward kernel for this configuration");
-  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), dim3(threads_for(p)), 0, stream, a);
+  hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H), parts), dim3(threads_for(p)), 0,
+                     stream, a);
   return launched("cp_backward_apply");
 }
 

@@ -71,8 +71,9 @@ __device__ __forceinline__ f32x4 lane_gamma(f32x4 x, f32x4& carry) {
   return out;
 }
 
-template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAIL>
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAIL, bool SPLIT>
 __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_walk(BwdArgs a) {
+  static_assert(!SPLIT || (APPLY && DECAY != DECAY_DIAG), "divided walks: apply, no or scalar decay");
   using G = Geo<E, DK, DV>;
   // dq, dk, dv in the input dtype, or in fp32 (GF32: for callers that sum them
   // further, e.g. over the heads sharing an input)
@@ -216,7 +217,13 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
     }
   }
 
-  for (int c = nc - 1; c >= 0; --c) {
+  // SPLIT: this workgroup emits chunks [c_lo, c_hi) of the shard; the later ones
+  // only carry the adjoint backwards (every workgroup starts at the shard's last
+  // chunk from its outgoing gradient, so the adjoint it reaches at c_hi is exact)
+  const int c_lo = SPLIT ? (int)((blockIdx.z * (int64_t)nc) / gridDim.z) : 0;
+  const int c_hi = SPLIT ? (int)(((blockIdx.z + 1) * (int64_t)nc) / gridDim.z) : nc;
+  for (int c = nc - 1; c >= c_lo; --c) {
+    const bool emit = !SPLIT || c < c_hi;   // uniform across the workgroup
     const int64_t t0 = tshard + (int64_t)c * CH;
     const int nv = TAIL ? valid(c) : CH;
     const bool full = !TAIL || nv >= CH;   // only a shard's last chunk is partial
@@ -323,7 +330,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
       }
     }
 
-    if constexpr (APPLY) {
+    if constexpr (APPLY) if (emit) {
       // ---- scores and score gradients (hi/lo) for the wave's tiles -------------------
 #pragma unroll
       for (int s = 0; s < (N_SCORE_TILES + G::NW - 1) / G::NW; ++s) {
@@ -835,8 +842,13 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
   template __global__ void bwd_walk<E, DK, DV, DEC, true, false, false>(BwdArgs);  \
   template __global__ void bwd_walk<E, DK, DV, DEC, false, false, true>(BwdArgs);  \
   template __global__ void bwd_walk<E, DK, DV, DEC, true, false, true>(BwdArgs);
-#define CPLA_INST_BWD3(E, D) CPLA_INST_BWD(E, D, D, 0) CPLA_INST_BWD(E, D, D, 1) CPLA_INST_BWD(E, D, D, 2)
-#define CPLA_INST_BWD3X(E, DK, DV) CPLA_INST_BWD(E, DK, DV, 0) CPLA_INST_BWD(E, DK, DV, 1) CPLA_INST_BWD(E, DK, DV, 2)
+#define CPLA_INST_BWD_SPLIT(E, DK, DV, DEC, GF)                                           \
+  template __global__ void bwd_walk<E, DK, DV, DEC, true, GF, false, true>(BwdArgs);     \
+  template __global__ void bwd_walk<E, DK, DV, DEC, true, GF, true, true>(BwdArgs);
+#define CPLA_INST_BWD3(E, D) CPLA_INST_BWD(E, D, D, 0) CPLA_INST_BWD(E, D, D, 1) CPLA_INST_BWD(E, D, D, 2) \
+  CPLA_INST_BWD_SPLIT(E, D, D, 0, false) CPLA_INST_BWD_SPLIT(E, D, D, 1, false)
+#define CPLA_INST_BWD3X(E, DK, DV) CPLA_INST_BWD(E, DK, DV, 0) CPLA_INST_BWD(E, DK, DV, 1) CPLA_INST_BWD(E, DK, DV, 2) \
+  CPLA_INST_BWD_SPLIT(E, DK, DV, 0, false) CPLA_INST_BWD_SPLIT(E, DK, DV, 1, false)
 CPLA_INST_BWD3(bf16_t, 16)
 CPLA_INST_BWD3(bf16_t, 64)
 CPLA_INST_BWD3(bf16_t, 128)
@@ -845,7 +857,8 @@ CPLA_INST_BWD3X(bf16_t, 128, 64)
 // fp32 gradients from bf16 inputs: the scalar decay (the Mamba2 parametrisation)
 #define CPLA_INST_BWD_GF32(DK, DV)                                                   \
   template __global__ void bwd_walk<bf16_t, DK, DV, 1, true, true, false>(BwdArgs); \
-  template __global__ void bwd_walk<bf16_t, DK, DV, 1, true, true, true>(BwdArgs);
+  template __global__ void bwd_walk<bf16_t, DK, DV, 1, true, true, true>(BwdArgs);  \
+  CPLA_INST_BWD_SPLIT(bf16_t, DK, DV, 1, true)
 CPLA_INST_BWD_GF32(16, 16)
 CPLA_INST_BWD_GF32(64, 64)
 CPLA_INST_BWD_GF32(128, 128)

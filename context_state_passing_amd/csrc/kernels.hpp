@@ -110,7 +110,10 @@ template <typename E, int D> __global__ void delta_grad(DeltaArgs a);
 // before them from the shard's incoming state (staging and state update only).
 template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL, bool SPLIT = false>
 __global__ void fwd_walk(FwdArgs a);
-template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAIL>
+// SPLIT (apply, no decay or scalar decay): as for fwd_walk, walking backwards:
+// workgroup z emits chunks [z nc / Z, (z + 1) nc / Z) after replaying the later
+// ones from the shard's outgoing gradient (staging and the adjoint update only).
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAIL, bool SPLIT = false>
 __global__ void bwd_walk(BwdArgs a);
 __global__ void affine_scan(ScanArgs a);
 
