@@ -8,6 +8,7 @@ several shards, and packed sequences with boundaries inside chunks. Full-size
 cases run the exact benchmark shapes on the GPU and compare sampled heads, which
 the oracle computes independently.
 """
+import dataclasses
 import sys
 
 import pytest
@@ -181,3 +182,30 @@ def test_full_size_sampled_heads(name, heads, gpu_available):
     got = gpu_run(wl, backward=True, heads=heads)
     ref = oracle_run(wl, backward=True, heads=heads)
     compare(wl, got, ref, backward=True)
+
+
+@pytest.mark.parametrize("name,over", [
+    ("scalar_fwd", dict(B=1, H=20, T=1000, num_shards=8, backward=True)),
+    ("identity_fwd", dict(B=1, H=20, T=1000, d=64, num_shards=8, backward=True, dtype=torch.bfloat16)),
+    ("packed_fwdbwd", dict(B=1, H=20, T=1000, d=64, num_shards=8, len_range=(30, 300))),
+])
+def test_divided_walks_bitwise(name, over, gpu_available):
+    # 20 heads x 8 shards = 160 workgroups per walk: one per (shard, row) on a
+    # 256-CU MI355X; two of those heads alone (16 workgroups) take the apply walks
+    # divided between two workgroups per shard (the second replays the first part).
+    # Every row is computed on its own, so the two heads' results must be the same
+    # bits either way.
+    _announce(f"divided walks {name}")
+    wl = workloads.make(name, **over)
+    heads = [3, 11]
+    full = gpu_run(wl, backward=True)
+    sub = dataclasses.replace(
+        wl, H=len(heads), q=wl.q[:, :, heads].contiguous(), k=wl.k[:, :, heads].contiguous(),
+        v=wl.v[:, :, heads].contiguous(), dO=wl.dO[:, :, heads].contiguous(),
+        g=None if wl.g is None else wl.g[:, :, heads].contiguous(),
+        initial_state=None if wl.initial_state is None else wl.initial_state[:, heads].contiguous())
+    part = gpu_run(sub, backward=True)
+    for key in ("o", "dq", "dk", "dv", "dg"):
+        if full[key] is None:
+            continue
+        assert (full[key][:, :, heads] == part[key]).all(), key
