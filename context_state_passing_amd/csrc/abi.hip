@@ -7,6 +7,8 @@
 // perform after gathering summaries runs here as the affine_scan kernel, since on
 // one GPU every shard's summary already sits in one buffer. Validation mirrors
 // _validate_summary_tensor and fails fast on uneven division.
+#include <mutex>
+#include <unordered_map>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -186,14 +188,37 @@ int device_cus() {
   return cache[dev];
 }
 
-// Workgroups per shard for the forward apply: two when one per (shard, row)
-// would leave more than half of the compute units idle and shards span two
-// chunks or more (the second replays the first half to reach its state), else one.
-unsigned apply_parts(const cpla_problem* p) {
+unsigned threads_for(const cpla_problem* p);
+
+// Workgroups of `kernel` (blocks of `threads`) resident per compute unit, from
+// the runtime's occupancy query (cached per kernel: it depends only on the
+// kernel's registers and LDS and on the block size, which the kernel fixes).
+int kernel_occupancy(const void* kernel, unsigned threads) {
+  static std::mutex mu;
+  static std::unordered_map<const void*, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(kernel);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, (int)threads, 0) != hipSuccess || n < 1) n = 1;
+  cache[kernel] = n;
+  return n;
+}
+
+// Workgroups per shard for an apply walk (divided kernel `kernel`): the largest
+// Z in {1, 2, 4} whose Z x (shards x rows) workgroups are all resident at once
+// (compute units x workgroups per unit) while no shard gets more parts than
+// chunks; each extra part replays the chunks before its own, so a division only
+// pays while it fills otherwise idle units.
+unsigned apply_parts(const cpla_problem* p, const void* kernel) {
   const int64_t units = (int64_t)(p->rank_end - p->rank_begin) * p->B * p->H;
   const int cus = device_cus();
-  if (cus <= 0 || 2 * units > cus) return 1;
-  return chunks_of(shard_len(p->T, p->num_shards, 0)) >= 2 ? 2u : 1u;
+  if (cus <= 0 || !kernel) return 1;
+  const int64_t slots = (int64_t)cus * kernel_occupancy(kernel, threads_for(p));
+  const int64_t nc = chunks_of(shard_len(p->T, p->num_shards, 0));
+  unsigned z = 1;
+  while (z < 4 && 2 * z <= nc && 2 * z * units <= slots) z *= 2;
+  return z;
 }
 template <bool APPLY>
 bwd_fn pick_bwd(const cpla_problem* p, bool grad_f32 = false, bool split = false) {
@@ -326,7 +351,7 @@ static cpla_status forward_apply(const cpla_problem* p, const cpla_packed* packe
   a.state_in = shard_in_state;
   a.out = o;
   a.chunk_states = reinterpret_cast<float*>(chunk_states);
-  const unsigned parts = apply_parts(p);
+  const unsigned parts = apply_parts(p, reinterpret_cast<const void*>(pick_fwd<true>(p, true)));
   fwd_fn fn = pick_fwd<true>(p, parts > 1);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no forward kernel for this configuration");
   hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H), parts), dim3(threads_for(p)), 0,
@@ -415,7 +440,8 @@ static cpla_status backward_apply(const cpla_problem* p, const cpla_packed* pack
   a.grad_in = shard_out_grad;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dw = dw;
   // divided walks for small grids (no decay or a scalar decay)
-  const unsigned parts = p->decay == CPLA_DECAY_DIAG ? 1u : apply_parts(p);
+  const unsigned parts =
+      p->decay == CPLA_DECAY_DIAG ? 1u : apply_parts(p, reinterpret_cast<const void*>(pick_bwd<true>(p, grad_f32, true)));
   bwd_fn fn = pick_bwd<true>(p, grad_f32, parts > 1);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no backward kernel for this configuration");
   hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H), parts), dim3(threads_for(p)), 0,
