@@ -209,3 +209,39 @@ def test_divided_walks_bitwise(name, over, gpu_available):
         if full[key] is None:
             continue
         assert (full[key][:, :, heads] == part[key]).all(), key
+
+
+def _sweep_cases(seed, n):
+    """Seeded random problems over every decay, head-size pair and dtype, with
+    uneven and empty shards, partial chunks, packing, S_init and weak decay."""
+    import random
+    rng = random.Random(seed)
+    dims = [((16, 16), torch.float32), ((64, 64), torch.float32), ((16, 16), torch.bfloat16),
+            ((64, 64), torch.bfloat16), ((128, 128), torch.bfloat16), ((64, 128), torch.bfloat16),
+            ((128, 64), torch.bfloat16)]
+    out = []
+    for i in range(n):
+        (dk, dv), dt = rng.choice(dims)
+        decay = rng.choice(["none", "scalar", "diag"])
+        T = rng.choice([rng.randint(1, 130), rng.randint(64, 700)])
+        if dt == torch.float32 and decay == "none":
+            T = min(T, 300)   # fp32 without decay: the fp32 bound holds up to a few hundred tokens
+        over = dict(B=rng.choice([1, 1, 2]), H=rng.choice([1, 2, 3]), T=T, d=dk, dv=dv,
+                    num_shards=rng.randint(1, 9), dtype=dt, backward=True,
+                    decay_scale=rng.choice([1.0, 1.0, 1e-2, 1e-3]))
+        if rng.random() < 0.35:
+            over.update(packed=True, len_range=(1, rng.randint(1, 300)))
+        elif rng.random() < 0.4:
+            over.update(with_initial_state=True)
+        out.append(({"none": "identity_fwd", "scalar": "scalar_fwd", "diag": "diag_fwdbwd"}[decay], over))
+    return out
+
+
+@pytest.mark.parametrize("case", range(60))
+def test_random_problems(case, gpu_available):
+    name, over = _sweep_cases(2026, 60)[case]
+    _announce(f"random {case}: {name} {over}")
+    wl = workloads.make(name, **over)
+    got = gpu_run(wl, backward=True)
+    ref = oracle_run(wl, backward=True)
+    compare(wl, got, ref, backward=True)
