@@ -158,3 +158,41 @@ def test_weighted_parity(case, gpu_available):
         want["d_initial_state"] = ref[4]
     for n in want:
         assert_close(n, _np(got[n]), want[n], rtol, atol)
+
+
+def _ssd_sweep(seed, n):
+    """Seeded random Mamba2 problems: state size / head dim pairs (N = P and
+    N != P), groups, uneven and empty shards, packing, an initial state."""
+    import random
+    rng = random.Random(seed)
+    pairs = [((16, 16), torch.float32), ((64, 64), torch.float32), ((16, 16), torch.bfloat16),
+             ((64, 64), torch.bfloat16), ((128, 128), torch.bfloat16), ((128, 64), torch.bfloat16),
+             ((64, 128), torch.bfloat16)]
+    out = []
+    for _ in range(n):
+        (N, P), dt = rng.choice(pairs)
+        H = rng.choice([1, 2, 4, 8])
+        over = dict(B=rng.choice([1, 2]), T=rng.choice([rng.randint(1, 130), rng.randint(64, 800)]), H=H,
+                    G=rng.choice([g for g in (1, 2, 4, 8) if H % g == 0]), N=N, P=P,
+                    num_shards=rng.randint(1, 9), dtype=dt)
+        if rng.random() < 0.35:
+            over.update(packed=True, len_range=(1, rng.randint(1, 300)))
+        elif rng.random() < 0.4:
+            over.update(with_initial_state=True)
+        out.append(over)
+    return out
+
+
+@pytest.mark.parametrize("case", range(30))
+def test_random_ssd_problems(case, gpu_available):
+    over = _ssd_sweep(2026, 30)[case]
+    print(f"[gpu-case] ssd random {case}: {over}", file=sys.stderr, flush=True)
+    wl = workloads.make_ssd(**over)
+    got, ref = _run_gpu(wl), _run_oracle(wl)
+    rtol, atol = tolerances(wl.dtype)
+    for name in ref:
+        if name != "d_dt":
+            assert_close(name, _np(got[name]), ref[name], rtol, atol)
+    err = np.abs(_np(got["d_dt"]) - ref["d_dt"])
+    lim = atol + rtol * np.abs(ref["d_dt"]) + 64 * 2.0 ** -24 * _ddt_term_scale(wl)
+    assert np.all(err <= lim), f"d_dt: {int((err > lim).sum())}/{err.size} outside"
