@@ -90,3 +90,32 @@ def test_delta_deterministic(gpu_available):
     b = _run_gpu(wl)
     for name in a:
         assert np.array_equal(a[name], b[name]), name
+
+
+def _delta_sweep(seed, n):
+    """Seeded random gated-delta problems: head sizes 16/32/64, both dtypes,
+    uneven and empty shards, packing, an initial state."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        over = dict(B=rng.choice([1, 2]), T=rng.choice([rng.randint(1, 130), rng.randint(64, 600)]),
+                    H=rng.choice([1, 2, 3]), d=rng.choice([16, 32, 64]), num_shards=rng.randint(1, 9),
+                    dtype=rng.choice([torch.float32, torch.bfloat16]))
+        if rng.random() < 0.35:
+            over.update(packed=True, len_range=(1, rng.randint(1, 300)))
+        elif rng.random() < 0.4:
+            over.update(with_initial_state=True)
+        out.append(over)
+    return out
+
+
+@pytest.mark.parametrize("case", range(30))
+def test_random_delta_problems(case, gpu_available):
+    over = _delta_sweep(2026, 30)[case]
+    print(f"[gpu-case] delta random {case}: {over}", file=sys.stderr, flush=True)
+    wl = workloads.make_delta(**over)
+    got, ref = _run_gpu(wl), _run_oracle(wl)
+    rtol, atol = tolerances(wl.dtype)
+    for name in ref:
+        assert_close(name, got[name], ref[name], rtol, atol)
