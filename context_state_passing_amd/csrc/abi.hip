@@ -175,33 +175,37 @@ fwd_fn pick_fwd(const cpla_problem* p, bool split = false) {
                        : pick_fwd_t<APPLY, false>(p->dtype, (int)p->dk, (int)p->dv, p->decay, split);
 }
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; 0 if unknown).
 int device_cus() {
-  static int cache[64] = {0};
+  static std::mutex mu;
+  static std::unordered_map<int, int> cache;
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev] = n;
-  }
-  return cache[dev];
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  cache[dev] = n;
+  return n;
 }
 
 unsigned threads_for(const cpla_problem* p);
 
 // Workgroups of `kernel` (blocks of `threads`) resident per compute unit, from
-// the runtime's occupancy query (cached per kernel: it depends only on the
-// kernel's registers and LDS and on the block size, which the kernel fixes).
+// the runtime's occupancy query (cached per device and kernel: it depends only
+// on the kernel's registers and LDS and on the block size, which the kernel fixes).
 int kernel_occupancy(const void* kernel, unsigned threads) {
   static std::mutex mu;
-  static std::unordered_map<const void*, int> cache;
+  static std::unordered_map<const void*, int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 1;
   std::lock_guard<std::mutex> lock(mu);
-  auto it = cache.find(kernel);
-  if (it != cache.end()) return it->second;
+  auto it = cache[dev].find(kernel);
+  if (it != cache[dev].end()) return it->second;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, (int)threads, 0) != hipSuccess || n < 1) n = 1;
-  cache[kernel] = n;
+  cache[dev][kernel] = n;
   return n;
 }
 
