@@ -6,7 +6,9 @@
 // step that the page's orchestrators (chunkwise_cp_forward / chunkwise_cp_backward)
 // perform after gathering summaries runs here as the affine_scan kernel, since on
 // one GPU every shard's summary already sits in one buffer. Validation mirrors
-// _validate_summary_tensor and fails fast on uneven division.
+// _validate_summary_tensor; the stream divides into shards as torch.chunk does
+// (shards.hpp), so uneven divisions are accepted.
+#include <atomic>
 #include <mutex>
 #include <unordered_map>
 #include <stdarg.h>
@@ -214,12 +216,20 @@ int kernel_occupancy(const void* kernel, unsigned threads) {
 // (compute units x workgroups per unit) while no shard gets more parts than
 // chunks; each extra part replays the chunks before its own, so a division only
 // pays while it fills otherwise idle units.
+std::atomic<int> g_forced_parts{0};   // cpla_set_apply_parts: 0 = automatic
+
 unsigned apply_parts(const cpla_problem* p, const void* kernel) {
   const int64_t units = (int64_t)(p->rank_end - p->rank_begin) * p->B * p->H;
+  const int64_t nc = chunks_of(shard_len(p->T, p->num_shards, 0));
+  const int forced = g_forced_parts.load(std::memory_order_relaxed);
+  if (forced > 0) {   // the forced count, halved until every part holds a chunk
+    unsigned z = (unsigned)forced;
+    while (z > 1 && (int64_t)z > nc) z /= 2;
+    return z;
+  }
   const int cus = device_cus();
   if (cus <= 0 || !kernel) return 1;
   const int64_t slots = (int64_t)cus * kernel_occupancy(kernel, threads_for(p));
-  const int64_t nc = chunks_of(shard_len(p->T, p->num_shards, 0));
   unsigned z = 1;
   while (z < 4 && 2 * z <= nc && 2 * z * units <= slots) z *= 2;
   return z;
@@ -265,6 +275,11 @@ using namespace cpla;
 
 extern "C" const char* cpla_last_error(void) { return last_error_buf(); }
 extern "C" int cpla_abi_version(void) { return CPLA_ABI_VERSION; }
+
+extern "C" int cpla_set_apply_parts(int parts) {
+  if (parts != 0 && parts != 1 && parts != 2 && parts != 4) return -1;
+  return cpla::g_forced_parts.exchange(parts);
+}
 
 extern "C" int64_t cpla_summary_width(const cpla_problem* p) {
   if (!p) return -1;

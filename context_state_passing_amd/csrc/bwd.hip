@@ -72,7 +72,7 @@ __device__ __forceinline__ f32x4 lane_gamma(f32x4 x, f32x4& carry) {
 }
 
 template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAIL, bool SPLIT>
-__global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_walk(BwdArgs a) {
+__global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 ? 2 : 4))) void bwd_walk(BwdArgs a) {
   static_assert(!SPLIT || (APPLY && DECAY != DECAY_DIAG), "divided walks: apply, no or scalar decay");
   using G = Geo<E, DK, DV>;
   // dq, dk, dv in the input dtype, or in fp32 (GF32: for callers that sum them
@@ -150,8 +150,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
 
   // dS: rows = all d_k tiles, columns = owned d_v tiles.  dT = dS^T: rows = all
   // d_v tiles, columns = owned d_k tiles (lane-fixed d).
-  f32x4 dS[G::NKT][G::CPWV];
-  f32x4 dT[APPLY ? G::NVT : 1][G::CPWK];
+  using AV = acc4<E>;   // fp32 accumulators for bf16 inputs, fp64 for fp32 inputs
+  AV dS[G::NKT][G::CPWV];
+  AV dT[APPLY ? G::NVT : 1][G::CPWK];
   {
     const float* gin = APPLY ? a.grad_in + (int64_t)(r * a.B * a.H + bh) * DK * DV : nullptr;
 #pragma unroll
@@ -316,7 +317,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
       const int l = lane_pick<APPLY>(), g = l >> 4, i16 = l & 15;
 #pragma unroll
       for (int m = 0; m < G::NKT; ++m) {
-        const f32x4 el = load4f(s_el + 16 * m + 4 * g);
+        const AV el = widen4<AV>(load4f(s_el + 16 * m + 4 * g));
 #pragma unroll
         for (int cc = 0; cc < G::CPWV; ++cc) dS[m][cc] *= el;
       }
@@ -338,7 +339,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
         if (s * G::NW + w >= N_SCORE_TILES) continue;
         const int idx = score_tile(s * G::NW + w);
         const int I = idx >> 2, J = idx & 3;
-        f32x4 xa = {0.f, 0.f, 0.f, 0.f}, xd = {0.f, 0.f, 0.f, 0.f};
+        AV xa = {0, 0, 0, 0}, xd = {0, 0, 0, 0};
         if (!score_tile_zero(idx)) {
 #pragma unroll
           for (int kd = 0; kd < G::DKP / 32; ++kd) {
@@ -372,8 +373,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
         for (int rr = 0; rr < 4; ++rr) {
           const int i = 16 * I + 4 * g + rr;
           const bool ok = i >= j && seg.index(i) == sj;
-          va[rr] = ok ? xa[rr] : 0.f;
-          vd[rr] = ok ? xd[rr] : 0.f;
+          va[rr] = ok ? (float)xa[rr] : 0.f;
+          vd[rr] = ok ? (float)xd[rr] : 0.f;
           if constexpr (SCAL) {
             // exp(Gam_i - Gam_j) and the input weight of token j, applied once
             const float dec = ok ? __expf(s_gam[i] - s_gam[j]) * s_w[j] : 0.f;
@@ -423,12 +424,12 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
         if (cn >= G::NVT) continue;
         // inter part K^ dS' for the four token blocks, contracting over d_k in
         // 32-wide steps (outer) so one split dS fragment is live at a time
-        f32x4 av[4];
+        AV av[4];
 #pragma unroll
-        for (int J = 0; J < 4; ++J) av[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int J = 0; J < 4; ++J) av[J] = AV{0, 0, 0, 0};
 #pragma unroll
         for (int kb = 0; kb < G::DKP / 32; ++kb) {
-          const f32x4 lo = dS[2 * kb][cc], hi = dS[2 * kb + 1][cc];
+          const AV lo = dS[2 * kb][cc], hi = dS[2 * kb + 1][cc];
           Frag<E> fs, fsl;
           acc_to_frag_split(fs, fsl, lo, hi);
 #pragma unroll
@@ -449,7 +450,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
           const int tj = 16 * J + i16;
-          f32x4 acc = av[J] * s_fk[tj];
+          AV acc = av[J] * s_fk[tj];
 #pragma unroll
           for (int ib = 0; ib < 2; ++ib) {
             if (ib == 0 && J >= 2) continue;
@@ -484,16 +485,16 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
         // in the permuted order {32kn + 4g + e, 32kn + 16 + 4g + e}, the positions the
         // dS^T accumulators hold, so T3 is an elementwise product on the way.
         float t3 = 0.f;
-        f32x4 ax[4];
+        AV ax[4];
 #pragma unroll
-        for (int I = 0; I < 4; ++I) ax[I] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int I = 0; I < 4; ++I) ax[I] = AV{0, 0, 0, 0};
 #pragma unroll
         for (int kn = 0; kn < G::DVP / 32; ++kn) {
           float x[8];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const f32x4 sv = s0r[cc][2 * kn + hh];
-            const f32x4 tv = dT[2 * kn + hh][cc];
+            const f32x4 tv = narrow4(dT[2 * kn + hh][cc]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               x[4 * hh + e] = sv[e];
@@ -530,11 +531,11 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
 #pragma unroll
           for (int I = 0; I < 4; ++I) {
             const int ti = 16 * I + i16;
-            f32x4 acc = ax[I];
+            AV acc = ax[I];
             if constexpr (SCAL) {
               const f32x4 q4 = load4f(s_q + ti * G::LDK + 16 * cm + 4 * g);
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) u1p[I] += q4[rr] * acc[rr];
+              for (int rr = 0; rr < 4; ++rr) u1p[I] += q4[rr] * (float)acc[rr];
             }
             acc *= s_fq[ti];
 #pragma unroll
@@ -557,7 +558,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
               for (int rr = 0; rr < 4; ++rr) {
                 const int d = d0 + rr;
                 const bool ok = d < DK;
-                wv[cc][I][rr] = ok ? q4[rr] * acc[rr] : 0.f;
+                wv[cc][I][rr] = ok ? q4[rr] * (float)acc[rr] : 0.f;
                 acc[rr] *= ok ? __expf(gm[rr]) : 0.f;
               }
             }
@@ -566,16 +567,16 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
         }
         // Y'^T = dS'^T V^T (dS' = dS scaled by exp(Gam_last[d]) for a diagonal decay),
         // contracting over d_v outer as above
-        f32x4 ay[4];
+        AV ay[4];
 #pragma unroll
-        for (int J = 0; J < 4; ++J) ay[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int J = 0; J < 4; ++J) ay[J] = AV{0, 0, 0, 0};
 #pragma unroll
         for (int kn = 0; kn < G::DVP / 32; ++kn) {
           float y[8];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            y[e] = dT[2 * kn][cc][e];
-            y[4 + e] = dT[2 * kn + 1][cc][e];
+            y[e] = (float)dT[2 * kn][cc][e];
+            y[4 + e] = (float)dT[2 * kn + 1][cc][e];
           }
           Frag<E> fdt, fdtl;
           split_frag(fdt, fdtl, y);
@@ -598,13 +599,13 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
             const int tj = 16 * J + i16;
-            f32x4 yv = ay[J] * s_fk[tj];
+            AV yv = ay[J] * s_fk[tj];
             if constexpr (SCAL) {
               const f32x4 k4 = load4f(s_k + tj * G::LDK + 16 * cm + 4 * g);
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) u4p[J] += k4[rr] * yv[rr];
+              for (int rr = 0; rr < 4; ++rr) u4p[J] += k4[rr] * (float)yv[rr];
             }
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            AV acc = {0, 0, 0, 0};
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib) {
               if (ib == 0 && J >= 2) continue;
@@ -624,9 +625,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
                 const int d = d0 + rr;
                 const bool ok = d < DK;
                 const float kt = ok ? k4[rr] : 0.f;
-                const float wfull = wv[cc][J][rr] - kt * acc[rr];
+                const float wfull = wv[cc][J][rr] - kt * (float)acc[rr];
                 wtot[cc][rr] += wfull;
-                wv[cc][J][rr] = kt * yv[rr] - wfull;
+                wv[cc][J][rr] = kt * (float)yv[rr] - wfull;
                 acc[rr] = ok ? (acc[rr] + yv[rr]) * __expf(-gm[rr]) : 0.f;
               }
             } else {
@@ -831,7 +832,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void bwd_wal
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int d = 16 * m + 4 * g + rr, n = 16 * cn + i16;
-          if (cn < G::NVT && d < DK && n < DV) gm[d * DV + n] = dS[m][cc][rr];
+          if (cn < G::NVT && d < DK && n < DV) gm[d * DV + n] = (float)dS[m][cc][rr];
         }
       }
   }

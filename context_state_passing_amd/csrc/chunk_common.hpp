@@ -378,6 +378,9 @@ __device__ __forceinline__ void store_split4(bf16_t* hi, bf16_t* lo, int off, co
 __device__ __forceinline__ void store_split4(float* hi, float*, int off, const f32x4& x) {
   *reinterpret_cast<f32x4*>(hi + off) = x;
 }
+__device__ __forceinline__ void store_split4(float* hi, float* lo, int off, const f64x4& x) {
+  store_split4(hi, lo, off, narrow4(x));
+}
 
 // Store 4 consecutive values (output feature 4g..4g+3 of a 16-wide tile).
 __device__ __forceinline__ void store4(bf16_t* p, const f32x4& x) {
@@ -387,5 +390,6 @@ __device__ __forceinline__ void store4(bf16_t* p, const f32x4& x) {
   *reinterpret_cast<bf16x4*>(p) = y;
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
+__device__ __forceinline__ void store4(float* p, const f64x4& x) { store4(p, narrow4(x)); }
 
 }  // namespace cpla

@@ -1,12 +1,19 @@
 // Device primitives for the chunkwise linear-attention kernels (gfx950 only).
 //
-// MFMA: v_mfma_f32_16x16x32_bf16 (bf16 operands) and v_mfma_f32_16x16x4_f32
-// (fp32 operands, eight issues per 32-deep step). A "fragment" is the 8 values a
+// MFMA: v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32 accumulators) and
+// v_mfma_f64_16x16x4_f64 (fp32 operands widened exactly to fp64, fp64
+// accumulators, eight issues per 32-deep step). A "fragment" is the 8 values a
 // lane contributes to one 16x16x32 step: lane l holds operand row/column l%16
 // and the 8 contraction indices {8g + e} (g = l/16), or a permuted set when the
-// fragment is rebuilt from accumulators (see acc_to_frag). The fp32 form splits
-// the same 8 indices over eight 16x16x4 issues, so both element types share
-// every layout below.
+// fragment is rebuilt from accumulators (see acc_to_frag). The fp64 form splits
+// the same 8 indices over eight 16x16x4 issues. Its accumulator tile puts rows
+// g, g+4, g+8, g+12 in lane group g (measured), where the fp32 tiles put rows
+// 4g..4g+3; the fp64 issue therefore takes its first operand's rows permuted
+// (a 4x4 transpose within each 16-lane group), which lands the product rows in
+// the fp32 layout, so both element types share every layout below. With fp32
+// inputs every product and every sum a walk carries from chunk to chunk is thus
+// formed in fp64, and a value is rounded to fp32 only where it is stored or
+// becomes an operand.
 //
 // LDS tiles are token-major (as the inputs sit in HBM) with 16 bytes of padding
 // per row. Contractions over features read fragments directly; contractions over
@@ -24,6 +31,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 
 constexpr int CH = 64;      // chunk length (tokens)
 // Waves per workgroup for a (padded) head size: 8 at 128 (two per SIMD, so one
@@ -70,12 +78,32 @@ __device__ __forceinline__ float to_f(float x) { return x; }
 
 template <typename E> constexpr int lds_pad() { return 16 / (int)sizeof(E); }
 
+// Accumulator tile (4 values per lane) of the products of E operands: fp32 for
+// bf16, fp64 for fp32.
+template <typename E> struct AccT;
+template <> struct AccT<bf16_t> { typedef f32x4 type; };
+template <> struct AccT<float> { typedef f64x4 type; };
+template <typename E> using acc4 = typename AccT<E>::type;
+// an fp32 vector as the accumulator type V (exact)
+template <typename V> __device__ __forceinline__ V widen4(const f32x4& x) { return __builtin_convertvector(x, V); }
+// accumulator values as fp32 (rounded once for fp64)
+__device__ __forceinline__ f32x4 narrow4(const f32x4& x) { return x; }
+__device__ __forceinline__ f32x4 narrow4(const f64x4& x) { return __builtin_convertvector(x, f32x4); }
+
 __device__ __forceinline__ void mma(f32x4& acc, const Frag<bf16_t>& a, const Frag<bf16_t>& b) {
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
 }
-__device__ __forceinline__ void mma(f32x4& acc, const Frag<float>& a, const Frag<float>& b) {
+// fp64 issue: lane l supplies row 4(x%4) + x/4 (x = l%16) of the first operand,
+// read from the lane holding that row, so that accumulator row 4g + rr sits in
+// lane group g as in the fp32 tiles
+__device__ __forceinline__ void mma(f64x4& acc, const Frag<float>& a, const Frag<float>& b) {
+  const int l = lane_id();
+  const int src = (l & 48) | ((l & 3) << 2) | ((l >> 2) & 3);
 #pragma unroll
-  for (int s = 0; s < 8; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[s], b.v[s], acc, 0, 0, 0);
+  for (int s = 0; s < 8; ++s) {
+    const float ar = __shfl(a.v[s], src, 64);
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)ar, (double)b.v[s], acc, 0, 0, 0);
+  }
 }
 
 template <typename E> __device__ __forceinline__ void frag_zero(Frag<E>& f) {
@@ -169,10 +197,10 @@ __device__ __forceinline__ int kidx_perm(int e, int l = lane_id()) { return 4 * 
 // Two 16x16 accumulator tiles stacked along their row index (rows r0..r0+31,
 // lane-fixed column) as one operand fragment contracting over those rows, in the
 // permuted order {r0 + 4g + e, r0 + 16 + 4g + e}. `s0`, `s1` scale rows.
-template <typename E>
-__device__ __forceinline__ void acc_to_frag(Frag<E>& f, const f32x4& lo, const f32x4& hi) {
+template <typename E, typename V>
+__device__ __forceinline__ void acc_to_frag(Frag<E>& f, const V& lo, const V& hi) {
 #pragma unroll
-  for (int e = 0; e < 4; ++e) { f.v[e] = to_e<E>(lo[e]); f.v[4 + e] = to_e<E>(hi[e]); }
+  for (int e = 0; e < 4; ++e) { f.v[e] = to_e<E>((float)lo[e]); f.v[4 + e] = to_e<E>((float)hi[e]); }
 }
 
 // ---- split bf16 arithmetic ---------------------------------------------------------
@@ -218,8 +246,8 @@ __device__ __forceinline__ void split_frag(Frag<bf16_t>& hi, Frag<bf16_t>& lo, c
   lo.v = __builtin_convertvector(r, bf16x8);
 }
 // acc += (a_hi + a_lo) (b_hi + b_lo), dropping lo*lo
-template <typename E>
-__device__ __forceinline__ void mma3(f32x4& acc, const Frag<E>& ah, const Frag<E>& al, const Frag<E>& bh,
+template <typename E, typename V>
+__device__ __forceinline__ void mma3(V& acc, const Frag<E>& ah, const Frag<E>& al, const Frag<E>& bh,
                                      const Frag<E>& bl) {
   mma(acc, ah, bh);
   if constexpr (Split<E>::on) {
@@ -228,23 +256,23 @@ __device__ __forceinline__ void mma3(f32x4& acc, const Frag<E>& ah, const Frag<E
   }
 }
 // acc += (a_hi + a_lo) b
-template <typename E>
-__device__ __forceinline__ void mma2a(f32x4& acc, const Frag<E>& ah, const Frag<E>& al, const Frag<E>& b) {
+template <typename E, typename V>
+__device__ __forceinline__ void mma2a(V& acc, const Frag<E>& ah, const Frag<E>& al, const Frag<E>& b) {
   mma(acc, ah, b);
   if constexpr (Split<E>::on) mma(acc, al, b);
 }
 // acc += a (b_hi + b_lo)
-template <typename E>
-__device__ __forceinline__ void mma2b(f32x4& acc, const Frag<E>& a, const Frag<E>& bh, const Frag<E>& bl) {
+template <typename E, typename V>
+__device__ __forceinline__ void mma2b(V& acc, const Frag<E>& a, const Frag<E>& bh, const Frag<E>& bl) {
   mma(acc, a, bh);
   if constexpr (Split<E>::on) mma(acc, a, bl);
 }
 // Two accumulator tiles (see acc_to_frag) as split hi/lo fragments.
-template <typename E>
-__device__ __forceinline__ void acc_to_frag_split(Frag<E>& hi, Frag<E>& lo, const f32x4& a, const f32x4& b) {
+template <typename E, typename V>
+__device__ __forceinline__ void acc_to_frag_split(Frag<E>& hi, Frag<E>& lo, const V& a, const V& b) {
   float x[8];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+  for (int e = 0; e < 4; ++e) { x[e] = (float)a[e]; x[4 + e] = (float)b[e]; }
   split_frag(hi, lo, x);
 }
 // Store x as hi (and lo) into two LDS tiles at the same offset.

@@ -18,8 +18,8 @@ namespace cpla {
 
 // S <- diag(exp(Gam_last)) keep*S + K^T V with the tail/decay token factors.
 // K^ = K exp(Gam_last - Gam) tail enters the MFMA split into hi + lo parts.
-template <typename E, int DK, int DV, int DECAY, int NKT_, int CPWV_>
-__device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* Kt, const E* Ktl, const E* Vt,
+template <typename E, int DK, int DV, int DECAY, int NKT_, int CPWV_, typename V>
+__device__ __forceinline__ void state_update(V (&S)[NKT_][CPWV_], const E* Kt, const E* Ktl, const E* Vt,
                                              const float* gam, const float* el, const float* fk,
                                              const ChunkSeg& seg, int l) {
   using G = Geo<E, DK, DV>;
@@ -91,7 +91,7 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[NKT_][CPWV_], const E* K
 }
 
 template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL, bool SPLIT>
-__global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_walk(FwdArgs a) {
+__global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 ? 2 : 4))) void fwd_walk(FwdArgs a) {
   static_assert(APPLY || !SPLIT, "only the apply walk divides a shard");
   using G = Geo<E, DK, DV>;
   // diagonal decay: the prepare walk stages Gam rows 32..63 in the v tile's buffer
@@ -125,7 +125,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
   const int64_t tshard = shard_begin(a.T, a.P, r), slen = shard_len(a.T, a.P, r);
   const int nc = (int)chunks_of(slen);
 
-  f32x4 S[G::NKT][G::CPWV];
+  acc4<E> S[G::NKT][G::CPWV];   // fp32 (bf16 inputs) or fp64 (fp32 inputs)
 #pragma unroll
   for (int m = 0; m < G::NKT; ++m)
 #pragma unroll
@@ -213,7 +213,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
         if (s * G::NW + w >= N_SCORE_TILES) continue;
         const int idx = score_tile(s * G::NW + w);
         const int I = idx >> 2, J = idx & 3;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc4<E> acc = {0, 0, 0, 0};
         if (!score_tile_zero(idx)) {
 #pragma unroll
           for (int kd = 0; kd < G::DKP / 32; ++kd) {
@@ -234,7 +234,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
           const int i = 16 * I + 4 * g + rr, j = 16 * J + i16;
           float x = 0.f;
           if (seg.same(i, j)) {
-            x = acc[rr];
+            x = (float)acc[rr];
             if constexpr (DECAY == DECAY_SCALAR) x *= __expf(s_gam[i] - s_gam[j]) * s_w[j];
           }
           store_split(s_a, s_al, i * G::LDA + j, x);
@@ -258,7 +258,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
         for (int jb = 0; jb < 2; ++jb) frag_tr(fvt[jb], s_v, G::LDV, 32 * jb, 16 * cn, l);
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          acc4<E> acc = {0, 0, 0, 0};
 #pragma unroll
           for (int kb = 0; kb < G::DKP / 32; ++kb) {
             Frag<E> fb, fbl;
@@ -300,7 +300,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int d = 16 * m + 4 * g + rr, n = 16 * cn + i16;
-              if (cn < G::NVT && d < DK && n < DV) cs[d * DV + n] = S[m][cc][rr];
+              if (cn < G::NVT && d < DK && n < DV) cs[d * DV + n] = (float)S[m][cc][rr];
             }
           }
       }
@@ -330,7 +330,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : 4)) void fwd_wal
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int d = 16 * m + 4 * g + rr, n = 16 * cn + i16;
-          if (cn < G::NVT && d < DK && n < DV) ds[d * DV + n] = S[m][cc][rr];
+          if (cn < G::NVT && d < DK && n < DV) ds[d * DV + n] = (float)S[m][cc][rr];
         }
       }
   }

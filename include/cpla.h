@@ -43,9 +43,13 @@
  *                 then dk*dv entries hold delta_S (or gamma), row = key dim.
  *                 M is 0 for a shard that contains a packed-sequence start.
  *       per-shard states [P, B, H, dk, dv] fp32
- *       chunk states [B, H, T/chunk, dk, dv] fp32: the state entering every
- *                 chunk (saved by the forward for the backward)
- *   - Shard r covers tokens [r*T/P, (r+1)*T/P) of every row.
+ *       chunk states [B, H, n_chunks, dk, dv] fp32: the state entering every
+ *                 64-token chunk of every shard, the shards' chunks in order
+ *                 (n_chunks = sum over shards of ceil(shard length / 64));
+ *                 saved by the forward for the backward
+ *   - Shard r covers tokens [r*L, min((r+1)*L, T)) of every row, L = ceil(T/P)
+ *     (torch.chunk's division: the last non-empty shard may be shorter and
+ *     trailing shards empty).
  *   - Alignment: every device pointer 16-byte aligned.
  *   - Validation happens on the host before any launch. On failure a call
  *     returns a non-zero cpla_status, launches nothing, and sets a message
@@ -305,6 +309,15 @@ cpla_status cpla_ssd_input_grads(const cpla_ssd_problem* p, const float* dt, con
 const char* cpla_last_error(void);
 
 int cpla_abi_version(void);
+
+/* Testing aid for the divided apply walks (no decay or a scalar decay): on grids
+ * too small to fill the GPU, cp_forward_apply and cp_backward_apply divide each
+ * shard's walk among up to four workgroups, each replaying the state (or adjoint)
+ * up to its own chunks, which gives the bits of the undivided walk. parts = 1, 2
+ * or 4 forces that division (halved until every part holds a chunk), 0 restores
+ * the automatic choice. Process-wide; returns the previous setting, or -1 (and
+ * changes nothing) for any other value. */
+int cpla_set_apply_parts(int parts);
 
 #ifdef __cplusplus
 }

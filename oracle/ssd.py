@@ -11,7 +11,7 @@ go through the linear-attention oracle — so that a test can pin the mapping
 between the two.
 
 Per (b, h) with group gr = h // (H // G) sharing B and C, state h_t of shape
-[N, P] (here P = N):
+[N, P] (state size N, head dim P; N and P may differ):
 
     h_{-1} = h_init (zero unless given);  h_{t-1} := 0 at a packed-sequence start
     a_t = exp(dt_t * A_h)
