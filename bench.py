@@ -45,8 +45,6 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", default="diag_fwdbwd")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold-steps", type=int, default=10,
-                    help="extra steps timed one by one after evicting L2 and the MALL (0 = skip)")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows (b,h) in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
@@ -108,30 +106,81 @@ def read_traffic():
         return None, "summary incomplete"
 
 
-def measured_copy_gbps(stream, reps: int = 10):
-    """Attainable HBM rate for context beside the published peak: a plain 1 GiB
-    fp32 device copy on the launch stream, (bytes read + bytes written) / time,
-    median of `reps` copies timed one by one with HIP events."""
+def _peaks_lib():
+    path = os.path.join(ROOT, "context_state_passing_amd", "libcpla_peaks.so")
+    L = ctypes.CDLL(path)
+    L.cpla_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+    L.cpla_peak_mfma.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    L.cpla_peak_mfma_flops.argtypes = [ctypes.c_int]
+    L.cpla_peak_mfma_flops.restype = ctypes.c_int64
+    return L
+
+
+def _median_ms(stream, fn, reps):
     import torch
-    n = (1 << 30) // 4
-    x = torch.empty(n, device=stream.device).fill_(1.0)
-    y = torch.empty_like(x)
-    with torch.cuda.stream(stream):
-        for _ in range(3):
-            y.copy_(x)
-        times = []
-        for _ in range(reps):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            y.copy_(x)
-            e1.record(stream)
-            e1.synchronize()
-            times.append(e0.elapsed_time(e1))
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        times.append(e0.elapsed_time(e1))
     times.sort()
-    ms = times[len(times) // 2]
+    return times[len(times) // 2]
+
+
+def measured_peaks(stream, reps: int = 10):
+    """Attainable peaks beside the published ones, from the hand-written probes of
+    libcpla_peaks.so on the launch stream: a streaming copy of 1 GiB (bytes read +
+    bytes written over the median time of `reps` copies; the best of three copy
+    variants and four grid sizes) and the MFMA issue loops (flops over the median
+    time; bf16 takes the better of the 16x16x32 and 32x32x16 issues)."""
+    import torch
+    L = _peaks_lib()
+    dev = stream.device
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    n = 1 << 30
+    x = torch.empty(n // 4, device=dev).fill_(1.0)
+    y = torch.empty_like(x)
+    best = None
+    for variant in (0, 1, 2):
+        for blocks in (cus * 4, cus * 8, cus * 16, cus * 32):
+            def copy(variant=variant, blocks=blocks):
+                rc = L.cpla_peak_copy(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()), n, blocks,
+                                      variant, sp)
+                if rc != 0:
+                    raise RuntimeError(f"cpla_peak_copy failed ({rc})")
+            copy()
+            ms = _median_ms(stream, copy, reps)
+            if best is None or ms < best[0]:
+                best = (ms, variant, blocks)
+    ms, variant, blocks = best
+    out = {"copy_GBps": 2 * n / (ms * 1e-3) / 1e9, "copy_ms": ms, "bytes": 2 * n,
+           "copy_note": f"hand-written streaming copy of 1 GiB (read + write), best of 3 variants x 4 grids: "
+                        f"variant {variant}, {blocks} workgroups, median of {reps}"}
     del x, y
-    return {"copy_GBps": 2 * n * 4 / (ms * 1e-3) / 1e9, "copy_ms": ms, "bytes": 2 * n * 4,
-            "note": "torch device copy of 1 GiB fp32 (read + write), median of %d" % reps}
+    mblocks = cus * 4            # sixteen waves per compute unit, four per SIMD
+    buf = torch.empty(mblocks * 256, device=dev)
+    rates = {}
+    for kind, iters in ((0, 2048), (3, 2048), (1, 512), (2, 256)):
+        def run(kind=kind, iters=iters):
+            rc = L.cpla_peak_mfma(kind, ctypes.c_void_p(buf.data_ptr()), mblocks, iters, sp)
+            if rc != 0:
+                raise RuntimeError(f"cpla_peak_mfma failed ({rc})")
+        run()
+        ms = _median_ms(stream, run, 5)
+        rates[kind] = mblocks * 4 * iters * L.cpla_peak_mfma_flops(kind) / (ms * 1e-3) / 1e12
+    out["mfma_bf16_TFLOPs"] = max(rates[0], rates[3])
+    out["mfma_bf16_16x16x32_TFLOPs"] = rates[0]
+    out["mfma_bf16_32x32x16_TFLOPs"] = rates[3]
+    out["mfma_f32_TFLOPs"] = rates[1]
+    out["mfma_f64_TFLOPs"] = rates[2]
+    out["mfma_note"] = (f"MFMA issue loops, {mblocks} workgroups of 4 waves, 8 (16x16) or 4 (32x32) independent "
+                        "accumulators per wave, median of 5")
+    return out
 
 
 # ---- CPU baseline: the fp64 oracle on a bounded sample ----------------------------------
@@ -162,8 +211,10 @@ def _oracle_row(args):
 
 
 def cpu_baseline(wl, rows_req):
-    """Oracle fwd+bwd on a few full-length (b, h) rows, one single-threaded
-    worker process per row, forked before the GPU is initialised."""
+    """Oracle fwd+bwd on a few full-length (b, h) rows, forked before the GPU is
+    initialised, in two modes: one single-threaded worker process per row (all the
+    cores the process may use, up to 16), and one row in this process on a single
+    thread (BLAS/OpenMP pools limited to one thread)."""
     global _WL
     import multiprocessing as mp
     _WL = wl
@@ -176,13 +227,18 @@ def cpu_baseline(wl, rows_req):
         per = pool.map(_oracle_row, pairs)
     wall = time.perf_counter() - t0
     tok_heads = rows * wl.T
-    return {"value": tok_heads / wl.H / wall, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-            "sample": f"fp64 oracle CP {'fwd' if wl.dO is None else 'fwd+bwd'} (summaries, composition, "
-                      f"per-token recurrence{'' if wl.dO is None else ' and adjoint'}) on "
-                      f"{rows} of the {wl.B * wl.H} (b,h) rows at full T={wl.T}, {wl.num_shards} shards; "
-                      f"{workers} single-threaded processes, wall {wall:.1f}s, {sum(per):.1f} CPU-s; "
-                      f"value = row-tokens/s / H",
-            "cpu_seconds": round(sum(per), 2)}
+    single = _oracle_row(pairs[0])       # the same work, one row, one thread, this process
+    what = (f"fp64 oracle CP {'fwd' if wl.dO is None else 'fwd+bwd'} (summaries, composition, "
+            f"per-token recurrence{'' if wl.dO is None else ' and adjoint'})")
+    return {"value": tok_heads / wl.H / wall, "unit": "tokens/s", "cores": avail, "kind": "oracle",
+            "threads": workers,
+            "sample": f"{what} on {rows} of the {wl.B * wl.H} (b,h) rows at full T={wl.T}, "
+                      f"{wl.num_shards} shards; {workers} single-threaded processes on the {avail} cores "
+                      f"this process may use, wall {wall:.1f}s, {sum(per):.1f} CPU-s; value = row-tokens/s / H",
+            "cpu_seconds": round(sum(per) + single, 2),
+            "single_thread": {"value": wl.T / wl.H / single, "unit": "tokens/s", "threads": 1,
+                              "sample": f"one (b,h) row at full T={wl.T}, one thread, {single:.1f}s"},
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
 
 
 # ---- Mamba2 (SSD) workload ----------------------------------------------------------------
@@ -545,33 +601,35 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    # Timed: exactly K steps, each after 512 MiB written to a scratch buffer
+    # outside its timed window (so that no input is left in L2 or the 256 MB MALL:
+    # every step reads its inputs from HBM), timed step by step with HIP events on
+    # the launch stream; the per-call breakdown comes from the same events.
+    flush = torch.empty(512 << 18, dtype=torch.float32, device=dev)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record(stream)
     for i in range(args.steps):
+        flush.fill_(float(i))
         step(evs[i])
-    t_end.record(stream)
     torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    per_step = [e[0].elapsed_time(e[nev - 1]) for e in evs]
+    ms_step = sum(per_step) / args.steps
     parts = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j in range(nev - 1)]
     names = ["cp_forward_prepare", "cp_forward_apply", "cp_backward_prepare", "cp_backward_apply"][:nev - 1]
-
-    # Cold caches: before each of a few steps (outside the timed region) write a
-    # 512 MiB scratch buffer so that no input is still resident in L2 or the MALL.
-    cold = []
-    flush = torch.empty(512 << 18, dtype=torch.float32, device=dev) if args.cold_steps > 0 else None
-    for i in range(args.cold_steps):
-        flush.fill_(float(i))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        cold.append(e0.elapsed_time(e1))
-    cold.sort()
     del flush
+
+    # Warm: the same K steps back to back (caches hold whatever the previous step left).
+    wevs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(args.steps)]
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0.record(stream)
+    for i in range(args.steps):
+        step(wevs[i])
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / args.steps
+    warm_parts = [sum(e[j].elapsed_time(e[j + 1]) for e in wevs) / args.steps for j in range(nev - 1)]
 
     tokens = B * T
     th = tokens * H
@@ -583,9 +641,11 @@ def main():
         dom_ms, dom_bytes, dom_name = parts[1], alg["bytes_fwd"] * th, "fwd_walk (cp_forward_apply)"
         traffic, tnote = None, "counters are taken for the backward walk of the default workload"
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    attainable = measured_copy_gbps(stream)
+    peaks = measured_peaks(stream)
     step_bytes = (alg["bytes_fwd"] + (alg["bytes_bwd_apply"] if backward else 0)) * th
     step_flops = (alg["flops_fwd"] + (alg["flops_bwd"] if backward else 0)) * th
+    step_gbps = step_bytes / (ms_step * 1e-3) / 1e9
+    step_tflops = step_flops / (ms_step * 1e-3) / 1e12
     out = {
         "metric": METRIC if wl.name == "diag_fwdbwd" else
                   f"{'fwd+bwd' if backward else 'fwd'} tokens/s, {wl.name} (B{B} H{H} T{T} d{d} {wl.decay} decay)",
@@ -601,25 +661,30 @@ def main():
         "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32",
         "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "dk": d, "dv": d, "chunk": wl.chunk,
-                   "shards": P, "decay": wl.decay, "parallelism": "single-gpu (shards simulated in HBM)"},
+                   "shards": P, "decay": wl.decay, "parallelism": "single-gpu (shards simulated in HBM)",
+                   "caches": "L2 and MALL flushed before every timed step"},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "traffic_note": tnote,
                      "algorithmic_bytes_per_launch": dom_bytes, "launch_ms": dom_ms,
-                     "frac_of_copy": achieved / attainable["copy_GBps"],
-                     "counted_frac_of_copy": None if traffic is None else
-                         traffic / (dom_ms * 1e-3) / 1e9 / attainable["copy_GBps"]},
-        "hbm_attainable": attainable,
+                     "measured_peak": peaks["copy_GBps"],
+                     "frac_of_measured": achieved / peaks["copy_GBps"],
+                     "counted_frac_of_measured": None if traffic is None else
+                         traffic / (dom_ms * 1e-3) / 1e9 / peaks["copy_GBps"]},
+        "measured_peaks": peaks,
         "step_breakdown_ms": dict(zip(names, parts)),
-        "step_roofline": {"algorithmic_GBps": step_bytes / (ms_step * 1e-3) / 1e9,
-                          "hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                          "mfma_TFLOPs": step_flops / (ms_step * 1e-3) / 1e12,
-                          "mfma_frac": step_flops / (ms_step * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS},
+        "step_roofline": {"algorithmic_GBps": step_gbps,
+                          "hbm_frac": step_gbps / HBM_PEAK_GBS,
+                          "hbm_frac_of_measured": step_gbps / peaks["copy_GBps"],
+                          "mfma_TFLOPs": step_tflops,
+                          "mfma_frac": step_tflops / MFMA_BF16_PEAK_TFLOPS,
+                          "mfma_frac_of_measured": step_tflops / peaks["mfma_bf16_TFLOPs"]},
         "fwd_tokens_per_s": tokens / ((parts[0] + parts[1]) * 1e-3),
-        "cold_cache": None if not cold else {
-            "ms_per_step_median": cold[len(cold) // 2], "ms_per_step_min": cold[0],
-            "tokens_per_s": tokens / (cold[len(cold) // 2] * 1e-3), "steps": len(cold),
-            "note": "512 MiB written before each step (outside the timed region) to evict L2 and MALL"},
+        "per_step_ms": {"min": min(per_step), "median": sorted(per_step)[len(per_step) // 2],
+                        "max": max(per_step)},
+        "warm": {"ms_per_step": warm_ms, "tokens_per_s": tokens / (warm_ms * 1e-3),
+                 "step_breakdown_ms": dict(zip(names, warm_parts)),
+                 "note": "the same steps back to back without flushing the caches"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

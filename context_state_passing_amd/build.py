@@ -2,7 +2,8 @@
 
 Every HIP translation unit is compiled for gfx950 only, with packed-fp32
 instructions disabled, then linked into ``context_state_passing_amd/libcpla.so``
-next to this file. ``build()`` always recompiles.
+next to this file; the benchmark's attainable-peak probes (``csrc/peaks.hip``)
+go into ``libcpla_peaks.so`` beside it. ``build()`` always recompiles.
 """
 from __future__ import annotations
 
@@ -17,9 +18,11 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcpla.so")
+PEAKS_LIB = os.path.join(PKG, "libcpla_peaks.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["abi.hip", "fwd.hip", "bwd.hip", "scan.hip", "ssd.hip", "delta.hip", "metadata.cpp"]
+PEAKS_SOURCES = ["peaks.hip"]
 
 HIP_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
@@ -47,18 +50,24 @@ def _compile(src):
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"linking libcpla.so failed:\n{res.stderr[-8000:]}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(out)} failed:\n{res.stderr[-8000:]}")
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PEAKS_SOURCES], PEAKS_LIB)
     if verbose:
-        print(f"built {LIB}", file=sys.stderr)
+        print(f"built {LIB} and {PEAKS_LIB}", file=sys.stderr)
     return LIB
 
 

@@ -32,6 +32,27 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(L, n), n
 
 
+def test_peaks_library_exports():
+    # the benchmark's attainable-peak probes (copy kernel, MFMA issue loops)
+    P = ctypes.CDLL(os.path.join(ROOT, "context_state_passing_amd", "libcpla_peaks.so"))
+    for n in ("cpla_peak_copy", "cpla_peak_mfma", "cpla_peak_mfma_flops"):
+        assert hasattr(P, n), n
+    P.cpla_peak_mfma_flops.restype = ctypes.c_int64
+    assert [P.cpla_peak_mfma_flops(k) for k in (0, 1, 2, 3, 4)] == [8 * 16384, 8 * 2048, 8 * 2048, 4 * 32768, 0]
+    # bad arguments are refused before any launch
+    P.cpla_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                 ctypes.c_void_p]
+    assert P.cpla_peak_copy(FAKE, FAKE, 15, 1, 0, None) == -1
+    assert P.cpla_peak_copy(MISALIGNED, FAKE, 16, 1, 0, None) == -1
+    assert P.cpla_peak_copy(FAKE, FAKE, 16, 1, 3, None) == -1
+
+
+def test_apply_parts_knob():
+    assert L.cpla_set_apply_parts(3) == -1
+    assert L.cpla_set_apply_parts(2) == 0
+    assert L.cpla_set_apply_parts(0) == 2
+
+
 def test_abi_version():
     assert L.cpla_abi_version() == 5
 
