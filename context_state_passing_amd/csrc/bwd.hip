@@ -96,7 +96,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   constexpr bool GSPLIT = !APPLY && DIAG && G::TILE_V * (int)sizeof(E) >= (CH / 2) * DK * 4;
   constexpr int GAM_BYTES = DIAG ? (GSPLIT ? CH / 2 : CH) * DK * 4 : 0;
   constexpr int AT_BYTES = APPLY ? (SP ? 4 : 2) * G::TILE_A * (int)sizeof(E) : 0;
-  constexpr int P_BYTES = (APPLY && SCAL) ? CH * (CH + 1) * 4 : 0;
+  // the scalar decay's dg / dw sums: fp32 for bf16 inputs, fp64 for fp32 inputs
+  using AS = typename std::conditional<sizeof(E) == 2, float, double>::type;
+  constexpr int P_BYTES = (APPLY && SCAL) ? CH * (CH + 1) * (int)sizeof(AS) : 0;
   constexpr int REG_BYTES = (GAM_BYTES > AT_BYTES + P_BYTES ? GAM_BYTES : AT_BYTES + P_BYTES) + 16;
   // Apply walk, bf16 with a diagonal decay: the next chunk's raw inputs are copied
   // into LDS by DMA once the dk phase is done (q into a buffer of its own; k, v,
@@ -119,21 +121,27 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   __shared__ __attribute__((aligned(16))) E s_pq[PF ? CH * DK : 8];
   constexpr int NRED = SCAL ? G::NW : 1;                          // scalar decay: per-wave T3 partials
   constexpr int NU = (APPLY && SCAL) ? G::NW * CH : 1;           // scalar dg token partials
-  __shared__ float s_gs[DIAG ? 1 : CH], s_fq[CH], s_fk[CH], s_red[NRED], s_el[DIAG ? G::DKP : 1];
-  __shared__ float s_u1[NU], s_u4[NU];
+  // Gam: fp64 for a scalar decay with fp32 inputs (see finish_gamma)
+  using GT = typename std::conditional<sizeof(E) == 4 && SCAL, double, float>::type;
+  __shared__ GT s_gs[DIAG ? 1 : CH];
+  __shared__ float s_fq[CH], s_fk[CH], s_el[DIAG ? G::DKP : 1];
+  __shared__ AS s_red[NRED], s_u1[NU], s_u4[NU];
   __shared__ float s_w[SCAL ? CH : 1];   // per-token input weights (scalar decay)
 
-  float* s_gam = DIAG ? reinterpret_cast<float*>(s_reg) : s_gs;
+  GT* s_gam = DIAG ? reinterpret_cast<GT*>(s_reg) : s_gs;
   E* s_ah = reinterpret_cast<E*>(s_reg);
   E* s_al = s_ah + G::TILE_A;
   E* s_dah = s_ah + (SP ? 2 : 1) * G::TILE_A;
   E* s_dal = s_dah + G::TILE_A;
-  float* s_p = reinterpret_cast<float*>(s_reg + AT_BYTES);
+  AS* s_p = reinterpret_cast<AS*>(s_reg + AT_BYTES);
   // the tile Q^ is read from in the dS update: scalar -> s_qh, else the q tile
   const E* qhat_h = SCAL ? s_qh : s_q;
   const E* qhat_l = SCAL ? s_qhl : s_ql;
   float* const gam_hi = GSPLIT ? reinterpret_cast<float*>(s_do) : nullptr;
-  const float* const gam_last = GSPLIT ? gam_hi + (CH / 2 - 1) * DK : s_gam + (CH - 1) * DK;
+  const GT* const gam_last = [&]() -> const GT* {
+    if constexpr (GSPLIT) return gam_hi + (CH / 2 - 1) * DK;
+    else return s_gam + (CH - 1) * DK;
+  }();
 
   const int w = wave_id(), l = lane_id(), g = l >> 4, i16 = l & 15;
   __builtin_assume(w >= 0 && w < G::NW);
@@ -185,7 +193,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   const E* k = reinterpret_cast<const E*>(a.k);
   const E* v = reinterpret_cast<const E*>(a.v);
   const E* dO = reinterpret_cast<const E*>(a.dO);
-  float gsum = 0.f;
+  GT gsum = 0;
   bool any_start = false;
 
   using GamR = GamRegs<DK, DECAY, G::NT>;
@@ -377,8 +385,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
           vd[rr] = ok ? (float)xd[rr] : 0.f;
           if constexpr (SCAL) {
             // exp(Gam_i - Gam_j) and the input weight of token j, applied once
-            const float dec = ok ? __expf(s_gam[i] - s_gam[j]) * s_w[j] : 0.f;
-            s_p[i * (CH + 1) + j] = va[rr] * vd[rr] * dec;   // exp(Gam_i - Gam_j) w_j (q_i.k_j)(dO_i.v_j)
+            const float dec = ok ? __expf((float)(s_gam[i] - s_gam[j])) * s_w[j] : 0.f;
+            // exp(Gam_i - Gam_j) w_j (q_i.k_j)(dO_i.v_j)
+            s_p[i * (CH + 1) + j] = (AS)(ok ? xa[rr] : 0) * (AS)(ok ? xd[rr] : 0) * (AS)dec;
             va[rr] *= dec;
             vd[rr] *= dec;
           }
@@ -467,8 +476,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
       // ---- dq^T and dk^T tiles: rows = owned d_k tiles, columns = tokens ---------------
       GE* dqp = reinterpret_cast<GE*>(a.dq);
       GE* dkp = reinterpret_cast<GE*>(a.dk);
-      float u1p[4] = {0.f, 0.f, 0.f, 0.f}, u4p[4] = {0.f, 0.f, 0.f, 0.f};  // scalar: per-I token partials
-      float t3p = 0.f;                                                      // scalar: T3 partial
+      AS u1p[4] = {0, 0, 0, 0}, u4p[4] = {0, 0, 0, 0};  // scalar: per-I token partials
+      AS t3p = 0;                                        // scalar: T3 partial
       // diagonal dg: wv holds w_t = Q~*(dq before exp(Gam)) - K~*(intra dk) after the dq
       // loop, then r_t = z_t - w_t with z_t = K~*(tail Y'); dg_t = sum_s w_s + T3 +
       // sum_{s<t} r_s (suffix sums of w plus prefix sums of z, rearranged)
@@ -484,7 +493,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
         // steps (outer) so only one split S0 fragment is live at a time. S0 is read
         // in the permuted order {32kn + 4g + e, 32kn + 16 + 4g + e}, the positions the
         // dS^T accumulators hold, so T3 is an elementwise product on the way.
-        float t3 = 0.f;
+        AS t3 = 0;
         AV ax[4];
 #pragma unroll
         for (int I = 0; I < 4; ++I) ax[I] = AV{0, 0, 0, 0};
@@ -494,11 +503,11 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const f32x4 sv = s0r[cc][2 * kn + hh];
-            const f32x4 tv = narrow4(dT[2 * kn + hh][cc]);
+            const AV tv = dT[2 * kn + hh][cc];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               x[4 * hh + e] = sv[e];
-              t3 += sv[e] * tv[e];
+              t3 += (AS)sv[e] * (AS)tv[e];
             }
           }
           Frag<E> fs0, fs0l;
@@ -514,7 +523,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
           t3 += __shfl_xor(t3, 16, 64);
           t3 += __shfl_xor(t3, 32, 64);
           if constexpr (DIAG) {
-            t3r[cc] = t3;   // for key dim dl in every lane of column i16; dS^T carries exp(Gam_last[d])
+            t3r[cc] = (float)t3;   // for key dim dl in every lane of column i16; dS^T carries exp(Gam_last[d])
           } else {
             if (g == 0) t3p += t3;
           }
@@ -535,7 +544,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
             if constexpr (SCAL) {
               const f32x4 q4 = load4f(s_q + ti * G::LDK + 16 * cm + 4 * g);
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) u1p[I] += q4[rr] * (float)acc[rr];
+              for (int rr = 0; rr < 4; ++rr) u1p[I] += (AS)q4[rr] * (AS)acc[rr];
             }
             acc *= s_fq[ti];
 #pragma unroll
@@ -603,7 +612,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
             if constexpr (SCAL) {
               const f32x4 k4 = load4f(s_k + tj * G::LDK + 16 * cm + 4 * g);
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) u4p[J] += k4[rr] * (float)yv[rr];
+              for (int rr = 0; rr < 4; ++rr) u4p[J] += (AS)k4[rr] * (AS)yv[rr];
             }
             AV acc = {0, 0, 0, 0};
 #pragma unroll
@@ -682,7 +691,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
         // token partials: reduce over the lane groups, then across waves
 #pragma unroll
         for (int I = 0; I < 4; ++I) {
-          float x1 = u1p[I], x4 = u4p[I];
+          AS x1 = u1p[I], x4 = u4p[I];
           x1 += __shfl_xor(x1, 16, 64);
           x1 += __shfl_xor(x1, 32, 64);
           x4 += __shfl_xor(x4, 16, 64);
@@ -692,12 +701,12 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
             s_u4[w * CH + 16 * I + i16] = x4;
           }
         }
-        t3p = wave_sum(g == 0 ? t3p : 0.f);
+        t3p = wave_sum(g == 0 ? t3p : (AS)0);
         if (l == 0) s_red[w] = t3p;
         __syncthreads();
         if (w == 0) {
           const int t = l;
-          float u1 = 0.f, u4 = 0.f;
+          AS u1 = 0, u4 = 0;
 #pragma unroll
           for (int ww = 0; ww < G::NW; ++ww) {
             u1 += s_u1[ww * CH + t];
@@ -705,33 +714,34 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
           }
           u1 *= s_fq[t];
           // T2 step: row t left of the diagonal minus column t below it
-          float rowl = 0.f, colb = 0.f;
+          AS rowl = 0, colb = 0;
           for (int j = 0; j < t; ++j) rowl += s_p[t * (CH + 1) + j];
           for (int i = t + 1; i < CH; ++i) colb += s_p[i * (CH + 1) + t];
-          float x = u1 + rowl - colb;
+          AS x = u1 + rowl - colb;
 #pragma unroll
           for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_down(x, off, 64);
+            const AS y = __shfl_down(x, off, 64);
             if (t + off < 64) x += y;
           }
-          float y4 = u4;
+          AS y4 = u4;
 #pragma unroll
           for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(y4, off, 64);
+            const AS y = __shfl_up(y4, off, 64);
             if (t >= off) y4 += y;
           }
           y4 -= u4;
-          float t3s = 0.f;
+          AS t3s = 0;
 #pragma unroll
           for (int ww = 0; ww < G::NW; ++ww) t3s += s_red[ww];
-          const float t3 = keep * __expf(s_gam[CH - 1]) * t3s;
-          float dgv = x + y4 + t3;
-          if ((seg.starts >> t) & 1ull) dgv = 0.f;
-          if (t < nv) a.dg[(b * a.T + t0 + t) * a.H + h] = dgv;
+          const AS t3 = (AS)(keep * __expf((float)s_gam[CH - 1])) * t3s;
+          AS dgv = x + y4 + t3;
+          if ((seg.starts >> t) & 1ull) dgv = 0;
+          if (t < nv) a.dg[(b * a.T + t0 + t) * a.H + h] = (float)dgv;
           // input-weight gradient dw_t = k_t^T dS_t v_t: the intra part is column t
           // of the P tile on and below the diagonal, the tail part is u4; both carry
           // w_t (in the score decay and the tail factor), divided out here
-          if (a.dw && t < nv) a.dw[(b * a.T + t0 + t) * a.H + h] = (colb + s_p[t * (CH + 1) + t] + u4) / s_w[t];
+          if (a.dw && t < nv)
+            a.dw[(b * a.T + t0 + t) * a.H + h] = (float)((colb + s_p[t * (CH + 1) + t] + u4) / (AS)s_w[t]);
         }
       }
     }
@@ -742,7 +752,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
     {
       // carried part: keep * dS' (diagonal: already scaled), keep * exp(Gam_last) dS
       // (scalar), keep * dS (none); keep = 0 when the chunk holds a start
-      const float f = SCAL ? keep * __expf(s_gam[CH - 1]) : keep;
+      const float f = SCAL ? keep * __expf((float)s_gam[CH - 1]) : keep;
       if (SCAL || seg.any()) {
 #pragma unroll
         for (int m = 0; m < G::NKT; ++m)
@@ -816,10 +826,10 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
     float* rec = a.summary + (int64_t)(r * a.B * a.H + bh) * a.W;
     const float keep = any_start ? 0.f : 1.f;
     if constexpr (DIAG) {
-      if (threadIdx.x < DK) rec[threadIdx.x] = keep * __expf(gsum);
+      if (threadIdx.x < DK) rec[threadIdx.x] = keep * __expf((float)gsum);
     } else {
       if (threadIdx.x < 4) {
-        float mval = SCAL ? __expf(gsum) : 1.f;
+        float mval = SCAL ? __expf((float)gsum) : 1.f;
         rec[threadIdx.x] = threadIdx.x == 0 ? keep * mval : 0.f;
       }
     }

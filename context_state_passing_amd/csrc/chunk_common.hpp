@@ -189,22 +189,26 @@ struct GamRegs {
 //   fk[j] = tail_j * (scalar ? exp(Gam_last - Gam_j) * w_j : 1)
 // and, for a scalar decay, the input weights w_j (1 without them) into wl.
 // Ends with a barrier.
-template <int DK, int DECAY, int NT>
-__device__ __forceinline__ void finish_gamma(GamRegs<DK, DECAY, NT>& R, const ChunkSeg& seg, float* gam,
+// GT, the type of the Gam buffer: float, or double for a scalar decay with fp32
+// inputs, whose exponent differences Gam_i - Gam_j would otherwise lose up to
+// |Gam| * 2^-24 to the rounding of the running sums (a relative error of that size
+// in the decay factor, far above fp32's own on sums that cancel).
+template <int DK, int DECAY, int NT, typename GT>
+__device__ __forceinline__ void finish_gamma(GamRegs<DK, DECAY, NT>& R, const ChunkSeg& seg, GT* gam,
                                              float* fq, float* fk, int tid = threadIdx.x,
                                              float* gam_hi = nullptr, float* wl = nullptr) {
   if constexpr (DECAY == DECAY_SCALAR) {
     if (tid < CH) {
-      float x = R.v[0];
+      GT x = R.v[0];
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
+        const GT y = __shfl_up(x, off, 64);
         if (tid >= off) x += y;
       }
       gam[tid] = x;
-      const float last = __shfl(x, 63, 64);
-      fq[tid] = seg.live(tid) ? __expf(x) : 0.f;
-      fk[tid] = seg.tail(tid) ? __expf(last - x) * R.wt : 0.f;
+      const GT last = __shfl(x, 63, 64);
+      fq[tid] = seg.live(tid) ? __expf((float)x) : 0.f;
+      fk[tid] = seg.tail(tid) ? __expf((float)(last - x)) * R.wt : 0.f;
       if (wl) wl[tid] = R.wt;
     }
   } else {
@@ -293,13 +297,13 @@ struct TileRegs {
 // MODE 0: copy into `hi`; 1: x*exp(Gam[i][d]); 2: x*exp(-Gam[i][d]); 3: x*fac[i] --
 // scaled modes are stored split (hi, and lo for bf16). Gam rows as finish_gamma
 // wrote them (gam_hi: rows 32..63, null for one contiguous tile). No barrier.
-template <typename E, int D, int DP, int LD, int MODE, int DK, int NT>
-__device__ __forceinline__ void store_tile(const TileRegs<E, D, NT>& R, E* hi, E* lo, const float* gam,
+template <typename E, int D, int DP, int LD, int MODE, int DK, int NT, typename GT = float>
+__device__ __forceinline__ void store_tile(const TileRegs<E, D, NT>& R, E* hi, E* lo, const GT* gam,
                                            const float* fac, int tid = threadIdx.x,
-                                           const float* gam_hi = nullptr) {
+                                           const GT* gam_hi = nullptr) {
   using TR = TileRegs<E, D, NT>;
   constexpr int VEC = TR::VEC;
-  const float* const g1 = gam_hi ? gam_hi - 32 * DK : gam;
+  const GT* const g1 = gam_hi ? gam_hi - 32 * DK : gam;
 #pragma unroll
   for (int p = 0; p < TR::PER; ++p) {
     const int v = tid + p * NT;
@@ -318,11 +322,11 @@ __device__ __forceinline__ void store_tile(const TileRegs<E, D, NT>& R, E* hi, E
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = R.r[p][e];
     }
-    const float* const grow = (i < 32 ? gam : g1) + i * DK + c;
+    const GT* const grow = (i < 32 ? gam : g1) + i * DK + c;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      if constexpr (MODE == 1) x[e] *= __expf(grow[e]);
-      if constexpr (MODE == 2) x[e] *= __expf(-grow[e]);
+      if constexpr (MODE == 1) x[e] *= __expf((float)grow[e]);
+      if constexpr (MODE == 2) x[e] *= __expf(-(float)grow[e]);
       if constexpr (MODE == 3) x[e] *= fac[i];
     }
     if constexpr (sizeof(E) == 2) {

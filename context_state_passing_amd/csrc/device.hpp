@@ -307,7 +307,7 @@ struct ChunkSeg {
   }
 };
 
-__device__ __forceinline__ float wave_sum(float x) {
+template <typename T> __device__ __forceinline__ T wave_sum(T x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
   return x;

@@ -11,6 +11,8 @@
 //   output  o_i = sum_j A_ij v_j + live_i * S0^T (q_i * exp(Gam_i))          (APPLY)
 //   state   S  = diag(exp(Gam_last)) [no start] S0 + sum_{j tail} diag(exp(Gam_last - Gam_j)) k_j v_j^T
 // which is the chunk algebra of S_t = diag(a_t) S_{t-1} + k_t v_t^T, o_t = S_t^T q_t.
+#include <type_traits>
+
 #include "chunk_common.hpp"
 #include "kernels.hpp"
 
@@ -18,16 +20,16 @@ namespace cpla {
 
 // S <- diag(exp(Gam_last)) keep*S + K^T V with the tail/decay token factors.
 // K^ = K exp(Gam_last - Gam) tail enters the MFMA split into hi + lo parts.
-template <typename E, int DK, int DV, int DECAY, int NKT_, int CPWV_, typename V>
+template <typename E, int DK, int DV, int DECAY, int NKT_, int CPWV_, typename V, typename GT>
 __device__ __forceinline__ void state_update(V (&S)[NKT_][CPWV_], const E* Kt, const E* Ktl, const E* Vt,
-                                             const float* gam, const float* el, const float* fk,
+                                             const GT* gam, const float* el, const float* fk,
                                              const ChunkSeg& seg, int l) {
   using G = Geo<E, DK, DV>;
   const int w = wave_id(), g = l >> 4;
   __builtin_assume(w >= 0 && w < G::NW);
   const float keep = seg.any() ? 0.f : 1.f;
   if constexpr (DECAY == DECAY_SCALAR) {
-    const float sc = keep * __expf(gam[CH - 1]);
+    const float sc = keep * __expf((float)gam[CH - 1]);
 #pragma unroll
     for (int m = 0; m < G::NKT; ++m)
 #pragma unroll
@@ -109,11 +111,17 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   constexpr int NAL = (APPLY && Split<E>::on) ? 1 : 0;
   __shared__ __attribute__((aligned(16))) E s_a[NQT * G::TILE_A + 8];    // scores, hi part
   __shared__ __attribute__((aligned(16))) E s_al[NAL * G::TILE_A + 8];   // scores, lo part
-  __shared__ float s_gam[GAM], s_fq[CH], s_fk[CH], s_el[G::DKP];
+  // Gam: fp64 for a scalar decay with fp32 inputs (see finish_gamma)
+  using GT = typename std::conditional<sizeof(E) == 4 && DECAY == DECAY_SCALAR, double, float>::type;
+  __shared__ GT s_gam[GAM];
+  __shared__ float s_fq[CH], s_fk[CH], s_el[G::DKP];
   __shared__ float s_w[DECAY == DECAY_SCALAR ? CH : 1];   // per-token input weights
 
   float* const gam_hi = GSPLIT ? reinterpret_cast<float*>(s_v) : nullptr;
-  const float* const gam_last = GSPLIT ? gam_hi + (CH / 2 - 1) * DK : s_gam + (CH - 1) * DK;
+  const GT* const gam_last = [&]() -> const GT* {
+    if constexpr (GSPLIT) return gam_hi + (CH / 2 - 1) * DK;
+    else return s_gam + (CH - 1) * DK;
+  }();
 
   const int w = wave_id(), l = lane_id(), g = l >> 4, i16 = l & 15;
   __builtin_assume(w >= 0 && w < G::NW);
@@ -146,7 +154,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   const E* q = reinterpret_cast<const E*>(a.q);
   const E* k = reinterpret_cast<const E*>(a.k);
   const E* v = reinterpret_cast<const E*>(a.v);
-  float gsum = 0.f;          // total log-decay of the shard (diag: column tid; else thread 0)
+  GT gsum = 0;               // total log-decay of the shard (diag: column tid; else thread 0)
   bool any_start = false;
 
   // prefetch registers for the next chunk's inputs (apply); the prepare walk runs
@@ -235,7 +243,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
           float x = 0.f;
           if (seg.same(i, j)) {
             x = (float)acc[rr];
-            if constexpr (DECAY == DECAY_SCALAR) x *= __expf(s_gam[i] - s_gam[j]) * s_w[j];
+            if constexpr (DECAY == DECAY_SCALAR) x *= __expf((float)(s_gam[i] - s_gam[j])) * s_w[j];
           }
           store_split(s_a, s_al, i * G::LDA + j, x);
         }
@@ -314,10 +322,10 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
     float* rec = a.summary + (int64_t)(r * a.B * a.H + bh) * a.W;
     const float keep = any_start ? 0.f : 1.f;
     if constexpr (DECAY == DECAY_DIAG) {
-      if (threadIdx.x < DK) rec[threadIdx.x] = keep * __expf(gsum);
+      if (threadIdx.x < DK) rec[threadIdx.x] = keep * __expf((float)gsum);
     } else {
       if (threadIdx.x < 4) {
-        float mval = (DECAY == DECAY_SCALAR) ? __expf(gsum) : 1.f;
+        float mval = (DECAY == DECAY_SCALAR) ? __expf((float)gsum) : 1.f;
         rec[threadIdx.x] = threadIdx.x == 0 ? keep * mval : 0.f;
       }
     }

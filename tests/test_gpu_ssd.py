@@ -7,16 +7,13 @@ Cases span several chunks per shard and several shards, groups shared by 1, 2
 and 4 heads, state sizes 16, 64 and 128, an initial state, and packed
 sequences with boundaries inside chunks. Tolerances are those of the
 linear-attention parity tests (fp32 rtol 1e-4 / atol 1e-5, bf16 rtol 2e-2 /
-atol 2e-3), plus, for d_dt only, the accumulation error of its two terms:
-d_dt = dw + A dg is a difference of fp32 quantities, each formed from
-chunk-wide sums (suffix sums over the chunk's 64 tokens of products over the
-state size), which cancel to results thousands of times smaller than
-themselves on some tokens; the bound added is 64 * 2^-24 * s, with s the
-largest |dw| + |A dg| in the token's 64-token chunk (terms from the oracle).
+atol 2e-3) for every output, d_dt included: d_dt = dw + A dg is a difference of
+two terms that cancel to results thousands of times smaller than themselves on
+some tokens, which the fp32 inputs meet because their walks form every sum, and
+the scalar decay's running log-decay, in fp64.
 """
 import sys
 
-import numpy as np
 import pytest
 import torch
 
@@ -85,32 +82,7 @@ def test_ssd_parity(case, gpu_available):
     ref = _run_oracle(wl)
     rtol, atol = tolerances(wl.dtype)
     for name in ref:
-        if name == "d_dt":
-            continue
         assert_close(name, _np(got[name]), ref[name], rtol, atol)
-    scale = _ddt_term_scale(wl)
-    err = np.abs(_np(got["d_dt"]) - ref["d_dt"])
-    lim = atol + rtol * np.abs(ref["d_dt"]) + 64 * 2.0 ** -24 * scale
-    assert np.all(err <= lim), f"d_dt: {int((err > lim).sum())}/{err.size} outside; worst excess {(err - lim).max():.3e}"
-
-
-def _ddt_term_scale(wl):
-    """|dw| + |A dg| per (b, t, h) from the linear-attention oracle under the SSD map."""
-    seq = None
-    if wl.cu_seqlens is not None:
-        seq = omd.seq_idx_rows(wl.cu_seqlens, wl.T)
-    x, dt, A, Bm, Cm = (_np(t) for t in (wl.x, wl.dt, wl.A, wl.Bm, wl.Cm))
-    grp = np.arange(wl.H) // (wl.H // wl.G)
-    g = A[None, None, :] * dt
-    res = orec.backward(Cm[:, :, grp], Bm[:, :, grp], x, g, "scalar", dO=_np(wl.dy),
-                        initial_state=_np(wl.initial_state), seq_idx=seq, w=dt)
-    term = np.abs(res[5]) + np.abs(A[None, None, :] * res[3])             # [B, T, H]
-    B_, T_, H_ = term.shape
-    nc = (T_ + 63) // 64
-    pad = np.zeros((B_, nc * 64, H_))
-    pad[:, :T_] = term
-    cmax = pad.reshape(B_, nc, 64, H_).max(axis=2, keepdims=True)
-    return np.broadcast_to(cmax, (B_, nc, 64, H_)).reshape(B_, nc * 64, H_)[:, :T_]
 
 
 def test_ssd_deterministic(gpu_available):
@@ -191,8 +163,4 @@ def test_random_ssd_problems(case, gpu_available):
     got, ref = _run_gpu(wl), _run_oracle(wl)
     rtol, atol = tolerances(wl.dtype)
     for name in ref:
-        if name != "d_dt":
-            assert_close(name, _np(got[name]), ref[name], rtol, atol)
-    err = np.abs(_np(got["d_dt"]) - ref["d_dt"])
-    lim = atol + rtol * np.abs(ref["d_dt"]) + 64 * 2.0 ** -24 * _ddt_term_scale(wl)
-    assert np.all(err <= lim), f"d_dt: {int((err > lim).sum())}/{err.size} outside"
+        assert_close(name, _np(got[name]), ref[name], rtol, atol)
