@@ -23,7 +23,7 @@ EXPORTS = [
     "cpla_ssd_inputs", "cpla_ssd_input_grads", "cp_forward_prepare_weighted", "cp_forward_apply_weighted",
     "cp_backward_apply_weighted", "cpla_delta_workspace_bytes", "cp_forward_prepare_delta",
     "cp_forward_apply_delta", "cp_backward_prepare_delta", "cp_backward_apply_delta",
-    "cpla_set_apply_parts",
+    "cpla_set_apply_parts", "cp_forward_apply_noalloc", "cpla_noalloc_scratch_bytes",
 ]
 
 
@@ -101,6 +101,10 @@ def lib() -> ctypes.CDLL:
             getattr(L, fn).restype = ctypes.c_int
         L.cpla_last_error.restype = ctypes.c_char_p
         L.cpla_abi_version.restype = ctypes.c_int
+        L.cp_forward_apply_noalloc.argtypes = [P, PK, V, V, V, V, V, V, V, V, V, V]
+        L.cp_forward_apply_noalloc.restype = ctypes.c_int
+        L.cpla_noalloc_scratch_bytes.argtypes = []
+        L.cpla_noalloc_scratch_bytes.restype = ctypes.c_int64
         L.cpla_set_apply_parts.argtypes = [ctypes.c_int]
         L.cpla_set_apply_parts.restype = ctypes.c_int
         _lib = L

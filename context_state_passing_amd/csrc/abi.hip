@@ -386,6 +386,62 @@ extern "C" cpla_status cp_forward_apply(const cpla_problem* p, const cpla_packed
                        chunk_states, stream);
 }
 
+// ---- cp_forward_apply without allocation --------------------------------------------
+// The composed incoming states of every shard ([P, B, H, dk, dv] fp32: written by
+// the prefix scan, read by the shard walks of the same call) live in this
+// file-scope device array instead of a caller buffer: one copy per GPU, held
+// until the process ends. In host code the array's name is not a device address;
+// the address comes from hipGetSymbolAddress, taken once per device with that
+// device current and kept in noalloc_ptr below.
+constexpr int64_t NOALLOC_SCRATCH_BYTES = int64_t(32) << 20;
+static __device__ __align__(256) float scratch[NOALLOC_SCRATCH_BYTES / 4];
+
+namespace {
+// Device address of `scratch` on the current device (nullptr and an error set on failure).
+float* noalloc_ptr() {
+  static std::mutex mu;
+  static float* ptrs[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    fail(CPLA_E_HIP, "cp_forward_apply_noalloc: no current device (or device index >= 64)");
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(CPLA_E_HIP, "cp_forward_apply_noalloc: hipGetSymbolAddress of the scratch failed: %s",
+           hipGetErrorString(e));
+      return nullptr;
+    }
+    ptrs[dev] = static_cast<float*>(ptr);
+  }
+  return ptrs[dev];
+}
+}  // namespace
+
+extern "C" int64_t cpla_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+extern "C" cpla_status cp_forward_apply_noalloc(const cpla_problem* p, const cpla_packed* packed, const void* q,
+                                                const void* k, const void* v, const float* g,
+                                                const float* fwd_summary, const float* initial_state, void* o,
+                                                float* final_state, void* chunk_states, hipStream_t stream) {
+  clear_error();
+  cpla_status st;
+  if ((st = check_problem(p)) != CPLA_OK) return st;
+  const int64_t need = (int64_t)p->num_shards * p->B * p->H * p->dk * p->dv * (int64_t)sizeof(float);
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(CPLA_E_UNSUPPORTED,
+                "cp_forward_apply_noalloc: the composed states of %d shards x %lld rows need %lld bytes; "
+                "its scratch holds %lld (use cp_forward_apply)",
+                p->num_shards, (long long)(p->B * p->H), (long long)need, (long long)NOALLOC_SCRATCH_BYTES);
+  float* const ptr = noalloc_ptr();
+  if (!ptr) return CPLA_E_HIP;
+  return forward_apply(p, packed, q, k, v, g, nullptr, fwd_summary, initial_state, o, ptr, final_state,
+                       chunk_states, stream);
+}
+
 extern "C" cpla_status cp_forward_apply_weighted(const cpla_problem* p, const cpla_packed* packed, const void* q,
                                                  const void* k, const void* v, const float* g, const float* w,
                                                  const float* fwd_summary, const float* initial_state, void* o,

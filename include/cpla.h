@@ -143,6 +143,31 @@ cpla_status cp_forward_apply(const cpla_problem* p, const cpla_packed* packed,
                              void* o, float* shard_in_state, float* final_state,
                              void* chunk_states, hipStream_t stream);
 
+/* cp_forward_apply_noalloc: cp_forward_apply for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). It computes exactly what cp_forward_apply computes,
+ * with the same kernels (same bits in o, final_state and chunk_states), but the
+ * composed incoming state of every shard -- the shard_in_state buffer that
+ * cp_forward_apply takes from the caller -- lives in a scratch array inside the
+ * library: one per GPU, cpla_noalloc_scratch_bytes() (32 MiB) in size, allocated
+ * when the library's code is loaded on that GPU and held until the process ends.
+ * The call itself allocates and frees nothing. It rejects with
+ * CPLA_E_UNSUPPORTED (launching nothing) a problem whose composed states need
+ * more: P * B * H * dk * dv * 4 bytes (the diagonal-decay workload B=4 H=16
+ * d=128 with 8 shards needs exactly 32 MiB). Every call on one GPU shares that
+ * GPU's scratch: calls that may overlap on one GPU (several streams, several
+ * host threads) race and must be serialised by the caller; the composed states
+ * are not returned (use cp_forward_apply to keep them). Other arguments, errors
+ * and ordering on `stream` as for cp_forward_apply. */
+cpla_status cp_forward_apply_noalloc(const cpla_problem* p, const cpla_packed* packed,
+                                     const void* q, const void* k, const void* v, const float* g,
+                                     const float* fwd_summary, const float* initial_state,
+                                     void* o, float* final_state, void* chunk_states,
+                                     hipStream_t stream);
+
+/* Size in bytes of the per-GPU scratch of cp_forward_apply_noalloc. */
+int64_t cpla_noalloc_scratch_bytes(void);
+
 /* cp_backward_prepare: for every handled shard, the gradient w.r.t. its
  * incoming state when no gradient arrives at its end (gamma), and its
  * transition, into bwd_summary[r]. With packed sequences it covers the shard's

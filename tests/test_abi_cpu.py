@@ -47,6 +47,17 @@ def test_peaks_library_exports():
     assert P.cpla_peak_copy(FAKE, FAKE, 16, 1, 3, None) == -1
 
 
+def test_noalloc_refuses_oversize_before_launch():
+    assert L.cpla_noalloc_scratch_bytes() == 32 << 20
+    p = prob(B=4, T=8192, H=16, num_shards=9, rank_end=9, decay=_lib.DECAY_DIAG)
+    st = L.cp_forward_apply_noalloc(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None,
+                                    None)
+    assert st == 5 and b"scratch holds" in L.cpla_last_error()
+    # an invalid problem is refused as by cp_forward_apply
+    assert L.cp_forward_apply_noalloc(ctypes.byref(prob(B=0)), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                      None, None, None) == 2
+
+
 def test_apply_parts_knob():
     assert L.cpla_set_apply_parts(3) == -1
     assert L.cpla_set_apply_parts(2) == 0
