@@ -24,6 +24,7 @@ EXPORTS = [
     "cp_backward_apply_weighted", "cpla_delta_workspace_bytes", "cp_forward_prepare_delta",
     "cp_forward_apply_delta", "cp_backward_prepare_delta", "cp_backward_apply_delta",
     "cpla_set_apply_parts", "cp_forward_apply_noalloc", "cpla_noalloc_scratch_bytes",
+    "cpla_check_decay_range",
 ]
 
 
@@ -105,6 +106,8 @@ def lib() -> ctypes.CDLL:
         L.cp_forward_apply_noalloc.restype = ctypes.c_int
         L.cpla_noalloc_scratch_bytes.argtypes = []
         L.cpla_noalloc_scratch_bytes.restype = ctypes.c_int64
+        L.cpla_check_decay_range.argtypes = [P, V, V, V]
+        L.cpla_check_decay_range.restype = ctypes.c_int
         L.cpla_set_apply_parts.argtypes = [ctypes.c_int]
         L.cpla_set_apply_parts.restype = ctypes.c_int
         _lib = L

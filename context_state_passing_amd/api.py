@@ -196,6 +196,21 @@ def make_problem(q, v, num_shards: int, decay: int, chunk: int = 64, rank_range=
     return Problem(B, T, H, dk, dv, num_shards, chunk, rb, re, _DTYPE[q.dtype], decay)
 
 
+def check_decay_range(g: torch.Tensor, num_shards: int, dk: Optional[int] = None) -> None:
+    """Raise CplaError (INVALID) if a diagonal log-decay g [B,T,H,dk] leaves the range
+    the kernels support (a chunk's running sum per key dim below
+    CPLA_DIAG_GAMMA_MIN); synchronises the current stream. Scalar decays have no
+    such limit."""
+    if g is None or g.dim() != 4:
+        return
+    B, T, H, d = g.shape
+    _expect("g", g, (B, T, H, d), torch.float32)
+    _expect_gpu("g", dict(g=g))
+    p = Problem(B, T, H, d, d, num_shards, 64, 0, num_shards, _lib.BF16, _lib.DECAY_DIAG)
+    count = torch.empty(4, dtype=torch.int32, device=g.device)
+    check(_lib.lib().cpla_check_decay_range(ctypes.byref(p), _ptr(g), _ptr(count), _stream()))
+
+
 def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch.Tensor] = None, *,
             num_shards: int, initial_state: Optional[torch.Tensor] = None, cu_seqlens=None,
             packed: Optional[PackedMeta] = None, save_for_backward: bool = True, chunk: int = 64,

@@ -21,7 +21,7 @@ LIB = os.path.join(PKG, "libcpla.so")
 PEAKS_LIB = os.path.join(PKG, "libcpla_peaks.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["abi.hip", "fwd.hip", "bwd.hip", "scan.hip", "ssd.hip", "delta.hip", "metadata.cpp"]
+SOURCES = ["abi.hip", "fwd.hip", "bwd.hip", "scan.hip", "ssd.hip", "delta.hip", "decay_check.hip", "metadata.cpp"]
 PEAKS_SOURCES = ["peaks.hip"]
 
 HIP_FLAGS = [

@@ -423,6 +423,39 @@ float* noalloc_ptr() {
 
 extern "C" int64_t cpla_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
 
+extern "C" cpla_status cpla_check_decay_range(const cpla_problem* p, const float* g, int32_t* count,
+                                              hipStream_t stream) {
+  clear_error();
+  cpla_status st;
+  if ((st = check_problem(p)) != CPLA_OK) return st;
+  if (p->decay != CPLA_DECAY_DIAG) return CPLA_OK;   // scalar decays are applied without a factorisation
+  if ((st = check_ptr(g, "g", true)) != CPLA_OK) return st;
+  if ((st = check_ptr(count, "count", true)) != CPLA_OK) return st;
+  const int64_t cps = chunks_of(shard_size(p->T, p->num_shards));
+  DecayCheckArgs a = {};
+  a.B = p->B; a.T = p->T; a.H = p->H; a.dk = p->dk;
+  a.nchunks = (int64_t)(p->rank_end - p->rank_begin) * cps;
+  a.n = a.B * a.H * a.nchunks * a.dk;
+  a.P = p->num_shards; a.rank_begin = p->rank_begin;
+  a.limit = CPLA_DIAG_GAMMA_MIN;
+  a.g = g;
+  a.count = count;
+  hipLaunchKernelGGL(decay_check_zero, dim3(1), dim3(1), 0, stream, count);
+  if ((st = launched("decay_check_zero")) != CPLA_OK) return st;
+  hipLaunchKernelGGL(decay_range, dim3((unsigned)((a.n + 255) / 256)), dim3(256), 0, stream, a);
+  if ((st = launched("decay_range")) != CPLA_OK) return st;
+  int32_t host = 0;
+  hipError_t e = hipMemcpyAsync(&host, count, sizeof(host), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(CPLA_E_HIP, "cpla_check_decay_range: %s", hipGetErrorString(e));
+  if (host > 0)
+    return fail(CPLA_E_INVALID,
+                "diagonal decay out of range: in %d (chunk, key dim) pairs the running log-decay of a 64-token "
+                "chunk falls below %.0f, where the factorised decay exp(+-sum) leaves fp32",
+                host, (double)CPLA_DIAG_GAMMA_MIN);
+  return CPLA_OK;
+}
+
 extern "C" cpla_status cp_forward_apply_noalloc(const cpla_problem* p, const cpla_packed* packed, const void* q,
                                                 const void* k, const void* v, const float* g,
                                                 const float* fwd_summary, const float* initial_state, void* o,

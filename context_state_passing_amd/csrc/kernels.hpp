@@ -117,4 +117,15 @@ template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAI
 __global__ void bwd_walk(BwdArgs a);
 __global__ void affine_scan(ScanArgs a);
 
+// Range check of a diagonal log-decay (cpla_check_decay_range).
+struct DecayCheckArgs {
+  int64_t B, T, H, dk, nchunks, n;   // nchunks: chunks of the handled shards; n = B*H*nchunks*dk
+  int P, rank_begin;
+  float limit;
+  const float* g;
+  int32_t* count;
+};
+__global__ void decay_check_zero(int32_t* count);
+__global__ void decay_range(DecayCheckArgs a);
+
 }  // namespace cpla

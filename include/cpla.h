@@ -33,9 +33,12 @@
  *       g, dg     scalar decay [B, T, H] fp32; diagonal decay [B, T, H, dk]
  *                 fp32; no decay: NULL. g <= 0 (log of a decay in (0, 1]).
  *                 Diagonal decay: within every 64-token chunk the running
- *                 sum of g per key dim must stay above about -80 (the kernels
- *                 factor the decay into exp(+-sum) that must stay finite in
- *                 fp32); stronger decays are outside the supported range.
+ *                 sum of g per key dim must stay at or above
+ *                 CPLA_DIAG_GAMMA_MIN = -80 (the kernels factor the decay into
+ *                 exp(+-sum), which must stay finite in fp32), i.e. an average
+ *                 of -1.25 per token over a whole chunk; stronger decays are
+ *                 outside the supported range, and cpla_check_decay_range
+ *                 reports them (the calls themselves do not read g on the host).
  *       states    [B, H, dk, dv] fp32 (S_init, final state and their grads)
  *       summaries [P, B, H, W] fp32, W = cpla_summary_width(): the first
  *                 m_slot entries hold the transition M (dk values for a
@@ -69,6 +72,10 @@ extern "C" {
 typedef struct ihipStream_t* hipStream_t;
 
 #define CPLA_ABI_VERSION 5
+
+/* Lower bound of the running log-decay within a 64-token chunk, per key dim, that
+ * the diagonal-decay kernels support (see the layout notes above). */
+#define CPLA_DIAG_GAMMA_MIN (-80.0f)
 
 typedef enum {
   CPLA_OK = 0,
@@ -164,6 +171,19 @@ cpla_status cp_forward_apply_noalloc(const cpla_problem* p, const cpla_packed* p
                                      const float* fwd_summary, const float* initial_state,
                                      void* o, float* final_state, void* chunk_states,
                                      hipStream_t stream);
+
+/* cpla_check_decay_range: opt-in validation of a diagonal log-decay g against
+ * the supported range (the layout notes above): counts, over the chunks of the
+ * handled shards [rank_begin, rank_end), the (chunk, key dim) pairs whose running
+ * sum of g from the chunk's first token falls below CPLA_DIAG_GAMMA_MIN (or is
+ * NaN), and returns CPLA_E_INVALID with that count in cpla_last_error() if any
+ * does. `count` is a caller-owned device int32 (16-byte aligned) the call
+ * overwrites. Unlike the other calls it synchronises `stream` (it reads the count
+ * back), so it is meant for debugging and input validation, not for the hot
+ * path. For no decay or a scalar decay (applied without a factorisation) it
+ * returns CPLA_OK without launching anything. */
+cpla_status cpla_check_decay_range(const cpla_problem* p, const float* g, int32_t* count,
+                                   hipStream_t stream);
 
 /* Size in bytes of the per-GPU scratch of cp_forward_apply_noalloc. */
 int64_t cpla_noalloc_scratch_bytes(void);

@@ -58,6 +58,18 @@ def test_noalloc_refuses_oversize_before_launch():
                                       None, None, None) == 2
 
 
+def test_decay_range_check_host_paths():
+    # nothing to check without a factorised decay: OK without launching
+    assert L.cpla_check_decay_range(ctypes.byref(prob()), FAKE, FAKE, None) == 0
+    assert L.cpla_check_decay_range(ctypes.byref(prob(decay=_lib.DECAY_NONE)), None, None, None) == 0
+    # a diagonal decay needs g and a device count (checked before any launch)
+    p = prob(decay=_lib.DECAY_DIAG)
+    assert L.cpla_check_decay_range(ctypes.byref(p), None, FAKE, None) == 1
+    assert L.cpla_check_decay_range(ctypes.byref(p), FAKE, None, None) == 1
+    assert L.cpla_check_decay_range(ctypes.byref(p), MISALIGNED, FAKE, None) == 4
+    assert L.cpla_check_decay_range(ctypes.byref(prob(B=0, decay=_lib.DECAY_DIAG)), FAKE, FAKE, None) == 2
+
+
 def test_apply_parts_knob():
     assert L.cpla_set_apply_parts(3) == -1
     assert L.cpla_set_apply_parts(2) == 0
