@@ -38,9 +38,15 @@ def _hipcc():
     return exe
 
 
+# The peak probes' MFMA loops keep their accumulators in VGPRs: left to itself the
+# compiler places them in AGPRs and copies them back and forth every iteration.
+EXTRA_FLAGS = {"peaks.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src):
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *HIP_FLAGS, "-I", INCLUDE, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-I", INCLUDE, "-I", CSRC, "-c",
+           os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd = [_hipcc(), "-O2", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC, "-c",
                os.path.join(CSRC, src), "-o", obj]

@@ -46,41 +46,51 @@ __global__ __launch_bounds__(MFMA_THREADS) void peak_mfma(float* __restrict__ ou
   const float x = 1.0f + 1e-3f * (float)(threadIdx.x & 63);
   float sum = 0.f;
   if constexpr (KIND == 0) {
-    bf16x8 a, b;
-    for (int e = 0; e < 8; ++e) { a[e] = (__bf16)(x * (e + 1)); b[e] = (__bf16)(1e-4f * (e + 1)); }
+    // a different second operand per chain: with one shared operand the compiler
+    // rotates the accumulators through other registers every iteration
+    bf16x8 a, b[CHAINS];
+    for (int e = 0; e < 8; ++e) a[e] = (__bf16)(x * (e + 1));
+    for (int c = 0; c < CHAINS; ++c)
+      for (int e = 0; e < 8; ++e) b[c][e] = (__bf16)(1e-4f * (e + 1 + c));
     f32x4 acc[CHAINS];
     for (int c = 0; c < CHAINS; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int it = 0; it < iters; ++it)
 #pragma unroll
-      for (int c = 0; c < CHAINS; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[c], 0, 0, 0);
+      for (int c = 0; c < CHAINS; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[c], acc[c], 0, 0, 0);
     for (int c = 0; c < CHAINS; ++c) sum += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
   } else if constexpr (KIND == 1) {
-    const float a = x, b = 1e-4f * x;
+    const float a = x;
+    float b[CHAINS];
+    for (int c = 0; c < CHAINS; ++c) b[c] = 1e-4f * x * (c + 1);
     f32x4 acc[CHAINS];
     for (int c = 0; c < CHAINS; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int it = 0; it < iters; ++it)
 #pragma unroll
-      for (int c = 0; c < CHAINS; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[c], 0, 0, 0);
+      for (int c = 0; c < CHAINS; ++c) acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b[c], acc[c], 0, 0, 0);
     for (int c = 0; c < CHAINS; ++c) sum += acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3];
   } else if constexpr (KIND == 3) {
     typedef float f32x16 __attribute__((ext_vector_type(16)));
-    bf16x8 a, b;
-    for (int e = 0; e < 8; ++e) { a[e] = (__bf16)(x * (e + 1)); b[e] = (__bf16)(1e-4f * (e + 1)); }
+    bf16x8 a, b[CHAINS / 2];
+    for (int e = 0; e < 8; ++e) a[e] = (__bf16)(x * (e + 1));
+    for (int c = 0; c < CHAINS / 2; ++c)
+      for (int e = 0; e < 8; ++e) b[c][e] = (__bf16)(1e-4f * (e + 1 + c));
     f32x16 acc[CHAINS / 2];
     for (int c = 0; c < CHAINS / 2; ++c)
       for (int e = 0; e < 16; ++e) acc[c][e] = 0.f;
     for (int it = 0; it < iters; ++it)
 #pragma unroll
-      for (int c = 0; c < CHAINS / 2; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+      for (int c = 0; c < CHAINS / 2; ++c) acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[c], acc[c], 0, 0, 0);
     for (int c = 0; c < CHAINS / 2; ++c)
       for (int e = 0; e < 16; ++e) sum += acc[c][e];
   } else {
-    const double a = x, b = 1e-4 * x;
+    const double a = x;
+    double b[CHAINS];
+    for (int c = 0; c < CHAINS; ++c) b[c] = 1e-4 * x * (c + 1);
     f64x4 acc[CHAINS];
     for (int c = 0; c < CHAINS; ++c) acc[c] = f64x4{0.0, 0.0, 0.0, 0.0};
     for (int it = 0; it < iters; ++it)
 #pragma unroll
-      for (int c = 0; c < CHAINS; ++c) acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[c], 0, 0, 0);
+      for (int c = 0; c < CHAINS; ++c) acc[c] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b[c], acc[c], 0, 0, 0);
     for (int c = 0; c < CHAINS; ++c) sum += (float)(acc[c][0] + acc[c][1] + acc[c][2] + acc[c][3]);
   }
   out[(int64_t)blockIdx.x * MFMA_THREADS + threadIdx.x] = sum;
