@@ -101,20 +101,24 @@ bool needs_tail(const cpla_problem* p) {
   return false;
 }
 
+// unpacked: the apply walk specialised for a stream without packed sequences
 template <typename E, int KK, int VV, int DEC, bool APPLY, bool TAIL>
-fwd_fn fwd_kernel(bool split) {
-  if constexpr (APPLY)
+fwd_fn fwd_kernel(bool split, bool unpacked) {
+  if constexpr (APPLY) {
+    if (unpacked) return split ? fwd_walk<E, KK, VV, DEC, true, TAIL, true, false>
+                               : fwd_walk<E, KK, VV, DEC, true, TAIL, false, false>;
     if (split) return fwd_walk<E, KK, VV, DEC, true, TAIL, true>;
+  }
   return fwd_walk<E, KK, VV, DEC, APPLY, TAIL>;
 }
 
 template <bool APPLY, bool TAIL>
-fwd_fn pick_fwd_t(int dtype, int DK, int DV, int decay, bool split) {
-#define CPLA_FWD_CASE(E, KK, VV)                                          \
-  if (DK == KK && DV == VV) {                                             \
-    if (decay == 0) return fwd_kernel<E, KK, VV, 0, APPLY, TAIL>(split);  \
-    if (decay == 1) return fwd_kernel<E, KK, VV, 1, APPLY, TAIL>(split);  \
-    return fwd_kernel<E, KK, VV, 2, APPLY, TAIL>(split);                  \
+fwd_fn pick_fwd_t(int dtype, int DK, int DV, int decay, bool split, bool unpacked) {
+#define CPLA_FWD_CASE(E, KK, VV)                                                    \
+  if (DK == KK && DV == VV) {                                                       \
+    if (decay == 0) return fwd_kernel<E, KK, VV, 0, APPLY, TAIL>(split, unpacked);  \
+    if (decay == 1) return fwd_kernel<E, KK, VV, 1, APPLY, TAIL>(split, unpacked);  \
+    return fwd_kernel<E, KK, VV, 2, APPLY, TAIL>(split, unpacked);                  \
   }
   if (dtype == CPLA_BF16) {
     CPLA_FWD_CASE(bf16_t, 16, 16)
@@ -132,29 +136,32 @@ fwd_fn pick_fwd_t(int dtype, int DK, int DV, int decay, bool split) {
 
 // the divided (SPLIT) variants exist for the apply walk without decay or with a scalar decay
 template <typename E, int KK, int VV, int DEC, bool APPLY, bool GF, bool TAIL>
-bwd_fn bwd_kernel(bool split) {
+bwd_fn bwd_kernel(bool split, bool unpacked) {
   if constexpr (APPLY && DEC != CPLA_DECAY_DIAG)
-    if (split) return bwd_walk<E, KK, VV, DEC, true, GF, TAIL, true>;
+    if (split) return unpacked ? bwd_walk<E, KK, VV, DEC, true, GF, TAIL, true, false>
+                               : bwd_walk<E, KK, VV, DEC, true, GF, TAIL, true>;
+  if constexpr (APPLY)
+    if (unpacked) return bwd_walk<E, KK, VV, DEC, true, GF, TAIL, false, false>;
   return bwd_walk<E, KK, VV, DEC, APPLY, GF, TAIL>;
 }
 
 template <bool APPLY, bool TAIL>
-bwd_fn pick_bwd_t(int dtype, int DK, int DV, int decay, bool grad_f32, bool split) {
+bwd_fn pick_bwd_t(int dtype, int DK, int DV, int decay, bool grad_f32, bool split, bool unpacked) {
   if (grad_f32) {   // fp32 gradients from bf16 inputs: scalar decay only
     if constexpr (!APPLY) return nullptr;
     if (dtype != CPLA_BF16 || decay != CPLA_DECAY_SCALAR) return nullptr;
-    if (DK == 16 && DV == 16) return bwd_kernel<bf16_t, 16, 16, 1, true, true, TAIL>(split);
-    if (DK == 64 && DV == 64) return bwd_kernel<bf16_t, 64, 64, 1, true, true, TAIL>(split);
-    if (DK == 128 && DV == 128) return bwd_kernel<bf16_t, 128, 128, 1, true, true, TAIL>(split);
-    if (DK == 64 && DV == 128) return bwd_kernel<bf16_t, 64, 128, 1, true, true, TAIL>(split);
-    if (DK == 128 && DV == 64) return bwd_kernel<bf16_t, 128, 64, 1, true, true, TAIL>(split);
+    if (DK == 16 && DV == 16) return bwd_kernel<bf16_t, 16, 16, 1, true, true, TAIL>(split, unpacked);
+    if (DK == 64 && DV == 64) return bwd_kernel<bf16_t, 64, 64, 1, true, true, TAIL>(split, unpacked);
+    if (DK == 128 && DV == 128) return bwd_kernel<bf16_t, 128, 128, 1, true, true, TAIL>(split, unpacked);
+    if (DK == 64 && DV == 128) return bwd_kernel<bf16_t, 64, 128, 1, true, true, TAIL>(split, unpacked);
+    if (DK == 128 && DV == 64) return bwd_kernel<bf16_t, 128, 64, 1, true, true, TAIL>(split, unpacked);
     return nullptr;
   }
-#define CPLA_BWD_CASE(E, KK, VV)                                               \
-  if (DK == KK && DV == VV) {                                                  \
-    if (decay == 0) return bwd_kernel<E, KK, VV, 0, APPLY, false, TAIL>(split); \
-    if (decay == 1) return bwd_kernel<E, KK, VV, 1, APPLY, false, TAIL>(split); \
-    return bwd_kernel<E, KK, VV, 2, APPLY, false, TAIL>(false);                \
+#define CPLA_BWD_CASE(E, KK, VV)                                                         \
+  if (DK == KK && DV == VV) {                                                            \
+    if (decay == 0) return bwd_kernel<E, KK, VV, 0, APPLY, false, TAIL>(split, unpacked); \
+    if (decay == 1) return bwd_kernel<E, KK, VV, 1, APPLY, false, TAIL>(split, unpacked); \
+    return bwd_kernel<E, KK, VV, 2, APPLY, false, TAIL>(false, unpacked);                \
   }
   if (dtype == CPLA_BF16) {
     CPLA_BWD_CASE(bf16_t, 16, 16)
@@ -172,9 +179,9 @@ bwd_fn pick_bwd_t(int dtype, int DK, int DV, int decay, bool grad_f32, bool spli
 
 // the kernel for a problem: the TAIL variant only when some shard ends inside a chunk
 template <bool APPLY>
-fwd_fn pick_fwd(const cpla_problem* p, bool split = false) {
-  return needs_tail(p) ? pick_fwd_t<APPLY, true>(p->dtype, (int)p->dk, (int)p->dv, p->decay, split)
-                       : pick_fwd_t<APPLY, false>(p->dtype, (int)p->dk, (int)p->dv, p->decay, split);
+fwd_fn pick_fwd(const cpla_problem* p, bool split = false, bool unpacked = false) {
+  return needs_tail(p) ? pick_fwd_t<APPLY, true>(p->dtype, (int)p->dk, (int)p->dv, p->decay, split, unpacked)
+                       : pick_fwd_t<APPLY, false>(p->dtype, (int)p->dk, (int)p->dv, p->decay, split, unpacked);
 }
 
 // Compute units of the current device (queried once per device; 0 if unknown).
@@ -235,9 +242,10 @@ unsigned apply_parts(const cpla_problem* p, const void* kernel) {
   return z;
 }
 template <bool APPLY>
-bwd_fn pick_bwd(const cpla_problem* p, bool grad_f32 = false, bool split = false) {
-  return needs_tail(p) ? pick_bwd_t<APPLY, true>(p->dtype, (int)p->dk, (int)p->dv, p->decay, grad_f32, split)
-                       : pick_bwd_t<APPLY, false>(p->dtype, (int)p->dk, (int)p->dv, p->decay, grad_f32, split);
+bwd_fn pick_bwd(const cpla_problem* p, bool grad_f32 = false, bool split = false, bool unpacked = false) {
+  return needs_tail(p)
+             ? pick_bwd_t<APPLY, true>(p->dtype, (int)p->dk, (int)p->dv, p->decay, grad_f32, split, unpacked)
+             : pick_bwd_t<APPLY, false>(p->dtype, (int)p->dk, (int)p->dv, p->decay, grad_f32, split, unpacked);
 }
 
 unsigned threads_for(const cpla_problem* p) {
@@ -370,8 +378,9 @@ static cpla_status forward_apply(const cpla_problem* p, const cpla_packed* packe
   a.state_in = shard_in_state;
   a.out = o;
   a.chunk_states = reinterpret_cast<float*>(chunk_states);
-  const unsigned parts = apply_parts(p, reinterpret_cast<const void*>(pick_fwd<true>(p, true)));
-  fwd_fn fn = pick_fwd<true>(p, parts > 1);
+  const bool unpacked = packed == nullptr;
+  const unsigned parts = apply_parts(p, reinterpret_cast<const void*>(pick_fwd<true>(p, true, unpacked)));
+  fwd_fn fn = pick_fwd<true>(p, parts > 1, unpacked);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no forward kernel for this configuration");
   hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H), parts), dim3(threads_for(p)), 0,
                      stream, a);
@@ -549,8 +558,10 @@ static cpla_status backward_apply(const cpla_problem* p, const cpla_packed* pack
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dw = dw;
   // divided walks for small grids (no decay or a scalar decay)
   const unsigned parts =
-      p->decay == CPLA_DECAY_DIAG ? 1u : apply_parts(p, reinterpret_cast<const void*>(pick_bwd<true>(p, grad_f32, true)));
-  bwd_fn fn = pick_bwd<true>(p, grad_f32, parts > 1);
+      p->decay == CPLA_DECAY_DIAG ? 1u
+                                  : apply_parts(p, reinterpret_cast<const void*>(
+                                                       pick_bwd<true>(p, grad_f32, true, packed == nullptr)));
+  bwd_fn fn = pick_bwd<true>(p, grad_f32, parts > 1, packed == nullptr);
   if (!fn) return fail(CPLA_E_UNSUPPORTED, "no backward kernel for this configuration");
   hipLaunchKernelGGL(fn, dim3(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H), parts), dim3(threads_for(p)), 0,
                      stream, a);

@@ -71,7 +71,7 @@ __device__ __forceinline__ f32x4 lane_gamma(f32x4 x, f32x4& carry) {
   return out;
 }
 
-template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAIL, bool SPLIT>
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAIL, bool SPLIT, bool PK>
 __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 ? 2 : 4))) void bwd_walk(BwdArgs a) {
   static_assert(!SPLIT || (APPLY && DECAY != DECAY_DIAG), "divided walks: apply, no or scalar decay");
   using G = Geo<E, DK, DV>;
@@ -148,7 +148,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   const int r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   // packed sequences: row b's sequence ids (one packing per batch row)
-  const int32_t* const seq_row = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
+  const int32_t* const seq_row = (PK && a.seq_idx) ? a.seq_idx + b * a.T : nullptr;
   // the shard's tokens [tshard, tshard + slen): torch.chunk's division of T into P
   const int64_t tshard = shard_begin(a.T, a.P, r), slen = shard_len(a.T, a.P, r);
   const int nc = (int)chunks_of(slen);
@@ -852,10 +852,14 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   template __global__ void bwd_walk<E, DK, DV, DEC, false, false, false>(BwdArgs); \
   template __global__ void bwd_walk<E, DK, DV, DEC, true, false, false>(BwdArgs);  \
   template __global__ void bwd_walk<E, DK, DV, DEC, false, false, true>(BwdArgs);  \
-  template __global__ void bwd_walk<E, DK, DV, DEC, true, false, true>(BwdArgs);
+  template __global__ void bwd_walk<E, DK, DV, DEC, true, false, true>(BwdArgs);   \
+  template __global__ void bwd_walk<E, DK, DV, DEC, true, false, false, false, false>(BwdArgs); \
+  template __global__ void bwd_walk<E, DK, DV, DEC, true, false, true, false, false>(BwdArgs);
 #define CPLA_INST_BWD_SPLIT(E, DK, DV, DEC, GF)                                           \
   template __global__ void bwd_walk<E, DK, DV, DEC, true, GF, false, true>(BwdArgs);     \
-  template __global__ void bwd_walk<E, DK, DV, DEC, true, GF, true, true>(BwdArgs);
+  template __global__ void bwd_walk<E, DK, DV, DEC, true, GF, true, true>(BwdArgs);      \
+  template __global__ void bwd_walk<E, DK, DV, DEC, true, GF, false, true, false>(BwdArgs); \
+  template __global__ void bwd_walk<E, DK, DV, DEC, true, GF, true, true, false>(BwdArgs);
 #define CPLA_INST_BWD3(E, D) CPLA_INST_BWD(E, D, D, 0) CPLA_INST_BWD(E, D, D, 1) CPLA_INST_BWD(E, D, D, 2) \
   CPLA_INST_BWD_SPLIT(E, D, D, 0, false) CPLA_INST_BWD_SPLIT(E, D, D, 1, false)
 #define CPLA_INST_BWD3X(E, DK, DV) CPLA_INST_BWD(E, DK, DV, 0) CPLA_INST_BWD(E, DK, DV, 1) CPLA_INST_BWD(E, DK, DV, 2) \
@@ -869,6 +873,8 @@ CPLA_INST_BWD3X(bf16_t, 128, 64)
 #define CPLA_INST_BWD_GF32(DK, DV)                                                   \
   template __global__ void bwd_walk<bf16_t, DK, DV, 1, true, true, false>(BwdArgs); \
   template __global__ void bwd_walk<bf16_t, DK, DV, 1, true, true, true>(BwdArgs);  \
+  template __global__ void bwd_walk<bf16_t, DK, DV, 1, true, true, false, false, false>(BwdArgs); \
+  template __global__ void bwd_walk<bf16_t, DK, DV, 1, true, true, true, false, false>(BwdArgs); \
   CPLA_INST_BWD_SPLIT(bf16_t, DK, DV, 1, true)
 CPLA_INST_BWD_GF32(16, 16)
 CPLA_INST_BWD_GF32(64, 64)

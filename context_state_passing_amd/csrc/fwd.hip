@@ -92,7 +92,7 @@ __device__ __forceinline__ void state_update(V (&S)[NKT_][CPWV_], const E* Kt, c
   }
 }
 
-template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL, bool SPLIT>
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL, bool SPLIT, bool PK>
 __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 ? 2 : 4))) void fwd_walk(FwdArgs a) {
   static_assert(APPLY || !SPLIT, "only the apply walk divides a shard");
   using G = Geo<E, DK, DV>;
@@ -128,7 +128,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   const int r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
   // packed sequences: row b's sequence ids (one packing per batch row)
-  const int32_t* const seq_row = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
+  const int32_t* const seq_row = (PK && a.seq_idx) ? a.seq_idx + b * a.T : nullptr;
   // the shard's tokens [tshard, tshard + slen): torch.chunk's division of T into P
   const int64_t tshard = shard_begin(a.T, a.P, r), slen = shard_len(a.T, a.P, r);
   const int nc = (int)chunks_of(slen);
@@ -350,7 +350,11 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   template __global__ void fwd_walk<E, DK, DV, DEC, false, true>(FwdArgs);        \
   template __global__ void fwd_walk<E, DK, DV, DEC, true, true>(FwdArgs);         \
   template __global__ void fwd_walk<E, DK, DV, DEC, true, false, true>(FwdArgs);  \
-  template __global__ void fwd_walk<E, DK, DV, DEC, true, true, true>(FwdArgs);
+  template __global__ void fwd_walk<E, DK, DV, DEC, true, true, true>(FwdArgs);   \
+  template __global__ void fwd_walk<E, DK, DV, DEC, true, false, false, false>(FwdArgs); \
+  template __global__ void fwd_walk<E, DK, DV, DEC, true, true, false, false>(FwdArgs);  \
+  template __global__ void fwd_walk<E, DK, DV, DEC, true, false, true, false>(FwdArgs);  \
+  template __global__ void fwd_walk<E, DK, DV, DEC, true, true, true, false>(FwdArgs);
 #define CPLA_INST_FWD3(E, D) CPLA_INST_FWD(E, D, D, 0) CPLA_INST_FWD(E, D, D, 1) CPLA_INST_FWD(E, D, D, 2)
 #define CPLA_INST_FWD3X(E, DK, DV) CPLA_INST_FWD(E, DK, DV, 0) CPLA_INST_FWD(E, DK, DV, 1) CPLA_INST_FWD(E, DK, DV, 2)
 CPLA_INST_FWD3(bf16_t, 16)

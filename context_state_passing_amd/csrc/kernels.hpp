@@ -108,12 +108,14 @@ template <typename E, int D> __global__ void delta_grad(DeltaArgs a);
 // SPLIT (apply only): the shard's chunks are divided among gridDim.z workgroups;
 // workgroup z emits chunks [z nc / Z, (z + 1) nc / Z) after replaying the ones
 // before them from the shard's incoming state (staging and state update only).
-template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL, bool SPLIT = false>
+// PK: the stream may be packed (a.seq_idx honoured); the apply walks of unpacked
+// problems take PK = false, where every sequence mask folds away at compile time.
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool TAIL, bool SPLIT = false, bool PK = true>
 __global__ void fwd_walk(FwdArgs a);
 // SPLIT (apply, no decay or scalar decay): as for fwd_walk, walking backwards:
 // workgroup z emits chunks [z nc / Z, (z + 1) nc / Z) after replaying the later
 // ones from the shard's outgoing gradient (staging and the adjoint update only).
-template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAIL, bool SPLIT = false>
+template <typename E, int DK, int DV, int DECAY, bool APPLY, bool GF32, bool TAIL, bool SPLIT = false, bool PK = true>
 __global__ void bwd_walk(BwdArgs a);
 __global__ void affine_scan(ScanArgs a);
 
