@@ -137,12 +137,25 @@ struct GamRegs {
   static constexpr int DMA_FLOATS = (DECAY == DECAY_DIAG) ? NT / 64 * (TOK + 1) * 64 : CH;
   __device__ __forceinline__ static constexpr int lds_shift(int s) { return (s & 3) + 16 * ((s >> 2) & 3); }
   __device__ __forceinline__ static int lds_row(int w, int s) { return w * (TOK + 1) * 64 + s * 64 + lds_shift(s); }
+  // Diagonal with 16-token parts of 16 columns (d_k 64 or 128): the wave's 64
+  // tokens x 16 columns are copied by four 16-byte DMA instructions instead, one
+  // per 16-token block I, which lands as 16 rows of 16 floats at blk(w, I); the
+  // blocks are 272 floats apart, so the four parts' reads of one row fall in
+  // different banks. It takes the same (TOK + 1) * 64 floats per wave.
+  static constexpr bool DMA16 = DECAY == DECAY_DIAG && TOK == 16 && CPW == 16;
+  __device__ __forceinline__ static int blk(int w, int I) { return (4 * w + I) * 272; }
   // TAIL: with n < CH (a shard's partial last chunk) lanes past the shard copy
   // nothing and load_lds returns 0 for them
   template <bool TAIL = false>
   __device__ __forceinline__ static void dma(const float* __restrict__ g, int64_t b, int64_t h, int64_t t0,
                                              int64_t T, int64_t H, float* buf, int tid, int w, int n = CH) {
-    if constexpr (DECAY == DECAY_DIAG) {
+    if constexpr (DMA16) {
+      const int l = tid & 63, r = l >> 2;
+      const float* src = g + ((b * T + t0 + r) * H + h) * DK + 16 * w + 4 * (l & 3);
+#pragma unroll
+      for (int I = 0; I < 4; ++I)
+        if (!TAIL || 16 * I + r < n) lds_dma<16>(src + (int64_t)(16 * I) * H * DK, buf + blk(w, I));
+    } else if constexpr (DECAY == DECAY_DIAG) {
       const int i0 = part(tid) * TOK;
       const float* src = g + ((b * T + t0 + i0) * H + h) * DK + column(tid);
 #pragma unroll
@@ -156,8 +169,13 @@ struct GamRegs {
   __device__ __forceinline__ void load_lds(const float* buf, int tid, int n = CH) {
     if constexpr (DECAY == DECAY_DIAG) {
       const int w = tid >> 6, l = tid & 63, i0 = part(tid) * TOK;
+      if constexpr (DMA16) {
 #pragma unroll
-      for (int s = 0; s < TOK; ++s) v[s] = buf[lds_row(w, s) + l];
+        for (int s = 0; s < TOK; ++s) v[s] = buf[blk(w, l >> 4) + 16 * s + (l & 15)];
+      } else {
+#pragma unroll
+        for (int s = 0; s < TOK; ++s) v[s] = buf[lds_row(w, s) + l];
+      }
       if constexpr (TAIL) {
 #pragma unroll
         for (int s = 0; s < TOK; ++s) v[s] = i0 + s < n ? v[s] : 0.f;
@@ -171,9 +189,8 @@ struct GamRegs {
   // accumulator layout of wave w's key tile, from the DMA buffer.
   template <bool TAIL = false>
   __device__ __forceinline__ static f32x4 lane_block(const float* buf, int w, int I, int l, int n = CH) {
-    static_assert(DECAY == DECAY_DIAG && TOK == 16 && CPW == 16, "lane layout needs 16-token parts of 16 columns");
-    const float* p = buf + lds_row(w, l & 15) + 16 * I + 4 * (l >> 4);
-    const f32x4 x = {p[0], p[1], p[2], p[3]};
+    static_assert(DMA16, "lane layout needs 16-token parts of 16 columns");
+    const f32x4 x = *reinterpret_cast<const f32x4*>(buf + blk(w, I) + 16 * (l & 15) + 4 * (l >> 4));
     if constexpr (!TAIL) return x;
     return 16 * I + (l & 15) >= n ? f32x4{0.f, 0.f, 0.f, 0.f} : x;
   }
