@@ -108,6 +108,12 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   // each chunk at its start instead.
   constexpr bool PF = APPLY && DIAG && SP && G::TILE_K >= CH * DV;
   static_assert(!PF || GamRegs<DK, DECAY, G::NT>::DMA_FLOATS * 4 <= REG_BYTES, "raw g must fit");
+  // Apply phases issue the products of GB token blocks term by term (every hi
+  // part, then every lo part), so that consecutive MFMAs accumulate into
+  // different tiles instead of each waiting on the one before it; d_k != d_v
+  // walks have no registers to spare for the extra fragments and take one block
+  // at a time.
+  constexpr int GB = G::DKP == G::DVP ? 4 : 1;
 
   __shared__ __attribute__((aligned(16))) E s_q[G::TILE_K];
   __shared__ __attribute__((aligned(16))) E s_ql[QLO * G::TILE_K + 8];
@@ -349,26 +355,35 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
         const int I = idx >> 2, J = idx & 3;
         AV xa = {0, 0, 0, 0}, xd = {0, 0, 0, 0};
         if (!score_tile_zero(idx)) {
+          // q.k (its split cross terms in accumulators of their own) and dO.v
+          // interleaved step by step, so that no MFMA waits on the one before it
+          constexpr int NKD = G::DKP / 32, NKN = G::DVP / 32;
+          AV xh = {0, 0, 0, 0}, xl = {0, 0, 0, 0};
 #pragma unroll
-          for (int kd = 0; kd < G::DKP / 32; ++kd) {
-            Frag<E> fa, fb, fal, fbl;
-            frag_direct(fa, s_q, G::LDK, 16 * I + i16, 32 * kd, l);
-            frag_direct(fb, s_k, G::LDK, 16 * J + i16, 32 * kd, l);
-            if constexpr (DIAG && SP) {
-              frag_direct(fal, s_ql, G::LDK, 16 * I + i16, 32 * kd, l);
-              frag_direct(fbl, s_kl, G::LDK, 16 * J + i16, 32 * kd, l);
-              mma3(xa, fa, fal, fb, fbl);
-            } else {
-              mma(xa, fa, fb);
+          for (int st = 0; st < (NKD > NKN ? NKD : NKN); ++st) {
+            if (st < NKD) {
+              Frag<E> fa, fb;
+              frag_direct(fa, s_q, G::LDK, 16 * I + i16, 32 * st, l);
+              frag_direct(fb, s_k, G::LDK, 16 * J + i16, 32 * st, l);
+              if constexpr (DIAG && SP) {
+                Frag<E> fal, fbl;
+                frag_direct(fal, s_ql, G::LDK, 16 * I + i16, 32 * st, l);
+                frag_direct(fbl, s_kl, G::LDK, 16 * J + i16, 32 * st, l);
+                mma(xa, fa, fb);
+                mma(xh, fa, fbl);
+                mma(xl, fal, fb);
+              } else {
+                mma(xa, fa, fb);
+              }
+            }
+            if (st < NKN) {
+              Frag<E> fa, fb;
+              frag_direct(fa, s_do, G::LDV, 16 * I + i16, 32 * st, l);
+              frag_direct(fb, s_v, G::LDV, 16 * J + i16, 32 * st, l);
+              mma(xd, fa, fb);
             }
           }
-#pragma unroll
-          for (int kn = 0; kn < G::DVP / 32; ++kn) {
-            Frag<E> fa, fb;
-            frag_direct(fa, s_do, G::LDV, 16 * I + i16, 32 * kn, l);
-            frag_direct(fb, s_v, G::LDV, 16 * J + i16, 32 * kn, l);
-            mma(xd, fa, fb);
-          }
+          if constexpr (DIAG && SP) xa += xh + xl;
         }
         // the tiles are stored transposed (row = key token j, column = query token
         // i): the lane's four rows i become one 8-byte write per part
@@ -442,34 +457,60 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
           Frag<E> fs, fsl;
           acc_to_frag_split(fs, fsl, lo, hi);
 #pragma unroll
-          for (int J = 0; J < 4; ++J) {
-            Frag<E> fb, fbl;
-            frag_direct_perm(fb, s_k, G::LDK, 16 * J + i16, 32 * kb, l);
+          for (int J0 = 0; J0 < 4; J0 += GB) {
+            Frag<E> fb[GB], fbl[GB];
+#pragma unroll
+            for (int u = 0; u < GB; ++u) {
+              frag_direct_perm(fb[u], s_k, G::LDK, 16 * (J0 + u) + i16, 32 * kb, l);
+              if constexpr (DIAG && SP) frag_direct_perm(fbl[u], s_kl, G::LDK, 16 * (J0 + u) + i16, 32 * kb, l);
+            }
+#pragma unroll
+            for (int u = 0; u < GB; ++u) mma(av[J0 + u], fs, fb[u]);
             if constexpr (DIAG && SP) {
-              frag_direct_perm(fbl, s_kl, G::LDK, 16 * J + i16, 32 * kb, l);
-              mma3(av[J], fs, fsl, fb, fbl);
-            } else {
-              mma2a(av[J], fs, fsl, fb);
+#pragma unroll
+              for (int u = 0; u < GB; ++u) mma(av[J0 + u], fs, fbl[u]);
+            }
+            if constexpr (SP) {
+#pragma unroll
+              for (int u = 0; u < GB; ++u) mma(av[J0 + u], fsl, fb[u]);
             }
           }
         }
         Frag<E> fdo[2];
 #pragma unroll
         for (int ib = 0; ib < 2; ++ib) frag_tr(fdo[ib], s_do, G::LDV, 32 * ib, 16 * cn, l);
+        // intra part: score-tile blocks ib = 0 (query tokens 0..31, key blocks 0 and
+        // 1) and ib = 1 (every key block)
+        AV accv[4];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) accv[J] = av[J] * s_fk[16 * J + i16];
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib) {
+#pragma unroll
+          for (int J0 = 0; J0 < (ib == 0 ? 2 : 4); J0 += GB) {
+            constexpr int U = GB;
+            Frag<E> fb[U], fbl[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+              if (ib == 0 && J0 + u >= 2) continue;
+              frag_direct(fb[u], s_ah, G::LDA, 16 * (J0 + u) + i16, 32 * ib, l);
+              if constexpr (SP) frag_direct(fbl[u], s_al, G::LDA, 16 * (J0 + u) + i16, 32 * ib, l);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+              if (!(ib == 0 && J0 + u >= 2)) mma(accv[J0 + u], fdo[ib], fb[u]);
+            if constexpr (SP) {
+#pragma unroll
+              for (int u = 0; u < U; ++u)
+                if (!(ib == 0 && J0 + u >= 2)) mma(accv[J0 + u], fdo[ib], fbl[u]);
+            }
+          }
+        }
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
           const int tj = 16 * J + i16;
-          AV acc = av[J] * s_fk[tj];
-#pragma unroll
-          for (int ib = 0; ib < 2; ++ib) {
-            if (ib == 0 && J >= 2) continue;
-            Frag<E> fb, fbl;
-            frag_direct(fb, s_ah, G::LDA, tj, 32 * ib, l);
-            if constexpr (SP) frag_direct(fbl, s_al, G::LDA, tj, 32 * ib, l);
-            mma2b(acc, fdo[ib], fb, fbl);
-          }
           const int n0 = 16 * cn + 4 * g;
-          if (n0 < DV && (full || tj < nv)) store4(dvp + tok_off(b, t0 + tj, h, a.T, a.H, DV) + n0, acc);
+          if (n0 < DV && (full || tj < nv)) store4(dvp + tok_off(b, t0 + tj, h, a.T, a.H, DV) + n0, accv[J]);
         }
       }
 
@@ -513,10 +554,16 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
           Frag<E> fs0, fs0l;
           split_frag(fs0, fs0l, x);
 #pragma unroll
-          for (int I = 0; I < 4; ++I) {
-            Frag<E> fb;
-            frag_direct_perm(fb, s_do, G::LDV, 16 * I + i16, 32 * kn, l);
-            mma2a(ax[I], fs0, fs0l, fb);
+          for (int I0 = 0; I0 < 4; I0 += GB) {
+            Frag<E> fb[GB];
+#pragma unroll
+            for (int u = 0; u < GB; ++u) frag_direct_perm(fb[u], s_do, G::LDV, 16 * (I0 + u) + i16, 32 * kn, l);
+#pragma unroll
+            for (int u = 0; u < GB; ++u) mma(ax[I0 + u], fs0, fb[u]);
+            if constexpr (SP) {
+#pragma unroll
+              for (int u = 0; u < GB; ++u) mma(ax[I0 + u], fs0l, fb[u]);
+            }
           }
         }
         if constexpr (HAS_DG) {
@@ -537,25 +584,50 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
             frag_tr(fkt[jb], s_k, G::LDK, 32 * jb, 16 * cm, l);
             if constexpr (DIAG && SP) frag_tr(fktl[jb], s_kl, G::LDK, 32 * jb, 16 * cm, l);
           }
+          // intra part for the four token blocks, term by term over the blocks (key
+          // blocks jb = 0 for every query block, jb = 1 for query blocks 2 and 3)
+          AV accq[4];
 #pragma unroll
           for (int I = 0; I < 4; ++I) {
             const int ti = 16 * I + i16;
-            AV acc = ax[I];
             if constexpr (SCAL) {
               const f32x4 q4 = load4f(s_q + ti * G::LDK + 16 * cm + 4 * g);
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) u1p[I] += (AS)q4[rr] * (AS)acc[rr];
+              for (int rr = 0; rr < 4; ++rr) u1p[I] += (AS)q4[rr] * (AS)ax[I][rr];
             }
-            acc *= s_fq[ti];
+            accq[I] = ax[I] * s_fq[ti];
+          }
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-              if (jb == 1 && I < 2) continue;
-              Frag<E> fb, fbl;
-              frag_tr(fb, s_dah, G::LDA, 32 * jb, 16 * I, l);
-              if constexpr (SP) frag_tr(fbl, s_dal, G::LDA, 32 * jb, 16 * I, l);
-              if constexpr (DIAG && SP) mma3(acc, fkt[jb], fktl[jb], fb, fbl);
-              else mma2b(acc, fkt[jb], fb, fbl);
+          for (int jb = 0; jb < 2; ++jb) {
+#pragma unroll
+            for (int I0 = 2 * jb; I0 < 4; I0 += GB) {
+              constexpr int U = GB;
+              Frag<E> fb[U], fbl[U];
+#pragma unroll
+              for (int u = 0; u < U; ++u) {
+                if (I0 + u >= 4) continue;
+                frag_tr(fb[u], s_dah, G::LDA, 32 * jb, 16 * (I0 + u), l);
+                if constexpr (SP) frag_tr(fbl[u], s_dal, G::LDA, 32 * jb, 16 * (I0 + u), l);
+              }
+#pragma unroll
+              for (int u = 0; u < U; ++u)
+                if (I0 + u < 4) mma(accq[I0 + u], fkt[jb], fb[u]);
+              if constexpr (SP) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                  if (I0 + u < 4) mma(accq[I0 + u], fkt[jb], fbl[u]);
+              }
+              if constexpr (DIAG && SP) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                  if (I0 + u < 4) mma(accq[I0 + u], fktl[jb], fb[u]);
+              }
             }
+          }
+#pragma unroll
+          for (int I = 0; I < 4; ++I) {
+            const int ti = 16 * I + i16;
+            AV acc = accq[I];
             const int d0 = 16 * cm + 4 * g;
             if constexpr (DIAG) {
               const f32x4 gm = lane_gamma(gl[cc][I], gcar);
@@ -590,10 +662,16 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
           Frag<E> fdt, fdtl;
           split_frag(fdt, fdtl, y);
 #pragma unroll
-          for (int J = 0; J < 4; ++J) {
-            Frag<E> fb;
-            frag_direct_perm(fb, s_v, G::LDV, 16 * J + i16, 32 * kn, l);
-            mma2a(ay[J], fdt, fdtl, fb);
+          for (int J0 = 0; J0 < 4; J0 += GB) {
+            Frag<E> fb[GB];
+#pragma unroll
+            for (int u = 0; u < GB; ++u) frag_direct_perm(fb[u], s_v, G::LDV, 16 * (J0 + u) + i16, 32 * kn, l);
+#pragma unroll
+            for (int u = 0; u < GB; ++u) mma(ay[J0 + u], fdt, fb[u]);
+            if constexpr (SP) {
+#pragma unroll
+              for (int u = 0; u < GB; ++u) mma(ay[J0 + u], fdtl, fb[u]);
+            }
           }
         }
         // dk^T = tail Y'^T + intra, per token block
@@ -605,6 +683,39 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
             frag_tr(fqt[jb], s_q, G::LDK, 32 * jb, 16 * cm, l);
             if constexpr (DIAG && SP) frag_tr(fqtl[jb], s_ql, G::LDK, 32 * jb, 16 * cm, l);
           }
+          // intra part for the four token blocks, term by term over the blocks (query
+          // blocks ib = 0 for key blocks 0 and 1, ib = 1 for every key block)
+          AV acck[4];
+#pragma unroll
+          for (int J = 0; J < 4; ++J) acck[J] = AV{0, 0, 0, 0};
+#pragma unroll
+          for (int ib = 0; ib < 2; ++ib) {
+            const int nj = ib == 0 ? 2 : 4;
+#pragma unroll
+            for (int J0 = 0; J0 < nj; J0 += GB) {
+              constexpr int U = GB;
+              Frag<E> fb[U], fbl[U];
+#pragma unroll
+              for (int u = 0; u < U; ++u) {
+                if (J0 + u >= nj) continue;
+                frag_direct(fb[u], s_dah, G::LDA, 16 * (J0 + u) + i16, 32 * ib, l);
+                if constexpr (SP) frag_direct(fbl[u], s_dal, G::LDA, 16 * (J0 + u) + i16, 32 * ib, l);
+              }
+#pragma unroll
+              for (int u = 0; u < U; ++u)
+                if (J0 + u < nj) mma(acck[J0 + u], fqt[ib], fb[u]);
+              if constexpr (SP) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                  if (J0 + u < nj) mma(acck[J0 + u], fqt[ib], fbl[u]);
+              }
+              if constexpr (DIAG && SP) {
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                  if (J0 + u < nj) mma(acck[J0 + u], fqtl[ib], fb[u]);
+              }
+            }
+          }
 #pragma unroll
           for (int J = 0; J < 4; ++J) {
             const int tj = 16 * J + i16;
@@ -614,16 +725,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
 #pragma unroll
               for (int rr = 0; rr < 4; ++rr) u4p[J] += (AS)k4[rr] * (AS)yv[rr];
             }
-            AV acc = {0, 0, 0, 0};
-#pragma unroll
-            for (int ib = 0; ib < 2; ++ib) {
-              if (ib == 0 && J >= 2) continue;
-              Frag<E> fb, fbl;
-              frag_direct(fb, s_dah, G::LDA, tj, 32 * ib, l);
-              if constexpr (SP) frag_direct(fbl, s_dal, G::LDA, tj, 32 * ib, l);
-              if constexpr (DIAG && SP) mma3(acc, fqt[ib], fqtl[ib], fb, fbl);
-              else mma2b(acc, fqt[ib], fb, fbl);
-            }
+            AV acc = acck[J];
             const int d0 = 16 * cm + 4 * g;
             if constexpr (DIAG) {
               const f32x4 gm = gl[cc][J];
@@ -776,23 +878,44 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
           const int cn = w + G::NW * cc;
           if (cn < G::NVT) frag_tr(fdo[cc], s_do, G::LDV, 32 * kb, 16 * cn, l);
         }
-        // dS[d][n] += sum_i Q^[i][d] dO[i][n]   (rows: every d tile; columns: owned n tiles)
+        // dS[d][n] += sum_i Q^[i][d] dO[i][n]   (rows: every d tile; columns: owned n tiles).
+        // Apply with GB > 1: four row tiles at a time, the hi parts and then the lo
+        // parts. The prepare walk runs four waves per SIMD, which cover each other's
+        // MFMA latency, and has no registers to spare: one row tile at a time.
+        constexpr int UM = (!APPLY || GB == 1) ? 1 : G::NKT < 4 ? G::NKT : 4;
 #pragma unroll
-        for (int m = 0; m < G::NKT; ++m) {
-          Frag<E> fa, fal;
-          frag_tr(fa, qhat_h, G::LDK, 32 * kb, 16 * m, l);
-          if constexpr (QSPLIT) frag_tr(fal, qhat_l, G::LDK, 32 * kb, 16 * m, l);
-          else frag_zero(fal);
-          if (mask_tok) {
-            frag_scale_tokens(fa, s_fq, 32 * kb, false, l);
-            frag_scale_tokens(fal, s_fq, 32 * kb, false, l);
-          }
+        for (int m0 = 0; m0 < G::NKT; m0 += UM) {
+          Frag<E> fa[UM], fal[UM];
 #pragma unroll
-          for (int cc = 0; cc < G::CPWV; ++cc)
-            if (w + G::NW * cc < G::NVT) {
-              if constexpr (QSPLIT) mma2a(dS[m][cc], fa, fal, fdo[cc]);
-              else mma(dS[m][cc], fa, fdo[cc]);
+          for (int u = 0; u < UM; ++u) {
+            frag_tr(fa[u], qhat_h, G::LDK, 32 * kb, 16 * (m0 + u), l);
+            if constexpr (QSPLIT) frag_tr(fal[u], qhat_l, G::LDK, 32 * kb, 16 * (m0 + u), l);
+            if (mask_tok) {
+              frag_scale_tokens(fa[u], s_fq, 32 * kb, false, l);
+              if constexpr (QSPLIT) frag_scale_tokens(fal[u], s_fq, 32 * kb, false, l);
             }
+          }
+          if constexpr (UM == 1) {
+#pragma unroll
+            for (int cc = 0; cc < G::CPWV; ++cc)
+              if (w + G::NW * cc < G::NVT) {
+                if constexpr (QSPLIT) mma2a(dS[m0][cc], fa[0], fal[0], fdo[cc]);
+                else mma(dS[m0][cc], fa[0], fdo[cc]);
+              }
+          } else {
+#pragma unroll
+            for (int u = 0; u < UM; ++u)
+#pragma unroll
+              for (int cc = 0; cc < G::CPWV; ++cc)
+                if (w + G::NW * cc < G::NVT) mma(dS[m0 + u][cc], fa[u], fdo[cc]);
+            if constexpr (QSPLIT) {
+#pragma unroll
+              for (int u = 0; u < UM; ++u)
+#pragma unroll
+                for (int cc = 0; cc < G::CPWV; ++cc)
+                  if (w + G::NW * cc < G::NVT) mma(dS[m0 + u][cc], fal[u], fdo[cc]);
+            }
+          }
         }
         // dS^T[n][d] += sum_i dO[i][n] Q^[i][d]   (rows: every n tile; columns: owned d tiles)
         if constexpr (APPLY) {
@@ -808,12 +931,18 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
               frag_scale_tokens(qa, s_fq, 32 * kb, false, l);
               frag_scale_tokens(qal, s_fq, 32 * kb, false, l);
             }
+            constexpr int UN = GB == 1 ? 1 : G::NVT < 4 ? G::NVT : 4;
 #pragma unroll
-            for (int nt = 0; nt < G::NVT; ++nt) {
-              Frag<E> fd;
-              frag_tr(fd, s_do, G::LDV, 32 * kb, 16 * nt, l);
-              if constexpr (QSPLIT) mma2b(dT[nt][cc], fd, qa, qal);
-              else mma(dT[nt][cc], fd, qa);
+            for (int n0 = 0; n0 < G::NVT; n0 += UN) {
+              Frag<E> fd[UN];
+#pragma unroll
+              for (int u = 0; u < UN; ++u) frag_tr(fd[u], s_do, G::LDV, 32 * kb, 16 * (n0 + u), l);
+#pragma unroll
+              for (int u = 0; u < UN; ++u) mma(dT[n0 + u][cc], fd[u], qa);
+              if constexpr (QSPLIT) {
+#pragma unroll
+                for (int u = 0; u < UN; ++u) mma(dT[n0 + u][cc], fd[u], qal);
+              }
             }
           }
         }
