@@ -20,7 +20,11 @@ namespace cpla {
 
 // S <- diag(exp(Gam_last)) keep*S + K^T V with the tail/decay token factors.
 // K^ = K exp(Gam_last - Gam) tail enters the MFMA split into hi + lo parts.
-template <typename E, int DK, int DV, int DECAY, int NKT_, int CPWV_, typename V, typename GT>
+// UM > 1: UM row tiles at a time, the hi products and then the lo products, so
+// that consecutive MFMAs accumulate into different tiles (for walks with
+// registers to spare; the prepare walk's four waves per SIMD cover each other's
+// MFMA latency instead).
+template <typename E, int DK, int DV, int DECAY, int UM, int NKT_, int CPWV_, typename V, typename GT>
 __device__ __forceinline__ void state_update(V (&S)[NKT_][CPWV_], const E* Kt, const E* Ktl, const E* Vt,
                                              const GT* gam, const float* el, const float* fk,
                                              const ChunkSeg& seg, int l) {
@@ -49,34 +53,63 @@ __device__ __forceinline__ void state_update(V (&S)[NKT_][CPWV_], const E* Kt, c
       if (c < G::NVT) frag_tr(bv[kb][cc], Vt, G::LDV, 32 * kb, 16 * c, l);
     }
   const bool scale_tok = (DECAY == DECAY_SCALAR) || seg.any();
-#pragma unroll
-  for (int m = 0; m < G::NKT; ++m) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      Frag<E> a, al;
-      frag_tr(a, Kt, G::LDK, 32 * kb, 16 * m, l);
-      if constexpr (DECAY == DECAY_DIAG && Split<E>::on) {
-        frag_tr(al, Ktl, G::LDK, 32 * kb, 16 * m, l);
-        if (scale_tok) {
-          frag_scale_tokens(a, fk, 32 * kb, false, l);
-          frag_scale_tokens(al, fk, 32 * kb, false, l);
-        }
-      } else if constexpr (DECAY == DECAY_SCALAR) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = to_f(a.v[e]) * fk[32 * kb + kidx(e, l)];
-        split_frag(a, al, x);
-      } else {
-        if (scale_tok) frag_scale_tokens(a, fk, 32 * kb, false, l);
-        frag_zero(al);
+  // the K^ fragment (hi, lo) of row tile m, token block kb
+  auto k_frag = [&](Frag<E>& a, Frag<E>& al, int m, int kb) {
+    frag_tr(a, Kt, G::LDK, 32 * kb, 16 * m, l);
+    if constexpr (DECAY == DECAY_DIAG && Split<E>::on) {
+      frag_tr(al, Ktl, G::LDK, 32 * kb, 16 * m, l);
+      if (scale_tok) {
+        frag_scale_tokens(a, fk, 32 * kb, false, l);
+        frag_scale_tokens(al, fk, 32 * kb, false, l);
       }
+    } else if constexpr (DECAY == DECAY_SCALAR) {
+      float x[8];
 #pragma unroll
-      for (int cc = 0; cc < G::CPWV; ++cc)
-        if (w + G::NW * cc < G::NVT) {
-          if constexpr (DECAY == DECAY_NONE || !Split<E>::on) mma(S[m][cc], a, bv[kb][cc]);
-          else mma2a(S[m][cc], a, al, bv[kb][cc]);
-        }
+      for (int e = 0; e < 8; ++e) x[e] = to_f(a.v[e]) * fk[32 * kb + kidx(e, l)];
+      split_frag(a, al, x);
+    } else {
+      if (scale_tok) frag_scale_tokens(a, fk, 32 * kb, false, l);
+      frag_zero(al);
     }
+  };
+  constexpr bool LO = DECAY != DECAY_NONE && Split<E>::on;
+  if constexpr (UM == 1) {
+#pragma unroll
+    for (int m = 0; m < G::NKT; ++m) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        Frag<E> a, al;
+        k_frag(a, al, m, kb);
+#pragma unroll
+        for (int cc = 0; cc < G::CPWV; ++cc)
+          if (w + G::NW * cc < G::NVT) {
+            if constexpr (!LO) mma(S[m][cc], a, bv[kb][cc]);
+            else mma2a(S[m][cc], a, al, bv[kb][cc]);
+          }
+      }
+    }
+  } else {
+    static_assert(G::NKT % UM == 0, "row tiles in whole groups");
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int m0 = 0; m0 < G::NKT; m0 += UM) {
+        Frag<E> a[UM], al[UM];
+#pragma unroll
+        for (int u = 0; u < UM; ++u) k_frag(a[u], al[u], m0 + u, kb);
+#pragma unroll
+        for (int u = 0; u < UM; ++u)
+#pragma unroll
+          for (int cc = 0; cc < G::CPWV; ++cc)
+            if (w + G::NW * cc < G::NVT) mma(S[m0 + u][cc], a[u], bv[kb][cc]);
+        if constexpr (LO) {
+#pragma unroll
+          for (int u = 0; u < UM; ++u)
+#pragma unroll
+            for (int cc = 0; cc < G::CPWV; ++cc)
+              if (w + G::NW * cc < G::NVT) mma(S[m0 + u][cc], al[u], bv[kb][cc]);
+        }
+      }
   }
   if constexpr (DECAY == DECAY_DIAG) {
     // K* = K exp(-Gam): restore exp(Gam_last - Gam_j) with a row factor exp(Gam_last[d])
@@ -103,6 +136,12 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   constexpr int GAM = (DECAY == DECAY_DIAG) ? (GSPLIT ? CH / 2 : CH) * DK : CH;
   constexpr int NQT = APPLY ? 1 : 0;
   constexpr int DSP = (DECAY == DECAY_DIAG && Split<E>::on) ? 1 : 0;   // exp-scaled tiles split
+  // The apply walk issues the products of GB token blocks term by term (every hi
+  // part, then every lo part), so that consecutive MFMAs accumulate into
+  // different tiles instead of each waiting on the one before it; d_k != d_v
+  // walks have no registers to spare for the extra fragments and take one block
+  // at a time.
+  constexpr int GB = G::DKP == G::DVP ? 4 : 1;
   __shared__ __attribute__((aligned(16))) E s_q[NQT * G::TILE_K + 8];
   __shared__ __attribute__((aligned(16))) E s_ql[NQT * DSP * G::TILE_K + 8];
   __shared__ __attribute__((aligned(16))) E s_k[G::TILE_K];
@@ -223,19 +262,26 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
         const int I = idx >> 2, J = idx & 3;
         acc4<E> acc = {0, 0, 0, 0};
         if (!score_tile_zero(idx)) {
+          // the split cross terms in accumulators of their own, so that no MFMA
+          // waits on the one before it
+          acc4<E> xh = {0, 0, 0, 0}, xl = {0, 0, 0, 0};
 #pragma unroll
           for (int kd = 0; kd < G::DKP / 32; ++kd) {
-            Frag<E> fa, fb, fal, fbl;
+            Frag<E> fa, fb;
             frag_direct(fa, s_q, G::LDK, 16 * I + i16, 32 * kd, l);
             frag_direct(fb, s_k, G::LDK, 16 * J + i16, 32 * kd, l);
             if constexpr (DSP) {
+              Frag<E> fal, fbl;
               frag_direct(fal, s_ql, G::LDK, 16 * I + i16, 32 * kd, l);
               frag_direct(fbl, s_kl, G::LDK, 16 * J + i16, 32 * kd, l);
-              mma3(acc, fa, fal, fb, fbl);
+              mma(acc, fa, fb);
+              mma(xh, fa, fbl);
+              mma(xl, fal, fb);
             } else {
               mma(acc, fa, fb);
             }
           }
+          if constexpr (DSP) acc += xh + xl;
         }
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
@@ -264,31 +310,58 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
         Frag<E> fvt[2];
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) frag_tr(fvt[jb], s_v, G::LDV, 32 * jb, 16 * cn, l);
+        // GB token blocks at a time: the inter part S0^T q~ (hi.hi, hi.lo, lo.hi over
+        // the blocks), then the intra part A v (score-tile blocks jb = 0 for every
+        // query block, jb = 1 for query blocks 2 and 3)
 #pragma unroll
-        for (int I = 0; I < 4; ++I) {
-          acc4<E> acc = {0, 0, 0, 0};
+        for (int I0 = 0; I0 < 4; I0 += GB) {
+          acc4<E> acc[GB];
+#pragma unroll
+          for (int u = 0; u < GB; ++u) acc[u] = acc4<E>{0, 0, 0, 0};
 #pragma unroll
           for (int kb = 0; kb < G::DKP / 32; ++kb) {
-            Frag<E> fb, fbl;
-            frag_direct_perm(fb, s_q, G::LDK, 16 * I + i16, 32 * kb, l);
+            Frag<E> fb[GB], fbl[GB];
+#pragma unroll
+            for (int u = 0; u < GB; ++u) {
+              frag_direct_perm(fb[u], s_q, G::LDK, 16 * (I0 + u) + i16, 32 * kb, l);
+              if constexpr (DSP) frag_direct_perm(fbl[u], s_ql, G::LDK, 16 * (I0 + u) + i16, 32 * kb, l);
+            }
+#pragma unroll
+            for (int u = 0; u < GB; ++u) mma(acc[u], fs[kb], fb[u]);
             if constexpr (DSP) {
-              frag_direct_perm(fbl, s_ql, G::LDK, 16 * I + i16, 32 * kb, l);
-              mma3(acc, fs[kb], fsl[kb], fb, fbl);
-            } else {
-              mma2a(acc, fs[kb], fsl[kb], fb);
+#pragma unroll
+              for (int u = 0; u < GB; ++u) mma(acc[u], fs[kb], fbl[u]);
+            }
+            if constexpr (Split<E>::on) {
+#pragma unroll
+              for (int u = 0; u < GB; ++u) mma(acc[u], fsl[kb], fb[u]);
             }
           }
-          acc *= s_fq[16 * I + i16];
+#pragma unroll
+          for (int u = 0; u < GB; ++u) acc[u] *= s_fq[16 * (I0 + u) + i16];
 #pragma unroll
           for (int jb = 0; jb < 2; ++jb) {
-            if (jb == 1 && I < 2) continue;
-            Frag<E> fb, fbl;
-            frag_direct(fb, s_a, G::LDA, 16 * I + i16, 32 * jb, l);
-            if constexpr (Split<E>::on) frag_direct(fbl, s_al, G::LDA, 16 * I + i16, 32 * jb, l);
-            mma2b(acc, fvt[jb], fb, fbl);
+            Frag<E> fb[GB], fbl[GB];
+#pragma unroll
+            for (int u = 0; u < GB; ++u) {
+              if (jb == 1 && I0 + u < 2) continue;
+              frag_direct(fb[u], s_a, G::LDA, 16 * (I0 + u) + i16, 32 * jb, l);
+              if constexpr (Split<E>::on) frag_direct(fbl[u], s_al, G::LDA, 16 * (I0 + u) + i16, 32 * jb, l);
+            }
+#pragma unroll
+            for (int u = 0; u < GB; ++u)
+              if (!(jb == 1 && I0 + u < 2)) mma(acc[u], fvt[jb], fb[u]);
+            if constexpr (Split<E>::on) {
+#pragma unroll
+              for (int u = 0; u < GB; ++u)
+                if (!(jb == 1 && I0 + u < 2)) mma(acc[u], fvt[jb], fbl[u]);
+            }
           }
-          const int n0 = 16 * cn + 4 * g;
-          if (n0 < DV && (full || 16 * I + i16 < nv)) store4(o + tok_off(b, t0 + 16 * I + i16, h, a.T, a.H, DV) + n0, acc);
+#pragma unroll
+          for (int u = 0; u < GB; ++u) {
+            const int n0 = 16 * cn + 4 * g, ti = 16 * (I0 + u) + i16;
+            if (n0 < DV && (full || ti < nv)) store4(o + tok_off(b, t0 + ti, h, a.T, a.H, DV) + n0, acc[u]);
+          }
         }
       }
     }
@@ -313,7 +386,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
           }
       }
     }
-    state_update<E, DK, DV, DECAY>(S, s_k, s_kl, s_v, s_gam, s_el, s_fk, seg, lane_pick<APPLY>());
+    state_update<E, DK, DV, DECAY, (APPLY && GB > 1) ? (G::NKT < 4 ? G::NKT : 4) : 1>(S, s_k, s_kl, s_v, s_gam, s_el, s_fk, seg,
+                                                            lane_pick<APPLY>());
     __syncthreads();
   }
 
