@@ -47,22 +47,30 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows (b,h) in the oracle sample (0 = auto)")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
+                    help="only run the hand-written 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
 
 
 def copy_calibration():
-    """A plain device-to-device copy of known size: under rocprofv3 --pmc, its
+    """The hand-written streaming copy (libcpla_peaks.so, four 16-byte vectors in
+    flight per thread) of 1 GiB, three times: under rocprofv3 --pmc, its
     FETCH_SIZE / WRITE_SIZE per dispatch divided by 1 GiB gives the scale that
     turns those counters into bytes."""
     import torch
-    n = (1 << 30) // 4
-    x = torch.randn(n, device="cuda:0")
+    L = _peaks_lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    n = 1 << 30
+    x = torch.empty(n // 4, device=dev).fill_(1.0)
     y = torch.empty_like(x)
     for _ in range(3):
-        y.copy_(x)
+        rc = L.cpla_peak_copy(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(y.data_ptr()), n, cus * 8, 0,
+                              ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"cpla_peak_copy failed ({rc})")
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "dispatches": 3}), flush=True)
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "dispatches": 3}), flush=True)
 
 
 # ---- algorithmic counts (per token-head, chunk C, head size d) ------------------------
