@@ -25,8 +25,10 @@
  *
  * Conventions shared by every call
  *   - Every pointer is caller-owned. Device pointers point to HBM; the library
- *     allocates nothing, keeps no pointer after returning, and enqueues all
- *     device work on `stream` without synchronising the host.
+ *     calls no allocator (the one buffer of its own is the static scratch array
+ *     of cp_forward_apply_noalloc), keeps no caller pointer after returning, and
+ *     enqueues all device work on `stream` without synchronising the host
+ *     (cpla_check_decay_range, which returns a count, synchronises `stream`).
  *   - Tensors are dense row-major with the last index fastest:
  *       q, k      [B, T, H, dk]   dtype (bf16 or fp32)
  *       v, o, dO  [B, T, H, dv]   dtype
