@@ -6,13 +6,18 @@ tokens, seeded synthetic inputs already resident in HBM. One step = the whole
 hot path: cp_forward_prepare, cp_forward_apply (prefix scan + local output),
 cp_backward_prepare, cp_backward_apply (suffix scan + local gradients).
 
-Prints ONE JSON line. `roofline` is for the dominant kernel (the backward shard
+Prints ONE JSON line. The headline times K steps, each right after a 512 MiB
+read that leaves no input in L2 or the memory-side cache (`warm` repeats the
+steps back to back). `roofline` is for the dominant kernel (the backward shard
 walk inside cp_backward_apply): algorithmic bytes per launch / its average
 duration from HIP events recorded on the launch stream around that call (the
-call also runs the small suffix-scan kernel). `traffic` comes from the committed
-rocprofv3 counter summary in profiles/, and is null if the kernel sources changed
-since it was taken. `cpu_baseline` times the fp64 oracle on a bounded sample,
-before the GPU is touched.
+call also runs the small suffix-scan kernel), against the published 8 TB/s and
+against the attainable peaks this run measures with the hand-written probes of
+libcpla_peaks.so (`measured_peaks`: a streaming copy, MFMA issue loops).
+`traffic` comes from the committed rocprofv3 counter summary in profiles/, and is
+null if the kernel sources changed since it was taken. `cpu_baseline` times the
+fp64 oracle on a bounded sample (and one row single-threaded), before the GPU is
+touched.
 """
 from __future__ import annotations
 
