@@ -98,7 +98,10 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   constexpr int AT_BYTES = APPLY ? (SP ? 4 : 2) * G::TILE_A * (int)sizeof(E) : 0;
   // the scalar decay's dg / dw sums: fp32 for bf16 inputs, fp64 for fp32 inputs
   using AS = typename std::conditional<sizeof(E) == 2, float, double>::type;
-  constexpr int P_BYTES = (APPLY && SCAL) ? CH * (CH + 1) * (int)sizeof(AS) : 0;
+  // scalar decay: per score tile, the row sums left of and the column sums below
+  // the diagonal of P_ij = exp(Gam_i - Gam_j) w_j (q_i.k_j)(dO_i.v_j) (16 tile
+  // slots of 16 rows and 16 columns), and P's diagonal
+  constexpr int P_BYTES = (APPLY && SCAL) ? (2 * 16 * 16 + CH) * (int)sizeof(AS) : 0;
   constexpr int REG_BYTES = (GAM_BYTES > AT_BYTES + P_BYTES ? GAM_BYTES : AT_BYTES + P_BYTES) + 16;
   // Apply walk, bf16 with a diagonal decay: the next chunk's raw inputs are copied
   // into LDS by DMA once the dk phase is done (q into a buffer of its own; k, v,
@@ -139,7 +142,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   E* s_al = s_ah + G::TILE_A;
   E* s_dah = s_ah + (SP ? 2 : 1) * G::TILE_A;
   E* s_dal = s_dah + G::TILE_A;
-  AS* s_p = reinterpret_cast<AS*>(s_reg + AT_BYTES);
+  AS* s_rowp = reinterpret_cast<AS*>(s_reg + AT_BYTES);
+  AS* s_colp = s_rowp + 16 * 16;
+  AS* s_pdiag = s_colp + 16 * 16;
   // the tile Q^ is read from in the dS update: scalar -> s_qh, else the q tile
   const E* qhat_h = SCAL ? s_qh : s_q;
   const E* qhat_l = SCAL ? s_qhl : s_ql;
@@ -392,6 +397,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
         f32x4 va, vd;
         const int j = 16 * J + i16;
         const int sj = seg.index(j);
+        AS prow[4], pcol = 0;   // scalar decay: P left of / below the diagonal
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
           const int i = 16 * I + 4 * g + rr;
@@ -401,11 +407,30 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
           if constexpr (SCAL) {
             // exp(Gam_i - Gam_j) and the input weight of token j, applied once
             const float dec = ok ? __expf((float)(s_gam[i] - s_gam[j])) * s_w[j] : 0.f;
-            // exp(Gam_i - Gam_j) w_j (q_i.k_j)(dO_i.v_j)
-            s_p[i * (CH + 1) + j] = (AS)(ok ? xa[rr] : 0) * (AS)(ok ? xd[rr] : 0) * (AS)dec;
+            // P_ij = exp(Gam_i - Gam_j) w_j (q_i.k_j)(dO_i.v_j)
+            const AS pv = (AS)(ok ? xa[rr] : 0) * (AS)(ok ? xd[rr] : 0) * (AS)dec;
+            prow[rr] = i > j ? pv : (AS)0;
+            pcol += i > j ? pv : (AS)0;
+            if (i == j) s_pdiag[i] = pv;
             va[rr] *= dec;
             vd[rr] *= dec;
           }
+        }
+        if constexpr (SCAL) {
+          // the tile's row sums (over its 16 columns: the lanes of a group) and
+          // column sums (over its 16 rows: rr and the lane groups), one slot per tile
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            AS x = prow[rr];
+            x += __shfl_xor(x, 1, 64);
+            x += __shfl_xor(x, 2, 64);
+            x += __shfl_xor(x, 4, 64);
+            x += __shfl_xor(x, 8, 64);
+            if (i16 == 0) s_rowp[16 * idx + 4 * g + rr] = x;
+          }
+          pcol += __shfl_xor(pcol, 16, 64);
+          pcol += __shfl_xor(pcol, 32, 64);
+          if (g == 0) s_colp[16 * idx + i16] = pcol;
         }
         store_split4(s_ah, s_al, j * G::LDA + 16 * I + 4 * g, va);
         store_split4(s_dah, s_dal, j * G::LDA + 16 * I + 4 * g, vd);
@@ -815,10 +840,16 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
             u4 += s_u4[ww * CH + t];
           }
           u1 *= s_fq[t];
-          // T2 step: row t left of the diagonal minus column t below it
+          // T2 step: row t left of the diagonal minus column t below it, from the
+          // score tiles' row sums (tiles (t/16, J), J <= t/16) and column sums
+          // (tiles (I, t/16), I >= t/16)
           AS rowl = 0, colb = 0;
-          for (int j = 0; j < t; ++j) rowl += s_p[t * (CH + 1) + j];
-          for (int i = t + 1; i < CH; ++i) colb += s_p[i * (CH + 1) + t];
+          const int bt = t >> 4, tt = t & 15;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (u <= bt) rowl += s_rowp[16 * (4 * bt + u) + tt];
+            if (u >= bt) colb += s_colp[16 * (4 * u + bt) + tt];
+          }
           AS x = u1 + rowl - colb;
 #pragma unroll
           for (int off = 1; off < 64; off <<= 1) {
@@ -843,7 +874,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
           // of the P tile on and below the diagonal, the tail part is u4; both carry
           // w_t (in the score decay and the tail factor), divided out here
           if (a.dw && t < nv)
-            a.dw[(b * a.T + t0 + t) * a.H + h] = (float)((colb + s_p[t * (CH + 1) + t] + u4) / (AS)s_w[t]);
+            a.dw[(b * a.T + t0 + t) * a.H + h] = (float)((colb + s_pdiag[t] + u4) / (AS)s_w[t]);
         }
       }
     }
