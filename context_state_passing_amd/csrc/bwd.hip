@@ -40,6 +40,39 @@ __device__ __forceinline__ float row_shr(float x) {
                                                                0xf, 0xf, true));
 }
 
+// Sum over the 16 lanes of each DPP row, in every lane of the row (quad swaps,
+// then the half-row and row mirrors: VALU only, no trip through the LDS unit).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp_f<0xB1>(x);    // quad_perm [1, 0, 3, 2]
+  x += dpp_f<0x4E>(x);    // quad_perm [2, 3, 0, 1]
+  x += dpp_f<0x141>(x);   // row_half_mirror
+  x += dpp_f<0x140>(x);   // row_mirror
+  return x;
+}
+__device__ __forceinline__ float lane_value(float x, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), lane));
+}
+// Sum over the 64 lanes, in every lane.
+__device__ __forceinline__ float wave_total(float x) {
+  x = row_sum(x);
+  return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
+}
+// Inclusive prefix sums over the 64 lanes: DPP scans within the rows, then the
+// totals of the earlier rows (their last lanes).
+__device__ __forceinline__ float wave_scan(float x) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  x += row_shr<8>(x);
+  const float r0 = lane_value(x, 15), r1 = lane_value(x, 31), r2 = lane_value(x, 47);
+  const int row = lane_id() >> 4;
+  return x + (row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f) + (row >= 3 ? r2 : 0.f);
+}
+
 // Inclusive prefix sums over the 16 lanes of each DPP row, per component.
 __device__ __forceinline__ f32x4 row_scan(f32x4 x) {
 #pragma unroll
@@ -422,10 +455,14 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
 #pragma unroll
           for (int rr = 0; rr < 4; ++rr) {
             AS x = prow[rr];
-            x += __shfl_xor(x, 1, 64);
-            x += __shfl_xor(x, 2, 64);
-            x += __shfl_xor(x, 4, 64);
-            x += __shfl_xor(x, 8, 64);
+            if constexpr (sizeof(AS) == 4) {
+              x = row_sum(x);
+            } else {
+              x += __shfl_xor(x, 1, 64);
+              x += __shfl_xor(x, 2, 64);
+              x += __shfl_xor(x, 4, 64);
+              x += __shfl_xor(x, 8, 64);
+            }
             if (i16 == 0) s_rowp[16 * idx + 4 * g + rr] = x;
           }
           pcol += __shfl_xor(pcol, 16, 64);
@@ -828,7 +865,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
             s_u4[w * CH + 16 * I + i16] = x4;
           }
         }
-        t3p = wave_sum(g == 0 ? t3p : (AS)0);
+        if constexpr (sizeof(AS) == 4) t3p = wave_total(g == 0 ? t3p : (AS)0);
+        else t3p = wave_sum(g == 0 ? t3p : (AS)0);
         if (l == 0) s_red[w] = t3p;
         __syncthreads();
         if (w == 0) {
@@ -851,16 +889,24 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
             if (u >= bt) colb += s_colp[16 * (4 * u + bt) + tt];
           }
           AS x = u1 + rowl - colb;
-#pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const AS y = __shfl_down(x, off, 64);
-            if (t + off < 64) x += y;
-          }
           AS y4 = u4;
+          if constexpr (sizeof(AS) == 4) {
+            // suffix sums of x (the total less the prefix before t), exclusive
+            // prefix sums of u4
+            const float px = wave_scan(x);
+            x = lane_value(px, 63) - px + x;
+            y4 = wave_scan(u4);
+          } else {
 #pragma unroll
-          for (int off = 1; off < 64; off <<= 1) {
-            const AS y = __shfl_up(y4, off, 64);
-            if (t >= off) y4 += y;
+            for (int off = 1; off < 64; off <<= 1) {
+              const AS y = __shfl_down(x, off, 64);
+              if (t + off < 64) x += y;
+            }
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+              const AS y = __shfl_up(y4, off, 64);
+              if (t >= off) y4 += y;
+            }
           }
           y4 -= u4;
           AS t3s = 0;
