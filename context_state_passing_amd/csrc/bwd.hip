@@ -85,12 +85,12 @@ __device__ __forceinline__ f32x4 row_scan(f32x4 x) {
   return x;
 }
 
-// Value of the row's last lane (lane 15 of each group of 16), per component.
-__device__ __forceinline__ f32x4 row_last(const f32x4& x) {
-  f32x4 y;
+// Sum over the 16 lanes of each DPP row (the last lane of its inclusive scan),
+// per component, in every lane of the row.
+__device__ __forceinline__ f32x4 row_total(f32x4 x) {
 #pragma unroll
-  for (int rr = 0; rr < 4; ++rr) y[rr] = __shfl(x[rr], 15, 16);
-  return y;
+  for (int rr = 0; rr < 4; ++rr) x[rr] = row_sum(x[rr]);
+  return x;
 }
 
 // Gam at token 16 I + (lane % 16) of the current block and key dims d0 .. d0+3
@@ -98,9 +98,10 @@ __device__ __forceinline__ f32x4 row_last(const f32x4& x) {
 // prefix sum over the row plus the total of the earlier blocks held in carry
 // (updated for the next block).
 __device__ __forceinline__ f32x4 lane_gamma(f32x4 x, f32x4& carry) {
+  const f32x4 tot = row_total(x);
   x = row_scan(x);
   const f32x4 out = x + carry;
-  carry += row_last(x);
+  carry += tot;
   return out;
 }
 
@@ -834,7 +835,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
             t3v[rr] = (d0 + rr < DK) ? keep * t3 : 0.f;
           }
           // total of w over the 64 tokens, and exclusive prefix sums of r over them
-          const f32x4 base = row_last(row_scan(wtot[cc])) + t3v;
+          const f32x4 base = row_total(wtot[cc]) + t3v;
           f32x4 pre_tot = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int I = 0; I < 4; ++I) {
@@ -843,7 +844,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) ex[rr] = row_shr<1>(x[rr]);
             f32x4 dgv = base + ex + pre_tot;
-            pre_tot += row_last(x);
+            pre_tot += row_total(wv[cc][I]);
             const int t = 16 * I + i16;
             if ((seg.starts >> t) & 1ull) dgv = f32x4{0.f, 0.f, 0.f, 0.f};
             if (d0 < DK && (full || t < nv)) store4(a.dg + tok_off(b, t0 + t, h, a.T, a.H, DK) + d0, dgv);
