@@ -19,7 +19,6 @@
 namespace cpla {
 
 // S <- diag(exp(Gam_last)) keep*S + K^T V with the tail/decay token factors.
-// K^ = K exp(Gam_last - Gam) tail enters the MFMA split into hi + lo parts.
 // UM > 1: UM row tiles at a time, the hi products and then the lo products, so
 // that consecutive MFMAs accumulate into different tiles (for walks with
 // registers to spare; the prepare walk's four waves per SIMD cover each other's
@@ -44,16 +43,37 @@ __device__ __forceinline__ void state_update(V (&S)[NKT_][CPWV_], const E* Kt, c
 #pragma unroll
       for (int cc = 0; cc < G::CPWV; ++cc) S[m][cc] *= keep;
   }
-  Frag<E> bv[2][G::CPWV];
+  // V fragments, once per token block. Without a diagonal decay the token factors
+  // fk (tail, and for a scalar decay exp(Gam_last - Gam_j) w_j) scale them here,
+  // 2 fragments per wave rather than every K fragment; the scalar-decay V^ = fk V
+  // enters the MFMA split into hi + lo parts. (A diagonal decay's factors differ
+  // per key dim and sit in the staged K~ tiles, hi + lo.)
+  constexpr bool VLO = DECAY == DECAY_SCALAR && Split<E>::on;
+  constexpr bool LO = (DECAY == DECAY_DIAG || DECAY == DECAY_SCALAR) && Split<E>::on;
+  const bool scale_tok = (DECAY == DECAY_SCALAR) || seg.any();
+  Frag<E> bv[2][G::CPWV], bvl[VLO ? 2 : 1][G::CPWV];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
     for (int cc = 0; cc < G::CPWV; ++cc) {
       const int c = w + G::NW * cc;
-      if (c < G::NVT) frag_tr(bv[kb][cc], Vt, G::LDV, 32 * kb, 16 * c, l);
+      if (c >= G::NVT) continue;
+      frag_tr(bv[kb][cc], Vt, G::LDV, 32 * kb, 16 * c, l);
+      if constexpr (DECAY == DECAY_SCALAR) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = to_f(bv[kb][cc].v[e]) * fk[32 * kb + kidx(e, l)];
+        if constexpr (VLO) {
+          split_frag(bv[kb][cc], bvl[kb][cc], x);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) frag_set(bv[kb][cc], e, x[e]);
+        }
+      } else if constexpr (DECAY == DECAY_NONE) {
+        if (scale_tok) frag_scale_tokens(bv[kb][cc], fk, 32 * kb, false, l);
+      }
     }
-  const bool scale_tok = (DECAY == DECAY_SCALAR) || seg.any();
-  // the K^ fragment (hi, lo) of row tile m, token block kb
+  // the K fragment of row tile m, token block kb (diagonal: K~ hi and lo)
   auto k_frag = [&](Frag<E>& a, Frag<E>& al, int m, int kb) {
     frag_tr(a, Kt, G::LDK, 32 * kb, 16 * m, l);
     if constexpr (DECAY == DECAY_DIAG && Split<E>::on) {
@@ -62,17 +82,15 @@ __device__ __forceinline__ void state_update(V (&S)[NKT_][CPWV_], const E* Kt, c
         frag_scale_tokens(a, fk, 32 * kb, false, l);
         frag_scale_tokens(al, fk, 32 * kb, false, l);
       }
-    } else if constexpr (DECAY == DECAY_SCALAR) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = to_f(a.v[e]) * fk[32 * kb + kidx(e, l)];
-      split_frag(a, al, x);
-    } else {
+    } else if constexpr (DECAY == DECAY_DIAG) {
       if (scale_tok) frag_scale_tokens(a, fk, 32 * kb, false, l);
-      frag_zero(al);
     }
   };
-  constexpr bool LO = DECAY != DECAY_NONE && Split<E>::on;
+  // the lo product: K~ lo times V (diagonal), K times V^ lo (scalar)
+  auto mma_lo = [&](V& acc, const Frag<E>& a, const Frag<E>& al, int kb, int cc) {
+    if constexpr (DECAY == DECAY_DIAG) mma(acc, al, bv[kb][cc]);
+    else mma(acc, a, bvl[kb][cc]);
+  };
   if constexpr (UM == 1) {
 #pragma unroll
     for (int m = 0; m < G::NKT; ++m) {
@@ -83,8 +101,8 @@ __device__ __forceinline__ void state_update(V (&S)[NKT_][CPWV_], const E* Kt, c
 #pragma unroll
         for (int cc = 0; cc < G::CPWV; ++cc)
           if (w + G::NW * cc < G::NVT) {
-            if constexpr (!LO) mma(S[m][cc], a, bv[kb][cc]);
-            else mma2a(S[m][cc], a, al, bv[kb][cc]);
+            mma(S[m][cc], a, bv[kb][cc]);
+            if constexpr (LO) mma_lo(S[m][cc], a, al, kb, cc);
           }
       }
     }
@@ -107,7 +125,7 @@ __device__ __forceinline__ void state_update(V (&S)[NKT_][CPWV_], const E* Kt, c
           for (int u = 0; u < UM; ++u)
 #pragma unroll
             for (int cc = 0; cc < G::CPWV; ++cc)
-              if (w + G::NW * cc < G::NVT) mma(S[m0 + u][cc], al[u], bv[kb][cc]);
+              if (w + G::NW * cc < G::NVT) mma_lo(S[m0 + u][cc], a[u], al[u], kb, cc);
         }
       }
   }
