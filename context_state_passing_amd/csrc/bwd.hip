@@ -121,8 +121,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   // k tile only in apply; lo part for the diagonal decay
   constexpr int KLO = (APPLY && DIAG && SP) ? 1 : 0;
   // Q^ = q exp(Gam_i) live_i (scalar decay), split
-  constexpr int QH = SCAL ? 1 : 0;
-  constexpr int QHL = (SCAL && SP) ? 1 : 0;
+  constexpr int QH = (SCAL && APPLY) ? 1 : 0;
+  constexpr int QHL = (SCAL && SP && APPLY) ? 1 : 0;
   // region: Gam (diag, fp32) during staging, then A/dA hi/lo and the scalar P tile.
   // The prepare walk (two workgroups per CU) stages Gam rows 32..63 in the dO
   // tile's buffer, written after the q tile is scaled (when they fit there: not
@@ -355,8 +355,6 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
       if constexpr (DIAG) {
         store_tile<E, DK, G::DKP, G::LDK, 1, DK, G::NT>(aq, s_q, s_ql, s_gam, nullptr, tidf, gam_hi);
         __syncthreads();   // the dO tile overwrites Gam rows 32..63
-      } else if constexpr (SCAL) {
-        store_tile<E, DK, G::DKP, G::LDK, 3, DK, G::NT>(aq, s_qh, s_qhl, s_gam, s_fq, tidf);
       } else {
         store_tile<E, DK, G::DKP, G::LDK, 0, DK, G::NT>(aq, s_q, nullptr, s_gam, nullptr, tidf);
       }
@@ -948,13 +946,31 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
       // token mask for Q^ where it is not baked into a tile (diagonal / no decay, packed chunks)
       const bool mask_tok = !SCAL && seg.any();
       constexpr bool QSPLIT = SP && (DIAG || SCAL);
+      // dS part: a scalar decay's token factors fq = live exp(Gam) scale the dO
+      // fragments (two per token block) instead, split hi/lo, against the plain q
+      // tile; a diagonal decay's depend on the key dim and sit in the Q~ tiles
+      constexpr bool DOSC = SCAL;
+      constexpr bool QSPLIT_S = QSPLIT && !DOSC, LO_B = DOSC && SP;
+      const E* const qs_h = DOSC ? s_q : qhat_h;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        Frag<E> fdo[G::CPWV];
+        Frag<E> fdo[G::CPWV], fdol[LO_B ? G::CPWV : 1];
 #pragma unroll
         for (int cc = 0; cc < G::CPWV; ++cc) {
           const int cn = w + G::NW * cc;
-          if (cn < G::NVT) frag_tr(fdo[cc], s_do, G::LDV, 32 * kb, 16 * cn, l);
+          if (cn >= G::NVT) continue;
+          frag_tr(fdo[cc], s_do, G::LDV, 32 * kb, 16 * cn, l);
+          if constexpr (DOSC) {
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = to_f(fdo[cc].v[e]) * s_fq[32 * kb + kidx(e, l)];
+            if constexpr (LO_B) {
+              split_frag(fdo[cc], fdol[cc], x);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) frag_set(fdo[cc], e, x[e]);
+            }
+          }
         }
         // dS[d][n] += sum_i Q^[i][d] dO[i][n]   (rows: every d tile; columns: owned n tiles).
         // Apply with GB > 1: four row tiles at a time, the hi parts and then the lo
@@ -966,19 +982,23 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
           Frag<E> fa[UM], fal[UM];
 #pragma unroll
           for (int u = 0; u < UM; ++u) {
-            frag_tr(fa[u], qhat_h, G::LDK, 32 * kb, 16 * (m0 + u), l);
-            if constexpr (QSPLIT) frag_tr(fal[u], qhat_l, G::LDK, 32 * kb, 16 * (m0 + u), l);
+            frag_tr(fa[u], qs_h, G::LDK, 32 * kb, 16 * (m0 + u), l);
+            if constexpr (QSPLIT_S) frag_tr(fal[u], qhat_l, G::LDK, 32 * kb, 16 * (m0 + u), l);
             if (mask_tok) {
               frag_scale_tokens(fa[u], s_fq, 32 * kb, false, l);
-              if constexpr (QSPLIT) frag_scale_tokens(fal[u], s_fq, 32 * kb, false, l);
+              if constexpr (QSPLIT_S) frag_scale_tokens(fal[u], s_fq, 32 * kb, false, l);
             }
           }
           if constexpr (UM == 1) {
 #pragma unroll
             for (int cc = 0; cc < G::CPWV; ++cc)
               if (w + G::NW * cc < G::NVT) {
-                if constexpr (QSPLIT) mma2a(dS[m0][cc], fa[0], fal[0], fdo[cc]);
-                else mma(dS[m0][cc], fa[0], fdo[cc]);
+                if constexpr (QSPLIT_S) {
+                  mma2a(dS[m0][cc], fa[0], fal[0], fdo[cc]);
+                } else {
+                  mma(dS[m0][cc], fa[0], fdo[cc]);
+                  if constexpr (LO_B) mma(dS[m0][cc], fa[0], fdol[cc]);
+                }
               }
           } else {
 #pragma unroll
@@ -986,12 +1006,15 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
 #pragma unroll
               for (int cc = 0; cc < G::CPWV; ++cc)
                 if (w + G::NW * cc < G::NVT) mma(dS[m0 + u][cc], fa[u], fdo[cc]);
-            if constexpr (QSPLIT) {
+            if constexpr (QSPLIT_S || LO_B) {
 #pragma unroll
               for (int u = 0; u < UM; ++u)
 #pragma unroll
                 for (int cc = 0; cc < G::CPWV; ++cc)
-                  if (w + G::NW * cc < G::NVT) mma(dS[m0 + u][cc], fal[u], fdo[cc]);
+                  if (w + G::NW * cc < G::NVT) {
+                    if constexpr (QSPLIT_S) mma(dS[m0 + u][cc], fal[u], fdo[cc]);
+                    else mma(dS[m0 + u][cc], fa[u], fdol[cc]);
+                  }
             }
           }
         }
