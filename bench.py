@@ -309,8 +309,7 @@ def main_ssd(args, rank):
     B, T, H, G, N, P = wl.B, wl.T, wl.H, wl.G, wl.N, wl.num_shards
     assert x.shape[-1] == N, "the SSD bench workload has its head dim equal to its state size"
     sp_ = SsdProblem(B, T, H, G, N, N, _lib.BF16 if wl.dtype == torch.bfloat16 else _lib.F32)
-    q = torch.empty_like(x)
-    k = torch.empty_like(x)
+    q, k = Cm, Bm            # read in place by the walks: one head of them per group of heads
     g = torch.empty_like(dt)
     p = make_problem(q, x, P, _lib.DECAY_SCALAR)
     L = _lib.lib()
@@ -333,7 +332,7 @@ def main_ssd(args, rank):
 
     def step(ev=None):
         if ev: ev[0].record(stream)
-        chk(L.cpla_ssd_inputs(sp, _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), _ptr(q), _ptr(k), _ptr(g), st))
+        chk(L.cpla_ssd_inputs(sp, _ptr(dt), _ptr(A), _ptr(Bm), _ptr(Cm), None, None, _ptr(g), st))
         if ev: ev[1].record(stream)
         chk(L.cp_forward_prepare_weighted(pp, None, _ptr(k), _ptr(x), _ptr(g), _ptr(dt), _ptr(fsum), st))
         if ev: ev[2].record(stream)
@@ -367,8 +366,9 @@ def main_ssd(args, rank):
     tokens = B * T
     th = tokens * H
     e = 2 if wl.dtype == torch.bfloat16 else 4
-    # dominant kernel: the weighted backward apply (q, k, v, dO, g, w in; fp32 dq, dk, dv and dg, dw out)
-    dom_bytes = (4 * N * e + 8 + 3 * N * 4 + 8) * th
+    # dominant kernel: the weighted backward apply (v, dO, g, w per head and q = C, k = B per group in;
+    # fp32 dq, dk, dv and dg, dw out)
+    dom_bytes = (2 * N * e + 2 * N * e * G / H + 8 + 3 * N * 4 + 8) * th
     dom_ms = parts[4]
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     # the SSD's own minimum per token-head: x, dy, dt in and dx, d_dt out, y out; B, C, dB, dC per group

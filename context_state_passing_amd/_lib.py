@@ -39,7 +39,7 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int64), ("T", ctypes.c_int64), ("H", ctypes.c_int64),
                 ("dk", ctypes.c_int64), ("dv", ctypes.c_int64), ("num_shards", ctypes.c_int32),
                 ("chunk", ctypes.c_int32), ("rank_begin", ctypes.c_int32), ("rank_end", ctypes.c_int32),
-                ("dtype", ctypes.c_int32), ("decay", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("decay", ctypes.c_int32), ("qk_heads", ctypes.c_int32)]
 
 
 class SsdProblem(ctypes.Structure):

@@ -188,12 +188,14 @@ def _decay_of(g: Optional[torch.Tensor], q: torch.Tensor) -> int:
 
 
 def make_problem(q, v, num_shards: int, decay: int, chunk: int = 64, rank_range=None) -> Problem:
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+    """The problem of q [B,T,Hq,dk] and v [B,T,H,dv]; Hq < H (a divisor of H) shares
+    each q and k head among H / Hq consecutive heads (qk_heads = Hq)."""
+    B, T, Hq, dk = q.shape
+    H, dv = v.shape[2], v.shape[3]
     if q.dtype not in _DTYPE:
         raise CplaError(3, f"dtype {q.dtype} unsupported")
     rb, re = (0, num_shards) if rank_range is None else rank_range
-    return Problem(B, T, H, dk, dv, num_shards, chunk, rb, re, _DTYPE[q.dtype], decay)
+    return Problem(B, T, H, dk, dv, num_shards, chunk, rb, re, _DTYPE[q.dtype], decay, 0 if Hq == H else Hq)
 
 
 def check_decay_range(g: torch.Tensor, num_shards: int, dk: Optional[int] = None) -> None:
@@ -216,15 +218,19 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
             packed: Optional[PackedMeta] = None, save_for_backward: bool = True, chunk: int = 64,
             out: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None):
     """o [B,T,H,dv] (dtype of q) and a Context for ``backward``. ``w`` [B,T,H] fp32:
-    per-token input weights (scalar decay): S_t = exp(g_t) S_{t-1} + w_t k_t v_t^T."""
+    per-token input weights (scalar decay): S_t = exp(g_t) S_{t-1} + w_t k_t v_t^T.
+    q and k may have fewer heads than v, a divisor Hq of H: head h then reads their
+    head h // (H // Hq) (Mamba2's B and C shared by a group of heads)."""
     if not torch.is_tensor(q) or q.dim() != 4 or not torch.is_tensor(v) or v.dim() != 4:
         raise CplaError(2, "q and v must be [B,T,H,d] tensors")
     if q.dtype not in _DTYPE:
         raise CplaError(3, f"dtype {q.dtype} unsupported")
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
-    _expect("q", q, (B, T, H, dk), q.dtype)
-    _expect("k", k, (B, T, H, dk), q.dtype)
+    B, T, Hq, dk = q.shape
+    H, dv = v.shape[2], v.shape[-1]
+    if Hq <= 0 or H % Hq != 0:
+        raise CplaError(2, f"q and k have {Hq} heads, which does not divide the {H} heads of v")
+    _expect("q", q, (B, T, Hq, dk), q.dtype)
+    _expect("k", k, (B, T, Hq, dk), q.dtype)
     _expect("v", v, (B, T, H, dv), q.dtype)
     if g is not None and g.dim() == 4:
         _expect("g", g, (B, T, H, dk), torch.float32)
@@ -240,8 +246,6 @@ def forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: Optional[torch
     if cu_seqlens is not None and packed is None:
         packed = packed_meta(cu_seqlens, q.shape[1], num_shards, q.device, q.shape[0])
     L = _lib.lib()
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
     W = L.cpla_summary_width(ctypes.byref(p))
     dev = q.device
     fsum = torch.empty((num_shards, B, H, W), device=dev, dtype=torch.float32)
@@ -272,11 +276,12 @@ def backward(dO: torch.Tensor, ctx: Context, d_final_state: Optional[torch.Tenso
     """(dq, dk, dv, dg, d_initial_state); dg is None without decay, d_initial_state
     None with packed sequences. With input weights (``w`` given to ``forward``) a
     sixth element dw [B,T,H] fp32 follows, and ``grad_dtype=torch.float32`` gives dq,
-    dk, dv in fp32 (bf16 inputs, scalar decay)."""
+    dk, dv in fp32 (bf16 inputs, scalar decay). dq and dk are per head [B,T,H,dk]
+    also where q and k are shared by groups of heads."""
     if ctx.chunk_states is None:
         raise CplaError(1, "forward was run with save_for_backward=False")
-    B, T, H, dk = ctx.q.shape
-    dv = ctx.v.shape[-1]
+    B, T, _, dk = ctx.q.shape
+    H, dv = ctx.v.shape[2], ctx.v.shape[-1]
     _expect("dO", dO, (B, T, H, dv), ctx.q.dtype, ctx.q.device)
     _expect("d_final_state", d_final_state, (B, H, dk, dv), torch.float32, ctx.q.device, optional=True)
     L = _lib.lib()
@@ -289,8 +294,8 @@ def backward(dO: torch.Tensor, ctx: Context, d_final_state: Optional[torch.Tenso
     gdt = ctx.q.dtype if grad_dtype is None else grad_dtype
     if gdt != ctx.q.dtype and ctx.w is None:
         raise CplaError(3, "fp32 gradients are available through the weighted backward only")
-    dq = torch.empty(ctx.q.shape, device=dev, dtype=gdt)
-    dk_ = torch.empty(ctx.k.shape, device=dev, dtype=gdt)
+    dq = torch.empty((B, T, H, dk), device=dev, dtype=gdt)
+    dk_ = torch.empty((B, T, H, dk), device=dev, dtype=gdt)
     dv_ = torch.empty(ctx.v.shape, device=dev, dtype=gdt)
     dg = None if ctx.g is None else torch.empty_like(ctx.g)
     dS0 = None
@@ -321,6 +326,8 @@ class ChunkwiseLinearAttention(torch.autograd.Function):
 
     @staticmethod
     def forward(fctx, q, k, v, g, initial_state, num_shards, cu_seqlens):
+        if q.dim() == 4 and v.dim() == 4 and q.shape[2] != v.shape[2]:
+            raise CplaError(2, "the autograd adapter takes q and k per head (their gradients are per head)")
         o, c = forward(q, k, v, g, num_shards=num_shards, initial_state=initial_state, cu_seqlens=cu_seqlens)
         fctx.cpla = c
         return o
@@ -339,9 +346,10 @@ def chunkwise_linear_attention(q, k, v, g=None, initial_state=None, *, num_shard
 
 # ---- Mamba2 (SSD) parametrisation ---------------------------------------------------------
 # Mamba2's selective state space runs through the weighted scalar-decay path:
-# cpla_ssd_inputs writes per-head q = C[group], k = B[group] and g = A dt; the CP
-# calls take v = x and input weights w = dt; cpla_ssd_input_grads takes the
-# gradients back (see include/cpla.h). dx is the dv of the CP backward.
+# cpla_ssd_inputs writes g = A dt; the CP calls read q = C and k = B in place (one
+# head of them per group of heads) and take v = x and input weights w = dt;
+# cpla_ssd_input_grads takes the gradients back (see include/cpla.h). dx is the dv
+# of the CP backward.
 
 @dataclasses.dataclass
 class SsdContext:
@@ -375,13 +383,10 @@ def ssd_forward(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Ten
     _expect("initial_state", initial_state, (Bt, H, N, P), torch.float32, optional=True)
     _expect_gpu("x", dict(x=x, dt=dt, A=A, B=B, C=C, initial_state=initial_state))
     sp = _ssd_problem(x, B)
-    qk_shape = (x.shape[0], x.shape[1], x.shape[2], B.shape[3])
-    q = torch.empty(qk_shape, device=x.device, dtype=x.dtype)
-    k = torch.empty(qk_shape, device=x.device, dtype=x.dtype)
     g = torch.empty(dt.shape, device=x.device, dtype=torch.float32)
-    check(_lib.lib().cpla_ssd_inputs(ctypes.byref(sp), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(q), _ptr(k),
+    check(_lib.lib().cpla_ssd_inputs(ctypes.byref(sp), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), None, None,
                                      _ptr(g), _stream()))
-    y, la = forward(q, k, x, g, num_shards=num_shards, initial_state=initial_state, cu_seqlens=cu_seqlens,
+    y, la = forward(C, B, x, g, num_shards=num_shards, initial_state=initial_state, cu_seqlens=cu_seqlens,
                     packed=packed, w=dt)
     return y, SsdContext(sp, dt, A, la)
 

@@ -58,8 +58,15 @@ cpla_status check_problem(const cpla_problem* p) {
                 (long long)p->dk, bf ? "bf16" : "fp32");
   }
   if (p->B * p->H > 65535) return fail(CPLA_E_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)(p->B * p->H));
+  if (p->qk_heads < 0 || (p->qk_heads > 0 && p->H % p->qk_heads != 0))
+    return fail(CPLA_E_SHAPE, "qk_heads=%d does not divide H=%lld", p->qk_heads, (long long)p->H);
+  if (p->qk_heads > 0 && p->qk_heads != p->H && p->decay != CPLA_DECAY_SCALAR)
+    return fail(CPLA_E_UNSUPPORTED, "q and k shared by groups of heads need a scalar decay");
   return CPLA_OK;
 }
+
+// heads of q and k (qk_heads 0 means one per head)
+int64_t qk_heads_of(const cpla_problem* p) { return p->qk_heads > 0 ? p->qk_heads : p->H; }
 
 cpla_status check_ptr(const void* ptr, const char* name, bool required) {
   if (!ptr) return required ? fail(CPLA_E_INVALID, "%s is NULL", name) : CPLA_OK;
@@ -326,6 +333,7 @@ static cpla_status forward_prepare(const cpla_problem* p, const cpla_packed* pac
   if ((st = check_ptr(fwd_summary, "fwd_summary", true)) != CPLA_OK) return st;
   FwdArgs a = {};
   a.B = p->B; a.T = p->T; a.H = p->H; a.W = cpla_summary_width(p);
+  a.Hqk = qk_heads_of(p); a.qk_div = (int)(p->H / a.Hqk);
   a.P = p->num_shards; a.rank_begin = p->rank_begin; a.m_slot = (int)m_slot_of(p);
   a.k = k; a.v = v; a.g = g; a.w = w;
   a.seq_idx = packed ? packed->seq_idx : nullptr;
@@ -372,6 +380,7 @@ static cpla_status forward_apply(const cpla_problem* p, const cpla_packed* packe
   if (st != CPLA_OK) return st;
   FwdArgs a = {};
   a.B = p->B; a.T = p->T; a.H = p->H; a.W = cpla_summary_width(p);
+  a.Hqk = qk_heads_of(p); a.qk_div = (int)(p->H / a.Hqk);
   a.P = p->num_shards; a.rank_begin = p->rank_begin; a.m_slot = (int)m_slot_of(p);
   a.q = q; a.k = k; a.v = v; a.g = g; a.w = w;
   a.seq_idx = packed ? packed->seq_idx : nullptr;
@@ -505,6 +514,7 @@ extern "C" cpla_status cp_backward_prepare(const cpla_problem* p, const cpla_pac
   if ((st = check_ptr(bwd_summary, "bwd_summary", true)) != CPLA_OK) return st;
   BwdArgs a = {};
   a.B = p->B; a.T = p->T; a.H = p->H; a.W = cpla_summary_width(p);
+  a.Hqk = qk_heads_of(p); a.qk_div = (int)(p->H / a.Hqk);
   a.P = p->num_shards; a.rank_begin = p->rank_begin; a.m_slot = (int)m_slot_of(p);
   a.q = q; a.g = g; a.dO = dO;
   a.seq_idx = packed ? packed->seq_idx : nullptr;
@@ -550,6 +560,7 @@ static cpla_status backward_apply(const cpla_problem* p, const cpla_packed* pack
   if (st != CPLA_OK) return st;
   BwdArgs a = {};
   a.B = p->B; a.T = p->T; a.H = p->H; a.W = cpla_summary_width(p);
+  a.Hqk = qk_heads_of(p); a.qk_div = (int)(p->H / a.Hqk);
   a.P = p->num_shards; a.rank_begin = p->rank_begin; a.m_slot = (int)m_slot_of(p);
   a.q = q; a.k = k; a.v = v; a.g = g; a.w = w; a.dO = dO;
   a.seq_idx = packed ? packed->seq_idx : nullptr;
@@ -604,6 +615,8 @@ cpla_status check_delta(const cpla_problem* p) {
   if (p->rank_begin < 0 || p->rank_end > p->num_shards || p->rank_begin >= p->rank_end)
     return fail(CPLA_E_INVALID, "rank range [%d, %d) outside [0, %d)", p->rank_begin, p->rank_end, p->num_shards);
   if (p->dk != p->dv) return fail(CPLA_E_UNSUPPORTED, "dk != dv unsupported");
+  if (p->qk_heads != 0 && p->qk_heads != p->H)
+    return fail(CPLA_E_UNSUPPORTED, "qk_heads=%d: the delta rule takes q and k per head", p->qk_heads);
   if (!(p->dk == 16 || p->dk == 32 || p->dk == 64))
     return fail(CPLA_E_UNSUPPORTED, "head dim %lld unsupported for the delta rule (16, 32, 64)", (long long)p->dk);
   if (p->B * p->H > 65535) return fail(CPLA_E_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)(p->B * p->H));

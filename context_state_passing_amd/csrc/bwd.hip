@@ -192,6 +192,10 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   __builtin_assume(w >= 0 && w < G::NW);
   const int r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  // head of q and k: a scalar decay (the Mamba2 map) may share them within a group
+  // of heads; the other decays read them per head
+  const int64_t hqk = DECAY == DECAY_SCALAR ? (int64_t)((unsigned)h / (unsigned)a.qk_div) : h;
+  const int64_t Hqk = DECAY == DECAY_SCALAR ? a.Hqk : a.H;
   // packed sequences: row b's sequence ids (one packing per batch row)
   const int32_t* const seq_row = (PK && a.seq_idx) ? a.seq_idx + b * a.T : nullptr;
   // the shard's tokens [tshard, tshard + slen): torch.chunk's division of T into P
@@ -246,14 +250,14 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   using TileV = TileRegs<E, DV, G::NT>;
   float* const pf_g = reinterpret_cast<float*>(s_reg);
   E* const pf_do = s_kl;
-  // raw inputs of the chunk starting at tn, by DMA into the regions above
-  // raw inputs of the chunk starting at tn (n of its tokens inside the shard)
+  // raw inputs of the chunk starting at tn (n of its tokens inside the shard), by
+  // DMA into the regions above
   auto prefetch = [&](int64_t tn, int tid, int n, auto tail) {
     constexpr bool TL = decltype(tail)::value;
     const int wv = wave_id();
     GamR::template dma<TL>(a.g, b, h, tn, a.T, a.H, pf_g, tid, wv, n);
-    TileK::template dma<TL>(q, b, h, tn, a.T, a.H, s_pq, tid, wv, n);
-    TileK::template dma<TL>(k, b, h, tn, a.T, a.H, s_k, tid, wv, n);
+    TileK::template dma<TL>(q, b, hqk, tn, a.T, Hqk, s_pq, tid, wv, n);
+    TileK::template dma<TL>(k, b, hqk, tn, a.T, Hqk, s_k, tid, wv, n);
     TileV::template dma<TL>(v, b, h, tn, a.T, a.H, s_v, tid, wv, n);
     TileV::template dma<TL>(dO, b, h, tn, a.T, a.H, pf_do, tid, wv, n);
   };
@@ -316,9 +320,9 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
       aseg.template load<TAIL>(seq_row, t0, tidf & 63, nv);
       agam.template load<TAIL>(a.g, b, h, t0, a.T, a.H, tidf, nv);
       if constexpr (APPLY) agam.template load_w<TAIL>(a.w, b, h, t0, a.T, a.H, tidf, nv);
-      aq.template load<TAIL>(q, b, h, t0, a.T, a.H, tidf, nv);
+      aq.template load<TAIL>(q, b, hqk, t0, a.T, Hqk, tidf, nv);
       if constexpr (APPLY) {
-        ak.template load<TAIL>(k, b, h, t0, a.T, a.H, tidf, nv);
+        ak.template load<TAIL>(k, b, hqk, t0, a.T, Hqk, tidf, nv);
         av_.template load<TAIL>(v, b, h, t0, a.T, a.H, tidf, nv);
       }
       ado.template load<TAIL>(dO, b, h, t0, a.T, a.H, tidf, nv);

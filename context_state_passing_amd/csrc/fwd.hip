@@ -184,6 +184,10 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
   __builtin_assume(w >= 0 && w < G::NW);
   const int r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  // head of q and k: a scalar decay (the Mamba2 map) may share them within a group
+  // of heads; the other decays read them per head
+  const int64_t hqk = DECAY == DECAY_SCALAR ? (int64_t)((unsigned)h / (unsigned)a.qk_div) : h;
+  const int64_t Hqk = DECAY == DECAY_SCALAR ? a.Hqk : a.H;
   // packed sequences: row b's sequence ids (one packing per batch row)
   const int32_t* const seq_row = (PK && a.seq_idx) ? a.seq_idx + b * a.T : nullptr;
   // the shard's tokens [tshard, tshard + slen): torch.chunk's division of T into P
@@ -228,8 +232,8 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
     rseg.template load<TAIL>(seq_row, t, lane_id(), n);
     rgam.template load<TAIL>(a.g, b, h, t, a.T, a.H, threadIdx.x, n);
     rgam.template load_w<TAIL>(a.w, b, h, t, a.T, a.H, threadIdx.x, n);
-    rk.template load<TAIL>(k, b, h, t, a.T, a.H, threadIdx.x, n);
-    if constexpr (APPLY) rq.template load<TAIL>(q, b, h, t, a.T, a.H, threadIdx.x, n);
+    rk.template load<TAIL>(k, b, hqk, t, a.T, Hqk, threadIdx.x, n);
+    if constexpr (APPLY) rq.template load<TAIL>(q, b, hqk, t, a.T, Hqk, threadIdx.x, n);
     rv.template load<TAIL>(v, b, h, t, a.T, a.H, threadIdx.x, n);
   };
   if constexpr (APPLY) prefetch(0);

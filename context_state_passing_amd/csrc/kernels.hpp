@@ -10,7 +10,8 @@ namespace cpla {
 
 struct FwdArgs {
   int64_t B, T, H, W;        // W: floats per summary record
-  int P, rank_begin, m_slot;
+  int64_t Hqk;               // heads of q and k (H, or G: head h reads head h / qk_div)
+  int P, rank_begin, m_slot, qk_div;
   const void* q;
   const void* k;
   const void* v;
@@ -25,7 +26,8 @@ struct FwdArgs {
 
 struct BwdArgs {
   int64_t B, T, H, W;
-  int P, rank_begin, m_slot;
+  int64_t Hqk;               // heads of q and k (as in FwdArgs); dq and dk are per head
+  int P, rank_begin, m_slot, qk_div;
   const void* q;
   const void* k;
   const void* v;

@@ -12,8 +12,10 @@
 // under the map, for head h of group gr = h / (H / G):
 //   q[b,t,h,:] = C[b,t,gr,:]   k[b,t,h,:] = B[b,t,gr,:]   v = x   w = dt   g[b,t,h] = A[h] dt[b,t,h]
 // (dt enters as the fp32 weight, so nothing is rounded on the way in).
-// ssd_inputs writes q, k, g; ssd_grads and ssd_dA take the fp32 gradients of the
-// weighted backward (dq, dk, dv, dg, dw) back to x, dt, A, B and C:
+// ssd_inputs writes g (and, if asked, per-head copies q, k; the walks can read B
+// and C in place through the problem's qk_heads = G); ssd_grads and ssd_dA take
+// the fp32 gradients of the weighted backward (dq, dk, dv, dg, dw) back to x, dt,
+// A, B and C:
 //   dx = dv,   d_dt = dw + A dg,   dA_h = sum_{b,t} dt dg,
 //   dB[gr] = sum_{h in gr} dk,   dC[gr] = sum_{h in gr} dq
 // (the head sums in fp32, each output rounded once).
@@ -69,7 +71,14 @@ __device__ __forceinline__ void cp4(float* d, const float* s) {
   *reinterpret_cast<f32x4*>(d) = *reinterpret_cast<const f32x4*>(s);
 }
 
-// One thread per (b, t, h, four features).
+// One thread per (b, t, h): g only (the walks read B and C in place).
+__global__ __launch_bounds__(256) void ssd_decay(SsdArgs a) {
+  const int64_t bth = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (bth >= a.B * a.T * a.H) return;
+  a.g[bth] = a.A[bth % a.H] * a.dt[bth];
+}
+
+// One thread per (b, t, h, four features): g and the per-head copies of B and C.
 template <typename E>
 __global__ __launch_bounds__(256) void ssd_inputs(SsdArgs a) {
   const int64_t nv = a.N / 4;
@@ -172,16 +181,22 @@ extern "C" cpla_status cpla_ssd_inputs(const cpla_ssd_problem* p, const float* d
   clear_error();
   cpla_status st = check_ssd(p);
   if (st != CPLA_OK) return st;
-  const void* in[] = {dt, A, Bm, Cm, q, k, g};
-  const char* nm[] = {"dt", "A", "B", "C", "q", "k", "g"};
-  for (int i = 0; i < 7; ++i)
+  if (!q != !k) return fail(CPLA_E_INVALID, "q and k must both be NULL (B and C read in place) or both given");
+  const bool copies = q != nullptr;
+  const void* in[] = {dt, A, g, Bm, Cm, q, k};
+  const char* nm[] = {"dt", "A", "g", "B", "C", "q", "k"};
+  for (int i = 0; i < (copies ? 7 : 3); ++i)
     if ((st = ptr_ok(in[i], nm[i])) != CPLA_OK) return st;
   SsdArgs a{};
   a.B = p->B; a.T = p->T; a.H = p->H; a.G = p->G; a.N = p->N; a.P = p->P;
   a.dt = dt; a.A = A; a.Bm = Bm; a.Cm = Cm; a.q = q; a.k = k; a.g = g;
-  const unsigned nb = blocks_for(p->B * p->T * p->H * (p->N / 4));
-  if (p->dtype == CPLA_BF16) hipLaunchKernelGGL(ssd_inputs<bf16_t>, dim3(nb), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(ssd_inputs<float>, dim3(nb), dim3(256), 0, stream, a);
+  if (!copies) {
+    hipLaunchKernelGGL(ssd_decay, dim3(blocks_for(p->B * p->T * p->H)), dim3(256), 0, stream, a);
+  } else {
+    const unsigned nb = blocks_for(p->B * p->T * p->H * (p->N / 4));
+    if (p->dtype == CPLA_BF16) hipLaunchKernelGGL(ssd_inputs<bf16_t>, dim3(nb), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(ssd_inputs<float>, dim3(nb), dim3(256), 0, stream, a);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(CPLA_E_HIP, "ssd_inputs launch: %s", hipGetErrorString(e));
   return CPLA_OK;

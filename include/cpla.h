@@ -73,7 +73,7 @@ extern "C" {
 
 typedef struct ihipStream_t* hipStream_t;
 
-#define CPLA_ABI_VERSION 5
+#define CPLA_ABI_VERSION 6
 
 /* Lower bound of the running log-decay within a 64-token chunk, per key dim, that
  * the diagonal-decay kernels support (see the layout notes above). */
@@ -108,6 +108,13 @@ typedef struct {
   int32_t rank_end;          /*   (0 and P on one GPU)                                  */
   int32_t dtype;             /* cpla_dtype of q, k, v, o, dO, dq, dk, dv                */
   int32_t decay;             /* cpla_decay                                              */
+  int32_t qk_heads;          /* heads of q and k: 0 (or H) = one per head; G with
+                                H % G == 0 = q and k are [B,T,G,dk] and head h reads
+                                their head h / (H / G) (Mamba2's B and C, shared by a
+                                group of heads). dq and dk stay per head [B,T,H,dk]
+                                (a group's sum is the gradient of the shared tensor).
+                                Scalar decay only (the others and the _delta calls take
+                                0 or H)                                                */
 } cpla_problem;
 
 /* Packed sequences. Passing NULL for the whole struct means "not packed": every
@@ -319,8 +326,10 @@ cpla_status cp_backward_apply_delta(const cpla_problem* p, const cpla_packed* pa
  *   h_t = exp(dt_t A_h) h_{t-1} + dt_t B_t x_t^T   (state N x P),   y_t = h_t^T C_t
  * is the weighted scalar-decay recurrence above with q = C[gr], k = B[gr], v = x,
  * g = A dt and w = dt: run cpla_ssd_inputs, the weighted cp_* calls (and
- * cp_backward_prepare) with v = x and w = dt, then cpla_ssd_input_grads.
- * Shapes: q, k [B,T,H,N], x and y [B,T,H,P], B, C [B,T,G,N] in `dtype`; dt, g
+ * cp_backward_prepare) with q = C, k = B, qk_heads = G, v = x and w = dt, then
+ * cpla_ssd_input_grads (run with per-head copies q, k and qk_heads = 0 instead,
+ * they give the same results).
+ * Shapes: x and y [B,T,H,P], B, C [B,T,G,N] in `dtype` (copies q, k [B,T,H,N]); dt, g
  * [B,T,H] and A [H] fp32 (dt already positive: any softplus or bias is the
  * caller's); the state is N x P per head, so the cp_* calls run with dk = N and
  * dv = P (bf16: N = P in {16, 64, 128} or (N, P) = (64, 128), (128, 64); fp32:
@@ -336,7 +345,9 @@ typedef struct {
   int32_t dtype;             /* cpla_dtype of x, B, C, q, k, dx, dB, dC                */
 } cpla_ssd_problem;
 
-/* q[b,t,h] = C[b,t,gr], k[b,t,h] = B[b,t,gr] (copies) and g = A dt (fp32). */
+/* g = A dt (fp32), and, when q and k are both non-NULL, per-head copies
+ * q[b,t,h] = C[b,t,gr], k[b,t,h] = B[b,t,gr]. With both NULL the cp_* calls read B
+ * and C in place: pass k = B, q = C and cpla_problem.qk_heads = G. */
 cpla_status cpla_ssd_inputs(const cpla_ssd_problem* p, const float* dt, const float* A,
                             const void* B, const void* C, void* q, void* k, float* g,
                             hipStream_t stream);

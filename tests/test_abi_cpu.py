@@ -77,7 +77,7 @@ def test_apply_parts_knob():
 
 
 def test_abi_version():
-    assert L.cpla_abi_version() == 5
+    assert L.cpla_abi_version() == 6
 
 
 def prob(**kw):
@@ -101,6 +101,8 @@ def fwd_prepare(p, k=FAKE, v=FAKE, g=FAKE, out=FAKE, packed=None):
     (dict(rank_begin=2, rank_end=2), 1), (dict(rank_end=5), 1), (dict(dv=32), 5), (dict(dk=32, dv=32), 5),
     (dict(dk=64, dv=16), 5), (dict(dk=64, dv=128, dtype=_lib.F32), 5), (dict(dk=16, dv=128), 5),
     (dict(dtype=_lib.F32), 5), (dict(num_shards=0), 2),
+    (dict(qk_heads=3), 2), (dict(qk_heads=-1), 2),     # q, k heads must divide H
+    (dict(qk_heads=1, decay=_lib.DECAY_DIAG), 5), (dict(qk_heads=1, decay=_lib.DECAY_NONE), 5),   # scalar only
 ])
 def test_problem_validation(kw, status):
     assert fwd_prepare(prob(**kw)) == status
@@ -279,7 +281,7 @@ def test_delta_validation():
     assert L.cpla_delta_workspace_bytes(ctypes.byref(p)) == 4 * (4 * tok + 2 * 1 * 2 * nct * 64 * 64)
     assert L.cpla_summary_width(ctypes.byref(p)) == 2 * 64 * 64
     for bad in [dict(dk=128, dv=128), dict(dk=64, dv=32), dict(decay=_lib.DECAY_DIAG), dict(chunk=32),
-                dict(num_shards=65, rank_end=65)]:
+                dict(num_shards=65, rank_end=65), dict(qk_heads=1)]:
         base = dict(dk=64, dv=64, dtype=_lib.F32, decay=_lib.DECAY_DELTA)
         base.update(bad)
         q = prob(**base)
@@ -315,3 +317,7 @@ def test_ssd_pointer_validation():
     p = ssd_prob()
     assert L.cpla_ssd_inputs(ctypes.byref(p), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert L.cpla_ssd_inputs(ctypes.byref(p), FAKE, FAKE, FAKE, MISALIGNED, FAKE, FAKE, FAKE, None) == 4
+    # per-head copies q, k: both or neither; without them B and C are not read here
+    assert L.cpla_ssd_inputs(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == 1
+    assert L.cpla_ssd_inputs(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, None, None, None) == 1   # g
+    assert L.cpla_ssd_inputs(ctypes.byref(p), None, FAKE, FAKE, FAKE, None, None, FAKE, None) == 1   # dt
