@@ -44,7 +44,8 @@ cpla_status check_problem(const cpla_problem* p) {
   if (p->chunk != 64) return fail(CPLA_E_UNSUPPORTED, "chunk %d unsupported (64 only)", p->chunk);
   if (p->num_shards <= 0) return fail(CPLA_E_SHAPE, "num_shards must be positive");
   // any T and num_shards: torch.chunk's division (shards.hpp), partial last chunks
-  if (p->num_shards > 64) return fail(CPLA_E_UNSUPPORTED, "num_shards=%d > 64 unsupported", p->num_shards);
+  if (p->num_shards > CPLA_MAX_SHARDS)
+    return fail(CPLA_E_UNSUPPORTED, "num_shards=%d > %d unsupported", p->num_shards, CPLA_MAX_SHARDS);
   if (p->rank_begin < 0 || p->rank_end > p->num_shards || p->rank_begin >= p->rank_end)
     return fail(CPLA_E_INVALID, "rank range [%d, %d) outside [0, %d)", p->rank_begin, p->rank_end, p->num_shards);
   const bool bf = p->dtype == CPLA_BF16;
@@ -611,7 +612,8 @@ cpla_status check_delta(const cpla_problem* p) {
   if (p->decay != CPLA_DECAY_DELTA) return fail(CPLA_E_INVALID, "the _delta calls need decay CPLA_DECAY_DELTA");
   if (p->chunk != 64) return fail(CPLA_E_UNSUPPORTED, "chunk %d unsupported (64 only)", p->chunk);
   if (p->num_shards <= 0) return fail(CPLA_E_SHAPE, "num_shards must be positive");
-  if (p->num_shards > 64) return fail(CPLA_E_UNSUPPORTED, "num_shards=%d > 64 unsupported", p->num_shards);
+  if (p->num_shards > CPLA_MAX_SHARDS)
+    return fail(CPLA_E_UNSUPPORTED, "num_shards=%d > %d unsupported", p->num_shards, CPLA_MAX_SHARDS);
   if (p->rank_begin < 0 || p->rank_end > p->num_shards || p->rank_begin >= p->rank_end)
     return fail(CPLA_E_INVALID, "rank range [%d, %d) outside [0, %d)", p->rank_begin, p->rank_end, p->num_shards);
   if (p->dk != p->dv) return fail(CPLA_E_UNSUPPORTED, "dk != dv unsupported");

@@ -261,6 +261,7 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     else x = (m == D + d) ? 1.f : 0.f;
     s_z[d * LZ + m] = x;
   }
+  __syncthreads();   // an empty shard writes its record from s_z right away
   for (int c = 0; c < nc; ++c) {
     const int64_t t0 = tshard + 64 * c;
     const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
@@ -448,6 +449,7 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
   const int w = threadIdx.x >> 6, l = lane_id();
   for (int e = threadIdx.x; e < D * D; e += NTH)
     s_ds[(e / D) * G::LD + e % D] = APPLY ? a.state_in[(r * a.B * a.H + bh) * (int64_t)(D * D) + e] : 0.f;
+  __syncthreads();   // an empty shard writes its record from s_ds right away
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t t0 = tshard + 64 * c;
     const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);

@@ -75,6 +75,9 @@ typedef struct ihipStream_t* hipStream_t;
 
 #define CPLA_ABI_VERSION 6
 
+/* Largest cpla_problem.num_shards the calls accept. */
+#define CPLA_MAX_SHARDS 1024
+
 /* Lower bound of the running log-decay within a 64-token chunk, per key dim, that
  * the diagonal-decay kernels support (see the layout notes above). */
 #define CPLA_DIAG_GAMMA_MIN (-80.0f)
@@ -99,7 +102,7 @@ typedef struct {
                                 tokens with its own packing. Head dims: dk == dv in
                                 {16, 64, 128} (bf16) or {16, 64} (fp32); dk != dv:
                                 bf16 (64, 128) or (128, 64); others CPLA_E_UNSUPPORTED */
-  int32_t num_shards;        /* P <= 64 shards of any T: torch.chunk's division (shard
+  int32_t num_shards;        /* P <= 1024 shards of any T: torch.chunk's division (shard
                                 size ceil(T/P), the last non-empty shard shorter, trailing
                                 shards empty when T is short; a shard's last chunk may be
                                 partial), the graceful division the mixle page relies on */

@@ -97,7 +97,7 @@ def fwd_prepare(p, k=FAKE, v=FAKE, g=FAKE, out=FAKE, packed=None):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(B=0), 2), (dict(dtype=7), 3), (dict(decay=5), 1), (dict(chunk=32), 5), (dict(T=0), 2),
-    (dict(T=64 * 65, num_shards=65), 5),
+    (dict(T=64 * 1025, num_shards=1025), 5),
     (dict(rank_begin=2, rank_end=2), 1), (dict(rank_end=5), 1), (dict(dv=32), 5), (dict(dk=32, dv=32), 5),
     (dict(dk=64, dv=16), 5), (dict(dk=64, dv=128, dtype=_lib.F32), 5), (dict(dk=16, dv=128), 5),
     (dict(dtype=_lib.F32), 5), (dict(num_shards=0), 2),
@@ -281,7 +281,7 @@ def test_delta_validation():
     assert L.cpla_delta_workspace_bytes(ctypes.byref(p)) == 4 * (4 * tok + 2 * 1 * 2 * nct * 64 * 64)
     assert L.cpla_summary_width(ctypes.byref(p)) == 2 * 64 * 64
     for bad in [dict(dk=128, dv=128), dict(dk=64, dv=32), dict(decay=_lib.DECAY_DIAG), dict(chunk=32),
-                dict(num_shards=65, rank_end=65), dict(qk_heads=1)]:
+                dict(num_shards=1025, rank_end=1025), dict(qk_heads=1)]:
         base = dict(dk=64, dv=64, dtype=_lib.F32, decay=_lib.DECAY_DELTA)
         base.update(bad)
         q = prob(**base)

@@ -30,6 +30,7 @@ CASES = {
     "bf16_d64": dict(B=2, T=1024, H=2, d=64, num_shards=4),
     "fp32_d64_uneven": dict(B=1, T=500, H=2, d=64, num_shards=3, dtype=torch.float32),
     "fp32_d32_empty_shards": dict(B=1, T=200, H=1, d=32, num_shards=64, dtype=torch.float32),
+    "fp32_d16_many_shards": dict(B=1, T=2000, H=1, d=16, num_shards=300, dtype=torch.float32),
     "fp32_d64_packed": dict(B=1, T=768, H=2, d=64, num_shards=4, packed=True, len_range=(30, 300),
                             dtype=torch.float32),
     "bf16_d64_rows_packed": dict(B=2, T=640, H=2, d=64, num_shards=5, packed=True, len_range=(1, 200)),

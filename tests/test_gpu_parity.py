@@ -55,7 +55,7 @@ SMALL = {
     "single_shard_bwd": ("diag_fwdbwd", {"B": 1, "H": 1, "T": 256, "num_shards": 1}, True),
     "scalar_d16_bf16_bwd": ("scalar_fwd", {"B": 1, "H": 2, "T": 512, "d": 16, "num_shards": 2,
                                            "backward": True}, True),
-    # edge cases: one chunk per shard; the largest shard count; no decay at d=128 bf16;
+    # edge cases: one chunk per shard; 64 shards; no decay at d=128 bf16;
     # diagonal decay at d=16 in both dtypes; many (b, h) rows
     "one_chunk_shards_bwd": ("diag_fwdbwd", {"B": 1, "H": 2, "T": 256, "num_shards": 4}, True),
     "max_shards_bwd": ("scalar_fwd", {"B": 1, "H": 1, "T": 4096, "d": 16, "num_shards": 64,
@@ -84,6 +84,15 @@ SMALL = {
     "uneven_subchunk_shards_bwd": ("diag_fwdbwd", {"B": 1, "H": 1, "T": 1000, "num_shards": 16}, True),
     "uneven_empty_shards_bwd": ("scalar_fwd", {"B": 1, "H": 2, "T": 200, "num_shards": 64, "backward": True,
                                                "decay_scale": 1e-2}, True),
+    # many shards: 256 of one chunk each; 200 uneven shards over packed sequences
+    # with the diagonal decay; the largest count, 1024 shards of 2 tokens
+    "many_shards_bwd": ("scalar_fwd", {"B": 1, "H": 2, "T": 16384, "d": 16, "num_shards": 256,
+                                       "backward": True, "decay_scale": 1e-2}, True),
+    "many_shards_packed_diag_bwd": ("diag_fwdbwd", {"B": 1, "H": 1, "T": 6000, "d": 64, "num_shards": 200,
+                                                    "packed": True, "len_range": (30, 900),
+                                                    "decay_scale": 1e-2}, True),
+    "max_shards_1024_bwd": ("scalar_fwd", {"B": 1, "H": 1, "T": 2048, "d": 16, "num_shards": 1024,
+                                           "backward": True, "decay_scale": 1e-3}, True),
     "tail_identity_fp32_bwd": ("identity_fwd", {"T": 100, "num_shards": 1, "backward": True}, True),
     "uneven_packed_bwd": ("packed_fwdbwd", {"T": 1000, "H": 2, "num_shards": 7, "len_range": (40, 300)}, True),
     "uneven_diag_d64_bwd": ("diag_fwdbwd", {"B": 2, "H": 1, "T": 450, "d": 64, "num_shards": 2}, True),
