@@ -17,7 +17,7 @@
 //
 // Kernels (one workgroup of eight waves each; every contraction is fp32 MFMA
 // 16x16x4 on fp32 LDS tiles, inputs widened on load):
-//   delta_wy      per chunk:  U~, W (triangular solve, one column per thread)
+//   delta_wy      per chunk:  U~, W ((I + A)^{-1} by 16 x 16 blocks, then MFMA products)
 //   delta_fwalk   per shard:  chunk walk of the state; prepare folds [delta_S | M]
 //                             from [0 | I], apply saves chunk states and U
 //   delta_scan    per (b,h):  composition S <- M S + delta_S over shards (or its
@@ -171,6 +171,54 @@ __device__ __forceinline__ void chunk_of(int64_t T, int P, int64_t idx, int64_t&
   c = idx % nsc;
 }
 
+// T = (I + A)^{-1} in place of a strictly lower-triangular [64][64] tile A (row
+// stride CH + 4), by 16 x 16 blocks: the unit lower-triangular diagonal blocks by
+// substitution, one lane of wave 0 per column (the column in registers), then the
+// blocks below them block row by block row,
+//   T_ij = -T_ii sum_{j <= k < i} A_ik T_kj,
+// one 16 x 16 output tile per wave (an MFMA accumulator tile is laid out as the
+// second operand of the next product, so -T_ii Y is formed from registers). Every
+// thread of the workgroup calls it; it ends with a barrier.
+__device__ __forceinline__ void unit_lower_inverse(float* s_a) {
+  constexpr int LC = CH + 4;
+  const int w = threadIdx.x >> 6, l = lane_id(), x = l & 15, kg = l >> 4;
+  if (w == 0) {
+    const int bi = kg, c = x;
+    const float* ab = s_a + 16 * bi * LC + 16 * bi;
+    float t[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = r == c ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < r; ++j) v -= ab[r * LC + j] * t[j];
+      t[r] = v;
+    }
+    asm volatile("" ::: "memory");   // the wave's reads of its blocks precede these writes
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s_a[(16 * bi + r) * LC + 16 * bi + c] = t[r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 1; i < 4; ++i) {
+    f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    const int j = w;
+    if (j < i) {
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      for (int k = j; k < i; ++k)
+        y = tile_mm<16>([&](int r, int q) { return s_a[(16 * i + r) * LC + 16 * k + q]; },
+                        [&](int q, int cc) { return s_a[(16 * k + q) * LC + 16 * j + cc]; }, y);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) z = mfma_f32(s_a[(16 * i + x) * LC + 16 * i + 4 * kg + st], y[st], z);
+    }
+    __syncthreads();   // block row i of A is read
+    if (j < i) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s_a[(16 * i + 4 * kg + q) * LC + 16 * j + x] = -z[q];
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace
 
 // ---- U~ and W per chunk ------------------------------------------------------------------
@@ -209,29 +257,31 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
   }
   __syncthreads();
 
-  // forward substitution (I + A) X = [beta V | beta live e^Gam K] in place in the
-  // LDS tiles (a register-resident column made the compiler hold the hoisted rows
-  // of A in every register and spill): four lanes per column, each summing every
-  // fourth earlier row; lane 0 of the four updates the row. The lanes of a column
-  // sit in one wave, whose LDS accesses complete in order.
-  const int col = 16 * (threadIdx.x >> 6) + (lane_id() >> 2), part = lane_id() & 3;
-  if (col < 2 * D) {   // uniform per wave
-    const bool isv = col < D;
-    const int cc = isv ? col : col - D;
-    float* xc = (isv ? s_v : s_k) + cc;
-    for (int i = part; i < CH; i += 4) xc[i * G::LD] *= isv ? s_t.beta[i] : s_t.beta[i] * s_t.eg[i];
-    asm volatile("" ::: "memory");
-    for (int i = 1; i < CH; ++i) {
-      const float* ai = s_a + i * G::LC;
-      float acc = 0.f;
-      for (int j = part; j < i; j += 4) acc += ai[j] * xc[j * G::LD];
-      acc += __shfl_xor(acc, 1, 64);
-      acc += __shfl_xor(acc, 2, 64);
-      if (part == 0) xc[i * G::LD] -= acc;
-      asm volatile("" ::: "memory");   // later rows re-read what lane 0 wrote
+  // [U~ | W] = (I + A)^{-1} [beta V | beta live e^Gam K]: T = (I + A)^{-1} in place of
+  // A, then the products T R by 16 x 16 tiles (T lower triangular: row tile ti
+  // takes k tiles 0..ti), written straight to the workspace
+  unit_lower_inverse(s_a);
+  {
+    constexpr int NCT = 2 * D / 16, NT_ = 4 * NCT;
+    for (int t = w; t < NT_; t += NWV) {
+      const int ti = t / NCT, tj = t % NCT;
+      const bool isv = tj < NCT / 2;
+      const float* src = isv ? s_v : s_k;
+      const int c0 = 16 * (isv ? tj : tj - NCT / 2);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kt = 0; kt <= ti; ++kt)
+        acc = tile_mm<16>([&](int i, int q) { return s_a[(16 * ti + i) * G::LC + 16 * kt + q]; },
+                          [&](int q, int j) {
+                            const int k = 16 * kt + q;
+                            return src[k * G::LD + c0 + j] * (isv ? s_t.beta[k] : s_t.beta[k] * s_t.eg[k]);
+                          }, acc);
+      float* dst = isv ? a.ws_ut : a.ws_w;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * ti + 4 * (l >> 4) + q;
+        if (i < n) dst[((b * a.T + t0 + i) * a.H + h) * D + c0 + (l & 15)] = acc[q];
+      }
     }
-    float* dst = isv ? a.ws_ut : a.ws_w;
-    for (int i = part; i < n; i += 4) dst[((b * a.T + t0 + i) * a.H + h) * D + cc] = xc[i * G::LD];
   }
 }
 
@@ -701,21 +751,38 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     }
   }
   __syncthreads();
-  // backward substitution (I + A)^T dB = [dU | dW] in place, four lanes per column
-  // as in the forward solve
+  // [dBv | dBk] = (I + A)^{-T} [dU | dW] in place: T = (I + A)^{-1} in place of A (dead
+  // after this), then T^T R by 16 x 16 tiles (row tile ti takes k tiles ti..3),
+  // held in registers until every wave has read R
+  unit_lower_inverse(s_a);
   {
-    const int col = 16 * w + (l >> 2), part = l & 3;
-    if (col < 2 * D) {
-      const bool isv = col < D;
-      float* xc = (isv ? s_dU : s_dW) + (isv ? col : col - D);
-      for (int i = CH - 2; i >= 0; --i) {
-        float acc = 0.f;
-        for (int j = i + 1 + part; j < CH; j += 4) acc += s_a[j * G::LC + i] * xc[j * G::LD];
-        acc += __shfl_xor(acc, 1, 64);
-        acc += __shfl_xor(acc, 2, 64);
-        if (part == 0) xc[i * G::LD] -= acc;
-        asm volatile("" ::: "memory");
-      }
+    constexpr int NCT = 2 * D / 16, NT_ = 4 * NCT, PW = (NT_ + NWV - 1) / NWV;
+    f32x4 res[PW];
+#pragma unroll
+    for (int m = 0; m < PW; ++m) {
+      const int t = w + NWV * m;
+      if (t >= NT_) continue;
+      const int ti = t / NCT, tj = t % NCT;
+      const bool isv = tj < NCT / 2;
+      const float* src = isv ? s_dU : s_dW;
+      const int c0 = 16 * (isv ? tj : tj - NCT / 2);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kt = ti; kt < 4; ++kt)
+        acc = tile_mm<16>([&](int i, int q) { return s_a[(16 * kt + q) * G::LC + 16 * ti + i]; },
+                          [&](int q, int j) { return src[(16 * kt + q) * G::LD + c0 + j]; }, acc);
+      res[m] = acc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < PW; ++m) {
+      const int t = w + NWV * m;
+      if (t >= NT_) continue;
+      const int ti = t / NCT, tj = t % NCT;
+      const bool isv = tj < NCT / 2;
+      float* dst = isv ? s_dU : s_dW;
+      const int c0 = 16 * (isv ? tj : tj - NCT / 2);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[(16 * ti + 4 * (l >> 4) + q) * G::LD + c0 + (l & 15)] = res[m][q];
     }
   }
   __syncthreads();
