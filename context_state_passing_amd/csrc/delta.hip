@@ -69,26 +69,70 @@ template <int D> struct DGeo {
   static constexpr int TILE_C = CH * LC;      // floats of a [64][64] tile
 };
 
-__device__ __forceinline__ float to_f32(float x) { return x; }
-__device__ __forceinline__ float to_f32(bf16_t x) { return (float)x; }
+
+// Input tiles staged through registers: fetch() issues a thread's global loads
+// (four elements each, in the input type), put() writes them widened to fp32 into
+// an LDS tile. Fetching several tiles before putting any keeps all their loads in
+// flight at once, and a walk fetches its next chunk while it computes the current
+// one.
+template <typename E> struct Raw4 { typedef f32x4 type; };
+template <> struct Raw4<bf16_t> { typedef bf16x4 type; };
+__device__ __forceinline__ f32x4 widen4(const f32x4& x) { return x; }
+__device__ __forceinline__ f32x4 widen4(const bf16x4& x) {
+  return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+}
+
+// [64][D] rows t0 .. t0 + 63 of a [B,T,H,D] tensor; rows past n read as zero
+template <typename E, int D> struct RowTile {
+  static constexpr int NV = CH * D / 4, PER = (NV + NTH - 1) / NTH;
+  typedef typename Raw4<E>::type R;
+  R v[PER];
+  __device__ __forceinline__ void fetch(const E* src, int64_t b, int64_t h, int64_t t0, int n, int64_t T,
+                                        int64_t H) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = threadIdx.x + p * NTH, i = e / (D / 4), c = 4 * (e % (D / 4));
+      v[p] = R{0, 0, 0, 0};
+      if ((NV % NTH == 0 || e < NV) && i < n) v[p] = *reinterpret_cast<const R*>(src + ((b * T + t0 + i) * H + h) * D + c);
+    }
+  }
+  __device__ __forceinline__ void put(float* dst, int ld = DGeo<D>::LD) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = threadIdx.x + p * NTH, i = e / (D / 4), c = 4 * (e % (D / 4));
+      if (NV % NTH == 0 || e < NV) *reinterpret_cast<f32x4*>(dst + i * ld + c) = widen4(v[p]);
+    }
+  }
+};
+
+// a row-major [D][D] fp32 matrix
+template <int D> struct MatTile {
+  static constexpr int NV = D * D / 4, PER = (NV + NTH - 1) / NTH;
+  f32x4 v[PER];
+  __device__ __forceinline__ void fetch(const float* src) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = threadIdx.x + p * NTH;
+      if (NV % NTH == 0 || e < NV) v[p] = *reinterpret_cast<const f32x4*>(src + 4 * e);
+    }
+  }
+  __device__ __forceinline__ void put(float* dst) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = threadIdx.x + p * NTH, i = e / (D / 4), c = 4 * (e % (D / 4));
+      if (NV % NTH == 0 || e < NV) *reinterpret_cast<f32x4*>(dst + i * DGeo<D>::LD + c) = v[p];
+    }
+  }
+};
 
 // [64][D] rows t0 .. t0 + 63 of a [B,T,H,D] tensor into an fp32 LDS tile; rows
 // past n read as zero.
 template <typename E, int D>
 __device__ __forceinline__ void load_rows(float* dst, const E* src, int64_t b, int64_t h, int64_t t0, int n,
                                           int64_t T, int64_t H) {
-  using G = DGeo<D>;
-  constexpr int PER_ROW = D / 4;
-  for (int e = threadIdx.x; e < CH * PER_ROW; e += NTH) {
-    const int i = e / PER_ROW, c = 4 * (e % PER_ROW);
-    f32x4 x = {0.f, 0.f, 0.f, 0.f};
-    if (i < n) {
-      const E* p = src + ((b * T + t0 + i) * H + h) * D + c;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = to_f32(p[u]);
-    }
-    *reinterpret_cast<f32x4*>(dst + i * G::LD + c) = x;
-  }
+  RowTile<E, D> t;
+  t.fetch(src, b, h, t0, n, T, H);
+  t.put(dst);
 }
 
 // rows i < n of an fp32 LDS tile into a [B,T,H,D] tensor of type E
@@ -109,10 +153,9 @@ __device__ __forceinline__ void store_rows(E* dst, const float* src, int64_t b, 
 // a [D][D] fp32 matrix between global (row-major) and an LDS tile
 template <int D>
 __device__ __forceinline__ void load_mat(float* dst, const float* src) {
-  for (int e = threadIdx.x; e < D * D / 4; e += NTH) {
-    const int i = e / (D / 4), c = 4 * (e % (D / 4));
-    *reinterpret_cast<f32x4*>(dst + i * DGeo<D>::LD + c) = *reinterpret_cast<const f32x4*>(src + i * D + c);
-  }
+  MatTile<D> t;
+  t.fetch(src);
+  t.put(dst);
 }
 template <int D>
 __device__ __forceinline__ void store_mat(float* dst, const float* src) {
@@ -236,9 +279,15 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
   if (r >= a.P || n <= 0) return;
   const int64_t t0 = shard_begin(a.T, a.P, r) + 64 * c;
   const int32_t* seq = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
-  load_rows<E, D>(s_k, reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
-  load_rows<E, D>(s_v, reinterpret_cast<const E*>(a.v), b, h, t0, n, a.T, a.H);
-  chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+  {
+    RowTile<E, D> rk, rv;
+    rk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+    rv.fetch(reinterpret_cast<const E*>(a.v), b, h, t0, n, a.T, a.H);
+    chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    rk.put(s_k);
+    rv.put(s_v);
+  }
+  __syncthreads();
 
   // A = strict-lower(beta_i D_ij k_i.k_j)
   const int w = threadIdx.x >> 6, l = lane_id();
@@ -312,17 +361,30 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     s_z[d * LZ + m] = x;
   }
   __syncthreads();   // an empty shard writes its record from s_z right away
+  // each chunk's W, k and U~ are fetched into registers while the chunk before it
+  // is being computed
+  RowTile<float, D> pw, pu;
+  RowTile<E, D> pk;
+  auto fetch_chunk = [&](int c) {
+    const int64_t t0 = tshard + 64 * c;
+    const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
+    pw.fetch(a.ws_w, b, h, t0, n, a.T, a.H);
+    pk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+    pu.fetch(a.ws_ut, b, h, t0, n, a.T, a.H);
+  };
+  if (nc > 0) fetch_chunk(0);
   for (int c = 0; c < nc; ++c) {
     const int64_t t0 = tshard + 64 * c;
     const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
-    load_rows<float, D>(s_w, a.ws_w, b, h, t0, n, a.T, a.H);
-    load_rows<E, D>(s_k, reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+    pw.put(s_w);
+    pk.put(s_k);
     // U~ into the first D columns of s_u (the M part takes no input)
-    for (int e = threadIdx.x; e < CH * NZ; e += NTH) {
-      const int i = e / NZ, m = e % NZ;
-      s_u[i * LZ + m] = (m < D && i < n) ? a.ws_ut[((b * a.T + t0 + i) * a.H + h) * D + m] : 0.f;
+    pu.put(s_u, LZ);
+    if constexpr (NZ > D) {
+      for (int e = threadIdx.x; e < CH * (NZ - D); e += NTH) s_u[(e / (NZ - D)) * LZ + D + e % (NZ - D)] = 0.f;
     }
     chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    if (c + 1 < nc) fetch_chunk(c + 1);
     if constexpr (APPLY) {
       float* cs = a.chunk_states + (bh * nct + cbase + c) * (int64_t)(D * D);
       for (int e = threadIdx.x; e < D * D; e += NTH) cs[e] = s_z[(e / D) * LZ + e % D];
@@ -446,11 +508,21 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
   const int64_t nct = row_chunks(a.T, a.P);
   const int32_t* seq = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
   const int w = threadIdx.x >> 6, l = lane_id();
-  load_rows<E, D>(s_q, reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
-  load_rows<E, D>(s_k, reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
-  load_rows<float, D>(s_u, a.ws_u, b, h, t0, n, a.T, a.H);
-  load_mat<D>(s_s, a.chunk_states + (bh * nct + idx) * (int64_t)(D * D));
-  chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+  {
+    RowTile<E, D> rq, rk;
+    RowTile<float, D> ru;
+    MatTile<D> rs;
+    rq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
+    rk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+    ru.fetch(a.ws_u, b, h, t0, n, a.T, a.H);
+    rs.fetch(a.chunk_states + (bh * nct + idx) * (int64_t)(D * D));
+    chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    rq.put(s_q);
+    rk.put(s_k);
+    ru.put(s_u);
+    rs.put(s_s);
+  }
+  __syncthreads();
   for (int t = w; t < 16; t += NWV) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -500,14 +572,28 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
   for (int e = threadIdx.x; e < D * D; e += NTH)
     s_ds[(e / D) * G::LD + e % D] = APPLY ? a.state_in[(r * a.B * a.H + bh) * (int64_t)(D * D) + e] : 0.f;
   __syncthreads();   // an empty shard writes its record from s_ds right away
+  // each chunk's q, k, dO and W are fetched into registers while the chunk after
+  // it (the walk runs backwards) is being computed
+  RowTile<E, D> pq, pk, pdo;
+  RowTile<float, D> pw;
+  auto fetch_chunk = [&](int c) {
+    const int64_t t0 = tshard + 64 * c;
+    const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
+    pq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
+    pk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+    pdo.fetch(reinterpret_cast<const E*>(a.dO), b, h, t0, n, a.T, a.H);
+    pw.fetch(a.ws_w, b, h, t0, n, a.T, a.H);
+  };
+  if (nc > 0) fetch_chunk(nc - 1);
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t t0 = tshard + 64 * c;
     const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
-    load_rows<E, D>(s_q, reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
-    load_rows<E, D>(s_k, reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
-    load_rows<E, D>(s_do, reinterpret_cast<const E*>(a.dO), b, h, t0, n, a.T, a.H);
-    load_rows<float, D>(s_w, a.ws_w, b, h, t0, n, a.T, a.H);
+    pq.put(s_q);
+    pk.put(s_k);
+    pdo.put(s_do);
+    pw.put(s_w);
     chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    if (c > 0) fetch_chunk(c - 1);
     if constexpr (APPLY) store_mat<D>(a.ws_dsc + (bh * nct + cbase + c) * (int64_t)(D * D), s_ds);
     for (int t = w; t < 16; t += NWV) {
       const int ti = t >> 2, tj = t & 3;
@@ -594,15 +680,27 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
   const int w = threadIdx.x >> 6, l = lane_id();
   float *s_q = s_slot[0], *s_k = s_slot[1], *s_do = s_slot[2], *s_u = s_slot[3], *s_s0 = s_slot[4],
         *s_ds = s_slot[5], *s_dp = s_slot[6], *s_dk = s_slot[7];
-  load_rows<E, D>(s_q, reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
-  load_rows<E, D>(s_k, reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
-  load_rows<E, D>(s_do, reinterpret_cast<const E*>(a.dO), b, h, t0, n, a.T, a.H);
-  load_rows<float, D>(s_u, a.ws_u, b, h, t0, n, a.T, a.H);
-  load_mat<D>(s_s0, a.chunk_states + (bh * nct + idx) * (int64_t)(D * D));
-  load_mat<D>(s_ds, a.ws_dsc + (bh * nct + idx) * (int64_t)(D * D));
-  for (int e = threadIdx.x; e < 3 * NWV * CH; e += NTH) (&s_rp[0][0][0])[e] = 0.f;
-  for (int e = threadIdx.x; e < NWV * CH; e += NTH) (&s_colp[0][0])[e] = 0.f;
-  chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+  {
+    RowTile<E, D> rq, rk, rdo;
+    RowTile<float, D> ru;
+    MatTile<D> rs0, rds;
+    rq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
+    rk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+    rdo.fetch(reinterpret_cast<const E*>(a.dO), b, h, t0, n, a.T, a.H);
+    ru.fetch(a.ws_u, b, h, t0, n, a.T, a.H);
+    rs0.fetch(a.chunk_states + (bh * nct + idx) * (int64_t)(D * D));
+    rds.fetch(a.ws_dsc + (bh * nct + idx) * (int64_t)(D * D));
+    for (int e = threadIdx.x; e < 3 * NWV * CH; e += NTH) (&s_rp[0][0][0])[e] = 0.f;
+    for (int e = threadIdx.x; e < NWV * CH; e += NTH) (&s_colp[0][0])[e] = 0.f;
+    chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    rq.put(s_q);
+    rk.put(s_k);
+    rdo.put(s_do);
+    ru.put(s_u);
+    rs0.put(s_s0);
+    rds.put(s_ds);
+  }
+  __syncthreads();
 
   // score tiles: dPr and the decay terms of dGam (rows of wave w's column tile tj = w)
   {
@@ -721,10 +819,18 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
 
   // phase 2: slots 0 V, 2 U~, 3 W, 6 dU; 1 K, 4 S0, 7 dk kept; 5 dW
   float *s_v = s_slot[0], *s_ut = s_slot[2], *s_w = s_slot[3], *s_dU = s_slot[6], *s_dW = s_slot[5];
-  load_rows<E, D>(s_v, reinterpret_cast<const E*>(a.v), b, h, t0, n, a.T, a.H);
-  load_rows<float, D>(s_ut, a.ws_ut, b, h, t0, n, a.T, a.H);
-  load_rows<float, D>(s_w, a.ws_w, b, h, t0, n, a.T, a.H);
-  load_rows<float, D>(s_dU, a.ws_du, b, h, t0, n, a.T, a.H);
+  {
+    RowTile<E, D> rv;
+    RowTile<float, D> rut, rw, rdu;
+    rv.fetch(reinterpret_cast<const E*>(a.v), b, h, t0, n, a.T, a.H);
+    rut.fetch(a.ws_ut, b, h, t0, n, a.T, a.H);
+    rw.fetch(a.ws_w, b, h, t0, n, a.T, a.H);
+    rdu.fetch(a.ws_du, b, h, t0, n, a.T, a.H);
+    rv.put(s_v);
+    rut.put(s_ut);
+    rw.put(s_w);
+    rdu.put(s_dU);
+  }
   __syncthreads();
   // dW = -dU S0^T
   for (int t = w; t < 4 * G::NTC; t += NWV) {
