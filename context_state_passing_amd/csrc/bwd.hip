@@ -85,11 +85,18 @@ __device__ __forceinline__ f32x4 row_scan(f32x4 x) {
   return x;
 }
 
-// Sum over the 16 lanes of each DPP row (the last lane of its inclusive scan),
-// per component, in every lane of the row.
+// Sum over the 16 lanes of each DPP row, per component, in every lane of the row.
 __device__ __forceinline__ f32x4 row_total(f32x4 x) {
 #pragma unroll
   for (int rr = 0; rr < 4; ++rr) x[rr] = row_sum(x[rr]);
+  return x;
+}
+
+// The last lane of each DPP row, per component, in every lane of the row (DPP
+// row_newbcast:15): the row total of an inclusive row scan in one move.
+__device__ __forceinline__ f32x4 row_last(f32x4 x) {
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) x[rr] = dpp_f<0x15F>(x[rr]);
   return x;
 }
 
@@ -98,10 +105,9 @@ __device__ __forceinline__ f32x4 row_total(f32x4 x) {
 // prefix sum over the row plus the total of the earlier blocks held in carry
 // (updated for the next block).
 __device__ __forceinline__ f32x4 lane_gamma(f32x4 x, f32x4& carry) {
-  const f32x4 tot = row_total(x);
   x = row_scan(x);
   const f32x4 out = x + carry;
-  carry += tot;
+  carry += row_last(x);
   return out;
 }
 
@@ -498,7 +504,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
             for (int I = 0; I < 4; ++I) {
               gl[cc][I] = f32x4{0.f, 0.f, 0.f, 0.f};
               if (d0 < DK && (full || 16 * I + i16 < nv))
-                gl[cc][I] = *reinterpret_cast<const f32x4*>(a.g + tok_off(b, t0 + 16 * I + i16, h, a.T, a.H, DK) + d0);
+                gl[cc][I] = *reinterpret_cast<const f32x4*>(a.g + tok_off(b, t0, h, a.T, a.H, DK) + tok_rel(16 * I + i16, a.H, DK) + d0);
             }
           }
         }
@@ -575,7 +581,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
         for (int J = 0; J < 4; ++J) {
           const int tj = 16 * J + i16;
           const int n0 = 16 * cn + 4 * g;
-          if (n0 < DV && (full || tj < nv)) store4(dvp + tok_off(b, t0 + tj, h, a.T, a.H, DV) + n0, accv[J]);
+          if (n0 < DV && (full || tj < nv)) store4(dvp + tok_off(b, t0, h, a.T, a.H, DV) + tok_rel(tj, a.H, DV) + n0, accv[J]);
         }
       }
 
@@ -708,7 +714,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
                 acc[rr] *= ok ? __expf(gm[rr]) : 0.f;
               }
             }
-            if (d0 < DK && (full || ti < nv)) store4(dqp + tok_off(b, t0 + ti, h, a.T, a.H, DK) + d0, acc);
+            if (d0 < DK && (full || ti < nv)) store4(dqp + tok_off(b, t0, h, a.T, a.H, DK) + tok_rel(ti, a.H, DK) + d0, acc);
           }
         }
         // Y'^T = dS'^T V^T (dS' = dS scaled by exp(Gam_last[d]) for a diagonal decay),
@@ -809,7 +815,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
             } else {
               acc += yv;
             }
-            if (d0 < DK && (full || tj < nv)) store4(dkp + tok_off(b, t0 + tj, h, a.T, a.H, DK) + d0, acc);
+            if (d0 < DK && (full || tj < nv)) store4(dkp + tok_off(b, t0, h, a.T, a.H, DK) + tok_rel(tj, a.H, DK) + d0, acc);
           }
         }
       }
@@ -846,10 +852,10 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) ex[rr] = row_shr<1>(x[rr]);
             f32x4 dgv = base + ex + pre_tot;
-            pre_tot += row_total(wv[cc][I]);
+            pre_tot += row_last(x);
             const int t = 16 * I + i16;
             if ((seg.starts >> t) & 1ull) dgv = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (d0 < DK && (full || t < nv)) store4(a.dg + tok_off(b, t0 + t, h, a.T, a.H, DK) + d0, dgv);
+            if (d0 < DK && (full || t < nv)) store4(a.dg + tok_off(b, t0, h, a.T, a.H, DK) + tok_rel(t, a.H, DK) + d0, dgv);
           }
         }
       }

@@ -53,6 +53,10 @@ __device__ __forceinline__ bool score_tile_zero(int idx) { return idx == 1 || id
 __device__ __forceinline__ int64_t tok_off(int64_t b, int64_t t, int64_t h, int64_t T, int64_t H, int D) {
   return ((b * T + t) * H + h) * (int64_t)D;
 }
+// Offset of token t0 + i from token t0 of the same row: the lane-dependent part of
+// an address as a 32-bit product (i < 64, H * D < 2^23), added to a chunk base
+// that is the same for the whole workgroup.
+__device__ __forceinline__ int tok_rel(int i, int64_t H, int D) { return i * ((int)H * D); }
 
 // ---- register prefetch ------------------------------------------------------------
 // A walk issues the next chunk's global loads into these registers before it

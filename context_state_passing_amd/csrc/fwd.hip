@@ -382,7 +382,7 @@ __global__ __launch_bounds__((Geo<E, DK, DV>::NT), (APPLY ? 1 : (sizeof(E) == 4 
 #pragma unroll
           for (int u = 0; u < GB; ++u) {
             const int n0 = 16 * cn + 4 * g, ti = 16 * (I0 + u) + i16;
-            if (n0 < DV && (full || ti < nv)) store4(o + tok_off(b, t0 + ti, h, a.T, a.H, DV) + n0, acc[u]);
+            if (n0 < DV && (full || ti < nv)) store4(o + tok_off(b, t0, h, a.T, a.H, DV) + tok_rel(ti, a.H, DV) + n0, acc[u]);
           }
         }
       }
