@@ -82,3 +82,25 @@ def test_ssd_and_delta_reject_mismatched_inputs():
     g, beta = torch.zeros(1, 64, 2), torch.zeros(1, 64, 2)
     assert _status(cpla.delta_forward, q, q, q, g, beta.double(), num_shards=1)[0] == 3
     assert _status(cpla.delta_forward, q, q, q, g, torch.zeros(1, 63, 2), num_shards=1)[0] == 2
+
+
+def test_grouped_qk_heads_shapes():
+    """q and k may have fewer heads than v (a divisor of H: groups of heads share
+    them); the problem then carries qk_heads, and the shapes are checked as such."""
+    bf = torch.bfloat16
+    q1, k1 = torch.zeros(B, T, 1, DK, dtype=bf), torch.zeros(B, T, 1, DK, dtype=bf)
+    v, g = torch.zeros(B, T, H, DV, dtype=bf), torch.zeros(B, T, H)
+    p = api.make_problem(q1, v, 2, 1)
+    assert (p.H, p.qk_heads, p.dk, p.dv) == (H, 1, DK, DV)
+    assert api.make_problem(torch.zeros(B, T, H, DK, dtype=bf), v, 2, 1).qk_heads == 0   # one per head
+    # accepted shapes reach the device check (host tensors)
+    st, msg = _status(cpla.forward, q1, k1, v, g, num_shards=2)
+    assert st == 1 and "GPU" in msg
+    # k with other heads than q, q heads not dividing v's, g per q/k head
+    assert _status(cpla.forward, q1, torch.zeros(B, T, H, DK, dtype=bf), v, g, num_shards=2)[0] == 2
+    v3 = torch.zeros(B, T, 3, DV, dtype=bf)
+    assert _status(cpla.forward, torch.zeros(B, T, 2, DK, dtype=bf), torch.zeros(B, T, 2, DK, dtype=bf), v3,
+                   torch.zeros(B, T, 3), num_shards=2)[0] == 2
+    assert _status(cpla.forward, q1, k1, v, torch.zeros(B, T, 1), num_shards=2)[0] == 2
+    # the autograd adapter returns per-head gradients, so it takes q and k per head
+    assert _status(cpla.chunkwise_linear_attention, q1, k1, v, g, None, num_shards=2)[0] == 2
