@@ -61,6 +61,40 @@ __device__ __forceinline__ f32x4 tile_mm(const FA& a, const FB& b, f32x4 acc) {
   return acc;
 }
 
+// The same tile product for bf16 inputs: every 32-deep step of k takes the eight
+// consecutive k of lane group l / 16 (the layout of v_mfma_f32_16x16x32_bf16),
+// splits each fp32 operand into bf16 hi + lo and issues hi*hi, hi*lo and lo*hi, so
+// the product keeps about 16 significant bits per operand (the LDS tiles and
+// intermediates stay fp32) at 3 bf16 MFMAs per 32-deep step instead of 8 fp32
+// ones. fp32 inputs keep the fp32 product (tile_mm).
+template <int K, class FA, class FB>
+__device__ __forceinline__ f32x4 tile_mm_split(const FA& a, const FB& b, f32x4 acc) {
+  static_assert(K % 32 == 0, "32-deep steps");
+  const int l = lane_id(), x = l & 15, kg = l >> 4;
+#pragma unroll
+  for (int st = 0; st < K / 32; ++st) {
+    float av[8], bv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      av[e] = a(x, 32 * st + 8 * kg + e);
+      bv[e] = b(32 * st + 8 * kg + e, x);
+    }
+    Frag<bf16_t> ah, al, bh, bl;
+    split_frag(ah, al, av);
+    split_frag(bh, bl, bv);
+    mma(acc, ah, bh);
+    mma(acc, ah, bl);
+    mma(acc, al, bh);
+  }
+  return acc;
+}
+// tile_mm for fp32 inputs, tile_mm_split for bf16 inputs (K a multiple of 32)
+template <int K, typename E, class FA, class FB>
+__device__ __forceinline__ f32x4 tile_mm_e(const FA& a, const FB& b, f32x4 acc) {
+  if constexpr (sizeof(E) == 2 && K % 32 == 0) return tile_mm_split<K>(a, b, acc);
+  else return tile_mm<K>(a, b, acc);
+}
+
 template <int D> struct DGeo {
   static constexpr int LD = D + 4;            // row stride of a [64][D] or [D][D] tile (floats)
   static constexpr int LC = CH + 4;           // row stride of a [64][64] tile
@@ -295,7 +329,7 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti)
-      acc = tile_mm<D>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+      acc = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -392,7 +426,7 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     // U_Z = U~_Z - W Z
     for (int t = w; t < 4 * (NZ / 16); t += NWV) {
       const int ti = t / (NZ / 16), tj = t % (NZ / 16);
-      f32x4 acc = tile_mm<D>([&](int i, int k) { return s_w[(16 * ti + i) * G::LD + k]; },
+      f32x4 acc = tile_mm_e<D, E>([&](int i, int k) { return s_w[(16 * ti + i) * G::LD + k]; },
                           [&](int k, int j) { return s_z[k * LZ + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -411,7 +445,7 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     const float sc = s_t.sc[0];
     for (int t = w; t < (D / 16) * (NZ / 16); t += NWV) {
       const int ti = t / (NZ / 16), tj = t % (NZ / 16);
-      f32x4 acc = tile_mm<CH>([&](int i, int k) { return s_k[k * G::LD + 16 * ti + i] * s_t.el[k]; },
+      f32x4 acc = tile_mm_e<CH, E>([&](int i, int k) { return s_k[k * G::LD + 16 * ti + i] * s_t.el[k]; },
                           [&](int k, int j) { return s_u[k * LZ + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -527,7 +561,7 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti)
-      acc = tile_mm<D>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+      acc = tile_mm_e<D, E>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -540,9 +574,9 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
   E* o = reinterpret_cast<E*>(a.out);
   for (int t = w; t < 4 * G::NTC; t += NWV) {
     const int ti = t / G::NTC, tj = t % G::NTC;
-    f32x4 x = tile_mm<D>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+    f32x4 x = tile_mm_e<D, E>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                       [&](int k, int j) { return s_s[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-    f32x4 y = tile_mm<CH>([&](int i, int k) { return s_p[(16 * ti + i) * G::LC + k]; },
+    f32x4 y = tile_mm_e<CH, E>([&](int i, int k) { return s_p[(16 * ti + i) * G::LC + k]; },
                       [&](int k, int j) { return s_u[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -599,7 +633,7 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
       const int ti = t >> 2, tj = t & 3;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       if (tj <= ti)
-        acc = tile_mm<D>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+        acc = tile_mm_e<D, E>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                       [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -612,9 +646,9 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
     // dU = P^T dO + K~ dS
     for (int t = w; t < 4 * G::NTC; t += NWV) {
       const int ti = t / G::NTC, tj = t % G::NTC;
-      f32x4 acc = tile_mm<CH>([&](int i, int k) { return s_p[k * G::LC + 16 * ti + i]; },
+      f32x4 acc = tile_mm_e<CH, E>([&](int i, int k) { return s_p[k * G::LC + 16 * ti + i]; },
                           [&](int k, int j) { return s_do[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      acc = tile_mm<D>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k] * s_t.el[16 * ti + i]; },
+      acc = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k] * s_t.el[16 * ti + i]; },
                     [&](int k, int j) { return s_ds[k * G::LD + 16 * tj + j]; }, acc);
 #pragma unroll
       for (int q = 0; q < 4; ++q) s_du[(16 * ti + 4 * (l >> 4) + q) * G::LD + 16 * tj + (l & 15)] = acc[q];
@@ -625,9 +659,9 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
     const float sc = s_t.sc[0];
     for (int t = w; t < G::NTC * G::NTC; t += NWV) {
       const int ti = t / G::NTC, tj = t % G::NTC;
-      f32x4 x = tile_mm<CH>([&](int i, int k) { return s_q[k * G::LD + 16 * ti + i] * s_t.eg[k]; },
+      f32x4 x = tile_mm_e<CH, E>([&](int i, int k) { return s_q[k * G::LD + 16 * ti + i] * s_t.eg[k]; },
                         [&](int k, int j) { return s_do[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 y = tile_mm<CH>([&](int i, int k) { return s_w[k * G::LD + 16 * ti + i]; },
+      f32x4 y = tile_mm_e<CH, E>([&](int i, int k) { return s_w[k * G::LD + 16 * ti + i]; },
                         [&](int k, int j) { return s_du[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -709,9 +743,9 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
       const int ti = t >> 2, tj = t & 3;
       f32x4 qk = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
       if (tj <= ti) {
-        qk = tile_mm<D>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+        qk = tile_mm_e<D, E>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                      [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, qk);
-        du = tile_mm<D>([&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
+        du = tile_mm_e<D, E>([&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
                      [&](int k, int j) { return s_u[(16 * tj + j) * G::LD + k]; }, du);
       }
       float rowp[4], colp = 0.f;
@@ -755,13 +789,13 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     E* dq = reinterpret_cast<E*>(a.dq);
     for (int t = w; t < 4 * G::NTC; t += NWV) {
       const int ti = t / G::NTC, tj = t % G::NTC;
-      f32x4 x = tile_mm<CH>([&](int i, int k) { return s_dp[(16 * ti + i) * G::LC + k]; },
+      f32x4 x = tile_mm_e<CH, E>([&](int i, int k) { return s_dp[(16 * ti + i) * G::LC + k]; },
                         [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 y = tile_mm<D>([&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
+      f32x4 y = tile_mm_e<D, E>([&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
                         [&](int k, int j) { return s_s0[(16 * tj + j) * G::LD + k]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 z = tile_mm<CH>([&](int i, int k) { return s_dp[k * G::LC + 16 * ti + i]; },
+      f32x4 z = tile_mm_e<CH, E>([&](int i, int k) { return s_dp[k * G::LC + 16 * ti + i]; },
                         [&](int k, int j) { return s_q[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 u = tile_mm<D>([&](int i, int k) { return s_u[(16 * ti + i) * G::LD + k]; },
+      f32x4 u = tile_mm_e<D, E>([&](int i, int k) { return s_u[(16 * ti + i) * G::LD + k]; },
                         [&](int k, int j) { return s_ds[(16 * tj + j) * G::LD + k]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -835,7 +869,7 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
   // dW = -dU S0^T
   for (int t = w; t < 4 * G::NTC; t += NWV) {
     const int ti = t / G::NTC, tj = t % G::NTC;
-    f32x4 x = tile_mm<D>([&](int i, int k) { return s_dU[(16 * ti + i) * G::LD + k]; },
+    f32x4 x = tile_mm_e<D, E>([&](int i, int k) { return s_dU[(16 * ti + i) * G::LD + k]; },
                       [&](int k, int j) { return s_s0[(16 * tj + j) * G::LD + k]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int q = 0; q < 4; ++q) s_dW[(16 * ti + 4 * (l >> 4) + q) * G::LD + 16 * tj + (l & 15)] = -x[q];
@@ -847,7 +881,7 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti)
-      acc = tile_mm<D>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+      acc = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -903,11 +937,11 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
       const int ti = t >> 2, tj = t & 3;
       f32x4 x = {0.f, 0.f, 0.f, 0.f}, kk = {0.f, 0.f, 0.f, 0.f};
       if (tj <= ti) {
-        x = tile_mm<D>([&](int i, int k) { return s_dU[(16 * ti + i) * G::LD + k]; },
+        x = tile_mm_e<D, E>([&](int i, int k) { return s_dU[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_ut[(16 * tj + j) * G::LD + k]; }, x);
-        x = tile_mm<D>([&](int i, int k) { return s_dW[(16 * ti + i) * G::LD + k]; },
+        x = tile_mm_e<D, E>([&](int i, int k) { return s_dW[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_w[(16 * tj + j) * G::LD + k]; }, x);
-        kk = tile_mm<D>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+        kk = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
                      [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, kk);
       }
       float colp = 0.f;
@@ -947,9 +981,9 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     E* dv = reinterpret_cast<E*>(a.dv);
     for (int t = w; t < 4 * G::NTC; t += NWV) {
       const int ti = t / G::NTC, tj = t % G::NTC;
-      f32x4 x = tile_mm<CH>([&](int i, int k) { return s_a[(16 * ti + i) * G::LC + k]; },
+      f32x4 x = tile_mm_e<CH, E>([&](int i, int k) { return s_a[(16 * ti + i) * G::LC + k]; },
                         [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      x = tile_mm<CH>([&](int i, int k) { return s_a[k * G::LC + 16 * ti + i]; },
+      x = tile_mm_e<CH, E>([&](int i, int k) { return s_a[k * G::LC + 16 * ti + i]; },
                   [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, x);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
