@@ -518,7 +518,7 @@ def main_delta(args, rank):
         "metric": f"fwd+bwd tokens/s, gated delta rule {wl.name} (B{B} H{H} T{T} d={d})",
         "value": tokens / (ms_step * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "vs_baseline": None, "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f32", "data": "synthetic",
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "dk": d, "dv": d, "chunk": 64, "shards": P,
                    "decay": "gated delta rule (dense transition)", "inputs": "bf16" if wl.dtype == torch.bfloat16
                    else "f32", "parallelism": "single-gpu (shards simulated in HBM)"},
@@ -526,6 +526,12 @@ def main_delta(args, rank):
                      "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
                      "traffic_note": "counters are taken for the default workload",
+                     "peak_note": ("fp32 arithmetic: with bf16 inputs the products run as split-bf16 MFMA "
+                                   "(hi*hi + hi*lo + lo*hi, three 16x16x32 bf16 issues per fp32-equivalent "
+                                   "step), whose ceiling for it is the bf16 peak / 3"
+                                   if wl.dtype == torch.bfloat16 else "fp32 MFMA"),
+                     "frac_of_split_ceiling": (achieved / (MFMA_BF16_PEAK_TFLOPS / 3)
+                                               if wl.dtype == torch.bfloat16 else None),
                      "algorithmic_flops_per_launch": dom_flops, "launch_ms": dom_ms},
         "step_breakdown_ms": dict(zip(names, parts)),
         "step_roofline": {"mfma_TFLOPs": step_flops / (ms_step * 1e-3) / 1e12,
