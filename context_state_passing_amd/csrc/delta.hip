@@ -208,17 +208,32 @@ struct ChunkTerms {
   float sc[4];
 };
 
-__device__ __forceinline__ void chunk_terms(ChunkTerms& s, const float* g, const float* beta, const int32_t* seq,
-                                            int64_t b, int64_t h, int64_t t0, int n, int64_t T, int64_t H) {
+// The per-token inputs of the terms (wave 0, lane = token), loaded by fetch() apart
+// from the computation: the walks load the next chunk's with its tiles, and the
+// per-chunk kernels issue them ahead of their tiles so that the terms need not wait
+// for the tiles' loads.
+struct TermRegs {
+  float gv = 0.f, bv = 0.f;
+  bool st = false;   // a sequence starts at the token
+  __device__ __forceinline__ void fetch(const float* g, const float* beta, const int32_t* seq, int64_t b, int64_t h,
+                                        int64_t t0, int n, int64_t T, int64_t H) {
+    if (threadIdx.x < CH) {
+      const int l = threadIdx.x;
+      const bool ok = l < n;
+      const int64_t t = t0 + l;
+      gv = ok ? g[(b * T + t) * H + h] : 0.f;
+      bv = ok ? beta[(b * T + t) * H + h] : 0.f;
+      st = false;
+      if (seq && ok) st = seq[t] != (t > 0 ? seq[t - 1] : -1);
+    }
+  }
+};
+
+__device__ __forceinline__ void chunk_terms(ChunkTerms& s, const TermRegs& in) {
   if (threadIdx.x < CH) {
     const int l = threadIdx.x;
-    const bool ok = l < n;
-    const int64_t t = t0 + l;
-    const float gv = ok ? g[(b * T + t) * H + h] : 0.f;
-    const float bv = ok ? beta[(b * T + t) * H + h] : 0.f;
-    bool st = false;
-    if (seq && ok) st = seq[t] != (t > 0 ? seq[t - 1] : -1);
-    const uint64_t starts = __ballot(st);
+    const float gv = in.gv, bv = in.bv;
+    const uint64_t starts = __ballot(in.st);
     const int cnt = __popcll(starts & ((2ull << l) - 1ull));
     // segment-local inclusive scan: add the partial of lane l - off when it is in
     // the same sequence (sequences are contiguous, so its partial is too)
@@ -315,9 +330,11 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
   const int32_t* seq = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
   {
     RowTile<E, D> rk, rv;
+    TermRegs tr;
+    tr.fetch(a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
     rk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
     rv.fetch(reinterpret_cast<const E*>(a.v), b, h, t0, n, a.T, a.H);
-    chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    chunk_terms(s_t, tr);
     rk.put(s_k);
     rv.put(s_v);
   }
@@ -399,9 +416,11 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
   // is being computed
   RowTile<float, D> pw, pu;
   RowTile<E, D> pk;
+  TermRegs pt;
   auto fetch_chunk = [&](int c) {
     const int64_t t0 = tshard + 64 * c;
     const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
+    pt.fetch(a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
     pw.fetch(a.ws_w, b, h, t0, n, a.T, a.H);
     pk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
     pu.fetch(a.ws_ut, b, h, t0, n, a.T, a.H);
@@ -417,7 +436,7 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     if constexpr (NZ > D) {
       for (int e = threadIdx.x; e < CH * (NZ - D); e += NTH) s_u[(e / (NZ - D)) * LZ + D + e % (NZ - D)] = 0.f;
     }
-    chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    chunk_terms(s_t, pt);
     if (c + 1 < nc) fetch_chunk(c + 1);
     if constexpr (APPLY) {
       float* cs = a.chunk_states + (bh * nct + cbase + c) * (int64_t)(D * D);
@@ -546,11 +565,13 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
     RowTile<E, D> rq, rk;
     RowTile<float, D> ru;
     MatTile<D> rs;
+    TermRegs tr;
+    tr.fetch(a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
     rq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
     rk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
     ru.fetch(a.ws_u, b, h, t0, n, a.T, a.H);
     rs.fetch(a.chunk_states + (bh * nct + idx) * (int64_t)(D * D));
-    chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    chunk_terms(s_t, tr);
     rq.put(s_q);
     rk.put(s_k);
     ru.put(s_u);
@@ -610,9 +631,11 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
   // it (the walk runs backwards) is being computed
   RowTile<E, D> pq, pk, pdo;
   RowTile<float, D> pw;
+  TermRegs pt;
   auto fetch_chunk = [&](int c) {
     const int64_t t0 = tshard + 64 * c;
     const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
+    pt.fetch(a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
     pq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
     pk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
     pdo.fetch(reinterpret_cast<const E*>(a.dO), b, h, t0, n, a.T, a.H);
@@ -626,7 +649,7 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
     pk.put(s_k);
     pdo.put(s_do);
     pw.put(s_w);
-    chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    chunk_terms(s_t, pt);
     if (c > 0) fetch_chunk(c - 1);
     if constexpr (APPLY) store_mat<D>(a.ws_dsc + (bh * nct + cbase + c) * (int64_t)(D * D), s_ds);
     for (int t = w; t < 16; t += NWV) {
@@ -718,6 +741,8 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     RowTile<E, D> rq, rk, rdo;
     RowTile<float, D> ru;
     MatTile<D> rs0, rds;
+    TermRegs tr;
+    tr.fetch(a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
     rq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
     rk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
     rdo.fetch(reinterpret_cast<const E*>(a.dO), b, h, t0, n, a.T, a.H);
@@ -726,7 +751,7 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     rds.fetch(a.ws_dsc + (bh * nct + idx) * (int64_t)(D * D));
     for (int e = threadIdx.x; e < 3 * NWV * CH; e += NTH) (&s_rp[0][0][0])[e] = 0.f;
     for (int e = threadIdx.x; e < NWV * CH; e += NTH) (&s_colp[0][0])[e] = 0.f;
-    chunk_terms(s_t, a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    chunk_terms(s_t, tr);
     rq.put(s_q);
     rk.put(s_k);
     rdo.put(s_do);
