@@ -619,8 +619,9 @@ cpla_status check_delta(const cpla_problem* p) {
   if (p->dk != p->dv) return fail(CPLA_E_UNSUPPORTED, "dk != dv unsupported");
   if (p->qk_heads != 0 && p->qk_heads != p->H)
     return fail(CPLA_E_UNSUPPORTED, "qk_heads=%d: the delta rule takes q and k per head", p->qk_heads);
-  if (!(p->dk == 16 || p->dk == 32 || p->dk == 64))
-    return fail(CPLA_E_UNSUPPORTED, "head dim %lld unsupported for the delta rule (16, 32, 64)", (long long)p->dk);
+  if (!(p->dk == 16 || p->dk == 32 || p->dk == 64 || (p->dk == 128 && p->dtype == CPLA_BF16)))
+    return fail(CPLA_E_UNSUPPORTED, "head dim %lld unsupported for the delta rule (16, 32, 64; 128 for bf16)",
+                (long long)p->dk);
   if (p->B * p->H > 65535) return fail(CPLA_E_UNSUPPORTED, "B*H=%lld exceeds 65535", (long long)(p->B * p->H));
   return CPLA_OK;
 }
@@ -668,21 +669,32 @@ enum DeltaPhase { DP_FWD_PREPARE, DP_FWD_APPLY_WALK, DP_FWD_OUT, DP_BWD_PREPARE,
 
 template <typename E, int D>
 void delta_launch(DeltaPhase ph, const cpla_problem* p, const DeltaArgs& a, hipStream_t stream) {
-  const dim3 ranks(p->rank_end - p->rank_begin, (unsigned)(p->B * p->H)), chunks(delta_chunks(p), (unsigned)(p->B * p->H));
+  const unsigned nr = p->rank_end - p->rank_begin, bh = (unsigned)(p->B * p->H), nch = delta_chunks(p);
   const dim3 nt(DELTA_THREADS);
   switch (ph) {
     case DP_FWD_PREPARE:
-      if (chunks.x) hipLaunchKernelGGL((delta_wy<E, D>), chunks, nt, 0, stream, a);
-      hipLaunchKernelGGL((delta_fwalk<E, D, false>), ranks, nt, 0, stream, a);
+      if (nch) hipLaunchKernelGGL((delta_wy<E, D>), dim3(nch, bh), nt, 0, stream, a);
+      hipLaunchKernelGGL((delta_fwalk<E, D, false>),
+                         dim3(nr, bh, FwalkSlab<D, false>::NZ / FwalkSlab<D, false>::SZ), nt, 0, stream, a);
       break;
-    case DP_FWD_APPLY_WALK: hipLaunchKernelGGL((delta_fwalk<E, D, true>), ranks, nt, 0, stream, a); break;
+    case DP_FWD_APPLY_WALK:
+      hipLaunchKernelGGL((delta_fwalk<E, D, true>),
+                         dim3(nr, bh, FwalkSlab<D, true>::NZ / FwalkSlab<D, true>::SZ), nt, 0, stream, a);
+      break;
     case DP_FWD_OUT:
-      if (chunks.x) hipLaunchKernelGGL((delta_out<E, D>), chunks, nt, 0, stream, a);
+      if (nch) hipLaunchKernelGGL((delta_out<E, D>), dim3(nch, bh, D / DeltaSlabs<D>::OUT), nt, 0, stream, a);
       break;
-    case DP_BWD_PREPARE: hipLaunchKernelGGL((delta_bwalk<E, D, false>), ranks, nt, 0, stream, a); break;
-    case DP_BWD_APPLY_WALK: hipLaunchKernelGGL((delta_bwalk<E, D, true>), ranks, nt, 0, stream, a); break;
+    case DP_BWD_PREPARE:
+      hipLaunchKernelGGL((delta_bwalk<E, D, false>), dim3(nr, bh, D / DeltaSlabs<D>::BWALK), nt, 0, stream, a);
+      break;
+    case DP_BWD_APPLY_WALK:
+      hipLaunchKernelGGL((delta_bwalk<E, D, true>), dim3(nr, bh, D / DeltaSlabs<D>::BWALK), nt, 0, stream, a);
+      break;
     case DP_BWD_GRAD:
-      if (chunks.x) hipLaunchKernelGGL((delta_grad<E, D>), chunks, nt, 0, stream, a);
+      if (nch) {
+        if constexpr (D > 64) hipLaunchKernelGGL((delta_grad_wide<E, D>), dim3(nch, bh), nt, 0, stream, a);
+        else hipLaunchKernelGGL((delta_grad<E, D>), dim3(nch, bh), nt, 0, stream, a);
+      }
       break;
   }
 }
@@ -691,7 +703,8 @@ template <typename E>
 void delta_launch_d(DeltaPhase ph, const cpla_problem* p, const DeltaArgs& a, hipStream_t stream) {
   if (p->dk == 16) delta_launch<E, 16>(ph, p, a, stream);
   else if (p->dk == 32) delta_launch<E, 32>(ph, p, a, stream);
-  else delta_launch<E, 64>(ph, p, a, stream);
+  else if (p->dk == 64) delta_launch<E, 64>(ph, p, a, stream);
+  else if constexpr (sizeof(E) == 2) delta_launch<E, 128>(ph, p, a, stream);   // 128: bf16 only (checked)
 }
 
 cpla_status delta_run(DeltaPhase ph, const cpla_problem* p, const DeltaArgs& a, hipStream_t stream, const char* what) {
@@ -715,7 +728,8 @@ cpla_status delta_scan_run(const cpla_problem* p, const float* summary, const in
   const dim3 grid((unsigned)s.BH);
   if (p->dk == 16) hipLaunchKernelGGL(delta_scan<16>, grid, dim3(DELTA_THREADS), 0, stream, s);
   else if (p->dk == 32) hipLaunchKernelGGL(delta_scan<32>, grid, dim3(DELTA_THREADS), 0, stream, s);
-  else hipLaunchKernelGGL(delta_scan<64>, grid, dim3(DELTA_THREADS), 0, stream, s);
+  else if (p->dk == 64) hipLaunchKernelGGL(delta_scan<64>, grid, dim3(DELTA_THREADS), 0, stream, s);
+  else hipLaunchKernelGGL(delta_scan<128>, grid, dim3(DELTA_THREADS), 0, stream, s);
   return launched("delta_scan");
 }
 

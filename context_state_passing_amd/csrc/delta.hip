@@ -15,8 +15,9 @@
 // The solve is the WY form of the product of the chunk's transitions: the
 // chunk's own map is M_c = live_last e^{Gam_last} I - K~^T W.
 //
-// Kernels (one workgroup of eight waves each; every contraction is fp32 MFMA
-// 16x16x4 on fp32 LDS tiles, inputs widened on load):
+// Kernels (one workgroup of eight waves each; contractions are MFMA products of
+// fp32 LDS tiles, inputs widened on load: fp32 16x16x4 for fp32 inputs, split bf16
+// 16x16x32 for bf16 inputs):
 //   delta_wy      per chunk:  U~, W ((I + A)^{-1} by 16 x 16 blocks, then MFMA products)
 //   delta_fwalk   per shard:  chunk walk of the state; prepare folds [delta_S | M]
 //                             from [0 | I], apply saves chunk states and U
@@ -26,7 +27,10 @@
 //   delta_bwalk   per shard:  reverse walk of dS; prepare gives gamma, apply saves
 //                             the chunk-end gradients and dU
 //   delta_grad    per chunk:  dq, dk, dv, dg, dbeta
-// This build covers d_k = d_v in {16, 32, 64}.
+// d_k = d_v in {16, 32, 64}, and 128 for bf16 inputs: there the walks and delta_out
+// split the state's columns over workgroups and the gradients take the value
+// dimension in slices (delta_grad_wide), as a fp32 state with the chunk's tiles
+// does not fit one workgroup's LDS.
 #include "kernels.hpp"
 #include "shards.hpp"
 
@@ -116,45 +120,47 @@ __device__ __forceinline__ f32x4 widen4(const bf16x4& x) {
   return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
 }
 
-// [64][D] rows t0 .. t0 + 63 of a [B,T,H,D] tensor; rows past n read as zero
-template <typename E, int D> struct RowTile {
-  static constexpr int NV = CH * D / 4, PER = (NV + NTH - 1) / NTH;
+// [64][W] columns c0 .. c0 + W - 1 of rows t0 .. t0 + 63 of a [B,T,H,D] tensor
+// (W = D: whole rows); rows past n read as zero. put() writes row i at dst + i ld.
+template <typename E, int D, int W = D> struct RowTile {
+  static constexpr int NV = CH * W / 4, PER = (NV + NTH - 1) / NTH;
   typedef typename Raw4<E>::type R;
   R v[PER];
   __device__ __forceinline__ void fetch(const E* src, int64_t b, int64_t h, int64_t t0, int n, int64_t T,
-                                        int64_t H) {
+                                        int64_t H, int c0 = 0) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int e = threadIdx.x + p * NTH, i = e / (D / 4), c = 4 * (e % (D / 4));
+      const int e = threadIdx.x + p * NTH, i = e / (W / 4), c = 4 * (e % (W / 4));
       v[p] = R{0, 0, 0, 0};
-      if ((NV % NTH == 0 || e < NV) && i < n) v[p] = *reinterpret_cast<const R*>(src + ((b * T + t0 + i) * H + h) * D + c);
+      if ((NV % NTH == 0 || e < NV) && i < n)
+        v[p] = *reinterpret_cast<const R*>(src + ((b * T + t0 + i) * H + h) * D + c0 + c);
     }
   }
-  __device__ __forceinline__ void put(float* dst, int ld = DGeo<D>::LD) const {
+  __device__ __forceinline__ void put(float* dst, int ld = W + 4) const {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int e = threadIdx.x + p * NTH, i = e / (D / 4), c = 4 * (e % (D / 4));
+      const int e = threadIdx.x + p * NTH, i = e / (W / 4), c = 4 * (e % (W / 4));
       if (NV % NTH == 0 || e < NV) *reinterpret_cast<f32x4*>(dst + i * ld + c) = widen4(v[p]);
     }
   }
 };
 
-// a row-major [D][D] fp32 matrix
-template <int D> struct MatTile {
-  static constexpr int NV = D * D / 4, PER = (NV + NTH - 1) / NTH;
+// columns c0 .. c0 + W - 1 of a row-major [D][D] fp32 matrix, put() as a [D][W + 4] tile
+template <int D, int W = D> struct MatTile {
+  static constexpr int NV = D * W / 4, PER = (NV + NTH - 1) / NTH;
   f32x4 v[PER];
-  __device__ __forceinline__ void fetch(const float* src) {
+  __device__ __forceinline__ void fetch(const float* src, int c0 = 0) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int e = threadIdx.x + p * NTH;
-      if (NV % NTH == 0 || e < NV) v[p] = *reinterpret_cast<const f32x4*>(src + 4 * e);
+      const int e = threadIdx.x + p * NTH, i = e / (W / 4), c = 4 * (e % (W / 4));
+      if (NV % NTH == 0 || e < NV) v[p] = *reinterpret_cast<const f32x4*>(src + i * D + c0 + c);
     }
   }
   __device__ __forceinline__ void put(float* dst) const {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int e = threadIdx.x + p * NTH, i = e / (D / 4), c = 4 * (e % (D / 4));
-      if (NV % NTH == 0 || e < NV) *reinterpret_cast<f32x4*>(dst + i * DGeo<D>::LD + c) = v[p];
+      const int e = threadIdx.x + p * NTH, i = e / (W / 4), c = 4 * (e % (W / 4));
+      if (NV % NTH == 0 || e < NV) *reinterpret_cast<f32x4*>(dst + i * (W + 4) + c) = v[p];
     }
   }
 };
@@ -169,18 +175,18 @@ __device__ __forceinline__ void load_rows(float* dst, const E* src, int64_t b, i
   t.put(dst);
 }
 
-// rows i < n of an fp32 LDS tile into a [B,T,H,D] tensor of type E
-template <typename E, int D>
+// rows i < n of a [64][W + 4] fp32 LDS tile into columns c0 .. c0 + W - 1 of a
+// [B,T,H,D] tensor of type E
+template <typename E, int D, int W = D>
 __device__ __forceinline__ void store_rows(E* dst, const float* src, int64_t b, int64_t h, int64_t t0, int n,
-                                           int64_t T, int64_t H) {
-  using G = DGeo<D>;
-  constexpr int PER_ROW = D / 4;
+                                           int64_t T, int64_t H, int c0 = 0) {
+  constexpr int PER_ROW = W / 4;
   for (int e = threadIdx.x; e < CH * PER_ROW; e += NTH) {
     const int i = e / PER_ROW, c = 4 * (e % PER_ROW);
     if (i >= n) continue;
-    E* p = dst + ((b * T + t0 + i) * H + h) * D + c;
+    E* p = dst + ((b * T + t0 + i) * H + h) * D + c0 + c;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) p[u] = (E)src[i * G::LD + c + u];
+    for (int u = 0; u < 4; ++u) p[u] = (E)src[i * (W + 4) + c + u];
   }
 }
 
@@ -191,11 +197,12 @@ __device__ __forceinline__ void load_mat(float* dst, const float* src) {
   t.fetch(src);
   t.put(dst);
 }
-template <int D>
-__device__ __forceinline__ void store_mat(float* dst, const float* src) {
-  for (int e = threadIdx.x; e < D * D / 4; e += NTH) {
-    const int i = e / (D / 4), c = 4 * (e % (D / 4));
-    *reinterpret_cast<f32x4*>(dst + i * D + c) = *reinterpret_cast<const f32x4*>(src + i * DGeo<D>::LD + c);
+// a [D][W + 4] LDS tile into columns c0 .. c0 + W - 1 of a row-major [D][D] matrix
+template <int D, int W = D>
+__device__ __forceinline__ void store_mat(float* dst, const float* src, int c0 = 0) {
+  for (int e = threadIdx.x; e < D * W / 4; e += NTH) {
+    const int i = e / (W / 4), c = 4 * (e % (W / 4));
+    *reinterpret_cast<f32x4*>(dst + i * D + c0 + c) = *reinterpret_cast<const f32x4*>(src + i * (W + 4) + c);
   }
 }
 
@@ -388,33 +395,40 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
 // ---- forward chunk walk of one shard ------------------------------------------------------
 // PREPARE: the augmented state Z = [delta_S | M] (D x 2D) from [0 | I], written to
 // the shard's record as [M | delta_S]. APPLY: S from the composed incoming state;
-// saves the state entering every chunk and U.
+// saves the state entering every chunk and U. The columns of Z evolve independently
+// (the transition acts on the key side), so a workgroup may own a slab of SZ of
+// them (blockIdx.z; at D = 128 the whole state does not fit the LDS).
 template <typename E, int D, bool APPLY>
 __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
   using G = DGeo<D>;
   constexpr int NZ = APPLY ? D : 2 * D;
-  constexpr int LZ = NZ + 4;
+  constexpr int SZ = FwalkSlab<D, APPLY>::SZ;
+  constexpr int LZ = SZ + 4;
   __shared__ __attribute__((aligned(16))) float s_z[D * LZ], s_u[CH * LZ], s_w[G::TILE], s_k[G::TILE];
   __shared__ ChunkTerms s_t;
   const int64_t r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int z0 = SZ == NZ ? 0 : SZ * blockIdx.z;                 // first column of Z owned here
+  const bool takes_u = SZ == NZ || z0 < D;                        // the slab holds delta_S columns
   const int64_t tshard = shard_begin(a.T, a.P, r), slen = shard_len(a.T, a.P, r);
   const int nc = (int)chunks_of(slen);
   const int64_t cbase = shard_chunk_base(a.T, a.P, r), nct = row_chunks(a.T, a.P);
   const int32_t* seq = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
   const int w = threadIdx.x >> 6, l = lane_id();
 
-  for (int e = threadIdx.x; e < D * NZ; e += NTH) {
-    const int d = e / NZ, m = e % NZ;
+  for (int e = threadIdx.x; e < D * SZ; e += NTH) {
+    const int d = e / SZ, m = e % SZ, mz = z0 + m;
     float x;
-    if constexpr (APPLY) x = a.state_in[((r * a.B * a.H + bh) * D + d) * D + m];
-    else x = (m == D + d) ? 1.f : 0.f;
+    if constexpr (APPLY) x = a.state_in[((r * a.B * a.H + bh) * D + d) * D + mz];
+    else x = (mz == D + d) ? 1.f : 0.f;
     s_z[d * LZ + m] = x;
   }
   __syncthreads();   // an empty shard writes its record from s_z right away
   // each chunk's W, k and U~ are fetched into registers while the chunk before it
   // is being computed
-  RowTile<float, D> pw, pu;
+  constexpr int UW = SZ < D ? SZ : D;            // U~ columns a slab takes
+  RowTile<float, D> pw;
+  RowTile<float, D, UW> pu;
   RowTile<E, D> pk;
   TermRegs pt;
   auto fetch_chunk = [&](int c) {
@@ -423,7 +437,7 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     pt.fetch(a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
     pw.fetch(a.ws_w, b, h, t0, n, a.T, a.H);
     pk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
-    pu.fetch(a.ws_ut, b, h, t0, n, a.T, a.H);
+    if (takes_u) pu.fetch(a.ws_ut, b, h, t0, n, a.T, a.H, z0);
   };
   if (nc > 0) fetch_chunk(0);
   for (int c = 0; c < nc; ++c) {
@@ -431,20 +445,21 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
     pw.put(s_w);
     pk.put(s_k);
-    // U~ into the first D columns of s_u (the M part takes no input)
-    pu.put(s_u, LZ);
-    if constexpr (NZ > D) {
-      for (int e = threadIdx.x; e < CH * (NZ - D); e += NTH) s_u[(e / (NZ - D)) * LZ + D + e % (NZ - D)] = 0.f;
+    // U~ into the slab's delta_S columns of s_u (the M part takes no input)
+    if (takes_u) pu.put(s_u, LZ);
+    if constexpr (SZ > UW || NZ > D) {
+      const int zu = takes_u ? UW : 0;           // columns filled from U~
+      for (int e = threadIdx.x; e < CH * (SZ - zu); e += NTH) s_u[(e / (SZ - zu)) * LZ + zu + e % (SZ - zu)] = 0.f;
     }
     chunk_terms(s_t, pt);
     if (c + 1 < nc) fetch_chunk(c + 1);
     if constexpr (APPLY) {
       float* cs = a.chunk_states + (bh * nct + cbase + c) * (int64_t)(D * D);
-      for (int e = threadIdx.x; e < D * D; e += NTH) cs[e] = s_z[(e / D) * LZ + e % D];
+      for (int e = threadIdx.x; e < D * SZ; e += NTH) cs[(e / SZ) * D + z0 + e % SZ] = s_z[(e / SZ) * LZ + e % SZ];
     }
     // U_Z = U~_Z - W Z
-    for (int t = w; t < 4 * (NZ / 16); t += NWV) {
-      const int ti = t / (NZ / 16), tj = t % (NZ / 16);
+    for (int t = w; t < 4 * (SZ / 16); t += NWV) {
+      const int ti = t / (SZ / 16), tj = t % (SZ / 16);
       f32x4 acc = tile_mm_e<D, E>([&](int i, int k) { return s_w[(16 * ti + i) * G::LD + k]; },
                           [&](int k, int j) { return s_z[k * LZ + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -455,15 +470,15 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     }
     __syncthreads();
     if constexpr (APPLY) {
-      for (int e = threadIdx.x; e < CH * D; e += NTH) {
-        const int i = e / D, m = e % D;
-        if (i < n) a.ws_u[((b * a.T + t0 + i) * a.H + h) * D + m] = s_u[i * LZ + m];
+      for (int e = threadIdx.x; e < CH * SZ; e += NTH) {
+        const int i = e / SZ, m = e % SZ;
+        if (i < n) a.ws_u[((b * a.T + t0 + i) * a.H + h) * D + z0 + m] = s_u[i * LZ + m];
       }
     }
     // Z <- live_last e^Gam_last Z + K~^T U_Z
     const float sc = s_t.sc[0];
-    for (int t = w; t < (D / 16) * (NZ / 16); t += NWV) {
-      const int ti = t / (NZ / 16), tj = t % (NZ / 16);
+    for (int t = w; t < (D / 16) * (SZ / 16); t += NWV) {
+      const int ti = t / (SZ / 16), tj = t % (SZ / 16);
       f32x4 acc = tile_mm_e<CH, E>([&](int i, int k) { return s_k[k * G::LD + 16 * ti + i] * s_t.el[k]; },
                           [&](int k, int j) { return s_u[k * LZ + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
@@ -475,10 +490,12 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     __syncthreads();
   }
   if constexpr (!APPLY) {
+    // record [M | delta_S]: Z column mz < D is delta_S column mz, else M column mz - D
     float* rec = a.summary + (r * a.B * a.H + bh) * (int64_t)(2 * D * D);
-    for (int e = threadIdx.x; e < 2 * D * D; e += NTH) {
-      const int part = e / (D * D), f = e % (D * D), d = f / D, m = f % D;
-      rec[e] = part == 0 ? s_z[d * LZ + D + m] : s_z[d * LZ + m];
+    for (int e = threadIdx.x; e < D * SZ; e += NTH) {
+      const int d = e / SZ, m = e % SZ, mz = z0 + m;
+      const int64_t off = mz < D ? (int64_t)D * D + d * D + mz : d * D + (mz - D);
+      rec[off] = s_z[d * LZ + m];
     }
   }
 }
@@ -544,16 +561,20 @@ __global__ __launch_bounds__(NTH) void delta_scan(DeltaScanArgs a) {
 }
 
 // ---- output per chunk --------------------------------------------------------------------
+// O = live e^Gam Q S + P U, P = tril(Q K^T) . D; a workgroup computes the value
+// columns v0 .. v0 + SV - 1 (blockIdx.z) of one chunk.
 template <typename E, int D>
 __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
   using G = DGeo<D>;
-  __shared__ __attribute__((aligned(16))) float s_q[G::TILE], s_k[G::TILE], s_u[G::TILE], s_s[D * G::LD],
+  constexpr int SV = DeltaSlabs<D>::OUT, LV = SV + 4;
+  __shared__ __attribute__((aligned(16))) float s_q[G::TILE], s_k[G::TILE], s_u[CH * LV], s_s[D * LV],
       s_p[G::TILE_C];
   __shared__ ChunkTerms s_t;
   int64_t r, c;
   const int64_t idx = a.chunk_begin + blockIdx.x;
   chunk_of(a.T, a.P, idx, r, c);
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int v0 = SV == D ? 0 : SV * blockIdx.z;
   const int64_t slen = shard_len(a.T, a.P, r);
   const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
   if (r >= a.P || n <= 0) return;
@@ -563,14 +584,14 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
   const int w = threadIdx.x >> 6, l = lane_id();
   {
     RowTile<E, D> rq, rk;
-    RowTile<float, D> ru;
-    MatTile<D> rs;
+    RowTile<float, D, SV> ru;
+    MatTile<D, SV> rs;
     TermRegs tr;
     tr.fetch(a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
     rq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
     rk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
-    ru.fetch(a.ws_u, b, h, t0, n, a.T, a.H);
-    rs.fetch(a.chunk_states + (bh * nct + idx) * (int64_t)(D * D));
+    ru.fetch(a.ws_u, b, h, t0, n, a.T, a.H, v0);
+    rs.fetch(a.chunk_states + (bh * nct + idx) * (int64_t)(D * D), v0);
     chunk_terms(s_t, tr);
     rq.put(s_q);
     rk.put(s_k);
@@ -593,15 +614,15 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
   }
   __syncthreads();
   E* o = reinterpret_cast<E*>(a.out);
-  for (int t = w; t < 4 * G::NTC; t += NWV) {
-    const int ti = t / G::NTC, tj = t % G::NTC;
+  for (int t = w; t < 4 * (SV / 16); t += NWV) {
+    const int ti = t / (SV / 16), tj = t % (SV / 16);
     f32x4 x = tile_mm_e<D, E>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
-                      [&](int k, int j) { return s_s[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+                      [&](int k, int j) { return s_s[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
     f32x4 y = tile_mm_e<CH, E>([&](int i, int k) { return s_p[(16 * ti + i) * G::LC + k]; },
-                      [&](int k, int j) { return s_u[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+                      [&](int k, int j) { return s_u[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+      const int i = 16 * ti + 4 * (l >> 4) + q, j = v0 + 16 * tj + (l & 15);
       if (i < n) o[((b * a.T + t0 + i) * a.H + h) * D + j] = (E)(s_t.eg[i] * x[q] + y[q]);
     }
   }
@@ -610,26 +631,32 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
 // ---- reverse chunk walk of one shard ------------------------------------------------------
 // dU = P^T dO + K~ dS, dS <- live_last e^Gam_last dS + (live e^Gam Q)^T dO - W^T dU,
 // from dS = 0 (PREPARE: gamma, written with a copy of the shard's M) or from the
-// composed gradient (APPLY: saves the gradient at every chunk's end and dU).
+// composed gradient (APPLY: saves the gradient at every chunk's end and dU). The
+// value columns of dS and dU evolve independently: a workgroup owns SV of them
+// (blockIdx.z).
 template <typename E, int D, bool APPLY>
 __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
   using G = DGeo<D>;
-  __shared__ __attribute__((aligned(16))) float s_q[G::TILE], s_k[G::TILE], s_do[G::TILE], s_w[G::TILE],
-      s_du[G::TILE], s_ds[D * G::LD], s_p[G::TILE_C];
+  constexpr int SV = DeltaSlabs<D>::BWALK, LV = SV + 4;
+  __shared__ __attribute__((aligned(16))) float s_q[G::TILE], s_k[G::TILE], s_do[CH * LV], s_w[G::TILE],
+      s_du[CH * LV], s_ds[D * LV], s_p[G::TILE_C];
   __shared__ ChunkTerms s_t;
   const int64_t r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int v0 = SV == D ? 0 : SV * blockIdx.z;
   const int64_t tshard = shard_begin(a.T, a.P, r), slen = shard_len(a.T, a.P, r);
   const int nc = (int)chunks_of(slen);
   const int64_t cbase = shard_chunk_base(a.T, a.P, r), nct = row_chunks(a.T, a.P);
   const int32_t* seq = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
   const int w = threadIdx.x >> 6, l = lane_id();
-  for (int e = threadIdx.x; e < D * D; e += NTH)
-    s_ds[(e / D) * G::LD + e % D] = APPLY ? a.state_in[(r * a.B * a.H + bh) * (int64_t)(D * D) + e] : 0.f;
+  for (int e = threadIdx.x; e < D * SV; e += NTH)
+    s_ds[(e / SV) * LV + e % SV] =
+        APPLY ? a.state_in[(r * a.B * a.H + bh) * (int64_t)(D * D) + (e / SV) * D + v0 + e % SV] : 0.f;
   __syncthreads();   // an empty shard writes its record from s_ds right away
   // each chunk's q, k, dO and W are fetched into registers while the chunk after
   // it (the walk runs backwards) is being computed
-  RowTile<E, D> pq, pk, pdo;
+  RowTile<E, D> pq, pk;
+  RowTile<E, D, SV> pdo;
   RowTile<float, D> pw;
   TermRegs pt;
   auto fetch_chunk = [&](int c) {
@@ -638,7 +665,7 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
     pt.fetch(a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
     pq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
     pk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
-    pdo.fetch(reinterpret_cast<const E*>(a.dO), b, h, t0, n, a.T, a.H);
+    pdo.fetch(reinterpret_cast<const E*>(a.dO), b, h, t0, n, a.T, a.H, v0);
     pw.fetch(a.ws_w, b, h, t0, n, a.T, a.H);
   };
   if (nc > 0) fetch_chunk(nc - 1);
@@ -651,7 +678,7 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
     pw.put(s_w);
     chunk_terms(s_t, pt);
     if (c > 0) fetch_chunk(c - 1);
-    if constexpr (APPLY) store_mat<D>(a.ws_dsc + (bh * nct + cbase + c) * (int64_t)(D * D), s_ds);
+    if constexpr (APPLY) store_mat<D, SV>(a.ws_dsc + (bh * nct + cbase + c) * (int64_t)(D * D), s_ds, v0);
     for (int t = w; t < 16; t += NWV) {
       const int ti = t >> 2, tj = t & 3;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -667,40 +694,41 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
     }
     __syncthreads();
     // dU = P^T dO + K~ dS
-    for (int t = w; t < 4 * G::NTC; t += NWV) {
-      const int ti = t / G::NTC, tj = t % G::NTC;
+    for (int t = w; t < 4 * (SV / 16); t += NWV) {
+      const int ti = t / (SV / 16), tj = t % (SV / 16);
       f32x4 acc = tile_mm_e<CH, E>([&](int i, int k) { return s_p[k * G::LC + 16 * ti + i]; },
-                          [&](int k, int j) { return s_do[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+                          [&](int k, int j) { return s_do[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
       acc = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k] * s_t.el[16 * ti + i]; },
-                    [&](int k, int j) { return s_ds[k * G::LD + 16 * tj + j]; }, acc);
+                    [&](int k, int j) { return s_ds[k * LV + 16 * tj + j]; }, acc);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s_du[(16 * ti + 4 * (l >> 4) + q) * G::LD + 16 * tj + (l & 15)] = acc[q];
+      for (int q = 0; q < 4; ++q) s_du[(16 * ti + 4 * (l >> 4) + q) * LV + 16 * tj + (l & 15)] = acc[q];
     }
     __syncthreads();
-    if constexpr (APPLY) store_rows<float, D>(a.ws_du, s_du, b, h, t0, n, a.T, a.H);
+    if constexpr (APPLY) store_rows<float, D, SV>(a.ws_du, s_du, b, h, t0, n, a.T, a.H, v0);
     // dS <- sc dS + (eg Q)^T dO - W^T dU
     const float sc = s_t.sc[0];
-    for (int t = w; t < G::NTC * G::NTC; t += NWV) {
-      const int ti = t / G::NTC, tj = t % G::NTC;
+    for (int t = w; t < G::NTC * (SV / 16); t += NWV) {
+      const int ti = t / (SV / 16), tj = t % (SV / 16);
       f32x4 x = tile_mm_e<CH, E>([&](int i, int k) { return s_q[k * G::LD + 16 * ti + i] * s_t.eg[k]; },
-                        [&](int k, int j) { return s_do[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+                        [&](int k, int j) { return s_do[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 y = tile_mm_e<CH, E>([&](int i, int k) { return s_w[k * G::LD + 16 * ti + i]; },
-                        [&](int k, int j) { return s_du[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+                        [&](int k, int j) { return s_du[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int d = 16 * ti + 4 * (l >> 4) + q, m = 16 * tj + (l & 15);
-        s_ds[d * G::LD + m] = sc * s_ds[d * G::LD + m] + x[q] - y[q];
+        s_ds[d * LV + m] = sc * s_ds[d * LV + m] + x[q] - y[q];
       }
     }
     __syncthreads();
   }
   if constexpr (!APPLY) {
+    // record [M | gamma]: M copied from the forward record by the first slab
     float* rec = a.summary + (r * a.B * a.H + bh) * (int64_t)(2 * D * D);
     const float* frec = a.fwd_summary + (r * a.B * a.H + bh) * (int64_t)(2 * D * D);
-    for (int e = threadIdx.x; e < D * D; e += NTH) {
-      rec[e] = frec[e];
-      rec[D * D + e] = s_ds[(e / D) * G::LD + e % D];
-    }
+    if (blockIdx.z == 0)
+      for (int e = threadIdx.x; e < D * D; e += NTH) rec[e] = frec[e];
+    for (int e = threadIdx.x; e < D * SV; e += NTH)
+      rec[D * D + (e / SV) * D + v0 + e % SV] = s_ds[(e / SV) * LV + e % SV];
   }
 }
 
@@ -1053,13 +1081,399 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
   }
 }
 
-#define CPLA_INST_DELTA(E, D)                                                  \
+// ---- gradients per chunk, wide heads --------------------------------------------------------
+// The formulas of delta_grad, for heads whose state and value-side tiles do not fit
+// the LDS together (D = 128): the value dimension is taken in slices of SV columns.
+// Every contraction over it (dO U^T, dO S0^T, U dS^T, dU S0^T, dBv U~^T, the row sums
+// of dBv . V and <dS, S0>) accumulates over the slices in registers, dv = beta dBv
+// is written slice by slice, and the key-side rest follows once, as in delta_grad.
+template <typename E, int D>
+__global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
+  using G = DGeo<D>;
+  constexpr int SV = DeltaSlabs<D>::GRAD, LV = SV + 4, NSL = D / SV, NVT = SV / 16;
+  constexpr int TV = CH * LV, TS = D * LV;     // a [64][SV] and a [D][SV] slice tile
+  constexpr int ARENA = 5 * TV + 2 * TS;
+  static_assert(ARENA >= 2 * G::TILE, "Q and the score tile, then W and dW, reuse the slice tiles");
+  static_assert(4 * G::NTC == 4 * NWV && 4 * NVT == NWV, "tile ownership below assumes D = 8 * 16, SV = 32");
+  __shared__ __attribute__((aligned(16))) float s_k[G::TILE], s_tm[G::TILE_C], s_ar[ARENA];
+  __shared__ ChunkTerms s_t;
+  __shared__ float s_rp[3][NWV][CH];   // per-wave row partials
+  __shared__ float s_colp[NWV][CH];    // per-wave column partials
+  __shared__ float s_cp[2][CH];        // column sums
+  __shared__ float s_red[NWV];
+  int64_t r, c;
+  const int64_t idx = a.chunk_begin + blockIdx.x;
+  chunk_of(a.T, a.P, idx, r, c);
+  const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
+  const int64_t slen = shard_len(a.T, a.P, r);
+  const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
+  if (r >= a.P || n <= 0) return;
+  const int64_t t0 = shard_begin(a.T, a.P, r) + 64 * c;
+  const int64_t nct = row_chunks(a.T, a.P);
+  const int32_t* seq = a.seq_idx ? a.seq_idx + b * a.T : nullptr;
+  const int w = threadIdx.x >> 6, l = lane_id();
+  const float* cs0 = a.chunk_states + (bh * nct + idx) * (int64_t)(D * D);
+  const float* cds = a.ws_dsc + (bh * nct + idx) * (int64_t)(D * D);
+  float *s_do = s_ar, *s_u = s_ar + TV, *s_du = s_ar + 2 * TV, *s_ut = s_ar + 3 * TV, *s_v = s_ar + 4 * TV,
+        *s_s0 = s_ar + 5 * TV, *s_ds = s_ar + 5 * TV + TS;
+
+  // K and the terms; Q is held in registers until the slices are done
+  RowTile<E, D> rq;
+  {
+    RowTile<E, D> rk;
+    TermRegs tr;
+    tr.fetch(a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
+    rk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+    rq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
+    for (int e = threadIdx.x; e < 3 * NWV * CH; e += NTH) (&s_rp[0][0][0])[e] = 0.f;
+    for (int e = threadIdx.x; e < NWV * CH; e += NTH) (&s_colp[0][0])[e] = 0.f;
+    chunk_terms(s_t, tr);
+    rk.put(s_k);
+  }
+  __syncthreads();
+  // T = (I + A)^{-1}, A = strict-lower(beta_i D_ij k_i.k_j)
+  for (int t = w; t < 16; t += NWV) {
+    const int ti = t >> 2, tj = t & 3;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (tj <= ti)
+      acc = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+                    [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+      const bool ok = j < i && s_t.cnt[i] == s_t.cnt[j];
+      s_tm[i * G::LC + j] = ok ? s_t.beta[i] * __expf(s_t.gam[i] - s_t.gam[j]) * acc[q] : 0.f;
+    }
+  }
+  __syncthreads();
+  unit_lower_inverse(s_tm);
+
+  // Sums over the value dimension. Score-shaped [64][64] tiles: wave w owns tiles
+  // w and w + NWV (row tile t / 4, column tile t % 4, lower ones only); key-shaped
+  // [64][D] tiles: wave w owns column tile w of every row tile.
+  f32x4 x_dou[2], x_dbu[2], x_dos[4], x_uds[4], x_dus[4];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) x_dou[m] = x_dbu[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int m = 0; m < 4; ++m) x_dos[m] = x_uds[m] = x_dus[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float sp = 0.f, r2 = 0.f;            // <dS, S0> partial; rowsum(dBv . V) (lane = token, wave 0)
+  RowTile<E, D, SV> pdo, pv;
+  RowTile<float, D, SV> pu, pdu, put_;
+  MatTile<D, SV> ps0, pds;
+  auto fetch_slice = [&](int v0) {
+    pdo.fetch(reinterpret_cast<const E*>(a.dO), b, h, t0, n, a.T, a.H, v0);
+    pu.fetch(a.ws_u, b, h, t0, n, a.T, a.H, v0);
+    pdu.fetch(a.ws_du, b, h, t0, n, a.T, a.H, v0);
+    ps0.fetch(cs0, v0);
+    pds.fetch(cds, v0);
+    put_.fetch(a.ws_ut, b, h, t0, n, a.T, a.H, v0);
+    pv.fetch(reinterpret_cast<const E*>(a.v), b, h, t0, n, a.T, a.H, v0);
+  };
+  fetch_slice(0);
+  E* dv = reinterpret_cast<E*>(a.dv);
+  for (int sl = 0; sl < NSL; ++sl) {
+    const int v0 = SV * sl;
+    pdo.put(s_do);
+    pu.put(s_u);
+    pdu.put(s_du);
+    ps0.put(s_s0);
+    pds.put(s_ds);
+    put_.put(s_ut);
+    pv.put(s_v);
+    __syncthreads();
+    if (sl + 1 < NSL) fetch_slice(v0 + SV);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int t = w + NWV * m, ti = t >> 2, tj = t & 3;
+      if (tj <= ti)
+        x_dou[m] = tile_mm_e<SV, E>([&](int i, int k) { return s_do[(16 * ti + i) * LV + k]; },
+                                    [&](int k, int j) { return s_u[(16 * tj + j) * LV + k]; }, x_dou[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      x_dos[m] = tile_mm_e<SV, E>([&](int i, int k) { return s_do[(16 * m + i) * LV + k]; },
+                                  [&](int k, int j) { return s_s0[(16 * w + j) * LV + k]; }, x_dos[m]);
+      x_uds[m] = tile_mm_e<SV, E>([&](int i, int k) { return s_u[(16 * m + i) * LV + k]; },
+                                  [&](int k, int j) { return s_ds[(16 * w + j) * LV + k]; }, x_uds[m]);
+      x_dus[m] = tile_mm_e<SV, E>([&](int i, int k) { return s_du[(16 * m + i) * LV + k]; },
+                                  [&](int k, int j) { return s_s0[(16 * w + j) * LV + k]; }, x_dus[m]);
+    }
+    for (int e = threadIdx.x; e < D * SV; e += NTH) sp += s_ds[(e / SV) * LV + e % SV] * s_s0[(e / SV) * LV + e % SV];
+    // dBv = T^T dU over the slice (row tile ti takes k tiles ti..3), dv = beta dBv
+    f32x4 bv;
+    {
+      const int ti = w / NVT, tj = w % NVT;
+      bv = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kt = ti; kt < 4; ++kt)
+        bv = tile_mm<16>([&](int i, int q) { return s_tm[(16 * kt + q) * G::LC + 16 * ti + i]; },
+                         [&](int q, int j) { return s_du[(16 * kt + q) * LV + 16 * tj + j]; }, bv);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * ti + 4 * (l >> 4) + q;
+        if (i < n) dv[((b * a.T + t0 + i) * a.H + h) * D + v0 + 16 * tj + (l & 15)] = (E)(s_t.beta[i] * bv[q]);
+      }
+    }
+    __syncthreads();   // every read of dU is done
+    {
+      const int ti = w / NVT, tj = w % NVT;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s_du[(16 * ti + 4 * (l >> 4) + q) * LV + 16 * tj + (l & 15)] = bv[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int t = w + NWV * m, ti = t >> 2, tj = t & 3;
+      if (tj <= ti)
+        x_dbu[m] = tile_mm_e<SV, E>([&](int i, int k) { return s_du[(16 * ti + i) * LV + k]; },
+                                    [&](int k, int j) { return s_ut[(16 * tj + j) * LV + k]; }, x_dbu[m]);
+    }
+    if (threadIdx.x < CH) {
+      const int i = threadIdx.x;
+#pragma unroll 8
+      for (int j = 0; j < SV; ++j) r2 += s_du[i * LV + j] * s_v[i * LV + j];
+    }
+    __syncthreads();   // the slice tiles are read
+  }
+  sp = wave_sum(sp);
+  if (l == 0) s_red[w] = sp;
+
+  // Q and the score tile in the slice space: dPr = (dO U^T) . D and the decay terms
+  // of dGam
+  float *s_q = s_ar, *s_dp = s_ar + G::TILE;
+  rq.put(s_q);
+  RowTile<float, D> rw;
+  rw.fetch(a.ws_w, b, h, t0, n, a.T, a.H);
+  __syncthreads();
+  {
+    float colacc = 0.f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int t = w + NWV * m, ti = t >> 2, tj = t & 3;
+      f32x4 qk = {0.f, 0.f, 0.f, 0.f};
+      if (tj <= ti)
+        qk = tile_mm_e<D, E>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, qk);
+      float rowp[4], colp = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+        const bool ok = j <= i && s_t.cnt[i] == s_t.cnt[j];
+        const float dpr = ok ? __expf(s_t.gam[i] - s_t.gam[j]) * x_dou[m][q] : 0.f;
+        s_dp[i * G::LC + j] = dpr;
+        const float pa = dpr * qk[q];
+        rowp[q] = pa;
+        colp += pa;
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float x = rowp[q];
+        x += __shfl_xor(x, 1, 64);
+        x += __shfl_xor(x, 2, 64);
+        x += __shfl_xor(x, 4, 64);
+        x += __shfl_xor(x, 8, 64);
+        if ((l & 15) == 0) s_rp[0][w][16 * ti + 4 * (l >> 4) + q] = x;
+      }
+      colp += __shfl_xor(colp, 16, 64);
+      colp += __shfl_xor(colp, 32, 64);
+      colacc += colp;
+    }
+    if (l < 16) s_colp[w][16 * (w & 3) + l] = colacc;   // the wave's column tile, over its row tiles
+  }
+  __syncthreads();
+  if (threadIdx.x < CH) {
+    float x = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) x += s_colp[ww][threadIdx.x];
+    s_cp[0][threadIdx.x] = x;
+  }
+  // dq = dPr K + eg (dO S0^T); dk (part, kept in registers) = dPr^T Q + el (U dS^T);
+  // row partials of Q . (dO S0^T) and el (U dS^T) . K
+  f32x4 dkp[4];
+  {
+    E* dq = reinterpret_cast<E*>(a.dq);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int ti = m, tj = w;
+      f32x4 x = tile_mm_e<CH, E>([&](int i, int k) { return s_dp[(16 * ti + i) * G::LC + k]; },
+                        [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+      f32x4 z = tile_mm_e<CH, E>([&](int i, int k) { return s_dp[k * G::LC + 16 * ti + i]; },
+                        [&](int k, int j) { return s_q[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+        const float eg = s_t.eg[i], el = s_t.el[i];
+        const float y = x_dos[m][q];
+        if (i < n) dq[((b * a.T + t0 + i) * a.H + h) * D + j] = (E)(x[q] + eg * y);
+        const float ue = el * x_uds[m][q];
+        dkp[m][q] = z[q] + ue;
+        float p1 = eg * y * s_q[i * G::LD + j];
+        float p2 = ue * s_k[i * G::LD + j];
+        p1 += __shfl_xor(p1, 1, 64);
+        p1 += __shfl_xor(p1, 2, 64);
+        p1 += __shfl_xor(p1, 4, 64);
+        p1 += __shfl_xor(p1, 8, 64);
+        p2 += __shfl_xor(p2, 1, 64);
+        p2 += __shfl_xor(p2, 2, 64);
+        p2 += __shfl_xor(p2, 4, 64);
+        p2 += __shfl_xor(p2, 8, 64);
+        if ((l & 15) == 0) {
+          s_rp[1][w][i] = p1;
+          s_rp[2][w][i] = p2;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // dGam (partial) into s_cp[1]
+  if (threadIdx.x < CH) {
+    const int i = threadIdx.x;
+    float rowpa = 0.f, qdos = 0.f, tk = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) {
+      rowpa += s_rp[0][ww][i];
+      qdos += s_rp[1][ww][i];
+      tk += s_rp[2][ww][i];
+    }
+    float dgam = rowpa - s_cp[0][i] + qdos - tk;
+    float tks = tk;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) tks += __shfl_xor(tks, off, 64);
+    if (i == CH - 1) {
+      float spp = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < NWV; ++ww) spp += s_red[ww];
+      dgam += tks + s_t.sc[0] * spp;
+    }
+    s_cp[1][i] = dgam;
+  }
+  // W and dW = -dU S0^T in the slice space (Q and dPr are dead)
+  float *s_w = s_ar, *s_dW = s_ar + G::TILE;
+  rw.put(s_w);
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s_dW[(16 * m + 4 * (l >> 4) + q) * G::LD + 16 * w + (l & 15)] = -x_dus[m][q];
+  __syncthreads();
+  // dBk = T^T dW in place, held in registers until every wave has read dW
+  {
+    f32x4 res[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int ti = m, tj = w;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int kt = ti; kt < 4; ++kt)
+        acc = tile_mm<16>([&](int i, int q) { return s_tm[(16 * kt + q) * G::LC + 16 * ti + i]; },
+                          [&](int q, int j) { return s_dW[(16 * kt + q) * G::LD + 16 * tj + j]; }, acc);
+      res[m] = acc;
+    }
+    for (int e = threadIdx.x; e < 2 * NWV * CH; e += NTH) (&s_rp[0][0][0])[e] = 0.f;
+    for (int e = threadIdx.x; e < NWV * CH; e += NTH) (&s_colp[0][0])[e] = 0.f;
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s_dW[(16 * m + 4 * (l >> 4) + q) * G::LD + 16 * w + (l & 15)] = res[m][q];
+  }
+  __syncthreads();
+  // dA = strict-lower(-(dBv U~^T + dBk W^T)); dAr = dA . D . beta_i in place of T;
+  // row sums of dA . D . KK^T (dbeta) and column sums of dA . A (dGam)
+  {
+    float colacc = 0.f;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int t = w + NWV * m, ti = t >> 2, tj = t & 3;
+      f32x4 x = x_dbu[m], kk = {0.f, 0.f, 0.f, 0.f};
+      if (tj <= ti) {
+        x = tile_mm_e<D, E>([&](int i, int k) { return s_dW[(16 * ti + i) * G::LD + k]; },
+                    [&](int k, int j) { return s_w[(16 * tj + j) * G::LD + k]; }, x);
+        kk = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, kk);
+      }
+      float colp = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+        const bool ok = j < i && s_t.cnt[i] == s_t.cnt[j];
+        const float dec = ok ? __expf(s_t.gam[i] - s_t.gam[j]) : 0.f;
+        const float da = ok ? -x[q] : 0.f;
+        const float r1 = da * dec * kk[q];
+        s_tm[i * G::LC + j] = da * dec * s_t.beta[i];
+        colp += r1 * s_t.beta[i];
+        float x1 = r1;
+        x1 += __shfl_xor(x1, 1, 64);
+        x1 += __shfl_xor(x1, 2, 64);
+        x1 += __shfl_xor(x1, 4, 64);
+        x1 += __shfl_xor(x1, 8, 64);
+        if ((l & 15) == 0) s_rp[0][w][i] = x1;
+      }
+      colp += __shfl_xor(colp, 16, 64);
+      colp += __shfl_xor(colp, 32, 64);
+      colacc += colp;
+    }
+    if (l < 16) s_colp[w][16 * (w & 3) + l] = colacc;
+  }
+  __syncthreads();
+  if (threadIdx.x < CH) {
+    float x = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) x += s_colp[ww][threadIdx.x];
+    s_cp[0][threadIdx.x] = x;
+  }
+  __syncthreads();
+  // dk = part + dAr K + dAr^T K + beta eg dBk
+  {
+    E* dk = reinterpret_cast<E*>(a.dk);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int ti = m, tj = w;
+      f32x4 x = tile_mm_e<CH, E>([&](int i, int k) { return s_tm[(16 * ti + i) * G::LC + k]; },
+                        [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, dkp[m]);
+      x = tile_mm_e<CH, E>([&](int i, int k) { return s_tm[k * G::LC + 16 * ti + i]; },
+                  [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, x);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+        if (i < n)
+          dk[((b * a.T + t0 + i) * a.H + h) * D + j] = (E)(x[q] + s_t.beta[i] * s_t.eg[i] * s_dW[i * G::LD + j]);
+      }
+    }
+  }
+  // dbeta and dg (wave 0, lane = token)
+  if (threadIdx.x < CH) {
+    const int i = threadIdx.x;
+    float r3 = 0.f;
+    for (int j = 0; j < D; ++j) r3 += s_dW[i * G::LD + j] * s_k[i * G::LD + j];
+    float r1 = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NWV; ++ww) r1 += s_rp[0][ww][i];
+    const float bt = s_t.beta[i], eg = s_t.eg[i];
+    const float dbeta = r1 + r2 + eg * r3;
+    const float dgam = s_cp[1][i] + bt * r1 - s_cp[0][i] + bt * eg * r3;
+    const int cnt = s_t.cnt[i];
+    float x = dgam;
+#pragma unroll
+    for (int off = 1; off < CH; off <<= 1) {
+      const float y = __shfl_down(x, off, 64);
+      const int cy = __shfl_down(cnt, off, 64);
+      if (i + off < CH && cy == cnt) x += y;
+    }
+    const bool start = i == 0 ? (seq && cnt == 1) : cnt != s_t.cnt[i - 1];
+    if (i < n) {
+      a.dbeta[(b * a.T + t0 + i) * a.H + h] = dbeta;
+      a.dg[(b * a.T + t0 + i) * a.H + h] = start ? 0.f : x;
+    }
+  }
+}
+
+#define CPLA_INST_DELTA_WALKS(E, D)                                            \
   template __global__ void delta_wy<E, D>(DeltaArgs);                          \
   template __global__ void delta_fwalk<E, D, false>(DeltaArgs);                \
   template __global__ void delta_fwalk<E, D, true>(DeltaArgs);                 \
   template __global__ void delta_out<E, D>(DeltaArgs);                         \
   template __global__ void delta_bwalk<E, D, false>(DeltaArgs);                \
-  template __global__ void delta_bwalk<E, D, true>(DeltaArgs);                 \
+  template __global__ void delta_bwalk<E, D, true>(DeltaArgs);
+#define CPLA_INST_DELTA(E, D)                                                  \
+  CPLA_INST_DELTA_WALKS(E, D)                                                  \
   template __global__ void delta_grad<E, D>(DeltaArgs);
 CPLA_INST_DELTA(float, 16)
 CPLA_INST_DELTA(float, 32)
@@ -1067,8 +1481,11 @@ CPLA_INST_DELTA(float, 64)
 CPLA_INST_DELTA(bf16_t, 16)
 CPLA_INST_DELTA(bf16_t, 32)
 CPLA_INST_DELTA(bf16_t, 64)
+CPLA_INST_DELTA_WALKS(bf16_t, 128)
+template __global__ void delta_grad_wide<bf16_t, 128>(DeltaArgs);
 template __global__ void delta_scan<16>(DeltaScanArgs);
 template __global__ void delta_scan<32>(DeltaScanArgs);
 template __global__ void delta_scan<64>(DeltaScanArgs);
+template __global__ void delta_scan<128>(DeltaScanArgs);
 
 }  // namespace cpla

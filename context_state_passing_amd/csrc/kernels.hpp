@@ -60,6 +60,19 @@ struct ScanArgs {
 // at every chunk's end) [B,H,row_chunks,D,D].
 constexpr int DELTA_THREADS = 512;   // threads per workgroup of every delta-rule kernel
 
+// State columns per workgroup (the grid's z extent is the width over these): the
+// state's columns evolve independently, and at D = 128 a whole fp32 state with the
+// chunk's tiles does not fit the LDS.
+template <int D> struct DeltaSlabs {
+  static constexpr int OUT = D <= 64 ? D : 64;     // delta_out: value columns
+  static constexpr int BWALK = D <= 64 ? D : 32;   // delta_bwalk: value columns of dS
+  static constexpr int GRAD = 32;                  // delta_grad_wide: value slice
+};
+template <int D, bool APPLY> struct FwalkSlab {     // delta_fwalk: columns of [delta_S | M] or S
+  static constexpr int NZ = APPLY ? D : 2 * D;
+  static constexpr int SZ = D <= 64 ? NZ : 64;
+};
+
 struct DeltaArgs {
   int64_t B, T, H;
   int P, rank_begin;
@@ -104,6 +117,7 @@ template <int D> __global__ void delta_scan(DeltaScanArgs a);
 template <typename E, int D> __global__ void delta_out(DeltaArgs a);
 template <typename E, int D, bool APPLY> __global__ void delta_bwalk(DeltaArgs a);
 template <typename E, int D> __global__ void delta_grad(DeltaArgs a);
+template <typename E, int D> __global__ void delta_grad_wide(DeltaArgs a);
 
 // TAIL: some shard's length is not a multiple of the chunk (a partial last chunk
 // to mask); without it every guard compiles away.

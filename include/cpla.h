@@ -290,7 +290,7 @@ cpla_status cpla_seq_idx_from_cu_seqlens(const int32_t* cu_seqlens, int32_t n_se
  *   o_t = S_t^T q_t,  S_{t-1} := 0 where token t starts a packed sequence,
  * so M is a full d_k x d_k matrix (zero for a shard holding a start) and the
  * composition multiplies matrices (M^T backwards). Problem: decay =
- * CPLA_DECAY_DELTA, dk == dv in {16, 32, 64}, dtype fp32 or bf16; g and beta
+ * CPLA_DECAY_DELTA, dk == dv in {16, 32, 64} (fp32 or bf16) or 128 (bf16); g and beta
  * [B,T,H] fp32 (beta is the write strength, usually in (0, 1); keys are usually
  * L2-normalised by the caller, and q carries any scale). Summary records
  * (cpla_summary_width = dk*dk + dk*dv floats): [M (dk x dk, row-major) | delta_S

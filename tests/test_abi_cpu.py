@@ -288,6 +288,11 @@ def test_delta_validation():
         assert L.cpla_delta_workspace_bytes(ctypes.byref(q)) == -1, bad
         st = L.cp_forward_prepare_delta(ctypes.byref(q), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
         assert st in (1, 5), (bad, st)
+    # d = 128 is taken in bf16 (fp32 is refused above); other head sizes are not
+    wide = prob(dk=128, dv=128, dtype=_lib.BF16, decay=_lib.DECAY_DELTA, T=1000, num_shards=3, rank_end=3)
+    assert L.cpla_delta_workspace_bytes(ctypes.byref(wide)) == 4 * (4 * 2 * tok + 2 * 1 * 2 * nct * 128 * 128)
+    odd = prob(dk=96, dv=96, dtype=_lib.BF16, decay=_lib.DECAY_DELTA)
+    assert L.cpla_delta_workspace_bytes(ctypes.byref(odd)) == -1
     # a NULL workspace or beta is refused before any launch
     assert L.cp_forward_prepare_delta(ctypes.byref(p), None, FAKE, FAKE, FAKE, None, FAKE, FAKE, None) == 1
     assert L.cp_forward_prepare_delta(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == 1

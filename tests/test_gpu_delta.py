@@ -6,7 +6,7 @@ composed incoming states, every gradient (dq, dk, dv, dg, dbeta, dS_init), the
 backward summaries (gamma) and the composed outgoing gradients.
 
 Cases span several chunks per shard and several shards, d = 16, 32, 64 in fp32
-and bf16, an initial state, uneven shards with partial last chunks and empty
+and bf16 and d = 128 in bf16, an initial state, uneven shards with partial last chunks and empty
 shards, and packed sequences (one stream, and one packing per batch row) with
 boundaries inside chunks. Tolerances are the linear-attention ones (fp32 rtol
 1e-4 / atol 1e-5, bf16 rtol 2e-2 / atol 2e-3).
@@ -34,6 +34,11 @@ CASES = {
     "fp32_d64_packed": dict(B=1, T=768, H=2, d=64, num_shards=4, packed=True, len_range=(30, 300),
                             dtype=torch.float32),
     "bf16_d64_rows_packed": dict(B=2, T=640, H=2, d=64, num_shards=5, packed=True, len_range=(1, 200)),
+    # d = 128 (bf16): walks over state-column slabs, gradients over value slices
+    "bf16_d128": dict(B=1, T=1024, H=2, d=128, num_shards=4),
+    "bf16_d128_init_uneven": dict(B=1, T=500, H=2, d=128, num_shards=3, with_initial_state=True),
+    "bf16_d128_rows_packed": dict(B=2, T=640, H=1, d=128, num_shards=5, packed=True, len_range=(1, 200)),
+    "bf16_d128_empty_shards": dict(B=1, T=150, H=1, d=128, num_shards=40),
 }
 
 
@@ -115,6 +120,34 @@ def _delta_sweep(seed, n):
 def test_random_delta_problems(case, gpu_available):
     over = _delta_sweep(2026, 30)[case]
     print(f"[gpu-case] delta random {case}: {over}", file=sys.stderr, flush=True)
+    wl = workloads.make_delta(**over)
+    got, ref = _run_gpu(wl), _run_oracle(wl)
+    rtol, atol = tolerances(wl.dtype)
+    for name in ref:
+        assert_close(name, got[name], ref[name], rtol, atol)
+
+
+def _delta_sweep_wide(seed, n):
+    """Seeded random d = 128 (bf16) problems: ragged lengths, uneven and empty
+    shards, packing, an initial state."""
+    import random
+    rng = random.Random(seed)
+    out = []
+    for _ in range(n):
+        over = dict(B=rng.choice([1, 2]), T=rng.choice([rng.randint(1, 130), rng.randint(64, 400)]),
+                    H=rng.choice([1, 2]), d=128, num_shards=rng.randint(1, 7), dtype=torch.bfloat16)
+        if rng.random() < 0.35:
+            over.update(packed=True, len_range=(1, rng.randint(1, 250)))
+        elif rng.random() < 0.4:
+            over.update(with_initial_state=True)
+        out.append(over)
+    return out
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_delta_problems_d128(case, gpu_available):
+    over = _delta_sweep_wide(2027, 8)[case]
+    print(f"[gpu-case] delta random d128 {case}: {over}", file=sys.stderr, flush=True)
     wl = workloads.make_delta(**over)
     got, ref = _run_gpu(wl), _run_oracle(wl)
     rtol, atol = tolerances(wl.dtype)
