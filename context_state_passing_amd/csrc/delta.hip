@@ -70,10 +70,14 @@ __device__ __forceinline__ f32x4 tile_mm(const FA& a, const FB& b, f32x4 acc) {
 // splits each fp32 operand into bf16 hi + lo and issues hi*hi, hi*lo and lo*hi, so
 // the product keeps about 16 significant bits per operand (the LDS tiles and
 // intermediates stay fp32) at 3 bf16 MFMAs per 32-deep step instead of 8 fp32
-// ones. fp32 inputs keep the fp32 product (tile_mm).
-template <int K, class FA, class FB>
+// ones. An operand flagged exact (AX, BX) holds bf16 values exactly (a bf16 input
+// read back from its widened tile, unscaled): its lo part is zero, so it is
+// converted without a split and the products with its lo part are not issued (the
+// sum is the same). fp32 inputs keep the fp32 product (tile_mm).
+template <int K, bool AX, bool BX, class FA, class FB>
 __device__ __forceinline__ f32x4 tile_mm_split(const FA& a, const FB& b, f32x4 acc) {
   static_assert(K % 32 == 0, "32-deep steps");
+  typedef float f32x8 __attribute__((ext_vector_type(8)));
   const int l = lane_id(), x = l & 15, kg = l >> 4;
 #pragma unroll
   for (int st = 0; st < K / 32; ++st) {
@@ -84,18 +88,20 @@ __device__ __forceinline__ f32x4 tile_mm_split(const FA& a, const FB& b, f32x4 a
       bv[e] = b(32 * st + 8 * kg + e, x);
     }
     Frag<bf16_t> ah, al, bh, bl;
-    split_frag(ah, al, av);
-    split_frag(bh, bl, bv);
+    if constexpr (AX) ah.v = __builtin_convertvector((f32x8{av[0], av[1], av[2], av[3], av[4], av[5], av[6], av[7]}), bf16x8);
+    else split_frag(ah, al, av);
+    if constexpr (BX) bh.v = __builtin_convertvector((f32x8{bv[0], bv[1], bv[2], bv[3], bv[4], bv[5], bv[6], bv[7]}), bf16x8);
+    else split_frag(bh, bl, bv);
     mma(acc, ah, bh);
-    mma(acc, ah, bl);
-    mma(acc, al, bh);
+    if constexpr (!BX) mma(acc, ah, bl);
+    if constexpr (!AX) mma(acc, al, bh);
   }
   return acc;
 }
 // tile_mm for fp32 inputs, tile_mm_split for bf16 inputs (K a multiple of 32)
-template <int K, typename E, class FA, class FB>
+template <int K, typename E, bool AX = false, bool BX = false, class FA, class FB>
 __device__ __forceinline__ f32x4 tile_mm_e(const FA& a, const FB& b, f32x4 acc) {
-  if constexpr (sizeof(E) == 2 && K % 32 == 0) return tile_mm_split<K>(a, b, acc);
+  if constexpr (sizeof(E) == 2 && K % 32 == 0) return tile_mm_split<K, AX, BX>(a, b, acc);
   else return tile_mm<K>(a, b, acc);
 }
 
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti)
-      acc = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+      acc = tile_mm_e<D, E, true, true>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -603,7 +609,7 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti)
-      acc = tile_mm_e<D, E>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+      acc = tile_mm_e<D, E, true, true>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -616,7 +622,7 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
   E* o = reinterpret_cast<E*>(a.out);
   for (int t = w; t < 4 * (SV / 16); t += NWV) {
     const int ti = t / (SV / 16), tj = t % (SV / 16);
-    f32x4 x = tile_mm_e<D, E>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+    f32x4 x = tile_mm_e<D, E, true, false>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                       [&](int k, int j) { return s_s[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
     f32x4 y = tile_mm_e<CH, E>([&](int i, int k) { return s_p[(16 * ti + i) * G::LC + k]; },
                       [&](int k, int j) { return s_u[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -683,7 +689,7 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
       const int ti = t >> 2, tj = t & 3;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       if (tj <= ti)
-        acc = tile_mm_e<D, E>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+        acc = tile_mm_e<D, E, true, true>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                       [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -696,7 +702,7 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
     // dU = P^T dO + K~ dS
     for (int t = w; t < 4 * (SV / 16); t += NWV) {
       const int ti = t / (SV / 16), tj = t % (SV / 16);
-      f32x4 acc = tile_mm_e<CH, E>([&](int i, int k) { return s_p[k * G::LC + 16 * ti + i]; },
+      f32x4 acc = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_p[k * G::LC + 16 * ti + i]; },
                           [&](int k, int j) { return s_do[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
       acc = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k] * s_t.el[16 * ti + i]; },
                     [&](int k, int j) { return s_ds[k * LV + 16 * tj + j]; }, acc);
@@ -709,7 +715,7 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
     const float sc = s_t.sc[0];
     for (int t = w; t < G::NTC * (SV / 16); t += NWV) {
       const int ti = t / (SV / 16), tj = t % (SV / 16);
-      f32x4 x = tile_mm_e<CH, E>([&](int i, int k) { return s_q[k * G::LD + 16 * ti + i] * s_t.eg[k]; },
+      f32x4 x = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_q[k * G::LD + 16 * ti + i] * s_t.eg[k]; },
                         [&](int k, int j) { return s_do[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 y = tile_mm_e<CH, E>([&](int i, int k) { return s_w[k * G::LD + 16 * ti + i]; },
                         [&](int k, int j) { return s_du[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -796,9 +802,9 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
       const int ti = t >> 2, tj = t & 3;
       f32x4 qk = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
       if (tj <= ti) {
-        qk = tile_mm_e<D, E>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+        qk = tile_mm_e<D, E, true, true>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                      [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, qk);
-        du = tile_mm_e<D, E>([&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
+        du = tile_mm_e<D, E, true, false>([&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
                      [&](int k, int j) { return s_u[(16 * tj + j) * G::LD + k]; }, du);
       }
       float rowp[4], colp = 0.f;
@@ -842,11 +848,11 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     E* dq = reinterpret_cast<E*>(a.dq);
     for (int t = w; t < 4 * G::NTC; t += NWV) {
       const int ti = t / G::NTC, tj = t % G::NTC;
-      f32x4 x = tile_mm_e<CH, E>([&](int i, int k) { return s_dp[(16 * ti + i) * G::LC + k]; },
+      f32x4 x = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_dp[(16 * ti + i) * G::LC + k]; },
                         [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 y = tile_mm_e<D, E>([&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
+      f32x4 y = tile_mm_e<D, E, true, false>([&](int i, int k) { return s_do[(16 * ti + i) * G::LD + k]; },
                         [&](int k, int j) { return s_s0[(16 * tj + j) * G::LD + k]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 z = tile_mm_e<CH, E>([&](int i, int k) { return s_dp[k * G::LC + 16 * ti + i]; },
+      f32x4 z = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_dp[k * G::LC + 16 * ti + i]; },
                         [&](int k, int j) { return s_q[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 u = tile_mm_e<D, E>([&](int i, int k) { return s_u[(16 * ti + i) * G::LD + k]; },
                         [&](int k, int j) { return s_ds[(16 * tj + j) * G::LD + k]; }, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -934,7 +940,7 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti)
-      acc = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+      acc = tile_mm_e<D, E, true, true>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -994,7 +1000,7 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
                     [&](int k, int j) { return s_ut[(16 * tj + j) * G::LD + k]; }, x);
         x = tile_mm_e<D, E>([&](int i, int k) { return s_dW[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_w[(16 * tj + j) * G::LD + k]; }, x);
-        kk = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+        kk = tile_mm_e<D, E, true, true>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
                      [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, kk);
       }
       float colp = 0.f;
@@ -1034,9 +1040,9 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     E* dv = reinterpret_cast<E*>(a.dv);
     for (int t = w; t < 4 * G::NTC; t += NWV) {
       const int ti = t / G::NTC, tj = t % G::NTC;
-      f32x4 x = tile_mm_e<CH, E>([&](int i, int k) { return s_a[(16 * ti + i) * G::LC + k]; },
+      f32x4 x = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_a[(16 * ti + i) * G::LC + k]; },
                         [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      x = tile_mm_e<CH, E>([&](int i, int k) { return s_a[k * G::LC + 16 * ti + i]; },
+      x = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_a[k * G::LC + 16 * ti + i]; },
                   [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, x);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -1136,7 +1142,7 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti)
-      acc = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+      acc = tile_mm_e<D, E, true, true>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -1186,12 +1192,12 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
     for (int m = 0; m < 2; ++m) {
       const int t = w + NWV * m, ti = t >> 2, tj = t & 3;
       if (tj <= ti)
-        x_dou[m] = tile_mm_e<SV, E>([&](int i, int k) { return s_do[(16 * ti + i) * LV + k]; },
+        x_dou[m] = tile_mm_e<SV, E, true, false>([&](int i, int k) { return s_do[(16 * ti + i) * LV + k]; },
                                     [&](int k, int j) { return s_u[(16 * tj + j) * LV + k]; }, x_dou[m]);
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-      x_dos[m] = tile_mm_e<SV, E>([&](int i, int k) { return s_do[(16 * m + i) * LV + k]; },
+      x_dos[m] = tile_mm_e<SV, E, true, false>([&](int i, int k) { return s_do[(16 * m + i) * LV + k]; },
                                   [&](int k, int j) { return s_s0[(16 * w + j) * LV + k]; }, x_dos[m]);
       x_uds[m] = tile_mm_e<SV, E>([&](int i, int k) { return s_u[(16 * m + i) * LV + k]; },
                                   [&](int k, int j) { return s_ds[(16 * w + j) * LV + k]; }, x_uds[m]);
@@ -1251,7 +1257,7 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
       const int t = w + NWV * m, ti = t >> 2, tj = t & 3;
       f32x4 qk = {0.f, 0.f, 0.f, 0.f};
       if (tj <= ti)
-        qk = tile_mm_e<D, E>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+        qk = tile_mm_e<D, E, true, true>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
                      [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, qk);
       float rowp[4], colp = 0.f;
 #pragma unroll
@@ -1294,9 +1300,9 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int ti = m, tj = w;
-      f32x4 x = tile_mm_e<CH, E>([&](int i, int k) { return s_dp[(16 * ti + i) * G::LC + k]; },
+      f32x4 x = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_dp[(16 * ti + i) * G::LC + k]; },
                         [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      f32x4 z = tile_mm_e<CH, E>([&](int i, int k) { return s_dp[k * G::LC + 16 * ti + i]; },
+      f32x4 z = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_dp[k * G::LC + 16 * ti + i]; },
                         [&](int k, int j) { return s_q[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -1386,7 +1392,7 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
       if (tj <= ti) {
         x = tile_mm_e<D, E>([&](int i, int k) { return s_dW[(16 * ti + i) * G::LD + k]; },
                     [&](int k, int j) { return s_w[(16 * tj + j) * G::LD + k]; }, x);
-        kk = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
+        kk = tile_mm_e<D, E, true, true>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
                      [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, kk);
       }
       float colp = 0.f;
@@ -1426,9 +1432,9 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int ti = m, tj = w;
-      f32x4 x = tile_mm_e<CH, E>([&](int i, int k) { return s_tm[(16 * ti + i) * G::LC + k]; },
+      f32x4 x = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_tm[(16 * ti + i) * G::LC + k]; },
                         [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, dkp[m]);
-      x = tile_mm_e<CH, E>([&](int i, int k) { return s_tm[k * G::LC + 16 * ti + i]; },
+      x = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_tm[k * G::LC + 16 * ti + i]; },
                   [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, x);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

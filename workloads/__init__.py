@@ -288,6 +288,7 @@ class DeltaSpec:
 
 DELTA_SPECS = {
     "delta_fwdbwd": DeltaSpec(7, 2, 8192, 16, 64, torch.bfloat16, 8),
+    "delta_d128_fwdbwd": DeltaSpec(8, 2, 8192, 16, 128, torch.bfloat16, 8),
 }
 
 
