@@ -31,6 +31,8 @@
 // split the state's columns over workgroups and the gradients take the value
 // dimension in slices (delta_grad_wide), as a fp32 state with the chunk's tiles
 // does not fit one workgroup's LDS.
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "shards.hpp"
 
@@ -148,6 +150,29 @@ template <typename E, int D, int W = D> struct RowTile {
       const int e = threadIdx.x + p * NTH, i = e / (W / 4), c = 4 * (e % (W / 4));
       if (NV % NTH == 0 || e < NV) *reinterpret_cast<f32x4*>(dst + i * ld + c) = widen4(v[p]);
     }
+  }
+  // into a tile of the input type itself (no widening)
+  __device__ __forceinline__ void put_raw(E* dst, int ld) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = threadIdx.x + p * NTH, i = e / (W / 4), c = 4 * (e % (W / 4));
+      if (NV % NTH == 0 || e < NV) *reinterpret_cast<R*>(dst + i * ld + c) = v[p];
+    }
+  }
+};
+
+// LDS type and row stride of the raw q, k, v tiles: widened to fp32 as a rule; for
+// bf16 inputs at D = 128 they stay bf16 (exact, half the bytes), which lets the
+// walks and delta_out own wider state slabs. Row strides keep rows 16-byte aligned.
+template <typename E, int D> struct InTile {
+  static constexpr bool raw = sizeof(E) == 2 && D > 64;
+  using T = typename std::conditional<raw, E, float>::type;
+  static constexpr int LD = raw ? D + 8 : D + 4;
+  static constexpr int TILE = CH * LD;
+  // a RowTile into such a tile
+  template <class RT> __device__ __forceinline__ static void put(const RT& t, T* dst) {
+    if constexpr (raw) t.put_raw(dst, LD);
+    else t.put(dst, LD);
   }
 };
 
@@ -330,7 +355,9 @@ __device__ __forceinline__ void unit_lower_inverse(float* s_a) {
 template <typename E, int D>
 __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
   using G = DGeo<D>;
-  __shared__ __attribute__((aligned(16))) float s_k[G::TILE], s_v[G::TILE], s_a[G::TILE_C];
+  using IT = InTile<E, D>;
+  __shared__ __attribute__((aligned(16))) typename IT::T s_k[IT::TILE], s_v[IT::TILE];
+  __shared__ __attribute__((aligned(16))) float s_a[G::TILE_C];
   __shared__ ChunkTerms s_t;
   int64_t r, c;
   const int64_t idx = a.chunk_begin + blockIdx.x;
@@ -348,8 +375,8 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
     rk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
     rv.fetch(reinterpret_cast<const E*>(a.v), b, h, t0, n, a.T, a.H);
     chunk_terms(s_t, tr);
-    rk.put(s_k);
-    rv.put(s_v);
+    IT::put(rk, s_k);
+    IT::put(rv, s_v);
   }
   __syncthreads();
 
@@ -359,8 +386,8 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti)
-      acc = tile_mm_e<D, E, true, true>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k]; },
-                    [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
+      acc = tile_mm_e<D, E, true, true>([&](int i, int k) { return (float)s_k[(16 * ti + i) * IT::LD + k]; },
+                    [&](int k, int j) { return (float)s_k[(16 * tj + j) * IT::LD + k]; }, acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
@@ -379,14 +406,14 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
     for (int t = w; t < NT_; t += NWV) {
       const int ti = t / NCT, tj = t % NCT;
       const bool isv = tj < NCT / 2;
-      const float* src = isv ? s_v : s_k;
+      const typename IT::T* src = isv ? s_v : s_k;
       const int c0 = 16 * (isv ? tj : tj - NCT / 2);
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int kt = 0; kt <= ti; ++kt)
         acc = tile_mm<16>([&](int i, int q) { return s_a[(16 * ti + i) * G::LC + 16 * kt + q]; },
                           [&](int q, int j) {
                             const int k = 16 * kt + q;
-                            return src[k * G::LD + c0 + j] * (isv ? s_t.beta[k] : s_t.beta[k] * s_t.eg[k]);
+                            return (float)src[k * IT::LD + c0 + j] * (isv ? s_t.beta[k] : s_t.beta[k] * s_t.eg[k]);
                           }, acc);
       float* dst = isv ? a.ws_ut : a.ws_w;
 #pragma unroll
@@ -410,7 +437,9 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
   constexpr int NZ = APPLY ? D : 2 * D;
   constexpr int SZ = FwalkSlab<D, APPLY>::SZ;
   constexpr int LZ = SZ + 4;
-  __shared__ __attribute__((aligned(16))) float s_z[D * LZ], s_u[CH * LZ], s_w[G::TILE], s_k[G::TILE];
+  using IT = InTile<E, D>;
+  __shared__ __attribute__((aligned(16))) float s_z[D * LZ], s_u[CH * LZ], s_w[G::TILE];
+  __shared__ __attribute__((aligned(16))) typename IT::T s_k[IT::TILE];
   __shared__ ChunkTerms s_t;
   const int64_t r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
@@ -450,7 +479,7 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     const int64_t t0 = tshard + 64 * c;
     const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
     pw.put(s_w);
-    pk.put(s_k);
+    IT::put(pk, s_k);
     // U~ into the slab's delta_S columns of s_u (the M part takes no input)
     if (takes_u) pu.put(s_u, LZ);
     if constexpr (SZ > UW || NZ > D) {
@@ -485,7 +514,7 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
     const float sc = s_t.sc[0];
     for (int t = w; t < (D / 16) * (SZ / 16); t += NWV) {
       const int ti = t / (SZ / 16), tj = t % (SZ / 16);
-      f32x4 acc = tile_mm_e<CH, E>([&](int i, int k) { return s_k[k * G::LD + 16 * ti + i] * s_t.el[k]; },
+      f32x4 acc = tile_mm_e<CH, E>([&](int i, int k) { return (float)s_k[k * IT::LD + 16 * ti + i] * s_t.el[k]; },
                           [&](int k, int j) { return s_u[k * LZ + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -573,8 +602,9 @@ template <typename E, int D>
 __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
   using G = DGeo<D>;
   constexpr int SV = DeltaSlabs<D>::OUT, LV = SV + 4;
-  __shared__ __attribute__((aligned(16))) float s_q[G::TILE], s_k[G::TILE], s_u[CH * LV], s_s[D * LV],
-      s_p[G::TILE_C];
+  using IT = InTile<E, D>;
+  __shared__ __attribute__((aligned(16))) typename IT::T s_q[IT::TILE], s_k[IT::TILE];
+  __shared__ __attribute__((aligned(16))) float s_u[CH * LV], s_s[D * LV], s_p[G::TILE_C];
   __shared__ ChunkTerms s_t;
   int64_t r, c;
   const int64_t idx = a.chunk_begin + blockIdx.x;
@@ -599,8 +629,8 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
     ru.fetch(a.ws_u, b, h, t0, n, a.T, a.H, v0);
     rs.fetch(a.chunk_states + (bh * nct + idx) * (int64_t)(D * D), v0);
     chunk_terms(s_t, tr);
-    rq.put(s_q);
-    rk.put(s_k);
+    IT::put(rq, s_q);
+    IT::put(rk, s_k);
     ru.put(s_u);
     rs.put(s_s);
   }
@@ -609,8 +639,8 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
     const int ti = t >> 2, tj = t & 3;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (tj <= ti)
-      acc = tile_mm_e<D, E, true, true>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
-                    [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
+      acc = tile_mm_e<D, E, true, true>([&](int i, int k) { return (float)s_q[(16 * ti + i) * IT::LD + k]; },
+                    [&](int k, int j) { return (float)s_k[(16 * tj + j) * IT::LD + k]; }, acc);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
@@ -622,7 +652,7 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
   E* o = reinterpret_cast<E*>(a.out);
   for (int t = w; t < 4 * (SV / 16); t += NWV) {
     const int ti = t / (SV / 16), tj = t % (SV / 16);
-    f32x4 x = tile_mm_e<D, E, true, false>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
+    f32x4 x = tile_mm_e<D, E, true, false>([&](int i, int k) { return (float)s_q[(16 * ti + i) * IT::LD + k]; },
                       [&](int k, int j) { return s_s[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
     f32x4 y = tile_mm_e<CH, E>([&](int i, int k) { return s_p[(16 * ti + i) * G::LC + k]; },
                       [&](int k, int j) { return s_u[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
@@ -644,8 +674,10 @@ template <typename E, int D, bool APPLY>
 __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
   using G = DGeo<D>;
   constexpr int SV = DeltaSlabs<D>::BWALK, LV = SV + 4;
-  __shared__ __attribute__((aligned(16))) float s_q[G::TILE], s_k[G::TILE], s_do[CH * LV], s_w[G::TILE],
-      s_du[CH * LV], s_ds[D * LV], s_p[G::TILE_C];
+  using IT = InTile<E, D>;
+  __shared__ __attribute__((aligned(16))) typename IT::T s_q[IT::TILE], s_k[IT::TILE];
+  __shared__ __attribute__((aligned(16))) float s_do[CH * LV], s_w[G::TILE], s_du[CH * LV], s_ds[D * LV],
+      s_p[G::TILE_C];
   __shared__ ChunkTerms s_t;
   const int64_t r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
@@ -678,8 +710,8 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
   for (int c = nc - 1; c >= 0; --c) {
     const int64_t t0 = tshard + 64 * c;
     const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
-    pq.put(s_q);
-    pk.put(s_k);
+    IT::put(pq, s_q);
+    IT::put(pk, s_k);
     pdo.put(s_do);
     pw.put(s_w);
     chunk_terms(s_t, pt);
@@ -689,8 +721,8 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
       const int ti = t >> 2, tj = t & 3;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       if (tj <= ti)
-        acc = tile_mm_e<D, E, true, true>([&](int i, int k) { return s_q[(16 * ti + i) * G::LD + k]; },
-                      [&](int k, int j) { return s_k[(16 * tj + j) * G::LD + k]; }, acc);
+        acc = tile_mm_e<D, E, true, true>([&](int i, int k) { return (float)s_q[(16 * ti + i) * IT::LD + k]; },
+                      [&](int k, int j) { return (float)s_k[(16 * tj + j) * IT::LD + k]; }, acc);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
@@ -699,13 +731,21 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
       }
     }
     __syncthreads();
-    // dU = P^T dO + K~ dS
+    // dU = P^T dO + K~ dS; with bf16 k tiles the row factor of K~ = el K is applied to
+    // the product instead (k stays exact)
     for (int t = w; t < 4 * (SV / 16); t += NWV) {
       const int ti = t / (SV / 16), tj = t % (SV / 16);
       f32x4 acc = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_p[k * G::LC + 16 * ti + i]; },
                           [&](int k, int j) { return s_do[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      acc = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * G::LD + k] * s_t.el[16 * ti + i]; },
-                    [&](int k, int j) { return s_ds[k * LV + 16 * tj + j]; }, acc);
+      if constexpr (IT::raw) {
+        const f32x4 y = tile_mm_e<D, E, true, false>([&](int i, int k) { return (float)s_k[(16 * ti + i) * IT::LD + k]; },
+                      [&](int k, int j) { return s_ds[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] += s_t.el[16 * ti + 4 * (l >> 4) + q] * y[q];
+      } else {
+        acc = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * IT::LD + k] * s_t.el[16 * ti + i]; },
+                      [&](int k, int j) { return s_ds[k * LV + 16 * tj + j]; }, acc);
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) s_du[(16 * ti + 4 * (l >> 4) + q) * LV + 16 * tj + (l & 15)] = acc[q];
     }
@@ -715,7 +755,7 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
     const float sc = s_t.sc[0];
     for (int t = w; t < G::NTC * (SV / 16); t += NWV) {
       const int ti = t / (SV / 16), tj = t % (SV / 16);
-      f32x4 x = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_q[k * G::LD + 16 * ti + i] * s_t.eg[k]; },
+      f32x4 x = tile_mm_e<CH, E, false, true>([&](int i, int k) { return (float)s_q[k * IT::LD + 16 * ti + i] * s_t.eg[k]; },
                         [&](int k, int j) { return s_do[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 y = tile_mm_e<CH, E>([&](int i, int k) { return s_w[k * G::LD + 16 * ti + i]; },
                         [&](int k, int j) { return s_du[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});

@@ -64,13 +64,13 @@ constexpr int DELTA_THREADS = 512;   // threads per workgroup of every delta-rul
 // state's columns evolve independently, and at D = 128 a whole fp32 state with the
 // chunk's tiles does not fit the LDS.
 template <int D> struct DeltaSlabs {
-  static constexpr int OUT = D <= 64 ? D : 64;     // delta_out: value columns
-  static constexpr int BWALK = D <= 64 ? D : 32;   // delta_bwalk: value columns of dS
+  static constexpr int OUT = D;                    // delta_out: value columns
+  static constexpr int BWALK = D <= 64 ? D : 64;   // delta_bwalk: value columns of dS
   static constexpr int GRAD = 32;                  // delta_grad_wide: value slice
 };
 template <int D, bool APPLY> struct FwalkSlab {     // delta_fwalk: columns of [delta_S | M] or S
   static constexpr int NZ = APPLY ? D : 2 * D;
-  static constexpr int SZ = D <= 64 ? NZ : 64;
+  static constexpr int SZ = D <= 64 ? NZ : D;
 };
 
 struct DeltaArgs {
