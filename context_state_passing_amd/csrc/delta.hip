@@ -162,10 +162,11 @@ template <typename E, int D, int W = D> struct RowTile {
 };
 
 // LDS type and row stride of the raw q, k, v tiles: widened to fp32 as a rule; for
-// bf16 inputs at D = 128 they stay bf16 (exact, half the bytes), which lets the
-// walks and delta_out own wider state slabs. Row strides keep rows 16-byte aligned.
-template <typename E, int D> struct InTile {
-  static constexpr bool raw = sizeof(E) == 2 && D > 64;
+// bf16 inputs at D = 128 (and where a kernel asks for it, RAW) they stay bf16
+// (exact, half the bytes), which lets the walks and delta_out own wider state
+// slabs, or more workgroups share a CU. Row strides keep rows 16-byte aligned.
+template <typename E, int D, bool RAW = (D > 64)> struct InTile {
+  static constexpr bool raw = sizeof(E) == 2 && RAW;
   using T = typename std::conditional<raw, E, float>::type;
   static constexpr int LD = raw ? D + 8 : D + 4;
   static constexpr int TILE = CH * LD;
@@ -355,7 +356,7 @@ __device__ __forceinline__ void unit_lower_inverse(float* s_a) {
 template <typename E, int D>
 __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
   using G = DGeo<D>;
-  using IT = InTile<E, D>;
+  using IT = InTile<E, D, (D >= 64)>;
   __shared__ __attribute__((aligned(16))) typename IT::T s_k[IT::TILE], s_v[IT::TILE];
   __shared__ __attribute__((aligned(16))) float s_a[G::TILE_C];
   __shared__ ChunkTerms s_t;
@@ -602,7 +603,7 @@ template <typename E, int D>
 __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
   using G = DGeo<D>;
   constexpr int SV = DeltaSlabs<D>::OUT, LV = SV + 4;
-  using IT = InTile<E, D>;
+  using IT = InTile<E, D, (D >= 64)>;
   __shared__ __attribute__((aligned(16))) typename IT::T s_q[IT::TILE], s_k[IT::TILE];
   __shared__ __attribute__((aligned(16))) float s_u[CH * LV], s_s[D * LV], s_p[G::TILE_C];
   __shared__ ChunkTerms s_t;
