@@ -713,6 +713,12 @@ cpla_status delta_run(DeltaPhase ph, const cpla_problem* p, const DeltaArgs& a, 
   return launched(what);
 }
 
+// one workgroup per (b, h) and slab of the state's columns
+template <int D>
+void delta_scan_launch(const DeltaScanArgs& s, hipStream_t stream) {
+  hipLaunchKernelGGL(delta_scan<D>, dim3((unsigned)s.BH, D / DeltaSlabs<D>::SCAN), dim3(DELTA_THREADS), 0, stream, s);
+}
+
 cpla_status delta_scan_run(const cpla_problem* p, const float* summary, const int32_t* slice, const float* init,
                            float* out, float* fin, int reverse, hipStream_t stream) {
   DeltaScanArgs s = {};
@@ -725,11 +731,10 @@ cpla_status delta_scan_run(const cpla_problem* p, const float* summary, const in
   s.init = init;
   s.out = out;
   s.fin = fin;
-  const dim3 grid((unsigned)s.BH);
-  if (p->dk == 16) hipLaunchKernelGGL(delta_scan<16>, grid, dim3(DELTA_THREADS), 0, stream, s);
-  else if (p->dk == 32) hipLaunchKernelGGL(delta_scan<32>, grid, dim3(DELTA_THREADS), 0, stream, s);
-  else if (p->dk == 64) hipLaunchKernelGGL(delta_scan<64>, grid, dim3(DELTA_THREADS), 0, stream, s);
-  else hipLaunchKernelGGL(delta_scan<128>, grid, dim3(DELTA_THREADS), 0, stream, s);
+  if (p->dk == 16) delta_scan_launch<16>(s, stream);
+  else if (p->dk == 32) delta_scan_launch<32>(s, stream);
+  else if (p->dk == 64) delta_scan_launch<64>(s, stream);
+  else delta_scan_launch<128>(s, stream);
   return launched("delta_scan");
 }
 

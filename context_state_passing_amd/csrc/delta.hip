@@ -541,59 +541,67 @@ __global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
 // unpacked); reverse: out[r] = fold of dS <- M_j^T dS + gamma_j over (r, frs_r)
 // backwards (dS_final at the last rank unpacked). A shard holding a start has
 // M = 0, so folding through it restarts the fold. The running value after the
-// last shard is the final state / dS_init.
+// last shard is the final state / dS_init. The columns of S fold independently: a
+// workgroup owns SC of them (blockIdx.y) and fetches the next shard's M while it
+// folds the current one.
 template <int D>
 __global__ __launch_bounds__(NTH) void delta_scan(DeltaScanArgs a) {
   using G = DGeo<D>;
-  __shared__ __attribute__((aligned(16))) float s_s[D * G::LD], s_m[D * G::LD];
+  constexpr int SC = DeltaSlabs<D>::SCAN, LC = SC + 4;
+  __shared__ __attribute__((aligned(16))) float s_s[D * LC], s_m[D * G::LD];
   const int64_t bh = blockIdx.x;
+  const int c0 = SC == D ? 0 : SC * blockIdx.y;
   const int w = threadIdx.x >> 6, l = lane_id();
   const int32_t* slice = a.slice ? a.slice + (bh / a.H) * a.P : nullptr;
   constexpr int64_t REC = 2 * D * D;
-  for (int e = threadIdx.x; e < D * D; e += NTH)
-    s_s[(e / D) * G::LD + e % D] = a.init ? a.init[bh * D * D + e] : 0.f;
+  for (int e = threadIdx.x; e < D * SC; e += NTH)
+    s_s[(e / SC) * LC + e % SC] = a.init ? a.init[bh * D * D + (e / SC) * D + c0 + e % SC] : 0.f;
+  MatTile<D> pm;
+  auto rec_of = [&](int s) { return a.summary + ((a.reverse ? a.P - 1 - s : s) * a.BH + bh) * REC; };
+  pm.fetch(rec_of(0));
   __syncthreads();
   for (int s = 0; s < a.P; ++s) {
     const int q = a.reverse ? a.P - 1 - s : s;
     if (s > 0 && slice && slice[q] == (a.reverse ? q + 1 : q)) {
-      for (int e = threadIdx.x; e < D * D; e += NTH) s_s[(e / D) * G::LD + e % D] = 0.f;
+      for (int e = threadIdx.x; e < D * SC; e += NTH) s_s[(e / SC) * LC + e % SC] = 0.f;
       __syncthreads();
     }
-    store_mat<D>(a.out + (q * a.BH + bh) * (int64_t)(D * D), s_s);
-    const float* rec = a.summary + (q * a.BH + bh) * REC;
-    load_mat<D>(s_m, rec);
+    store_mat<D, SC>(a.out + (q * a.BH + bh) * (int64_t)(D * D), s_s, c0);
+    const float* rec = rec_of(s);
+    pm.put(s_m);
     __syncthreads();
-    constexpr int NT2 = (D / 16) * (D / 16), PW = (NT2 + NWV - 1) / NWV;
+    if (s + 1 < a.P) pm.fetch(rec_of(s + 1));
+    constexpr int NT2 = (D / 16) * (SC / 16), PW = (NT2 + NWV - 1) / NWV;
     f32x4 res[PW];
 #pragma unroll
     for (int m = 0; m < PW; ++m) {
       const int t = w + NWV * m;
       if (t >= NT2) continue;
-      const int ti = t / (D / 16), tj = t % (D / 16);
+      const int ti = t / (SC / 16), tj = t % (SC / 16);
       f32x4 acc = a.reverse
           ? tile_mm<D>([&](int i, int k) { return s_m[k * G::LD + 16 * ti + i]; },
-                    [&](int k, int j) { return s_s[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f})
+                    [&](int k, int j) { return s_s[k * LC + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f})
           : tile_mm<D>([&](int i, int k) { return s_m[(16 * ti + i) * G::LD + k]; },
-                    [&](int k, int j) { return s_s[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+                    [&](int k, int j) { return s_s[k * LC + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const int i = 16 * ti + 4 * (l >> 4) + u, j = 16 * tj + (l & 15);
+        const int i = 16 * ti + 4 * (l >> 4) + u, j = c0 + 16 * tj + (l & 15);
         acc[u] += rec[D * D + i * D + j];
       }
       res[m] = acc;
     }
-    __syncthreads();   // every read of s_s is done
+    __syncthreads();   // every read of s_s and s_m is done
 #pragma unroll
     for (int m = 0; m < PW; ++m) {
       const int t = w + NWV * m;
       if (t >= NT2) continue;
-      const int ti = t / (D / 16), tj = t % (D / 16);
+      const int ti = t / (SC / 16), tj = t % (SC / 16);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) s_s[(16 * ti + 4 * (l >> 4) + u) * G::LD + 16 * tj + (l & 15)] = res[m][u];
+      for (int u = 0; u < 4; ++u) s_s[(16 * ti + 4 * (l >> 4) + u) * LC + 16 * tj + (l & 15)] = res[m][u];
     }
     __syncthreads();
   }
-  if (a.fin) store_mat<D>(a.fin + bh * (int64_t)(D * D), s_s);
+  if (a.fin) store_mat<D, SC>(a.fin + bh * (int64_t)(D * D), s_s, c0);
 }
 
 // ---- output per chunk --------------------------------------------------------------------

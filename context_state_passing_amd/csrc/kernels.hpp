@@ -67,6 +67,7 @@ template <int D> struct DeltaSlabs {
   static constexpr int OUT = D;                    // delta_out: value columns
   static constexpr int BWALK = D <= 64 ? D : 64;   // delta_bwalk: value columns of dS
   static constexpr int GRAD = 32;                  // delta_grad_wide: value slice
+  static constexpr int SCAN = D <= 32 ? D : 32;    // delta_scan: columns of S or dS
 };
 template <int D, bool APPLY> struct FwalkSlab {     // delta_fwalk: columns of [delta_S | M] or S
   static constexpr int NZ = APPLY ? D : 2 * D;
