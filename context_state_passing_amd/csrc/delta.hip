@@ -1136,20 +1136,22 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
   }
 }
 
-// ---- gradients per chunk, wide heads --------------------------------------------------------
-// The formulas of delta_grad, for heads whose state and value-side tiles do not fit
-// the LDS together (D = 128): the value dimension is taken in slices of SV columns.
+// ---- gradients per chunk, value slices ------------------------------------------------------
+// The formulas of delta_grad with the value dimension taken in slices of SV
+// columns, for heads whose state and value-side tiles do not fit the LDS together
+// (D = 128), or so that two workgroups share a CU (D = 64, 16-column slices, 80 KB).
 // Every contraction over it (dO U^T, dO S0^T, U dS^T, dU S0^T, dBv U~^T, the row sums
 // of dBv . V and <dS, S0>) accumulates over the slices in registers, dv = beta dBv
 // is written slice by slice, and the key-side rest follows once, as in delta_grad.
 template <typename E, int D>
-__global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
+__global__ __launch_bounds__(NTH, DeltaSlabs<D>::GRAD_OCC) void delta_grad_wide(DeltaArgs a) {
   using G = DGeo<D>;
   constexpr int SV = DeltaSlabs<D>::GRAD, LV = SV + 4, NSL = D / SV, NVT = SV / 16;
+  constexpr int KT = 4 * G::NTC / NWV;         // key-shaped [64][D] tiles per wave
   constexpr int TV = CH * LV, TS = D * LV;     // a [64][SV] and a [D][SV] slice tile
   constexpr int ARENA = 5 * TV + 2 * TS;
   static_assert(ARENA >= 2 * G::TILE, "Q and the score tile, then W and dW, reuse the slice tiles");
-  static_assert(4 * G::NTC == 4 * NWV && 4 * NVT == NWV, "tile ownership below assumes D = 8 * 16, SV = 32");
+  static_assert((4 * G::NTC) % NWV == 0 && 4 * NVT <= NWV, "tile ownership");
   __shared__ __attribute__((aligned(16))) float s_k[G::TILE], s_tm[G::TILE_C], s_ar[ARENA];
   __shared__ ChunkTerms s_t;
   __shared__ float s_rp[3][NWV][CH];   // per-wave row partials
@@ -1179,7 +1181,7 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
     TermRegs tr;
     tr.fetch(a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
     rk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
-    rq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
+    if (DeltaSlabs<D>::GRAD_OCC <= 2) rq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
     for (int e = threadIdx.x; e < 3 * NWV * CH; e += NTH) (&s_rp[0][0][0])[e] = 0.f;
     for (int e = threadIdx.x; e < NWV * CH; e += NTH) (&s_colp[0][0])[e] = 0.f;
     chunk_terms(s_t, tr);
@@ -1205,12 +1207,13 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
 
   // Sums over the value dimension. Score-shaped [64][64] tiles: wave w owns tiles
   // w and w + NWV (row tile t / 4, column tile t % 4, lower ones only); key-shaped
-  // [64][D] tiles: wave w owns column tile w of every row tile.
-  f32x4 x_dou[2], x_dbu[2], x_dos[4], x_uds[4], x_dus[4];
+  // [64][D] tiles: wave w owns tiles t = w + NWV m, m < KT (row tile t / NTC, column
+  // tile t % NTC).
+  f32x4 x_dou[2], x_dbu[2], x_dos[KT], x_uds[KT], x_dus[KT];
 #pragma unroll
   for (int m = 0; m < 2; ++m) x_dou[m] = x_dbu[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int m = 0; m < 4; ++m) x_dos[m] = x_uds[m] = x_dus[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int m = 0; m < KT; ++m) x_dos[m] = x_uds[m] = x_dus[m] = f32x4{0.f, 0.f, 0.f, 0.f};
   float sp = 0.f, r2 = 0.f;            // <dS, S0> partial; rowsum(dBv . V) (lane = token, wave 0)
   RowTile<E, D, SV> pdo, pv;
   RowTile<float, D, SV> pu, pdu, put_;
@@ -1224,10 +1227,14 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
     put_.fetch(a.ws_ut, b, h, t0, n, a.T, a.H, v0);
     pv.fetch(reinterpret_cast<const E*>(a.v), b, h, t0, n, a.T, a.H, v0);
   };
-  fetch_slice(0);
+  // at one workgroup per CU the next slice is fetched while this one is computed;
+  // at two the other workgroup covers the loads, and the registers are needed
+  constexpr bool PREFETCH = DeltaSlabs<D>::GRAD_OCC <= 2;
+  if (PREFETCH) fetch_slice(0);
   E* dv = reinterpret_cast<E*>(a.dv);
   for (int sl = 0; sl < NSL; ++sl) {
     const int v0 = SV * sl;
+    if (!PREFETCH) fetch_slice(v0);
     pdo.put(s_do);
     pu.put(s_u);
     pdu.put(s_du);
@@ -1236,7 +1243,7 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
     put_.put(s_ut);
     pv.put(s_v);
     __syncthreads();
-    if (sl + 1 < NSL) fetch_slice(v0 + SV);
+    if (PREFETCH && sl + 1 < NSL) fetch_slice(v0 + SV);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int t = w + NWV * m, ti = t >> 2, tj = t & 3;
@@ -1245,20 +1252,22 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
                                     [&](int k, int j) { return s_u[(16 * tj + j) * LV + k]; }, x_dou[m]);
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      x_dos[m] = tile_mm_e<SV, E, true, false>([&](int i, int k) { return s_do[(16 * m + i) * LV + k]; },
-                                  [&](int k, int j) { return s_s0[(16 * w + j) * LV + k]; }, x_dos[m]);
-      x_uds[m] = tile_mm_e<SV, E>([&](int i, int k) { return s_u[(16 * m + i) * LV + k]; },
-                                  [&](int k, int j) { return s_ds[(16 * w + j) * LV + k]; }, x_uds[m]);
-      x_dus[m] = tile_mm_e<SV, E>([&](int i, int k) { return s_du[(16 * m + i) * LV + k]; },
-                                  [&](int k, int j) { return s_s0[(16 * w + j) * LV + k]; }, x_dus[m]);
+    for (int m = 0; m < KT; ++m) {
+      const int t = w + NWV * m, ti = t / G::NTC, tj = t % G::NTC;
+      x_dos[m] = tile_mm_e<SV, E, true, false>([&](int i, int k) { return s_do[(16 * ti + i) * LV + k]; },
+                                  [&](int k, int j) { return s_s0[(16 * tj + j) * LV + k]; }, x_dos[m]);
+      x_uds[m] = tile_mm_e<SV, E>([&](int i, int k) { return s_u[(16 * ti + i) * LV + k]; },
+                                  [&](int k, int j) { return s_ds[(16 * tj + j) * LV + k]; }, x_uds[m]);
+      x_dus[m] = tile_mm_e<SV, E>([&](int i, int k) { return s_du[(16 * ti + i) * LV + k]; },
+                                  [&](int k, int j) { return s_s0[(16 * tj + j) * LV + k]; }, x_dus[m]);
     }
     for (int e = threadIdx.x; e < D * SV; e += NTH) sp += s_ds[(e / SV) * LV + e % SV] * s_s0[(e / SV) * LV + e % SV];
-    // dBv = T^T dU over the slice (row tile ti takes k tiles ti..3), dv = beta dBv
-    f32x4 bv;
-    {
+    // dBv = T^T dU over the slice (row tile ti takes k tiles ti..3; waves w < 4 NVT,
+    // one tile each), dv = beta dBv
+    f32x4 bv = {0.f, 0.f, 0.f, 0.f};
+    const bool owns_bv = w < 4 * NVT;
+    if (owns_bv) {
       const int ti = w / NVT, tj = w % NVT;
-      bv = f32x4{0.f, 0.f, 0.f, 0.f};
       for (int kt = ti; kt < 4; ++kt)
         bv = tile_mm<16>([&](int i, int q) { return s_tm[(16 * kt + q) * G::LC + 16 * ti + i]; },
                          [&](int q, int j) { return s_du[(16 * kt + q) * LV + 16 * tj + j]; }, bv);
@@ -1269,7 +1278,7 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
       }
     }
     __syncthreads();   // every read of dU is done
-    {
+    if (owns_bv) {
       const int ti = w / NVT, tj = w % NVT;
 #pragma unroll
       for (int q = 0; q < 4; ++q) s_du[(16 * ti + 4 * (l >> 4) + q) * LV + 16 * tj + (l & 15)] = bv[q];
@@ -1295,6 +1304,7 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
   // Q and the score tile in the slice space: dPr = (dO U^T) . D and the decay terms
   // of dGam
   float *s_q = s_ar, *s_dp = s_ar + G::TILE;
+  if (DeltaSlabs<D>::GRAD_OCC > 2) rq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
   rq.put(s_q);
   RowTile<float, D> rw;
   rw.fetch(a.ws_w, b, h, t0, n, a.T, a.H);
@@ -1343,12 +1353,12 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
   }
   // dq = dPr K + eg (dO S0^T); dk (part, kept in registers) = dPr^T Q + el (U dS^T);
   // row partials of Q . (dO S0^T) and el (U dS^T) . K
-  f32x4 dkp[4];
+  f32x4 dkp[KT];
   {
     E* dq = reinterpret_cast<E*>(a.dq);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int ti = m, tj = w;
+    for (int m = 0; m < KT; ++m) {
+      const int t = w + NWV * m, ti = t / G::NTC, tj = t % G::NTC;
       f32x4 x = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_dp[(16 * ti + i) * G::LC + k]; },
                         [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
       f32x4 z = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_dp[k * G::LC + 16 * ti + i]; },
@@ -1405,16 +1415,18 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
   float *s_w = s_ar, *s_dW = s_ar + G::TILE;
   rw.put(s_w);
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < KT; ++m) {
+    const int t = w + NWV * m, ti = t / G::NTC, tj = t % G::NTC;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s_dW[(16 * m + 4 * (l >> 4) + q) * G::LD + 16 * w + (l & 15)] = -x_dus[m][q];
+    for (int q = 0; q < 4; ++q) s_dW[(16 * ti + 4 * (l >> 4) + q) * G::LD + 16 * tj + (l & 15)] = -x_dus[m][q];
+  }
   __syncthreads();
   // dBk = T^T dW in place, held in registers until every wave has read dW
   {
-    f32x4 res[4];
+    f32x4 res[KT];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int ti = m, tj = w;
+    for (int m = 0; m < KT; ++m) {
+      const int t = w + NWV * m, ti = t / G::NTC, tj = t % G::NTC;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int kt = ti; kt < 4; ++kt)
         acc = tile_mm<16>([&](int i, int q) { return s_tm[(16 * kt + q) * G::LC + 16 * ti + i]; },
@@ -1425,9 +1437,11 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
     for (int e = threadIdx.x; e < NWV * CH; e += NTH) (&s_colp[0][0])[e] = 0.f;
     __syncthreads();
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < KT; ++m) {
+      const int t = w + NWV * m, ti = t / G::NTC, tj = t % G::NTC;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s_dW[(16 * m + 4 * (l >> 4) + q) * G::LD + 16 * w + (l & 15)] = res[m][q];
+      for (int q = 0; q < 4; ++q) s_dW[(16 * ti + 4 * (l >> 4) + q) * G::LD + 16 * tj + (l & 15)] = res[m][q];
+    }
   }
   __syncthreads();
   // dA = strict-lower(-(dBv U~^T + dBk W^T)); dAr = dA . D . beta_i in place of T;
@@ -1479,8 +1493,8 @@ __global__ __launch_bounds__(NTH) void delta_grad_wide(DeltaArgs a) {
   {
     E* dk = reinterpret_cast<E*>(a.dk);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int ti = m, tj = w;
+    for (int m = 0; m < KT; ++m) {
+      const int t = w + NWV * m, ti = t / G::NTC, tj = t % G::NTC;
       f32x4 x = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_tm[(16 * ti + i) * G::LC + k]; },
                         [&](int k, int j) { return s_k[k * G::LD + 16 * tj + j]; }, dkp[m]);
       x = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_tm[k * G::LC + 16 * ti + i]; },
@@ -1538,6 +1552,7 @@ CPLA_INST_DELTA(bf16_t, 32)
 CPLA_INST_DELTA(bf16_t, 64)
 CPLA_INST_DELTA_WALKS(bf16_t, 128)
 template __global__ void delta_grad_wide<bf16_t, 128>(DeltaArgs);
+template __global__ void delta_grad_wide<bf16_t, 64>(DeltaArgs);
 template __global__ void delta_scan<16>(DeltaScanArgs);
 template __global__ void delta_scan<32>(DeltaScanArgs);
 template __global__ void delta_scan<64>(DeltaScanArgs);

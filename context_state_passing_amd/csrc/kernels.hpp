@@ -66,7 +66,9 @@ constexpr int DELTA_THREADS = 512;   // threads per workgroup of every delta-rul
 template <int D> struct DeltaSlabs {
   static constexpr int OUT = D;                    // delta_out: value columns
   static constexpr int BWALK = D <= 64 ? D : 64;   // delta_bwalk: value columns of dS
-  static constexpr int GRAD = 32;                  // delta_grad_wide: value slice
+  static constexpr int GRAD = D > 64 ? 32 : 16;    // delta_grad_wide: value slice
+  static constexpr int GRAD_OCC = D > 64 ? 2 : 4;  // delta_grad_wide: waves per SIMD aimed at (4: two
+                                                   // workgroups per CU, 128 registers per lane)
   static constexpr int SCAN = D <= 32 ? D : 32;    // delta_scan: columns of S or dS
 };
 template <int D, bool APPLY> struct FwalkSlab {     // delta_fwalk: columns of [delta_S | M] or S
