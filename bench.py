@@ -522,7 +522,8 @@ def main_delta(args, rank):
         "config": {"workload": wl.name, "B": B, "T": T, "H": H, "dk": d, "dv": d, "chunk": 64, "shards": P,
                    "decay": "gated delta rule (dense transition)", "inputs": "bf16" if wl.dtype == torch.bfloat16
                    else "f32", "parallelism": "single-gpu (shards simulated in HBM)"},
-        "roofline": {"bound": "mfma", "kernel": "cp_backward_apply_delta (delta_scan, delta_bwalk, delta_grad)",
+        "roofline": {"bound": "mfma", "kernel": "cp_backward_apply_delta (delta_scan, delta_bwalk, delta_grad"
+                   + ("_wide" if wl.dtype == torch.bfloat16 and d >= 64 else "") + ")",
                      "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": None,
                      "traffic_note": "counters are taken for the default workload",
