@@ -433,12 +433,12 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
 // (the transition acts on the key side), so a workgroup may own a slab of SZ of
 // them (blockIdx.z; at D = 128 the whole state does not fit the LDS).
 template <typename E, int D, bool APPLY>
-__global__ __launch_bounds__(NTH) void delta_fwalk(DeltaArgs a) {
+__global__ __launch_bounds__(NTH, (FwalkSlab<D, APPLY>::OCC)) void delta_fwalk(DeltaArgs a) {
   using G = DGeo<D>;
   constexpr int NZ = APPLY ? D : 2 * D;
   constexpr int SZ = FwalkSlab<D, APPLY>::SZ;
   constexpr int LZ = SZ + 4;
-  using IT = InTile<E, D>;
+  using IT = InTile<E, D, (D > 64 || FwalkSlab<D, APPLY>::HALF)>;
   __shared__ __attribute__((aligned(16))) float s_z[D * LZ], s_u[CH * LZ], s_w[G::TILE];
   __shared__ __attribute__((aligned(16))) typename IT::T s_k[IT::TILE];
   __shared__ ChunkTerms s_t;

@@ -73,7 +73,11 @@ template <int D> struct DeltaSlabs {
 };
 template <int D, bool APPLY> struct FwalkSlab {     // delta_fwalk: columns of [delta_S | M] or S
   static constexpr int NZ = APPLY ? D : 2 * D;
-  static constexpr int SZ = D <= 64 ? NZ : D;
+  // D = 64 apply: two slabs, so that twice the workgroups run two per CU (measured:
+  // the prepare walk does not gain from it)
+  static constexpr bool HALF = D == 64 && APPLY;
+  static constexpr int SZ = D <= 64 ? (HALF ? NZ / 2 : NZ) : D;
+  static constexpr int OCC = HALF ? 4 : 2;         // waves per SIMD aimed at
 };
 
 struct DeltaArgs {
