@@ -680,13 +680,18 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
 // value columns of dS and dU evolve independently: a workgroup owns SV of them
 // (blockIdx.z).
 template <typename E, int D, bool APPLY>
-__global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
+__global__ __launch_bounds__(NTH, DeltaSlabs<D>::BWALK_OCC) void delta_bwalk(DeltaArgs a) {
   using G = DGeo<D>;
   constexpr int SV = DeltaSlabs<D>::BWALK, LV = SV + 4;
-  using IT = InTile<E, D>;
+  // D = 64: 32-column slabs with bf16 q, k and dU in the score tile's space (P is
+  // dead once dU is formed): 73 KB, two workgroups per CU
+  constexpr bool DU_IN_P = D == 64;
+  static_assert(!DU_IN_P || CH * LV <= G::TILE_C, "dU fits the score tile");
+  using IT = InTile<E, D, (D >= 64)>;
   __shared__ __attribute__((aligned(16))) typename IT::T s_q[IT::TILE], s_k[IT::TILE];
-  __shared__ __attribute__((aligned(16))) float s_do[CH * LV], s_w[G::TILE], s_du[CH * LV], s_ds[D * LV],
-      s_p[G::TILE_C];
+  __shared__ __attribute__((aligned(16))) float s_do[CH * LV], s_w[G::TILE], s_du_own[DU_IN_P ? 4 : CH * LV],
+      s_ds[D * LV], s_p[G::TILE_C];
+  float* const s_du = DU_IN_P ? s_p : s_du_own;
   __shared__ ChunkTerms s_t;
   const int64_t r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
@@ -740,23 +745,43 @@ __global__ __launch_bounds__(NTH) void delta_bwalk(DeltaArgs a) {
       }
     }
     __syncthreads();
-    // dU = P^T dO + K~ dS; with bf16 k tiles the row factor of K~ = el K is applied to
-    // the product instead (k stays exact)
-    for (int t = w; t < 4 * (SV / 16); t += NWV) {
+    // dU = P^T dO + K~ dS; at D = 128 the row factor of K~ = el K is applied to the
+    // product instead (k stays exact). Where dU takes the score tile's space, every
+    // wave's tiles are held until all have read P.
+    constexpr int NDU = 4 * (SV / 16), PDU = (NDU + NWV - 1) / NWV;
+    f32x4 du_res[PDU];
+#pragma unroll
+    for (int m = 0; m < PDU; ++m) {
+      const int t = w + NWV * m;
+      if (t >= NDU) continue;
       const int ti = t / (SV / 16), tj = t % (SV / 16);
       f32x4 acc = tile_mm_e<CH, E, false, true>([&](int i, int k) { return s_p[k * G::LC + 16 * ti + i]; },
                           [&](int k, int j) { return s_do[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
-      if constexpr (IT::raw) {
+      if constexpr (D > 64) {
         const f32x4 y = tile_mm_e<D, E, true, false>([&](int i, int k) { return (float)s_k[(16 * ti + i) * IT::LD + k]; },
                       [&](int k, int j) { return s_ds[k * LV + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
         for (int q = 0; q < 4; ++q) acc[q] += s_t.el[16 * ti + 4 * (l >> 4) + q] * y[q];
       } else {
-        acc = tile_mm_e<D, E>([&](int i, int k) { return s_k[(16 * ti + i) * IT::LD + k] * s_t.el[16 * ti + i]; },
+        acc = tile_mm_e<D, E>([&](int i, int k) { return (float)s_k[(16 * ti + i) * IT::LD + k] * s_t.el[16 * ti + i]; },
                       [&](int k, int j) { return s_ds[k * LV + 16 * tj + j]; }, acc);
       }
+      du_res[m] = acc;
+      if constexpr (!DU_IN_P) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) s_du[(16 * ti + 4 * (l >> 4) + q) * LV + 16 * tj + (l & 15)] = acc[q];
+        for (int q = 0; q < 4; ++q) s_du[(16 * ti + 4 * (l >> 4) + q) * LV + 16 * tj + (l & 15)] = acc[q];
+      }
+    }
+    if constexpr (DU_IN_P) {
+      __syncthreads();   // every read of P is done
+#pragma unroll
+      for (int m = 0; m < PDU; ++m) {
+        const int t = w + NWV * m;
+        if (t >= NDU) continue;
+        const int ti = t / (SV / 16), tj = t % (SV / 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s_du[(16 * ti + 4 * (l >> 4) + q) * LV + 16 * tj + (l & 15)] = du_res[m][q];
+      }
     }
     __syncthreads();
     if constexpr (APPLY) store_rows<float, D, SV>(a.ws_du, s_du, b, h, t0, n, a.T, a.H, v0);

@@ -65,7 +65,8 @@ constexpr int DELTA_THREADS = 512;   // threads per workgroup of every delta-rul
 // chunk's tiles does not fit the LDS.
 template <int D> struct DeltaSlabs {
   static constexpr int OUT = D;                    // delta_out: value columns
-  static constexpr int BWALK = D <= 64 ? D : 64;   // delta_bwalk: value columns of dS
+  static constexpr int BWALK = D < 64 ? D : (D == 64 ? 32 : 64);   // delta_bwalk: value columns of dS
+  static constexpr int BWALK_OCC = D == 64 ? 4 : 2;                 // delta_bwalk: waves per SIMD aimed at
   static constexpr int GRAD = D > 64 ? 32 : 16;    // delta_grad_wide: value slice
   static constexpr int GRAD_OCC = D > 64 ? 2 : 4;  // delta_grad_wide: waves per SIMD aimed at (4: two
                                                    // workgroups per CU, 128 registers per lane)
