@@ -8,9 +8,11 @@ backward summaries (gamma) and the composed outgoing gradients.
 Cases span several chunks per shard and several shards, d = 16, 32, 64 in fp32
 and bf16 and d = 128 in bf16, an initial state, uneven shards with partial last chunks and empty
 shards, and packed sequences (one stream, and one packing per batch row) with
-boundaries inside chunks. Tolerances are the linear-attention ones (fp32 rtol
+boundaries inside chunks; the two benchmark workloads (d = 64 and 128) at full
+size, on sampled (b, h) rows. Tolerances are the linear-attention ones (fp32 rtol
 1e-4 / atol 1e-5, bf16 rtol 2e-2 / atol 2e-3).
 """
+import dataclasses
 import sys
 
 import numpy as np
@@ -153,3 +155,34 @@ def test_random_delta_problems_d128(case, gpu_available):
     rtol, atol = tolerances(wl.dtype)
     for name in ref:
         assert_close(name, got[name], ref[name], rtol, atol)
+
+
+# The benchmark workloads at full size, in the launch configuration the bench
+# times (B2 H16 T8192, 8 shards, bf16): every output of the GPU run for a few
+# sampled (b, h) rows against the oracle run on those rows alone (rows are
+# independent problems).
+BENCH_ROWS = {"d64": ("delta_fwdbwd", 64, [(0, 3), (1, 12)]), "d128": ("delta_d128_fwdbwd", 128, [(1, 5)])}
+
+
+def _row(name, x, b, h):
+    if name in ("M", "delta_S", "S_in", "gamma", "dS_out"):
+        return x[:, b:b + 1, h:h + 1]
+    if name in ("final_state", "d_initial_state"):
+        return x[b:b + 1, h:h + 1]
+    return x[b:b + 1, :, h:h + 1]
+
+
+@pytest.mark.parametrize("case", sorted(BENCH_ROWS))
+def test_delta_bench_shape_sampled_rows(case, gpu_available):
+    name, d, rows = BENCH_ROWS[case]
+    print(f"[gpu-case] delta bench shape {name} rows {rows}", file=sys.stderr, flush=True)
+    wl = workloads.make_delta(name)
+    assert (wl.B, wl.T, wl.H, wl.d, wl.num_shards) == (2, 8192, 16, d, 8)
+    got = _run_gpu(wl)
+    rtol, atol = tolerances(wl.dtype)
+    for b, h in rows:
+        one = dataclasses.replace(wl, B=1, H=1, **{n: getattr(wl, n)[b:b + 1, :, h:h + 1].contiguous()
+                                                  for n in ("q", "k", "v", "g", "beta", "dO")})
+        ref = _run_oracle(one)
+        for n in ref:
+            assert_close(f"{n}[b={b},h={h}]", _row(n, got[n], b, h), ref[n], rtol, atol)
