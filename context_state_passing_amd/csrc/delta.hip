@@ -26,11 +26,13 @@
 //   delta_out     per chunk:  O
 //   delta_bwalk   per shard:  reverse walk of dS; prepare gives gamma, apply saves
 //                             the chunk-end gradients and dU
-//   delta_grad    per chunk:  dq, dk, dv, dg, dbeta
-// d_k = d_v in {16, 32, 64}, and 128 for bf16 inputs: there the walks and delta_out
-// split the state's columns over workgroups and the gradients take the value
-// dimension in slices (delta_grad_wide), as a fp32 state with the chunk's tiles
-// does not fit one workgroup's LDS.
+//   delta_grad    per chunk:  dq, dk, dv, dg, dbeta (delta_grad_wide: the same over
+//                             value slices)
+// d_k = d_v in {16, 32, 64}, and 128 for bf16 inputs: there the walks split the
+// state's columns over workgroups and the gradients take the value dimension in
+// slices, as a fp32 state with the chunk's tiles does not fit one workgroup's LDS.
+// At d = 64 (bf16) the apply and reverse walks and the gradients use the same
+// splits so that two workgroups share a CU.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -431,7 +433,8 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
 // the shard's record as [M | delta_S]. APPLY: S from the composed incoming state;
 // saves the state entering every chunk and U. The columns of Z evolve independently
 // (the transition acts on the key side), so a workgroup may own a slab of SZ of
-// them (blockIdx.z; at D = 128 the whole state does not fit the LDS).
+// them (blockIdx.z; at D = 128 the whole [delta_S | M] does not fit the LDS, at
+// D = 64 two half-width apply walks share a CU).
 template <typename E, int D, bool APPLY>
 __global__ __launch_bounds__(NTH, (FwalkSlab<D, APPLY>::OCC)) void delta_fwalk(DeltaArgs a) {
   using G = DGeo<D>;
@@ -1199,7 +1202,8 @@ __global__ __launch_bounds__(NTH, DeltaSlabs<D>::GRAD_OCC) void delta_grad_wide(
   float *s_do = s_ar, *s_u = s_ar + TV, *s_du = s_ar + 2 * TV, *s_ut = s_ar + 3 * TV, *s_v = s_ar + 4 * TV,
         *s_s0 = s_ar + 5 * TV, *s_ds = s_ar + 5 * TV + TS;
 
-  // K and the terms; Q is held in registers until the slices are done
+  // K and the terms; Q is fetched here and held in registers until the slices are
+  // done, except at two workgroups per CU (fetched after them: registers)
   RowTile<E, D> rq;
   {
     RowTile<E, D> rk;
