@@ -1582,6 +1582,7 @@ CPLA_INST_DELTA(bf16_t, 64)
 CPLA_INST_DELTA_WALKS(bf16_t, 128)
 template __global__ void delta_grad_wide<bf16_t, 128>(DeltaArgs);
 template __global__ void delta_grad_wide<bf16_t, 64>(DeltaArgs);
+template __global__ void delta_grad_wide<float, 64>(DeltaArgs);
 template __global__ void delta_scan<16>(DeltaScanArgs);
 template __global__ void delta_scan<32>(DeltaScanArgs);
 template __global__ void delta_scan<64>(DeltaScanArgs);
