@@ -692,8 +692,8 @@ void delta_launch(DeltaPhase ph, const cpla_problem* p, const DeltaArgs& a, hipS
       break;
     case DP_BWD_GRAD:
       if (nch) {
-        // value slices: needed at D = 128, two workgroups per CU at D = 64
-        if constexpr (D >= 64)
+        // value slices: needed at D = 128, two workgroups per CU at D = 32, 64
+        if constexpr (D >= 32)
           hipLaunchKernelGGL((delta_grad_wide<E, D>), dim3(nch, bh), nt, 0, stream, a);
         else hipLaunchKernelGGL((delta_grad<E, D>), dim3(nch, bh), nt, 0, stream, a);
       }

@@ -1583,6 +1583,8 @@ CPLA_INST_DELTA_WALKS(bf16_t, 128)
 template __global__ void delta_grad_wide<bf16_t, 128>(DeltaArgs);
 template __global__ void delta_grad_wide<bf16_t, 64>(DeltaArgs);
 template __global__ void delta_grad_wide<float, 64>(DeltaArgs);
+template __global__ void delta_grad_wide<bf16_t, 32>(DeltaArgs);
+template __global__ void delta_grad_wide<float, 32>(DeltaArgs);
 template __global__ void delta_scan<16>(DeltaScanArgs);
 template __global__ void delta_scan<32>(DeltaScanArgs);
 template __global__ void delta_scan<64>(DeltaScanArgs);
