@@ -138,12 +138,14 @@ template <typename E, int D, int W = D> struct RowTile {
   R v[PER];
   __device__ __forceinline__ void fetch(const E* src, int64_t b, int64_t h, int64_t t0, int n, int64_t T,
                                         int64_t H, int c0 = 0) {
+    // the chunk's first row once in 64 bits, rows within it in 32 (i < 64, H D < 2^23)
+    const E* base = src + ((b * T + t0) * H + h) * D + c0;
+    const int rs = (int)H * D;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int e = threadIdx.x + p * NTH, i = e / (W / 4), c = 4 * (e % (W / 4));
       v[p] = R{0, 0, 0, 0};
-      if ((NV % NTH == 0 || e < NV) && i < n)
-        v[p] = *reinterpret_cast<const R*>(src + ((b * T + t0 + i) * H + h) * D + c0 + c);
+      if ((NV % NTH == 0 || e < NV) && i < n) v[p] = *reinterpret_cast<const R*>(base + (i * rs + c));
     }
   }
   __device__ __forceinline__ void put(float* dst, int ld = W + 4) const {
@@ -262,8 +264,9 @@ struct TermRegs {
       const int l = threadIdx.x;
       const bool ok = l < n;
       const int64_t t = t0 + l;
-      gv = ok ? g[(b * T + t) * H + h] : 0.f;
-      bv = ok ? beta[(b * T + t) * H + h] : 0.f;
+      const int64_t first = (b * T + t0) * H + h;   // the chunk's first token; tokens within it in 32 bits
+      gv = ok ? g[first + l * (int)H] : 0.f;
+      bv = ok ? beta[first + l * (int)H] : 0.f;
       st = false;
       if (seq && ok) st = seq[t] != (t > 0 ? seq[t - 1] : -1);
     }
