@@ -118,6 +118,12 @@ template <int D> struct DGeo {
 };
 
 
+// index of (b, t0, h) in a [B,T,H] layout: the chunk's first token; the chunk's
+// rows follow at 32-bit offsets i H (i < 64, H d < 2^23)
+__device__ __forceinline__ int64_t row0(int64_t b, int64_t t0, int64_t h, int64_t T, int64_t H) {
+  return (b * T + t0) * H + h;
+}
+
 // Input tiles staged through registers: fetch() issues a thread's global loads
 // (four elements each, in the input type), put() writes them widened to fp32 into
 // an LDS tile. Fetching several tiles before putting any keeps all their loads in
@@ -220,7 +226,7 @@ __device__ __forceinline__ void store_rows(E* dst, const float* src, int64_t b, 
   for (int e = threadIdx.x; e < CH * PER_ROW; e += NTH) {
     const int i = e / PER_ROW, c = 4 * (e % PER_ROW);
     if (i >= n) continue;
-    E* p = dst + ((b * T + t0 + i) * H + h) * D + c0 + c;
+    E* p = dst + row0(b, t0, h, T, H) * D + c0 + (i * ((int)H * D) + c);
 #pragma unroll
     for (int u = 0; u < 4; ++u) p[u] = (E)src[i * (W + 4) + c + u];
   }
@@ -425,7 +431,7 @@ __global__ __launch_bounds__(NTH) void delta_wy(DeltaArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = 16 * ti + 4 * (l >> 4) + q;
-        if (i < n) dst[((b * a.T + t0 + i) * a.H + h) * D + c0 + (l & 15)] = acc[q];
+        if (i < n) dst[row0(b, t0, h, a.T, a.H) * D + (i * ((int)a.H * D) + c0 + (l & 15))] = acc[q];
       }
     }
   }
@@ -514,7 +520,7 @@ __global__ __launch_bounds__(NTH, (FwalkSlab<D, APPLY>::OCC)) void delta_fwalk(D
     if constexpr (APPLY) {
       for (int e = threadIdx.x; e < CH * SZ; e += NTH) {
         const int i = e / SZ, m = e % SZ;
-        if (i < n) a.ws_u[((b * a.T + t0 + i) * a.H + h) * D + z0 + m] = s_u[i * LZ + m];
+        if (i < n) a.ws_u[row0(b, t0, h, a.T, a.H) * D + (i * ((int)a.H * D) + z0 + m)] = s_u[i * LZ + m];
       }
     }
     // Z <- live_last e^Gam_last Z + K~^T U_Z
@@ -674,7 +680,7 @@ __global__ __launch_bounds__(NTH) void delta_out(DeltaArgs a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int i = 16 * ti + 4 * (l >> 4) + q, j = v0 + 16 * tj + (l & 15);
-      if (i < n) o[((b * a.T + t0 + i) * a.H + h) * D + j] = (E)(s_t.eg[i] * x[q] + y[q]);
+      if (i < n) o[row0(b, t0, h, a.T, a.H) * D + (i * ((int)a.H * D) + j)] = (E)(s_t.eg[i] * x[q] + y[q]);
     }
   }
 }
@@ -940,7 +946,7 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
       for (int q = 0; q < 4; ++q) {
         const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
         const float eg = s_t.eg[i], el = s_t.el[i];
-        if (i < n) dq[((b * a.T + t0 + i) * a.H + h) * D + j] = (E)(x[q] + eg * y[q]);
+        if (i < n) dq[row0(b, t0, h, a.T, a.H) * D + (i * ((int)a.H * D) + j)] = (E)(x[q] + eg * y[q]);
         const float ue = el * u[q];
         s_dk[i * G::LD + j] = z[q] + ue;
         float p1 = eg * y[q] * s_q[i * G::LD + j];
@@ -1129,7 +1135,7 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
         const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
         if (i < n) {
           const float bt = s_t.beta[i];
-          const int64_t off = ((b * a.T + t0 + i) * a.H + h) * D + j;
+          const int64_t off = row0(b, t0, h, a.T, a.H) * D + (i * ((int)a.H * D) + j);
           dk[off] = (E)(s_dk[i * G::LD + j] + x[q] + bt * s_t.eg[i] * s_dW[i * G::LD + j]);
           dv[off] = (E)(bt * s_dU[i * G::LD + j]);
         }
@@ -1161,8 +1167,8 @@ __global__ __launch_bounds__(NTH) void delta_grad(DeltaArgs a) {
     }
     const bool start = i == 0 ? (seq && cnt == 1) : cnt != s_t.cnt[i - 1];
     if (i < n) {
-      a.dbeta[(b * a.T + t0 + i) * a.H + h] = dbeta;
-      a.dg[(b * a.T + t0 + i) * a.H + h] = start ? 0.f : x;
+      a.dbeta[row0(b, t0, h, a.T, a.H) + i * (int)a.H] = dbeta;
+      a.dg[row0(b, t0, h, a.T, a.H) + i * (int)a.H] = start ? 0.f : x;
     }
   }
 }
@@ -1306,7 +1312,7 @@ __global__ __launch_bounds__(NTH, DeltaSlabs<D>::GRAD_OCC) void delta_grad_wide(
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int i = 16 * ti + 4 * (l >> 4) + q;
-        if (i < n) dv[((b * a.T + t0 + i) * a.H + h) * D + v0 + 16 * tj + (l & 15)] = (E)(s_t.beta[i] * bv[q]);
+        if (i < n) dv[row0(b, t0, h, a.T, a.H) * D + (i * ((int)a.H * D) + v0 + 16 * tj + (l & 15))] = (E)(s_t.beta[i] * bv[q]);
       }
     }
     __syncthreads();   // every read of dU is done
@@ -1400,7 +1406,7 @@ __global__ __launch_bounds__(NTH, DeltaSlabs<D>::GRAD_OCC) void delta_grad_wide(
         const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
         const float eg = s_t.eg[i], el = s_t.el[i];
         const float y = x_dos[m][q];
-        if (i < n) dq[((b * a.T + t0 + i) * a.H + h) * D + j] = (E)(x[q] + eg * y);
+        if (i < n) dq[row0(b, t0, h, a.T, a.H) * D + (i * ((int)a.H * D) + j)] = (E)(x[q] + eg * y);
         const float ue = el * x_uds[m][q];
         dkp[m][q] = z[q] + ue;
         float p1 = eg * y * s_q[i * G::LD + j];
@@ -1535,7 +1541,7 @@ __global__ __launch_bounds__(NTH, DeltaSlabs<D>::GRAD_OCC) void delta_grad_wide(
       for (int q = 0; q < 4; ++q) {
         const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
         if (i < n)
-          dk[((b * a.T + t0 + i) * a.H + h) * D + j] = (E)(x[q] + s_t.beta[i] * s_t.eg[i] * s_dW[i * G::LD + j]);
+          dk[row0(b, t0, h, a.T, a.H) * D + (i * ((int)a.H * D) + j)] = (E)(x[q] + s_t.beta[i] * s_t.eg[i] * s_dW[i * G::LD + j]);
       }
     }
   }
@@ -1560,8 +1566,8 @@ __global__ __launch_bounds__(NTH, DeltaSlabs<D>::GRAD_OCC) void delta_grad_wide(
     }
     const bool start = i == 0 ? (seq && cnt == 1) : cnt != s_t.cnt[i - 1];
     if (i < n) {
-      a.dbeta[(b * a.T + t0 + i) * a.H + h] = dbeta;
-      a.dg[(b * a.T + t0 + i) * a.H + h] = start ? 0.f : x;
+      a.dbeta[row0(b, t0, h, a.T, a.H) + i * (int)a.H] = dbeta;
+      a.dg[row0(b, t0, h, a.T, a.H) + i * (int)a.H] = start ? 0.f : x;
     }
   }
 }
