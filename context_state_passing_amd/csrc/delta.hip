@@ -1265,9 +1265,10 @@ __global__ __launch_bounds__(NTH, DeltaSlabs<D>::GRAD_OCC) void delta_grad_wide(
     put_.fetch(a.ws_ut, b, h, t0, n, a.T, a.H, v0);
     pv.fetch(reinterpret_cast<const E*>(a.v), b, h, t0, n, a.T, a.H, v0);
   };
-  // at one workgroup per CU the next slice is fetched while this one is computed;
-  // at two the other workgroup covers the loads, and the registers are needed
-  constexpr bool PREFETCH = DeltaSlabs<D>::GRAD_OCC <= 2;
+  // the next slice is fetched while this one is computed, except at D = 64, where
+  // the registers it needs cost as many spills as it saves (measured; two
+  // workgroups share a CU there and cover each other's loads)
+  constexpr bool PREFETCH = D != 64;
   if (PREFETCH) fetch_slice(0);
   E* dv = reinterpret_cast<E*>(a.dv);
   for (int sl = 0; sl < NSL; ++sl) {
