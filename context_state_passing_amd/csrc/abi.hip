@@ -682,7 +682,9 @@ void delta_launch(DeltaPhase ph, const cpla_problem* p, const DeltaArgs& a, hipS
                          dim3(nr, bh, FwalkSlab<D, true>::NZ / FwalkSlab<D, true>::SZ), nt, 0, stream, a);
       break;
     case DP_FWD_OUT:
-      if (nch) hipLaunchKernelGGL((delta_out<E, D>), dim3(nch, bh, D / DeltaSlabs<D>::OUT), nt, 0, stream, a);
+      // the half-width bf16 apply walk (D = 64) has written o itself
+      if constexpr (!(FwalkSlab<D, true>::HALF && sizeof(E) == 2))
+        if (nch) hipLaunchKernelGGL((delta_out<E, D>), dim3(nch, bh, D / DeltaSlabs<D>::OUT), nt, 0, stream, a);
       break;
     case DP_BWD_PREPARE:
       hipLaunchKernelGGL((delta_bwalk<E, D, false>), dim3(nr, bh, D / DeltaSlabs<D>::BWALK), nt, 0, stream, a);

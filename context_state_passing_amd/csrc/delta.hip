@@ -451,8 +451,13 @@ __global__ __launch_bounds__(NTH, (FwalkSlab<D, APPLY>::OCC)) void delta_fwalk(D
   constexpr int SZ = FwalkSlab<D, APPLY>::SZ;
   constexpr int LZ = SZ + 4;
   using IT = InTile<E, D, (D > 64 || FwalkSlab<D, APPLY>::HALF)>;
+  // the half-width bf16 apply walk (D = 64) also forms the output of its value
+  // columns, O = live e^Gam Q S + P U (delta_out's work, the state and U being at
+  // hand): Q and the score tile P fit beside the slab at two workgroups per CU
+  constexpr bool FOLD = FwalkSlab<D, APPLY>::HALF && sizeof(E) == 2;
   __shared__ __attribute__((aligned(16))) float s_z[D * LZ], s_u[CH * LZ], s_w[G::TILE];
-  __shared__ __attribute__((aligned(16))) typename IT::T s_k[IT::TILE];
+  __shared__ __attribute__((aligned(16))) typename IT::T s_k[IT::TILE], s_q[FOLD ? IT::TILE : 8];
+  __shared__ __attribute__((aligned(16))) float s_p[FOLD ? G::TILE_C : 4];
   __shared__ ChunkTerms s_t;
   const int64_t r = a.rank_begin + blockIdx.x;
   const int64_t bh = blockIdx.y, b = bh / a.H, h = bh % a.H;
@@ -477,7 +482,7 @@ __global__ __launch_bounds__(NTH, (FwalkSlab<D, APPLY>::OCC)) void delta_fwalk(D
   constexpr int UW = SZ < D ? SZ : D;            // U~ columns a slab takes
   RowTile<float, D> pw;
   RowTile<float, D, UW> pu;
-  RowTile<E, D> pk;
+  RowTile<E, D> pk, pq;
   TermRegs pt;
   auto fetch_chunk = [&](int c) {
     const int64_t t0 = tshard + 64 * c;
@@ -485,6 +490,7 @@ __global__ __launch_bounds__(NTH, (FwalkSlab<D, APPLY>::OCC)) void delta_fwalk(D
     pt.fetch(a.g, a.beta, seq, b, h, t0, n, a.T, a.H);
     pw.fetch(a.ws_w, b, h, t0, n, a.T, a.H);
     pk.fetch(reinterpret_cast<const E*>(a.k), b, h, t0, n, a.T, a.H);
+    if constexpr (FOLD) pq.fetch(reinterpret_cast<const E*>(a.q), b, h, t0, n, a.T, a.H);
     if (takes_u) pu.fetch(a.ws_ut, b, h, t0, n, a.T, a.H, z0);
   };
   if (nc > 0) fetch_chunk(0);
@@ -493,6 +499,7 @@ __global__ __launch_bounds__(NTH, (FwalkSlab<D, APPLY>::OCC)) void delta_fwalk(D
     const int n = (int)(slen - 64 * c < CH ? slen - 64 * c : CH);
     pw.put(s_w);
     IT::put(pk, s_k);
+    if constexpr (FOLD) IT::put(pq, s_q);
     // U~ into the slab's delta_S columns of s_u (the M part takes no input)
     if (takes_u) pu.put(s_u, LZ);
     if constexpr (SZ > UW || NZ > D) {
@@ -505,18 +512,73 @@ __global__ __launch_bounds__(NTH, (FwalkSlab<D, APPLY>::OCC)) void delta_fwalk(D
       float* cs = a.chunk_states + (bh * nct + cbase + c) * (int64_t)(D * D);
       for (int e = threadIdx.x; e < D * SZ; e += NTH) cs[(e / SZ) * D + z0 + e % SZ] = s_z[(e / SZ) * LZ + e % SZ];
     }
-    // U_Z = U~_Z - W Z
-    for (int t = w; t < 4 * (SZ / 16); t += NWV) {
-      const int ti = t / (SZ / 16), tj = t % (SZ / 16);
-      f32x4 acc = tile_mm_e<D, E>([&](int i, int k) { return s_w[(16 * ti + i) * G::LD + k]; },
-                          [&](int k, int j) { return s_z[k * LZ + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+    // U_Z = U~_Z - W Z (and, folding the output, Q S for the same tiles and the
+    // score tile P, both taken before Z is updated)
+    constexpr int NUT = 4 * (SZ / 16), PUT = (NUT + NWV - 1) / NWV;
+    f32x4 xo[FOLD ? PUT : 1];
+    if constexpr (!FOLD) {
+      for (int t = w; t < NUT; t += NWV) {
+        const int ti = t / (SZ / 16), tj = t % (SZ / 16);
+        f32x4 acc = tile_mm_e<D, E>([&](int i, int k) { return s_w[(16 * ti + i) * G::LD + k]; },
+                            [&](int k, int j) { return s_z[k * LZ + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
-        s_u[i * LZ + j] -= acc[q];
+        for (int q = 0; q < 4; ++q) {
+          const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+          s_u[i * LZ + j] -= acc[q];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < PUT; ++m) {
+        const int t = w + NWV * m;
+        if (t >= NUT) continue;
+        const int ti = t / (SZ / 16), tj = t % (SZ / 16);
+        f32x4 acc = tile_mm_e<D, E>([&](int i, int k) { return s_w[(16 * ti + i) * G::LD + k]; },
+                            [&](int k, int j) { return s_z[k * LZ + 16 * tj + j]; }, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+          s_u[i * LZ + j] -= acc[q];
+        }
+        xo[m] = tile_mm_e<D, E, true, false>([&](int i, int k) { return (float)s_q[(16 * ti + i) * IT::LD + k]; },
+                                             [&](int k, int j) { return s_z[k * LZ + 16 * tj + j]; },
+                                             f32x4{0.f, 0.f, 0.f, 0.f});
+      }
+      for (int t = w; t < 16; t += NWV) {
+        const int ti = t >> 2, tj = t & 3;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (tj <= ti)
+          acc = tile_mm_e<D, E, true, true>([&](int i, int k) { return (float)s_q[(16 * ti + i) * IT::LD + k]; },
+                                            [&](int k, int j) { return (float)s_k[(16 * tj + j) * IT::LD + k]; }, acc);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = 16 * ti + 4 * (l >> 4) + q, j = 16 * tj + (l & 15);
+          const bool ok = j <= i && s_t.cnt[i] == s_t.cnt[j];
+          s_p[i * G::LC + j] = ok ? __expf(s_t.gam[i] - s_t.gam[j]) * acc[q] : 0.f;
+        }
       }
     }
     __syncthreads();
+    if constexpr (FOLD) {
+      // O = live e^Gam Q S + P U for the slab's value columns
+      E* o = reinterpret_cast<E*>(a.out);
+#pragma unroll
+      for (int m = 0; m < PUT; ++m) {
+        const int t = w + NWV * m;
+        if (t >= NUT) continue;
+        const int ti = t / (SZ / 16), tj = t % (SZ / 16);
+        const f32x4 y = tile_mm_e<CH, E>([&](int i, int k) { return s_p[(16 * ti + i) * G::LC + k]; },
+                                         [&](int k, int j) { return s_u[k * LZ + 16 * tj + j]; },
+                                         f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = 16 * ti + 4 * (l >> 4) + q;
+          if (i < n)
+            o[row0(b, t0, h, a.T, a.H) * D + (i * ((int)a.H * D) + z0 + 16 * tj + (l & 15))] =
+                (E)(s_t.eg[i] * xo[m][q] + y[q]);
+        }
+      }
+    }
     if constexpr (APPLY) {
       for (int e = threadIdx.x; e < CH * SZ; e += NTH) {
         const int i = e / SZ, m = e % SZ;
