@@ -23,7 +23,7 @@
 //                             from [0 | I], apply saves chunk states and U
 //   delta_scan    per (b,h):  composition S <- M S + delta_S over shards (or its
 //                             transpose backwards)
-//   delta_out     per chunk:  O
+//   delta_out     per chunk:  O (d = 64, bf16: formed by the apply walk instead)
 //   delta_bwalk   per shard:  reverse walk of dS; prepare gives gamma, apply saves
 //                             the chunk-end gradients and dU
 //   delta_grad    per chunk:  dq, dk, dv, dg, dbeta (delta_grad_wide: the same over
